@@ -1,0 +1,563 @@
+// Host side of the C ABI declared in include/cca.h: config validation, size
+// queries, the RoPE table, launch sequencing and the event-based kernel timer.
+// No kernel arithmetic lives here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/cca.h"
+#include "cca_internal.h"
+
+using namespace cca;
+
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+
+struct cca_handle {
+  cca_config cfg;
+  Dims dm;
+  float2* rope = nullptr;     // [max_seq_len][d/2] (cos, sin)
+  int device = 0;
+  bool profiling = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+};
+
+namespace {
+
+void put_msg(char* msg, size_t len, const char* fmt, ...) {
+  if (!msg || len == 0) return;
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(msg, len, fmt, ap);
+  va_end(ap);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t esize(const Dims& dm) { return dm.bf16 ? 2 : 4; }
+
+Dims make_dims(const cca_config& c) {
+  Dims dm{};
+  dm.E = c.E;
+  dm.Hq = c.n_q_heads;
+  dm.Hkv = c.n_kv_heads;
+  dm.d = c.E / (c.C * c.n_q_heads);
+  dm.G = dm.Hq / dm.Hkv;
+  dm.kq = c.conv_kernel_q;
+  dm.kk = c.conv_kernel_k;
+  dm.sv = c.v_shift_channels;
+  dm.nq = dm.Hq * dm.d;
+  dm.nk = dm.Hkv * dm.d;
+  dm.nqkv = dm.nq + 2 * dm.nk;
+  dm.state_w = (dm.kq - 1) * dm.nq + (dm.kk - 1) * dm.nk + dm.nk;
+  dm.max_seq_len = c.max_seq_len;
+  dm.flags = c.flags;
+  dm.bf16 = c.dtype == CCA_BF16;
+  return dm;
+}
+
+// Saved-buffer regions (see cca_saved_bytes).
+constexpr int kSavedRegions = 7;
+struct SavedLayout {
+  size_t off[kSavedRegions];
+  size_t total;
+};
+
+SavedLayout saved_layout(const Dims& dm, long B, long S) {
+  const size_t es = esize(dm);
+  const size_t sz[kSavedRegions] = {
+      (size_t)(B * S * dm.nqkv) * 4,                                // q~|k~|v~ fp32
+      (size_t)(B * S * dm.nq) * es, (size_t)(B * S * dm.nk) * es,   // Q'', K''
+      (size_t)(B * S * dm.nk) * es, (size_t)(B * S * dm.nq) * es,   // V', O
+      (size_t)(B * dm.Hq * S) * 4,                                  // lse
+      (size_t)(B * S * dm.nq) * 4};                                 // O fp32
+  SavedLayout L{};
+  size_t o = 0;
+  for (int i = 0; i < kSavedRegions; ++i) {
+    L.off[i] = o;
+    o = align256(o + sz[i]);
+  }
+  L.total = o;
+  return L;
+}
+
+struct DecodeLayout {
+  size_t qkv, q, o, part, total;
+};
+
+DecodeLayout decode_layout(const Dims& dm, long B) {
+  const size_t es = esize(dm);
+  DecodeLayout L{};
+  size_t o = 0;
+  L.qkv = o; o = align256(o + B * dm.nqkv * 4);
+  L.q = o;   o = align256(o + B * dm.nq * es);
+  L.o = o;   o = align256(o + B * dm.nq * es);
+  L.part = o; o = align256(o + decode_part_floats(dm, (int)B) * 4);
+  L.total = o;
+  return L;
+}
+
+struct BwdLayout {
+  size_t dO, Dsum, dq, dk, dv, dqkv, part, scratch, total;
+};
+
+BwdLayout bwd_layout(const Dims& dm, long B, long S) {
+  const size_t es = esize(dm);
+  BwdLayout L{};
+  size_t o = 0;
+  L.dO = o;      o = align256(o + (size_t)(B * S * dm.nq) * es);
+  L.Dsum = o;    o = align256(o + (size_t)(B * dm.Hq * S) * 4);
+  L.dq = o;      o = align256(o + (size_t)(B * S * dm.nq) * 4);
+  L.dk = o;      o = align256(o + (size_t)(B * S * dm.nk) * 4);
+  L.dv = o;      o = align256(o + (size_t)(B * S * dm.nk) * 4);
+  L.dqkv = o;    o = align256(o + (size_t)(B * S * dm.nqkv) * es);
+  L.part = o;    o = align256(o + mix_bwd_part_floats(dm, (int)B, (int)S) * 4);
+  L.scratch = o; o = align256(o + mix_bwd_scratch_floats(dm, (int)B, (int)S) * 4);
+  L.total = o;
+  return L;
+}
+
+// Runs one launch, bracketed by timing events when profiling is on.
+template <typename F>
+hipError_t timed(cca_handle* h, const char* name, hipStream_t s, F&& launch) {
+  if (!h->profiling) return launch();
+  ProfRec r{name, nullptr, nullptr};
+  for (hipEvent_t* e : {&r.start, &r.stop}) {
+    if (!h->pool.empty()) {
+      *e = h->pool.back();
+      h->pool.pop_back();
+    } else if (hipEventCreate(e) != hipSuccess) {
+      return hipErrorOutOfMemory;
+    }
+  }
+  hipEventRecord(r.start, s);
+  hipError_t err = launch();
+  hipEventRecord(r.stop, s);
+  h->recs.push_back(r);
+  return err;
+}
+
+GemmArgs gemm_nt(int M, int N, int K, const void* a, long lda, const void* b, long ldb, void* c,
+                 long ldc) {
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.a = a; g.lda = lda;
+  g.b_ptr[0] = b; g.b_start[0] = 0; g.b_nseg = 1; g.ldb = ldb;
+  g.c_ptr[0] = c; g.c_start[0] = 0; g.c_nseg = 1; g.ldc = ldc;
+  return g;
+}
+
+// Down-projection: C[M, nqkv] = A[M, E] * [W_q; W_k; W_v]^T
+GemmArgs gemm_down(const Dims& dm, int M, const void* a, const cca_weights* w, void* c) {
+  GemmArgs g = gemm_nt(M, dm.nqkv, dm.E, a, dm.E, w->w_q, dm.E, c, dm.nqkv);
+  g.b_ptr[1] = w->w_k; g.b_start[1] = dm.nq;
+  g.b_ptr[2] = w->w_v; g.b_start[2] = dm.nq + dm.nk;
+  g.b_nseg = 3;
+  return g;
+}
+
+#define CCA_TRY_HIP(expr)                         \
+  do {                                            \
+    hipError_t e_ = (expr);                       \
+    if (e_ != hipSuccess) return CCA_ERR_HIP;     \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* cca_status_string(cca_status s) {
+  switch (s) {
+    case CCA_OK: return "ok";
+    case CCA_ERR_INVALID_CONFIG: return "invalid config";
+    case CCA_ERR_INVALID_ARG: return "invalid argument";
+    case CCA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case CCA_ERR_CAPACITY: return "position or length exceeds max_seq_len";
+    case CCA_ERR_HIP: return "HIP runtime error";
+    case CCA_ERR_OOM: return "out of device memory";
+  }
+  return "unknown status";
+}
+
+cca_status cca_validate_config(const cca_config* c, char* msg, size_t msg_len) {
+  if (!c) { put_msg(msg, msg_len, "config is NULL"); return CCA_ERR_INVALID_CONFIG; }
+  if (c->struct_size != sizeof(cca_config)) {
+    put_msg(msg, msg_len, "struct_size %u != %zu", c->struct_size, sizeof(cca_config));
+    return CCA_ERR_INVALID_CONFIG;
+  }
+  if (c->E <= 0 || c->C <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0) {
+    put_msg(msg, msg_len, "E, C and head counts must be positive");
+    return CCA_ERR_INVALID_CONFIG;
+  }
+  if (c->E % (c->C * c->n_q_heads) != 0) {
+    put_msg(msg, msg_len, "E %% (C * n_q_heads) != 0");
+    return CCA_ERR_INVALID_CONFIG;
+  }
+  if (c->n_q_heads % c->n_kv_heads != 0) {
+    put_msg(msg, msg_len, "n_q_heads %% n_kv_heads != 0");
+    return CCA_ERR_INVALID_CONFIG;
+  }
+  const int d = c->E / (c->C * c->n_q_heads);
+  if (d < 2 || d % 2 != 0) {
+    put_msg(msg, msg_len, "head dim d = %d must be even", d);
+    return CCA_ERR_INVALID_CONFIG;
+  }
+  if (c->max_seq_len < 1) { put_msg(msg, msg_len, "max_seq_len < 1"); return CCA_ERR_INVALID_CONFIG; }
+  if (c->conv_kernel_q < 1 || c->conv_kernel_k < 1) {
+    put_msg(msg, msg_len, "conv kernel sizes must be >= 1");
+    return CCA_ERR_INVALID_CONFIG;
+  }
+  if (c->v_shift_channels < 0 || c->v_shift_channels > d) {
+    put_msg(msg, msg_len, "v_shift_channels must be in [0, d]");
+    return CCA_ERR_INVALID_CONFIG;
+  }
+  if (c->flags & ~(uint32_t)CCA_DEFAULT_FLAGS) {
+    put_msg(msg, msg_len, "unknown flag bits");
+    return CCA_ERR_INVALID_CONFIG;
+  }
+  if ((c->flags & CCA_ROPE) && !(c->rope_base > 1.0)) {
+    put_msg(msg, msg_len, "rope_base must be > 1");
+    return CCA_ERR_INVALID_CONFIG;
+  }
+  if (c->dtype != CCA_F32 && c->dtype != CCA_BF16) {
+    put_msg(msg, msg_len, "dtype must be CCA_F32 or CCA_BF16");
+    return CCA_ERR_INVALID_CONFIG;
+  }
+  // consistent, but outside what the kernels here implement
+  if (d > 128) { put_msg(msg, msg_len, "head dim %d > 128", d); return CCA_ERR_UNSUPPORTED; }
+  if (c->conv_kernel_q > kMaxConv || c->conv_kernel_k > kMaxConv) {
+    put_msg(msg, msg_len, "conv kernel size > %d", kMaxConv);
+    return CCA_ERR_UNSUPPORTED;
+  }
+  if (c->n_q_heads / c->n_kv_heads > kMaxGroup) {
+    put_msg(msg, msg_len, "more than %d query heads per KV head", kMaxGroup);
+    return CCA_ERR_UNSUPPORTED;
+  }
+  if (c->dtype == CCA_BF16 && (c->E % 8 != 0 || d % 8 != 0)) {
+    put_msg(msg, msg_len, "bf16 needs E and d multiples of 8");
+    return CCA_ERR_UNSUPPORTED;
+  }
+  if ((long)c->max_seq_len * d > (1L << 31)) {
+    put_msg(msg, msg_len, "max_seq_len * d too large");
+    return CCA_ERR_UNSUPPORTED;
+  }
+  put_msg(msg, msg_len, "ok");
+  return CCA_OK;
+}
+
+cca_status cca_create(const cca_config* cfg, cca_handle** out) {
+  if (!out) return CCA_ERR_INVALID_ARG;
+  *out = nullptr;
+  cca_status st = cca_validate_config(cfg, nullptr, 0);
+  if (st != CCA_OK) return st;
+  cca_handle* h = new (std::nothrow) cca_handle();
+  if (!h) return CCA_ERR_OOM;
+  h->cfg = *cfg;
+  h->dm = make_dims(*cfg);
+  if (hipGetDevice(&h->device) != hipSuccess) { delete h; return CCA_ERR_HIP; }
+  // RoPE angles p * base^(-2i/d) in float64, stored as fp32 cos/sin pairs
+  const int half = h->dm.d / 2;
+  const size_t n = (size_t)cfg->max_seq_len * half;
+  std::vector<float2> tab;
+  try {
+    tab.resize(n);
+  } catch (...) {
+    delete h;
+    return CCA_ERR_OOM;
+  }
+  for (int i = 0; i < half; ++i) {
+    const double inv = std::pow(cfg->rope_base > 1.0 ? cfg->rope_base : 10000.0,
+                                -2.0 * (double)i / (double)h->dm.d);
+    for (int p = 0; p < cfg->max_seq_len; ++p) {
+      const double ang = (double)p * inv;
+      tab[(size_t)p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+    }
+  }
+  if (hipMalloc((void**)&h->rope, n * sizeof(float2)) != hipSuccess) {
+    delete h;
+    return CCA_ERR_OOM;
+  }
+  if (hipMemcpy(h->rope, tab.data(), n * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess) {
+    hipFree(h->rope);
+    delete h;
+    return CCA_ERR_HIP;
+  }
+  *out = h;
+  return CCA_OK;
+}
+
+void cca_destroy(cca_handle* h) {
+  if (!h) return;
+  for (auto& r : h->recs) { hipEventDestroy(r.start); hipEventDestroy(r.stop); }
+  for (auto e : h->pool) hipEventDestroy(e);
+  if (h->rope) hipFree(h->rope);
+  delete h;
+}
+
+size_t cca_saved_bytes(const cca_handle* h, int32_t B, int32_t S) {
+  if (!h || B <= 0 || S <= 0) return 0;
+  return saved_layout(h->dm, B, S).total;
+}
+
+cca_status cca_saved_offsets(const cca_handle* h, int32_t B, int32_t S, size_t offsets[7]) {
+  if (!h || B <= 0 || S <= 0 || !offsets) return CCA_ERR_INVALID_ARG;
+  SavedLayout L = saved_layout(h->dm, B, S);
+  for (int i = 0; i < kSavedRegions; ++i) offsets[i] = L.off[i];
+  return CCA_OK;
+}
+
+size_t cca_state_bytes(const cca_handle* h, int32_t B) {
+  if (!h || B <= 0) return 0;
+  return (size_t)B * h->dm.state_w * esize(h->dm);
+}
+
+size_t cca_workspace_bytes(const cca_handle* h, int op, int32_t B, int32_t S) {
+  if (!h || B <= 0) return 0;
+  switch (op) {
+    case CCA_OP_PREFILL: return S > 0 ? saved_layout(h->dm, B, S).total : 0;
+    case CCA_OP_DECODE: return decode_layout(h->dm, B).total;
+    case CCA_OP_BACKWARD: return S > 0 ? bwd_layout(h->dm, B, S).total : 0;
+  }
+  return 0;
+}
+
+cca_status cca_forward_prefill(cca_handle* h, const cca_weights* w, const void* x, int32_t B,
+                               int32_t S, void* y, void* saved, void* k_cache, void* v_cache,
+                               void* state, void* workspace, void* stream) {
+  try {
+    if (!h || !w || !x || !y) return CCA_ERR_INVALID_ARG;
+    if (B < 1 || S < 1) return CCA_ERR_INVALID_ARG;
+    if (S > h->cfg.max_seq_len) return CCA_ERR_CAPACITY;
+    if (!w->w_q || !w->w_k || !w->w_v || !w->w_o || !w->conv_q || !w->conv_k)
+      return CCA_ERR_INVALID_ARG;
+    if ((k_cache == nullptr) != (v_cache == nullptr)) return CCA_ERR_INVALID_ARG;
+    void* buf = saved ? saved : workspace;
+    if (!buf) return CCA_ERR_INVALID_ARG;
+    for (const void* p : {x, (const void*)y, w->w_q, w->w_k, w->w_v, w->w_o, w->conv_q,
+                          w->conv_k, (const void*)buf, (const void*)k_cache,
+                          (const void*)v_cache, (const void*)state})
+      if (!aligned16(p)) return CCA_ERR_INVALID_ARG;
+    const Dims& dm = h->dm;
+    hipStream_t s = (hipStream_t)stream;
+    SavedLayout L = saved_layout(dm, B, S);
+    char* base = (char*)buf;
+    float* qkv = (float*)(base + L.off[0]);
+    void* qr = base + L.off[1];
+    void* kr = base + L.off[2];
+    void* vs = base + L.off[3];
+    void* o = base + L.off[4];
+    float* lse = (float*)(base + L.off[5]);
+    float* o32 = saved ? (float*)(base + L.off[6]) : nullptr;
+    const int M = B * S;
+
+    GemmArgs gd = gemm_down(dm, M, x, w, qkv);
+    CCA_TRY_HIP(timed(h, "proj_down", s, [&] { return launch_gemm(gd, GemmLayout::NT, dm.bf16, true, s); }));
+
+    MixArgs ma{};
+    ma.dm = dm; ma.B = B; ma.S = S; ma.qkv = qkv;
+    ma.conv_q = w->conv_q; ma.conv_k = w->conv_k; ma.rope = h->rope;
+    ma.q_out = qr; ma.k_out = kr; ma.v_out = vs;
+    ma.k_out2 = k_cache; ma.v_out2 = v_cache; ma.cap2 = dm.max_seq_len;
+    CCA_TRY_HIP(timed(h, "mix", s, [&] { return launch_mix_fwd(ma, s); }));
+    if (state)
+      CCA_TRY_HIP(timed(h, "write_state", s, [&] { return launch_write_state(dm, B, S, qkv, state, s); }));
+
+    AttnArgs aa{};
+    aa.dm = dm; aa.B = B; aa.Sq = S;
+    aa.q = qr; aa.k = kr; aa.v = vs;
+    aa.kv_bs = (long)dm.Hkv * S * dm.d; aa.kv_hs = (long)S * dm.d;
+    aa.o = o; aa.o32 = o32; aa.lse = lse; aa.decode = false;
+    CCA_TRY_HIP(timed(h, "attn", s, [&] { return launch_attn_fwd(aa, s); }));
+
+    GemmArgs gu = gemm_nt(M, dm.E, dm.nq, o, dm.nq, w->w_o, dm.nq, y, dm.E);
+    CCA_TRY_HIP(timed(h, "proj_up", s, [&] { return launch_gemm(gu, GemmLayout::NT, dm.bf16, false, s); }));
+    return CCA_OK;
+  } catch (const std::bad_alloc&) {
+    return CCA_ERR_OOM;
+  } catch (...) {
+    return CCA_ERR_HIP;
+  }
+}
+
+cca_status cca_decode_step(cca_handle* h, const cca_weights* w, const void* x_new,
+                           const int32_t* pos_host, int32_t B, void* k_cache, void* v_cache,
+                           void* state, void* y_new, void* workspace, void* stream) {
+  try {
+    if (!h || !w || !x_new || !pos_host || !k_cache || !v_cache || !state || !y_new || !workspace)
+      return CCA_ERR_INVALID_ARG;
+    if (B < 1) return CCA_ERR_INVALID_ARG;
+    if (B > kMaxDecodeBatch) return CCA_ERR_UNSUPPORTED;
+    if (!w->w_q || !w->w_k || !w->w_v || !w->w_o || !w->conv_q || !w->conv_k)
+      return CCA_ERR_INVALID_ARG;
+    for (const void* p : {x_new, (const void*)k_cache, (const void*)v_cache, (const void*)state,
+                          (const void*)y_new, (const void*)workspace, w->w_q, w->w_k, w->w_v,
+                          w->w_o, w->conv_q, w->conv_k})
+      if (!aligned16(p)) return CCA_ERR_INVALID_ARG;
+    DecodePos pos{};
+    for (int b = 0; b < B; ++b) {
+      if (pos_host[b] < 0 || pos_host[b] >= h->cfg.max_seq_len) return CCA_ERR_CAPACITY;
+      pos.p[b] = pos_host[b];
+    }
+    const Dims& dm = h->dm;
+    hipStream_t s = (hipStream_t)stream;
+    DecodeLayout L = decode_layout(dm, B);
+    char* base = (char*)workspace;
+    float* qkv = (float*)(base + L.qkv);
+    void* qn = base + L.q;
+    void* on = base + L.o;
+
+    GemmArgs gd = gemm_down(dm, B, x_new, w, qkv);
+    CCA_TRY_HIP(timed(h, "decode_proj_down", s, [&] { return launch_gemm(gd, GemmLayout::NT, dm.bf16, true, s); }));
+
+    MixDecodeArgs md{};
+    md.dm = dm; md.B = B; md.pos = pos; md.qkv = qkv;
+    md.conv_q = w->conv_q; md.conv_k = w->conv_k; md.rope = h->rope;
+    md.state = state; md.k_cache = k_cache; md.v_cache = v_cache; md.q_out = qn;
+    CCA_TRY_HIP(timed(h, "decode_mix", s, [&] { return launch_mix_decode(md, s); }));
+
+    AttnArgs aa{};
+    aa.dm = dm; aa.B = B; aa.Sq = 1;
+    aa.q = qn; aa.k = k_cache; aa.v = v_cache;
+    aa.kv_bs = (long)dm.Hkv * dm.max_seq_len * dm.d; aa.kv_hs = (long)dm.max_seq_len * dm.d;
+    aa.o = on; aa.lse = nullptr; aa.decode = true; aa.pos = pos;
+    aa.part = (float*)(base + L.part); aa.nsplit = decode_nsplit(dm, B);
+    CCA_TRY_HIP(timed(h, "decode_attn", s, [&] { return launch_attn_decode(aa, s); }));
+
+    GemmArgs gu = gemm_nt(B, dm.E, dm.nq, on, dm.nq, w->w_o, dm.nq, y_new, dm.E);
+    CCA_TRY_HIP(timed(h, "decode_proj_up", s, [&] { return launch_gemm(gu, GemmLayout::NT, dm.bf16, false, s); }));
+    return CCA_OK;
+  } catch (const std::bad_alloc&) {
+    return CCA_ERR_OOM;
+  } catch (...) {
+    return CCA_ERR_HIP;
+  }
+}
+
+cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, const void* dy,
+                        const void* saved, int32_t B, int32_t S, const cca_grads* g,
+                        void* workspace, void* stream) {
+  try {
+    if (!h || !w || !x || !dy || !saved || !g || !workspace) return CCA_ERR_INVALID_ARG;
+    if (B < 1 || S < 1) return CCA_ERR_INVALID_ARG;
+    if (S > h->cfg.max_seq_len) return CCA_ERR_CAPACITY;
+    if (!g->dx || !g->dw_q || !g->dw_k || !g->dw_v || !g->dw_o || !g->dconv_q || !g->dconv_k)
+      return CCA_ERR_INVALID_ARG;
+    if (!w->w_q || !w->w_k || !w->w_v || !w->w_o || !w->conv_q || !w->conv_k)
+      return CCA_ERR_INVALID_ARG;
+    for (const void* p : {x, dy, saved, (const void*)workspace, (const void*)g->dx,
+                          (const void*)g->dw_q, (const void*)g->dw_k, (const void*)g->dw_v,
+                          (const void*)g->dw_o, (const void*)g->dconv_q, (const void*)g->dconv_k,
+                          w->w_q, w->w_k, w->w_v, w->w_o, w->conv_q, w->conv_k})
+      if (!aligned16(p)) return CCA_ERR_INVALID_ARG;
+    const Dims& dm = h->dm;
+    hipStream_t s = (hipStream_t)stream;
+    SavedLayout SL = saved_layout(dm, B, S);
+    BwdLayout L = bwd_layout(dm, B, S);
+    const char* sb = (const char*)saved;
+    char* wb = (char*)workspace;
+    const float* qkv = (const float*)(sb + SL.off[0]);
+    const void* qr = sb + SL.off[1];
+    const void* kr = sb + SL.off[2];
+    const void* vs = sb + SL.off[3];
+    const void* o = sb + SL.off[4];
+    const float* lse = (const float*)(sb + SL.off[5]);
+    const float* o32 = (const float*)(sb + SL.off[6]);
+    void* dO = wb + L.dO;
+    float* Dsum = (float*)(wb + L.Dsum);
+    float* dq = (float*)(wb + L.dq);
+    float* dk = (float*)(wb + L.dk);
+    float* dv = (float*)(wb + L.dv);
+    void* dqkv = wb + L.dqkv;
+    const int M = B * S;
+
+    // dO = dY W_o ; dW_o = dY^T O
+    GemmArgs g1 = gemm_nt(M, dm.nq, dm.E, dy, dm.E, w->w_o, dm.nq, dO, dm.nq);
+    CCA_TRY_HIP(timed(h, "bwd_proj_up_dx", s, [&] { return launch_gemm(g1, GemmLayout::NN, dm.bf16, false, s); }));
+    GemmArgs g2 = gemm_nt(dm.E, dm.nq, M, dy, dm.E, o, dm.nq, g->dw_o, dm.nq);
+    CCA_TRY_HIP(timed(h, "bwd_proj_up_dw", s, [&] { return launch_gemm(g2, GemmLayout::TN, dm.bf16, true, s); }));
+
+    AttnBwdArgs ab{};
+    ab.dm = dm; ab.B = B; ab.S = S;
+    ab.q = qr; ab.k = kr; ab.v = vs; ab.o32 = o32; ab.dO = dO; ab.lse = lse; ab.Dsum = Dsum;
+    ab.dq = dq; ab.dk = dk; ab.dv = dv;
+    CCA_TRY_HIP(timed(h, "bwd_attn", s, [&] { return launch_attn_bwd(ab, s); }));
+
+    MixBwdArgs mb{};
+    mb.dm = dm; mb.B = B; mb.S = S; mb.qkv = qkv;
+    mb.conv_q = w->conv_q; mb.conv_k = w->conv_k; mb.rope = h->rope;
+    mb.dq = dq; mb.dk = dk; mb.dv = dv; mb.dqkv = dqkv;
+    mb.dconv_part = (float*)(wb + L.part);
+    mb.dconv_q = (float*)g->dconv_q; mb.dconv_k = (float*)g->dconv_k;
+    mb.scratch = (float*)(wb + L.scratch);
+    CCA_TRY_HIP(timed(h, "bwd_mix", s, [&] { return launch_mix_bwd(mb, s); }));
+
+    // dx = dq~ W_q + dk~ W_k + dv~ W_v ; dW_* = d*~^T x
+    GemmArgs g3 = gemm_nt(M, dm.E, dm.nqkv, dqkv, dm.nqkv, w->w_q, dm.E, g->dx, dm.E);
+    g3.b_ptr[1] = w->w_k; g3.b_start[1] = dm.nq;
+    g3.b_ptr[2] = w->w_v; g3.b_start[2] = dm.nq + dm.nk;
+    g3.b_nseg = 3;
+    CCA_TRY_HIP(timed(h, "bwd_proj_down_dx", s, [&] { return launch_gemm(g3, GemmLayout::NN, dm.bf16, false, s); }));
+    GemmArgs g4 = gemm_nt(dm.nqkv, dm.E, M, dqkv, dm.nqkv, x, dm.E, g->dw_q, dm.E);
+    g4.c_ptr[1] = g->dw_k; g4.c_start[1] = dm.nq;
+    g4.c_ptr[2] = g->dw_v; g4.c_start[2] = dm.nq + dm.nk;
+    g4.c_nseg = 3;
+    CCA_TRY_HIP(timed(h, "bwd_proj_down_dw", s, [&] { return launch_gemm(g4, GemmLayout::TN, dm.bf16, true, s); }));
+    return CCA_OK;
+  } catch (const std::bad_alloc&) {
+    return CCA_ERR_OOM;
+  } catch (...) {
+    return CCA_ERR_HIP;
+  }
+}
+
+cca_status cca_profile_enable(cca_handle* h, int enable) {
+  if (!h) return CCA_ERR_INVALID_ARG;
+  for (auto& r : h->recs) { h->pool.push_back(r.start); h->pool.push_back(r.stop); }
+  h->recs.clear();
+  h->profiling = enable != 0;
+  return CCA_OK;
+}
+
+int cca_profile_read(cca_handle* h, cca_kernel_time* out, int max) {
+  if (!h) return -1;
+  std::vector<std::string> order;
+  std::map<std::string, std::pair<int, double>> acc;
+  for (auto& r : h->recs) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.stop) != hipSuccess) return -1;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return -1;
+    auto it = acc.find(r.name);
+    if (it == acc.end()) {
+      order.push_back(r.name);
+      acc[r.name] = {1, ms};
+    } else {
+      it->second.first += 1;
+      it->second.second += ms;
+    }
+  }
+  int n = 0;
+  for (auto& name : order) {
+    if (out && n < max) {
+      std::memset(out[n].name, 0, sizeof(out[n].name));
+      std::strncpy(out[n].name, name.c_str(), sizeof(out[n].name) - 1);
+      out[n].launches = acc[name].first;
+      out[n].total_ms = acc[name].second;
+    }
+    ++n;
+  }
+  return n;
+}
+
+}  // extern "C"

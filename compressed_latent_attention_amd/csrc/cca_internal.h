@@ -1,0 +1,169 @@
+// Internal declarations shared by the host sequencing code (api.cpp) and the
+// HIP kernels of the CCA / CCGQA layer.  gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cca {
+
+using bf16 = __bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxDecodeBatch = 256;
+constexpr int kMaxConv = 4;
+constexpr int kMaxGroup = 8;
+constexpr uint32_t kQkPre = 1u, kQkPost = 2u, kRope = 4u, kVShift = 8u;
+
+// Per-layer sizes, derived once from the config and passed to kernels by value.
+struct Dims {
+  int E, Hq, Hkv, d, G, kq, kk, sv;
+  int nq, nk, nqkv;         // Hq*d, Hkv*d, (Hq+2*Hkv)*d
+  int state_w;              // elements of rolling state per sequence
+  int max_seq_len;
+  uint32_t flags;
+  bool bf16;
+};
+
+struct DecodePos {
+  int32_t p[kMaxDecodeBatch];
+};
+
+// ------------------------------------------------------------------ GEMM
+// C(m, n) = sum_k A(m, k) * B(k, n), fp32 accumulation.
+//   A(m, k) = a[m*lda + k] when a_kc (K-contiguous) else a[k*lda + m].
+//   B(k, n) = b[n*ldb + k] when b_kc else b[k*ldb + n].  B's storage rows
+//   (n when b_kc, k otherwise) may be split over up to 3 buffers: storage row
+//   r lives in segment s = the last with b_start[s] <= r, at
+//   b_ptr[s] + (r - b_start[s]) * ldb.
+//   C(m, n) = c_ptr[s][(m - c_start[s]) * ldc + n], segments along m.
+struct GemmArgs {
+  int M, N, K;
+  const void* a;
+  long lda;
+  const void* b_ptr[3];
+  int b_start[3];
+  int b_nseg;
+  long ldb;
+  void* c_ptr[3];
+  int c_start[3];
+  int c_nseg;
+  long ldc;
+};
+
+enum class GemmLayout { NT, NN, TN };   // (a_kc, b_kc) = (1,1), (1,0), (0,0)
+
+// in_bf16: A and B are bf16 (else fp32); out_f32: C is fp32 (else same as inputs).
+hipError_t launch_gemm(const GemmArgs& g, GemmLayout layout, bool in_bf16, bool out_f32,
+                       hipStream_t s);
+
+// ------------------------------------------------------------------ mix
+// Causal conv + QK-mean + value shift + RoPE over a prefill.
+//   qkv [B*S, nqkv] (q~ | k~ | v~); rope [max_seq_len, d/2] float2 (cos, sin).
+//   Outputs (row stride in tokens given by *_ld, batch stride by *_bs elems):
+//   q_out [B, Hq, S, d]; k_out, v_out [B, Hkv, ld, d].  k2/v2 optional second
+//   destination (the cache) with its own row capacity.
+struct MixArgs {
+  Dims dm;
+  int B, S;
+  const float* qkv;
+  const void* conv_q;
+  const void* conv_k;
+  const float2* rope;
+  void* q_out;
+  void* k_out;
+  void* v_out;
+  void* k_out2;
+  void* v_out2;
+  int cap2;                 // row capacity of k_out2 / v_out2
+};
+hipError_t launch_mix_fwd(const MixArgs& a, hipStream_t s);
+
+// Writes the rolling state after the last token of each sequence.
+hipError_t launch_write_state(const Dims& dm, int B, int S, const float* qkv, void* state,
+                              hipStream_t s);
+
+// Decode: one token per sequence; reads/updates state, writes the cache row
+// pos[b] and q_out [B, Hq, d].
+struct MixDecodeArgs {
+  Dims dm;
+  int B;
+  DecodePos pos;
+  const float* qkv;         // [B, nqkv] fp32
+  const void* conv_q;
+  const void* conv_k;
+  const float2* rope;
+  void* state;              // [B, state_w], updated in place
+  void* k_cache;            // [B, Hkv, max_seq_len, d]
+  void* v_cache;
+  void* q_out;              // [B, Hq, d]
+};
+hipError_t launch_mix_decode(const MixDecodeArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+// Causal attention.  Query row t of sequence b sits at position
+// (decode ? pos[b] : t) and sees keys 0..position.
+//   q [B, Hq, Sq, d]; k, v: element (b, g, j, c) at k[b*kv_bs + g*kv_hs + j*d + c];
+//   o: token-major [B, Sq, Hq*d]; lse [B, Hq, Sq] fp32 (nullable).
+struct AttnArgs {
+  Dims dm;
+  int B, Sq;
+  const void* q;
+  const void* k;
+  const void* v;
+  long kv_bs, kv_hs;
+  void* o;
+  float* o32;               // optional fp32 copy of o (same layout), nullable
+  float* lse;
+  bool decode;
+  DecodePos pos;
+  // split-key partials for decode (fp32 workspace), see launch_attn_decode
+  float* part;
+  int nsplit;
+};
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);
+int decode_nsplit(const Dims& dm, int B);
+size_t decode_part_floats(const Dims& dm, int B);
+
+// ------------------------------------------------------------------ backward
+struct AttnBwdArgs {
+  Dims dm;
+  int B, S;
+  const void* q;     // Q'' [B,Hq,S,d]
+  const void* k;     // K'' [B,Hkv,S,d]
+  const void* v;     // V'  [B,Hkv,S,d]
+  const float* o32;  // O   [B,S,Hq*d] fp32 (saved by the forward)
+  const void* dO;    // dO  [B,S,Hq*d]
+  const float* lse;  // [B,Hq,S]
+  float* Dsum;       // [B,Hq,S] workspace
+  float* dq;         // dQ'' [B,Hq,S,d] fp32
+  float* dk;         // dK'' [B,Hkv,S,d] fp32
+  float* dv;         // dV'  [B,Hkv,S,d] fp32
+};
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
+
+struct MixBwdArgs {
+  Dims dm;
+  int B, S;
+  const float* qkv;      // saved q~ | k~ | v~ [B*S, nqkv] fp32
+  const void* conv_q;
+  const void* conv_k;
+  const float2* rope;
+  const float* dq;       // dQ'' [B,Hq,S,d] fp32
+  const float* dk;       // dK'' fp32
+  const float* dv;       // dV'  fp32
+  void* dqkv;            // out: dq~ | dk~ | dv~ [B*S, nqkv]
+  float* dconv_part;     // [nblk, Hq*kq*d*d + Hkv*kk*d*d] partial tap grads
+  float* dconv_q;        // final fp32 [Hq,kq,d,d]
+  float* dconv_k;        // final fp32 [Hkv,kk,d,d]
+  float* scratch;        // fp32 workspace for dq^ / dk^ [B*S, nq + nk]
+};
+hipError_t launch_mix_bwd(const MixBwdArgs& a, hipStream_t s);
+size_t mix_bwd_part_floats(const Dims& dm, int B, int S);
+size_t mix_bwd_scratch_floats(const Dims& dm, int B, int S);
+
+}  // namespace cca

@@ -1,0 +1,269 @@
+// cca_mix: the operations CCA applies to the compressed latents before
+// attention (CCA-es §2.B "Innovaciones Clave"; CCA-fr §2 "Innovations Clés"):
+//   1. causal grouped convolution of q~ and k~ along the sequence, mixing the
+//      channels of each head (k taps of d x d, tap j on lag j),
+//   2. QK-mean: adds the mean of Q and K before and after the convolution,
+//   3. value shift: the last s_v channels of each KV head come from token t-1,
+//   4. RoPE in the latent (CCA-es §3 item 2), rotate-half, angles from a
+//      float64-built cos/sin table.
+// Everything one KV group needs (its G query heads and its K head) is handled
+// by one work-group, so QK-mean and RoPE need no cross-group traffic.
+//
+// This file holds the generic kernels (any even d <= 128, fp32 or bf16
+// storage, fp32 arithmetic) and the decode-step mix; the MFMA prefill mix for
+// bf16 lives in mix_mfma.hip.
+#include "cca_internal.h"
+
+namespace cca {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float ldf(const void* p, long i) {
+  return (float)reinterpret_cast<const T*>(p)[i];
+}
+template <typename T>
+__device__ __forceinline__ void stf(void* p, long i, float v) {
+  reinterpret_cast<T*>(p)[i] = (T)v;
+}
+
+constexpr int TT = 4;   // tokens per work-group in the generic prefill mix
+
+// QK-mean for one channel of one token, from the pre-conv (u) and post-conv
+// (cv) values of the group's heads laid out [head][d] (q heads 0..G-1, then
+// the k head at index G).  hh < G gives q'_hh, hh == G gives k'.
+__device__ __forceinline__ float qk_mixed(const float* u, const float* cv, int G, int d, int hh,
+                                          int ch, uint32_t flags) {
+  const float a = (flags & kQkPre) ? 0.5f : 0.0f;
+  const float b = (flags & kQkPost) ? 0.5f : 0.0f;
+  const float pre_k = u[G * d + ch], post_k = cv[G * d + ch];
+  if (hh < G) {
+    const float pre_q = u[hh * d + ch], post_q = cv[hh * d + ch];
+    return post_q + a * (pre_q + pre_k) + b * (post_q + post_k);
+  }
+  float mpre = 0.0f, mpost = 0.0f;
+  for (int i = 0; i < G; ++i) {
+    mpre += u[i * d + ch];
+    mpost += cv[i * d + ch];
+  }
+  mpre /= (float)G;
+  mpost /= (float)G;
+  return post_k + a * (mpre + pre_k) + b * (mpost + post_k);
+}
+
+__device__ __forceinline__ float rope_rot(float x, float partner, int c, int half, float2 cs) {
+  // (lo, hi) -> (lo cos - hi sin, hi cos + lo sin)
+  return c < half ? x * cs.x - partner * cs.y : x * cs.x + partner * cs.y;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void mix_fwd_simple(MixArgs a) {
+  extern __shared__ float smem[];
+  const Dims& dm = a.dm;
+  const int d = dm.d, G = dm.G, NH = G + 1;
+  const int KM = max(dm.kq, dm.kk);
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int t0 = blockIdx.x * TT;
+  float* u = smem;                                  // [TT+KM-1][NH][d]
+  float* cv = smem + (TT + KM - 1) * NH * d;        // [TT][NH][d]
+  const int rows = TT + KM - 1;
+  for (int i = threadIdx.x; i < rows * NH * d; i += blockDim.x) {
+    const int r = i / (NH * d), hh = (i / d) % NH, c = i % d;
+    const int t = t0 - (KM - 1) + r;
+    const int col = hh < G ? (g * G + hh) * d : dm.nq + g * d;
+    u[i] = (t >= 0 && t < a.S) ? a.qkv[(long)(b * a.S + t) * dm.nqkv + col + c] : 0.0f;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < TT * NH * d; i += blockDim.x) {
+    const int tt = i / (NH * d), hh = (i / d) % NH, c = i % d;
+    const bool isq = hh < G;
+    const int k = isq ? dm.kq : dm.kk;
+    const long tap0 = isq ? (long)(g * G + hh) * dm.kq * d * d : (long)g * dm.kk * d * d;
+    const void* taps = isq ? a.conv_q : a.conv_k;
+    float s = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const float* src = u + ((tt + KM - 1 - j) * NH + hh) * d;
+      const long base = tap0 + ((long)j * d + c) * d;
+      for (int e = 0; e < d; ++e) s += ldf<T>(taps, base + e) * src[e];
+    }
+    cv[i] = s;
+  }
+  __syncthreads();
+  const int half = d / 2;
+  for (int i = threadIdx.x; i < TT * d; i += blockDim.x) {
+    const int tt = i / d, c = i % d;
+    const int t = t0 + tt;
+    if (t >= a.S) continue;
+    const float* ut = u + (tt + KM - 1) * NH * d;
+    const float* ct = cv + tt * NH * d;
+    const int cp = c < half ? c + half : c - half;
+    const float2 cs = (dm.flags & kRope) ? a.rope[(long)t * half + (c % half)] : make_float2(1.f, 0.f);
+    for (int hh = 0; hh < NH; ++hh) {
+      const float x = qk_mixed(ut, ct, G, d, hh, c, dm.flags);
+      const float xp = qk_mixed(ut, ct, G, d, hh, cp, dm.flags);
+      const float r = rope_rot(x, xp, c, half, cs);
+      if (hh < G) {
+        stf<T>(a.q_out, ((long)(b * dm.Hq + g * G + hh) * a.S + t) * d + c, r);
+      } else {
+        stf<T>(a.k_out, ((long)(b * dm.Hkv + g) * a.S + t) * d + c, r);
+        if (a.k_out2) stf<T>(a.k_out2, ((long)(b * dm.Hkv + g) * a.cap2 + t) * d + c, r);
+      }
+    }
+    const bool shifted = (dm.flags & kVShift) && c >= d - dm.sv;
+    const long vcol = dm.nq + dm.nk + g * d + c;
+    float v;
+    if (shifted)
+      v = t > 0 ? a.qkv[(long)(b * a.S + t - 1) * dm.nqkv + vcol] : 0.0f;
+    else
+      v = a.qkv[(long)(b * a.S + t) * dm.nqkv + vcol];
+    stf<T>(a.v_out, ((long)(b * dm.Hkv + g) * a.S + t) * d + c, v);
+    if (a.v_out2) stf<T>(a.v_out2, ((long)(b * dm.Hkv + g) * a.cap2 + t) * d + c, v);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void write_state_kernel(Dims dm, int S, const float* qkv,
+                                                          void* state) {
+  const int b = blockIdx.x;
+  const int nqpart = (dm.kq - 1) * dm.nq, nkpart = (dm.kk - 1) * dm.nk;
+  for (int i = threadIdx.x; i < dm.state_w; i += blockDim.x) {
+    int lag, col;
+    if (i < nqpart) {
+      lag = i / dm.nq + 1;
+      col = i % dm.nq;
+    } else if (i < nqpart + nkpart) {
+      lag = (i - nqpart) / dm.nk + 1;
+      col = dm.nq + (i - nqpart) % dm.nk;
+    } else {
+      lag = 1;
+      col = dm.nq + dm.nk + (i - nqpart - nkpart);
+    }
+    const int t = S - lag;
+    const float v = t >= 0 ? qkv[(long)(b * S + t) * dm.nqkv + col] : 0.0f;
+    stf<T>(state, (long)b * dm.state_w + i, v);
+  }
+}
+
+// Decode-step mix: one token per sequence at position pos[b]; the lags of
+// the convolution and the previous value come from the rolling state, which
+// is advanced in place.  One work-group per (KV group, sequence).
+template <typename T>
+__global__ __launch_bounds__(256) void mix_decode_kernel(MixDecodeArgs a) {
+  extern __shared__ float smem[];
+  const Dims& dm = a.dm;
+  const int d = dm.d, G = dm.G, NH = G + 1;
+  const int KM = max(dm.kq, dm.kk);
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int p = a.pos.p[b];
+  float* u = smem;                       // [KM][NH][d]  lag j = row j
+  float* cv = u + KM * NH * d;           // [NH][d]
+  float* vprev = cv + NH * d;            // [d]
+  const long srow = (long)b * dm.state_w;
+  const int nqpart = (dm.kq - 1) * dm.nq, nkpart = (dm.kk - 1) * dm.nk;
+  for (int i = threadIdx.x; i < KM * NH * d; i += blockDim.x) {
+    const int j = i / (NH * d), hh = (i / d) % NH, c = i % d;
+    const bool isq = hh < G;
+    float v = 0.0f;
+    if (j == 0) {
+      const int col = isq ? (g * G + hh) * d : dm.nq + g * d;
+      v = a.qkv[(long)b * dm.nqkv + col + c];
+    } else if (isq && j < dm.kq) {
+      v = ldf<T>(a.state, srow + (long)(j - 1) * dm.nq + (g * G + hh) * d + c);
+    } else if (!isq && j < dm.kk) {
+      v = ldf<T>(a.state, srow + nqpart + (long)(j - 1) * dm.nk + g * d + c);
+    }
+    u[i] = v;
+  }
+  for (int c = threadIdx.x; c < d; c += blockDim.x)
+    vprev[c] = ldf<T>(a.state, srow + nqpart + nkpart + g * d + c);
+  __syncthreads();
+  for (int i = threadIdx.x; i < NH * d; i += blockDim.x) {
+    const int hh = i / d, c = i % d;
+    const bool isq = hh < G;
+    const int k = isq ? dm.kq : dm.kk;
+    const long tap0 = isq ? (long)(g * G + hh) * dm.kq * d * d : (long)g * dm.kk * d * d;
+    const void* taps = isq ? a.conv_q : a.conv_k;
+    float s = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const float* src = u + (j * NH + hh) * d;
+      const long base = tap0 + ((long)j * d + c) * d;
+      for (int e = 0; e < d; ++e) s += ldf<T>(taps, base + e) * src[e];
+    }
+    cv[i] = s;
+  }
+  __syncthreads();
+  const int half = d / 2;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    const int cp = c < half ? c + half : c - half;
+    const float2 cs = (dm.flags & kRope) ? a.rope[(long)p * half + (c % half)] : make_float2(1.f, 0.f);
+    for (int hh = 0; hh < NH; ++hh) {
+      const float x = qk_mixed(u, cv, G, d, hh, c, dm.flags);
+      const float xp = qk_mixed(u, cv, G, d, hh, cp, dm.flags);
+      const float r = rope_rot(x, xp, c, half, cs);
+      if (hh < G)
+        stf<T>(a.q_out, (long)(b * dm.Hq + g * G + hh) * d + c, r);
+      else
+        stf<T>(a.k_cache, ((long)(b * dm.Hkv + g) * dm.max_seq_len + p) * d + c, r);
+    }
+    const bool shifted = (dm.flags & kVShift) && c >= d - dm.sv;
+    const float vnew = a.qkv[(long)b * dm.nqkv + dm.nq + dm.nk + g * d + c];
+    stf<T>(a.v_cache, ((long)(b * dm.Hkv + g) * dm.max_seq_len + p) * d + c,
+           shifted ? vprev[c] : vnew);
+  }
+  // advance the state: the new token becomes lag 1 (every read above is done)
+  for (int i = threadIdx.x; i < NH * d; i += blockDim.x) {
+    const int hh = i / d, c = i % d;
+    const bool isq = hh < G;
+    const int k = isq ? dm.kq : dm.kk;
+    for (int j = 1; j < k; ++j) {
+      const float v = u[((j - 1) * NH + hh) * d + c];
+      if (isq)
+        stf<T>(a.state, srow + (long)(j - 1) * dm.nq + (g * G + hh) * d + c, v);
+      else
+        stf<T>(a.state, srow + nqpart + (long)(j - 1) * dm.nk + g * d + c, v);
+    }
+  }
+  for (int c = threadIdx.x; c < d; c += blockDim.x)
+    stf<T>(a.state, srow + nqpart + nkpart + g * d + c,
+           a.qkv[(long)b * dm.nqkv + dm.nq + dm.nk + g * d + c]);
+}
+
+}  // namespace
+
+hipError_t launch_mix_fwd_mfma(const MixArgs& a, hipStream_t s);   // mix_mfma.hip
+bool mix_fwd_mfma_supported(const Dims& dm);
+
+hipError_t launch_mix_fwd(const MixArgs& a, hipStream_t s) {
+  const Dims& dm = a.dm;
+  if (dm.bf16 && mix_fwd_mfma_supported(dm)) return launch_mix_fwd_mfma(a, s);
+  const int KM = max(dm.kq, dm.kk);
+  const size_t lds = (size_t)((TT + KM - 1) + TT) * (dm.G + 1) * dm.d * sizeof(float);
+  dim3 grid((a.S + TT - 1) / TT, dm.Hkv, a.B);
+  if (dm.bf16)
+    hipLaunchKernelGGL(mix_fwd_simple<bf16>, grid, dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL(mix_fwd_simple<float>, grid, dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_state(const Dims& dm, int B, int S, const float* qkv, void* state,
+                              hipStream_t s) {
+  if (dm.bf16)
+    hipLaunchKernelGGL(write_state_kernel<bf16>, dim3(B), dim3(256), 0, s, dm, S, qkv, state);
+  else
+    hipLaunchKernelGGL(write_state_kernel<float>, dim3(B), dim3(256), 0, s, dm, S, qkv, state);
+  return hipGetLastError();
+}
+
+hipError_t launch_mix_decode(const MixDecodeArgs& a, hipStream_t s) {
+  const Dims& dm = a.dm;
+  const int KM = max(dm.kq, dm.kk);
+  const size_t lds = (size_t)((KM + 1) * (dm.G + 1) * dm.d + dm.d) * sizeof(float);
+  dim3 grid(dm.Hkv, a.B);
+  if (dm.bf16)
+    hipLaunchKernelGGL(mix_decode_kernel<bf16>, grid, dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL(mix_decode_kernel<float>, grid, dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace cca

@@ -1,0 +1,177 @@
+// cca_bwd, latent-mixing part: adjoints of RoPE, QK-mean, the causal grouped
+// convolution and the value shift (the operations of CCA-es §2.B and §3
+// item 2, taken in reverse order), plus the conv-tap gradients.
+//
+//   RoPE:     dq' = R(-phi) dQ''                 (rotation is orthogonal)
+//   QK-mean:  dq^_h = (1 + b/2) dq'_h + b/(2G) dk'_g
+//             dk^_g = (1 + b/2) dk'_g + b/2 sum_h dq'_h
+//             dq~_h += a/2 dq'_h + a/(2G) dk'_g,  dk~_g += a/2 sum_h dq'_h + a/2 dk'_g
+//   conv:     dq~[t] += sum_j A_j^T dq^[t + j],   dA_j = sum_t dq^[t] q~[t - j]^T
+//   shift:    dv~[t, c] = mask(c) ? dV'[t + 1, c] (0 at the last token) : dV'[t, c]
+// with a = [QK-mean pre], b = [QK-mean post] halves folded in as in the forward.
+// Tap gradients are summed per block of tokens and then over blocks in a
+// fixed order (deterministic).
+#include "cca_internal.h"
+
+namespace cca {
+namespace {
+
+constexpr int TB = 256;        // tokens per tap-gradient partial block
+
+template <typename T>
+__device__ __forceinline__ float ldf(const void* p, long i) {
+  return (float)reinterpret_cast<const T*>(p)[i];
+}
+template <typename T>
+__device__ __forceinline__ void stf(void* p, long i, float v) {
+  reinterpret_cast<T*>(p)[i] = (T)v;
+}
+
+// scratch row layout per token: [dq^ (nq) | dk^ (nk) | dq~ direct (nq) | dk~ direct (nk)]
+template <typename T>
+__global__ __launch_bounds__(256) void mix_bwd_pointwise(MixBwdArgs a) {
+  __shared__ float dqp[kMaxGroup + 1][128];   // dq'_h (h < G), dk'_g at [G]
+  const Dims& dm = a.dm;
+  const int d = dm.d, G = dm.G, half = d / 2;
+  const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const float2 one = make_float2(1.f, 0.f);
+  for (int i = threadIdx.x; i < (G + 1) * d; i += blockDim.x) {
+    const int hh = i / d, c = i % d;
+    const float* src = hh < G ? a.dq : a.dk;
+    const long row = hh < G ? ((long)(b * dm.Hq + g * G + hh) * a.S + t) * d
+                            : ((long)(b * dm.Hkv + g) * a.S + t) * d;
+    const int cp = c < half ? c + half : c - half;
+    const float x = src[row + c], xp = src[row + cp];
+    const float2 cs = (dm.flags & kRope) ? a.rope[(long)t * half + (c % half)] : one;
+    // inverse rotation: (lo, hi) -> (lo cos + hi sin, hi cos - lo sin)
+    dqp[hh][c] = c < half ? x * cs.x + xp * cs.y : x * cs.x - xp * cs.y;
+  }
+  __syncthreads();
+  const float A = (dm.flags & kQkPre) ? 0.5f : 0.0f;
+  const float Bc = (dm.flags & kQkPost) ? 0.5f : 0.0f;
+  const int W = 2 * (dm.nq + dm.nk);
+  float* srow = a.scratch + (long)(b * a.S + t) * W;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    float sum_q = 0.0f;
+    for (int i = 0; i < G; ++i) sum_q += dqp[i][c];
+    const float dkp = dqp[G][c];
+    for (int i = 0; i < G; ++i) {
+      const int h = g * G + i;
+      srow[h * d + c] = (1.0f + Bc) * dqp[i][c] + (Bc / G) * dkp;
+      srow[dm.nq + dm.nk + h * d + c] = A * dqp[i][c] + (A / G) * dkp;
+    }
+    srow[dm.nq + g * d + c] = (1.0f + Bc) * dkp + Bc * sum_q;
+    srow[2 * dm.nq + dm.nk + g * d + c] = A * sum_q + A * dkp;
+    // value shift adjoint
+    const bool shifted = (dm.flags & kVShift) && c >= d - dm.sv;
+    const long vrow = (long)(b * dm.Hkv + g) * a.S;
+    float dvv;
+    if (shifted)
+      dvv = t + 1 < a.S ? a.dv[(vrow + t + 1) * d + c] : 0.0f;
+    else
+      dvv = a.dv[(vrow + t) * d + c];
+    stf<T>(a.dqkv, (long)(b * a.S + t) * dm.nqkv + dm.nq + dm.nk + g * d + c, dvv);
+  }
+}
+
+// dq~ = direct + conv adjoint, one work-group per (token, head, sequence) over
+// all Hq + Hkv heads.
+template <typename T>
+__global__ __launch_bounds__(128) void mix_bwd_conv_input(MixBwdArgs a) {
+  const Dims& dm = a.dm;
+  const int d = dm.d;
+  const int t = blockIdx.x, hh = blockIdx.y, b = blockIdx.z;
+  const bool isq = hh < dm.Hq;
+  const int h = isq ? hh : hh - dm.Hq;
+  const int k = isq ? dm.kq : dm.kk;
+  const void* taps = isq ? a.conv_q : a.conv_k;
+  const long tap0 = (long)h * k * d * d;
+  const int W = 2 * (dm.nq + dm.nk);
+  const int col = isq ? h * d : dm.nq + h * d;              // dq^ / dk^ column in scratch
+  const int dcol = dm.nq + dm.nk + col;                      // direct term column
+  for (int c2 = threadIdx.x; c2 < d; c2 += blockDim.x) {
+    float s = a.scratch[(long)(b * a.S + t) * W + dcol + c2];
+    for (int j = 0; j < k; ++j) {
+      if (t + j >= a.S) break;
+      const float* g = a.scratch + (long)(b * a.S + t + j) * W + col;
+      for (int c = 0; c < d; ++c) s += ldf<T>(taps, tap0 + ((long)j * d + c) * d + c2) * g[c];
+    }
+    const int ocol = isq ? h * d : dm.nq + h * d;
+    stf<T>(a.dqkv, (long)(b * a.S + t) * dm.nqkv + ocol + c2, s);
+  }
+}
+
+// Partial tap gradients over one block of TB tokens for one head:
+// part[blk][head taps] = sum_{t in blk} dq^[t][c] * q~[t - j][c2].
+template <typename T>
+__global__ __launch_bounds__(256) void mix_bwd_tap_partial(MixBwdArgs a) {
+  const Dims& dm = a.dm;
+  const int d = dm.d;
+  const int blk = blockIdx.x, hh = blockIdx.y;
+  const int nblk_s = (a.S + TB - 1) / TB;
+  const int b = blk / nblk_s, t0 = (blk % nblk_s) * TB;
+  const bool isq = hh < dm.Hq;
+  const int h = isq ? hh : hh - dm.Hq;
+  const int k = isq ? dm.kq : dm.kk;
+  const int W = 2 * (dm.nq + dm.nk);
+  const int gcol = isq ? h * d : dm.nq + h * d;
+  const int xcol = isq ? h * d : dm.nq + h * d;               // q~ / k~ in qkv
+  const long per_blk = (long)dm.Hq * dm.kq * d * d + (long)dm.Hkv * dm.kk * d * d;
+  const long off = isq ? (long)h * dm.kq * d * d : (long)dm.Hq * dm.kq * d * d + (long)h * dm.kk * d * d;
+  float* out = a.dconv_part + blk * per_blk + off;
+  const int t1 = min(a.S, t0 + TB);
+  for (int e = threadIdx.x; e < k * d * d; e += blockDim.x) {
+    const int j = e / (d * d), c = (e / d) % d, c2 = e % d;
+    float s = 0.0f;
+    for (int t = max(t0, j); t < t1; ++t)
+      s += a.scratch[(long)(b * a.S + t) * W + gcol + c] *
+           a.qkv[(long)(b * a.S + t - j) * dm.nqkv + xcol + c2];
+    out[e] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void mix_bwd_tap_reduce(MixBwdArgs a, int nblk) {
+  const Dims& dm = a.dm;
+  const long nq = (long)dm.Hq * dm.kq * dm.d * dm.d;
+  const long per_blk = nq + (long)dm.Hkv * dm.kk * dm.d * dm.d;
+  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= per_blk) return;
+  float s = 0.0f;
+  for (int i = 0; i < nblk; ++i) s += a.dconv_part[(long)i * per_blk + e];
+  if (e < nq)
+    a.dconv_q[e] = s;
+  else
+    a.dconv_k[e - nq] = s;
+}
+
+int tap_blocks(int B, int S) { return B * ((S + TB - 1) / TB); }
+
+}  // namespace
+
+size_t mix_bwd_part_floats(const Dims& dm, int B, int S) {
+  const long per_blk = (long)dm.Hq * dm.kq * dm.d * dm.d + (long)dm.Hkv * dm.kk * dm.d * dm.d;
+  return (size_t)tap_blocks(B, S) * per_blk;
+}
+
+size_t mix_bwd_scratch_floats(const Dims& dm, int B, int S) {
+  return (size_t)B * S * 2 * (dm.nq + dm.nk);
+}
+
+hipError_t launch_mix_bwd(const MixBwdArgs& a, hipStream_t s) {
+  const Dims& dm = a.dm;
+  const int nblk = tap_blocks(a.B, a.S);
+  const long per_blk = (long)dm.Hq * dm.kq * dm.d * dm.d + (long)dm.Hkv * dm.kk * dm.d * dm.d;
+  if (dm.bf16) {
+    hipLaunchKernelGGL(mix_bwd_pointwise<bf16>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mix_bwd_conv_input<bf16>, dim3(a.S, dm.Hq + dm.Hkv, a.B), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(mix_bwd_tap_partial<bf16>, dim3(nblk, dm.Hq + dm.Hkv), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(mix_bwd_pointwise<float>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mix_bwd_conv_input<float>, dim3(a.S, dm.Hq + dm.Hkv, a.B), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(mix_bwd_tap_partial<float>, dim3(nblk, dm.Hq + dm.Hkv), dim3(256), 0, s, a);
+  }
+  hipLaunchKernelGGL(mix_bwd_tap_reduce, dim3((per_blk + 255) / 256), dim3(256), 0, s, a, nblk);
+  return hipGetLastError();
+}
+
+}  // namespace cca

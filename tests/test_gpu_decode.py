@@ -1,0 +1,117 @@
+"""GPU parity of the decode step against the float64 oracle.
+
+* decode == prefill: a GPU prefill of S tokens (writing the cache and the
+  rolling state) followed by GPU decode steps reproduces the oracle's prefill
+  rows S, S+1, and the cache rows and state the oracle leaves;
+* the 32-sequence CCGQA decode over a seeded 32768-token cache, every output
+  element against the oracle's decode step.
+"""
+import numpy as np
+import pytest
+
+from compressed_latent_attention_amd.synthetic import (WORKLOADS, Workload, make_inputs,
+                                                       round_bf16)
+from oracle import cca as O
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from gpu_helpers import (TOL, dev, dev_weights, host, layer_of, params_of, rel,  # noqa: E402
+                         run_prefill, say, spec_of)
+
+CASES = [
+    Workload("f32_decode", B=2, S=29, E=128, C=2, Hq=4, Hkv=2, dtype="f32", seed=51),
+    Workload("f32_decode_k3", B=1, S=5, E=64, C=1, Hq=2, Hkv=2, kq=3, kk=1, dtype="f32", seed=52),
+    Workload("bf16_decode", B=3, S=150, E=512, C=1, Hq=4, Hkv=2, seed=53),
+    Workload("bf16_decode_g4", B=2, S=64, E=512, C=1, Hq=4, Hkv=1, kq=3, kk=2, seed=54),
+    Workload("bf16_decode_first", B=2, S=1, E=512, C=1, Hq=4, Hkv=2, seed=55),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=[c.name for c in CASES])
+def test_decode_continues_prefill(w):
+    say(f"[decode] {w}")
+    steps = 2
+    full = w.replace(S=w.S + steps)
+    inp = make_inputs(full)
+    spec = spec_of(w)
+    y_ref, sv = O.forward(inp["x"], params_of(inp), spec, return_saved=True)
+    pre = dict(inp)
+    pre["x"] = inp["x"][:, :w.S]
+    r = run_prefill(w.replace(max_seq_len=w.S + 8), pre, with_saved=False, with_cache=True)
+    layer, kc, vc, st, wts = r["layer"], r["k_cache"], r["v_cache"], r["state"], r["w"]
+    tol = TOL[w.dtype]
+    for i in range(steps):
+        p = w.S + i
+        xn = dev(inp["x"][:, p], w)
+        y = layer.decode_step(wts, xn, [p] * w.B, kc, vc, st)
+        torch.cuda.synchronize()
+        e_y = rel(host(y), y_ref[:, p])
+        e_k = rel(host(kc[:, :, p]), np.stack([s[p] for s in sv["k_rope"]]))
+        e_v = rel(host(vc[:, :, p]), np.stack([s[p] for s in sv["v_shift"]]))
+        say(f"  step {i}: y {e_y:.2e} k {e_k:.2e} v {e_v:.2e}")
+        assert e_y <= tol and e_k <= tol and e_v <= tol
+    # the state after the last step is the state a prefill of S + steps leaves
+    e_s = rel(host(st), np.stack(sv["state"]))
+    assert e_s <= tol, e_s
+
+
+def test_prefill_writes_cache_and_state():
+    w = Workload("bf16_cache", B=2, S=77, E=512, C=1, Hq=4, Hkv=2, seed=56, max_seq_len=100)
+    inp = make_inputs(w)
+    r = run_prefill(w, inp, with_saved=False, with_cache=True)
+    _, sv = O.forward(inp["x"], params_of(inp), spec_of(w), return_saved=True)
+    kc = host(r["k_cache"])
+    assert rel(kc[:, :, :w.S], np.stack(sv["k_rope"]).transpose(0, 2, 1, 3)) <= TOL["bf16"]
+    assert rel(host(r["v_cache"])[:, :, :w.S],
+               np.stack(sv["v_shift"]).transpose(0, 2, 1, 3)) <= TOL["bf16"]
+    assert np.all(kc[:, :, w.S:] == 0)           # rows past S are untouched
+    assert rel(host(r["state"]), np.stack(sv["state"])) <= TOL["bf16"]
+
+
+def test_decode_ccgqa_32k_full_size():
+    """32 sequences, each with a 32768-token seeded cache, one new token each:
+    y, the written cache row and the advanced state, every element."""
+    w = WORKLOADS["ccgqa_decode_32k"]
+    say(f"[decode32k] {w}")
+    inp = make_inputs(w)
+    layer = layer_of(w)
+    wts = dev_weights(inp, w)
+    kc = dev(inp["k_cache"], w)
+    vc = dev(inp["v_cache"], w)
+    st = dev(inp["state"], w)
+    xn = dev(inp["x_new"], w)
+    y = layer.decode_step(wts, xn, inp["pos"].tolist(), kc, vc, st)
+    torch.cuda.synchronize()
+    y_ref, kc_ref, vc_ref, st_ref = O.decode_step(inp["x_new"], params_of(inp), spec_of(w),
+                                                  inp["k_cache"], inp["v_cache"], inp["state"],
+                                                  inp["pos"])
+    p = w.S
+    errs = {"y": rel(host(y), y_ref), "k": rel(host(kc[:, :, p]), kc_ref[:, :, p]),
+            "v": rel(host(vc[:, :, p]), vc_ref[:, :, p]), "state": rel(host(st), st_ref)}
+    say(f"  rel errors {errs}")
+    for k, e in errs.items():
+        assert e <= TOL["bf16"], (k, e)
+    # rows before p are untouched
+    assert torch.equal(kc[:, :, :p], dev(inp["k_cache"][:, :, :p], w))
+
+
+def test_decode_rejects_positions_beyond_capacity():
+    import compressed_latent_attention_amd as cca
+    w = Workload("bf16_cap", B=1, S=4, E=512, C=1, Hq=4, Hkv=2, seed=57, max_seq_len=8)
+    layer = layer_of(w)
+    inp = make_inputs(w.replace(kind="prefill"))
+    wts = dev_weights(inp, w)
+    kc = torch.zeros((1, 2, 8, 128), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    st = torch.zeros((1, layer.state_width()), dtype=torch.bfloat16, device="cuda")
+    xn = torch.zeros((1, 512), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(cca.CCAError) as ei:
+        layer.decode_step(wts, xn, [8], kc, vc, st)
+    assert ei.value.status == cca.CCA_ERR_CAPACITY
+    with pytest.raises(cca.CCAError):
+        layer.decode_step(wts, xn, [-1], kc, vc, st)
+    assert torch.count_nonzero(kc) == 0
