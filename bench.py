@@ -1,0 +1,181 @@
+"""Benchmark of the CCA / CCGQA layer on one MI355X.
+
+Headline: CCGQA prefill (B=1, S=16384, E=2048, 4 query heads x 128, 2 KV heads
+x 128, conv kernels 2, QK-mean, value shift on d/2 channels, RoPE base 1e4),
+bf16 storage with fp32 accumulation, synthetic seeded inputs resident in HBM.
+A step is one cca_forward_prefill: down-projection, mix, attention,
+up-projection.  Prints one JSON line (rank 0) with tokens/s, the roofline of
+the dominant kernel (attention) timed with HIP events on the launch stream,
+and the float64 CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--rows prefill,decode,backward]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def attention_flops(S: int, Hq: int, d: int) -> float:
+    # QK^T and PV over the S(S+1)/2 visible (query, key) pairs, 2 flops per MAC
+    return 4.0 * Hq * d * S * (S + 1) / 2
+
+
+def prefill_flops(w) -> dict:
+    S, E, d = w.B * w.S, w.E, w.d
+    nq, nk = w.Hq * d, w.Hkv * d
+    return {
+        "proj_down": 2.0 * S * E * (nq + 2 * nk),
+        "mix": 2.0 * S * (w.Hq * w.kq + w.Hkv * w.kk) * d * d,
+        "attn": w.B * attention_flops(w.S, w.Hq, d),
+        "proj_up": 2.0 * S * nq * E,
+    }
+
+
+def time_oracle_sample(w, inp, n_rows=256):
+    """The oracle's forward on the full sequence for every linear step, and
+    attention plus the output projection for n_rows query rows spread evenly
+    over the sequence; the full-workload time is extrapolated as
+    t_linear + t_rows * S / n_rows (attention cost per row grows linearly with
+    its position, so evenly spaced rows average it)."""
+    from oracle import cca as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    spec = O.Spec(E=w.E, C=w.C, Hq=w.Hq, Hkv=w.Hkv, kq=w.kq, kk=w.kk, rope_base=w.rope_base,
+                  s_v=w.s_v)
+    p = {k: inp[k] for k in ("w_q", "w_k", "w_v", "w_o", "conv_q", "conv_k")}
+    x = inp["x"][0].astype(np.float64)
+    S, G, d = w.S, w.G, w.d
+    t0 = time.perf_counter()
+    q_lat = O.project(x, p["w_q"]).reshape(S, w.Hq, d)
+    k_lat = O.project(x, p["w_k"]).reshape(S, w.Hkv, d)
+    v_lat = O.project(x, p["w_v"]).reshape(S, w.Hkv, d)
+    q_c = O.conv_causal(q_lat, p["conv_q"])
+    k_c = O.conv_causal(k_lat, p["conv_k"])
+    q_m, k_m = O.qk_mean(q_lat, k_lat, q_c, k_c, G, True, True)
+    v_s = O.value_shift(v_lat, spec.mask())
+    pos = np.arange(S)
+    k_r = O.rope(k_m, pos, w.rope_base)
+    q_r = O.rope(q_m, pos, w.rope_base)
+    t_lin = time.perf_counter() - t0
+    rows = np.linspace(0, S - 1, n_rows).astype(np.int64)
+    t1 = time.perf_counter()
+    o, _ = O.attention(q_r[rows], k_r, v_s, G, q_pos=rows, block=16)
+    O.project(o.reshape(len(rows), -1), p["w_o"])
+    t_rows = time.perf_counter() - t1
+    est = t_lin + t_rows * S / n_rows
+    return {"value": S / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"float64 numpy oracle: every linear step over all {S} tokens "
+                       f"({t_lin:.1f} s) plus attention and W_o for {n_rows} evenly spaced "
+                       f"query rows ({t_rows:.1f} s), extrapolated to the full sequence "
+                       f"({est:.1f} s)")}
+
+
+def bench_prefill(args, torch, cca, w, inp):
+    from compressed_latent_attention_amd.synthetic import WORKLOADS  # noqa: F401
+    dt = torch.bfloat16
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt)
+    layer = cca.CCALayer(w.E, w.C, w.Hq, w.Hkv, w.capacity, w.kq, w.kk, w.s_v, w.flags,
+                         w.rope_base, w.dtype)
+    wts = {k: dev(inp[k]) for k in ("w_q", "w_k", "w_v", "w_o", "conv_q", "conv_k")}
+    x = dev(inp["x"])
+    B, S = w.B, w.S
+    y = torch.empty_like(x)
+    ws = layer.workspace(cca.CCA_OP_PREFILL, B, S)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        cca.cca_forward_prefill(layer.handle, wts, x, B, S, y, None, None, None, None, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    cca.cca_profile_enable(layer.handle, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = cca.cca_profile_read(layer.handle)
+    cca.cca_profile_enable(layer.handle, False)
+    return elapsed, prof, layer
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rows", default="prefill",
+                    help="comma list: prefill (headline), decode, backward")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import compressed_latent_attention_amd as cca
+    from compressed_latent_attention_amd.synthetic import WORKLOADS, make_inputs
+
+    w = WORKLOADS["ccgqa_prefill_16k"]
+    inp = make_inputs(w)
+    elapsed, prof, _ = bench_prefill(args, torch, cca, w, inp)
+    ms = elapsed * 1000.0 / args.steps
+    tokens = w.B * w.S * args.steps
+    fl = prefill_flops(w)
+    launches, total_ms = prof.get("attn", (0, 0.0))
+    attn_ms = total_ms / max(launches, 1)
+    attn_tflops = fl["attn"] / (attn_ms * 1e-3) / 1e12
+    kernels = {k: {"avg_ms": v[1] / max(v[0], 1), "launches": v[0],
+                   "tflops": (fl[k] / (v[1] / max(v[0], 1) * 1e-3) / 1e12) if k in fl else None}
+               for k, v in prof.items()}
+    total_flops = sum(fl.values())
+    out = {
+        "metric": "CCGQA prefill tokens/sec at S=16k, E=2048 (1 GPU) + % bf16 MFMA peak",
+        "value": tokens / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "ccgqa_prefill_16k", "global_batch": w.B, "seq_len": w.S,
+                   "E": w.E, "C": w.C, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+                   "conv_kernels": [w.kq, w.kk], "parallelism": "none (1 GPU)"},
+        "layer_tflops": total_flops / (ms * 1e-3) / 1e12,
+        "layer_frac_of_bf16_peak": total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": "attn", "achieved": attn_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flops_per_launch": fl["attn"], "avg_launch_ms": attn_ms},
+        "kernels": kernels,
+    }
+    rows = [r.strip() for r in args.rows.split(",") if r.strip()]
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = time_oracle_sample(w, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
