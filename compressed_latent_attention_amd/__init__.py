@@ -237,7 +237,7 @@ class CCALayer:
         return load().cca_saved_bytes(self.handle, B, S)
 
     def saved_offsets(self, B, S):
-        offs = (c_size_t * 7)()
+        offs = (c_size_t * 8)()
         _check(load().cca_saved_offsets(self.handle, B, S, offs), "cca_saved_offsets")
         return list(offs)
 

@@ -69,7 +69,8 @@ Dims make_dims(const cca_config& c) {
 }
 
 // Saved-buffer regions (see cca_saved_bytes).
-constexpr int kSavedRegions = 7;
+constexpr int kSavedRegions = 8;
+long pad64(long S) { return (S + 63) / 64 * 64; }
 struct SavedLayout {
   size_t off[kSavedRegions];
   size_t total;
@@ -82,7 +83,8 @@ SavedLayout saved_layout(const Dims& dm, long B, long S) {
       (size_t)(B * S * dm.nq) * es, (size_t)(B * S * dm.nk) * es,   // Q'', K''
       (size_t)(B * S * dm.nk) * es, (size_t)(B * S * dm.nq) * es,   // V', O
       (size_t)(B * dm.Hq * S) * 4,                                  // lse
-      (size_t)(B * S * dm.nq) * 4};                                 // O fp32
+      (size_t)(B * S * dm.nq) * 4,                                  // O fp32
+      (size_t)(B * pad64(S) * dm.nk) * es};                         // V' transposed
   SavedLayout L{};
   size_t o = 0;
   for (int i = 0; i < kSavedRegions; ++i) {
@@ -311,7 +313,7 @@ size_t cca_saved_bytes(const cca_handle* h, int32_t B, int32_t S) {
   return saved_layout(h->dm, B, S).total;
 }
 
-cca_status cca_saved_offsets(const cca_handle* h, int32_t B, int32_t S, size_t offsets[7]) {
+cca_status cca_saved_offsets(const cca_handle* h, int32_t B, int32_t S, size_t offsets[8]) {
   if (!h || B <= 0 || S <= 0 || !offsets) return CCA_ERR_INVALID_ARG;
   SavedLayout L = saved_layout(h->dm, B, S);
   for (int i = 0; i < kSavedRegions; ++i) offsets[i] = L.off[i];
@@ -360,6 +362,8 @@ cca_status cca_forward_prefill(cca_handle* h, const cca_weights* w, const void* 
     void* o = base + L.off[4];
     float* lse = (float*)(base + L.off[5]);
     float* o32 = saved ? (float*)(base + L.off[6]) : nullptr;
+    void* vt = base + L.off[7];
+    const bool mfma = prefill_uses_mfma(dm);
     const int M = B * S;
 
     GemmArgs gd = gemm_down(dm, M, x, w, qkv);
@@ -368,8 +372,9 @@ cca_status cca_forward_prefill(cca_handle* h, const cca_weights* w, const void* 
     MixArgs ma{};
     ma.dm = dm; ma.B = B; ma.S = S; ma.qkv = qkv;
     ma.conv_q = w->conv_q; ma.conv_k = w->conv_k; ma.rope = h->rope;
-    ma.q_out = qr; ma.k_out = kr; ma.v_out = vs;
+    ma.q_out = qr; ma.k_out = kr; ma.v_out = (saved || !mfma) ? vs : nullptr;
     ma.k_out2 = k_cache; ma.v_out2 = v_cache; ma.cap2 = dm.max_seq_len;
+    ma.vt_out = vt; ma.s_pad = (int)pad64(S);
     CCA_TRY_HIP(timed(h, "mix", s, [&] { return launch_mix_fwd(ma, s); }));
     if (state)
       CCA_TRY_HIP(timed(h, "write_state", s, [&] { return launch_write_state(dm, B, S, qkv, state, s); }));
@@ -378,6 +383,7 @@ cca_status cca_forward_prefill(cca_handle* h, const cca_weights* w, const void* 
     aa.dm = dm; aa.B = B; aa.Sq = S;
     aa.q = qr; aa.k = kr; aa.v = vs;
     aa.kv_bs = (long)dm.Hkv * S * dm.d; aa.kv_hs = (long)S * dm.d;
+    aa.vt = vt; aa.s_pad = (int)pad64(S);
     aa.o = o; aa.o32 = o32; aa.lse = lse; aa.decode = false;
     CCA_TRY_HIP(timed(h, "attn", s, [&] { return launch_attn_fwd(aa, s); }));
 

@@ -81,10 +81,9 @@ __global__ __launch_bounds__(AT) void attn_fwd_simple(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s);   // attn_mfma.hip
-bool attn_fwd_mfma_supported(const Dims& dm);
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
-  if (a.dm.bf16 && !a.decode && attn_fwd_mfma_supported(a.dm)) return launch_attn_fwd_mfma(a, s);
+  if (!a.decode && prefill_uses_mfma(a.dm)) return launch_attn_fwd_mfma(a, s);
   dim3 grid(a.Sq, a.dm.Hq, a.B);
   if (a.dm.bf16)
     hipLaunchKernelGGL(attn_fwd_simple<bf16>, grid, dim3(AT), 0, s, a);

@@ -79,8 +79,13 @@ struct MixArgs {
   void* k_out2;
   void* v_out2;
   int cap2;                 // row capacity of k_out2 / v_out2
+  void* vt_out;             // V' transposed [B, Hkv, d, s_pad] (MFMA path), nullable
+  int s_pad;                // S rounded up to a multiple of 64; rows [S, s_pad) are zero
 };
 hipError_t launch_mix_fwd(const MixArgs& a, hipStream_t s);
+// True when prefill uses the MFMA mix + attention pair, which exchange V' in
+// the transposed layout (and need the standard one only for saved / cache).
+bool prefill_uses_mfma(const Dims& dm);
 
 // Writes the rolling state after the last token of each sequence.
 hipError_t launch_write_state(const Dims& dm, int B, int S, const float* qkv, void* state,
@@ -115,6 +120,8 @@ struct AttnArgs {
   const void* k;
   const void* v;
   long kv_bs, kv_hs;
+  const void* vt;           // V' transposed [B, Hkv, d, s_pad] (MFMA prefill path)
+  int s_pad;
   void* o;
   float* o32;               // optional fp32 copy of o (same layout), nullable
   float* lse;

@@ -232,9 +232,11 @@ __global__ __launch_bounds__(256) void mix_decode_kernel(MixDecodeArgs a) {
 hipError_t launch_mix_fwd_mfma(const MixArgs& a, hipStream_t s);   // mix_mfma.hip
 bool mix_fwd_mfma_supported(const Dims& dm);
 
+bool prefill_uses_mfma(const Dims& dm) { return dm.bf16 && mix_fwd_mfma_supported(dm); }
+
 hipError_t launch_mix_fwd(const MixArgs& a, hipStream_t s) {
   const Dims& dm = a.dm;
-  if (dm.bf16 && mix_fwd_mfma_supported(dm)) return launch_mix_fwd_mfma(a, s);
+  if (prefill_uses_mfma(dm)) return launch_mix_fwd_mfma(a, s);
   const int KM = max(dm.kq, dm.kk);
   const size_t lds = (size_t)((TT + KM - 1) + TT) * (dm.G + 1) * dm.d * sizeof(float);
   dim3 grid((a.S + TT - 1) / TT, dm.Hkv, a.B);

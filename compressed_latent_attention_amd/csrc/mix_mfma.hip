@@ -178,22 +178,48 @@ __global__ __launch_bounds__(256) void mix_fwd_mfma_kernel(MixArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-  // value shift: plain coalesced copy of this group's V for the 128 tokens
+  // value shift.  Pass 1: the shifted V of these 128 tokens, read coalesced
+  // from the fp32 latent, rounded to bf16 into an LDS tile (rows past S are
+  // zero) and written in the standard layout when asked.  Pass 2: the tile is
+  // written transposed, V'^T[c][t], which the MFMA attention reads.
+  __syncthreads();                           // kbuf is free again
+  constexpr int VLD = D + 8;
+  bf16* vtile = reinterpret_cast<bf16*>(kbuf);   // [TW][VLD]
   const int vcol = dm.nq + dm.nk + g * D;
-  bf16* vo = reinterpret_cast<bf16*>(a.v_out) + ((long)(b * dm.Hkv + g) * S) * D;
+  bf16* vo = a.v_out ? reinterpret_cast<bf16*>(a.v_out) + ((long)(b * dm.Hkv + g) * S) * D
+                     : nullptr;
   bf16* vo2 = a.v_out2 ? reinterpret_cast<bf16*>(a.v_out2) + ((long)(b * dm.Hkv + g) * a.cap2) * D
                        : nullptr;
   const int first_shift = (dm.flags & kVShift) ? D - dm.sv : D;
   for (int e = threadIdx.x; e < TW * D; e += 256) {
-    const int t = t0 + e / D, c = e % D;
-    if (t >= S) break;
-    float v;
-    if (c >= first_shift)
-      v = t > 0 ? qkv_b[(long)(t - 1) * dm.nqkv + vcol + c] : 0.0f;
-    else
-      v = qkv_b[(long)t * dm.nqkv + vcol + c];
-    vo[(long)t * D + c] = (bf16)v;
-    if (vo2) vo2[(long)t * D + c] = (bf16)v;
+    const int tt = e / D, c = e % D;
+    const int t = t0 + tt;
+    float v = 0.0f;
+    if (t < S) {
+      if (c >= first_shift)
+        v = t > 0 ? qkv_b[(long)(t - 1) * dm.nqkv + vcol + c] : 0.0f;
+      else
+        v = qkv_b[(long)t * dm.nqkv + vcol + c];
+    }
+    const bf16 vb = (bf16)v;
+    vtile[tt * VLD + c] = vb;
+    if (t < S) {
+      if (vo) vo[(long)t * D + c] = vb;
+      if (vo2) vo2[(long)t * D + c] = vb;
+    }
+  }
+  if (a.vt_out) {
+    __syncthreads();
+    bf16* vt = reinterpret_cast<bf16*>(a.vt_out) + (long)(b * dm.Hkv + g) * D * a.s_pad;
+    for (int e = threadIdx.x; e < D * (TW / 8); e += 256) {
+      const int c = e / (TW / 8), m = e % (TW / 8);
+      const int t = t0 + 8 * m;
+      if (t >= a.s_pad) continue;
+      bf16x8 pk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pk[i] = vtile[(8 * m + i) * VLD + c];
+      *reinterpret_cast<bf16x8*>(vt + (long)c * a.s_pad + t) = pk;
+    }
   }
 }
 

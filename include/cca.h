@@ -131,11 +131,13 @@ size_t cca_workspace_bytes(const cca_handle* h, int op, int32_t B, int32_t S);
  *   o       [B, S, Hq*d]        dt    (attention output before W_o)
  *   lse     [B, Hq, S]          fp32  (natural log of each softmax denominator)
  *   o_f32   [B, S, Hq*d]        fp32  (the same output before rounding to dt)
+ *   v_t     [B, Hkv, d, S64]    dt    (V' transposed, S64 = S rounded up to 64;
+ *                                      written only on the bf16 d = 128 path)
  * The backward forms rowsum(dO * O) from o_f32: with near-one-hot attention
  * rows that sum cancels, and O rounded to bf16 would cost ~2% in dQ and dK.
- * cca_saved_offsets writes the 7 byte offsets into offsets[0..6]. */
+ * cca_saved_offsets writes the 8 byte offsets into offsets[0..7]. */
 size_t cca_saved_bytes(const cca_handle* h, int32_t B, int32_t S);
-cca_status cca_saved_offsets(const cca_handle* h, int32_t B, int32_t S, size_t offsets[7]);
+cca_status cca_saved_offsets(const cca_handle* h, int32_t B, int32_t S, size_t offsets[8]);
 
 /* Bytes of rolling decode state per batch: B * W elements of dt where
  * W = (kq-1)*Hq*d + (kk-1)*Hkv*d + Hkv*d holds, per sequence,
