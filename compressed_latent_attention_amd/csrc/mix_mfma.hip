@@ -1,147 +1,147 @@
 // cca_mix for bf16, d = 128, on MFMA: the causal grouped convolution of q~ and
 // k~ (CCA-es §2.B.1 "Mezcla Convolucional"), QK-mean (§2.B.2), value shift
-// (§2.B.3) and RoPE (§3 item 2) in one pass per (128 tokens, KV group).
+// (§2.B.3) and RoPE (§3 item 2) in one pass per (64 tokens, KV group).
 //
 // The convolution of one head is a GEMM: out[t, c] = sum_{j, c'} u[t - j, c'] *
-// A_j[c, c'] with M = tokens, N = channels, K = k * d.  Operand A (u) comes
-// from the fp32 latent in two bf16 halves (hi = bf16(u), lo = bf16(u - hi)), so
-// the product keeps ~16 mantissa bits of q~ and k~ with fp32 accumulation;
-// operand B is the bf16 tap row A_j[c, 8 channels], read straight from L2.
-// With lane = output channel and registers = tokens, every element a wave
-// needs for QK-mean (the same token and channel of the group's G query heads
-// and its K head) and for RoPE (channels c and c + d/2) sits in one lane.
+// A_j[c, c'] with M = tokens, N = channels, K = k * d.  The fp32 latent tile of
+// the head (64 tokens plus the k - 1 halo tokens before them) is staged in LDS
+// with coalesced 16-byte loads; operand A is read from it in two bf16 halves
+// (hi = bf16(u), lo = bf16(u - hi)), so the product keeps ~16 mantissa bits of
+// q~ and k~ with fp32 accumulation; operand B is the bf16 tap row A_j[c, 8
+// channels] read from L2.  With lane = output channel and registers = tokens,
+// everything QK-mean needs (the same token and channel of the group's query
+// heads and its K head) and both channels of a RoPE pair (c, c + d/2) sit in
+// one lane.
 //
-// Wave w of the 4: tokens t0 + 64*(w/2) .. +63 (two 32-token blocks), channel
-// blocks {w%2, w%2 + 2} (32 channels each: RoPE partners).
+// Wave w of the 4: tokens t0 + 32*(w/2) .. +31, channel blocks {w%2, w%2 + 2}.
 #include "cca_internal.h"
 
 namespace cca {
 namespace {
 
 constexpr int D = 128;
-constexpr int TW = 128;          // tokens per work-group
+constexpr int TW = 64;               // tokens per work-group
+constexpr int ULD = D + 4;           // LDS row stride (floats): 528 B, conflict-free b128 reads
+constexpr int UROWS = TW + kMaxConv - 1;
 
-struct ConvAcc {
-  f32x16 v[2][2];                // [token block][channel block]
-};
+typedef f32x16 Acc2[2];              // [channel block]
 
-__device__ __forceinline__ void zero(ConvAcc& a) {
+__device__ __forceinline__ void zero(Acc2& a) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) a.v[i][j][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) a[j][r] = 0.0f;
 }
 
-// acc += conv of one head: u column `col` of the fp32 latent (row stride
-// nqkv), taps [k][D][D] bf16.
-__device__ __forceinline__ void conv_head(ConvAcc& acc, const float* qkv_b, int nqkv, int col,
-                                          int S, int tw0, const bf16* taps, int k, int cb0,
-                                          int lane) {
+// Rows t0 - halo .. t0 + TW - 1 of latent column block `col` into LDS (zero
+// outside [0, S)).  LDS row i holds token t0 - halo + i.
+__device__ __forceinline__ void load_tile(float* u, const float* qkv_b, int nqkv, int col, int S,
+                                          int t0, int halo) {
+  const int rows = TW + halo;
+  for (int e = threadIdx.x; e < rows * (D / 4); e += 256) {
+    const int i = e / (D / 4), ch = (e % (D / 4)) * 4;
+    const int t = t0 - halo + i;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (t >= 0 && t < S) v = *reinterpret_cast<const f32x4*>(qkv_b + (long)t * nqkv + col + ch);
+    *reinterpret_cast<f32x4*>(u + i * ULD + ch) = v;
+  }
+}
+
+// acc += conv of one head whose tile is in LDS (row of token t: t - t0 + halo).
+__device__ __forceinline__ void conv_head(Acc2& acc, const float* u, int halo, int tw0_rel,
+                                          const bf16* taps, int k, int cb0, int lane) {
   const int l32 = lane & 31, hi = lane >> 5;
   for (int j = 0; j < k; ++j) {
+    const float* urow = u + (tw0_rel + l32 - j + halo) * ULD + hi * 8;
+    const bf16* trow0 = taps + ((long)j * D + cb0 * 32 + l32) * D + hi * 8;
+    const bf16* trow1 = trow0 + 64 * D;
 #pragma unroll 2
     for (int ks = 0; ks < 8; ++ks) {
-      bf16x8 ahi[2], alo[2], bt[2];
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(urow + ks * 16);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(urow + ks * 16 + 4);
+      bf16x8 ahi, alo;
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int t = tw0 + tb * 32 + l32 - j;
-        f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-        if (t >= 0 && t < S) {
-          const float* p = qkv_b + (long)t * nqkv + col + ks * 16 + hi * 8;
-          x0 = *reinterpret_cast<const f32x4*>(p);
-          x1 = *reinterpret_cast<const f32x4*>(p + 4);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16 h0 = (bf16)x0[e], h1 = (bf16)x1[e];
-          ahi[tb][e] = h0;
-          ahi[tb][e + 4] = h1;
-          alo[tb][e] = (bf16)(x0[e] - (float)h0);
-          alo[tb][e + 4] = (bf16)(x1[e] - (float)h1);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const bf16 h0 = (bf16)x0[e], h1 = (bf16)x1[e];
+        ahi[e] = h0;
+        ahi[e + 4] = h1;
+        alo[e] = (bf16)(x0[e] - (float)h0);
+        alo[e + 4] = (bf16)(x1[e] - (float)h1);
       }
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int c = (cb0 + 2 * cb) * 32 + l32;
-        bt[cb] = *reinterpret_cast<const bf16x8*>(taps + ((long)j * D + c) * D + ks * 16 + hi * 8);
-      }
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          acc.v[tb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[tb], bt[cb], acc.v[tb][cb], 0, 0, 0);
-          acc.v[tb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[tb], bt[cb], acc.v[tb][cb], 0, 0, 0);
-        }
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(trow0 + ks * 16);
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(trow1 + ks * 16);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b0, acc[0], 0, 0, 0);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b0, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b1, acc[1], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b1, acc[1], 0, 0, 0);
     }
   }
 }
 
-__global__ __launch_bounds__(256) void mix_fwd_mfma_kernel(MixArgs a) {
-  // k^ of every wave, kept lane-private: element (tb, cb, r) of thread x at
-  // kbuf[((tb * 2 + cb) * 16 + r) * 256 + x]
-  __shared__ float kbuf[64 * 256];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mix_fwd_mfma_kernel(MixArgs a) {
+  __shared__ __attribute__((aligned(16))) float uk[UROWS * ULD];   // k~ tile
+  __shared__ __attribute__((aligned(16))) float uq[UROWS * ULD];   // current q~ tile, then v~
   const Dims& dm = a.dm;
   const int G = dm.G, S = a.S;
   const int g = blockIdx.y, b = blockIdx.z;
   const int t0 = blockIdx.x * TW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int tw0 = t0 + 64 * (wave >> 1);     // this wave's first token
+  const int tw0_rel = 32 * (wave >> 1);      // this wave's first token, relative to t0
   const int cb0 = wave & 1;                  // channel blocks cb0 and cb0 + 2
   const float* qkv_b = a.qkv + (long)b * S * dm.nqkv;
   const float A = (dm.flags & kQkPre) ? 0.5f : 0.0f;
   const float Bc = (dm.flags & kQkPost) ? 0.5f : 0.0f;
   const bool rope = (dm.flags & kRope) != 0;
   const int kcol = dm.nq + g * D;
-
-  // token of register r in token block tb; channel of channel block cb
-  auto tok = [&](int tb, int r) { return tw0 + tb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3); };
+  const int hq = dm.kq - 1, hk = dm.kk - 1;  // halo rows of the q and k tiles
   const int c_lo = cb0 * 32 + l32;           // < 64: RoPE pair (c_lo, c_lo + 64)
+  // register r holds token tw0_rel + 8*(r/4) + 4*hi + r%4 (relative to t0)
+  auto trel = [&](int r) { return tw0_rel + 8 * (r >> 2) + 4 * hi + (r & 3); };
 
-  ConvAcc qacc, mpost;
-  zero(qacc);
-  conv_head(qacc, qkv_b, dm.nqkv, kcol, S, tw0,
+  load_tile(uk, qkv_b, dm.nqkv, kcol, S, t0, hk);
+  __syncthreads();
+  Acc2 kacc, qacc, mpost, mpre;
+  zero(kacc);
+  conv_head(kacc, uk, hk, tw0_rel,
             reinterpret_cast<const bf16*>(a.conv_k) + (long)g * dm.kk * D * D, dm.kk, cb0, lane);
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) kbuf[((tb * 2 + cb) * 16 + r) * 256 + threadIdx.x] = qacc.v[tb][cb][r];
   zero(mpost);
+  zero(mpre);
 
   for (int i = 0; i < G; ++i) {
     const int h = g * G + i;
+    if (i > 0) __syncthreads();              // every wave is done with the previous q tile
+    load_tile(uq, qkv_b, dm.nqkv, h * D, S, t0, hq);
+    __syncthreads();
     zero(qacc);
-    conv_head(qacc, qkv_b, dm.nqkv, h * D, S, tw0,
+    conv_head(qacc, uq, hq, tw0_rel,
               reinterpret_cast<const bf16*>(a.conv_q) + (long)h * dm.kq * D * D, dm.kq, cb0,
               lane);
     bf16* qo = reinterpret_cast<bf16*>(a.q_out) + ((long)(b * dm.Hq + h) * S) * D;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int r = 0; r < 16; ++r) {
+      const int tr = trel(r);
+      const int t = t0 + tr;
+      float x[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = tok(tb, r);
-        if (t >= S) continue;
-        float x[2];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const int c = c_lo + 64 * cb;
-          const float qh = qacc.v[tb][cb][r];
-          const float kh = kbuf[((tb * 2 + cb) * 16 + r) * 256 + threadIdx.x];
-          mpost.v[tb][cb][r] += qh;
-          const float qp = qkv_b[(long)t * dm.nqkv + h * D + c];
-          const float kp = qkv_b[(long)t * dm.nqkv + kcol + c];
-          x[cb] = qh + A * (qp + kp) + Bc * (qh + kh);
-        }
+      for (int cb = 0; cb < 2; ++cb) {
+        const int c = c_lo + 64 * cb;
+        const float qh = qacc[cb][r], kh = kacc[cb][r];
+        const float qp = uq[(tr + hq) * ULD + c];
+        const float kp = uk[(tr + hk) * ULD + c];
+        mpost[cb][r] += qh;
+        mpre[cb][r] += qp;
+        x[cb] = qh + A * (qp + kp) + Bc * (qh + kh);
+      }
+      if (t < S) {
         float2 cs = make_float2(1.f, 0.f);
         if (rope) cs = a.rope[(long)t * (D / 2) + c_lo];
         qo[(long)t * D + c_lo] = (bf16)(x[0] * cs.x - x[1] * cs.y);
         qo[(long)t * D + c_lo + 64] = (bf16)(x[1] * cs.x + x[0] * cs.y);
-        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_sched_barrier(0);     // keep the epilogue's loads from piling up
+    }
   }
 
   // k' = k^ + a/2 (mean_g q~ + k~) + b/2 (mean_g q^ + k^)
@@ -150,21 +150,18 @@ __global__ __launch_bounds__(256) void mix_fwd_mfma_kernel(MixArgs a) {
   bf16* ko2 = a.k_out2 ? reinterpret_cast<bf16*>(a.k_out2) + ((long)(b * dm.Hkv + g) * a.cap2) * D
                        : nullptr;
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
+  for (int r = 0; r < 16; ++r) {
+    const int tr = trel(r);
+    const int t = t0 + tr;
+    float x[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = tok(tb, r);
-      if (t >= S) continue;
-      float x[2];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int c = c_lo + 64 * cb;
-        float mpre = 0.0f;
-        for (int i = 0; i < G; ++i) mpre += qkv_b[(long)t * dm.nqkv + (g * G + i) * D + c];
-        const float kh = kbuf[((tb * 2 + cb) * 16 + r) * 256 + threadIdx.x];
-        const float kp = qkv_b[(long)t * dm.nqkv + kcol + c];
-        x[cb] = kh + A * (mpre * invG + kp) + Bc * (mpost.v[tb][cb][r] * invG + kh);
-      }
+    for (int cb = 0; cb < 2; ++cb) {
+      const int c = c_lo + 64 * cb;
+      const float kh = kacc[cb][r];
+      const float kp = uk[(tr + hk) * ULD + c];
+      x[cb] = kh + A * (mpre[cb][r] * invG + kp) + Bc * (mpost[cb][r] * invG + kh);
+    }
+    if (t < S) {
       float2 cs = make_float2(1.f, 0.f);
       if (rope) cs = a.rope[(long)t * (D / 2) + c_lo];
       const bf16 lo = (bf16)(x[0] * cs.x - x[1] * cs.y);
@@ -175,49 +172,44 @@ __global__ __launch_bounds__(256) void mix_fwd_mfma_kernel(MixArgs a) {
         ko2[(long)t * D + c_lo] = lo;
         ko2[(long)t * D + c_lo + 64] = hv;
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
-  // value shift.  Pass 1: the shifted V of these 128 tokens, read coalesced
-  // from the fp32 latent, rounded to bf16 into an LDS tile (rows past S are
-  // zero) and written in the standard layout when asked.  Pass 2: the tile is
-  // written transposed, V'^T[c][t], which the MFMA attention reads.
-  __syncthreads();                           // kbuf is free again
-  constexpr int VLD = D + 8;
-  bf16* vtile = reinterpret_cast<bf16*>(kbuf);   // [TW][VLD]
+  // value shift: v~ rows t0 - 1 .. t0 + TW - 1 into LDS (reusing the q tile),
+  // then V' in the standard layout (when asked) and transposed, V'^T[c][t]
+  __syncthreads();
   const int vcol = dm.nq + dm.nk + g * D;
+  load_tile(uq, qkv_b, dm.nqkv, vcol, S, t0, 1);
+  __syncthreads();
+  const int first_shift = (dm.flags & kVShift) ? D - dm.sv : D;
   bf16* vo = a.v_out ? reinterpret_cast<bf16*>(a.v_out) + ((long)(b * dm.Hkv + g) * S) * D
                      : nullptr;
   bf16* vo2 = a.v_out2 ? reinterpret_cast<bf16*>(a.v_out2) + ((long)(b * dm.Hkv + g) * a.cap2) * D
                        : nullptr;
-  const int first_shift = (dm.flags & kVShift) ? D - dm.sv : D;
-  for (int e = threadIdx.x; e < TW * D; e += 256) {
-    const int tt = e / D, c = e % D;
-    const int t = t0 + tt;
-    float v = 0.0f;
-    if (t < S) {
-      if (c >= first_shift)
-        v = t > 0 ? qkv_b[(long)(t - 1) * dm.nqkv + vcol + c] : 0.0f;
-      else
-        v = qkv_b[(long)t * dm.nqkv + vcol + c];
-    }
-    const bf16 vb = (bf16)v;
-    vtile[tt * VLD + c] = vb;
-    if (t < S) {
-      if (vo) vo[(long)t * D + c] = vb;
-      if (vo2) vo2[(long)t * D + c] = vb;
+  if (vo || vo2) {
+    for (int e = threadIdx.x; e < TW * D; e += 256) {
+      const int tr = e / D, c = e % D;
+      const int t = t0 + tr;
+      if (t >= S) break;
+      const bf16 v = (bf16)uq[(tr + (c >= first_shift ? 0 : 1)) * ULD + c];
+      if (vo) vo[(long)t * D + c] = v;
+      if (vo2) vo2[(long)t * D + c] = v;
     }
   }
   if (a.vt_out) {
-    __syncthreads();
     bf16* vt = reinterpret_cast<bf16*>(a.vt_out) + (long)(b * dm.Hkv + g) * D * a.s_pad;
     for (int e = threadIdx.x; e < D * (TW / 8); e += 256) {
-      const int c = e / (TW / 8), m = e % (TW / 8);
+      const int c = e % D, m = e / D;
       const int t = t0 + 8 * m;
       if (t >= a.s_pad) continue;
+      const int row_off = c >= first_shift ? 0 : 1;
       bf16x8 pk;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pk[i] = vtile[(8 * m + i) * VLD + c];
+      for (int i = 0; i < 8; ++i) {
+        // tokens at or past S are zero: the padding of V'^T up to s_pad
+        pk[i] = (bf16)(t + i < S ? uq[(8 * m + i + row_off) * ULD + c] : 0.0f);
+      }
       *reinterpret_cast<bf16x8*>(vt + (long)c * a.s_pad + t) = pk;
     }
   }
@@ -228,6 +220,7 @@ __global__ __launch_bounds__(256) void mix_fwd_mfma_kernel(MixArgs a) {
 bool mix_fwd_mfma_supported(const Dims& dm) { return dm.bf16 && dm.d == D; }
 
 hipError_t launch_mix_fwd_mfma(const MixArgs& a, hipStream_t s) {
+  if (a.vt_out && (a.s_pad % 64 != 0 || a.s_pad < a.S)) return hipErrorInvalidValue;
   dim3 grid((a.S + TW - 1) / TW, a.dm.Hkv, a.B);
   hipLaunchKernelGGL(mix_fwd_mfma_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
