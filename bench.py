@@ -124,6 +124,9 @@ def main():
     ap.add_argument("--rows", default="prefill",
                     help="comma list: prefill (headline), decode, backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (steps times), the "
+                         "reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer library has no multi-GPU path "
@@ -131,6 +134,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n, "launches": args.steps}), flush=True)
+        return
     import compressed_latent_attention_amd as cca
     from compressed_latent_attention_amd.synthetic import WORKLOADS, make_inputs
 
