@@ -1,0 +1,187 @@
+// Large bf16 GEMM for the projections of the CCA layer (cca_proj): C = A B^T
+// with A [M, K] and B [N, K] both K-contiguous ("NT"), fp32 accumulation,
+// fp32 or bf16 output.  It serves the down-projection of x to the latent
+// q~ | k~ | v~ (CCA-es §2.A "Principio Fundamental"; CCA-fr §2 "Projection
+// vers l'Espace Latent") and the output projection O W_o^T.
+//
+// Work-group tile 256 x 256 x 64, four waves of 128 x 128, one wave per SIMD:
+// each wave holds 16 accumulator blocks of v_mfma_f32_32x32x16_bf16 (256
+// registers) and issues 16 MFMAs per 16-wide k step from two double-buffered
+// sets of operand fragments.  Tiles of A and B move from global memory to LDS
+// with buffer loads that write LDS directly (16 bytes per lane), two stages
+// deep; LDS rows (64 k = 128 B) are unpadded with their 16-byte chunks
+// XOR-swizzled by row, so that the fragment reads are free of bank conflicts.
+// Rows past M or past the end of B's segment read as zero (buffer range
+// check), so ragged M and N need no special path.  Tiles are numbered so that
+// the tiles of one XCD (work-groups are dealt to the 8 XCDs round-robin) are
+// consecutive and share rows of A in that XCD's L2.
+#include "cca_internal.h"
+
+namespace cca {
+namespace {
+
+constexpr int TM = 256, TN = 256, TK = 64;
+constexpr int A_BYTES = TM * TK * 2;
+constexpr int B_BYTES = TN * TK * 2;
+constexpr int STAGE = A_BYTES + B_BYTES;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS byte offset of 16-byte chunk c (of 8) in tile row r.
+__device__ __forceinline__ int sw(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(bf16* p, float v) { *p = (bf16)v; }
+
+// One 256-row x 64-k operand tile into LDS: rows row0 .. of a K-contiguous
+// matrix at base (row stride ld elements), `rows` of them valid; k from k0.
+// Wave w writes 1 KB blocks 8w .. 8w + 7 (8 rows each); lane L lands at row
+// 8 blk + L / 8, chunk position L % 8 and fetches the chunk the swizzle puts
+// there.
+__device__ __forceinline__ void dma_tile(char* dst, const bf16* base, long ld, int rows, int K,
+                                         int k0, int wave, int lane) {
+  const int nrec = ((rows - 1) * (int)ld + K - k0) * 2;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(base + k0), 0, nrec, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int blk = wave * 8 + i;
+    const int r = blk * 8 + (lane >> 3), pos = lane & 7;
+    const int src = r * (int)ld * 2 + ((pos ^ ((r >> 1) & 7)) << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16, src, 0, 0, 0);
+  }
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+
+  // tile of this work-group: XCD x (= blockIdx % 8) takes a consecutive run
+  const int nt = tiles_m * tiles_n;
+  const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int t = xcd * (nt >> 3) + min(xcd, nt & 7) + loc;
+  const int tm = t / tiles_n, tn = t % tiles_n;
+  const int m0 = tm * TM, n0 = tn * TN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  // A rows m0 .., B rows n0 .. (inside one segment of B, checked by the host)
+  const bf16* abase = reinterpret_cast<const bf16*>(g.a) + (long)m0 * g.lda;
+  const int arows = min(g.M - m0, TM);
+  int s = 0;
+  if (g.b_nseg > 1 && n0 >= g.b_start[1]) s = 1;
+  if (g.b_nseg > 2 && n0 >= g.b_start[2]) s = 2;
+  const int seg_end = s + 1 < g.b_nseg ? g.b_start[s + 1] : g.N;
+  const bf16* bbase = reinterpret_cast<const bf16*>(g.b_ptr[s]) + (long)(n0 - g.b_start[s]) * g.ldb;
+  const int brows = min(seg_end - n0, TN);
+
+  const int nk = g.K / TK;
+  dma_tile(lds, abase, g.lda, arows, g.K, 0, wave, lane);
+  dma_tile(lds + A_BYTES, bbase, g.ldb, brows, g.K, 0, wave, lane);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // fragment addresses within a stage: row (wm*128 + i*32 + l32) of A and
+  // (wn*128 + j*32 + l32) of B, chunk 2 ks + hi; the swizzle term depends on
+  // l32 only, so the i / j blocks are immediate offsets.
+  int aoff[4], boff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    aoff[ks] = sw(wm * 128 + l32, 2 * ks + hi);
+    boff[ks] = A_BYTES + sw(wn * 128 + l32, 2 * ks + hi);
+  }
+  wait_dma();
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* st = lds + (kt & 1) * STAGE;
+    if (kt + 1 < nk) {
+      char* nx = lds + ((kt + 1) & 1) * STAGE;
+      dma_tile(nx, abase, g.lda, arows, g.K, (kt + 1) * TK, wave, lane);
+      dma_tile(nx + A_BYTES, bbase, g.ldb, brows, g.K, (kt + 1) * TK, wave, lane);
+    }
+    bf16x8 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa[0][i] = *reinterpret_cast<const bf16x8*>(st + aoff[0] + i * 32 * 128);
+      fb[0][i] = *reinterpret_cast<const bf16x8*>(st + boff[0] + i * 32 * 128);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          fa[cur ^ 1][i] = *reinterpret_cast<const bf16x8*>(st + aoff[ks + 1] + i * 32 * 128);
+          fb[cur ^ 1][i] = *reinterpret_cast<const bf16x8*>(st + boff[ks + 1] + i * 32 * 128);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j],
+                                                              0, 0, 0);
+    }
+    wait_dma();
+    __syncthreads();
+  }
+
+  // D layout of 32x32 MFMA: lane holds column l32, rows 8*(r/4) + 4*hi + r%4.
+  // One C segment (checked by the host): a uniform tile base plus 32-bit lane
+  // offsets.
+  char* cbase = reinterpret_cast<char*>(g.c_ptr[0]) + ((long)m0 * g.ldc + n0) * sizeof(OutT);
+  const int ldc = (int)g.ldc;
+  const int mrem = g.M - m0, nrem = g.N - n0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nl = wn * 128 + j * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ml = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (ml < mrem && nl < nrem)
+          store_out(reinterpret_cast<OutT*>(cbase + (ml * ldc + nl) * (int)sizeof(OutT)),
+                    acc[i][j][r]);
+      }
+    }
+}
+
+}  // namespace
+
+// Launches the 256 x 256 NT kernel when the shape suits it: K a multiple of 64,
+// every B segment starting at a multiple of 256, one C segment, row strides
+// that keep 16-byte alignment, and enough tiles to fill the chip.  Returns false (nothing
+// launched) otherwise.
+bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError_t* err) {
+  if (g.K % TK != 0 || g.K <= 0 || g.lda % 8 != 0 || g.ldb % 8 != 0 || g.c_nseg != 1)
+    return false;
+  if ((long)TM * g.ldc * 4 >= (1L << 31)) return false;
+  for (int i = 1; i < g.b_nseg; ++i)
+    if (g.b_start[i] % TN != 0) return false;
+  if ((long)TM * g.lda * 2 >= (1L << 31) || (long)TN * g.ldb * 2 >= (1L << 31)) return false;
+  const int tiles_m = (g.M + TM - 1) / TM, tiles_n = (g.N + TN - 1) / TN;
+  if ((long)tiles_m * tiles_n < 64) return false;
+  dim3 grid(tiles_m * tiles_n);
+  if (out_f32)
+    hipLaunchKernelGGL(gemm_nt_256_kernel<float>, grid, dim3(256), 0, s, g, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL(gemm_nt_256_kernel<bf16>, grid, dim3(256), 0, s, g, tiles_m, tiles_n);
+  *err = hipGetLastError();
+  return true;
+}
+
+}  // namespace cca

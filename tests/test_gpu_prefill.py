@@ -87,12 +87,12 @@ def test_prefill_cca_4k_bf16():
     check_prefill(w, make_inputs(w))
 
 
-def test_prefill_ccgqa_16k_sampled_rows():
-    """Full-size CCGQA prefill (S = 16384) in the launch configuration the
-    benchmark times; y checked on 48 sampled rows including the first and last."""
-    w = WORKLOADS["ccgqa_prefill_16k"]
+def check_sampled_rows(w: Workload, n_random=43):
+    """y of a large prefill on sampled rows (the first and last included): the
+    oracle computes K'' and V' for every token and attention only for the
+    sampled query rows."""
     inp = make_inputs(w)
-    say(f"[prefill16k] {w}")
+    say(f"[prefill sampled] {w}")
     r = run_prefill(w, inp, with_saved=False)
     y = host(r["y"])[0]
     spec = spec_of(w)
@@ -109,7 +109,7 @@ def test_prefill_ccgqa_16k_sampled_rows():
     pos = np.arange(S)
     k_r = O.rope(k_m, pos, w.rope_base)
     rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, S - 1], rng.integers(0, S, 43)]))
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, S - 1], rng.integers(0, S, n_random)]))
     q_r = O.rope(q_m[rows], rows, w.rope_base)
     o, _ = O.attention(q_r, k_r, v_s, G, q_pos=rows)
     y_ref = O.project(o.reshape(len(rows), -1), p["w_o"])
@@ -117,6 +117,19 @@ def test_prefill_ccgqa_16k_sampled_rows():
     say(f"  sampled rows rel error {e:.3e}")
     assert e <= TOL["bf16"]
     assert np.all(np.isfinite(y))
+
+
+def test_prefill_ccgqa_16k_sampled_rows():
+    """Full-size CCGQA prefill (S = 16384) in the launch configuration the
+    benchmark times."""
+    check_sampled_rows(WORKLOADS["ccgqa_prefill_16k"])
+
+
+def test_prefill_ragged_large_sampled_rows():
+    """S = 5000 at E = 2048: the 256 x 256 projection GEMMs with a ragged last
+    row tile (5000 = 19 * 256 + 136) and the attention's ragged last block."""
+    check_sampled_rows(Workload("ccgqa_ragged_5000", B=1, S=5000, E=2048, C=4, Hq=4, Hkv=2,
+                                seed=43), n_random=60)
 
 
 def test_causality_bit_identical_on_gpu():
