@@ -116,13 +116,158 @@ def bench_prefill(args, torch, cca, w, inp):
     return elapsed, prof, layer
 
 
+DECODE_BYTES_NOTE = ("K and V caches over positions 0..pos of every sequence + all weights "
+                     "+ x_new, y_new, the rolling state and the new cache rows")
+
+
+def decode_bytes(w) -> float:
+    """Algorithmic HBM bytes of one decode step: the cache rows attention reads
+    (positions 0..pos, K and V), every weight once, and the per-token
+    activations (x_new, y_new, the state read and written, the cache rows
+    written)."""
+    es = 2
+    d, nq, nk = w.d, w.Hq * w.d, w.Hkv * w.d
+    keys = w.S + 1
+    cache = 2.0 * w.B * w.Hkv * keys * d * es
+    weights = (w.E * (nq + 2 * nk) + w.E * nq + (w.Hq * w.kq + w.Hkv * w.kk) * d * d) * es
+    state_w = (w.kq - 1) * nq + (w.kk - 1) * nk + nk
+    acts = w.B * (2 * w.E + 2 * state_w + 2 * nk) * es
+    return cache + weights + acts
+
+
+def backward_flops(w) -> dict:
+    """Algorithmic FLOPs of one backward pass: the attention backward as five
+    causal matmuls (S recompute, dP, dV, dQ, dK), the four projection GEMM
+    gradients (dx and dW for W_o and for W_qkv) and the conv gradients."""
+    S, E, d = w.B * w.S, w.E, w.d
+    nq, nk = w.Hq * d, w.Hkv * d
+    attn = 5.0 / 2.0 * w.B * attention_flops(w.S, w.Hq, d)
+    gemm = 2.0 * (2.0 * S * nq * E) + 2.0 * (2.0 * S * E * (nq + 2 * nk))
+    conv = 2.0 * (2.0 * S * (w.Hq * w.kq + w.Hkv * w.kk) * d * d)
+    return {"attn": attn, "gemm": gemm, "conv": conv}
+
+
+def _time_loop(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def bench_decode(args, torch, cca):
+    """32-sequence CCGQA decode step over a 32768-token cache.  The cache, the
+    state and x_new are drawn on the GPU from a seeded torch generator (N(0,1),
+    the same law as the parity workload; the timing does not depend on the
+    values), the weights from the seeded parity recipe."""
+    from compressed_latent_attention_amd.synthetic import WORKLOADS, make_inputs
+    w = WORKLOADS["ccgqa_decode_32k"]
+    layer = cca.CCALayer(w.E, w.C, w.Hq, w.Hkv, w.capacity, w.kq, w.kk, w.s_v, w.flags,
+                         w.rope_base, w.dtype)
+    wi = make_inputs(w.replace(S=1, B=1))     # weights only (same draw order and seed)
+    dt = torch.bfloat16
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt)
+    wts = {k: dev(wi[k]) for k in ("w_q", "w_k", "w_v", "w_o", "conv_q", "conv_k")}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    shape = (w.B, w.Hkv, w.capacity, w.d)
+    kc = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(dt)
+    vc = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(dt)
+    st = torch.randn((w.B, layer.state_width()), generator=gen, device="cuda").to(dt)
+    xn = torch.randn((w.B, w.E), generator=gen, device="cuda").to(dt)
+    pos = [w.S] * w.B
+    ws = layer.workspace(cca.CCA_OP_DECODE, w.B, 0)
+    yn = torch.empty_like(xn)
+    stream = torch.cuda.current_stream()
+    arr_pos = pos
+
+    def step():
+        cca.cca_decode_step(layer.handle, wts, xn, arr_pos, w.B, kc, vc, st, yn, ws, stream)
+
+    steps = max(args.steps, 10)
+    sec = _time_loop(torch, step, steps, args.warmup)
+    cca.cca_profile_enable(layer.handle, True)
+    _time_loop(torch, step, 5, 0)
+    prof = cca.cca_profile_read(layer.handle)
+    cca.cca_profile_enable(layer.handle, False)
+    byts = decode_bytes(w)
+    kernels = {k: {"avg_ms": v[1] / max(v[0], 1), "launches": v[0]} for k, v in prof.items()}
+    attn_ms = kernels.get("decode_attn", {}).get("avg_ms", float("nan"))
+    cache_bytes = 2.0 * w.B * w.Hkv * (w.S + 1) * w.d * 2
+    layer.close()
+    return {
+        "workload": f"ccgqa_decode_32k: B={w.B}, cache {w.S} tokens, E={w.E}, Hq={w.Hq}, "
+                    f"Hkv={w.Hkv}, d={w.d}, bf16",
+        "tokens_per_s": w.B / sec,
+        "ms_per_step": sec * 1e3,
+        "hbm_bytes_per_step": byts,
+        "bytes_note": DECODE_BYTES_NOTE,
+        "GBps": byts / sec / 1e9,
+        "frac_of_hbm_peak": byts / sec / 1e9 / PEAK_HBM_GBS,
+        "attn_kernel": {"avg_ms": attn_ms, "cache_bytes": cache_bytes,
+                        "GBps": cache_bytes / (attn_ms * 1e-3) / 1e9,
+                        "frac_of_hbm_peak": cache_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "kernels": kernels,
+    }
+
+
+def bench_backward(args, torch, cca):
+    """CCGQA backward at S=16384 from a saved prefill of the same seeded x."""
+    from compressed_latent_attention_amd.synthetic import WORKLOADS, make_inputs
+    w = WORKLOADS["ccgqa_backward_16k"]
+    inp = make_inputs(w)
+    layer = cca.CCALayer(w.E, w.C, w.Hq, w.Hkv, w.capacity, w.kq, w.kk, w.s_v, w.flags,
+                         w.rope_base, w.dtype)
+    dt = torch.bfloat16
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt)
+    wts = {k: dev(inp[k]) for k in ("w_q", "w_k", "w_v", "w_o", "conv_q", "conv_k")}
+    x, dy = dev(inp["x"]), dev(inp["dy"])
+    saved = torch.empty(layer.saved_bytes(w.B, w.S), dtype=torch.uint8, device="cuda")
+    layer.forward_prefill(wts, x, saved=saved)
+    grads = {"dx": torch.empty_like(x)}
+    for n in ("w_q", "w_k", "w_v", "w_o", "conv_q", "conv_k"):
+        grads["d" + n] = torch.empty(wts[n].shape, dtype=torch.float32, device="cuda")
+    ws = layer.workspace(cca.CCA_OP_BACKWARD, w.B, w.S)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        cca.cca_backward(layer.handle, wts, x, dy, saved, w.B, w.S, grads, ws, stream)
+
+    steps = max(1, args.bwd_steps)
+    sec = _time_loop(torch, step, steps, 1)
+    cca.cca_profile_enable(layer.handle, True)
+    _time_loop(torch, step, 1, 0)
+    prof = cca.cca_profile_read(layer.handle)
+    cca.cca_profile_enable(layer.handle, False)
+    fl = backward_flops(w)
+    total = sum(fl.values())
+    kernels = {k: {"avg_ms": v[1] / max(v[0], 1), "launches": v[0]} for k, v in prof.items()}
+    layer.close()
+    return {
+        "workload": f"ccgqa_backward_16k: B={w.B}, S={w.S}, E={w.E}, Hq={w.Hq}, Hkv={w.Hkv}, "
+                    f"d={w.d}, bf16 storage, fp32 accumulation",
+        "tokens_per_s": w.B * w.S / sec,
+        "ms_per_step": sec * 1e3,
+        "flops_per_step": total,
+        "flops_note": "attention backward as 5 causal matmuls (S recompute, dP, dV, dQ, dK) + "
+                      "4 projection GEMM gradients + conv tap and input gradients",
+        "TFLOPs": total / sec / 1e12,
+        "frac_of_bf16_peak": total / sec / 1e12 / PEAK_BF16_TFLOPS,
+        "kernels": kernels,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rows", default="prefill",
-                    help="comma list: prefill (headline), decode, backward")
+    ap.add_argument("--rows", default="prefill,decode,backward",
+                    help="comma list: prefill (headline, always run), decode, backward")
+    ap.add_argument("--bwd-steps", type=int, default=3, help="timed backward steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (steps times), the "
@@ -184,6 +329,10 @@ def main():
         "kernels": kernels,
     }
     rows = [r.strip() for r in args.rows.split(",") if r.strip()]
+    if "decode" in rows:
+        out["decode"] = bench_decode(args, torch, cca)
+    if "backward" in rows:
+        out["backward"] = bench_backward(args, torch, cca)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = time_oracle_sample(w, inp)
     print(json.dumps(out), flush=True)

@@ -1,7 +1,203 @@
-// placeholder decode attention: routes to the generic kernel
+// cca_decode, attention part: one new token per sequence attends over the
+// compressed latent KV cache (CCA-es §2.C "CCGQA": the smaller cache speeds up
+// decoding; CCA-fr §4 "Décodage").  The step streams the K and V caches once,
+// so it is bound by HBM bandwidth.
+//
+// Split over keys (flash-decoding): work-group (chunk, KV head g, sequence b)
+// takes keys [512 chunk, 512 chunk + 512) of that sequence's cache, up to its
+// position, and serves all G query heads that read KV head g, so each cache
+// byte is read once per step.
+//   1. S = Q K^T on MFMA: A = the G queries (rows, padded to 32 with zeros,
+//      scaled to log2 units), B = K^T straight from global memory (lane = key,
+//      16 bytes of its row per load); 4 waves x 4 blocks of 32 keys.
+//   2. The chunk's row max m and sum l of p = exp2(s - m) (scores in LDS).
+//   3. O_chunk = P V on the vector ALU: lane = 2 channels, one coalesced
+//      256-byte row of V per wave load, p broadcast from LDS.
+// Partials (O_chunk, m, l) go to the workspace; a second kernel merges the
+// chunks of each (sequence, query head) and writes O in bf16.
+// bf16 storage, d = 128; fp32 accumulation and softmax.
 #include "cca_internal.h"
+
 namespace cca {
-int decode_nsplit(const Dims&, int) { return 1; }
-size_t decode_part_floats(const Dims&, int) { return 0; }
-hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s) { return launch_attn_fwd(a, s); }
+namespace {
+
+constexpr int D = 128;
+constexpr int CK = 512;          // keys per work-group
+constexpr int NW = 4;            // waves per work-group
+constexpr int PSTRIDE = D + 2;   // floats per partial: O[0..D), m, l
+
+bool fast_decode(const Dims& dm) { return dm.bf16 && dm.d == D && dm.G <= kMaxGroup; }
+
+__global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) float ps[CK][kMaxGroup];   // scores, then p
+  __shared__ float opart[NW][kMaxGroup][D];
+  __shared__ float stat[kMaxGroup][2];                             // m, l per query
+
+  const Dims& dm = a.dm;
+  const int G = dm.G;
+  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int nsplit = gridDim.x;
+  const int nkeys = a.pos.p[b] + 1;
+  const int k0 = chunk * CK;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  // partial of (b, query head g*G + q, chunk): part[((b*Hq + g*G + q)*nsplit + chunk)*PSTRIDE]
+  float* part = a.part + ((long)(b * dm.Hq + g * G) * nsplit + chunk) * PSTRIDE;
+  if (k0 >= nkeys) {                         // chunk past this sequence's position
+    if (threadIdx.x < G) {
+      part[(long)threadIdx.x * nsplit * PSTRIDE + D] = -INFINITY;
+      part[(long)threadIdx.x * nsplit * PSTRIDE + D + 1] = 0.0f;
+    }
+    return;
+  }
+  const int kend = min(nkeys, k0 + CK);
+  const bf16* kb = reinterpret_cast<const bf16*>(a.k) + (long)b * a.kv_bs + (long)g * a.kv_hs;
+  const bf16* vb = reinterpret_cast<const bf16*>(a.v) + (long)b * a.kv_bs + (long)g * a.kv_hs;
+
+  // ---- 1. scores.  A operand: lane (l32 = query row, hi) holds channels
+  // 16 ks + 8 hi + 0..7 of query g*G + l32 (zero rows past G).
+  const float scale = 1.44269504088896340736f / sqrtf((float)D);
+  bf16x8 qf[8];
+  {
+    const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + ((long)b * dm.Hq + g * G + l32) * D;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (bf16)0.0f;
+      if (l32 < G) v = *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + hi * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)((float)v[e] * scale);
+    }
+  }
+  for (int blk = wave; blk < CK / 32; blk += NW) {
+    const int key = k0 + blk * 32 + l32;
+    const bool valid = key < kend;
+    bf16x8 kf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (valid) {
+        kf[ks] = *reinterpret_cast<const bf16x8*>(kb + (long)key * D + ks * 16 + hi * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kf[ks][e] = (bf16)0.0f;
+      }
+    }
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[ks], acc, 0, 0, 0);
+    // D[query][key]: lane holds key column l32, query rows 8*(r/4) + 4*hi + r%4
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int q = 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (q < G) ps[blk * 32 + l32][q] = valid ? acc[r] : -INFINITY;
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. max and sum over the chunk, one wave per query (G <= 8 queries)
+  for (int q = wave; q < G; q += NW) {
+    float m = -INFINITY;
+    for (int i = lane; i < CK; i += 64) m = fmaxf(m, ps[i][q]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float l = 0.0f;
+    for (int i = lane; i < CK; i += 64) {
+      const float p = __builtin_amdgcn_exp2f(ps[i][q] - m);   // masked keys: 0
+      ps[i][q] = p;
+      l += p;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+    if (lane == 0) {
+      stat[q][0] = m;
+      stat[q][1] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. O_chunk = P V: wave w takes keys w*128 .. w*128+127 of the chunk,
+  // lane the channels 2 lane, 2 lane + 1.
+  float o[kMaxGroup][2];
+#pragma unroll
+  for (int q = 0; q < kMaxGroup; ++q) o[q][0] = o[q][1] = 0.0f;
+  const int i0 = wave * (CK / NW);
+  const int i1 = min(i0 + CK / NW, kend - k0);
+  const bf16* vrow = vb + (long)k0 * D + 2 * lane;
+#pragma unroll 8
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(vrow + (long)i * D);
+    const float v0 = __uint_as_float(u << 16), v1 = __uint_as_float(u & 0xffff0000u);
+    const f32x4 pa = *reinterpret_cast<const f32x4*>(&ps[i][0]);
+    const f32x4 pb = *reinterpret_cast<const f32x4*>(&ps[i][4]);
+#pragma unroll
+    for (int q = 0; q < kMaxGroup; ++q) {
+      if (q < G) {
+        const float p = q < 4 ? pa[q] : pb[q - 4];
+        o[q][0] = fmaf(p, v0, o[q][0]);
+        o[q][1] = fmaf(p, v1, o[q][1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kMaxGroup; ++q)
+    if (q < G) {
+      opart[wave][q][2 * lane] = o[q][0];
+      opart[wave][q][2 * lane + 1] = o[q][1];
+    }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * D; e += 256) {
+    const int q = e / D, c = e % D;
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum += opart[w][q][c];
+    part[(long)q * nsplit * PSTRIDE + c] = sum;
+  }
+  if (threadIdx.x < G) {
+    part[(long)threadIdx.x * nsplit * PSTRIDE + D] = stat[threadIdx.x][0];
+    part[(long)threadIdx.x * nsplit * PSTRIDE + D + 1] = stat[threadIdx.x][1];
+  }
+}
+
+// Merge of the chunk partials of (sequence b, query head h): one thread per
+// channel.  Chunk 0 always holds key 0, so the merged max is finite.
+__global__ __launch_bounds__(D) void attn_decode_merge_kernel(AttnArgs a) {
+  const Dims& dm = a.dm;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int nsplit = a.nsplit;
+  const float* part = a.part + (long)(b * dm.Hq + h) * nsplit * PSTRIDE;
+  float m = -INFINITY;
+  for (int c = 0; c < nsplit; ++c) m = fmaxf(m, part[(long)c * PSTRIDE + D]);
+  float l = 0.0f, o = 0.0f;
+  for (int c = 0; c < nsplit; ++c) {
+    const float mc = part[(long)c * PSTRIDE + D];
+    if (mc == -INFINITY) continue;
+    const float w = __builtin_amdgcn_exp2f(mc - m);
+    l = fmaf(part[(long)c * PSTRIDE + D + 1], w, l);
+    o = fmaf(part[(long)c * PSTRIDE + threadIdx.x], w, o);
+  }
+  reinterpret_cast<bf16*>(a.o)[((long)b * dm.Hq + h) * D + threadIdx.x] = (bf16)(o / l);
+}
+
+}  // namespace
+
+int decode_nsplit(const Dims& dm, int) {
+  return fast_decode(dm) ? (dm.max_seq_len + CK - 1) / CK : 1;
+}
+
+size_t decode_part_floats(const Dims& dm, int B) {
+  return fast_decode(dm) ? (size_t)B * dm.Hq * decode_nsplit(dm, B) * PSTRIDE : 0;
+}
+
+hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s) {
+  if (!fast_decode(a.dm)) return launch_attn_fwd(a, s);
+  if (a.part == nullptr || a.nsplit != decode_nsplit(a.dm, a.B)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_decode_split_kernel, dim3(a.nsplit, a.dm.Hkv, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_decode_merge_kernel, dim3(a.dm.Hq, a.B), dim3(D), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace cca
