@@ -43,6 +43,28 @@ def prefill_flops(w) -> dict:
     }
 
 
+def attention_traffic_bytes():
+    """HBM bytes per attention launch from the committed rocprofv3 PMC record
+    (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the counter
+    reads for a plain copy of known size), or None when the attention kernel's
+    source has changed since the counters were taken."""
+    import hashlib
+    rec_path = os.path.join(ROOT, "profiles", "attn_prefill_16k_traffic.txt")
+    src_path = os.path.join(ROOT, "compressed_latent_attention_amd", "csrc", "attn_mfma.hip")
+    try:
+        rec = {}
+        for line in open(rec_path):
+            if line.strip() and not line.startswith("#"):
+                k, v = line.split()[:2]
+                rec[k] = v
+        if hashlib.sha256(open(src_path, "rb").read()).hexdigest() != rec["source_sha256"]:
+            return None
+        return (float(rec["fetch_kib"]) * 1024 * float(rec["fetch_scale"]) +
+                float(rec["write_kib"]) * 1024 * float(rec["write_scale"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def time_oracle_sample(w, inp, n_rows=256):
     """The oracle's forward on the full sequence for every linear step, and
     attention plus the output projection for n_rows query rows spread evenly
@@ -324,7 +346,7 @@ def main():
         "layer_frac_of_bf16_peak": total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "kernel": "attn", "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": attention_traffic_bytes(),
                      "flops_per_launch": fl["attn"], "avg_launch_ms": attn_ms},
         "kernels": kernels,
     }
