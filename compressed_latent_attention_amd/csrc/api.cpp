@@ -112,7 +112,7 @@ DecodeLayout decode_layout(const Dims& dm, long B) {
 }
 
 struct BwdLayout {
-  size_t dO, Dsum, dq, dk, dv, dqkv, part, scratch, total;
+  size_t dO, Dsum, dq, dk, dv, dqkv, part, scratch, trans, total;
 };
 
 BwdLayout bwd_layout(const Dims& dm, long B, long S) {
@@ -127,6 +127,7 @@ BwdLayout bwd_layout(const Dims& dm, long B, long S) {
   L.dqkv = o;    o = align256(o + (size_t)(B * S * dm.nqkv) * es);
   L.part = o;    o = align256(o + mix_bwd_part_floats(dm, (int)B, (int)S) * 4);
   L.scratch = o; o = align256(o + mix_bwd_scratch_floats(dm, (int)B, (int)S) * 4);
+  L.trans = o;   o = align256(o + attn_bwd_transpose_bytes(dm, (int)B, (int)S));
   L.total = o;
   return L;
 }
@@ -498,6 +499,15 @@ cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, cons
     ab.dm = dm; ab.B = B; ab.S = S;
     ab.q = qr; ab.k = kr; ab.v = vs; ab.o32 = o32; ab.dO = dO; ab.lse = lse; ab.Dsum = Dsum;
     ab.dq = dq; ab.dk = dk; ab.dv = dv;
+    {
+      // transposed copies for the MFMA path: Q''^T | K''^T | dO^T, each 256-byte aligned
+      const long sp = pad64(S);
+      char* t = wb + L.trans;
+      ab.s_pad = (int)sp;
+      ab.qT = t;
+      ab.kT = t + align256((size_t)B * dm.nq * sp * esize(dm));
+      ab.dOT = (char*)ab.kT + align256((size_t)B * dm.nk * sp * esize(dm));
+    }
     CCA_TRY_HIP(timed(h, "bwd_attn", s, [&] { return launch_attn_bwd(ab, s); }));
 
     MixBwdArgs mb{};

@@ -24,19 +24,24 @@
 //                  Accumulator row i of each 16-row group holds key
 //                  8*((i/4)%2) ... permuted so that the 8 scores a lane passes
 //                  to P V are 8 consecutive keys;
-//   O^T += V^T P^T A = V^T rows (LDS), B = P^T straight from the S^T
-//                  accumulators rounded to bf16.
+//   O^T += V^T P^T v_mfma_f32_32x32x16_f16 with A = V^T rows (LDS, the fp16
+//                  copy of V' the mix writes), B = P^T straight from the S^T
+//                  accumulators rounded to fp16: 11 significant bits keep the
+//                  saved O accurate enough for the backward's rowsum(dO * O),
+//                  which the softmax gradient amplifies.
 // Tiles move from global memory to LDS with buffer loads that write LDS
 // directly (16 bytes per lane), so no registers stage them.  LDS rows are
 // unpadded; 16-byte chunks are XOR-swizzled by row so that the MFMA operand
 // reads are free of bank conflicts.
-// Softmax in base 2: Q is scaled by log2(e)/sqrt(d) as it is loaded, and each
-// S^T chain starts from -m (m = the row's exponent offset), so the MFMA result
-// is already the exp2 argument.  The offset is only raised when a row's max
-// grows by more than 8 (a factor 2^8 in probability: lazy rescaling); until
-// then probabilities stay below 256, which fp32 and bf16 hold as well as any
-// other value, and the tile needs no rescale of O and no subtraction.  fp32
-// accumulators throughout.
+// Softmax in base 2: each S^T chain starts from -m (m = the row's running
+// offset, in raw score units), so the MFMA result minus the offset only needs
+// one multiply by log2(e)/sqrt(d) before exp2.  Q stays exactly the stored
+// bf16 Q'' (scaling it before the MFMA would round it a second time, and the
+// saved LSE would then disagree with the scores the backward recomputes).  The
+// offset is only raised when a row's max grows by more than 2^8 in
+// probability (lazy rescaling); until then probabilities stay below 256, which
+// fp32 and bf16 hold as well as any other value, and the tile needs no
+// rescale of O and no subtraction.  fp32 accumulators throughout.
 #include "cca_internal.h"
 
 namespace cca {
@@ -48,6 +53,7 @@ constexpr int BN = 64;         // keys per tile
 constexpr int KT_BYTES = BN * D * 2;      // K tile: 64 rows of 256 B
 constexpr int VT_BYTES = D * BN * 2;      // V^T tile: 128 rows of 128 B
 constexpr int HALF_BYTES = 2 * (KT_BYTES + VT_BYTES);   // one half's two K + V^T buffers
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr float kLazyLog2 = 8.0f;                        // rescale when the max grows by > 2^8
 constexpr int MERGE_STRIDE = 66;                         // floats per lane: 64 of O^T, m, l
 
@@ -113,7 +119,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // the current tile (when qk, two chains).  krow: the K row this lane's
 // accumulator column block reads, l32 with bits 2 and 3 swapped.
 __device__ __forceinline__ void mfma_phase(bool pv, bool qk, f32x16 (&oacc)[4],
-                                           const bf16x8 (&pf)[4], const char* vs_,
+                                           const f16x8 (&pf)[4], const char* vs_,
                                            f32x16 (&sacc)[2], const char* ks_,
                                            const bf16x8 (&qf)[8], const f32x16& minit, int l32,
                                            int krow, int hi) {
@@ -122,9 +128,9 @@ __device__ __forceinline__ void mfma_phase(bool pv, bool qk, f32x16 (&oacc)[4],
     for (int pk = 0; pk < 4; ++pk)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const bf16x8 vf =
-            *reinterpret_cast<const bf16x8*>(vs_ + v_off(mb * 32 + l32, 2 * pk + hi));
-        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pk], oacc[mb], 0, 0, 0);
+        const f16x8 vf =
+            *reinterpret_cast<const f16x8*>(vs_ + v_off(mb * 32 + l32, 2 * pk + hi));
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[pk], oacc[mb], 0, 0, 0);
       }
   }
   if (qk) {
@@ -188,8 +194,8 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
   const int nvalid = kt_max >= half ? (kt_max - half) / 2 + 1 : 0;
   const float scale = 1.44269504088896340736f / sqrtf((float)D);
 
-  // Q^T fragments, scaled to log2 units, first: the prologue's waits then
-  // cover them, so no later wait stalls on them.
+  // Q^T fragments first: the prologue's waits then cover them, so no later
+  // wait stalls on them.
   // Lane holds query my_q, channels 16*ks + 8*hi + 0..7.
   bf16x8 qf[8];
 #pragma unroll
@@ -201,10 +207,6 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
       for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)0.0f;
     }
   }
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)((float)qf[ks][e] * scale);
 
   // prologue: K and V of tile 0 and K of tile 1 into LDS.  Tile 0 is loaded
   // unconditionally (a one-tile block has half 1 load key tile 0, which it
@@ -222,12 +224,13 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
-  float m_use = 0.0f, l_run = 0.0f;    // exponent offset (log2 units), row sum
+  float m_use = 0.0f, l_run = 0.0f;    // exponent offset (raw score units), row sum
+  const float lazy_raw = kLazyLog2 / scale;
   f32x16 minit;                        // -m_use in every register
 #pragma unroll
   for (int r = 0; r < 16; ++r) minit[r] = 0.0f;
   f32x16 sacc[2];                      // S^T - m of the tile between its two phases
-  bf16x8 pf[4];                        // P^T of the tile between softmax and P V
+  f16x8 pf[4];                         // P^T (fp16) of the tile between softmax and P V
   __syncthreads();
 
   // Phases: each half runs M0 V0 M1 V1 ... M(niter) V(niter), where M(j) = the
@@ -268,10 +271,10 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
       // when any row of the wave needs it, but every other row shifts by an
       // exact 0, so a row's arithmetic never depends on another row's scores
       // (an earlier row stays bit-identical whatever later tokens hold).
-      const bool grow = j == 0 || mt > kLazyLog2;
+      const bool grow = j == 0 || mt > lazy_raw;
       if (__any(grow)) {
         const float delta = grow ? mt : 0.0f;
-        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        const float alpha = __builtin_amdgcn_exp2f(-delta * scale);
         m_use += delta;
         l_run *= alpha;
 #pragma unroll
@@ -290,9 +293,9 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
       for (int pk = 0; pk < 4; ++pk)
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8) {
-          const float pv = __builtin_amdgcn_exp2f(sacc[pk >> 1][8 * (pk & 1) + s8]);
+          const float pv = __builtin_amdgcn_exp2f(sacc[pk >> 1][8 * (pk & 1) + s8] * scale);
           ls += pv;
-          pf[pk][s8] = (bf16)pv;
+          pf[pk][s8] = (_Float16)pv;
         }
       l_run += xhalf_sum(ls);
     }
@@ -328,8 +331,8 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
     // half 0 always took tile 0, so its offset is finite.
     const float m_b = mg[64 * 64], l_b = mg[65 * 64];
     const float mn = fmaxf(m_use, m_b);
-    const float wa = __builtin_amdgcn_exp2f(m_use - mn);
-    const float wb = __builtin_amdgcn_exp2f(m_b - mn);
+    const float wa = __builtin_amdgcn_exp2f((m_use - mn) * scale);
+    const float wb = __builtin_amdgcn_exp2f((m_b - mn) * scale);
     l_run = l_run * wa + l_b * wb;
     m_use = mn;
 #pragma unroll
@@ -358,10 +361,10 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
         *reinterpret_cast<bf16x4*>(orow + c) = v4;
         if (orow32) *reinterpret_cast<f32x4*>(orow32 + c) = f4;
       }
-    // natural-log LSE of the unscaled scores: (m + log2 l) ln 2
+    // natural-log LSE of the scaled scores: (m log2(e)/sqrt(d) + log2 l) ln 2
     if (hi == 0 && a.lse)
       a.lse[(long)(b * dm.Hq + h) * S + my_q] =
-          (m_use + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f;
+          (m_use * scale + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f;
   }
 }
 

@@ -150,8 +150,17 @@ struct AttnBwdArgs {
   float* dq;         // dQ'' [B,Hq,S,d] fp32
   float* dk;         // dK'' [B,Hkv,S,d] fp32
   float* dv;         // dV'  [B,Hkv,S,d] fp32
+  // MFMA path workspace (bf16 storage, d = 128): fp16 transposed copies, rows
+  // padded to s_pad
+  void* qT;          // Q''^T [B,Hq,d,s_pad] fp16
+  void* kT;          // K''^T [B,Hkv,d,s_pad]
+  void* dOT;         // dO^T  [B,Hq,d,s_pad]
+  int s_pad;         // S rounded up to a multiple of 64
 };
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
+// Bytes of the transposed copies the MFMA attention backward needs (0 when
+// the config takes the generic path).
+size_t attn_bwd_transpose_bytes(const Dims& dm, int B, int S);
 
 struct MixBwdArgs {
   Dims dm;

@@ -198,19 +198,25 @@ void mix_fwd_mfma_kernel(MixArgs a) {
     }
   }
   if (a.vt_out) {
-    bf16* vt = reinterpret_cast<bf16*>(a.vt_out) + (long)(b * dm.Hkv + g) * D * a.s_pad;
+    // V'^T feeds only the attention's P V product, which runs in fp16 so that P
+    // keeps 11 significant bits.  It holds the stored bf16 V' values, converted
+    // exactly, so the forward's O and the backward (which reads the bf16 V')
+    // see the same V'.
+    _Float16* vt = reinterpret_cast<_Float16*>(a.vt_out) + (long)(b * dm.Hkv + g) * D * a.s_pad;
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
     for (int e = threadIdx.x; e < D * (TW / 8); e += 256) {
       const int c = e % D, m = e / D;
       const int t = t0 + 8 * m;
       if (t >= a.s_pad) continue;
       const int row_off = c >= first_shift ? 0 : 1;
-      bf16x8 pk;
+      f16x8 pk;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         // tokens at or past S are zero: the padding of V'^T up to s_pad
-        pk[i] = (bf16)(t + i < S ? uq[(8 * m + i + row_off) * ULD + c] : 0.0f);
+        const bf16 v = (bf16)(t + i < S ? uq[(8 * m + i + row_off) * ULD + c] : 0.0f);
+        pk[i] = (_Float16)(float)v;
       }
-      *reinterpret_cast<bf16x8*>(vt + (long)c * a.s_pad + t) = pk;
+      *reinterpret_cast<f16x8*>(vt + (long)c * a.s_pad + t) = pk;
     }
   }
 }

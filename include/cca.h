@@ -131,10 +131,12 @@ size_t cca_workspace_bytes(const cca_handle* h, int op, int32_t B, int32_t S);
  *   o       [B, S, Hq*d]        dt    (attention output before W_o)
  *   lse     [B, Hq, S]          fp32  (natural log of each softmax denominator)
  *   o_f32   [B, S, Hq*d]        fp32  (the same output before rounding to dt)
- *   v_t     [B, Hkv, d, S64]    dt    (V' transposed, S64 = S rounded up to 64;
- *                                      written only on the bf16 d = 128 path)
- * The backward forms rowsum(dO * O) from o_f32: with near-one-hot attention
- * rows that sum cancels, and O rounded to bf16 would cost ~2% in dQ and dK.
+ *   v_t     [B, Hkv, d, S64]    fp16  (V' transposed, S64 = S rounded up to 64;
+ *                                      written only on the bf16 d = 128 path,
+ *                                      holding the bf16 V' values exactly)
+ * The backward forms rowsum(dO * O) from o_f32, and the softmax gradient
+ * amplifies any error in it (O rounded to bf16 would cost ~3% in dQ and dK;
+ * the forward therefore multiplies P, rounded to fp16, by this fp16 V'^T).
  * cca_saved_offsets writes the 8 byte offsets into offsets[0..7]. */
 size_t cca_saved_bytes(const cca_handle* h, int32_t B, int32_t S);
 cca_status cca_saved_offsets(const cca_handle* h, int32_t B, int32_t S, size_t offsets[8]);
