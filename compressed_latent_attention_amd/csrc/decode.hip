@@ -11,8 +11,8 @@
 //      scaled to log2 units), B = K^T straight from global memory (lane = key,
 //      16 bytes of its row per load); 4 waves x 4 blocks of 32 keys.
 //   2. The chunk's row max m and sum l of p = exp2(s - m) (scores in LDS).
-//   3. O_chunk = P V on the vector ALU: lane = 2 channels, one coalesced
-//      256-byte row of V per wave load, p broadcast from LDS.
+//   3. O_chunk = P V on the vector ALU: lane = 8 channels of one of 4 keys,
+//      so a wave load covers four 256-byte V rows; p broadcast from LDS.
 // Partials (O_chunk, m, l) go to the workspace; a second kernel merges the
 // chunks of each (sequence, query head) and writes O in bf16.
 // bf16 storage, d = 128; fp32 accumulation and softmax.
@@ -26,7 +26,11 @@ constexpr int CK = 512;          // keys per work-group
 constexpr int NW = 4;            // waves per work-group
 constexpr int PSTRIDE = D + 2;   // floats per partial: O[0..D), m, l
 
-bool fast_decode(const Dims& dm) { return dm.bf16 && dm.d == D && dm.G <= kMaxGroup; }
+constexpr int MAX_SPLIT = 1024;  // chunks per sequence the merge kernel holds: caches up to 512K
+
+bool fast_decode(const Dims& dm) {
+  return dm.bf16 && dm.d == D && dm.G <= kMaxGroup && dm.max_seq_len <= MAX_SPLIT * CK;
+}
 
 __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float ps[CK][kMaxGroup];   // scores, then p
@@ -119,34 +123,43 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // ---- 3. O_chunk = P V: wave w takes keys w*128 .. w*128+127 of the chunk,
-  // lane the channels 2 lane, 2 lane + 1.
-  float o[kMaxGroup][2];
+  // ---- 3. O_chunk = P V: wave w takes keys w*128 .. w*128+127 of the chunk;
+  // lane = (key slot L / 16, channels 8 (L % 16) .. + 7), so one wave load
+  // covers 4 whole 256-byte V rows.  The 4 key slots are summed with two
+  // shuffles, the 4 waves through LDS.
+  const int slot = lane >> 4, cc = (lane & 15) * 8;
+  float o[kMaxGroup][8];
 #pragma unroll
-  for (int q = 0; q < kMaxGroup; ++q) o[q][0] = o[q][1] = 0.0f;
+  for (int q = 0; q < kMaxGroup; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[q][e] = 0.0f;
   const int i0 = wave * (CK / NW);
   const int i1 = min(i0 + CK / NW, kend - k0);
-  const bf16* vrow = vb + (long)k0 * D + 2 * lane;
-#pragma unroll 8
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t u = *reinterpret_cast<const uint32_t*>(vrow + (long)i * D);
-    const float v0 = __uint_as_float(u << 16), v1 = __uint_as_float(u & 0xffff0000u);
+  const bf16* vbase = vb + (long)k0 * D + cc;
+#pragma unroll 4
+  for (int i = i0 + slot; i < i1; i += 4) {
+    const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(vbase + (long)i * D);
     const f32x4 pa = *reinterpret_cast<const f32x4*>(&ps[i][0]);
     const f32x4 pb = *reinterpret_cast<const f32x4*>(&ps[i][4]);
 #pragma unroll
     for (int q = 0; q < kMaxGroup; ++q) {
       if (q < G) {
         const float p = q < 4 ? pa[q] : pb[q - 4];
-        o[q][0] = fmaf(p, v0, o[q][0]);
-        o[q][1] = fmaf(p, v1, o[q][1]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[q][e] = fmaf(p, (float)v8[e], o[q][e]);
       }
     }
   }
 #pragma unroll
   for (int q = 0; q < kMaxGroup; ++q)
     if (q < G) {
-      opart[wave][q][2 * lane] = o[q][0];
-      opart[wave][q][2 * lane + 1] = o[q][1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = o[q][e];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (slot == 0) opart[wave][q][cc + e] = v;
+      }
     }
   __syncthreads();
   for (int e = threadIdx.x; e < G * D; e += 256) {
@@ -162,24 +175,46 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
   }
 }
 
-// Merge of the chunk partials of (sequence b, query head h): one thread per
-// channel.  Chunk 0 always holds key 0, so the merged max is finite.
+// Merge of the chunk partials of (sequence b, query head h): the chunk maxima
+// and weights in parallel (one thread per chunk, through LDS), then one thread
+// per channel sums its weighted partial O over the chunks.  Chunk 0 always
+// holds key 0, so the merged max is finite and the weight sum is >= 1.
 __global__ __launch_bounds__(D) void attn_decode_merge_kernel(AttnArgs a) {
+  __shared__ float wgt[MAX_SPLIT];
+  __shared__ float red[D / 64][2];
   const Dims& dm = a.dm;
   const int h = blockIdx.x, b = blockIdx.y;
   const int nsplit = a.nsplit;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const float* part = a.part + (long)(b * dm.Hq + h) * nsplit * PSTRIDE;
   float m = -INFINITY;
-  for (int c = 0; c < nsplit; ++c) m = fmaxf(m, part[(long)c * PSTRIDE + D]);
-  float l = 0.0f, o = 0.0f;
-  for (int c = 0; c < nsplit; ++c) {
+  for (int c = t; c < nsplit; c += D) m = fmaxf(m, part[(long)c * PSTRIDE + D]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) red[wave][0] = m;
+  __syncthreads();
+  m = red[0][0];
+#pragma unroll
+  for (int w = 1; w < D / 64; ++w) m = fmaxf(m, red[w][0]);
+  float l = 0.0f;
+  for (int c = t; c < nsplit; c += D) {
     const float mc = part[(long)c * PSTRIDE + D];
-    if (mc == -INFINITY) continue;
-    const float w = __builtin_amdgcn_exp2f(mc - m);
-    l = fmaf(part[(long)c * PSTRIDE + D + 1], w, l);
-    o = fmaf(part[(long)c * PSTRIDE + threadIdx.x], w, o);
+    const float wc = mc == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mc - m);
+    wgt[c] = wc;
+    l = fmaf(part[(long)c * PSTRIDE + D + 1], wc, l);
   }
-  reinterpret_cast<bf16*>(a.o)[((long)b * dm.Hq + h) * D + threadIdx.x] = (bf16)(o / l);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+  __syncthreads();
+  if (lane == 0) red[wave][1] = l;
+  __syncthreads();
+  l = red[0][1];
+#pragma unroll
+  for (int w = 1; w < D / 64; ++w) l += red[w][1];
+  float o = 0.0f;
+#pragma unroll 8
+  for (int c = 0; c < nsplit; ++c) o = fmaf(part[(long)c * PSTRIDE + t], wgt[c], o);
+  reinterpret_cast<bf16*>(a.o)[((long)b * dm.Hq + h) * D + t] = (bf16)(o / l);
 }
 
 }  // namespace
@@ -194,7 +229,8 @@ size_t decode_part_floats(const Dims& dm, int B) {
 
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s) {
   if (!fast_decode(a.dm)) return launch_attn_fwd(a, s);
-  if (a.part == nullptr || a.nsplit != decode_nsplit(a.dm, a.B)) return hipErrorInvalidValue;
+  if (a.part == nullptr || a.nsplit != decode_nsplit(a.dm, a.B) || a.nsplit > MAX_SPLIT)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_decode_split_kernel, dim3(a.nsplit, a.dm.Hkv, a.B), dim3(256), 0, s, a);
   hipLaunchKernelGGL(attn_decode_merge_kernel, dim3(a.dm.Hq, a.B), dim3(D), 0, s, a);
   return hipGetLastError();

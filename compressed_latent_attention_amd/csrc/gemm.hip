@@ -251,12 +251,15 @@ hipError_t launch_layout(const GemmArgs& g, bool in_bf16, bool out_f32, hipStrea
 }  // namespace
 
 bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError_t* err);
+bool launch_gemm_nt_small(const GemmArgs& g, bool out_f32, hipStream_t s, hipError_t* err);
 
 hipError_t launch_gemm(const GemmArgs& g, GemmLayout layout, bool in_bf16, bool out_f32,
                        hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   hipError_t err = hipSuccess;
-  if (layout == GemmLayout::NT && in_bf16 && launch_gemm_nt_big(g, out_f32, s, &err)) return err;
+  if (layout == GemmLayout::NT && in_bf16 &&
+      (launch_gemm_nt_big(g, out_f32, s, &err) || launch_gemm_nt_small(g, out_f32, s, &err)))
+    return err;
   switch (layout) {
     case GemmLayout::NT: return launch_layout<true, true>(g, in_bf16, out_f32, s);
     case GemmLayout::NN: return launch_layout<true, false>(g, in_bf16, out_f32, s);

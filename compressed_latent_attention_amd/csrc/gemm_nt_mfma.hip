@@ -185,3 +185,88 @@ bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError
 }
 
 }  // namespace cca
+
+// ------------------------------------------------------------------ small M
+// C = A B^T for few rows of A (the decode step's tokens): work-group = 32
+// output columns x 32 rows; its eight waves split K eight ways, each issuing
+// the global loads of up to eight 16-wide k steps (both fragments, 16 bytes per
+// lane, straight into registers) before their chain of
+// v_mfma_f32_32x32x16_bf16, so one memory round trip covers most of K; the
+// eight partial tiles are summed in LDS in a fixed order.  B's rows may come
+// from up to three segments (the concatenated W_q | W_k | W_v).  Requires
+// K % 128 == 0.
+namespace cca {
+namespace {
+
+constexpr int SW = 8;   // waves per small-M work-group
+
+__device__ __forceinline__ void store_small(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_small(bf16* p, float v) { *p = (bf16)v; }
+
+template <typename OutT>
+__global__ __launch_bounds__(64 * SW) void gemm_nt_small_kernel(GemmArgs g) {
+  __shared__ float part[SW][32][33];
+  const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int m = m0 + l32, n = n0 + l32;
+  // rows past M or N read row 0 (valid memory); their results are never stored
+  const bf16* arow = reinterpret_cast<const bf16*>(g.a) + (long)(m < g.M ? m : 0) * g.lda;
+  const int nn = n < g.N ? n : 0;
+  int s = 0;
+  if (g.b_nseg > 1 && nn >= g.b_start[1]) s = 1;
+  if (g.b_nseg > 2 && nn >= g.b_start[2]) s = 2;
+  const bf16* brow = reinterpret_cast<const bf16*>(g.b_ptr[s]) + (long)(nn - g.b_start[s]) * g.ldb;
+  const int kw = g.K / SW, k0 = wave * kw;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  for (int kb = k0; kb < k0 + kw; kb += 128) {
+    bf16x8 af[8], bfr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = kb + 16 * i + 8 * hi;
+      if (kb + 16 * i < k0 + kw) {
+        af[i] = *reinterpret_cast<const bf16x8*>(arow + k);
+        bfr[i] = *reinterpret_cast<const bf16x8*>(brow + k);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (kb + 16 * i < k0 + kw)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[i], acc, 0, 0, 0);
+  }
+  // D layout: lane holds column l32 (n), rows 8*(r/4) + 4*hi + r%4 (m)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part[wave][8 * (r >> 2) + 4 * hi + (r & 3)][l32] = acc[r];
+  __syncthreads();
+  for (int e = threadIdx.x; e < 32 * 32; e += 64 * SW) {
+    const int mi = e / 32, ni = e % 32;
+    if (m0 + mi >= g.M || n0 + ni >= g.N) continue;
+    float v = part[0][mi][ni];
+#pragma unroll
+    for (int w = 1; w < SW; ++w) v += part[w][mi][ni];
+    int cs = 0;
+    if (g.c_nseg > 1 && m0 + mi >= g.c_start[1]) cs = 1;
+    if (g.c_nseg > 2 && m0 + mi >= g.c_start[2]) cs = 2;
+    OutT* crow = reinterpret_cast<OutT*>(g.c_ptr[cs]) + (long)(m0 + mi - g.c_start[cs]) * g.ldc;
+    store_small(crow + n0 + ni, v);
+  }
+}
+
+}  // namespace
+
+// Launches the small-M kernel for M <= 64 rows (decode); false otherwise.
+bool launch_gemm_nt_small(const GemmArgs& g, bool out_f32, hipStream_t s, hipError_t* err) {
+  if (g.M > 64 || g.K % (16 * SW) != 0 || g.K <= 0 || g.lda % 8 != 0 || g.ldb % 8 != 0)
+    return false;
+  dim3 grid((g.N + 31) / 32, (g.M + 31) / 32);
+  if (out_f32)
+    hipLaunchKernelGGL(gemm_nt_small_kernel<float>, grid, dim3(64 * SW), 0, s, g);
+  else
+    hipLaunchKernelGGL(gemm_nt_small_kernel<bf16>, grid, dim3(64 * SW), 0, s, g);
+  *err = hipGetLastError();
+  return true;
+}
+
+}  // namespace cca

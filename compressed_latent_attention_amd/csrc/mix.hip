@@ -176,19 +176,42 @@ __global__ __launch_bounds__(256) void mix_decode_kernel(MixDecodeArgs a) {
   for (int c = threadIdx.x; c < d; c += blockDim.x)
     vprev[c] = ldf<T>(a.state, srow + nqpart + nkpart + g * d + c);
   __syncthreads();
-  for (int i = threadIdx.x; i < NH * d; i += blockDim.x) {
-    const int hh = i / d, c = i % d;
-    const bool isq = hh < G;
-    const int k = isq ? dm.kq : dm.kk;
-    const long tap0 = isq ? (long)(g * G + hh) * dm.kq * d * d : (long)g * dm.kk * d * d;
-    const void* taps = isq ? a.conv_q : a.conv_k;
-    float s = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const float* src = u + (j * NH + hh) * d;
-      const long base = tap0 + ((long)j * d + c) * d;
-      for (int e = 0; e < d; ++e) s += ldf<T>(taps, base + e) * src[e];
+  // conv: each output channel (head hh, channel c) is a dot product of k tap
+  // rows with the lags; 16 lanes share one output, each taking every 16th
+  // group of 8 input channels (16-byte tap loads when d % 8 == 0), then a
+  // 4-step shuffle sum.
+  {
+    const int sub = threadIdx.x & 15;
+    for (int task = threadIdx.x >> 4; task < NH * d; task += blockDim.x >> 4) {
+      const int hh = task / d, c = task % d;
+      const bool isq = hh < G;
+      const int k = isq ? dm.kq : dm.kk;
+      const long tap0 = isq ? (long)(g * G + hh) * dm.kq * d * d : (long)g * dm.kk * d * d;
+      const T* taps = reinterpret_cast<const T*>(isq ? a.conv_q : a.conv_k);
+      float s = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        const float* src = u + (j * NH + hh) * d;
+        const T* trow = taps + tap0 + ((long)j * d + c) * d;
+        for (int e0 = 8 * sub; e0 < d; e0 += 128) {
+          if (d % 8 == 0) {
+            T tv[8];
+            if (sizeof(T) == 2) {
+              *reinterpret_cast<bf16x8*>(tv) = *reinterpret_cast<const bf16x8*>(trow + e0);
+            } else {
+              *reinterpret_cast<f32x4*>(tv) = *reinterpret_cast<const f32x4*>(trow + e0);
+              *reinterpret_cast<f32x4*>(tv + 4) = *reinterpret_cast<const f32x4*>(trow + e0 + 4);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s = fmaf((float)tv[i], src[e0 + i], s);
+          } else {
+            for (int i = 0; i < 8 && e0 + i < d; ++i) s = fmaf((float)trow[e0 + i], src[e0 + i], s);
+          }
+        }
+      }
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      if (sub == 0) cv[task] = s;
     }
-    cv[i] = s;
   }
   __syncthreads();
   const int half = d / 2;
