@@ -3,6 +3,7 @@
 // No kernel arithmetic lives here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -112,8 +113,15 @@ DecodeLayout decode_layout(const Dims& dm, long B) {
 }
 
 struct BwdLayout {
-  size_t dO, Dsum, dq, dk, dv, dqkv, part, scratch, trans, total;
+  size_t dO, Dsum, dq, dk, dv, dqkv, part, scratch, trans;
+  size_t wT, tA, tB, gpart;   // bf16 backward GEMMs: transposed operands, split-K partials
+  size_t total;
 };
+
+constexpr int kMaxSplit = 16;
+
+// bf16 backward GEMMs run on the NT kernels with transposed operands.
+bool bwd_gemm_nt(const Dims& dm) { return dm.bf16 && dm.E % 64 == 0 && dm.nqkv % 64 == 0; }
 
 BwdLayout bwd_layout(const Dims& dm, long B, long S) {
   const size_t es = esize(dm);
@@ -128,6 +136,15 @@ BwdLayout bwd_layout(const Dims& dm, long B, long S) {
   L.part = o;    o = align256(o + mix_bwd_part_floats(dm, (int)B, (int)S) * 4);
   L.scratch = o; o = align256(o + mix_bwd_scratch_floats(dm, (int)B, (int)S) * 4);
   L.trans = o;   o = align256(o + attn_bwd_transpose_bytes(dm, (int)B, (int)S));
+  L.wT = L.tA = L.tB = L.gpart = o;
+  if (bwd_gemm_nt(dm)) {
+    const size_t Mp = (size_t)pad64(B * S);
+    const size_t wmax = std::max((size_t)dm.nq * dm.E, (size_t)dm.E * dm.nqkv);
+    L.wT = o;    o = align256(o + wmax * 2);
+    L.tA = o;    o = align256(o + (size_t)dm.E * Mp * 2);
+    L.tB = o;    o = align256(o + (size_t)std::max(dm.nq, dm.nqkv) * Mp * 2);
+    L.gpart = o; o = align256(o + (size_t)kMaxSplit * wmax * 4);
+  }
   L.total = o;
   return L;
 }
@@ -489,11 +506,54 @@ cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, cons
     void* dqkv = wb + L.dqkv;
     const int M = B * S;
 
+    const bool nt = bwd_gemm_nt(dm);
+    const int Mp = (int)pad64(M);
+    void* wT = wb + L.wT;
+    void* tA = wb + L.tA;
+    void* tB = wb + L.tB;
+    float* gpart = (float*)(wb + L.gpart);
+    // weight gradient C[Mo x No] (fp32, segments along Mo) = A^T-major operands
+    // at[Mo x Mp] . bt[No x Mp]^T on the NT kernel, split over K when the
+    // output alone cannot fill the chip; partials summed in a fixed order.
+    auto weight_grad = [&](int Mo, int No, const void* at, const void* bt, GemmArgs gout) {
+      GemmArgs gg = gemm_nt(Mo, No, Mp, at, Mp, bt, Mp, gpart, No);
+      const int tiles = ((Mo + 255) / 256) * ((No + 255) / 256);
+      int ks = 1;
+      while (ks < kMaxSplit && tiles * ks < 256 && (Mp / 64) % (2 * ks) == 0) ks *= 2;
+      gg.ksplit = ks;
+      gg.c_split_stride = (long)Mo * No;
+      hipError_t e = hipSuccess;
+      if (ks > 1 && launch_gemm_nt_big(gg, true, s, &e)) {
+        if (e != hipSuccess) return e;
+        float* outs[3] = {(float*)gout.c_ptr[0], (float*)gout.c_ptr[1], (float*)gout.c_ptr[2]};
+        return launch_splitk_reduce(gpart, ks, Mo, No, outs, gout.c_start, gout.c_nseg, gout.ldc,
+                                    s);
+      }
+      gout.a = at; gout.lda = Mp; gout.b_ptr[0] = bt; gout.ldb = Mp; gout.K = Mp;
+      return launch_gemm(gout, GemmLayout::NT, true, true, s);
+    };
+
     // dO = dY W_o ; dW_o = dY^T O
-    GemmArgs g1 = gemm_nt(M, dm.nq, dm.E, dy, dm.E, w->w_o, dm.nq, dO, dm.nq);
-    CCA_TRY_HIP(timed(h, "bwd_proj_up_dx", s, [&] { return launch_gemm(g1, GemmLayout::NN, dm.bf16, false, s); }));
-    GemmArgs g2 = gemm_nt(dm.E, dm.nq, M, dy, dm.E, o, dm.nq, g->dw_o, dm.nq);
-    CCA_TRY_HIP(timed(h, "bwd_proj_up_dw", s, [&] { return launch_gemm(g2, GemmLayout::TN, dm.bf16, true, s); }));
+    if (nt) {
+      CCA_TRY_HIP(timed(h, "bwd_proj_up_dx", s, [&] {
+        hipError_t e = launch_transpose_bf16(w->w_o, dm.nq, dm.E, dm.nq, dm.E, wT, dm.E, s);
+        if (e != hipSuccess) return e;
+        GemmArgs g1 = gemm_nt(M, dm.nq, dm.E, dy, dm.E, wT, dm.E, dO, dm.nq);
+        return launch_gemm(g1, GemmLayout::NT, true, false, s);
+      }));
+      CCA_TRY_HIP(timed(h, "bwd_proj_up_dw", s, [&] {
+        hipError_t e = launch_transpose_bf16(dy, dm.E, M, dm.E, Mp, tA, Mp, s);
+        if (e == hipSuccess) e = launch_transpose_bf16(o, dm.nq, M, dm.nq, Mp, tB, Mp, s);
+        if (e != hipSuccess) return e;
+        GemmArgs gout = gemm_nt(dm.E, dm.nq, Mp, nullptr, 0, nullptr, 0, g->dw_o, dm.nq);
+        return weight_grad(dm.E, dm.nq, tA, tB, gout);
+      }));
+    } else {
+      GemmArgs g1 = gemm_nt(M, dm.nq, dm.E, dy, dm.E, w->w_o, dm.nq, dO, dm.nq);
+      CCA_TRY_HIP(timed(h, "bwd_proj_up_dx", s, [&] { return launch_gemm(g1, GemmLayout::NN, dm.bf16, false, s); }));
+      GemmArgs g2 = gemm_nt(dm.E, dm.nq, M, dy, dm.E, o, dm.nq, g->dw_o, dm.nq);
+      CCA_TRY_HIP(timed(h, "bwd_proj_up_dw", s, [&] { return launch_gemm(g2, GemmLayout::TN, dm.bf16, true, s); }));
+    }
 
     AttnBwdArgs ab{};
     ab.dm = dm; ab.B = B; ab.S = S;
@@ -520,16 +580,37 @@ cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, cons
     CCA_TRY_HIP(timed(h, "bwd_mix", s, [&] { return launch_mix_bwd(mb, s); }));
 
     // dx = dq~ W_q + dk~ W_k + dv~ W_v ; dW_* = d*~^T x
-    GemmArgs g3 = gemm_nt(M, dm.E, dm.nqkv, dqkv, dm.nqkv, w->w_q, dm.E, g->dx, dm.E);
-    g3.b_ptr[1] = w->w_k; g3.b_start[1] = dm.nq;
-    g3.b_ptr[2] = w->w_v; g3.b_start[2] = dm.nq + dm.nk;
-    g3.b_nseg = 3;
-    CCA_TRY_HIP(timed(h, "bwd_proj_down_dx", s, [&] { return launch_gemm(g3, GemmLayout::NN, dm.bf16, false, s); }));
     GemmArgs g4 = gemm_nt(dm.nqkv, dm.E, M, dqkv, dm.nqkv, x, dm.E, g->dw_q, dm.E);
     g4.c_ptr[1] = g->dw_k; g4.c_start[1] = dm.nq;
     g4.c_ptr[2] = g->dw_v; g4.c_start[2] = dm.nq + dm.nk;
     g4.c_nseg = 3;
-    CCA_TRY_HIP(timed(h, "bwd_proj_down_dw", s, [&] { return launch_gemm(g4, GemmLayout::TN, dm.bf16, true, s); }));
+    if (nt) {
+      CCA_TRY_HIP(timed(h, "bwd_proj_down_dx", s, [&] {
+        // [W_q; W_k; W_v]^T [E x nqkv], one segment at a time
+        const void* seg[3] = {w->w_q, w->w_k, w->w_v};
+        const int rows[3] = {dm.nq, dm.nk, dm.nk}, col0[3] = {0, dm.nq, dm.nq + dm.nk};
+        for (int i = 0; i < 3; ++i) {
+          hipError_t e = launch_transpose_bf16(seg[i], dm.E, rows[i], dm.E, rows[i],
+                                               (char*)wT + (size_t)col0[i] * 2, dm.nqkv, s);
+          if (e != hipSuccess) return e;
+        }
+        GemmArgs g3 = gemm_nt(M, dm.E, dm.nqkv, dqkv, dm.nqkv, wT, dm.nqkv, g->dx, dm.E);
+        return launch_gemm(g3, GemmLayout::NT, true, false, s);
+      }));
+      CCA_TRY_HIP(timed(h, "bwd_proj_down_dw", s, [&] {
+        hipError_t e = launch_transpose_bf16(dqkv, dm.nqkv, M, dm.nqkv, Mp, tB, Mp, s);
+        if (e == hipSuccess) e = launch_transpose_bf16(x, dm.E, M, dm.E, Mp, tA, Mp, s);
+        if (e != hipSuccess) return e;
+        return weight_grad(dm.nqkv, dm.E, tB, tA, g4);
+      }));
+    } else {
+      GemmArgs g3 = gemm_nt(M, dm.E, dm.nqkv, dqkv, dm.nqkv, w->w_q, dm.E, g->dx, dm.E);
+      g3.b_ptr[1] = w->w_k; g3.b_start[1] = dm.nq;
+      g3.b_ptr[2] = w->w_v; g3.b_start[2] = dm.nq + dm.nk;
+      g3.b_nseg = 3;
+      CCA_TRY_HIP(timed(h, "bwd_proj_down_dx", s, [&] { return launch_gemm(g3, GemmLayout::NN, dm.bf16, false, s); }));
+      CCA_TRY_HIP(timed(h, "bwd_proj_down_dw", s, [&] { return launch_gemm(g4, GemmLayout::TN, dm.bf16, true, s); }));
+    }
     return CCA_OK;
   } catch (const std::bad_alloc&) {
     return CCA_ERR_OOM;

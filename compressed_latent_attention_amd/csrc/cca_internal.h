@@ -52,6 +52,11 @@ struct GemmArgs {
   int c_start[3];
   int c_nseg;
   long ldc;
+  // split-K (256 x 256 NT kernel only): ksplit > 1 makes work-group z of the
+  // grid's y dimension sum k in [z K/ksplit, (z+1) K/ksplit) into fp32
+  // c_ptr[0] + z * c_split_stride (one segment); 0 or 1 = no split
+  int ksplit;
+  long c_split_stride;
 };
 
 enum class GemmLayout { NT, NN, TN };   // (a_kc, b_kc) = (1,1), (1,0), (0,0)
@@ -59,6 +64,18 @@ enum class GemmLayout { NT, NN, TN };   // (a_kc, b_kc) = (1,1), (1,0), (0,0)
 // in_bf16: A and B are bf16 (else fp32); out_f32: C is fp32 (else same as inputs).
 hipError_t launch_gemm(const GemmArgs& g, GemmLayout layout, bool in_bf16, bool out_f32,
                        hipStream_t s);
+
+// The 256 x 256 bf16 NT kernel when the shape suits it (see gemm_nt_mfma.hip);
+// false and nothing launched otherwise.
+bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError_t* err);
+// out[c][r] = in[r][c] for r < R, c < C (bf16), zero for R <= r < Rp;
+// C and Rp multiples of 8, 16-byte aligned rows.
+hipError_t launch_transpose_bf16(const void* in, long ld_in, int R, int C, int Rp, void* out,
+                                 long ld_out, hipStream_t s);
+// Sums split-K partials part[z][m][n] (z < ksplit, fixed order) into fp32
+// outputs: row m goes to out[seg] + (m - start[seg]) * ld, segments along m.
+hipError_t launch_splitk_reduce(const float* part, int ksplit, int M, int N, float* const out[3],
+                                const int start[3], int nseg, long ld, hipStream_t s);
 
 // ------------------------------------------------------------------ mix
 // Causal conv + QK-mean + value shift + RoPE over a prefill.

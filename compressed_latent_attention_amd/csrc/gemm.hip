@@ -250,7 +250,6 @@ hipError_t launch_layout(const GemmArgs& g, bool in_bf16, bool out_f32, hipStrea
 
 }  // namespace
 
-bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError_t* err);
 bool launch_gemm_nt_small(const GemmArgs& g, bool out_f32, hipStream_t s, hipError_t* err);
 
 hipError_t launch_gemm(const GemmArgs& g, GemmLayout layout, bool in_bf16, bool out_f32,

@@ -57,6 +57,9 @@ __device__ __forceinline__ void dma_tile(char* dst, const bf16* base, long ld, i
 template <typename OutT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  // split-K: this work-group sums k in [kbeg, kbeg + klen)
+  const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
+  const int klen = g.K / nsplit, kbeg = blockIdx.y * klen;
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
 
   // tile of this work-group: XCD x (= blockIdx % 8) takes a consecutive run
@@ -81,9 +84,9 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   const bf16* bbase = reinterpret_cast<const bf16*>(g.b_ptr[s]) + (long)(n0 - g.b_start[s]) * g.ldb;
   const int brows = min(seg_end - n0, TN);
 
-  const int nk = g.K / TK;
-  dma_tile(lds, abase, g.lda, arows, g.K, 0, wave, lane);
-  dma_tile(lds + A_BYTES, bbase, g.ldb, brows, g.K, 0, wave, lane);
+  const int nk = klen / TK;
+  dma_tile(lds, abase, g.lda, arows, g.K, kbeg, wave, lane);
+  dma_tile(lds + A_BYTES, bbase, g.ldb, brows, g.K, kbeg, wave, lane);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -109,8 +112,8 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     const char* st = lds + (kt & 1) * STAGE;
     if (kt + 1 < nk) {
       char* nx = lds + ((kt + 1) & 1) * STAGE;
-      dma_tile(nx, abase, g.lda, arows, g.K, (kt + 1) * TK, wave, lane);
-      dma_tile(nx + A_BYTES, bbase, g.ldb, brows, g.K, (kt + 1) * TK, wave, lane);
+      dma_tile(nx, abase, g.lda, arows, g.K, kbeg + (kt + 1) * TK, wave, lane);
+      dma_tile(nx + A_BYTES, bbase, g.ldb, brows, g.K, kbeg + (kt + 1) * TK, wave, lane);
     }
     bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
@@ -142,7 +145,8 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   // D layout of 32x32 MFMA: lane holds column l32, rows 8*(r/4) + 4*hi + r%4.
   // One C segment (checked by the host): a uniform tile base plus 32-bit lane
   // offsets.
-  char* cbase = reinterpret_cast<char*>(g.c_ptr[0]) + ((long)m0 * g.ldc + n0) * sizeof(OutT);
+  char* cbase = reinterpret_cast<char*>(g.c_ptr[0]) +
+                ((long)blockIdx.y * g.c_split_stride + (long)m0 * g.ldc + n0) * sizeof(OutT);
   const int ldc = (int)g.ldc;
   const int mrem = g.M - m0, nrem = g.N - n0;
 #pragma unroll
@@ -174,8 +178,10 @@ bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError
     if (g.b_start[i] % TN != 0) return false;
   if ((long)TM * g.lda * 2 >= (1L << 31) || (long)TN * g.ldb * 2 >= (1L << 31)) return false;
   const int tiles_m = (g.M + TM - 1) / TM, tiles_n = (g.N + TN - 1) / TN;
-  if ((long)tiles_m * tiles_n < 64) return false;
-  dim3 grid(tiles_m * tiles_n);
+  const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
+  if (nsplit > 1 && (!out_f32 || (g.K / nsplit) % TK != 0 || g.K % nsplit != 0)) return false;
+  if ((long)tiles_m * tiles_n * nsplit < 64) return false;
+  dim3 grid(tiles_m * tiles_n, nsplit);
   if (out_f32)
     hipLaunchKernelGGL(gemm_nt_256_kernel<float>, grid, dim3(256), 0, s, g, tiles_m, tiles_n);
   else
@@ -267,6 +273,87 @@ bool launch_gemm_nt_small(const GemmArgs& g, bool out_f32, hipStream_t s, hipErr
     hipLaunchKernelGGL(gemm_nt_small_kernel<bf16>, grid, dim3(64 * SW), 0, s, g);
   *err = hipGetLastError();
   return true;
+}
+
+}  // namespace cca
+
+// ------------------------------------------------------------------ helpers
+// Transpose of a bf16 matrix through a 64 x 64 LDS tile (16-byte loads and
+// stores), and the fixed-order sum of split-K partials.  They let the
+// backward pass run its transposed-operand GEMMs on the NT kernel above.
+namespace cca {
+namespace {
+
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* in, long ld_in, int R,
+                                                             int C, int Rp, bf16* out,
+                                                             long ld_out) {
+  __shared__ bf16 tile[64][64 + 2];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  for (int f = threadIdx.x; f < 64 * 8; f += 256) {
+    const int row = f >> 3, c8 = (f & 7) * 8;
+    const int r = r0 + row, c = c0 + c8;
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (bf16)0.0f;
+    if (r < R && c < C) v = *reinterpret_cast<const bf16x8*>(in + (long)r * ld_in + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[row][c8 + e] = v[e];
+  }
+  __syncthreads();
+  for (int f = threadIdx.x; f < 64 * 8; f += 256) {
+    const int col = f >> 3, r8 = (f & 7) * 8;
+    const int c = c0 + col, r = r0 + r8;
+    if (c >= C || r >= Rp) continue;
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[r8 + e][col];
+    *reinterpret_cast<bf16x8*>(out + (long)c * ld_out + r) = v;
+  }
+}
+
+struct ReduceArgs {
+  const float* part;
+  int ksplit, M, N;
+  float* out[3];
+  int start[3];
+  int nseg;
+  long ld;
+};
+
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs a) {
+  const long e = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  const long total = (long)a.M * a.N;
+  if (e >= total) return;
+  f32x4 s = *reinterpret_cast<const f32x4*>(a.part + e);
+  for (int z = 1; z < a.ksplit; ++z) s += *reinterpret_cast<const f32x4*>(a.part + z * total + e);
+  const int m = (int)(e / a.N), n = (int)(e % a.N);
+  int sg = 0;
+  if (a.nseg > 1 && m >= a.start[1]) sg = 1;
+  if (a.nseg > 2 && m >= a.start[2]) sg = 2;
+  *reinterpret_cast<f32x4*>(a.out[sg] + (long)(m - a.start[sg]) * a.ld + n) = s;
+}
+
+}  // namespace
+
+hipError_t launch_transpose_bf16(const void* in, long ld_in, int R, int C, int Rp, void* out,
+                                 long ld_out, hipStream_t s) {
+  if (C % 8 != 0 || Rp % 8 != 0 || Rp < R || ld_in % 8 != 0 || ld_out % 8 != 0)
+    return hipErrorInvalidValue;
+  dim3 grid((Rp + 63) / 64, (C + 63) / 64);
+  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, (const bf16*)in, ld_in, R, C,
+                     Rp, (bf16*)out, ld_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const float* part, int ksplit, int M, int N, float* const out[3],
+                                const int start[3], int nseg, long ld, hipStream_t s) {
+  if (N % 4 != 0 || ld % 4 != 0) return hipErrorInvalidValue;
+  ReduceArgs a{};
+  a.part = part; a.ksplit = ksplit; a.M = M; a.N = N; a.nseg = nseg; a.ld = ld;
+  for (int i = 0; i < 3; ++i) { a.out[i] = out[i]; a.start[i] = start[i]; }
+  const long total = (long)M * N / 4;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace cca

@@ -24,6 +24,10 @@ CASES = [
     Workload("bf16_bwd_gqa", B=1, S=300, E=512, C=1, Hq=4, Hkv=2, seed=64, kind="backward"),
     Workload("bf16_bwd_b2", B=2, S=129, E=1024, C=2, Hq=4, Hkv=4, kq=2, kk=3, seed=65,
              kind="backward"),
+    # large enough that the weight gradients run split over K (16 partial sums)
+    # on the 256 x 256 kernel, and the attention backward spans 16 key blocks
+    Workload("bf16_bwd_splitk", B=1, S=2048, E=1024, C=2, Hq=4, Hkv=2, seed=67,
+             kind="backward"),
 ]
 
 
