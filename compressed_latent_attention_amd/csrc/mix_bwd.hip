@@ -11,6 +11,8 @@
 // with a = [QK-mean pre], b = [QK-mean post] halves folded in as in the forward.
 // Tap gradients are summed per block of tokens and then over blocks in a
 // fixed order (deterministic).
+#include <algorithm>
+
 #include "cca_internal.h"
 
 namespace cca {
@@ -130,6 +132,155 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial(MixBwdArgs a) {
   }
 }
 
+// ---- d = 128: LDS-tiled, register-blocked fp32 versions of the two kernels
+// above (same sums, exact fp32).
+constexpr int TD = 128;
+
+// dq~ = direct + sum_j A_j^T dq^[t + j] for 64 tokens of one head: the dq^ tile
+// (64 tokens plus the k - 1 after them) sits transposed in LDS, the taps of
+// one lag go through LDS 32 input channels at a time; thread = 4 tokens x 8
+// output channels.
+template <typename T>
+__global__ __launch_bounds__(256) void mix_bwd_conv_input_128(MixBwdArgs a) {
+  constexpr int TT = 64, TR = TT + kMaxConv;          // tile rows incl. halo, padded
+  __shared__ __attribute__((aligned(16))) float gT[TD][TR];   // dq^ transposed [c][t - t0]
+  __shared__ __attribute__((aligned(16))) float tp[32][TD];   // taps A_j[c0 + i][c2]
+  const Dims& dm = a.dm;
+  const int t0 = blockIdx.x * TT, hh = blockIdx.y, b = blockIdx.z;
+  const bool isq = hh < dm.Hq;
+  const int h = isq ? hh : hh - dm.Hq;
+  const int k = isq ? dm.kq : dm.kk;
+  const T* taps = reinterpret_cast<const T*>(isq ? a.conv_q : a.conv_k) + (long)h * k * TD * TD;
+  const int W = 2 * (dm.nq + dm.nk);
+  const int col = isq ? h * TD : dm.nq + h * TD;       // dq^ / dk^ column in scratch
+  const int dcol = dm.nq + dm.nk + col;                // direct term
+  const float* srow0 = a.scratch + (long)b * a.S * W;
+  for (int e = threadIdx.x; e < TR * (TD / 4); e += 256) {
+    const int r = e / (TD / 4), c4 = (e % (TD / 4)) * 4;
+    const int t = t0 + r;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (r < TT + k - 1 && t < a.S) v = *reinterpret_cast<const f32x4*>(srow0 + (long)t * W + col + c4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gT[c4 + i][r] = v[i];
+  }
+  const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;   // tokens 4ty.., channels 8tx..
+  float acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[i][n] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    for (int c0 = 0; c0 < TD; c0 += 32) {
+      __syncthreads();                                   // tile ready / previous taps read
+      for (int e = threadIdx.x; e < 32 * TD; e += 256) {
+        const int i = e / TD, c2 = e % TD;
+        tp[i][c2] = (float)taps[((long)j * TD + c0 + i) * TD + c2];
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int i = 0; i < 32; ++i) {
+        const int c = c0 + i;
+        float g[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) g[r] = gT[c][4 * ty + r + j];
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(&tp[i][8 * tx]);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(&tp[i][8 * tx + 4]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int n = 0; n < 4; ++n) {
+            acc[r][n] = fmaf(g[r], w0[n], acc[r][n]);
+            acc[r][n + 4] = fmaf(g[r], w1[n], acc[r][n + 4]);
+          }
+        }
+      }
+    }
+  }
+  const int ocol = isq ? h * TD : dm.nq + h * TD;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = t0 + 4 * ty + r;
+    if (t >= a.S) continue;
+    const float* dir = srow0 + (long)t * W + dcol + 8 * tx;
+    T* out = reinterpret_cast<T*>(a.dqkv) + (long)(b * a.S + t) * dm.nqkv + ocol + 8 * tx;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) out[n] = (T)(acc[r][n] + dir[n]);
+  }
+}
+
+// Partial tap gradient of one head and lag over one block of TB tokens:
+// part[blk][taps of (head, j)][c][c2] = sum_t dq^[t][c] q~[t - j][c2].  Tokens
+// pass through LDS 32 at a time; thread = 8 c x 8 c2.
+template <typename T>
+__global__ __launch_bounds__(256) void mix_bwd_tap_partial_128(MixBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float gq[32][TD];
+  __shared__ __attribute__((aligned(16))) float xq[32][TD];
+  const Dims& dm = a.dm;
+  const int blk = blockIdx.x, hh = blockIdx.y, j = blockIdx.z;
+  const int nblk_s = (a.S + TB - 1) / TB;
+  const int b = blk / nblk_s, tb0 = (blk % nblk_s) * TB;
+  const bool isq = hh < dm.Hq;
+  const int h = isq ? hh : hh - dm.Hq;
+  const int k = isq ? dm.kq : dm.kk;
+  if (j >= k) return;
+  const int W = 2 * (dm.nq + dm.nk);
+  const int gcol = isq ? h * TD : dm.nq + h * TD;
+  const long per_blk = (long)dm.Hq * dm.kq * TD * TD + (long)dm.Hkv * dm.kk * TD * TD;
+  const long off = isq ? (long)h * dm.kq * TD * TD
+                       : (long)dm.Hq * dm.kq * TD * TD + (long)h * dm.kk * TD * TD;
+  const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;   // c = 8ty.., c2 = 8tx..
+  float acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[i][n] = 0.0f;
+  const int tend = min(a.S, tb0 + TB);
+  for (int t0 = tb0; t0 < tend; t0 += 32) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < 32 * (TD / 4); e += 256) {
+      const int r = e / (TD / 4), c4 = (e % (TD / 4)) * 4;
+      const int t = t0 + r;
+      f32x4 gv = {0.f, 0.f, 0.f, 0.f}, xv = {0.f, 0.f, 0.f, 0.f};
+      if (t < tend) {
+        gv = *reinterpret_cast<const f32x4*>(a.scratch + (long)(b * a.S + t) * W + gcol + c4);
+        if (t - j >= 0)
+          xv = *reinterpret_cast<const f32x4*>(a.qkv + (long)(b * a.S + t - j) * dm.nqkv + gcol + c4);
+      }
+      *reinterpret_cast<f32x4*>(&gq[r][c4]) = gv;
+      *reinterpret_cast<f32x4*>(&xq[r][c4]) = xv;
+    }
+    __syncthreads();
+#pragma unroll 2
+    for (int r = 0; r < 32; ++r) {
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&gq[r][8 * ty]);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(&gq[r][8 * ty + 4]);
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(&xq[r][8 * tx]);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(&xq[r][8 * tx + 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          acc[i][n] = fmaf(g0[i], x0[n], acc[i][n]);
+          acc[i][n + 4] = fmaf(g0[i], x1[n], acc[i][n + 4]);
+          acc[i + 4][n] = fmaf(g1[i], x0[n], acc[i + 4][n]);
+          acc[i + 4][n + 4] = fmaf(g1[i], x1[n], acc[i + 4][n + 4]);
+        }
+    }
+  }
+  float* out = a.dconv_part + blk * per_blk + off + (long)j * TD * TD;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f32x4 v0, v1;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      v0[n] = acc[i][n];
+      v1[n] = acc[i][n + 4];
+    }
+    *reinterpret_cast<f32x4*>(out + (long)(8 * ty + i) * TD + 8 * tx) = v0;
+    *reinterpret_cast<f32x4*>(out + (long)(8 * ty + i) * TD + 8 * tx + 4) = v1;
+  }
+}
+
 __global__ __launch_bounds__(256) void mix_bwd_tap_reduce(MixBwdArgs a, int nblk) {
   const Dims& dm = a.dm;
   const long nq = (long)dm.Hq * dm.kq * dm.d * dm.d;
@@ -161,7 +312,19 @@ hipError_t launch_mix_bwd(const MixBwdArgs& a, hipStream_t s) {
   const Dims& dm = a.dm;
   const int nblk = tap_blocks(a.B, a.S);
   const long per_blk = (long)dm.Hq * dm.kq * dm.d * dm.d + (long)dm.Hkv * dm.kk * dm.d * dm.d;
-  if (dm.bf16) {
+  const int kmax = std::max(dm.kq, dm.kk);
+  if (dm.d == TD) {
+    const dim3 gin((a.S + 63) / 64, dm.Hq + dm.Hkv, a.B), gtap(nblk, dm.Hq + dm.Hkv, kmax);
+    if (dm.bf16) {
+      hipLaunchKernelGGL(mix_bwd_pointwise<bf16>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(mix_bwd_conv_input_128<bf16>, gin, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(mix_bwd_tap_partial_128<bf16>, gtap, dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(mix_bwd_pointwise<float>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(mix_bwd_conv_input_128<float>, gin, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(mix_bwd_tap_partial_128<float>, gtap, dim3(256), 0, s, a);
+    }
+  } else if (dm.bf16) {
     hipLaunchKernelGGL(mix_bwd_pointwise<bf16>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
     hipLaunchKernelGGL(mix_bwd_conv_input<bf16>, dim3(a.S, dm.Hq + dm.Hkv, a.B), dim3(128), 0, s, a);
     hipLaunchKernelGGL(mix_bwd_tap_partial<bf16>, dim3(nblk, dm.Hq + dm.Hkv), dim3(256), 0, s, a);

@@ -21,6 +21,9 @@ CASES = [
              seed=62, kind="backward"),
     Workload("f32_bwd_flags", B=1, S=33, E=64, C=1, Hq=2, Hkv=1, flags=2 | 8, sv=5,
              dtype="f32", seed=63, kind="backward"),
+    # d = 128 in fp32: the tiled conv-input and tap-gradient kernels, ragged tiles
+    Workload("f32_bwd_d128", B=2, S=300, E=256, C=1, Hq=2, Hkv=1, kq=3, kk=2, dtype="f32",
+             seed=68, kind="backward"),
     Workload("bf16_bwd_gqa", B=1, S=300, E=512, C=1, Hq=4, Hkv=2, seed=64, kind="backward"),
     Workload("bf16_bwd_b2", B=2, S=129, E=1024, C=2, Hq=4, Hkv=4, kq=2, kk=3, seed=65,
              kind="backward"),
