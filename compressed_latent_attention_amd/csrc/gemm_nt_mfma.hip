@@ -9,8 +9,13 @@
 // registers) and issues 16 MFMAs per 16-wide k step from two double-buffered
 // sets of operand fragments.  Tiles of A and B move from global memory to LDS
 // with buffer loads that write LDS directly (16 bytes per lane), two stages
-// deep; LDS rows (64 k = 128 B) are unpadded with their 16-byte chunks
-// XOR-swizzled by row, so that the fragment reads are free of bank conflicts.
+// deep; the next stage's sixteen 1 KB copies per wave are issued one after
+// every four MFMAs rather than in a burst: a copy's issue waits until the
+// address unit takes it, and with one wave per SIMD a burst would leave the
+// MFMA unit idle for that long (spread out, the copies stay below the unit's
+// rate and issue at once).  LDS rows (64 k = 128 B) are unpadded with their
+// 16-byte chunks XOR-swizzled by row, so that the fragment reads are free of
+// bank conflicts.
 // Rows past M or past the end of B's segment read as zero (buffer range
 // check), so ragged M and N need no special path.  Tiles are numbered so that
 // the tiles of one XCD (work-groups are dealt to the 8 XCDs round-robin) are
@@ -52,6 +57,18 @@ __device__ __forceinline__ void dma_tile(char* dst, const bf16* base, long ld, i
     const int src = r * (int)ld * 2 + ((pos ^ ((r >> 1) & 7)) << 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16, src, 0, 0, 0);
   }
+}
+
+// Block i (0..7) of this wave's share of dma_tile, alone.
+__device__ __forceinline__ void dma_part(char* dst, const bf16* base, long ld, int rows, int K,
+                                         int k0, int wave, int lane, int i) {
+  const int nrec = ((rows - 1) * (int)ld + K - k0) * 2;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(base + k0), 0, nrec, 0x00020000);
+  const int blk = wave * 8 + i;
+  const int r = blk * 8 + (lane >> 3), pos = lane & 7;
+  const int src = r * (int)ld * 2 + ((pos ^ ((r >> 1) & 7)) << 4);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16, src, 0, 0, 0);
 }
 
 template <typename OutT>
@@ -110,11 +127,11 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
 
   for (int kt = 0; kt < nk; ++kt) {
     const char* st = lds + (kt & 1) * STAGE;
-    if (kt + 1 < nk) {
-      char* nx = lds + ((kt + 1) & 1) * STAGE;
-      dma_tile(nx, abase, g.lda, arows, g.K, kbeg + (kt + 1) * TK, wave, lane);
-      dma_tile(nx + A_BYTES, bbase, g.ldb, brows, g.K, kbeg + (kt + 1) * TK, wave, lane);
-    }
+    // next stage's copy, one 1 KB block after every four MFMAs (the last step
+    // copies its own k range again into the idle stage, so the loop body has
+    // no branch)
+    char* nx = lds + ((kt + 1) & 1) * STAGE;
+    const int knx = kbeg + min(kt + 1, nk - 1) * TK;
     bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -132,11 +149,17 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j],
                                                               0, 0, 0);
+        const int blk = ks * 4 + i;          // 16 blocks: A 0..7, B 8..15
+        __builtin_amdgcn_sched_barrier(0);
+        if (blk < 8) dma_part(nx, abase, g.lda, arows, g.K, knx, wave, lane, blk);
+        else dma_part(nx + A_BYTES, bbase, g.ldb, brows, g.K, knx, wave, lane, blk - 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     wait_dma();
     __syncthreads();
