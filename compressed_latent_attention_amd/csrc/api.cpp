@@ -97,7 +97,7 @@ SavedLayout saved_layout(const Dims& dm, long B, long S) {
 }
 
 struct DecodeLayout {
-  size_t qkv, q, o, part, total;
+  size_t qkv, q, o, part, cv, total;
 };
 
 DecodeLayout decode_layout(const Dims& dm, long B) {
@@ -108,6 +108,7 @@ DecodeLayout decode_layout(const Dims& dm, long B) {
   L.q = o;   o = align256(o + B * dm.nq * es);
   L.o = o;   o = align256(o + B * dm.nq * es);
   L.part = o; o = align256(o + decode_part_floats(dm, (int)B) * 4);
+  L.cv = o;   o = align256(o + mix_decode_cv_floats(dm, (int)B) * 4);
   L.total = o;
   return L;
 }
@@ -449,6 +450,7 @@ cca_status cca_decode_step(cca_handle* h, const cca_weights* w, const void* x_ne
     md.dm = dm; md.B = B; md.pos = pos; md.qkv = qkv;
     md.conv_q = w->conv_q; md.conv_k = w->conv_k; md.rope = h->rope;
     md.state = state; md.k_cache = k_cache; md.v_cache = v_cache; md.q_out = qn;
+    md.cv = (float*)(base + L.cv);
     CCA_TRY_HIP(timed(h, "decode_mix", s, [&] { return launch_mix_decode(md, s); }));
 
     AttnArgs aa{};

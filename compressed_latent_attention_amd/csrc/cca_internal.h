@@ -122,8 +122,10 @@ struct MixDecodeArgs {
   void* k_cache;            // [B, Hkv, max_seq_len, d]
   void* v_cache;
   void* q_out;              // [B, Hq, d]
+  float* cv;                // [B, Hq + Hkv, d] fp32 workspace: convolution outputs
 };
 hipError_t launch_mix_decode(const MixDecodeArgs& a, hipStream_t s);
+size_t mix_decode_cv_floats(const Dims& dm, int B);
 
 // ------------------------------------------------------------------ attention
 // Causal attention.  Query row t of sequence b sits at position

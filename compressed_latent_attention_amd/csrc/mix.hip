@@ -14,6 +14,8 @@
 // bf16 lives in mix_mfma.hip.
 #include "cca_internal.h"
 
+#include <algorithm>
+
 namespace cca {
 namespace {
 
@@ -143,9 +145,152 @@ __global__ __launch_bounds__(256) void write_state_kernel(Dims dm, int S, const 
   }
 }
 
-// Decode-step mix: one token per sequence at position pos[b]; the lags of
-// the convolution and the previous value come from the rolling state, which
-// is advanced in place.  One work-group per (KV group, sequence).
+// Decode-step mix, part 1: the causal grouped convolution of the new token of
+// every sequence, for every query and key head: cv[b, hg, c] =
+// sum_j sum_c' u_j[b, hg, c'] A_{hg, j}[c, c'], where u_0 is the token's
+// latent (qkv) and u_j (j >= 1) the lag-j latent from the rolling state; hg
+// runs over the query heads, then the key heads.  Work-group = one head x CB
+// output channels x BC sequences: its tap rows go to LDS (fp32, rows padded by
+// 4 so the 16 lanes that read 16 different rows hit different banks), then the
+// lags of its sequences; thread = one (sequence, channel) dot product over
+// k * d inputs, 4 at a time.  The staging loads use clamped indices (a
+// duplicate load is stored nowhere), so they issue back to back.
+constexpr int CB = 16;                  // output channels per work-group
+constexpr int BCMAX = 16;               // sequences per work-group (256 threads / CB)
+
+template <typename T>
+__global__ __launch_bounds__(256) void mix_decode_conv_kernel(MixDecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  const Dims& dm = a.dm;
+  const int d = dm.d, TS = d + 4;       // tap row stride (floats)
+  const int hg = blockIdx.x, c0 = blockIdx.y * CB, b0 = blockIdx.z * BCMAX;
+  const int nb = min(BCMAX, a.B - b0);
+  const bool isq = hg < dm.Hq;
+  const int k = isq ? dm.kq : dm.kk;
+  const int nqpart = (dm.kq - 1) * dm.nq;
+  float* tap = smem;                    // [k][CB][TS]
+  float* u = smem + k * CB * TS;        // [BCMAX][k][d]
+  const T* taps = reinterpret_cast<const T*>(isq ? a.conv_q : a.conv_k) +
+                  (long)(isq ? hg : hg - dm.Hq) * k * d * d;
+  const int col0 = isq ? hg * d : dm.nq + (hg - dm.Hq) * d;   // column in qkv and in the state
+  const int t = threadIdx.x;
+  constexpr int EV = 16 / sizeof(T);    // tap elements per 16-byte load
+  if (d % EV == 0) {
+    // tap rows (rows past d read row d - 1 and store zeros)
+    const int dv = d / EV, nvec = k * CB * dv;
+    for (int base = 0; base < nvec; base += 2 * 256) {
+      T v[2][EV];
+      int dst[2];
+      bool ok[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int i = base + r * 256 + t, ic = min(i, nvec - 1);
+        const int j = ic / (CB * dv), cl = (ic / dv) % CB, e = (ic % dv) * EV;
+        dst[r] = i < nvec ? (j * CB + cl) * TS + e : -1;
+        ok[r] = c0 + cl < d;
+        *reinterpret_cast<f32x4*>(v[r]) = *reinterpret_cast<const f32x4*>(
+            taps + ((long)j * d + min(c0 + cl, d - 1)) * d + e);
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        if (dst[r] >= 0)
+#pragma unroll
+          for (int q = 0; q < EV; ++q) tap[dst[r] + q] = ok[r] ? (float)v[r][q] : 0.0f;
+    }
+  } else {
+    for (int i = t; i < k * CB * d; i += blockDim.x) {
+      const int j = i / (CB * d), cl = (i / d) % CB, e = i % d;
+      tap[(j * CB + cl) * TS + e] =
+          c0 + cl < d ? (float)taps[((long)j * d + c0 + cl) * d + e] : 0.0f;
+    }
+  }
+  if (d % 4 == 0) {
+    // lag 0 from qkv, 4 channels per load
+    const int n0 = nb * (d / 4);
+    for (int base = 0; base < n0; base += 2 * 256) {
+      f32x4 v[2];
+      int dst[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int i = base + r * 256 + t, ic = min(i, n0 - 1);
+        const int bb = ic / (d / 4), e = (ic % (d / 4)) * 4;
+        dst[r] = i < n0 ? bb * k * d + e : -1;
+        v[r] = *reinterpret_cast<const f32x4*>(a.qkv + (long)(b0 + bb) * dm.nqkv + col0 + e);
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        if (dst[r] >= 0) *reinterpret_cast<f32x4*>(u + dst[r]) = v[r];
+    }
+    // lags 1 .. k - 1 from the state
+    const int nl = nb * (k - 1) * (d / 4);
+    for (int base = 0; base < nl; base += 2 * 256) {
+      float v[2][4];
+      int dst[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int i = base + r * 256 + t, ic = min(i, nl - 1);
+        const int e = (ic % (d / 4)) * 4, j = 1 + (ic / (d / 4)) % (k - 1),
+                  bb = ic / ((k - 1) * (d / 4));
+        dst[r] = i < nl ? (bb * k + j) * d + e : -1;
+        const long srow = (long)(b0 + bb) * dm.state_w;
+        const long off = isq ? srow + (long)(j - 1) * dm.nq + col0 + e
+                             : srow + nqpart + (long)(j - 1) * dm.nk + (col0 - dm.nq) + e;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[r][q] = ldf<T>(a.state, off + q);
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        if (dst[r] >= 0)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) u[dst[r] + q] = v[r][q];
+    }
+  } else {
+    for (int i = t; i < nb * k * d; i += blockDim.x) {
+      const int bb = i / (k * d), j = (i / d) % k, e = i % d;
+      const int b = b0 + bb;
+      float v;
+      if (j == 0) {
+        v = a.qkv[(long)b * dm.nqkv + col0 + e];
+      } else {
+        const long srow = (long)b * dm.state_w;
+        v = isq ? ldf<T>(a.state, srow + (long)(j - 1) * dm.nq + col0 + e)
+                : ldf<T>(a.state, srow + nqpart + (long)(j - 1) * dm.nk + (col0 - dm.nq) + e);
+      }
+      u[i] = v;
+    }
+  }
+  __syncthreads();
+  const int cl = t % CB, o = t / CB;
+  if (o >= nb || c0 + cl >= d) return;
+  float s0 = 0.0f, s1 = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const float* ur = u + (o * k + j) * d;
+    const float* tr = tap + (j * CB + cl) * TS;
+    if (d % 8 == 0) {
+#pragma unroll 4
+      for (int e = 0; e < d; e += 8) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(ur + e);
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(tr + e);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(ur + e + 4);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(tr + e + 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          s0 = fmaf(w0[q], x0[q], s0);
+          s1 = fmaf(w1[q], x1[q], s1);
+        }
+      }
+    } else {
+      for (int e = 0; e < d; ++e) s0 = fmaf(tr[e], ur[e], s0);
+    }
+  }
+  a.cv[((long)(b0 + o) * (dm.Hq + dm.Hkv) + hg) * d + c0 + cl] = s0 + s1;
+}
+
+// Decode-step mix, part 2: one token per sequence at position pos[b].  From
+// the convolution outputs cv and the pre-convolution latents (lag 0 from qkv,
+// the lags of the state) it forms QK-mean, RoPE, the value shift, writes q and
+// the caches, and advances the rolling state in place.  One work-group per (KV
+// group, sequence).
 template <typename T>
 __global__ __launch_bounds__(256) void mix_decode_kernel(MixDecodeArgs a) {
   extern __shared__ float smem[];
@@ -159,6 +304,7 @@ __global__ __launch_bounds__(256) void mix_decode_kernel(MixDecodeArgs a) {
   float* vprev = cv + NH * d;            // [d]
   const long srow = (long)b * dm.state_w;
   const int nqpart = (dm.kq - 1) * dm.nq, nkpart = (dm.kk - 1) * dm.nk;
+#pragma unroll 4
   for (int i = threadIdx.x; i < KM * NH * d; i += blockDim.x) {
     const int j = i / (NH * d), hh = (i / d) % NH, c = i % d;
     const bool isq = hh < G;
@@ -173,46 +319,14 @@ __global__ __launch_bounds__(256) void mix_decode_kernel(MixDecodeArgs a) {
     }
     u[i] = v;
   }
+#pragma unroll 4
+  for (int i = threadIdx.x; i < NH * d; i += blockDim.x) {
+    const int hh = i / d, c = i % d;
+    const int hgl = hh < G ? g * G + hh : dm.Hq + g;
+    cv[i] = a.cv[((long)b * (dm.Hq + dm.Hkv) + hgl) * d + c];
+  }
   for (int c = threadIdx.x; c < d; c += blockDim.x)
     vprev[c] = ldf<T>(a.state, srow + nqpart + nkpart + g * d + c);
-  __syncthreads();
-  // conv: each output channel (head hh, channel c) is a dot product of k tap
-  // rows with the lags; 16 lanes share one output, each taking every 16th
-  // group of 8 input channels (16-byte tap loads when d % 8 == 0), then a
-  // 4-step shuffle sum.
-  {
-    const int sub = threadIdx.x & 15;
-    for (int task = threadIdx.x >> 4; task < NH * d; task += blockDim.x >> 4) {
-      const int hh = task / d, c = task % d;
-      const bool isq = hh < G;
-      const int k = isq ? dm.kq : dm.kk;
-      const long tap0 = isq ? (long)(g * G + hh) * dm.kq * d * d : (long)g * dm.kk * d * d;
-      const T* taps = reinterpret_cast<const T*>(isq ? a.conv_q : a.conv_k);
-      float s = 0.0f;
-      for (int j = 0; j < k; ++j) {
-        const float* src = u + (j * NH + hh) * d;
-        const T* trow = taps + tap0 + ((long)j * d + c) * d;
-        for (int e0 = 8 * sub; e0 < d; e0 += 128) {
-          if (d % 8 == 0) {
-            T tv[8];
-            if (sizeof(T) == 2) {
-              *reinterpret_cast<bf16x8*>(tv) = *reinterpret_cast<const bf16x8*>(trow + e0);
-            } else {
-              *reinterpret_cast<f32x4*>(tv) = *reinterpret_cast<const f32x4*>(trow + e0);
-              *reinterpret_cast<f32x4*>(tv + 4) = *reinterpret_cast<const f32x4*>(trow + e0 + 4);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) s = fmaf((float)tv[i], src[e0 + i], s);
-          } else {
-            for (int i = 0; i < 8 && e0 + i < d; ++i) s = fmaf((float)trow[e0 + i], src[e0 + i], s);
-          }
-        }
-      }
-#pragma unroll
-      for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off);
-      if (sub == 0) cv[task] = s;
-    }
-  }
   __syncthreads();
   const int half = d / 2;
   for (int c = threadIdx.x; c < d; c += blockDim.x) {
@@ -279,8 +393,21 @@ hipError_t launch_write_state(const Dims& dm, int B, int S, const float* qkv, vo
   return hipGetLastError();
 }
 
+size_t mix_decode_cv_floats(const Dims& dm, int B) { return (size_t)B * (dm.Hq + dm.Hkv) * dm.d; }
+
 hipError_t launch_mix_decode(const MixDecodeArgs& a, hipStream_t s) {
   const Dims& dm = a.dm;
+  if (a.cv == nullptr) return hipErrorInvalidValue;
+  // part 1: LDS = k CB (d + 4) tap floats + BCMAX k d lag floats
+  const int k = max(dm.kq, dm.kk);
+  const size_t lds1 = ((size_t)k * CB * (dm.d + 4) + (size_t)BCMAX * k * dm.d) * sizeof(float);
+  if (lds1 > 64 * 1024) return hipErrorInvalidValue;
+  dim3 grid1(dm.Hq + dm.Hkv, (dm.d + CB - 1) / CB, (a.B + BCMAX - 1) / BCMAX);
+  if (dm.bf16)
+    hipLaunchKernelGGL(mix_decode_conv_kernel<bf16>, grid1, dim3(256), lds1, s, a);
+  else
+    hipLaunchKernelGGL(mix_decode_conv_kernel<float>, grid1, dim3(256), lds1, s, a);
+  // part 2
   const int KM = max(dm.kq, dm.kk);
   const size_t lds = (size_t)((KM + 1) * (dm.G + 1) * dm.d + dm.d) * sizeof(float);
   dim3 grid(dm.Hkv, a.B);
