@@ -97,7 +97,7 @@ SavedLayout saved_layout(const Dims& dm, long B, long S) {
 }
 
 struct DecodeLayout {
-  size_t qkv, q, o, part, cv, total;
+  size_t qkv, q, o, part, cv, gpart, total;
 };
 
 DecodeLayout decode_layout(const Dims& dm, long B) {
@@ -109,6 +109,7 @@ DecodeLayout decode_layout(const Dims& dm, long B) {
   L.o = o;   o = align256(o + B * dm.nq * es);
   L.part = o; o = align256(o + decode_part_floats(dm, (int)B) * 4);
   L.cv = o;   o = align256(o + mix_decode_cv_floats(dm, (int)B) * 4);
+  L.gpart = o; o = align256(o + (dm.bf16 ? gemm_skinny_part_floats() * 4 : 0));
   L.total = o;
   return L;
 }
@@ -444,7 +445,14 @@ cca_status cca_decode_step(cca_handle* h, const cca_weights* w, const void* x_ne
     void* on = base + L.o;
 
     GemmArgs gd = gemm_down(dm, B, x_new, w, qkv);
-    CCA_TRY_HIP(timed(h, "decode_proj_down", s, [&] { return launch_gemm(gd, GemmLayout::NT, dm.bf16, true, s); }));
+    float* gpart = dm.bf16 ? (float*)(base + L.gpart) : nullptr;
+    // few rows: the split-K skinny GEMM when the shape suits it, else the generic path
+    auto gemm_decode = [&](const GemmArgs& ga, bool out_f32) {
+      hipError_t e = hipSuccess;
+      if (dm.bf16 && launch_gemm_skinny(ga, out_f32, gpart, s, &e)) return e;
+      return launch_gemm(ga, GemmLayout::NT, dm.bf16, out_f32, s);
+    };
+    CCA_TRY_HIP(timed(h, "decode_proj_down", s, [&] { return gemm_decode(gd, true); }));
 
     MixDecodeArgs md{};
     md.dm = dm; md.B = B; md.pos = pos; md.qkv = qkv;
@@ -462,7 +470,7 @@ cca_status cca_decode_step(cca_handle* h, const cca_weights* w, const void* x_ne
     CCA_TRY_HIP(timed(h, "decode_attn", s, [&] { return launch_attn_decode(aa, s); }));
 
     GemmArgs gu = gemm_nt(B, dm.E, dm.nq, on, dm.nq, w->w_o, dm.nq, y_new, dm.E);
-    CCA_TRY_HIP(timed(h, "decode_proj_up", s, [&] { return launch_gemm(gu, GemmLayout::NT, dm.bf16, false, s); }));
+    CCA_TRY_HIP(timed(h, "decode_proj_up", s, [&] { return gemm_decode(gu, false); }));
     return CCA_OK;
   } catch (const std::bad_alloc&) {
     return CCA_ERR_OOM;

@@ -68,6 +68,12 @@ hipError_t launch_gemm(const GemmArgs& g, GemmLayout layout, bool in_bf16, bool 
 // The 256 x 256 bf16 NT kernel when the shape suits it (see gemm_nt_mfma.hip);
 // false and nothing launched otherwise.
 bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError_t* err);
+// Split-K NT GEMM for few rows of A (the decode step): partial tiles in an fp32
+// buffer of gemm_skinny_part_floats() floats, then a fixed-order sum; false when
+// the shape does not suit it (nothing launched).
+bool launch_gemm_skinny(const GemmArgs& g, bool out_f32, float* part, hipStream_t s,
+                        hipError_t* err);
+size_t gemm_skinny_part_floats();
 // out[c][r] = in[r][c] for r < R, c < C (bf16), zero for R <= r < Rp;
 // C and Rp multiples of 8, 16-byte aligned rows.
 hipError_t launch_transpose_bf16(const void* in, long ld_in, int R, int C, int Rp, void* out,

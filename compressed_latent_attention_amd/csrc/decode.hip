@@ -32,10 +32,14 @@ bool fast_decode(const Dims& dm) {
   return dm.bf16 && dm.d == D && dm.G <= kMaxGroup && dm.max_seq_len <= MAX_SPLIT * CK;
 }
 
+// GQ: the group size rounded up to a power of two (the kernel is instantiated
+// for 1, 2, 4, 8), so P V keeps only that many accumulator rows in registers.
+template <int GQ>
 __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) float ps[CK][kMaxGroup];   // scores, then p
-  __shared__ float opart[NW][kMaxGroup][D];
-  __shared__ float stat[kMaxGroup][2];                             // m, l per query
+  constexpr int PW = GQ < 4 ? 4 : GQ;                              // p row: 16-byte aligned
+  // scores, then p; after P V the same memory holds the waves' partial O
+  __shared__ __attribute__((aligned(16))) float ps[CK * PW > NW * GQ * D ? CK * PW : NW * GQ * D];
+  __shared__ float stat[GQ][2];                                    // m, l per query
 
   const Dims& dm = a.dm;
   const int G = dm.G;
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int q = 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (q < G) ps[blk * 32 + l32][q] = valid ? acc[r] : -INFINITY;
+      if (q < G) ps[(blk * 32 + l32) * PW + q] = valid ? acc[r] : -INFINITY;
     }
   }
   __syncthreads();
@@ -105,13 +109,13 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
   // ---- 2. max and sum over the chunk, one wave per query (G <= 8 queries)
   for (int q = wave; q < G; q += NW) {
     float m = -INFINITY;
-    for (int i = lane; i < CK; i += 64) m = fmaxf(m, ps[i][q]);
+    for (int i = lane; i < CK; i += 64) m = fmaxf(m, ps[i * PW + q]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
     float l = 0.0f;
     for (int i = lane; i < CK; i += 64) {
-      const float p = __builtin_amdgcn_exp2f(ps[i][q] - m);   // masked keys: 0
-      ps[i][q] = p;
+      const float p = __builtin_amdgcn_exp2f(ps[i * PW + q] - m);   // masked keys: 0
+      ps[i * PW + q] = p;
       l += p;
     }
 #pragma unroll
@@ -128,9 +132,9 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
   // covers 4 whole 256-byte V rows.  The 4 key slots are summed with two
   // shuffles, the 4 waves through LDS.
   const int slot = lane >> 4, cc = (lane & 15) * 8;
-  float o[kMaxGroup][8];
+  float o[GQ][8];
 #pragma unroll
-  for (int q = 0; q < kMaxGroup; ++q)
+  for (int q = 0; q < GQ; ++q)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[q][e] = 0.0f;
   const int i0 = wave * (CK / NW);
@@ -139,10 +143,11 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
 #pragma unroll 4
   for (int i = i0 + slot; i < i1; i += 4) {
     const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(vbase + (long)i * D);
-    const f32x4 pa = *reinterpret_cast<const f32x4*>(&ps[i][0]);
-    const f32x4 pb = *reinterpret_cast<const f32x4*>(&ps[i][4]);
+    const f32x4 pa = *reinterpret_cast<const f32x4*>(&ps[i * PW]);
+    f32x4 pb = pa;
+    if (GQ > 4) pb = *reinterpret_cast<const f32x4*>(&ps[i * PW + 4]);
 #pragma unroll
-    for (int q = 0; q < kMaxGroup; ++q) {
+    for (int q = 0; q < GQ; ++q) {
       if (q < G) {
         const float p = q < 4 ? pa[q] : pb[q - 4];
 #pragma unroll
@@ -150,23 +155,28 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
       }
     }
   }
+  // the four key slots of a wave are summed with two shuffles, the waves
+  // through LDS (over the scores, once every wave is done with them)
 #pragma unroll
-  for (int q = 0; q < kMaxGroup; ++q)
-    if (q < G) {
+  for (int q = 0; q < GQ; ++q)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = o[q][e];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        if (slot == 0) opart[wave][q][cc + e] = v;
-      }
+    for (int e = 0; e < 8; ++e) {
+      o[q][e] += __shfl_xor(o[q][e], 16);
+      o[q][e] += __shfl_xor(o[q][e], 32);
     }
+  __syncthreads();
+  float* opart = ps;                          // [NW][GQ][D]
+#pragma unroll
+  for (int q = 0; q < GQ; ++q)
+    if (q < G && slot == 0)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) opart[(wave * GQ + q) * D + cc + e] = o[q][e];
   __syncthreads();
   for (int e = threadIdx.x; e < G * D; e += 256) {
     const int q = e / D, c = e % D;
     float sum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) sum += opart[w][q][c];
+    for (int w = 0; w < NW; ++w) sum += opart[(w * GQ + q) * D + c];
     part[(long)q * nsplit * PSTRIDE + c] = sum;
   }
   if (threadIdx.x < G) {
@@ -231,7 +241,15 @@ hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s) {
   if (!fast_decode(a.dm)) return launch_attn_fwd(a, s);
   if (a.part == nullptr || a.nsplit != decode_nsplit(a.dm, a.B) || a.nsplit > MAX_SPLIT)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_decode_split_kernel, dim3(a.nsplit, a.dm.Hkv, a.B), dim3(256), 0, s, a);
+  const dim3 grid(a.nsplit, a.dm.Hkv, a.B);
+  if (a.dm.G <= 1)
+    hipLaunchKernelGGL(attn_decode_split_kernel<1>, grid, dim3(256), 0, s, a);
+  else if (a.dm.G <= 2)
+    hipLaunchKernelGGL(attn_decode_split_kernel<2>, grid, dim3(256), 0, s, a);
+  else if (a.dm.G <= 4)
+    hipLaunchKernelGGL(attn_decode_split_kernel<4>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_decode_split_kernel<8>, grid, dim3(256), 0, s, a);
   hipLaunchKernelGGL(attn_decode_merge_kernel, dim3(a.dm.Hq, a.B), dim3(D), 0, s, a);
   return hipGetLastError();
 }

@@ -300,6 +300,122 @@ bool launch_gemm_nt_small(const GemmArgs& g, bool out_f32, hipStream_t s, hipErr
 
 }  // namespace cca
 
+// ------------------------------------------------------------------ skinny, split K
+// C = A B^T for the decode step's few rows (M <= 256) spread over the whole
+// chip: work-group = 32 rows x 32 columns x one of KS slices of K (KS chosen so
+// that the grid holds about 256 work-groups).  Its four waves take a quarter
+// of the slice each and issue the loads of four 16-wide k steps (both
+// fragments, 16 bytes per lane) together before their MFMAs; the four partial
+// tiles are summed in LDS in a fixed order and written to an fp32 partial
+// buffer [KS, Mp, Np]; a second kernel sums the KS partials in order and
+// writes C (fp32 or bf16).  Same operand conventions as the small-M kernel.
+namespace cca {
+namespace {
+
+constexpr int SK_WGS = 256;      // target work-groups
+constexpr int SK_MAX_PART = SK_WGS * 32 * 32;   // partial floats at most (KS > 1)
+
+__global__ __launch_bounds__(256) void gemm_skinny_partial_kernel(GemmArgs g, int kc, int Mp,
+                                                                  int Np, float* part) {
+  __shared__ float red[4][32][33];
+  const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 32, ks = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int m = m0 + l32, n = n0 + l32;
+  // rows past M or N read row 0 (valid memory); their sums land in the
+  // partial buffer's padding and are never read
+  const bf16* arow = reinterpret_cast<const bf16*>(g.a) + (long)(m < g.M ? m : 0) * g.lda;
+  const int nn = n < g.N ? n : 0;
+  int sg = 0;
+  if (g.b_nseg > 1 && nn >= g.b_start[1]) sg = 1;
+  if (g.b_nseg > 2 && nn >= g.b_start[2]) sg = 2;
+  const bf16* brow =
+      reinterpret_cast<const bf16*>(g.b_ptr[sg]) + (long)(nn - g.b_start[sg]) * g.ldb;
+  const int kw = kc / 4, k0 = ks * kc + wave * kw;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  for (int kb = k0; kb < k0 + kw; kb += 64) {
+    bf16x8 af[4], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = kb + 16 * i + 8 * hi;
+      af[i] = *reinterpret_cast<const bf16x8*>(arow + k);
+      bfr[i] = *reinterpret_cast<const bf16x8*>(brow + k);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[i], acc, 0, 0, 0);
+  }
+  // D layout: lane holds column l32 (n), rows 8*(r/4) + 4*hi + r%4 (m)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[wave][8 * (r >> 2) + 4 * hi + (r & 3)][l32] = acc[r];
+  __syncthreads();
+  float* pb = part + ((long)ks * Mp + m0) * Np + n0;
+  for (int e = threadIdx.x; e < 32 * 32; e += 256) {
+    const int mi = e / 32, ni = e % 32;
+    pb[(long)mi * Np + ni] = ((red[0][mi][ni] + red[1][mi][ni]) + red[2][mi][ni]) + red[3][mi][ni];
+  }
+}
+
+__device__ __forceinline__ void store4s(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void store4s(bf16* p, f32x4 v) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void gemm_skinny_reduce_kernel(GemmArgs g, int KS, int Mp, int Np,
+                                                                 const float* part) {
+  const int nq = g.N / 4;
+  const long q = (long)blockIdx.x * 256 + threadIdx.x;   // group of 4 columns
+  if (q >= (long)g.M * nq) return;
+  const int m = (int)(q / nq), n = (int)(q % nq) * 4;
+  f32x4 s = *reinterpret_cast<const f32x4*>(part + (long)m * Np + n);
+  for (int z = 1; z < KS; ++z) s += *reinterpret_cast<const f32x4*>(part + ((long)z * Mp + m) * Np + n);
+  int cs = 0;
+  if (g.c_nseg > 1 && m >= g.c_start[1]) cs = 1;
+  if (g.c_nseg > 2 && m >= g.c_start[2]) cs = 2;
+  store4s(reinterpret_cast<OutT*>(g.c_ptr[cs]) + (long)(m - g.c_start[cs]) * g.ldc + n, s);
+}
+
+}  // namespace
+
+size_t gemm_skinny_part_floats() { return SK_MAX_PART; }
+
+// Launches the split-K pair when it suits the shape (M <= 256, fewer than 64
+// output tiles of 32 x 32, K a multiple of 256 so that four waves get whole
+// 16-wide steps in every slice, N and ldc multiples of 4 for the 4-wide output
+// stores, and at least two slices to go around); false (nothing launched)
+// otherwise.
+bool launch_gemm_skinny(const GemmArgs& g, bool out_f32, float* part, hipStream_t s,
+                        hipError_t* err) {
+  if (part == nullptr || g.M <= 0 || g.M > 256 || g.K % 256 != 0 || g.lda % 8 != 0 ||
+      g.ldb % 8 != 0 || g.N % 4 != 0 || g.ldc % 4 != 0)
+    return false;
+  const int mb = (g.M + 31) / 32, nb = (g.N + 31) / 32;
+  // with 64 or more 32 x 32 tiles the small-M kernel (one launch, eight
+  // waves per tile) fills enough CUs; the second launch would cost more
+  if (mb * nb >= 64) return false;
+  int KS = 1;
+  while ((long)mb * nb * KS * 2 <= SK_WGS && g.K % (KS * 2 * 256) == 0) KS *= 2;
+  if (KS < 2) return false;
+  const int Mp = mb * 32, Np = nb * 32;
+  if ((long)KS * Mp * Np > SK_MAX_PART) return false;
+  hipLaunchKernelGGL(gemm_skinny_partial_kernel, dim3(nb, mb, KS), dim3(256), 0, s, g, g.K / KS,
+                     Mp, Np, part);
+  const long groups = (long)g.M * (g.N / 4);
+  const dim3 rgrid((unsigned)((groups + 255) / 256));
+  if (out_f32)
+    hipLaunchKernelGGL(gemm_skinny_reduce_kernel<float>, rgrid, dim3(256), 0, s, g, KS, Mp, Np,
+                       (const float*)part);
+  else
+    hipLaunchKernelGGL(gemm_skinny_reduce_kernel<bf16>, rgrid, dim3(256), 0, s, g, KS, Mp, Np,
+                       (const float*)part);
+  *err = hipGetLastError();
+  return true;
+}
+
+}  // namespace cca
+
 // ------------------------------------------------------------------ helpers
 // Transpose of a bf16 matrix through a 64 x 64 LDS tile (16-byte loads and
 // stores), and the fixed-order sum of split-K partials.  They let the
