@@ -577,6 +577,8 @@ cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, cons
       ab.qT = t;
       ab.kT = t + align256((size_t)B * dm.nq * sp * esize(dm));
       ab.dOT = (char*)ab.kT + align256((size_t)B * dm.nk * sp * esize(dm));
+      ab.dk2 = (float*)((char*)ab.dOT + align256((size_t)B * dm.nq * sp * esize(dm)));
+      ab.dv2 = (float*)((char*)ab.dk2 + align256((size_t)B * S * dm.nk * 4));
     }
     CCA_TRY_HIP(timed(h, "bwd_attn", s, [&] { return launch_attn_bwd(ab, s); }));
 

@@ -10,7 +10,10 @@
 //   prep  — Q''^T, K''^T, dO^T (channel-major copies, rows padded to s_pad) and
 //           D = rowsum(dO * O) from the saved fp32 O;
 //   dkdv  — work-group = 128 keys of one KV head, 4 waves of 32 keys; loops over
-//           the query blocks (32 queries) of every head of the group:
+//           the query blocks (32 queries) of every head of the group; two
+//           work-groups share each key block's query range (first and second
+//           half, the second writing to scratch that a small kernel adds in),
+//           so that the causal triangle spreads over twice as many CUs:
 //             S = Q K^T, dP = dO V^T (A = Q / dO rows from LDS, B = the wave's
 //             K / V rows held in registers), P and dS in registers, then
 //             dV += P^T dO and dK += dS^T Q (A = P^T / dS^T straight from the
@@ -192,7 +195,10 @@ void bwd_dkdv_kernel(AttnBwdArgs a) {
   __shared__ __attribute__((aligned(16))) DkdvStage stg[2];
   const Dims& dm = a.dm;
   const int S = a.S, G = dm.G;
-  const int k0 = blockIdx.x * 128, g = blockIdx.y, b = blockIdx.z;   // low blocks = most work
+  // two work-groups per key block, each taking half of its query blocks (the
+  // first half holds the diagonal); low blocks = most work, dispatched first
+  const int part = blockIdx.x & 1;
+  const int k0 = (blockIdx.x >> 1) * 128, g = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int kw0 = k0 + wave * 32;
@@ -219,17 +225,21 @@ void bwd_dkdv_kernel(AttnBwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.0f;
 
-  // steps: (head hh of the group, query block) for query blocks starting at k0
-  const int qb0 = k0 / TB;
-  const int nqb = (S + TB - 1) / TB - qb0;
+  // steps: (head hh of the group, query block) for this part's query blocks
+  const int nqb_all = (S + TB - 1) / TB - k0 / TB;
+  const int nfirst = (nqb_all + 1) / 2;
+  const int qb0 = k0 / TB + (part ? nfirst : 0);
+  const int nqb = part ? nqb_all - nfirst : nfirst;
   const int nsteps = G * nqb;
   const int prow = perm_row(l32);
   auto head_of = [&](int s) { return g * G + s / nqb; };
   auto q0_of = [&](int s) { return (qb0 + s % nqb) * TB; };
   DkdvRegs pre;
-  dkdv_load(a, b, head_of(0), q0_of(0), t, pre);
-  dkdv_store(stg[0], t, pre);
-  if (nsteps > 1) dkdv_load(a, b, head_of(1), q0_of(1), t, pre);
+  if (nsteps > 0) {
+    dkdv_load(a, b, head_of(0), q0_of(0), t, pre);
+    dkdv_store(stg[0], t, pre);
+    if (nsteps > 1) dkdv_load(a, b, head_of(1), q0_of(1), t, pre);
+  }
   __syncthreads();
 
   for (int s = 0; s < nsteps; ++s) {
@@ -288,8 +298,8 @@ void bwd_dkdv_kernel(AttnBwdArgs a) {
 
   // D layout: lane holds channel nb*32 + l32, key rows 8 (r/4) + 4 hi + r%4
   const float inv = 1.0f / sqrtf((float)D);
-  float* dkb = a.dk + ((long)(b * dm.Hkv + g) * S) * D;
-  float* dvb = a.dv + ((long)(b * dm.Hkv + g) * S) * D;
+  float* dkb = (part ? a.dk2 : a.dk) + ((long)(b * dm.Hkv + g) * S) * D;
+  float* dvb = (part ? a.dv2 : a.dv) + ((long)(b * dm.Hkv + g) * S) * D;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -300,6 +310,15 @@ void bwd_dkdv_kernel(AttnBwdArgs a) {
         dvb[(long)key * D + nb * 32 + l32] = dv[nb][r];
       }
     }
+}
+
+// dk += dk2, dv += dv2: the two halves of every key block, in a fixed order.
+__global__ __launch_bounds__(256) void bwd_dkdv_sum_kernel(float* dk, const float* dk2, float* dv,
+                                                           const float* dv2, long n4) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  reinterpret_cast<f32x4*>(dk)[i] += reinterpret_cast<const f32x4*>(dk2)[i];
+  reinterpret_cast<f32x4*>(dv)[i] += reinterpret_cast<const f32x4*>(dv2)[i];
 }
 
 // ------------------------------------------------------------------ dq
@@ -456,7 +475,7 @@ size_t attn_bwd_transpose_bytes(const Dims& dm, int B, int S) {
   const size_t sp = (size_t)(S + 63) / 64 * 64;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   return al((size_t)B * dm.nq * sp * 2) + al((size_t)B * dm.nk * sp * 2) +
-         al((size_t)B * dm.nq * sp * 2);
+         al((size_t)B * dm.nq * sp * 2) + 2 * al((size_t)B * S * dm.nk * 4);
 }
 
 hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) {
@@ -465,7 +484,12 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(a.s_pad / 64, dm.Hq + dm.Hkv, a.B), dim3(256), 0, s,
                      a);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((a.S + 127) / 128, dm.Hkv, a.B), dim3(256), 0, s, a);
+  if (!a.dk2 || !a.dv2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(2 * ((a.S + 127) / 128), dm.Hkv, a.B), dim3(256), 0, s,
+                     a);
+  const long n4 = (long)a.B * dm.Hkv * a.S * D / 4;
+  hipLaunchKernelGGL(bwd_dkdv_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                     a.dk, a.dk2, a.dv, a.dv2, n4);
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(((a.S + 127) / 128) * dm.Hq * a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }

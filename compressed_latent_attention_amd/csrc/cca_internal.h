@@ -181,10 +181,14 @@ struct AttnBwdArgs {
   void* kT;          // K''^T [B,Hkv,d,s_pad]
   void* dOT;         // dO^T  [B,Hq,d,s_pad]
   int s_pad;         // S rounded up to a multiple of 64
+  // dK / dV of the second half of each key block's query range (fp32, same
+  // layout as dk / dv), added into dk / dv before the kernels return
+  float* dk2;
+  float* dv2;
 };
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
-// Bytes of the transposed copies the MFMA attention backward needs (0 when
-// the config takes the generic path).
+// Bytes of the MFMA attention backward's workspace: the transposed copies and
+// the second-half dK / dV partials (0 when the config takes the generic path).
 size_t attn_bwd_transpose_bytes(const Dims& dm, int B, int S);
 
 struct MixBwdArgs {
