@@ -32,7 +32,7 @@
 // row index swapped, so that the 8 accumulator registers a lane passes on
 // cover 8 consecutive queries (keys) and P / dS feed the next MFMA without a
 // shuffle.  Tiles are staged through registers into padded LDS rows
-// (conflict-free 16-byte reads), double-buffered with one barrier per step.
+// (conflict-free 16-byte reads), with one barrier per step.
 #include "cca_internal.h"
 
 namespace cca {
@@ -147,6 +147,9 @@ struct DkdvRegs {
   float lse2, dsum;
 };
 
+// Registers of one step: buffer loads whose resources end at row S - 1, so rows
+// past the sequence read as zero without a branch (the loop body stays one
+// block); lse of a query past S becomes +inf (its P is zero).
 __device__ __forceinline__ void dkdv_load(const AttnBwdArgs& a, int b, int h, int q0, int t,
                                           DkdvRegs& r) {
   const Dims& dm = a.dm;
@@ -155,22 +158,31 @@ __device__ __forceinline__ void dkdv_load(const AttnBwdArgs& a, int b, int h, in
   const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + (long)b * S * dm.nq + h * D;
   const f16* qtb = reinterpret_cast<const f16*>(a.qT) + ((long)(b * dm.Hq + h) * D) * a.s_pad;
   const f16* dtb = reinterpret_cast<const f16*>(a.dOT) + ((long)(b * dm.Hq + h) * D) * a.s_pad;
+  const __amdgpu_buffer_rsrc_t qrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)qb, 0, S * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t drs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)dob, 0, ((S - 1) * dm.nq + D) * 2, 0x00020000);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int f = t + 256 * i;
     const int row = f >> 4, ch = (f & 15) * 8;           // natural: 32 rows x 16 chunks
     const int q = q0 + row;
-    r.qn[i] = q < S ? *reinterpret_cast<const bf16x8*>(qb + (long)q * D + ch) : zero8();
-    r.don[i] = q < S ? *reinterpret_cast<const bf16x8*>(dob + (long)q * dm.nq + ch) : zero8();
+    r.qn[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, (q * D + ch) * 2, 0, 0));
+    r.don[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(drs, (q * dm.nq + ch) * 2, 0, 0));
     const int c = f >> 2, col = (f & 3) * 8;             // transposed: 128 rows x 4 chunks
     r.qt[i] = *reinterpret_cast<const f16x8*>(qtb + (long)c * a.s_pad + q0 + col);
     r.dot[i] = *reinterpret_cast<const f16x8*>(dtb + (long)c * a.s_pad + q0 + col);
   }
-  if (t < TB) {
-    const int q = q0 + t;
-    r.lse2 = q < S ? a.lse[(long)(b * dm.Hq + h) * S + q] * kLog2e : INFINITY;
-    r.dsum = q < S ? a.Dsum[(long)(b * dm.Hq + h) * S + q] : 0.0f;
-  }
+  // every thread loads query q0 + t % 32 (the stage stores the 32 values from
+  // all waves: the same value to the same address)
+  const int q = q0 + (t & (TB - 1));
+  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.lse + (long)(b * dm.Hq + h) * S), 0, S * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.Dsum + (long)(b * dm.Hq + h) * S), 0, S * 4, 0x00020000);
+  const float lv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, q * 4, 0, 0));
+  r.dsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, q * 4, 0, 0));
+  r.lse2 = fmaf(lv, kLog2e, q < S ? 0.0f : INFINITY);
 }
 
 __device__ __forceinline__ void dkdv_store(DkdvStage& st, int t, const DkdvRegs& r) {
@@ -184,15 +196,30 @@ __device__ __forceinline__ void dkdv_store(DkdvStage& st, int t, const DkdvRegs&
     *reinterpret_cast<f16x8*>(st.qt + c * TLD + col) = r.qt[i];
     *reinterpret_cast<f16x8*>(st.dot + c * TLD + col) = r.dot[i];
   }
-  if (t < TB) {
-    st.lse2[t] = r.lse2;
-    st.dsum[t] = r.dsum;
+  st.lse2[t & (TB - 1)] = r.lse2;
+  st.dsum[t & (TB - 1)] = r.dsum;
+}
+
+// S = Q K^T and dP = dO V^T of one step: the stage's Q / dO rows (A, read with
+// the permuted row so that P / dS come out as 8 consecutive queries per lane)
+// times the wave's K / V rows held in registers (B).
+__device__ __forceinline__ void dkdv_sdp(const DkdvStage& st, const bf16x8 (&kf)[8],
+                                         const bf16x8 (&vf)[8], int prow, int hi, f32x16& sacc,
+                                         f32x16& pacc) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(st.qn + prow * NLD + ks * 16 + hi * 8);
+    const bf16x8 da = *reinterpret_cast<const bf16x8*>(st.don + prow * NLD + ks * 16 + hi * 8);
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sacc, 0, 0, 0);
+    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], pacc, 0, 0, 0);
   }
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(AttnBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) DkdvStage stg[2];
+  __shared__ __attribute__((aligned(16))) DkdvStage stg[3];
   const Dims& dm = a.dm;
   const int S = a.S, G = dm.G;
   // two work-groups per key block, each taking half of its query blocks (the
@@ -232,30 +259,37 @@ void bwd_dkdv_kernel(AttnBwdArgs a) {
   const int nqb = part ? nqb_all - nfirst : nfirst;
   const int nsteps = G * nqb;
   const int prow = perm_row(l32);
-  auto head_of = [&](int s) { return g * G + s / nqb; };
-  auto q0_of = [&](int s) { return (qb0 + s % nqb) * TB; };
-  DkdvRegs pre;
+  // step s clamped to the last one: the pipeline's loads past the end repeat
+  // it into a stage nobody reads again
+  auto head_of = [&](int s) { return g * G + min(s, nsteps - 1) / nqb; };
+  auto q0_of = [&](int s) { return (qb0 + min(s, nsteps - 1) % nqb) * TB; };
+
+  // Software pipeline over three LDS stages (step s in stage s % 3).  Iteration
+  // s computes S and dP of step s + 1 and the softmax of step s in one block
+  // (the MFMAs run while the vector ALU exponentiates), then dV and dK of step
+  // s; it stores the registers of step s + 2 into the stage step s - 1 used and
+  // loads step s + 3 into registers.  A barrier per step waits only for LDS
+  // operations, so the global loads stay in flight across it.  Steps whose
+  // queries all precede the wave's keys are computed like the others: their P
+  // is exactly zero.
   if (nsteps > 0) {
+    DkdvRegs pre;
     dkdv_load(a, b, head_of(0), q0_of(0), t, pre);
     dkdv_store(stg[0], t, pre);
-    if (nsteps > 1) dkdv_load(a, b, head_of(1), q0_of(1), t, pre);
-  }
-  __syncthreads();
+    dkdv_load(a, b, head_of(1), q0_of(1), t, pre);
+    dkdv_store(stg[1], t, pre);
+    dkdv_load(a, b, head_of(2), q0_of(2), t, pre);
+    __syncthreads();
+    f32x16 sacc, pacc;
+    dkdv_sdp(stg[0], kf, vf, prow, hi, sacc, pacc);
 
-  for (int s = 0; s < nsteps; ++s) {
-    const DkdvStage& st = stg[s & 1];
-    const int q0 = q0_of(s);
-    if (q0 + TB - 1 >= kw0) {                // else every query precedes every key of the wave
-      f32x16 sacc, pacc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(st.qn + prow * NLD + ks * 16 + hi * 8);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(st.don + prow * NLD + ks * 16 + hi * 8);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], pacc, 0, 0, 0);
-      }
+    for (int s = 0; s < nsteps; ++s) {
+      const DkdvStage& st = stg[s % 3];
+      const int q0 = q0_of(s);
+      dkdv_store(stg[(s + 2) % 3], t, pre);
+      dkdv_load(a, b, head_of(s + 3), q0_of(s + 3), t, pre);
+      f32x16 sn, pn;
+      dkdv_sdp(stg[(s + 1) % 3], kf, vf, prow, hi, sn, pn);
       // lane (key l32, hi): register r is query q0 + 16 (r / 8) + 8 hi + r % 8
       f16x8 pf[2], sf[2];
 #pragma unroll
@@ -288,12 +322,11 @@ void bwd_dkdv_kernel(AttnBwdArgs a) {
           dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pf[ks], db, dv[nb], 0, 0, 0);
           dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sf[ks], qbv, dk[nb], 0, 0, 0);
         }
+      sacc = sn;
+      pacc = pn;
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // this wave's LDS reads and stores are done
+      __builtin_amdgcn_s_barrier();
     }
-    if (s + 1 < nsteps) {
-      dkdv_store(stg[(s + 1) & 1], t, pre);
-      if (s + 2 < nsteps) dkdv_load(a, b, head_of(s + 2), q0_of(s + 2), t, pre);
-    }
-    __syncthreads();
   }
 
   // D layout: lane holds channel nb*32 + l32, key rows 8 (r/4) + 4 hi + r%4
