@@ -4,11 +4,12 @@
 //
 // The convolution of one head is a GEMM: out[t, c] = sum_{j, c'} u[t - j, c'] *
 // A_j[c, c'] with M = tokens, N = channels, K = k * d.  The fp32 latent tile of
-// the head (64 tokens plus the k - 1 halo tokens before them) is staged in LDS
-// with coalesced 16-byte loads; operand A is read from it in two bf16 halves
-// (hi = bf16(u), lo = bf16(u - hi)), so the product keeps ~16 mantissa bits of
-// q~ and k~ with fp32 accumulation; operand B is the bf16 tap row A_j[c, 8
-// channels] read from L2.  With lane = output channel and registers = tokens,
+// the head (64 tokens plus the k - 1 halo tokens before them) is read with
+// coalesced 16-byte loads and staged in LDS as two bf16 halves, hi = bf16(u)
+// and lo = bf16(u - hi), each converted once; operand A is read from both, so
+// the product keeps ~16 mantissa bits of q~ and k~ with fp32 accumulation
+// (hi + lo also stands in for u in QK-mean, and V' = bf16(v~) is hi itself);
+// operand B is the bf16 tap row A_j[c, 8 channels] read from L2.  With lane = output channel and registers = tokens,
 // everything QK-mean needs (the same token and channel of the group's query
 // heads and its K head) and both channels of a RoPE pair (c, c + d/2) sit in
 // one lane.
@@ -21,8 +22,9 @@ namespace {
 
 constexpr int D = 128;
 constexpr int TW = 64;               // tokens per work-group
-constexpr int ULD = D + 4;           // LDS row stride (floats): 528 B, conflict-free b128 reads
+constexpr int ULD = D + 8;           // LDS row stride (bf16): 272 B, conflict-free b128 reads
 constexpr int UROWS = TW + kMaxConv - 1;
+constexpr int UHALF = UROWS * ULD;   // lo rows follow the hi rows
 
 typedef f32x16 Acc2[2];              // [channel block]
 
@@ -33,41 +35,85 @@ __device__ __forceinline__ void zero(Acc2& a) {
     for (int r = 0; r < 16; ++r) a[j][r] = 0.0f;
 }
 
-// Rows t0 - halo .. t0 + TW - 1 of latent column block `col` into LDS (zero
-// outside [0, S)).  LDS row i holds token t0 - halo + i.
-__device__ __forceinline__ void load_tile(float* u, const float* qkv_b, int nqkv, int col, int S,
+// Rows t0 - halo .. t0 + TW - 1 of latent column block `col` into LDS as hi
+// (u[0 .. UHALF)) and lo (u[UHALF ..)) bf16 halves (zero outside [0, S)).  LDS
+// row i holds token t0 - halo + i.  The loads go through a buffer resource over
+// the tile's rows inside [0, S) (a row before it wraps to a huge offset):
+// out-of-range rows read as zero without a branch, so each batch of four loads is in flight
+// together before its conversions and LDS stores.
+__device__ __forceinline__ void load_tile(bf16* u, const float* qkv_b, int nqkv, int col, int S,
                                           int t0, int halo) {
-  const int rows = TW + halo;
-  for (int e = threadIdx.x; e < rows * (D / 4); e += 256) {
-    const int i = e / (D / 4), ch = (e % (D / 4)) * 4;
-    const int t = t0 - halo + i;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (t >= 0 && t < S) v = *reinterpret_cast<const f32x4*>(qkv_b + (long)t * nqkv + col + ch);
-    *reinterpret_cast<f32x4*>(u + i * ULD + ch) = v;
+  const int n = (TW + halo) * (D / 4);
+  // resource over the tile's rows inside [0, S), based at its first one
+  const int r0 = max(t0 - halo, 0), r1 = min(S, t0 + TW);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qkv_b + (long)r0 * nqkv + col), 0, r1 > r0 ? ((r1 - r0 - 1) * nqkv + D) * 4 : 0,
+      0x00020000);
+  constexpr int NB = 4;
+  for (int base = 0; base < n; base += NB * 256) {
+    f32x4 v[NB];
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      const int e = min(base + r * 256 + (int)threadIdx.x, n - 1);
+      const int i = e / (D / 4), ch = (e % (D / 4)) * 4;
+      const int t = t0 - halo + i;
+      v[r] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((t - r0) * nqkv + ch) * 4, 0, 0));
+    }
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      const int e = base + r * 256 + (int)threadIdx.x;
+      if (e < n) {
+        const int i = e / (D / 4), ch = (e % (D / 4)) * 4;
+        bf16x4 h, l;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          h[q] = (bf16)v[r][q];
+          l[q] = (bf16)(v[r][q] - (float)h[q]);
+        }
+        *reinterpret_cast<bf16x4*>(u + i * ULD + ch) = h;
+        *reinterpret_cast<bf16x4*>(u + UHALF + i * ULD + ch) = l;
+      }
+    }
   }
 }
 
+// cos / sin of channel pair c_lo for the 16 token rows a lane's accumulator
+// registers hold (row r: first + 8 (r / 4) + r % 4, relative to the tile), all
+// 16 loads in flight together; (1, 0) without RoPE.  Rows past the sequence
+// (nrem = tokens of the tile inside it) read the last row: no branch, and
+// their results are never stored.
+__device__ __forceinline__ void load_rope(float2 (&cs)[16], const float2* rope_t0, int first,
+                                          int c_lo, int nrem) {
+  if (rope_t0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tr = min(first + 8 * (r >> 2) + (r & 3), nrem - 1);
+      cs[r] = rope_t0[tr * (D / 2) + c_lo];
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cs[r] = make_float2(1.f, 0.f);
+  }
+}
+
+// The pre-convolution value hi + lo of LDS row i, channel c.
+__device__ __forceinline__ float uval(const bf16* u, int i, int c) {
+  return (float)u[i * ULD + c] + (float)u[UHALF + i * ULD + c];
+}
+
 // acc += conv of one head whose tile is in LDS (row of token t: t - t0 + halo).
-__device__ __forceinline__ void conv_head(Acc2& acc, const float* u, int halo, int tw0_rel,
+__device__ __forceinline__ void conv_head(Acc2& acc, const bf16* u, int halo, int tw0_rel,
                                           const bf16* taps, int k, int cb0, int lane) {
   const int l32 = lane & 31, hi = lane >> 5;
   for (int j = 0; j < k; ++j) {
-    const float* urow = u + (tw0_rel + l32 - j + halo) * ULD + hi * 8;
+    const bf16* urow = u + (tw0_rel + l32 - j + halo) * ULD + hi * 8;
     const bf16* trow0 = taps + ((long)j * D + cb0 * 32 + l32) * D + hi * 8;
     const bf16* trow1 = trow0 + 64 * D;
-#pragma unroll 2
+#pragma unroll 4
     for (int ks = 0; ks < 8; ++ks) {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(urow + ks * 16);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(urow + ks * 16 + 4);
-      bf16x8 ahi, alo;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16 h0 = (bf16)x0[e], h1 = (bf16)x1[e];
-        ahi[e] = h0;
-        ahi[e + 4] = h1;
-        alo[e] = (bf16)(x0[e] - (float)h0);
-        alo[e + 4] = (bf16)(x1[e] - (float)h1);
-      }
+      const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(urow + ks * 16);
+      const bf16x8 alo = *reinterpret_cast<const bf16x8*>(urow + UHALF + ks * 16);
       const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(trow0 + ks * 16);
       const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(trow1 + ks * 16);
       acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b0, acc[0], 0, 0, 0);
@@ -80,8 +126,8 @@ __device__ __forceinline__ void conv_head(Acc2& acc, const float* u, int halo, i
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mix_fwd_mfma_kernel(MixArgs a) {
-  __shared__ __attribute__((aligned(16))) float uk[UROWS * ULD];   // k~ tile
-  __shared__ __attribute__((aligned(16))) float uq[UROWS * ULD];   // current q~ tile, then v~
+  __shared__ __attribute__((aligned(16))) bf16 uk[2 * UHALF];   // k~ tile (hi, lo)
+  __shared__ __attribute__((aligned(16))) bf16 uq[2 * UHALF];   // current q~ tile, then v~
   const Dims& dm = a.dm;
   const int G = dm.G, S = a.S;
   const int g = blockIdx.y, b = blockIdx.z;
@@ -100,6 +146,7 @@ void mix_fwd_mfma_kernel(MixArgs a) {
   // register r holds token tw0_rel + 8*(r/4) + 4*hi + r%4 (relative to t0)
   auto trel = [&](int r) { return tw0_rel + 8 * (r >> 2) + 4 * hi + (r & 3); };
 
+  const float2* rope_t0 = rope ? a.rope + (long)t0 * (D / 2) : nullptr;
   load_tile(uk, qkv_b, dm.nqkv, kcol, S, t0, hk);
   __syncthreads();
   Acc2 kacc, qacc, mpost, mpre;
@@ -118,7 +165,10 @@ void mix_fwd_mfma_kernel(MixArgs a) {
     conv_head(qacc, uq, hq, tw0_rel,
               reinterpret_cast<const bf16*>(a.conv_q) + (long)h * dm.kq * D * D, dm.kq, cb0,
               lane);
-    bf16* qo = reinterpret_cast<bf16*>(a.q_out) + ((long)(b * dm.Hq + h) * S) * D;
+    // tile bases plus 32-bit offsets (tokens relative to t0)
+    bf16* qo = reinterpret_cast<bf16*>(a.q_out) + ((long)(b * dm.Hq + h) * S + t0) * D;
+    float2 csr[16];
+    load_rope(csr, rope_t0, trel(0), c_lo, S - t0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tr = trel(r);
@@ -128,27 +178,28 @@ void mix_fwd_mfma_kernel(MixArgs a) {
       for (int cb = 0; cb < 2; ++cb) {
         const int c = c_lo + 64 * cb;
         const float qh = qacc[cb][r], kh = kacc[cb][r];
-        const float qp = uq[(tr + hq) * ULD + c];
-        const float kp = uk[(tr + hk) * ULD + c];
+        const float qp = uval(uq, tr + hq, c);
+        const float kp = uval(uk, tr + hk, c);
         mpost[cb][r] += qh;
         mpre[cb][r] += qp;
         x[cb] = qh + A * (qp + kp) + Bc * (qh + kh);
       }
       if (t < S) {
-        float2 cs = make_float2(1.f, 0.f);
-        if (rope) cs = a.rope[(long)t * (D / 2) + c_lo];
-        qo[(long)t * D + c_lo] = (bf16)(x[0] * cs.x - x[1] * cs.y);
-        qo[(long)t * D + c_lo + 64] = (bf16)(x[1] * cs.x + x[0] * cs.y);
+        const float2 cs = csr[r];
+        qo[tr * D + c_lo] = (bf16)(x[0] * cs.x - x[1] * cs.y);
+        qo[tr * D + c_lo + 64] = (bf16)(x[1] * cs.x + x[0] * cs.y);
       }
-      __builtin_amdgcn_sched_barrier(0);     // keep the epilogue's loads from piling up
     }
   }
 
   // k' = k^ + a/2 (mean_g q~ + k~) + b/2 (mean_g q^ + k^)
   const float invG = 1.0f / (float)G;
-  bf16* ko = reinterpret_cast<bf16*>(a.k_out) + ((long)(b * dm.Hkv + g) * S) * D;
-  bf16* ko2 = a.k_out2 ? reinterpret_cast<bf16*>(a.k_out2) + ((long)(b * dm.Hkv + g) * a.cap2) * D
-                       : nullptr;
+  bf16* ko = reinterpret_cast<bf16*>(a.k_out) + ((long)(b * dm.Hkv + g) * S + t0) * D;
+  bf16* ko2 = a.k_out2
+                  ? reinterpret_cast<bf16*>(a.k_out2) + ((long)(b * dm.Hkv + g) * a.cap2 + t0) * D
+                  : nullptr;
+  float2 csr[16];
+  load_rope(csr, rope_t0, trel(0), c_lo, S - t0);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int tr = trel(r);
@@ -158,22 +209,20 @@ void mix_fwd_mfma_kernel(MixArgs a) {
     for (int cb = 0; cb < 2; ++cb) {
       const int c = c_lo + 64 * cb;
       const float kh = kacc[cb][r];
-      const float kp = uk[(tr + hk) * ULD + c];
+      const float kp = uval(uk, tr + hk, c);
       x[cb] = kh + A * (mpre[cb][r] * invG + kp) + Bc * (mpost[cb][r] * invG + kh);
     }
     if (t < S) {
-      float2 cs = make_float2(1.f, 0.f);
-      if (rope) cs = a.rope[(long)t * (D / 2) + c_lo];
+      const float2 cs = csr[r];
       const bf16 lo = (bf16)(x[0] * cs.x - x[1] * cs.y);
       const bf16 hv = (bf16)(x[1] * cs.x + x[0] * cs.y);
-      ko[(long)t * D + c_lo] = lo;
-      ko[(long)t * D + c_lo + 64] = hv;
+      ko[tr * D + c_lo] = lo;
+      ko[tr * D + c_lo + 64] = hv;
       if (ko2) {
-        ko2[(long)t * D + c_lo] = lo;
-        ko2[(long)t * D + c_lo + 64] = hv;
+        ko2[tr * D + c_lo] = lo;
+        ko2[tr * D + c_lo + 64] = hv;
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 
   // value shift: v~ rows t0 - 1 .. t0 + TW - 1 into LDS (reusing the q tile),
@@ -192,7 +241,7 @@ void mix_fwd_mfma_kernel(MixArgs a) {
       const int tr = e / D, c = e % D;
       const int t = t0 + tr;
       if (t >= S) break;
-      const bf16 v = (bf16)uq[(tr + (c >= first_shift ? 0 : 1)) * ULD + c];
+      const bf16 v = uq[(tr + (c >= first_shift ? 0 : 1)) * ULD + c];   // hi = bf16(v~)
       if (vo) vo[(long)t * D + c] = v;
       if (vo2) vo2[(long)t * D + c] = v;
     }
@@ -213,7 +262,7 @@ void mix_fwd_mfma_kernel(MixArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         // tokens at or past S are zero: the padding of V'^T up to s_pad
-        const bf16 v = (bf16)(t + i < S ? uq[(8 * m + i + row_off) * ULD + c] : 0.0f);
+        const bf16 v = t + i < S ? uq[(8 * m + i + row_off) * ULD + c] : (bf16)0.0f;
         pk[i] = (_Float16)(float)v;
       }
       *reinterpret_cast<f16x8*>(vt + (long)c * a.s_pad + t) = pk;
