@@ -61,6 +61,13 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
   const int kend = min(nkeys, k0 + CK);
   const bf16* kb = reinterpret_cast<const bf16*>(a.k) + (long)b * a.kv_bs + (long)g * a.kv_hs;
   const bf16* vb = reinterpret_cast<const bf16*>(a.v) + (long)b * a.kv_bs + (long)g * a.kv_hs;
+  // K and V through buffer resources that end at key nkeys - 1: keys past the
+  // sequence read as zero without a branch (their scores are masked anyway),
+  // so the load loops stay single blocks with every load in flight
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, nkeys * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, nkeys * D * 2, 0x00020000);
 
   // ---- 1. scores.  A operand: lane (l32 = query row, hi) holds channels
   // 16 ks + 8 hi + 0..7 of query g*G + l32 (zero rows past G).
@@ -83,20 +90,19 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
     const bool valid = key < kend;
     bf16x8 kf[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (valid) {
-        kf[ks] = *reinterpret_cast<const bf16x8*>(kb + (long)key * D + ks * 16 + hi * 8);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kf[ks][e] = (bf16)0.0f;
-      }
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      kf[ks] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, (key * D + ks * 16 + hi * 8) * 2, 0, 0));
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[ks], acc, 0, 0, 0);
+    // all eight K loads in flight before the MFMAs (masks: 0x020 vector
+    // memory read, 0x008 MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     // D[query][key]: lane holds key column l32, query rows 8*(r/4) + 4*hi + r%4
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -137,22 +143,22 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
   for (int q = 0; q < GQ; ++q)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[q][e] = 0.0f;
-  const int i0 = wave * (CK / NW);
-  const int i1 = min(i0 + CK / NW, kend - k0);
-  const bf16* vbase = vb + (long)k0 * D + cc;
-#pragma unroll 4
-  for (int i = i0 + slot; i < i1; i += 4) {
-    const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(vbase + (long)i * D);
+  // keys past the sequence have p = 0 and read V as zero; rows q >= G use
+  // unwritten scores and are never stored, so the loop has no branch
+  const int i0 = wave * (CK / NW) + slot;
+#pragma unroll 8
+  for (int it = 0; it < CK / NW / 4; ++it) {
+    const int i = i0 + 4 * it;
+    const bf16x8 v8 = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, ((k0 + i) * D + cc) * 2, 0, 0));
     const f32x4 pa = *reinterpret_cast<const f32x4*>(&ps[i * PW]);
     f32x4 pb = pa;
     if (GQ > 4) pb = *reinterpret_cast<const f32x4*>(&ps[i * PW + 4]);
 #pragma unroll
     for (int q = 0; q < GQ; ++q) {
-      if (q < G) {
-        const float p = q < 4 ? pa[q] : pb[q - 4];
+      const float p = q < 4 ? pa[q] : pb[q - 4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[q][e] = fmaf(p, (float)v8[e], o[q][e]);
-      }
+      for (int e = 0; e < 8; ++e) o[q][e] = fmaf(p, (float)v8[e], o[q][e]);
     }
   }
   // the four key slots of a wave are summed with two shuffles, the waves
