@@ -85,29 +85,50 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
       for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)((float)v[e] * scale);
     }
   }
-  for (int blk = wave; blk < CK / 32; blk += NW) {
-    const int key = k0 + blk * 32 + l32;
-    const bool valid = key < kend;
-    bf16x8 kf[8];
+  // One ring of eight 16-byte fragments per lane streams the wave's whole
+  // share of the chunk: K fragment ks of the next key block is requested as
+  // soon as the MFMA that reads fragment ks of this block has been issued, and
+  // after the last block the same slots request the first eight V rows of
+  // P V, which stay in flight through the softmax.
+  constexpr int NB = CK / 32 / NW;                 // key blocks per wave
+  const int slot = lane >> 4, cc = (lane & 15) * 8;
+  const int i0 = wave * (CK / NW) + slot;          // P V: this lane's first key
+  auto kload = [&](int bi, int ks) {
+    const int key = k0 + (wave + bi * NW) * 32 + l32;
+    return __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, (key * D + ks * 16 + hi * 8) * 2, 0, 0));
+  };
+  auto vload = [&](int it) {
+    return __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, ((k0 + i0 + 4 * it) * D + cc) * 2, 0, 0));
+  };
+  bf16x8 ring[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      kf[ks] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, (key * D + ks * 16 + hi * 8) * 2, 0, 0));
+  for (int ks = 0; ks < 8; ++ks) ring[ks] = kload(0, ks);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi) {
+    const int blk = wave + bi * NW;
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[ks], acc, 0, 0, 0);
-    // all eight K loads in flight before the MFMAs (masks: 0x020 vector
-    // memory read, 0x008 MFMA)
-    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    // D[query][key]: lane holds key column l32, query rows 8*(r/4) + 4*hi + r%4
+    for (int ks = 0; ks < 8; ++ks) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], ring[ks], acc, 0, 0, 0);
+      ring[ks] = bi + 1 < NB ? kload(bi + 1, ks) : vload(ks);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {     // masks: 0x008 MFMA, 0x020 vector memory read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    const bool valid = k0 + blk * 32 + l32 < kend;
+    // D[query][key]: lane holds key column l32, query rows 8*(r/4) + 4*hi + r%4.
+    // Rows G .. GQ-1 come from zero query rows and are never read.
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int q = 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (q < G) ps[(blk * 32 + l32) * PW + q] = valid ? acc[r] : -INFINITY;
+      if (q < GQ) ps[(blk * 32 + l32) * PW + q] = valid ? acc[r] : -INFINITY;
     }
   }
   __syncthreads();
@@ -137,7 +158,6 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
   // lane = (key slot L / 16, channels 8 (L % 16) .. + 7), so one wave load
   // covers 4 whole 256-byte V rows.  The 4 key slots are summed with two
   // shuffles, the 4 waves through LDS.
-  const int slot = lane >> 4, cc = (lane & 15) * 8;
   float o[GQ][8];
 #pragma unroll
   for (int q = 0; q < GQ; ++q)
@@ -145,12 +165,14 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
     for (int e = 0; e < 8; ++e) o[q][e] = 0.0f;
   // keys past the sequence have p = 0 and read V as zero; rows q >= G use
   // unwritten scores and are never stored, so the loop has no branch
-  const int i0 = wave * (CK / NW) + slot;
-#pragma unroll 8
-  for (int it = 0; it < CK / NW / 4; ++it) {
+  // P V continues the ring: slot it % 8 holds V rows of iteration it and is
+  // refilled with iteration it + 8 once read
+  constexpr int NIT = CK / NW / 4;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const bf16x8 v8 = ring[it & 7];
+    if (it + 8 < NIT) ring[it & 7] = vload(it + 8);
     const int i = i0 + 4 * it;
-    const bf16x8 v8 = __builtin_bit_cast(
-        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, ((k0 + i) * D + cc) * 2, 0, 0));
     const f32x4 pa = *reinterpret_cast<const f32x4*>(&ps[i * PW]);
     f32x4 pb = pa;
     if (GQ > 4) pb = *reinterpret_cast<const f32x4*>(&ps[i * PW + 4]);
