@@ -3,74 +3,98 @@
 // decoding; CCA-fr §4 "Décodage").  The step streams the K and V caches once,
 // so it is bound by HBM bandwidth.
 //
-// Split over keys (flash-decoding): work-group (chunk, KV head g, sequence b)
-// takes keys [512 chunk, 512 chunk + 512) of that sequence's cache, up to its
-// position, and serves all G query heads that read KV head g, so each cache
-// byte is read once per step.
+// Split over keys (flash-decoding): about 256 work-groups in all, nsplit per
+// (KV head g, sequence b), each serving all G query heads that read head g, so
+// each cache byte is read once per step.  The 4 nsplit waves of one (b, g)
+// take its 32-key blocks round robin, so together they sweep its K and V as
+// one window; every wave keeps its own online softmax:
 //   1. S = Q K^T on MFMA: A = the G queries (rows, padded to 32 with zeros,
 //      scaled to log2 units), B = K^T straight from global memory (lane = key,
-//      16 bytes of its row per load); 4 waves x 4 blocks of 32 keys.
-//   2. The chunk's row max m and sum l of p = exp2(s - m) (scores in LDS).
-//   3. O_chunk = P V on the vector ALU: lane = 8 channels of one of 4 keys,
-//      so a wave load covers four 256-byte V rows; p broadcast from LDS.
-// Partials (O_chunk, m, l) go to the workspace; a second kernel merges the
-// chunks of each (sequence, query head) and writes O in bf16.
+//      16 bytes of its row per load).
+//   2. Block max over the 32 keys by DPP and a swizzle, rescale of the running
+//      O and l, p = exp2(s - m) to a per-wave LDS row block.
+//   3. O += P V on the vector ALU: lane = 8 channels of one of 4 keys, so a
+//      wave load covers four 256-byte V rows.
+// The next block's K and V rows are requested while the current one is
+// computed.  The four waves of a work-group merge in LDS into one partial
+// (O, m, l); a second kernel merges the partials of each (sequence, query
+// head) and writes O in bf16.
 // bf16 storage, d = 128; fp32 accumulation and softmax.
 #include "cca_internal.h"
+
+#include <algorithm>
 
 namespace cca {
 namespace {
 
 constexpr int D = 128;
-constexpr int CK = 512;          // keys per work-group
 constexpr int NW = 4;            // waves per work-group
+constexpr int TARGET_WGS = 256;  // work-groups per launch: two per CU, all resident at once
 constexpr int PSTRIDE = D + 2;   // floats per partial: O[0..D), m, l
 
-constexpr int MAX_SPLIT = 1024;  // chunks per sequence the merge kernel holds: caches up to 512K
+constexpr int MAX_SPLIT = 1024;  // work-groups per (sequence, KV head) the merge kernel holds
 
-bool fast_decode(const Dims& dm) {
-  return dm.bf16 && dm.d == D && dm.G <= kMaxGroup && dm.max_seq_len <= MAX_SPLIT * CK;
+bool fast_decode(const Dims& dm) { return dm.bf16 && dm.d == D && dm.G <= kMaxGroup; }
+
+// Max over each 32-lane half of the wave: DPP within rows of 16 lanes (swap
+// neighbours, pairs, mirror in 8, mirror in 16), then a swizzle that exchanges
+// the two rows of each half.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float half_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));    // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_mov<0x4E>(v));    // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_mov<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_mov<0x140>(v));   // row_mirror
+  // swizzle, bit mode: and_mask 0x1F, or_mask 0, xor_mask 0x10
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
 }
 
 // GQ: the group size rounded up to a power of two (the kernel is instantiated
 // for 1, 2, 4, 8), so P V keeps only that many accumulator rows in registers.
+//
+// Work-group (split, KV head g, sequence b); its wave w takes the 32-key
+// blocks (i nsplit + split) NW + w, i = 0, 1, ..., so the nsplit NW waves of
+// one (sequence, head) read consecutive 8 KB blocks and sweep its K and V as
+// one wide window.  Each wave runs its own online softmax over its blocks with
+// no barrier: while block n is scored and accumulated, the K and V rows of
+// block n + 1 are already requested (a ring of 8 + 8 fragment registers, each
+// slot refilled as soon as it has been read).  The four waves are merged in
+// LDS at the end.
 template <int GQ>
-__global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
-  constexpr int PW = GQ < 4 ? 4 : GQ;                              // p row: 16-byte aligned
-  // scores, then p; after P V the same memory holds the waves' partial O
-  __shared__ __attribute__((aligned(16))) float ps[CK * PW > NW * GQ * D ? CK * PW : NW * GQ * D];
-  __shared__ float stat[GQ][2];                                    // m, l per query
+__global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
+  constexpr int PW = 8;                              // p row per key: queries 0..7
+  constexpr int NR = GQ < 4 ? GQ : 4;                // score rows per lane half that matter
+  __shared__ __attribute__((aligned(16))) float pbuf[NW][32 * PW];   // p of the current block
+  __shared__ __attribute__((aligned(16))) float ow[NW][GQ][D];       // per-wave O, then merged
+  __shared__ float mlw[NW][GQ][2];                                   // per-wave m, l
 
   const Dims& dm = a.dm;
   const int G = dm.G;
-  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int nsplit = gridDim.x;
   const int nkeys = a.pos.p[b] + 1;
-  const int k0 = chunk * CK;
+  const int nblk = (nkeys + 31) / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  // partial of (b, query head g*G + q, chunk): part[((b*Hq + g*G + q)*nsplit + chunk)*PSTRIDE]
-  float* part = a.part + ((long)(b * dm.Hq + g * G) * nsplit + chunk) * PSTRIDE;
-  if (k0 >= nkeys) {                         // chunk past this sequence's position
-    if (threadIdx.x < G) {
-      part[(long)threadIdx.x * nsplit * PSTRIDE + D] = -INFINITY;
-      part[(long)threadIdx.x * nsplit * PSTRIDE + D + 1] = 0.0f;
-    }
-    return;
-  }
-  const int kend = min(nkeys, k0 + CK);
+  const int first = split * NW + wave, stride = nsplit * NW;
+  const int nit = first < nblk ? (nblk - first + stride - 1) / stride : 0;
   const bf16* kb = reinterpret_cast<const bf16*>(a.k) + (long)b * a.kv_bs + (long)g * a.kv_hs;
   const bf16* vb = reinterpret_cast<const bf16*>(a.v) + (long)b * a.kv_bs + (long)g * a.kv_hs;
   // K and V through buffer resources that end at key nkeys - 1: keys past the
-  // sequence read as zero without a branch (their scores are masked anyway),
-  // so the load loops stay single blocks with every load in flight
+  // sequence (the tail of the last block, the prefetch after it) read as zero
+  // without a branch; their scores are masked
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, nkeys * D * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, nkeys * D * 2, 0x00020000);
 
-  // ---- 1. scores.  A operand: lane (l32 = query row, hi) holds channels
-  // 16 ks + 8 hi + 0..7 of query g*G + l32 (zero rows past G).
+  // S = Q K^T on MFMA.  A operand: lane (l32 = query row, hi) holds channels
+  // 16 ks + 8 hi + 0..7 of query g*G + l32 (zero rows past G), scaled to log2
+  // units; B operand: lane (l32 = key, hi) holds the same channels of its key.
+  // D[query][key]: lane holds key l32, query rows 4 hi + r in acc[r], r < 4.
   const float scale = 1.44269504088896340736f / sqrtf((float)D);
   bf16x8 qf[8];
   {
@@ -85,106 +109,107 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
       for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)((float)v[e] * scale);
     }
   }
-  // One ring of eight 16-byte fragments per lane streams the wave's whole
-  // share of the chunk: K fragment ks of the next key block is requested as
-  // soon as the MFMA that reads fragment ks of this block has been issued, and
-  // after the last block the same slots request the first eight V rows of
-  // P V, which stay in flight through the softmax.
-  constexpr int NB = CK / 32 / NW;                 // key blocks per wave
+  // P V on the vector ALU: lane = (key slot L / 16, channels 8 (L % 16) .. + 7)
+  // takes keys slot + 4 i (i < 8) of a block, so one wave load covers four
+  // whole 256-byte V rows.
   const int slot = lane >> 4, cc = (lane & 15) * 8;
-  const int i0 = wave * (CK / NW) + slot;          // P V: this lane's first key
-  auto kload = [&](int bi, int ks) {
-    const int key = k0 + (wave + bi * NW) * 32 + l32;
-    return __builtin_bit_cast(
-        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, (key * D + ks * 16 + hi * 8) * 2, 0, 0));
+  auto kload = [&](int blk, int ks) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                          krs, ((blk * 32 + l32) * D + ks * 16 + hi * 8) * 2, 0, 0));
   };
-  auto vload = [&](int it) {
-    return __builtin_bit_cast(
-        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, ((k0 + i0 + 4 * it) * D + cc) * 2, 0, 0));
+  auto vload = [&](int blk, int i) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                          vrs, ((blk * 32 + slot + 4 * i) * D + cc) * 2, 0, 0));
   };
-  bf16x8 ring[8];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) ring[ks] = kload(0, ks);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int bi = 0; bi < NB; ++bi) {
-    const int blk = wave + bi * NW;
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], ring[ks], acc, 0, 0, 0);
-      ring[ks] = bi + 1 < NB ? kload(bi + 1, ks) : vload(ks);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {     // masks: 0x008 MFMA, 0x020 vector memory read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    const bool valid = k0 + blk * 32 + l32 < kend;
-    // D[query][key]: lane holds key column l32, query rows 8*(r/4) + 4*hi + r%4.
-    // Rows G .. GQ-1 come from zero query rows and are never read.
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int q = 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (q < GQ) ps[(blk * 32 + l32) * PW + q] = valid ? acc[r] : -INFINITY;
-    }
-  }
-  __syncthreads();
 
-  // ---- 2. max and sum over the chunk, one wave per query (G <= 8 queries)
-  for (int q = wave; q < G; q += NW) {
-    float m = -INFINITY;
-    for (int i = lane; i < CK; i += 64) m = fmaxf(m, ps[i * PW + q]);
+  float m[NR], lsum[NR];                 // running max and this lane's share of the sum
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    float l = 0.0f;
-    for (int i = lane; i < CK; i += 64) {
-      const float p = __builtin_amdgcn_exp2f(ps[i * PW + q] - m);   // masked keys: 0
-      ps[i * PW + q] = p;
-      l += p;
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-    if (lane == 0) {
-      stat[q][0] = m;
-      stat[q][1] = l;
-    }
+  for (int r = 0; r < NR; ++r) {
+    m[r] = -INFINITY;
+    lsum[r] = 0.0f;
   }
-  __syncthreads();
-
-  // ---- 3. O_chunk = P V: wave w takes keys w*128 .. w*128+127 of the chunk;
-  // lane = (key slot L / 16, channels 8 (L % 16) .. + 7), so one wave load
-  // covers 4 whole 256-byte V rows.  The 4 key slots are summed with two
-  // shuffles, the 4 waves through LDS.
   float o[GQ][8];
 #pragma unroll
   for (int q = 0; q < GQ; ++q)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[q][e] = 0.0f;
-  // keys past the sequence have p = 0 and read V as zero; rows q >= G use
-  // unwritten scores and are never stored, so the loop has no branch
-  // P V continues the ring: slot it % 8 holds V rows of iteration it and is
-  // refilled with iteration it + 8 once read
-  constexpr int NIT = CK / NW / 4;
+
+  bf16x8 kr[8], vr[8];
+  int blk = first;
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const bf16x8 v8 = ring[it & 7];
-    if (it + 8 < NIT) ring[it & 7] = vload(it + 8);
-    const int i = i0 + 4 * it;
-    const f32x4 pa = *reinterpret_cast<const f32x4*>(&ps[i * PW]);
-    f32x4 pb = pa;
-    if (GQ > 4) pb = *reinterpret_cast<const f32x4*>(&ps[i * PW + 4]);
+  for (int j = 0; j < 8; ++j) kr[j] = kload(blk, j);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) vr[j] = vload(blk, j);
+  float* pw = pbuf[wave];
+  for (int it = 0; it < nit; ++it) {
+    const int nxt = blk + stride;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kr[ks], acc, 0, 0, 0);
+      kr[ks] = kload(nxt, ks);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // V work stays below: its waits come later
+    // online softmax over this block (block max over the 32 keys of each half)
+    const bool valid = blk * 32 + l32 < nkeys;
+    float p[4], al[4];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float s = valid ? acc[r] : -INFINITY;
+      float mb = s;
+      mb = half_max(mb);
+      const float mn = fmaxf(m[r], mb);            // finite: key 32 blk is valid
+      al[r] = __builtin_amdgcn_exp2f(m[r] - mn);
+      m[r] = mn;
+      p[r] = __builtin_amdgcn_exp2f(s - mn);
+      lsum[r] = fmaf(lsum[r], al[r], p[r]);
+    }
+#pragma unroll
+    for (int r = NR; r < 4; ++r) p[r] = 0.0f;
+    // p to this wave's LDS row block: [key l32][query 4 hi + r].  LDS accesses
+    // of one wave complete in order, so the reads below see these writes and
+    // the next block's writes follow these reads.
+    *reinterpret_cast<f32x4*>(&pw[l32 * PW + 4 * hi]) = f32x4{p[0], p[1], p[2], p[3]};
+    // rescale O by each query's factor (uniform over its lane half)
 #pragma unroll
     for (int q = 0; q < GQ; ++q) {
-      const float p = q < 4 ? pa[q] : pb[q - 4];
+      const float aq = __int_as_float(
+          __builtin_amdgcn_readlane(__float_as_int(al[q & 3]), (q >> 2) * 32));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[q][e] = fmaf(p, (float)v8[e], o[q][e]);
+      for (int e = 0; e < 8; ++e) o[q][e] *= aq;
     }
+    // the p rows of this lane's 8 keys, read together (one wait)
+    f32x4 pa[8], pb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pa[i] = *reinterpret_cast<const f32x4*>(&pw[(slot + 4 * i) * PW]);
+      if (GQ > 4) pb[i] = *reinterpret_cast<const f32x4*>(&pw[(slot + 4 * i) * PW + 4]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // the slot is refilled only once its rows are converted, so the new
+      // load lands in the same registers (no copy that would wait for it)
+      float vf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vf[e] = (float)vr[i][e];
+      __builtin_amdgcn_sched_barrier(0);
+      vr[i] = vload(nxt, i);
+#pragma unroll
+      for (int q = 0; q < GQ; ++q) {
+        const float pq = q < 4 ? pa[i][q] : pb[i][q - 4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[q][e] = fmaf(pq, vf[e], o[q][e]);
+      }
+    }
+    blk = nxt;
   }
-  // the four key slots of a wave are summed with two shuffles, the waves
-  // through LDS (over the scores, once every wave is done with them)
+  // this wave's l (over the 32 lanes of each half) and O (over the 4 key slots)
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) lsum[r] += __shfl_xor(lsum[r], off);
 #pragma unroll
   for (int q = 0; q < GQ; ++q)
 #pragma unroll
@@ -192,30 +217,50 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a) {
       o[q][e] += __shfl_xor(o[q][e], 16);
       o[q][e] += __shfl_xor(o[q][e], 32);
     }
-  __syncthreads();
-  float* opart = ps;                          // [NW][GQ][D]
+  if (slot == 0)
 #pragma unroll
-  for (int q = 0; q < GQ; ++q)
-    if (q < G && slot == 0)
+    for (int q = 0; q < GQ; ++q)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) opart[(wave * GQ + q) * D + cc + e] = o[q][e];
+      for (int e = 0; e < 8; ++e) ow[wave][q][cc + e] = o[q][e];
+  if (l32 == 0)
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      if (4 * hi + r < GQ) {
+        mlw[wave][4 * hi + r][0] = m[r];
+        mlw[wave][4 * hi + r][1] = lsum[r];
+      }
   __syncthreads();
+  // merge the four waves (a wave with no block has m = -inf, l = 0, O = 0)
+  // partial of (b, query head g*G + q, split): part[((b*Hq + g*G + q)*nsplit + split)*PSTRIDE]
+  float* part = a.part + ((long)(b * dm.Hq + g * G) * nsplit + split) * PSTRIDE;
   for (int e = threadIdx.x; e < G * D; e += 256) {
     const int q = e / D, c = e % D;
-    float sum = 0.0f;
+    float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) sum += opart[(w * GQ + q) * D + c];
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, mlw[w][q][0]);
+    float sum = 0.0f;
+    if (mx != -INFINITY)
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum = fmaf(ow[w][q][c], __builtin_amdgcn_exp2f(mlw[w][q][0] - mx), sum);
     part[(long)q * nsplit * PSTRIDE + c] = sum;
   }
   if (threadIdx.x < G) {
-    part[(long)threadIdx.x * nsplit * PSTRIDE + D] = stat[threadIdx.x][0];
-    part[(long)threadIdx.x * nsplit * PSTRIDE + D + 1] = stat[threadIdx.x][1];
+    const int q = threadIdx.x;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, mlw[w][q][0]);
+    float l = 0.0f;
+    if (mx != -INFINITY)
+#pragma unroll
+      for (int w = 0; w < NW; ++w) l = fmaf(mlw[w][q][1], __builtin_amdgcn_exp2f(mlw[w][q][0] - mx), l);
+    part[(long)q * nsplit * PSTRIDE + D] = mx;
+    part[(long)q * nsplit * PSTRIDE + D + 1] = l;
   }
 }
 
-// Merge of the chunk partials of (sequence b, query head h): the chunk maxima
-// and weights in parallel (one thread per chunk, through LDS), then one thread
-// per channel sums its weighted partial O over the chunks.  Chunk 0 always
+// Merge of the nsplit partials of (sequence b, query head h): their maxima
+// and weights in parallel (one thread per partial, through LDS), then one
+// thread per channel sums its weighted partial O over them.  Partial 0 always
 // holds key 0, so the merged max is finite and the weight sum is >= 1.
 __global__ __launch_bounds__(D) void attn_decode_merge_kernel(AttnArgs a) {
   __shared__ float wgt[MAX_SPLIT];
@@ -257,8 +302,13 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(AttnArgs a) {
 
 }  // namespace
 
-int decode_nsplit(const Dims& dm, int) {
-  return fast_decode(dm) ? (dm.max_seq_len + CK - 1) / CK : 1;
+// Work-groups per (sequence, KV head): about TARGET_WGS in all, at most one
+// wave per 32-key block of the cache.
+int decode_nsplit(const Dims& dm, int B) {
+  if (!fast_decode(dm)) return 1;
+  const int nblk = (dm.max_seq_len + 31) / 32;
+  const int ns = TARGET_WGS / std::max(1, B * dm.Hkv);
+  return std::max(1, std::min({ns, nblk / NW, MAX_SPLIT}));
 }
 
 size_t decode_part_floats(const Dims& dm, int B) {

@@ -28,6 +28,12 @@ CASES = [
     Workload("bf16_decode", B=3, S=150, E=512, C=1, Hq=4, Hkv=2, seed=53),
     Workload("bf16_decode_g4", B=2, S=64, E=512, C=1, Hq=4, Hkv=1, kq=3, kk=2, seed=54),
     Workload("bf16_decode_first", B=2, S=1, E=512, C=1, Hq=4, Hkv=2, seed=55),
+    # one query head per KV head, and eight: the other group-size instances
+    Workload("bf16_decode_mha", B=2, S=90, E=512, C=1, Hq=4, Hkv=4, seed=57),
+    Workload("bf16_decode_g8", B=2, S=70, E=1024, C=1, Hq=8, Hkv=1, seed=58),
+    # one sequence over a longer cache: several work-groups per head, waves
+    # with no block, a partly valid last block
+    Workload("bf16_decode_long", B=1, S=1000, E=512, C=1, Hq=4, Hkv=2, seed=59),
 ]
 
 
