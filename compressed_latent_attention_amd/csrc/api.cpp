@@ -452,10 +452,18 @@ cca_status cca_decode_step(cca_handle* h, const cca_weights* w, const void* x_ne
       if (dm.bf16 && launch_gemm_skinny(ga, out_f32, gpart, s, &e)) return e;
       return launch_gemm(ga, GemmLayout::NT, dm.bf16, out_f32, s);
     };
-    CCA_TRY_HIP(timed(h, "decode_proj_down", s, [&] { return gemm_decode(gd, true); }));
+    // the fused mix sums the skinny GEMM's K-slice partials itself (no reduce launch)
+    SkinnyPartials sp{qkv, 1, 0, dm.nqkv};
+    CCA_TRY_HIP(timed(h, "decode_proj_down", s, [&] {
+      hipError_t e = hipSuccess;
+      if (mix_decode_fused_ok(dm) && launch_gemm_skinny(gd, true, gpart, s, &e, &sp)) return e;
+      sp = SkinnyPartials{qkv, 1, 0, dm.nqkv};
+      return gemm_decode(gd, true);
+    }));
 
     MixDecodeArgs md{};
-    md.dm = dm; md.B = B; md.pos = pos; md.qkv = qkv;
+    md.dm = dm; md.B = B; md.pos = pos;
+    md.qkv = sp.part; md.qkv_ks = sp.KS; md.qkv_kstride = sp.kstride; md.qkv_ld = sp.ld;
     md.conv_q = w->conv_q; md.conv_k = w->conv_k; md.rope = h->rope;
     md.state = state; md.k_cache = k_cache; md.v_cache = v_cache; md.q_out = qn;
     md.cv = (float*)(base + L.cv);

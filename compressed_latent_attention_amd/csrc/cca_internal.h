@@ -71,8 +71,16 @@ bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError
 // Split-K NT GEMM for few rows of A (the decode step): partial tiles in an fp32
 // buffer of gemm_skinny_part_floats() floats, then a fixed-order sum; false when
 // the shape does not suit it (nothing launched).
+// With keep set, the sum is left to the consumer: only the partials are
+// written, C(m, n) = sum over z < keep->KS of part[z * keep->kstride + m * keep->ld + n].
+struct SkinnyPartials {
+  const float* part;
+  int KS;
+  long kstride;
+  int ld;
+};
 bool launch_gemm_skinny(const GemmArgs& g, bool out_f32, float* part, hipStream_t s,
-                        hipError_t* err);
+                        hipError_t* err, SkinnyPartials* keep = nullptr);
 size_t gemm_skinny_part_floats();
 // out[c][r] = in[r][c] for r < R, c < C (bf16), zero for R <= r < Rp;
 // C and Rp multiples of 8, 16-byte aligned rows.
@@ -120,7 +128,10 @@ struct MixDecodeArgs {
   Dims dm;
   int B;
   DecodePos pos;
-  const float* qkv;         // [B, nqkv] fp32
+  const float* qkv;         // [B, nqkv] fp32, or the first of qkv_ks K-slice partials:
+  int qkv_ks;               // qkv~(b, col) = sum_z qkv[z * qkv_kstride + b * qkv_ld + col]
+  long qkv_kstride;
+  int qkv_ld;
   const void* conv_q;
   const void* conv_k;
   const float2* rope;
@@ -131,6 +142,9 @@ struct MixDecodeArgs {
   float* cv;                // [B, Hq + Hkv, d] fp32 workspace: convolution outputs
 };
 hipError_t launch_mix_decode(const MixDecodeArgs& a, hipStream_t s);
+// The single-kernel decode mix (bf16, d = 128, up to 4 taps) takes qkv~ as
+// K-slice partials; the two-kernel path needs qkv_ks == 1.
+bool mix_decode_fused_ok(const Dims& dm);
 size_t mix_decode_cv_floats(const Dims& dm, int B);
 
 // ------------------------------------------------------------------ attention

@@ -385,9 +385,10 @@ size_t gemm_skinny_part_floats() { return SK_MAX_PART; }
 // output tiles of 32 x 32, K a multiple of 256 so that four waves get whole
 // 16-wide steps in every slice, N and ldc multiples of 4 for the 4-wide output
 // stores, and at least two slices to go around); false (nothing launched)
-// otherwise.
+// otherwise.  With keep set only the partials are written, for a consumer
+// that sums them itself.
 bool launch_gemm_skinny(const GemmArgs& g, bool out_f32, float* part, hipStream_t s,
-                        hipError_t* err) {
+                        hipError_t* err, SkinnyPartials* keep) {
   if (part == nullptr || g.M <= 0 || g.M > 256 || g.K % 256 != 0 || g.lda % 8 != 0 ||
       g.ldb % 8 != 0 || g.N % 4 != 0 || g.ldc % 4 != 0)
     return false;
@@ -402,6 +403,11 @@ bool launch_gemm_skinny(const GemmArgs& g, bool out_f32, float* part, hipStream_
   if ((long)KS * Mp * Np > SK_MAX_PART) return false;
   hipLaunchKernelGGL(gemm_skinny_partial_kernel, dim3(nb, mb, KS), dim3(256), 0, s, g, g.K / KS,
                      Mp, Np, part);
+  if (keep != nullptr) {
+    *keep = SkinnyPartials{part, KS, (long)Mp * Np, Np};
+    *err = hipGetLastError();
+    return true;
+  }
   const long groups = (long)g.M * (g.N / 4);
   const dim3 rgrid((unsigned)((groups + 255) / 256));
   if (out_f32)

@@ -364,6 +364,197 @@ __global__ __launch_bounds__(256) void mix_decode_kernel(MixDecodeArgs a) {
            a.qkv[(long)b * dm.nqkv + dm.nq + dm.nk + g * d + c]);
 }
 
+// Sum over each row of 16 lanes, left in every lane of the row: DPP swap of
+// neighbours, of pairs, mirror within 8, mirror within 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141>(v);   // row_half_mirror
+  v += dpp_mov<0x140>(v);   // row_mirror
+  return v;
+}
+
+// Decode-step mix in one kernel (bf16 storage, d = 128, at most 4 taps):
+// one work-group of 1024 threads per (KV group g, sequence b) does what the
+// two kernels above do for that group, with the token's latents summed from
+// the projection's K-slice partials as they are read.  The step is a chain of
+// tiny dependent phases, so every global read is issued at the start, in one
+// round: the K-slice partials, the state's lags and previous v, the RoPE pairs
+// of position p, and the tap rows of each wave's first 12 convolution groups.
+//   1. lag 0 of the G query heads, the key head and the new v (sums of the
+//      partials), the lags >= 1 and the previous v to LDS;
+//   2. convolution: a group = 4 consecutive output channels of one (head, tap)
+//      pair, whose tap rows are 1 KB contiguous: one 16-byte load per lane
+//      (lane = row slot L / 16, input channels 8 (L % 16) .. + 7), partial dot
+//      products with the lag-j latent from LDS, summed over the 16 lanes of a
+//      row by DPP;
+//   3. the taps' terms summed per (head, channel), then QK-mean, RoPE, value
+//      shift, the q / cache stores and the advanced state as above.
+// The group's state is read in 1. and written in 3. by this work-group only.
+constexpr int FD = 128;                 // head dim of the fused path
+constexpr int FKMAX = 4;                // taps per convolution at most
+constexpr int FNH = kMaxGroup + 1;      // heads of a KV group: G query heads + 1 key head
+constexpr int FZ = 8;                   // K-slice partials read in the first round
+
+__global__ __launch_bounds__(1024) void mix_decode_fused_kernel(MixDecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) float u[FKMAX][FNH][FD];     // pre-conv latents by lag
+  __shared__ __attribute__((aligned(16))) float cvp[FKMAX][FNH][FD];   // convolution terms by tap
+  __shared__ __attribute__((aligned(16))) float cv[FNH][FD];           // convolution outputs
+  __shared__ __attribute__((aligned(16))) float vnew[FD];
+  __shared__ __attribute__((aligned(16))) float vprev[FD];
+  __shared__ float2 rope_cs[FD / 2];
+  const Dims& dm = a.dm;
+  const int G = dm.G, NH = G + 1, kq = dm.kq, kk = dm.kk, KM = max(kq, kk);
+  const int g = blockIdx.x, b = blockIdx.y, p = a.pos.p[b];
+  // the wave index in a scalar register: group indices, (head, tap) pairs and
+  // the choice of tap tensor are then uniform, with no per-lane pointer select
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int slot = lane >> 4, ci = (lane & 15) * 8;
+  const long srow = (long)b * dm.state_w;
+  const int nqpart = (kq - 1) * dm.nq, nkpart = (kk - 1) * dm.nk;
+  const bf16* st = reinterpret_cast<const bf16*>(a.state);
+  const int half = FD / 2;
+  const int nr = G * kq + kk, ngroups = nr * (FD / 4);
+  // integer division by run-time values expands to long scalar sequences that
+  // every wave would issue; the divisors here are small: k <= 4 as
+  // r * ceil(65536 / k) >> 16 (exact for r < 4096), NH <= 9 through a float
+  // reciprocal ((r + 0.5) / NH stays >= 0.5 / NH away from an integer)
+  const int mkq = (65536 + kq - 1) / kq;
+  auto div_kq = [&](int r) { return (r * mkq) >> 16; };
+  const float inv_nh = 1.0f / (float)NH;
+  auto div_nh = [&](int r) { return (int)(((float)r + 0.5f) * inv_nh); };
+  auto pair_of = [&](int r, int& hh, int& j) {      // (head, tap) pair r (r < 36)
+    const int qh = div_kq(r);
+    hh = r < G * kq ? qh : G;
+    j = r < G * kq ? r - qh * kq : r - G * kq;
+  };
+  // tap matrix of pair r: conv_q matrix g G kq + r for r < G kq (pairs run
+  // head-major, tap-minor), else conv_k matrix g kk + r - G kq; the tensor is
+  // chosen by a byte offset, not a pointer select
+  const char* tq = reinterpret_cast<const char*>(a.conv_q);
+  const long dqk = reinterpret_cast<const char*>(a.conv_k) - tq;
+  const int GK = G * kq;
+  auto tap_load = [&](int q) {                      // this lane's 16 bytes of group q
+    const int r = q >> 5, c = (q & 31) * 4 + slot;  // FD / 4 = 32 groups per pair
+    const long mat = r < GK ? (long)g * GK + r : (long)g * kk + (r - GK);
+    const char* row = tq + (r < GK ? 0 : dqk) + ((mat * FD + c) * FD + ci) * 2;
+    return *reinterpret_cast<const bf16x8*>(row);
+  };
+
+  // ---- every global read, one round (clamped indices: a duplicate read is stored nowhere)
+  constexpr int NB = 12;                            // groups per wave per round (192 = 16 x 12)
+  bf16x8 w[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) w[i] = tap_load(min(wave + 16 * i, ngroups - 1));
+  // lag 0: row hh (query heads, key head, then v) x 4 channels per thread
+  const int n0 = (NH + 1) * (FD / 4);
+  const int t0 = min(t, n0 - 1), hh0 = t0 / (FD / 4), c0 = (t0 % (FD / 4)) * 4;
+  const int col0 = hh0 < G ? (g * G + hh0) * FD : hh0 == G ? dm.nq + g * FD : dm.nq + dm.nk + g * FD;
+  const float* src0 = a.qkv + (long)b * a.qkv_ld + col0 + c0;
+  f32x4 part0[FZ];
+#pragma unroll
+  for (int z = 0; z < FZ; ++z)
+    part0[z] = *reinterpret_cast<const f32x4*>(src0 + (long)min(z, a.qkv_ks - 1) * a.qkv_kstride);
+  // lags 1 .. k - 1 (item = lag, head, 8 channels), then the previous v
+  const int nl = (KM - 1) * NH * (FD / 8);
+  const int e1 = min(t, nl + FD / 8 - 1), cl = (e1 % (FD / 8)) * 8, rl = e1 / (FD / 8);
+  const int rq = div_nh(rl), hl = rl - rq * NH, jl = 1 + rq;
+  const bool lag_ok = t < nl && jl < (hl < G ? kq : kk);
+  const long offl = !lag_ok ? srow + nqpart + nkpart + g * FD + cl
+                  : hl < G ? srow + (long)(jl - 1) * dm.nq + (g * G + hl) * FD + cl
+                           : srow + nqpart + (long)(jl - 1) * dm.nk + g * FD + cl;
+  const bf16x8 lagv = *reinterpret_cast<const bf16x8*>(st + offl);
+  // RoPE pairs of position p
+  const float2 csv = (dm.flags & kRope) ? a.rope[(long)p * half + min(t, half - 1)] : make_float2(1.f, 0.f);
+
+  // ---- 1. to LDS
+  if (t < n0) {
+    f32x4 sum = part0[0];
+#pragma unroll
+    for (int z = 1; z < FZ; ++z)
+      if (z < a.qkv_ks) sum += part0[z];
+    for (int z = FZ; z < a.qkv_ks; ++z)               // more slices than the first round took
+      sum += *reinterpret_cast<const f32x4*>(src0 + (long)z * a.qkv_kstride);
+    *reinterpret_cast<f32x4*>(hh0 <= G ? &u[0][hh0][c0] : &vnew[c0]) = sum;
+  }
+  if (lag_ok || (t >= nl && t < nl + FD / 8)) {
+    float* dst = lag_ok ? &u[jl][hl][cl] : &vprev[cl];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dst[q] = (float)lagv[q];
+  }
+  if (t < half) rope_cs[t] = csv;
+  __syncthreads();
+
+  // ---- 2. convolution terms: wave takes groups wave + 16 i
+  for (int q0 = wave; q0 < ngroups; q0 += 16 * NB) {
+    if (q0 != wave) {                                  // groups past the first round's
+#pragma unroll
+      for (int i = 0; i < NB; ++i) w[i] = tap_load(min(q0 + 16 * i, ngroups - 1));
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int q = q0 + 16 * i;
+      if (q >= ngroups) break;                         // uniform over the wave
+      int hh, j;
+      pair_of(q / (FD / 4), hh, j);
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(&u[j][hh][ci]);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(&u[j][hh][ci + 4]);
+      float sum = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sum = fmaf((float)w[i][e], x0[e], sum);
+        sum = fmaf((float)w[i][4 + e], x1[e], sum);
+      }
+      // every lane of the row holds the sum: all 16 store it (same address, same value)
+      cvp[j][hh][(q % (FD / 4)) * 4 + slot] = row16_sum(sum);
+    }
+  }
+  __syncthreads();
+  for (int e = t; e < NH * FD; e += 1024) {
+    const int hh = e / FD, c = e % FD, k = hh < G ? kq : kk;
+    float sum = cvp[0][hh][c];
+    for (int j = 1; j < k; ++j) sum += cvp[j][hh][c];
+    cv[hh][c] = sum;
+  }
+  __syncthreads();
+
+  // ---- 3. QK-mean and RoPE: item = (head, channel), up to 9 x 128 of them
+  for (int e = t; e < NH * FD; e += 1024) {
+    const int hh = e / FD, c = e % FD, cp = c < half ? c + half : c - half;
+    const float x = qk_mixed(&u[0][0][0], &cv[0][0], G, FD, hh, c, dm.flags);
+    const float xp = qk_mixed(&u[0][0][0], &cv[0][0], G, FD, hh, cp, dm.flags);
+    const float r = rope_rot(x, xp, c, half, rope_cs[c % half]);
+    if (hh < G)
+      stf<bf16>(a.q_out, (long)(b * dm.Hq + g * G + hh) * FD + c, r);
+    else
+      stf<bf16>(a.k_cache, ((long)(b * dm.Hkv + g) * dm.max_seq_len + p) * FD + c, r);
+  }
+  // value shift, the v cache row and the v of the state
+  if (t < FD) {
+    const bool shifted = (dm.flags & kVShift) && t >= FD - dm.sv;
+    stf<bf16>(a.v_cache, ((long)(b * dm.Hkv + g) * dm.max_seq_len + p) * FD + t,
+              shifted ? vprev[t] : vnew[t]);
+    stf<bf16>(a.state, srow + nqpart + nkpart + g * FD + t, vnew[t]);
+  }
+  // the rolling state advances: lag j takes lag j - 1 (item = head x 8 channels of one lag)
+  for (int j = 1; j < KM; ++j)
+    for (int e = t; e < NH * (FD / 8); e += 1024) {
+      const int hh = e / (FD / 8), c = (e % (FD / 8)) * 8;
+      const bool isq = hh < G;
+      if (j >= (isq ? kq : kk)) continue;
+      const long off = isq ? srow + (long)(j - 1) * dm.nq + (g * G + hh) * FD + c
+                           : srow + nqpart + (long)(j - 1) * dm.nk + g * FD + c;
+      bf16x8 v;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = (bf16)u[j - 1][hh][c + q];
+      *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.state) + off) = v;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_mix_fwd_mfma(const MixArgs& a, hipStream_t s);   // mix_mfma.hip
@@ -395,9 +586,19 @@ hipError_t launch_write_state(const Dims& dm, int B, int S, const float* qkv, vo
 
 size_t mix_decode_cv_floats(const Dims& dm, int B) { return (size_t)B * (dm.Hq + dm.Hkv) * dm.d; }
 
+bool mix_decode_fused_ok(const Dims& dm) {
+  return dm.bf16 && dm.d == FD && dm.G <= kMaxGroup && dm.kq >= 1 && dm.kq <= FKMAX &&
+         dm.kk >= 1 && dm.kk <= FKMAX;
+}
+
 hipError_t launch_mix_decode(const MixDecodeArgs& a, hipStream_t s) {
   const Dims& dm = a.dm;
-  if (a.cv == nullptr) return hipErrorInvalidValue;
+  if (a.qkv_ks < 1 || a.qkv_ld < dm.nqkv) return hipErrorInvalidValue;
+  if (mix_decode_fused_ok(dm)) {
+    hipLaunchKernelGGL(mix_decode_fused_kernel, dim3(dm.Hkv, a.B), dim3(1024), 0, s, a);
+    return hipGetLastError();
+  }
+  if (a.cv == nullptr || a.qkv_ks != 1 || a.qkv_ld != dm.nqkv) return hipErrorInvalidValue;
   // part 1: LDS = k CB (d + 4) tap floats + BCMAX k d lag floats
   const int k = max(dm.kq, dm.kk);
   const size_t lds1 = ((size_t)k * CB * (dm.d + 4) + (size_t)BCMAX * k * dm.d) * sizeof(float);
