@@ -9,11 +9,12 @@
 // registers) and issues 16 MFMAs per 16-wide k step from two double-buffered
 // sets of operand fragments.  Tiles of A and B move from global memory to LDS
 // with buffer loads that write LDS directly (16 bytes per lane), two stages
-// deep; the next stage's sixteen 1 KB copies per wave are issued one after
-// every four MFMAs rather than in a burst: a copy's issue waits until the
-// address unit takes it, and with one wave per SIMD a burst would leave the
-// MFMA unit idle for that long (spread out, the copies stay below the unit's
-// rate and issue at once).  LDS rows (64 k = 128 B) are unpadded with their
+// deep; the next stage's sixteen 1 KB copies per wave are issued two after
+// every four MFMAs over the first half of the k step rather than in a burst:
+// a copy's issue waits until the address unit takes it, and with one wave per
+// SIMD a burst would leave the MFMA unit idle for that long, while copies
+// spread over the whole step leave the last ones' memory latency exposed at
+// the end-of-step wait.  LDS rows (64 k = 128 B) are unpadded with their
 // 16-byte chunks XOR-swizzled by row, so that the fragment reads are free of
 // bank conflicts.
 // Rows past M or past the end of B's segment read as zero (buffer range
@@ -154,10 +155,16 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j],
                                                               0, 0, 0);
-        const int blk = ks * 4 + i;          // 16 blocks: A 0..7, B 8..15
+        const int pt = ks * 4 + i;           // issue point 0..15
         __builtin_amdgcn_sched_barrier(0);
-        if (blk < 8) dma_part(nx, abase, g.lda, arows, g.K, knx, wave, lane, blk);
-        else dma_part(nx + A_BYTES, bbase, g.ldb, brows, g.K, knx, wave, lane, blk - 8);
+        if (pt < 16 / 2) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int blk = pt * 2 + u;    // 16 blocks: A 0..7, B 8..15
+            if (blk < 8) dma_part(nx, abase, g.lda, arows, g.K, knx, wave, lane, blk);
+            else dma_part(nx + A_BYTES, bbase, g.ldb, brows, g.K, knx, wave, lane, blk - 8);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
