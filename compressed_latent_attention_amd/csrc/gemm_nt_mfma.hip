@@ -4,13 +4,15 @@
 // q~ | k~ | v~ (CCA-es §2.A "Principio Fundamental"; CCA-fr §2 "Projection
 // vers l'Espace Latent") and the output projection O W_o^T.
 //
-// Work-group tile 256 x 256 x 64, four waves of 128 x 128, one wave per SIMD:
-// each wave holds 16 accumulator blocks of v_mfma_f32_32x32x16_bf16 (256
-// registers) and issues 16 MFMAs per 16-wide k step from two double-buffered
-// sets of operand fragments.  Tiles of A and B move from global memory to LDS
+// Work-group tile 256 x 256 x 64, either four waves of 128 x 128, one wave per
+// SIMD (each wave holds 16 accumulator blocks of v_mfma_f32_32x32x16_bf16, 256
+// registers, and issues 16 MFMAs per 16-wide k step), or eight waves of
+// 128 x 64, two per SIMD, when the grid holds two or more work-groups per CU;
+// operand fragments are double-buffered.  Tiles of A and B move from global memory to LDS
 // with buffer loads that write LDS directly (16 bytes per lane), two stages
-// deep; the next stage's sixteen 1 KB copies per wave are issued two after
-// every four MFMAs over the first half of the k step rather than in a burst:
+// deep; the next stage's 1 KB copies (16 per wave with four waves, 8 with
+// eight) are issued after every four MFMAs over the first half of the k step
+// rather than in a burst:
 // a copy's issue waits until the address unit takes it, and with one wave per
 // SIMD a burst would leave the MFMA unit idle for that long, while copies
 // spread over the whole step leave the last ones' memory latency exposed at
@@ -43,38 +45,46 @@ __device__ __forceinline__ void store_out(bf16* p, float v) { *p = (bf16)v; }
 
 // One 256-row x 64-k operand tile into LDS: rows row0 .. of a K-contiguous
 // matrix at base (row stride ld elements), `rows` of them valid; k from k0.
-// Wave w writes 1 KB blocks 8w .. 8w + 7 (8 rows each); lane L lands at row
-// 8 blk + L / 8, chunk position L % 8 and fetches the chunk the swizzle puts
-// there.
+// With NW waves, wave w writes 1 KB blocks CB w .. CB w + CB - 1 (CB = 32 / NW,
+// 8 rows each); lane L lands at row 8 blk + L / 8, chunk position L % 8 and
+// fetches the chunk the swizzle puts there.
+template <int CB>
 __device__ __forceinline__ void dma_tile(char* dst, const bf16* base, long ld, int rows, int K,
                                          int k0, int wave, int lane) {
   const int nrec = ((rows - 1) * (int)ld + K - k0) * 2;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(base + k0), 0, nrec, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int blk = wave * 8 + i;
+  for (int i = 0; i < CB; ++i) {
+    const int blk = wave * CB + i;
     const int r = blk * 8 + (lane >> 3), pos = lane & 7;
     const int src = r * (int)ld * 2 + ((pos ^ ((r >> 1) & 7)) << 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16, src, 0, 0, 0);
   }
 }
 
-// Block i (0..7) of this wave's share of dma_tile, alone.
+// Block i (0 .. CB - 1) of this wave's share of dma_tile, alone.
+template <int CB>
 __device__ __forceinline__ void dma_part(char* dst, const bf16* base, long ld, int rows, int K,
                                          int k0, int wave, int lane, int i) {
   const int nrec = ((rows - 1) * (int)ld + K - k0) * 2;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(base + k0), 0, nrec, 0x00020000);
-  const int blk = wave * 8 + i;
+  const int blk = wave * CB + i;
   const int r = blk * 8 + (lane >> 3), pos = lane & 7;
   const int src = r * (int)ld * 2 + ((pos ^ ((r >> 1) & 7)) << 4);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16, src, 0, 0, 0);
 }
 
-template <typename OutT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// NW = 4: waves of 128 x 128 (256 accumulator registers), one per SIMD;
+// NW = 8: waves of 128 x 64, two per SIMD, so one wave's MFMAs cover the
+// other's copy issue, fragment waits and barrier.
+template <typename OutT, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  constexpr int WN = NW / 2;                 // waves along N
+  constexpr int NJ = TN / WN / 32;           // 32-column blocks per wave: 4 or 2
+  constexpr int CB = 32 / NW;                // 1 KB copy blocks per wave per operand tile
   // split-K: this work-group sums k in [kbeg, kbeg + klen)
   const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
   const int klen = g.K / nsplit, kbeg = blockIdx.y * klen;
@@ -89,7 +99,7 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, hi = lane >> 5;
 
   // A rows m0 .., B rows n0 .. (inside one segment of B, checked by the host)
@@ -103,14 +113,14 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   const int brows = min(seg_end - n0, TN);
 
   const int nk = klen / TK;
-  dma_tile(lds, abase, g.lda, arows, g.K, kbeg, wave, lane);
-  dma_tile(lds + A_BYTES, bbase, g.ldb, brows, g.K, kbeg, wave, lane);
+  dma_tile<CB>(lds, abase, g.lda, arows, g.K, kbeg, wave, lane);
+  dma_tile<CB>(lds + A_BYTES, bbase, g.ldb, brows, g.K, kbeg, wave, lane);
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -121,7 +131,7 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     aoff[ks] = sw(wm * 128 + l32, 2 * ks + hi);
-    boff[ks] = A_BYTES + sw(wn * 128 + l32, 2 * ks + hi);
+    boff[ks] = A_BYTES + sw(wn * (NJ * 32) + l32, 2 * ks + hi);
   }
   wait_dma();
   __syncthreads();
@@ -133,36 +143,37 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     // no branch)
     char* nx = lds + ((kt + 1) & 1) * STAGE;
     const int knx = kbeg + min(kt + 1, nk - 1) * TK;
-    bf16x8 fa[2][4], fb[2][4];
+    bf16x8 fa[2][4], fb[2][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[0][i] = *reinterpret_cast<const bf16x8*>(st + aoff[0] + i * 32 * 128);
-      fb[0][i] = *reinterpret_cast<const bf16x8*>(st + boff[0] + i * 32 * 128);
-    }
+    for (int i = 0; i < 4; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(st + aoff[0] + i * 32 * 128);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) fb[0][j] = *reinterpret_cast<const bf16x8*>(st + boff[0] + j * 32 * 128);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int cur = ks & 1;
       if (ks + 1 < 4) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
           fa[cur ^ 1][i] = *reinterpret_cast<const bf16x8*>(st + aoff[ks + 1] + i * 32 * 128);
-          fb[cur ^ 1][i] = *reinterpret_cast<const bf16x8*>(st + boff[ks + 1] + i * 32 * 128);
-        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          fb[cur ^ 1][j] = *reinterpret_cast<const bf16x8*>(st + boff[ks + 1] + j * 32 * 128);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j],
                                                               0, 0, 0);
-        const int pt = ks * 4 + i;           // issue point 0..15
+        // issue points 0..15; the 2 CB copies go out over the first 8 (CB / 4 each)
+        const int pt = ks * 4 + i;
         __builtin_amdgcn_sched_barrier(0);
-        if (pt < 16 / 2) {
+        if (pt < 8) {
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int blk = pt * 2 + u;    // 16 blocks: A 0..7, B 8..15
-            if (blk < 8) dma_part(nx, abase, g.lda, arows, g.K, knx, wave, lane, blk);
-            else dma_part(nx + A_BYTES, bbase, g.ldb, brows, g.K, knx, wave, lane, blk - 8);
+          for (int u = 0; u < CB / 4; ++u) {
+            const int blk = pt * (CB / 4) + u;   // A blocks 0 .. CB-1, then B
+            if (blk < CB) dma_part<CB>(nx, abase, g.lda, arows, g.K, knx, wave, lane, blk);
+            else dma_part<CB>(nx + A_BYTES, bbase, g.ldb, brows, g.K, knx, wave, lane, blk - CB);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -182,8 +193,8 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int nl = wn * 128 + j * 32 + l32;
+    for (int j = 0; j < NJ; ++j) {
+      const int nl = wn * (NJ * 32) + j * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ml = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -212,10 +223,17 @@ bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError
   if (nsplit > 1 && (!out_f32 || (g.K / nsplit) % TK != 0 || g.K % nsplit != 0)) return false;
   if ((long)tiles_m * tiles_n * nsplit < 64) return false;
   dim3 grid(tiles_m * tiles_n, nsplit);
-  if (out_f32)
-    hipLaunchKernelGGL(gemm_nt_256_kernel<float>, grid, dim3(256), 0, s, g, tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL(gemm_nt_256_kernel<bf16>, grid, dim3(256), 0, s, g, tiles_m, tiles_n);
+  // two or more work-groups per CU: 8 waves (they run one after another, and
+  // the second wave per SIMD hides stalls); fewer: 4 waves of 128 x 128, whose
+  // larger wave tiles read less LDS per MFMA
+  const bool w8 = (long)tiles_m * tiles_n * nsplit >= 512;
+  if (out_f32) {
+    if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+    else hipLaunchKernelGGL((gemm_nt_256_kernel<float, 4>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
+  } else {
+    if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 8>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+    else hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 4>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
+  }
   *err = hipGetLastError();
   return true;
 }
