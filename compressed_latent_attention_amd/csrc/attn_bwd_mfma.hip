@@ -373,13 +373,17 @@ __device__ __forceinline__ void dq_load(const AttnBwdArgs& a, int b, int g, int 
   const bf16* kb = reinterpret_cast<const bf16*>(a.k) + ((long)(b * dm.Hkv + g) * S) * D;
   const bf16* vb = reinterpret_cast<const bf16*>(a.v) + ((long)(b * dm.Hkv + g) * S) * D;
   const f16* ktb = reinterpret_cast<const f16*>(a.kT) + ((long)(b * dm.Hkv + g) * D) * a.s_pad;
+  // K and V rows through resources that end at row S - 1: rows past it read as
+  // zero without a branch, so the six loads of a thread issue back to back
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, S * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, S * D * 2, 0x00020000);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int f = t + 256 * i;
     const int row = f >> 4, ch = (f & 15) * 8;
     const int j = j0 + row;
-    r.kn[i] = j < S ? *reinterpret_cast<const bf16x8*>(kb + (long)j * D + ch) : zero8();
-    r.vn[i] = j < S ? *reinterpret_cast<const bf16x8*>(vb + (long)j * D + ch) : zero8();
+    r.kn[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, (j * D + ch) * 2, 0, 0));
+    r.vn[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, (j * D + ch) * 2, 0, 0));
     const int c = f >> 2, col = (f & 3) * 8;
     r.kt[i] = *reinterpret_cast<const f16x8*>(ktb + (long)c * a.s_pad + j0 + col);
   }
@@ -420,12 +424,17 @@ void bwd_dq_kernel(AttnBwdArgs a) {
   {
     const bf16* qbp = reinterpret_cast<const bf16*>(a.q) + ((long)(b * dm.Hq + h) * S) * D;
     const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + (long)b * S * dm.nq + h * D;
+    // rows past S read as zero through the resources' range check
+    const __amdgpu_buffer_rsrc_t qrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)qbp, 0, S * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t drs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)dob, 0, ((S - 1) * dm.nq + D) * 2, 0x00020000);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      qf[ks] = my_q < S ? *reinterpret_cast<const bf16x8*>(qbp + (long)my_q * D + ks * 16 + hi * 8)
-                        : zero8();
-      df[ks] = my_q < S ? *reinterpret_cast<const bf16x8*>(dob + (long)my_q * dm.nq + ks * 16 + hi * 8)
-                        : zero8();
+      qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                              qrs, (my_q * D + ks * 16 + hi * 8) * 2, 0, 0));
+      df[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                              drs, (my_q * dm.nq + ks * 16 + hi * 8) * 2, 0, 0));
     }
   }
   const float lse2 = my_q < S ? a.lse[(long)(b * dm.Hq + h) * S + my_q] * kLog2e : INFINITY;
@@ -452,13 +461,30 @@ void bwd_dq_kernel(AttnBwdArgs a) {
       f32x16 sacc, pacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
+      // K and V fragments through a ring of 4: the reads run 4 k slices ahead
+      // of the MFMAs instead of one read-wait-MFMA per slice
+      bf16x8 ka[4], va[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        ka[ks] = *reinterpret_cast<const bf16x8*>(st.kn + prow * NLD + ks * 16 + hi * 8);
+        va[ks] = *reinterpret_cast<const bf16x8*>(st.vn + prow * NLD + ks * 16 + hi * 8);
+      }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(st.kn + prow * NLD + ks * 16 + hi * 8);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(st.vn + prow * NLD + ks * 16 + hi * 8);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], pacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 3], qf[ks], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks & 3], df[ks], pacc, 0, 0, 0);
+        if (ks + 4 < 8) {
+          ka[ks & 3] = *reinterpret_cast<const bf16x8*>(st.kn + prow * NLD + (ks + 4) * 16 + hi * 8);
+          va[ks & 3] = *reinterpret_cast<const bf16x8*>(st.vn + prow * NLD + (ks + 4) * 16 + hi * 8);
+        }
       }
+      // K^T fragments of dQ += dS K, read before the softmax arithmetic covers them
+      f16x8 kt[2][4];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          kt[ks][nb] = *reinterpret_cast<const f16x8*>(st.kt + (nb * 32 + l32) * TLD + ks * 16 + hi * 8);
       // lane (query l32, hi): register r is key j0 + 16 (r / 8) + 8 hi + r % 8
       f16x8 sf[2];
 #pragma unroll
@@ -475,10 +501,8 @@ void bwd_dq_kernel(AttnBwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const f16x8 kb = *reinterpret_cast<const f16x8*>(st.kt + (nb * 32 + l32) * TLD + ks * 16 + hi * 8);
-          dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sf[ks], kb, dq[nb], 0, 0, 0);
-        }
+        for (int nb = 0; nb < 4; ++nb)
+          dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sf[ks], kt[ks][nb], dq[nb], 0, 0, 0);
     }
     if (s + 1 < nsteps) {
       dq_store(stg[(s + 1) & 1], t, pre);
