@@ -115,7 +115,7 @@ DecodeLayout decode_layout(const Dims& dm, long B) {
 }
 
 struct BwdLayout {
-  size_t dO, Dsum, dq, dk, dv, dqkv, part, scratch, trans;
+  size_t dO, Dsum, dq, dk, dv, dqkv, part, scratch, trans, tapT;
   size_t wT, tA, tB, gpart;   // bf16 backward GEMMs: transposed operands, split-K partials
   size_t total;
 };
@@ -138,6 +138,7 @@ BwdLayout bwd_layout(const Dims& dm, long B, long S) {
   L.part = o;    o = align256(o + mix_bwd_part_floats(dm, (int)B, (int)S) * 4);
   L.scratch = o; o = align256(o + mix_bwd_scratch_floats(dm, (int)B, (int)S) * 4);
   L.trans = o;   o = align256(o + attn_bwd_transpose_bytes(dm, (int)B, (int)S));
+  L.tapT = o;    o = align256(o + mix_bwd_tapT_bytes(dm));
   L.wT = L.tA = L.tB = L.gpart = o;
   if (bwd_gemm_nt(dm)) {
     const size_t Mp = (size_t)pad64(B * S);
@@ -597,6 +598,7 @@ cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, cons
     mb.dconv_part = (float*)(wb + L.part);
     mb.dconv_q = (float*)g->dconv_q; mb.dconv_k = (float*)g->dconv_k;
     mb.scratch = (float*)(wb + L.scratch);
+    mb.tapT = mix_bwd_tapT_bytes(dm) ? (void*)(wb + L.tapT) : nullptr;
     CCA_TRY_HIP(timed(h, "bwd_mix", s, [&] { return launch_mix_bwd(mb, s); }));
 
     // dx = dq~ W_q + dk~ W_k + dv~ W_v ; dW_* = d*~^T x

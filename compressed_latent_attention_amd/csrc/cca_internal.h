@@ -220,8 +220,10 @@ struct MixBwdArgs {
   float* dconv_q;        // final fp32 [Hq,kq,d,d]
   float* dconv_k;        // final fp32 [Hkv,kk,d,d]
   float* scratch;        // fp32 workspace for dq^ / dk^ [B*S, nq + nk]
+  void* tapT;            // bf16, d = 128: workspace for the transposed taps (mix_bwd_tapT_bytes)
 };
 hipError_t launch_mix_bwd(const MixBwdArgs& a, hipStream_t s);
+size_t mix_bwd_tapT_bytes(const Dims& dm);
 size_t mix_bwd_part_floats(const Dims& dm, int B, int S);
 size_t mix_bwd_scratch_floats(const Dims& dm, int B, int S);
 

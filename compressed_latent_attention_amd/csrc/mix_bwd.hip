@@ -281,6 +281,129 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_128(MixBwdArgs a) {
   }
 }
 
+// ---- bf16 storage, d = 128: the convolution adjoint on MFMA.
+// The adjoint contracts the taps over their first index (dq~[c'] = sum_c
+// A_j[c][c'] dq^[c]), and an MFMA operand lane holds 8 consecutive elements of
+// the contracted index, so the tap matrices are transposed once per call:
+// tapT[m][c'][c] = A_m[c][c'], m running over (head, tap) pairs as the taps are
+// stored (query heads, then key heads).
+__global__ __launch_bounds__(256) void mix_bwd_tap_transpose(MixBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[TD][TD + 8];
+  const Dims& dm = a.dm;
+  const int m = blockIdx.x, nqm = dm.Hq * dm.kq;
+  const bf16* src = m < nqm ? reinterpret_cast<const bf16*>(a.conv_q) + (long)m * TD * TD
+                            : reinterpret_cast<const bf16*>(a.conv_k) + (long)(m - nqm) * TD * TD;
+  bf16* dst = reinterpret_cast<bf16*>(a.tapT) + (long)m * TD * TD;
+  for (int e = threadIdx.x; e < TD * TD / 8; e += 256) {
+    const int r = e / (TD / 8), c8 = (e % (TD / 8)) * 8;
+    *reinterpret_cast<bf16x8*>(&tile[r][c8]) = *reinterpret_cast<const bf16x8*>(src + r * TD + c8);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < TD * TD / 8; e += 256) {
+    const int r = e / (TD / 8), c8 = (e % (TD / 8)) * 8;
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = tile[c8 + i][r];
+    *reinterpret_cast<bf16x8*>(dst + r * TD + c8) = v;
+  }
+}
+
+// dq~ = direct + sum_j A_j^T dq^[t + j] for 64 tokens of one head: a GEMM with
+// M = tokens, N = c', K = (j, c).  The dq^ tile (64 tokens plus the k - 1 after
+// them, zero past S) is staged in LDS once as two bf16 halves, hi = bf16(g) and
+// lo = bf16(g - hi), and operand A is read from both (~16 mantissa bits of dq^,
+// fp32 accumulation); operand B is a row of tapT (exact bf16 taps) from L2.
+// Wave w: tokens 32 (w / 2) .. + 31, output channel blocks 2 (w % 2), + 1.
+constexpr int CT = 64;                       // tokens per work-group
+constexpr int GLD = TD + 8;                  // LDS row stride (bf16): conflict-free 16-byte reads
+constexpr int GPLANE = (CT + kMaxConv - 1) * GLD;
+
+__global__ __launch_bounds__(256) void mix_bwd_conv_input_mfma(MixBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 gs[2 * GPLANE];
+  const Dims& dm = a.dm;
+  const int S = a.S;
+  const int t0 = blockIdx.x * CT, hh = blockIdx.y, b = blockIdx.z;
+  const bool isq = hh < dm.Hq;
+  const int h = isq ? hh : hh - dm.Hq;
+  const int k = isq ? dm.kq : dm.kk;
+  const int m0 = isq ? h * dm.kq : dm.Hq * dm.kq + h * dm.kk;   // the head's first tap matrix
+  const int W = 2 * (dm.nq + dm.nk);
+  const int col = isq ? h * TD : dm.nq + h * TD;                // dq^ column in scratch = dq~ column
+  const int dcol = dm.nq + dm.nk + col;                         // direct term
+  const float* srow0 = a.scratch + (long)b * S * W;
+  const int t = threadIdx.x;
+
+  // tile row i = token t0 + i; a resource over the rows inside [t0, S) reads
+  // the rest as zero without a branch
+  const int nrow = CT + k - 1, r1 = min(S, t0 + nrow);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(srow0 + (long)t0 * W + col), 0, r1 > t0 ? ((r1 - t0 - 1) * W + TD) * 4 : 0, 0x00020000);
+  const int n = nrow * (TD / 4);
+  for (int base = 0; base < n; base += 4 * 256) {
+    f32x4 v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = min(base + r * 256 + t, n - 1);
+      const int i = e / (TD / 4), c4 = (e % (TD / 4)) * 4;
+      v[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (i * W + c4) * 4, 0, 0));
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = base + r * 256 + t;
+      if (e < n) {
+        const int i = e / (TD / 4), c4 = (e % (TD / 4)) * 4;
+        bf16x4 hv, lv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          hv[q] = (bf16)v[r][q];
+          lv[q] = (bf16)(v[r][q] - (float)hv[q]);
+        }
+        *reinterpret_cast<bf16x4*>(gs + i * GLD + c4) = hv;
+        *reinterpret_cast<bf16x4*>(gs + GPLANE + i * GLD + c4) = lv;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int lane = t & 63, wave = t >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int tw = 32 * (wave >> 1), nb0 = 2 * (wave & 1);
+  f32x16 acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    // A: lane (token tw + l32, hi) holds channels 16 ks + 8 hi .. of dq^[t + j];
+    // B: lane (c' = nb 32 + l32, hi) holds the same channels of tapT row c'
+    const bf16* arow = gs + (tw + l32 + j) * GLD + hi * 8;
+    const bf16* b0p = reinterpret_cast<const bf16*>(a.tapT) + ((long)(m0 + j) * TD + nb0 * 32 + l32) * TD + hi * 8;
+    const bf16* b1p = b0p + 32 * TD;
+#pragma unroll 4
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(arow + ks * 16);
+      const bf16x8 alo = *reinterpret_cast<const bf16x8*>(arow + GPLANE + ks * 16);
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(b0p + ks * 16);
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(b1p + ks * 16);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b0, acc[0], 0, 0, 0);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b0, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b1, acc[1], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b1, acc[1], 0, 0, 0);
+    }
+  }
+  // D: lane holds column c' = nb 32 + l32, register r token tw + 8 (r / 4) + 4 hi + r % 4
+  bf16* out = reinterpret_cast<bf16*>(a.dqkv) + ((long)b * S + t0) * dm.nqkv + col;
+  const float* dir = srow0 + (long)t0 * W + dcol;
+#pragma unroll
+  for (int nbi = 0; nbi < 2; ++nbi) {
+    const int c = (nb0 + nbi) * 32 + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tr = tw + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (t0 + tr < S) out[(long)tr * dm.nqkv + c] = (bf16)(acc[nbi][r] + dir[(long)tr * W + c]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void mix_bwd_tap_reduce(MixBwdArgs a, int nblk) {
   const Dims& dm = a.dm;
   const long nq = (long)dm.Hq * dm.kq * dm.d * dm.d;
@@ -304,6 +427,10 @@ size_t mix_bwd_part_floats(const Dims& dm, int B, int S) {
   return (size_t)tap_blocks(B, S) * per_blk;
 }
 
+size_t mix_bwd_tapT_bytes(const Dims& dm) {
+  return dm.bf16 && dm.d == TD ? (size_t)(dm.Hq * dm.kq + dm.Hkv * dm.kk) * TD * TD * 2 : 0;
+}
+
 size_t mix_bwd_scratch_floats(const Dims& dm, int B, int S) {
   return (size_t)B * S * 2 * (dm.nq + dm.nk);
 }
@@ -316,8 +443,12 @@ hipError_t launch_mix_bwd(const MixBwdArgs& a, hipStream_t s) {
   if (dm.d == TD) {
     const dim3 gin((a.S + 63) / 64, dm.Hq + dm.Hkv, a.B), gtap(nblk, dm.Hq + dm.Hkv, kmax);
     if (dm.bf16) {
+      if (a.tapT == nullptr) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(mix_bwd_tap_transpose, dim3(dm.Hq * dm.kq + dm.Hkv * dm.kk), dim3(256), 0,
+                         s, a);
       hipLaunchKernelGGL(mix_bwd_pointwise<bf16>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
-      hipLaunchKernelGGL(mix_bwd_conv_input_128<bf16>, gin, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(mix_bwd_conv_input_mfma, dim3((a.S + CT - 1) / CT, dm.Hq + dm.Hkv, a.B),
+                         dim3(256), 0, s, a);
       hipLaunchKernelGGL(mix_bwd_tap_partial_128<bf16>, gtap, dim3(256), 0, s, a);
     } else {
       hipLaunchKernelGGL(mix_bwd_pointwise<float>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
