@@ -404,6 +404,130 @@ __global__ __launch_bounds__(256) void mix_bwd_conv_input_mfma(MixBwdArgs a) {
   }
 }
 
+// Partial tap gradient of one head and tap j over one block of TB tokens on
+// MFMA: part[blk][taps of (head, j)][c][c'] = sum_t dq^[t][c] q~[t - j][c'], a
+// GEMM with M = c, N = c', K = tokens.  Both operands need 8 consecutive
+// tokens per lane, so chunks of 64 tokens of dq^ and of q~ (shifted by j) are
+// staged transposed, [channel][token], as bf16 hi / lo halves; each product
+// takes hi*hi + hi*lo + lo*hi (~16 mantissa bits, fp32 accumulation).
+// Wave w: c blocks 2 (w / 2), + 1 and c' blocks 2 (w % 2), + 1 of 32.
+constexpr int GT = 64;                       // tokens per LDS chunk
+constexpr int TLDT = GT + 8;                 // transposed row stride (bf16)
+constexpr int TPLANE = TD * TLDT;
+
+__global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 gT[2 * TPLANE];   // dq^ [c][t], hi then lo
+  __shared__ __attribute__((aligned(16))) bf16 xT[2 * TPLANE];   // q~[t - j] [c'][t], hi then lo
+  const Dims& dm = a.dm;
+  const int S = a.S;
+  const int blk = blockIdx.x, hh = blockIdx.y, j = blockIdx.z;
+  const int nblk_s = (S + TB - 1) / TB;
+  const int b = blk / nblk_s, tb0 = (blk % nblk_s) * TB;
+  const bool isq = hh < dm.Hq;
+  const int h = isq ? hh : hh - dm.Hq;
+  const int k = isq ? dm.kq : dm.kk;
+  if (j >= k) return;
+  const int W = 2 * (dm.nq + dm.nk);
+  const int gcol = isq ? h * TD : dm.nq + h * TD;      // dq^ in scratch, q~ in qkv
+  const long per_blk = (long)dm.Hq * dm.kq * TD * TD + (long)dm.Hkv * dm.kk * TD * TD;
+  const long off = isq ? (long)h * dm.kq * TD * TD
+                       : (long)dm.Hq * dm.kq * TD * TD + (long)h * dm.kk * TD * TD;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int mb0 = 2 * (wave >> 1), nb0 = 2 * (wave & 1);
+  const int tend = min(S, tb0 + TB);
+  // resources over the rows this block reads: dq^ rows [tb0, tend), q~ rows
+  // [max(tb0 - j, 0), tend - j); rows outside read as zero without a branch
+  const float* gbase = a.scratch + ((long)b * S + tb0) * W + gcol;
+  const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)gbase, 0, ((tend - tb0 - 1) * W + TD) * 4, 0x00020000);
+  const int xr0 = max(tb0 - j, 0), xr1 = tend - j;
+  const float* xbase = a.qkv + ((long)b * S + xr0) * dm.nqkv + gcol;
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)xbase, 0, xr1 > xr0 ? ((xr1 - xr0 - 1) * dm.nqkv + TD) * 4 : 0, 0x00020000);
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  // Staging map: load p = 8 wave + i covers tokens 16 (p % 4) + L % 16 and
+  // float4 groups 4 (p / 4) + L / 16, so one wave's transposed 2-byte stores of
+  // a channel row go to 16 consecutive tokens (bank-conflict free) while each
+  // load reads 64 contiguous bytes of 16 rows.
+  auto stage_rc = [&](int i, int& r, int& c4) {
+    const int pidx = 8 * wave + i;
+    r = 16 * (pidx & 3) + (lane & 15);
+    c4 = 4 * (4 * (pidx >> 2) + (lane >> 4));
+  };
+  for (int c0 = tb0; c0 < tend; c0 += GT) {
+    // 64 tokens x 32 float4 per operand: 8 of each per thread, all in flight
+    f32x4 gv[8], xv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int r, c4;
+      stage_rc(i, r, c4);
+      const int tok = c0 + r;
+      gv[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            grs, ((tok - tb0) * W + c4) * 4, 0, 0));
+      // q~ row tok - j; before row 0 the offset wraps past the range (zero)
+      xv[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            xrs, ((tok - j - xr0) * dm.nqkv + c4) * 4, 0, 0));
+    }
+    __syncthreads();                                     // the previous chunk's reads are done
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int r, c4;
+      stage_rc(i, r, c4);
+      const bool live = c0 + r < tend;                   // tokens past the block: zero
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float g = live ? gv[i][q] : 0.0f, x = live ? xv[i][q] : 0.0f;
+        const bf16 gh = (bf16)g, xh = (bf16)x;
+        gT[(c4 + q) * TLDT + r] = gh;
+        gT[TPLANE + (c4 + q) * TLDT + r] = (bf16)(g - (float)gh);
+        xT[(c4 + q) * TLDT + r] = xh;
+        xT[TPLANE + (c4 + q) * TLDT + r] = (bf16)(x - (float)xh);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < GT / 16; ++ks) {
+      bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ar = ((mb0 + i) * 32 + l32) * TLDT + ks * 16 + hi * 8;
+        const int br = ((nb0 + i) * 32 + l32) * TLDT + ks * 16 + hi * 8;
+        ah[i] = *reinterpret_cast<const bf16x8*>(gT + ar);
+        al[i] = *reinterpret_cast<const bf16x8*>(gT + TPLANE + ar);
+        bh[i] = *reinterpret_cast<const bf16x8*>(xT + br);
+        bl[i] = *reinterpret_cast<const bf16x8*>(xT + TPLANE + br);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mi], bh[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mi], bl[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mi], bh[ni], acc[mi][ni], 0, 0, 0);
+        }
+    }
+  }
+  // D: lane holds column c' = nb 32 + l32, register r row c = mb 32 + 8 (r / 4) + 4 hi + r % 4
+  float* out = a.dconv_part + blk * per_blk + off + (long)j * TD * TD;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = (mb0 + mi) * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        out[(long)c * TD + (nb0 + ni) * 32 + l32] = acc[mi][ni][r];
+      }
+}
+
 __global__ __launch_bounds__(256) void mix_bwd_tap_reduce(MixBwdArgs a, int nblk) {
   const Dims& dm = a.dm;
   const long nq = (long)dm.Hq * dm.kq * dm.d * dm.d;
@@ -449,7 +573,7 @@ hipError_t launch_mix_bwd(const MixBwdArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(mix_bwd_pointwise<bf16>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
       hipLaunchKernelGGL(mix_bwd_conv_input_mfma, dim3((a.S + CT - 1) / CT, dm.Hq + dm.Hkv, a.B),
                          dim3(256), 0, s, a);
-      hipLaunchKernelGGL(mix_bwd_tap_partial_128<bf16>, gtap, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(mix_bwd_tap_partial_mfma, gtap, dim3(256), 0, s, a);
     } else {
       hipLaunchKernelGGL(mix_bwd_pointwise<float>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
       hipLaunchKernelGGL(mix_bwd_conv_input_128<float>, gin, dim3(256), 0, s, a);
