@@ -339,16 +339,17 @@ __global__ __launch_bounds__(256) void mix_bwd_conv_input_mfma(MixBwdArgs a) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(srow0 + (long)t0 * W + col), 0, r1 > t0 ? ((r1 - t0 - 1) * W + TD) * 4 : 0, 0x00020000);
   const int n = nrow * (TD / 4);
-  for (int base = 0; base < n; base += 4 * 256) {
-    f32x4 v[4];
+  constexpr int CNB = 9;                       // 9 x 256 >= 67 rows x 32 float4: one round
+  for (int base = 0; base < n; base += CNB * 256) {
+    f32x4 v[CNB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < CNB; ++r) {
       const int e = min(base + r * 256 + t, n - 1);
       const int i = e / (TD / 4), c4 = (e % (TD / 4)) * 4;
       v[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (i * W + c4) * 4, 0, 0));
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < CNB; ++r) {
       const int e = base + r * 256 + t;
       if (e < n) {
         const int i = e / (TD / 4), c4 = (e % (TD / 4)) * 4;
@@ -372,13 +373,23 @@ __global__ __launch_bounds__(256) void mix_bwd_conv_input_mfma(MixBwdArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+  // the epilogue's direct terms, loaded now so their latency overlaps the MFMAs
+  const float* dir = srow0 + (long)t0 * W + dcol;
+  float dv[2][16];
+#pragma unroll
+  for (int nbi = 0; nbi < 2; ++nbi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tr = min(tw + 8 * (r >> 2) + 4 * hi + (r & 3), S - 1 - t0);
+      dv[nbi][r] = dir[(long)tr * W + (nb0 + nbi) * 32 + l32];
+    }
   for (int j = 0; j < k; ++j) {
     // A: lane (token tw + l32, hi) holds channels 16 ks + 8 hi .. of dq^[t + j];
     // B: lane (c' = nb 32 + l32, hi) holds the same channels of tapT row c'
     const bf16* arow = gs + (tw + l32 + j) * GLD + hi * 8;
     const bf16* b0p = reinterpret_cast<const bf16*>(a.tapT) + ((long)(m0 + j) * TD + nb0 * 32 + l32) * TD + hi * 8;
     const bf16* b1p = b0p + 32 * TD;
-#pragma unroll 4
+#pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(arow + ks * 16);
       const bf16x8 alo = *reinterpret_cast<const bf16x8*>(arow + GPLANE + ks * 16);
@@ -392,14 +403,13 @@ __global__ __launch_bounds__(256) void mix_bwd_conv_input_mfma(MixBwdArgs a) {
   }
   // D: lane holds column c' = nb 32 + l32, register r token tw + 8 (r / 4) + 4 hi + r % 4
   bf16* out = reinterpret_cast<bf16*>(a.dqkv) + ((long)b * S + t0) * dm.nqkv + col;
-  const float* dir = srow0 + (long)t0 * W + dcol;
 #pragma unroll
   for (int nbi = 0; nbi < 2; ++nbi) {
     const int c = (nb0 + nbi) * 32 + l32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tr = tw + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (t0 + tr < S) out[(long)tr * dm.nqkv + c] = (bf16)(acc[nbi][r] + dir[(long)tr * W + c]);
+      if (t0 + tr < S) out[(long)tr * dm.nqkv + c] = (bf16)(acc[nbi][r] + dv[nbi][r]);
     }
   }
 }
