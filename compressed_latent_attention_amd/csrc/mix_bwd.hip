@@ -281,6 +281,93 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_128(MixBwdArgs a) {
   }
 }
 
+// ---- d = 128, group size G = 1, 2, 4 or 8 (compile-time, so the group's rows
+// stay in named registers): the pointwise adjoints with 16 tokens per
+// work-group.  Thread =
+// (token t0 + tid / 16, channels 4 (tid % 16) .. + 3 of the low half and their
+// RoPE partners + 64 in the high half) for every head of the KV group, so the
+// inverse rotation, the QK-mean adjoint (which mixes the group's heads at one
+// channel) and the value-shift adjoint stay in registers, with 16-byte loads
+// and stores.
+constexpr int PT = 16;                       // tokens per work-group
+
+template <typename T, int G>
+__global__ __launch_bounds__(256) void mix_bwd_pointwise_128(MixBwdArgs a) {
+  const Dims& dm = a.dm;
+  const int S = a.S;
+  constexpr int H = TD / 2;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int t = blockIdx.x * PT + threadIdx.x / 16, cq = (threadIdx.x % 16) * 4;
+  if (t >= S) return;
+  // every read first (the group's rows, both dV' rows, then the RoPE pairs),
+  // so they are in flight together
+  f32x4 lo[G + 1], hi[G + 1];
+#pragma unroll
+  for (int hh = 0; hh <= G; ++hh) {
+    const float* src = hh < G ? a.dq + ((long)(b * dm.Hq + g * G + hh) * S + t) * TD
+                              : a.dk + ((long)(b * dm.Hkv + g) * S + t) * TD;
+    lo[hh] = *reinterpret_cast<const f32x4*>(src + cq);
+    hi[hh] = *reinterpret_cast<const f32x4*>(src + cq + H);
+  }
+  const long vrow = (long)(b * dm.Hkv + g) * S;
+  f32x4 dvn[2], dvx[2];
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+    const int c0 = cq + part * H;
+    dvn[part] = *reinterpret_cast<const f32x4*>(a.dv + (vrow + t) * TD + c0);
+    dvx[part] = *reinterpret_cast<const f32x4*>(a.dv + (vrow + min(t + 1, S - 1)) * TD + c0);
+  }
+  // cos / sin of pairs cq .. cq + 3 at position t
+  f32x4 cs_c = {1.f, 1.f, 1.f, 1.f}, cs_s = {0.f, 0.f, 0.f, 0.f};
+  if (dm.flags & kRope) {
+    const f32x4 r0 = *reinterpret_cast<const f32x4*>(a.rope + (long)t * H + cq);
+    const f32x4 r1 = *reinterpret_cast<const f32x4*>(a.rope + (long)t * H + cq + 2);
+    cs_c = f32x4{r0[0], r0[2], r1[0], r1[2]};
+    cs_s = f32x4{r0[1], r0[3], r1[1], r1[3]};
+  }
+  // dq'_h (h < G) and dk'_g (index G): inverse rotation of dQ'' / dK'',
+  // (lo, hi) -> (lo cos + hi sin, hi cos - lo sin)
+#pragma unroll
+  for (int hh = 0; hh <= G; ++hh) {
+    const f32x4 xl = lo[hh], xh = hi[hh];
+    lo[hh] = xl * cs_c + xh * cs_s;
+    hi[hh] = xh * cs_c - xl * cs_s;
+  }
+  const float A = (dm.flags & kQkPre) ? 0.5f : 0.0f;
+  const float Bc = (dm.flags & kQkPost) ? 0.5f : 0.0f;
+  const int W = 2 * (dm.nq + dm.nk);
+  float* srow = a.scratch + ((long)b * S + t) * W;
+  f32x4 sl = {0.f, 0.f, 0.f, 0.f}, sh = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    sl += lo[i];
+    sh += hi[i];
+  }
+  const f32x4 kl = lo[G], kh = hi[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int h = g * G + i;
+    *reinterpret_cast<f32x4*>(srow + h * TD + cq) = (1.0f + Bc) * lo[i] + (Bc / G) * kl;
+    *reinterpret_cast<f32x4*>(srow + h * TD + cq + H) = (1.0f + Bc) * hi[i] + (Bc / G) * kh;
+    *reinterpret_cast<f32x4*>(srow + dm.nq + dm.nk + h * TD + cq) = A * lo[i] + (A / G) * kl;
+    *reinterpret_cast<f32x4*>(srow + dm.nq + dm.nk + h * TD + cq + H) = A * hi[i] + (A / G) * kh;
+  }
+  *reinterpret_cast<f32x4*>(srow + dm.nq + g * TD + cq) = (1.0f + Bc) * kl + Bc * sl;
+  *reinterpret_cast<f32x4*>(srow + dm.nq + g * TD + cq + H) = (1.0f + Bc) * kh + Bc * sh;
+  *reinterpret_cast<f32x4*>(srow + 2 * dm.nq + dm.nk + g * TD + cq) = A * sl + A * kl;
+  *reinterpret_cast<f32x4*>(srow + 2 * dm.nq + dm.nk + g * TD + cq + H) = A * sh + A * kh;
+  // value shift adjoint: shifted channels take dV' of token t + 1 (zero at the last)
+  T* dvo = reinterpret_cast<T*>(a.dqkv) + ((long)b * S + t) * dm.nqkv + dm.nq + dm.nk + g * TD;
+  const int first_shift = (dm.flags & kVShift) ? TD - dm.sv : TD;
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+    const int c0 = cq + part * H;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      dvo[c0 + q] = (T)(c0 + q >= first_shift ? (t + 1 < S ? dvx[part][q] : 0.0f) : dvn[part][q]);
+  }
+}
+
 // ---- bf16 storage, d = 128: the convolution adjoint on MFMA.
 // The adjoint contracts the taps over their first index (dq~[c'] = sum_c
 // A_j[c][c'] dq^[c]), and an MFMA operand lane holds 8 consecutive elements of
@@ -561,6 +648,20 @@ size_t mix_bwd_part_floats(const Dims& dm, int B, int S) {
   return (size_t)tap_blocks(B, S) * per_blk;
 }
 
+// The d = 128 pointwise kernel for the group sizes it is instantiated for;
+// false (nothing launched) for others.
+template <typename T>
+bool launch_pointwise_128(const MixBwdArgs& a, hipStream_t s) {
+  const dim3 grid((a.S + PT - 1) / PT, a.dm.Hkv, a.B);
+  switch (a.dm.G) {
+    case 1: hipLaunchKernelGGL((mix_bwd_pointwise_128<T, 1>), grid, dim3(256), 0, s, a); return true;
+    case 2: hipLaunchKernelGGL((mix_bwd_pointwise_128<T, 2>), grid, dim3(256), 0, s, a); return true;
+    case 4: hipLaunchKernelGGL((mix_bwd_pointwise_128<T, 4>), grid, dim3(256), 0, s, a); return true;
+    case 8: hipLaunchKernelGGL((mix_bwd_pointwise_128<T, 8>), grid, dim3(256), 0, s, a); return true;
+    default: return false;
+  }
+}
+
 size_t mix_bwd_tapT_bytes(const Dims& dm) {
   return dm.bf16 && dm.d == TD ? (size_t)(dm.Hq * dm.kq + dm.Hkv * dm.kk) * TD * TD * 2 : 0;
 }
@@ -580,12 +681,14 @@ hipError_t launch_mix_bwd(const MixBwdArgs& a, hipStream_t s) {
       if (a.tapT == nullptr) return hipErrorInvalidValue;
       hipLaunchKernelGGL(mix_bwd_tap_transpose, dim3(dm.Hq * dm.kq + dm.Hkv * dm.kk), dim3(256), 0,
                          s, a);
-      hipLaunchKernelGGL(mix_bwd_pointwise<bf16>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
+      if (!launch_pointwise_128<bf16>(a, s))
+        hipLaunchKernelGGL(mix_bwd_pointwise<bf16>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
       hipLaunchKernelGGL(mix_bwd_conv_input_mfma, dim3((a.S + CT - 1) / CT, dm.Hq + dm.Hkv, a.B),
                          dim3(256), 0, s, a);
       hipLaunchKernelGGL(mix_bwd_tap_partial_mfma, gtap, dim3(256), 0, s, a);
     } else {
-      hipLaunchKernelGGL(mix_bwd_pointwise<float>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
+      if (!launch_pointwise_128<float>(a, s))
+        hipLaunchKernelGGL(mix_bwd_pointwise<float>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
       hipLaunchKernelGGL(mix_bwd_conv_input_128<float>, gin, dim3(256), 0, s, a);
       hipLaunchKernelGGL(mix_bwd_tap_partial_128<float>, gtap, dim3(256), 0, s, a);
     }

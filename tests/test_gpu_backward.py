@@ -27,6 +27,13 @@ CASES = [
     Workload("bf16_bwd_gqa", B=1, S=300, E=512, C=1, Hq=4, Hkv=2, seed=64, kind="backward"),
     Workload("bf16_bwd_b2", B=2, S=129, E=1024, C=2, Hq=4, Hkv=4, kq=2, kk=3, seed=65,
              kind="backward"),
+    # d = 128 with four and eight query heads per KV head (the group-size
+    # instances of the pointwise adjoint); the second without the post-conv
+    # QK-mean and with a 40-channel value shift
+    Workload("bf16_bwd_g4", B=1, S=200, E=512, C=1, Hq=4, Hkv=1, kq=3, kk=2, seed=69,
+             kind="backward"),
+    Workload("bf16_bwd_g8_flags", B=1, S=150, E=1024, C=1, Hq=8, Hkv=1, flags=1 | 4 | 8, sv=40,
+             seed=70, kind="backward"),
     # large enough that the weight gradients run split over K (16 partial sums)
     # on the 256 x 256 kernel, and the attention backward spans 16 key blocks
     Workload("bf16_bwd_splitk", B=1, S=2048, E=1024, C=2, Hq=4, Hkv=2, seed=67,
