@@ -15,7 +15,9 @@
 //           half, the second writing to scratch that a small kernel adds in),
 //           so that the causal triangle spreads over twice as many CUs:
 //             S = Q K^T, dP = dO V^T (A = Q / dO rows from LDS, B = the wave's
-//             K / V rows held in registers), P and dS in registers, then
+//             K / V rows held in registers; S starts at -inf for the causally
+//             masked pairs of diagonal steps, so exp2 needs no per-element
+//             test), P and dS in registers, then
 //             dV += P^T dO and dK += dS^T Q (A = P^T / dS^T straight from the
 //             accumulators, B = dO^T / Q^T columns from LDS);
 //   dq    — work-group = 128 queries of one head, 4 waves of 32 queries; loops
@@ -203,11 +205,14 @@ __device__ __forceinline__ void dkdv_store(DkdvStage& st, int t, const DkdvRegs&
 // S = Q K^T and dP = dO V^T of one step: the stage's Q / dO rows (A, read with
 // the permuted row so that P / dS come out as 8 consecutive queries per lane)
 // times the wave's K / V rows held in registers (B).
+// S starts from `sinit` (0, or -inf where a key follows a query: the causal
+// mask, so that exp2 gives P = 0 there without a per-element test).
 __device__ __forceinline__ void dkdv_sdp(const DkdvStage& st, const bf16x8 (&kf)[8],
-                                         const bf16x8 (&vf)[8], int prow, int hi, f32x16& sacc,
-                                         f32x16& pacc) {
+                                         const bf16x8 (&vf)[8], int prow, int hi,
+                                         const f32x16& sinit, f32x16& sacc, f32x16& pacc) {
+  sacc = sinit;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
+  for (int r = 0; r < 16; ++r) pacc[r] = 0.0f;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     const bf16x8 qa = *reinterpret_cast<const bf16x8*>(st.qn + prow * NLD + ks * 16 + hi * 8);
@@ -259,10 +264,23 @@ void bwd_dkdv_kernel(AttnBwdArgs a) {
   const int nqb = part ? nqb_all - nfirst : nfirst;
   const int nsteps = G * nqb;
   const int prow = perm_row(l32);
-  // step s clamped to the last one: the pipeline's loads past the end repeat
-  // it into a stage nobody reads again
-  auto head_of = [&](int s) { return g * G + min(s, nsteps - 1) / nqb; };
-  auto q0_of = [&](int s) { return (qb0 + min(s, nsteps - 1) % nqb) * TB; };
+  // Steps run head-major: step s = (head s / nqb, query block s % nqb).  The
+  // current step's block and the loaded step's (head, block) advance by
+  // counters (a division per step would cost ~40 scalar instructions in every
+  // wave); the loaded step stops at the last one, so the pipeline's loads past
+  // the end repeat it into a stage nobody reads again.
+  int cur_qi = 0;                                   // block index of step s
+  int ld_s = min(3, nsteps - 1);                    // step loaded next (s + 3, clamped)
+  int ld_h = ld_s / max(nqb, 1), ld_qi = ld_s - ld_h * nqb;
+  auto advance_load = [&]() {
+    if (ld_s < nsteps - 1) {
+      ++ld_s;
+      if (++ld_qi == nqb) {
+        ld_qi = 0;
+        ++ld_h;
+      }
+    }
+  };
 
   // Software pipeline over three LDS stages (step s in stage s % 3).  Iteration
   // s computes S and dP of step s + 1 and the softmax of step s in one block
@@ -274,22 +292,40 @@ void bwd_dkdv_kernel(AttnBwdArgs a) {
   // is exactly zero.
   if (nsteps > 0) {
     DkdvRegs pre;
-    dkdv_load(a, b, head_of(0), q0_of(0), t, pre);
-    dkdv_store(stg[0], t, pre);
-    dkdv_load(a, b, head_of(1), q0_of(1), t, pre);
-    dkdv_store(stg[1], t, pre);
-    dkdv_load(a, b, head_of(2), q0_of(2), t, pre);
+    // steps 0, 1, 2 (clamped): the few divisions happen once
+    for (int i = 0; i < 3; ++i) {
+      const int si = min(i, nsteps - 1), hi_ = si / nqb;
+      dkdv_load(a, b, g * G + hi_, (qb0 + si - hi_ * nqb) * TB, t, pre);
+      if (i < 2) dkdv_store(stg[i], t, pre);
+    }
     __syncthreads();
-    f32x16 sacc, pacc;
-    dkdv_sdp(stg[0], kf, vf, prow, hi, sacc, pacc);
+    // initial S of a step: -inf where the wave's key follows the query (only
+    // the steps whose queries reach below the wave's last key have any)
+    // lane (key l32, hi): register r is query q0 + 16 (r / 8) + 8 hi + r % 8
+    auto s_init = [&](int q0n, f32x16& si) {
+      if (q0n < kw0 + 31) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          si[r] = my_key > q0n + 16 * (r >> 3) + 8 * hi + (r & 7) ? -INFINITY : 0.0f;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) si[r] = 0.0f;
+      }
+    };
+    f32x16 sacc, pacc, sinit;
+    s_init(qb0 * TB, sinit);
+    dkdv_sdp(stg[0], kf, vf, prow, hi, sinit, sacc, pacc);
 
     for (int s = 0; s < nsteps; ++s) {
       const DkdvStage& st = stg[s % 3];
-      const int q0 = q0_of(s);
+      const int q0 = (qb0 + cur_qi) * TB;
+      if (++cur_qi == nqb) cur_qi = 0;
       dkdv_store(stg[(s + 2) % 3], t, pre);
-      dkdv_load(a, b, head_of(s + 3), q0_of(s + 3), t, pre);
+      dkdv_load(a, b, g * G + ld_h, (qb0 + ld_qi) * TB, t, pre);
+      advance_load();
       f32x16 sn, pn;
-      dkdv_sdp(stg[(s + 1) % 3], kf, vf, prow, hi, sn, pn);
+      s_init((qb0 + cur_qi) * TB, sinit);           // step s + 1's block (cur_qi has advanced)
+      dkdv_sdp(stg[(s + 1) % 3], kf, vf, prow, hi, sinit, sn, pn);
       // lane (key l32, hi): register r is query q0 + 16 (r / 8) + 8 hi + r % 8
       f16x8 pf[2], sf[2];
 #pragma unroll
@@ -304,9 +340,9 @@ void bwd_dkdv_kernel(AttnBwdArgs a) {
           const int r = 8 * half + e;
           const float lse2 = e < 4 ? l0[e] : l1[e - 4];
           const float dsm = e < 4 ? d0[e] : d1[e - 4];
-          const int q = q0 + qi + e;
-          float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c1, -lse2));
-          if (my_key > q) p = 0.0f;            // causal (queries past S have lse2 = +inf)
+
+          // masked pairs have S = -inf and queries past S lse2 = +inf: P = 0
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c1, -lse2));
           pf[half][e] = (f16)p;
           sf[half][e] = (f16)(p * (pacc[r] - dsm));
         }
