@@ -496,7 +496,19 @@ void bwd_dq_kernel(AttnBwdArgs a) {
     if (j0 <= qw0 + 31) {                    // else every key follows every query of the wave
       f32x16 sacc, pacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
+      for (int r = 0; r < 16; ++r) pacc[r] = 0.0f;
+      // S^T starts at -inf where the key follows the lane's query (only the
+      // steps whose keys reach past the wave's first query have any), so exp2
+      // gives P = 0 there without a per-element test.  Lane (query l32, hi):
+      // register r is key j0 + 16 (r / 8) + 8 hi + r % 8.
+      if (j0 + 31 > qw0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sacc[r] = j0 + 16 * (r >> 3) + 8 * hi + (r & 7) > my_q ? -INFINITY : 0.0f;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+      }
       // K and V fragments through a ring of 4: the reads run 4 k slices ahead
       // of the MFMAs instead of one read-wait-MFMA per slice
       bf16x8 ka[4], va[4];
@@ -528,9 +540,7 @@ void bwd_dq_kernel(AttnBwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * half + e;
-          const int key = j0 + 16 * half + 8 * hi + e;
-          float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c1, -lse2));
-          if (key > my_q) p = 0.0f;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c1, -lse2));
           sf[half][e] = (f16)(p * (pacc[r] - dsm));
         }
       // dQ += dS K: A = dS (lane = query row), B = K^T columns
