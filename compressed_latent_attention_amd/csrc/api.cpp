@@ -589,6 +589,10 @@ cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, cons
       ab.dk2 = (float*)((char*)ab.dOT + align256((size_t)B * dm.nq * sp * esize(dm)));
       ab.dv2 = (float*)((char*)ab.dk2 + align256((size_t)B * S * dm.nk * 4));
     }
+    // the mix backward's pointwise pass adds the second-half dK / dV partials
+    // as it reads dK / dV, when it can (no separate sum launch)
+    const bool sum_in_mix = attn_bwd_mfma_supported(dm) && mix_bwd_adds_dkdv2(dm);
+    ab.sum_by_consumer = sum_in_mix;
     CCA_TRY_HIP(timed(h, "bwd_attn", s, [&] { return launch_attn_bwd(ab, s); }));
 
     MixBwdArgs mb{};
@@ -599,6 +603,8 @@ cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, cons
     mb.dconv_q = (float*)g->dconv_q; mb.dconv_k = (float*)g->dconv_k;
     mb.scratch = (float*)(wb + L.scratch);
     mb.tapT = mix_bwd_tapT_bytes(dm) ? (void*)(wb + L.tapT) : nullptr;
+    mb.dk2 = sum_in_mix ? ab.dk2 : nullptr;
+    mb.dv2 = sum_in_mix ? ab.dv2 : nullptr;
     CCA_TRY_HIP(timed(h, "bwd_mix", s, [&] { return launch_mix_bwd(mb, s); }));
 
     // dx = dq~ W_q + dk~ W_k + dv~ W_v ; dW_* = d*~^T x

@@ -590,9 +590,11 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) {
   if (!a.dk2 || !a.dv2) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(2 * ((a.S + 127) / 128), dm.Hkv, a.B), dim3(256), 0, s,
                      a);
-  const long n4 = (long)a.B * dm.Hkv * a.S * D / 4;
-  hipLaunchKernelGGL(bwd_dkdv_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
-                     a.dk, a.dk2, a.dv, a.dv2, n4);
+  if (!a.sum_by_consumer) {
+    const long n4 = (long)a.B * dm.Hkv * a.S * D / 4;
+    hipLaunchKernelGGL(bwd_dkdv_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                       a.dk, a.dk2, a.dv, a.dv2, n4);
+  }
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(((a.S + 127) / 128) * dm.Hq * a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }

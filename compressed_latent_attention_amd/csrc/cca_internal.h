@@ -196,11 +196,16 @@ struct AttnBwdArgs {
   void* dOT;         // dO^T  [B,Hq,d,s_pad]
   int s_pad;         // S rounded up to a multiple of 64
   // dK / dV of the second half of each key block's query range (fp32, same
-  // layout as dk / dv), added into dk / dv before the kernels return
+  // layout as dk / dv), added into dk / dv before the kernels return, unless
+  // the consumer adds them as it reads dk / dv (sum_by_consumer)
   float* dk2;
   float* dv2;
+  bool sum_by_consumer;
 };
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
+// True when launch_attn_bwd takes the MFMA kernels (bf16, d = 128), which
+// produce the dk2 / dv2 second-half partials.
+bool attn_bwd_mfma_supported(const Dims& dm);
 // Bytes of the MFMA attention backward's workspace: the transposed copies and
 // the second-half dK / dV partials (0 when the config takes the generic path).
 size_t attn_bwd_transpose_bytes(const Dims& dm, int B, int S);
@@ -221,9 +226,14 @@ struct MixBwdArgs {
   float* dconv_k;        // final fp32 [Hkv,kk,d,d]
   float* scratch;        // fp32 workspace for dq^ / dk^ [B*S, nq + nk]
   void* tapT;            // bf16, d = 128: workspace for the transposed taps (mix_bwd_tapT_bytes)
+  // nullable: second-half partials the attention backward left for the
+  // consumer, added to dk / dv as they are read (only when mix_bwd_adds_dkdv2)
+  const float* dk2;
+  const float* dv2;
 };
 hipError_t launch_mix_bwd(const MixBwdArgs& a, hipStream_t s);
 size_t mix_bwd_tapT_bytes(const Dims& dm);
+bool mix_bwd_adds_dkdv2(const Dims& dm);
 size_t mix_bwd_part_floats(const Dims& dm, int B, int S);
 size_t mix_bwd_scratch_floats(const Dims& dm, int B, int S);
 

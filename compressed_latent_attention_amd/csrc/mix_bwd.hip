@@ -309,6 +309,13 @@ __global__ __launch_bounds__(256) void mix_bwd_pointwise_128(MixBwdArgs a) {
     lo[hh] = *reinterpret_cast<const f32x4*>(src + cq);
     hi[hh] = *reinterpret_cast<const f32x4*>(src + cq + H);
   }
+  // dK'' partial of the key block's second query half, when left to this kernel
+  f32x4 k2l = {0.f, 0.f, 0.f, 0.f}, k2h = {0.f, 0.f, 0.f, 0.f};
+  if (a.dk2) {
+    const float* src2 = a.dk2 + ((long)(b * dm.Hkv + g) * S + t) * TD;
+    k2l = *reinterpret_cast<const f32x4*>(src2 + cq);
+    k2h = *reinterpret_cast<const f32x4*>(src2 + cq + H);
+  }
   const long vrow = (long)(b * dm.Hkv + g) * S;
   f32x4 dvn[2], dvx[2];
 #pragma unroll
@@ -316,7 +323,13 @@ __global__ __launch_bounds__(256) void mix_bwd_pointwise_128(MixBwdArgs a) {
     const int c0 = cq + part * H;
     dvn[part] = *reinterpret_cast<const f32x4*>(a.dv + (vrow + t) * TD + c0);
     dvx[part] = *reinterpret_cast<const f32x4*>(a.dv + (vrow + min(t + 1, S - 1)) * TD + c0);
+    if (a.dv2) {
+      dvn[part] += *reinterpret_cast<const f32x4*>(a.dv2 + (vrow + t) * TD + c0);
+      dvx[part] += *reinterpret_cast<const f32x4*>(a.dv2 + (vrow + min(t + 1, S - 1)) * TD + c0);
+    }
   }
+  lo[G] += k2l;
+  hi[G] += k2h;
   // cos / sin of pairs cq .. cq + 3 at position t
   f32x4 cs_c = {1.f, 1.f, 1.f, 1.f}, cs_s = {0.f, 0.f, 0.f, 0.f};
   if (dm.flags & kRope) {
@@ -662,6 +675,10 @@ bool launch_pointwise_128(const MixBwdArgs& a, hipStream_t s) {
   }
 }
 
+bool mix_bwd_adds_dkdv2(const Dims& dm) {
+  return dm.d == TD && (dm.G == 1 || dm.G == 2 || dm.G == 4 || dm.G == 8);
+}
+
 size_t mix_bwd_tapT_bytes(const Dims& dm) {
   return dm.bf16 && dm.d == TD ? (size_t)(dm.Hq * dm.kq + dm.Hkv * dm.kk) * TD * TD * 2 : 0;
 }
@@ -675,6 +692,7 @@ hipError_t launch_mix_bwd(const MixBwdArgs& a, hipStream_t s) {
   const int nblk = tap_blocks(a.B, a.S);
   const long per_blk = (long)dm.Hq * dm.kq * dm.d * dm.d + (long)dm.Hkv * dm.kk * dm.d * dm.d;
   const int kmax = std::max(dm.kq, dm.kk);
+  if ((a.dk2 || a.dv2) && !mix_bwd_adds_dkdv2(dm)) return hipErrorInvalidValue;
   if (dm.d == TD) {
     const dim3 gin((a.S + 63) / 64, dm.Hq + dm.Hkv, a.B), gtap(nblk, dm.Hq + dm.Hkv, kmax);
     if (dm.bf16) {
