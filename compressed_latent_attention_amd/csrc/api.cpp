@@ -579,14 +579,15 @@ cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, cons
     ab.q = qr; ab.k = kr; ab.v = vs; ab.o32 = o32; ab.dO = dO; ab.lse = lse; ab.Dsum = Dsum;
     ab.dq = dq; ab.dk = dk; ab.dv = dv;
     {
-      // transposed copies for the MFMA path: Q''^T | K''^T | dO^T, each 256-byte aligned
+      // fp16 copies for the MFMA path: Q'' | K'' | V' | dO, each 256-byte aligned
       const long sp = pad64(S);
       char* t = wb + L.trans;
       ab.s_pad = (int)sp;
-      ab.qT = t;
-      ab.kT = t + align256((size_t)B * dm.nq * sp * esize(dm));
-      ab.dOT = (char*)ab.kT + align256((size_t)B * dm.nk * sp * esize(dm));
-      ab.dk2 = (float*)((char*)ab.dOT + align256((size_t)B * dm.nq * sp * esize(dm)));
+      ab.q16 = t;
+      ab.k16 = t + align256((size_t)B * dm.nq * sp * 2);
+      ab.v16 = (char*)ab.k16 + align256((size_t)B * dm.nk * sp * 2);
+      ab.do16 = (char*)ab.v16 + align256((size_t)B * dm.nk * sp * 2);
+      ab.dk2 = (float*)((char*)ab.do16 + align256((size_t)B * dm.nq * sp * 2));
       ab.dv2 = (float*)((char*)ab.dk2 + align256((size_t)B * S * dm.nk * 4));
     }
     // the mix backward's pointwise pass adds the second-half dK / dV partials

@@ -7,59 +7,54 @@
 //
 // Three kernels, no atomics (every sum has a fixed order, so results are
 // run-to-run identical):
-//   prep  — Q''^T, K''^T, dO^T (channel-major copies, rows padded to s_pad) and
-//           D = rowsum(dO * O) from the saved fp32 O;
-//   dkdv  — work-group = 128 keys of one KV head, 4 waves of 32 keys; loops over
-//           the query blocks (32 queries) of every head of the group; two
-//           work-groups share each key block's query range (first and second
-//           half, the second writing to scratch that a small kernel adds in),
-//           so that the causal triangle spreads over twice as many CUs:
-//             S = Q K^T, dP = dO V^T (A = Q / dO rows from LDS, B = the wave's
-//             K / V rows held in registers; S starts at -inf for the causally
-//             masked pairs of diagonal steps, so exp2 needs no per-element
-//             test), P and dS in registers, then
-//             dV += P^T dO and dK += dS^T Q (A = P^T / dS^T straight from the
-//             accumulators, B = dO^T / Q^T columns from LDS);
+//   prep  — fp16 copies of Q'', K'', V' and dO as head-major rows (zero from
+//           row S to s_pad) and D = rowsum(dO * O) from the saved fp32 O;
+//   dkdv  — work-group = 128 keys of one KV group, 8 waves.  Producers (waves
+//           0-3, 32 keys each, K and V rows in registers) compute S = Q K^T and
+//           dP = dO V^T, the softmax, dS and dK += dS^T Q, and leave P in LDS;
+//           consumers (waves 4-7, wave w + 4 on the SIMD of wave w) stage the
+//           Q / dO tiles into LDS and add dV += P^T dO one step behind.  The two
+//           waves of a SIMD overlap one's softmax with the other's MFMAs.  Two
+//           work-groups per key block: with an even group size each takes half
+//           of the group's heads, otherwise half of each head's query range;
+//           query blocks run in descending order, so the work-groups of a head
+//           read the same tile at about the same time;
 //   dq    — work-group = 128 queries of one head, 4 waves of 32 queries; loops
 //           over the key blocks (32 keys) up to the diagonal:
-//             S^T = K Q^T, dP^T = V dO^T (B = the wave's Q / dO held in
-//             registers), dQ += dS K (B = K^T columns from LDS).
-// S and dP use v_mfma_f32_32x32x16_bf16 on the stored bf16 tensors; dV, dK and
-// dQ use v_mfma_f32_32x32x16_f16: P and dS are rounded to fp16 (11 significant
-// bits), and the transposed copies of Q'', K'' and dO are written in fp16
-// (exact for bf16 values in fp16's normal range).  dS = P (dP - D) has rows
+//             S^T = K Q^T, dP^T = V dO^T (B = the wave's Q / dO rows held in
+//             registers), dQ += dS K.
+// Every product is a v_mfma_f32_32x32x16_f16 with fp32 accumulation.  The fp16
+// copies hold the stored bf16 values exactly while they lie in fp16's normal
+// range (|x| in [2^-14, 65504]; smaller gradients would need a loss scale); P
+// and dS are rounded to fp16 (11 significant bits).  dS = P (dP - D) has rows
 // that sum to zero, so dQ and dK cancel heavily; bf16 dS (8 bits) would cost
-// ~1% in them.  fp32 accumulation throughout.  The A
-// rows of S (queries in dkdv, keys in dq) are read with bits 2 and 3 of the
-// row index swapped, so that the 8 accumulator registers a lane passes on
-// cover 8 consecutive queries (keys) and P / dS feed the next MFMA without a
-// shuffle.  Tiles are staged through registers into padded LDS rows
-// (conflict-free 16-byte reads), with one barrier per step.
+// ~1% in them.  The transposed operands (Q^T and dO^T of dK and dV, K^T of dQ)
+// are read from the natural LDS tiles with ds_read_b64_tr_b16, so only natural
+// rows cross HBM.  The A rows of S (queries in dkdv, keys in dq) are read with
+// bits 2 and 3 of the row index swapped, so that the 8 accumulator registers a
+// lane passes on cover 8 consecutive queries (keys) and P / dS feed the next
+// MFMA without a shuffle.
 #include "cca_internal.h"
 
 namespace cca {
 namespace {
 
 constexpr int D = 128;
-constexpr int NLD = D + 8;      // natural tile row stride (elements), 272 B
 constexpr int TB = 32;          // tokens per step
-constexpr int TLD = TB + 8;     // transposed tile row stride (elements), 80 B
+constexpr int TROW = 160;       // LDS tile row stride, fp16 elements (320 B = 20 chunks of 16 B)
+constexpr int TILE = TB * TROW; // one tile: 32 token rows of 128 channels
 constexpr float kLog2e = 1.44269504088896340736f;
 
 typedef _Float16 f16;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 bool mfma_bwd(const Dims& dm) { return dm.bf16 && dm.d == D; }
 
 __device__ __forceinline__ int perm_row(int i) {   // swap bits 2 and 3
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
-}
-
-__device__ __forceinline__ bf16x8 zero8() {
-  bf16x8 z;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
-  return z;
 }
 
 __device__ __forceinline__ f16x8 to_f16(const bf16x8& v) {
@@ -69,316 +64,366 @@ __device__ __forceinline__ f16x8 to_f16(const bf16x8& v) {
   return r;
 }
 
+// ------------------------------------------------------------------ LDS tiles
+// A tile holds 32 token rows of 128 fp16 channels; chunk ch (channels 8 ch ..
+// 8 ch + 7) of row r sits at chunk ch ^ ((r >> 2) & 3) of a 20-chunk row.  The
+// row stride (4 chunks past a multiple of 16) spreads the 4 rows of a
+// transposing read over the 64 banks and the XOR spreads the 16 rows of an
+// A-operand read, so the three access patterns below (A-operand rows, the
+// transposing reads and the staging stores) are free of bank conflicts.
+__device__ __forceinline__ int tile_off(int r, int ch) {
+  return r * TROW + ((ch ^ ((r >> 2) & 3)) << 3);
+}
+
+// A operand of an MFMA over the channels: lane (row l32, hi) reads chunk
+// 2 ks + hi of row perm_row(l32), at ao[ks & 1] + 32 (ks >> 1).
+__device__ __forceinline__ void a_offsets(int prow, int hi, int (&ao)[2]) {
+  ao[0] = tile_off(prow, hi);
+  ao[1] = tile_off(prow, 2 + hi);
+}
+
+// B operand over the tokens (k = token rows, n = channels) straight from a
+// natural tile: lane (n = l32, hi) needs rows 16 ks + 8 hi + 0..7 of column
+// 32 nb + l32.  ds_read_b64_tr_b16 gives lane i of a 16-lane group, as its
+// element j, element i & 3 of the 8 bytes addressed by lane (i >> 2) + 4 j of
+// the group; so lane c of a group addresses row R + (c >> 2), columns
+// C + 4 (c & 3) .. + 3, and lane i receives rows R .. R + 3 of column C + i.
+// Two reads (R = 16 ks + 8 hi and R + 4) make the fragment; the lane's offsets
+// are to[r] + 2560 ks + 32 nb.
+__device__ __forceinline__ void t_offsets(int lane, int (&to)[2]) {
+  const int c = lane & 15, g = (lane >> 4) & 1, hi = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = 8 * hi + 4 * r + (c >> 2);
+    const int chunk = 2 * g + ((c & 3) >> 1);
+    to[r] = row * TROW + ((chunk ^ ((row >> 2) & 3)) << 3) + (c & 1) * 4;
+  }
+}
+
+__device__ __forceinline__ f16x8 read_t(const f16* tile, const int (&to)[2], int ks, int nb) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(tile + to[0] + 2560 * ks + 32 * nb));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(tile + to[1] + 2560 * ks + 32 * nb));
+  return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ f16x8 read_a(const f16* tile, const int (&ao)[2], int ks) {
+  return *reinterpret_cast<const f16x8*>(tile + ao[ks & 1] + 32 * (ks >> 1));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows16(const void* base, long row0, int nrows) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const f16*>(base) + row0 * D), 0, nrows * D * 2, 0x00020000);
+}
+
+__device__ __forceinline__ f16x8 load16(const __amdgpu_buffer_rsrc_t& rs, int elem) {
+  return __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, elem * 2, 0, 0));
+}
+
+// Work-group barrier that waits only for this wave's LDS operations, so
+// global loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------ prep
-// Tile of 64 tokens x 128 channels of one head: transpose through LDS.
-// blockIdx.y: 0..Hq-1 -> Q''^T and dO^T of head y (and D); Hq.. -> K''^T.
+// 64 tokens of one head per work-group.  blockIdx.y: 0..Hq-1 -> Q'' and dO of
+// head y (and D); Hq.. -> K'' and V' of KV head y - Hq.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnBwdArgs a) {
-  __shared__ bf16 tq[64][D + 2];
-  __shared__ bf16 tdo[64][D + 2];
   const Dims& dm = a.dm;
   const int S = a.S, sp = a.s_pad;
   const int t0 = blockIdx.x * 64, y = blockIdx.y, b = blockIdx.z;
   const bool is_q = y < dm.Hq;
   const int h = is_q ? y : y - dm.Hq;
-  const bf16* src = is_q ? reinterpret_cast<const bf16*>(a.q) + ((long)(b * dm.Hq + h) * S) * D
-                         : reinterpret_cast<const bf16*>(a.k) + ((long)(b * dm.Hkv + h) * S) * D;
-  const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + (long)b * S * dm.nq + h * D;
-  // load: thread -> (row, 8 channels)
+  const long hrow = (long)(b * (is_q ? dm.Hq : dm.Hkv) + h);
+  const bf16* src0 = is_q ? reinterpret_cast<const bf16*>(a.q) + hrow * S * D
+                          : reinterpret_cast<const bf16*>(a.k) + hrow * S * D;
+  const bf16* src1 = is_q ? reinterpret_cast<const bf16*>(a.dO) + (long)b * S * dm.nq + h * D
+                          : reinterpret_cast<const bf16*>(a.v) + hrow * S * D;
+  const long ld1 = is_q ? dm.nq : D;
+  f16* dst0 = reinterpret_cast<f16*>(is_q ? a.q16 : a.k16) + hrow * sp * D;
+  f16* dst1 = reinterpret_cast<f16*>(is_q ? a.do16 : a.v16) + hrow * sp * D;
+  // thread -> (row, 8 channels); rows past S are written as zero
   for (int f = threadIdx.x; f < 64 * (D / 8); f += 256) {
-    const int r = f / (D / 8), c = (f % (D / 8)) * 8;
+    const int r = f >> 4, c = (f & 15) * 8;
     const int t = t0 + r;
-    bf16x8 v = zero8(), w = zero8();
-    if (t < S) {
-      v = *reinterpret_cast<const bf16x8*>(src + (long)t * D + c);
-      if (is_q) w = *reinterpret_cast<const bf16x8*>(dob + (long)t * dm.nq + c);
-    }
+    bf16x8 v, w;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      tq[r][c + e] = v[e];
-      tdo[r][c + e] = w[e];
+    for (int e = 0; e < 8; ++e) v[e] = w[e] = (bf16)0.0f;
+    if (t < S) {
+      v = *reinterpret_cast<const bf16x8*>(src0 + (long)t * D + c);
+      w = *reinterpret_cast<const bf16x8*>(src1 + (long)t * ld1 + c);
     }
+    *reinterpret_cast<f16x8*>(dst0 + (long)t * D + c) = to_f16(v);
+    *reinterpret_cast<f16x8*>(dst1 + (long)t * D + c) = to_f16(w);
   }
-  // D_t = <dO_t, O_t> in fp32 (one wave per 16 tokens, 4 lanes per token... 64
-  // tokens x 128 channels: each thread sums 32 channels of one token)
+  // D_t = <dO_t, O_t> in fp32: each thread sums 32 channels of one token
   if (is_q) {
     const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
     const int t = t0 + r;
     float sacc = 0.0f;
     if (t < S) {
       const float* orow = a.o32 + ((long)(b * S + t) * dm.Hq + h) * D + part * 32;
-      const bf16* drow = dob + (long)t * dm.nq + part * 32;
+      const bf16* drow = src1 + (long)t * dm.nq + part * 32;
 #pragma unroll 8
       for (int c = 0; c < 32; ++c) sacc = fmaf((float)drow[c], orow[c], sacc);
     }
     sacc += __shfl_xor(sacc, 1);
     sacc += __shfl_xor(sacc, 2);
-    if (part == 0 && t < S) a.Dsum[(long)(b * dm.Hq + h) * S + t] = sacc;
-  }
-  __syncthreads();
-  // store: thread -> (channel, 8 tokens); tokens past S are zero (tile zeroed)
-  f16* dstq = reinterpret_cast<f16*>(is_q ? a.qT : a.kT) +
-              ((long)(b * (is_q ? dm.Hq : dm.Hkv) + h) * D) * sp;
-  f16* dstd = reinterpret_cast<f16*>(a.dOT) + ((long)(b * dm.Hq + h) * D) * sp;
-  for (int f = threadIdx.x; f < D * 8; f += 256) {
-    const int c = f / 8, r = (f % 8) * 8;
-    if (t0 + r >= sp) continue;
-    bf16x8 v, w;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v[e] = tq[r + e][c];
-      w[e] = tdo[r + e][c];
-    }
-    *reinterpret_cast<f16x8*>(dstq + (long)c * sp + t0 + r) = to_f16(v);
-    if (is_q) *reinterpret_cast<f16x8*>(dstd + (long)c * sp + t0 + r) = to_f16(w);
+    if (part == 0 && t < S) a.Dsum[hrow * S + t] = sacc;
   }
 }
 
 // ------------------------------------------------------------------ dkdv
 struct DkdvStage {
-  bf16 qn[TB * NLD];     // Q rows      [32 q][128 c]
-  bf16 don[TB * NLD];    // dO rows     [32 q][128 c]
-  f16 qt[D * TLD];       // Q^T         [128 c][32 q], fp16
-  f16 dot[D * TLD];      // dO^T        [128 c][32 q], fp16
+  f16 q[TILE];           // Q'' rows of the step's 32 queries
+  f16 dO[TILE];          // dO rows
   float lse2[TB];        // lse * log2(e); +inf past the sequence
   float dsum[TB];
 };
 
-struct DkdvRegs {
-  bf16x8 qn[2], don[2];
-  f16x8 qt[2], dot[2];
-  float lse2, dsum;
+struct DkdvSmem {
+  DkdvStage stg[3];
+  f16 pbuf[2][4][2 * 64 * 8];    // P of a step per producer: [parity][producer][ks][lane][8]
 };
 
-// Registers of one step: buffer loads whose resources end at row S - 1, so rows
-// past the sequence read as zero without a branch (the loop body stays one
-// block); lse of a query past S becomes +inf (its P is zero).
-__device__ __forceinline__ void dkdv_load(const AttnBwdArgs& a, int b, int h, int q0, int t,
+struct DkdvRegs {
+  f16x8 q[2], dO[2];
+  float lse, dsum, pad;
+};
+
+// Registers of one step (thread tc of the 256 consumers): rows of the fp16
+// copies (in range up to s_pad, so no test), lse / D of the step's queries
+// through resources that end at row S - 1 (past it: lse +inf, so P = 0).
+__device__ __forceinline__ void dkdv_load(const AttnBwdArgs& a, int b, int h, int q0, int tc,
                                           DkdvRegs& r) {
   const Dims& dm = a.dm;
   const int S = a.S;
-  const bf16* qb = reinterpret_cast<const bf16*>(a.q) + ((long)(b * dm.Hq + h) * S) * D;
-  const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + (long)b * S * dm.nq + h * D;
-  const f16* qtb = reinterpret_cast<const f16*>(a.qT) + ((long)(b * dm.Hq + h) * D) * a.s_pad;
-  const f16* dtb = reinterpret_cast<const f16*>(a.dOT) + ((long)(b * dm.Hq + h) * D) * a.s_pad;
-  const __amdgpu_buffer_rsrc_t qrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)qb, 0, S * D * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t drs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)dob, 0, ((S - 1) * dm.nq + D) * 2, 0x00020000);
+  const long hrow = (long)(b * dm.Hq + h);
+  const __amdgpu_buffer_rsrc_t qrs = rows16(a.q16, hrow * a.s_pad, a.s_pad);
+  const __amdgpu_buffer_rsrc_t drs = rows16(a.do16, hrow * a.s_pad, a.s_pad);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int f = t + 256 * i;
-    const int row = f >> 4, ch = (f & 15) * 8;           // natural: 32 rows x 16 chunks
-    const int q = q0 + row;
-    r.qn[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, (q * D + ch) * 2, 0, 0));
-    r.don[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(drs, (q * dm.nq + ch) * 2, 0, 0));
-    const int c = f >> 2, col = (f & 3) * 8;             // transposed: 128 rows x 4 chunks
-    r.qt[i] = *reinterpret_cast<const f16x8*>(qtb + (long)c * a.s_pad + q0 + col);
-    r.dot[i] = *reinterpret_cast<const f16x8*>(dtb + (long)c * a.s_pad + q0 + col);
-  }
-  // every thread loads query q0 + t % 32 (the stage stores the 32 values from
-  // all waves: the same value to the same address)
-  const int q = q0 + (t & (TB - 1));
-  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.lse + (long)(b * dm.Hq + h) * S), 0, S * 4, 0x00020000);
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.Dsum + (long)(b * dm.Hq + h) * S), 0, S * 4, 0x00020000);
-  const float lv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, q * 4, 0, 0));
-  r.dsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, q * 4, 0, 0));
-  r.lse2 = fmaf(lv, kLog2e, q < S ? 0.0f : INFINITY);
-}
-
-__device__ __forceinline__ void dkdv_store(DkdvStage& st, int t, const DkdvRegs& r) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int f = t + 256 * i;
+    const int f = tc + 256 * i;
     const int row = f >> 4, ch = (f & 15) * 8;
-    *reinterpret_cast<bf16x8*>(st.qn + row * NLD + ch) = r.qn[i];
-    *reinterpret_cast<bf16x8*>(st.don + row * NLD + ch) = r.don[i];
-    const int c = f >> 2, col = (f & 3) * 8;
-    *reinterpret_cast<f16x8*>(st.qt + c * TLD + col) = r.qt[i];
-    *reinterpret_cast<f16x8*>(st.dot + c * TLD + col) = r.dot[i];
+    r.q[i] = load16(qrs, (q0 + row) * D + ch);
+    r.dO[i] = load16(drs, (q0 + row) * D + ch);
   }
-  st.lse2[t & (TB - 1)] = r.lse2;
-  st.dsum[t & (TB - 1)] = r.dsum;
+  const int q = q0 + (tc & (TB - 1));
+  const __amdgpu_buffer_rsrc_t lrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.lse + hrow * S), 0, S * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.Dsum + hrow * S), 0, S * 4, 0x00020000);
+  r.lse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, q * 4, 0, 0));
+  r.dsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, q * 4, 0, 0));
+  r.pad = q < S ? 0.0f : INFINITY;
 }
 
-// S = Q K^T and dP = dO V^T of one step: the stage's Q / dO rows (A, read with
-// the permuted row so that P / dS come out as 8 consecutive queries per lane)
-// times the wave's K / V rows held in registers (B).
-// S starts from `sinit` (0, or -inf where a key follows a query: the causal
-// mask, so that exp2 gives P = 0 there without a per-element test).
-__device__ __forceinline__ void dkdv_sdp(const DkdvStage& st, const bf16x8 (&kf)[8],
-                                         const bf16x8 (&vf)[8], int prow, int hi,
-                                         const f32x16& sinit, f32x16& sacc, f32x16& pacc) {
-  sacc = sinit;
+__device__ __forceinline__ void dkdv_store(DkdvStage& st, int tc, const DkdvRegs& r) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) pacc[r] = 0.0f;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(st.qn + prow * NLD + ks * 16 + hi * 8);
-    const bf16x8 da = *reinterpret_cast<const bf16x8*>(st.don + prow * NLD + ks * 16 + hi * 8);
-    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sacc, 0, 0, 0);
-    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], pacc, 0, 0, 0);
+  for (int i = 0; i < 2; ++i) {
+    const int f = tc + 256 * i;
+    const int row = f >> 4, ch = f & 15;
+    *reinterpret_cast<f16x8*>(st.q + tile_off(row, ch)) = r.q[i];
+    *reinterpret_cast<f16x8*>(st.dO + tile_off(row, ch)) = r.dO[i];
   }
+  // every consumer wave stores the same 32 values (query tc % 32)
+  st.lse2[tc & (TB - 1)] = fmaf(r.lse, kLog2e, r.pad);
+  st.dsum[tc & (TB - 1)] = r.dsum;
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_kernel(AttnBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) DkdvStage stg[3];
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) DkdvSmem sm;
   const Dims& dm = a.dm;
   const int S = a.S, G = dm.G;
-  // two work-groups per key block, each taking half of its query blocks (the
-  // first half holds the diagonal); low blocks = most work, dispatched first
   const int part = blockIdx.x & 1;
   const int k0 = (blockIdx.x >> 1) * 128, g = blockIdx.y, b = blockIdx.z;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int pair = wave & 3;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + pair * 32;
   const int my_key = kw0 + l32;
-  const float c1 = kLog2e / sqrtf((float)D);
 
-  // B operands for S = Q K^T and dP = dO V^T: lane (key l32, hi) holds channels
-  // 16 ks + 8 hi + 0..7 of its key's K'' and V' rows.
-  bf16x8 kf[8], vf[8];
-  {
-    const bf16* kb = reinterpret_cast<const bf16*>(a.k) + ((long)(b * dm.Hkv + g) * S) * D;
-    const bf16* vb = reinterpret_cast<const bf16*>(a.v) + ((long)(b * dm.Hkv + g) * S) * D;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      kf[ks] = my_key < S ? *reinterpret_cast<const bf16x8*>(kb + (long)my_key * D + ks * 16 + hi * 8)
-                          : zero8();
-      vf[ks] = my_key < S ? *reinterpret_cast<const bf16x8*>(vb + (long)my_key * D + ks * 16 + hi * 8)
-                          : zero8();
-    }
-  }
-  f32x16 dk[4], dv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.0f;
-
-  // steps: (head hh of the group, query block) for this part's query blocks
-  const int nqb_all = (S + TB - 1) / TB - k0 / TB;
+  // Steps: (head, query block), head-major, query blocks in descending order.
+  const int qb_last = (S + TB - 1) / TB - 1;
+  const int nqb_all = qb_last + 1 - k0 / TB;
+  const bool split_heads = (G & 1) == 0;
   const int nfirst = (nqb_all + 1) / 2;
-  const int qb0 = k0 / TB + (part ? nfirst : 0);
-  const int nqb = part ? nqb_all - nfirst : nfirst;
-  const int nsteps = G * nqb;
-  const int prow = perm_row(l32);
-  // Steps run head-major: step s = (head s / nqb, query block s % nqb).  The
-  // current step's block and the loaded step's (head, block) advance by
-  // counters (a division per step would cost ~40 scalar instructions in every
-  // wave); the loaded step stops at the last one, so the pipeline's loads past
-  // the end repeat it into a stage nobody reads again.
-  int cur_qi = 0;                                   // block index of step s
-  int ld_s = min(3, nsteps - 1);                    // step loaded next (s + 3, clamped)
-  int ld_h = ld_s / max(nqb, 1), ld_qi = ld_s - ld_h * nqb;
-  auto advance_load = [&]() {
-    if (ld_s < nsteps - 1) {
-      ++ld_s;
-      if (++ld_qi == nqb) {
-        ld_qi = 0;
-        ++ld_h;
+  const int hbase = g * G + (split_heads ? part * (G / 2) : 0);
+  const int nh = split_heads ? G / 2 : G;
+  const int qtop = split_heads || part ? qb_last : k0 / TB + nfirst - 1;
+  const int nqb = split_heads ? nqb_all : (part ? nqb_all - nfirst : nfirst);
+  const int nsteps = nh * nqb;
+  const long kvrow = (long)(b * dm.Hkv + g);
+  int to[2];
+  t_offsets(lane, to);
+  // D layout of dK / dV: lane holds channel nb*32 + l32, key rows 8 (r/4) + 4 hi + r%4
+
+  if (wave < 4) {
+    // ---------------- producer: S, dP, softmax, dS, dK
+    const float c1 = kLog2e / sqrtf((float)D);
+    // B operands for S = Q K^T and dP = dO V^T: lane (key l32, hi) holds
+    // channels 16 ks + 8 hi + 0..7 of its key's K'' and V' rows (fp16 copies;
+    // rows past s_pad read as zero).
+    f16x8 kf[8], vf[8];
+    {
+      const __amdgpu_buffer_rsrc_t krs = rows16(a.k16, kvrow * a.s_pad, a.s_pad);
+      const __amdgpu_buffer_rsrc_t vrs = rows16(a.v16, kvrow * a.s_pad, a.s_pad);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        kf[ks] = load16(krs, my_key * D + ks * 16 + hi * 8);
+        vf[ks] = load16(vrs, my_key * D + ks * 16 + hi * 8);
       }
     }
-  };
-
-  // Software pipeline over three LDS stages (step s in stage s % 3).  Iteration
-  // s computes S and dP of step s + 1 and the softmax of step s in one block
-  // (the MFMAs run while the vector ALU exponentiates), then dV and dK of step
-  // s; it stores the registers of step s + 2 into the stage step s - 1 used and
-  // loads step s + 3 into registers.  A barrier per step waits only for LDS
-  // operations, so the global loads stay in flight across it.  Steps whose
-  // queries all precede the wave's keys are computed like the others: their P
-  // is exactly zero.
-  if (nsteps > 0) {
-    DkdvRegs pre;
-    // steps 0, 1, 2 (clamped): the few divisions happen once
-    for (int i = 0; i < 3; ++i) {
-      const int si = min(i, nsteps - 1), hi_ = si / nqb;
-      dkdv_load(a, b, g * G + hi_, (qb0 + si - hi_ * nqb) * TB, t, pre);
-      if (i < 2) dkdv_store(stg[i], t, pre);
-    }
-    __syncthreads();
-    // initial S of a step: -inf where the wave's key follows the query (only
-    // the steps whose queries reach below the wave's last key have any)
-    // lane (key l32, hi): register r is query q0 + 16 (r / 8) + 8 hi + r % 8
-    auto s_init = [&](int q0n, f32x16& si) {
-      if (q0n < kw0 + 31) {
+    f32x16 dk[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          si[r] = my_key > q0n + 16 * (r >> 3) + 8 * hi + (r & 7) ? -INFINITY : 0.0f;
-      } else {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) si[r] = 0.0f;
-      }
-    };
-    f32x16 sacc, pacc, sinit;
-    s_init(qb0 * TB, sinit);
-    dkdv_sdp(stg[0], kf, vf, prow, hi, sinit, sacc, pacc);
-
-    for (int s = 0; s < nsteps; ++s) {
-      const DkdvStage& st = stg[s % 3];
-      const int q0 = (qb0 + cur_qi) * TB;
-      if (++cur_qi == nqb) cur_qi = 0;
-      dkdv_store(stg[(s + 2) % 3], t, pre);
-      dkdv_load(a, b, g * G + ld_h, (qb0 + ld_qi) * TB, t, pre);
-      advance_load();
-      f32x16 sn, pn;
-      s_init((qb0 + cur_qi) * TB, sinit);           // step s + 1's block (cur_qi has advanced)
-      dkdv_sdp(stg[(s + 1) % 3], kf, vf, prow, hi, sinit, sn, pn);
-      // lane (key l32, hi): register r is query q0 + 16 (r / 8) + 8 hi + r % 8
-      f16x8 pf[2], sf[2];
+      for (int r = 0; r < 16; ++r) dk[i][r] = 0.0f;
+    if (nsteps > 0) {
+      int ao[2];
+      a_offsets(perm_row(l32), hi, ao);
+      int cur_qi = 0;                              // query block index of step s
+      lds_barrier();                               // the consumers have staged step 0
+      for (int s = 0; s < nsteps; ++s) {
+        const DkdvStage& st = sm.stg[s % 3];
+        const int q0 = (qtop - cur_qi) * TB;
+        cur_qi = cur_qi + 1 == nqb ? 0 : cur_qi + 1;
+        f16x8 qa[8], da[8];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int qi = 16 * half + 8 * hi;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(st.lse2 + qi);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(st.lse2 + qi + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(st.dsum + qi);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(st.dsum + qi + 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * half + e;
-          const float lse2 = e < 4 ? l0[e] : l1[e - 4];
-          const float dsm = e < 4 ? d0[e] : d1[e - 4];
-
-          // masked pairs have S = -inf and queries past S lse2 = +inf: P = 0
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c1, -lse2));
-          pf[half][e] = (f16)p;
-          sf[half][e] = (f16)(p * (pacc[r] - dsm));
+        for (int ks = 0; ks < 8; ++ks) {
+          qa[ks] = read_a(st.q, ao, ks);
+          da[ks] = read_a(st.dO, ao, ks);
         }
-      }
-      // dV += P^T dO, dK += dS^T Q: 4 channel blocks x 2 steps of 16 queries
+        // S starts at -inf where the key follows the query (the causal mask;
+        // only steps whose queries reach below the wave's last key have such
+        // pairs), so that exp2 gives P = 0 there without a per-element test.
+        // lane (key l32, hi): register r is query q0 + 16 (r / 8) + 8 hi + r % 8
+        f32x16 sacc, pacc;
+        if (q0 < kw0 + 31) {
+          const int dlt = my_key - q0 - 8 * hi;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+          for (int r = 0; r < 16; ++r) sacc[r] = dlt > 16 * (r >> 3) + (r & 7) ? -INFINITY : 0.0f;
+        } else {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int c = nb * 32 + l32;
-          const f16x8 db = *reinterpret_cast<const f16x8*>(st.dot + c * TLD + ks * 16 + hi * 8);
-          const f16x8 qbv = *reinterpret_cast<const f16x8*>(st.qt + c * TLD + ks * 16 + hi * 8);
-          dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pf[ks], db, dv[nb], 0, 0, 0);
-          dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sf[ks], qbv, dk[nb], 0, 0, 0);
+          for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
         }
-      sacc = sn;
-      pacc = pn;
-      __builtin_amdgcn_s_waitcnt(0xC07F);      // this wave's LDS reads and stores are done
-      __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pacc[r] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[ks], kf[ks], sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[ks], vf[ks], pacc, 0, 0, 0);
+        }
+        f16x8 pf[2], sf[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int qi = 16 * half + 8 * hi;
+          const f32x4 l0 = *reinterpret_cast<const f32x4*>(st.lse2 + qi);
+          const f32x4 l1 = *reinterpret_cast<const f32x4*>(st.lse2 + qi + 4);
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(st.dsum + qi);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(st.dsum + qi + 4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * half + e;
+            const float lse2 = e < 4 ? l0[e] : l1[e - 4];
+            const float dsm = e < 4 ? d0[e] : d1[e - 4];
+            // masked pairs have S = -inf and queries past S lse2 = +inf: P = 0
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c1, -lse2));
+            pf[half][e] = (f16)p;
+            sf[half][e] = (f16)(p * (pacc[r] - dsm));
+          }
+        }
+        f16* pw = sm.pbuf[s & 1][pair] + lane * 8;
+        *reinterpret_cast<f16x8*>(pw) = pf[0];
+        *reinterpret_cast<f16x8*>(pw + 512) = pf[1];
+        // dK += dS^T Q: 4 channel blocks x 2 steps of 16 queries, Q^T read
+        // transposed from the Q tile
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sf[ks], read_t(st.q, to, ks, nb), dk[nb],
+                                                            0, 0, 0);
+        lds_barrier();
+      }
+      lds_barrier();                               // the consumers' last step
     }
+    const float inv = 1.0f / sqrtf((float)D);
+    float* dkb = (part ? a.dk2 : a.dk) + kvrow * S * D;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (key < S) dkb[(long)key * D + nb * 32 + l32] = dk[nb][r] * inv;
+      }
+  } else {
+    // ---------------- consumer: staging and dV += P^T dO, one step behind
+    const int tc = t - 256;
+    f32x16 dv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dv[i][r] = 0.0f;
+    if (nsteps > 0) {
+      // steps are loaded in order; the loaded step stops at the last one, so
+      // loads past the end repeat it into registers nobody stores
+      int ld_s = 0, ld_h = 0, ld_qi = 0;
+      auto load_next = [&](DkdvRegs& r) {
+        dkdv_load(a, b, hbase + ld_h, (qtop - ld_qi) * TB, tc, r);
+        const bool more = ld_s < nsteps - 1;
+        const bool wrap = more && ld_qi + 1 == nqb;
+        ld_s += more ? 1 : 0;
+        ld_qi = wrap ? 0 : ld_qi + (more ? 1 : 0);
+        ld_h += wrap ? 1 : 0;
+      };
+      DkdvRegs r0, r1;                             // step j is staged through r(j % 2)
+      load_next(r0);
+      load_next(r1);
+      dkdv_store(sm.stg[0], tc, r0);
+      load_next(r0);
+      lds_barrier();
+      // iteration s: dV of step s - 1; stage step s + 1 and load step s + 3
+      auto iter = [&](int s, DkdvRegs& rs) {
+        if (s >= 1) {
+          const DkdvStage& sp = sm.stg[(s - 1) % 3];
+          const f16* pr = sm.pbuf[(s - 1) & 1][pair] + lane * 8;
+          f16x8 pa[2];
+          pa[0] = *reinterpret_cast<const f16x8*>(pr);
+          pa[1] = *reinterpret_cast<const f16x8*>(pr + 512);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+              dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], read_t(sp.dO, to, ks, nb),
+                                                              dv[nb], 0, 0, 0);
+        }
+        if (s + 1 < nsteps) {
+          dkdv_store(sm.stg[(s + 1) % 3], tc, rs);
+          load_next(rs);
+        }
+        lds_barrier();
+      };
+      for (int s = 0; s <= nsteps; s += 2) {
+        iter(s, r1);                               // stores step s + 1 (in r1), loads s + 3
+        if (s + 1 <= nsteps) iter(s + 1, r0);
+      }
+    }
+    float* dvb = (part ? a.dv2 : a.dv) + kvrow * S * D;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (key < S) dvb[(long)key * D + nb * 32 + l32] = dv[nb][r];
+      }
   }
-
-  // D layout: lane holds channel nb*32 + l32, key rows 8 (r/4) + 4 hi + r%4
-  const float inv = 1.0f / sqrtf((float)D);
-  float* dkb = (part ? a.dk2 : a.dk) + ((long)(b * dm.Hkv + g) * S) * D;
-  float* dvb = (part ? a.dv2 : a.dv) + ((long)(b * dm.Hkv + g) * S) * D;
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (key < S) {
-        dkb[(long)key * D + nb * 32 + l32] = dk[nb][r] * inv;
-        dvb[(long)key * D + nb * 32 + l32] = dv[nb][r];
-      }
-    }
 }
 
 // dk += dk2, dv += dv2: the two halves of every key block, in a fixed order.
@@ -392,36 +437,25 @@ __global__ __launch_bounds__(256) void bwd_dkdv_sum_kernel(float* dk, const floa
 
 // ------------------------------------------------------------------ dq
 struct DqStage {
-  bf16 kn[TB * NLD];     // K rows   [32 keys][128 c]
-  bf16 vn[TB * NLD];     // V rows   [32 keys][128 c]
-  f16 kt[D * TLD];       // K^T      [128 c][32 keys], fp16
+  f16 k[TILE];           // K'' rows of the step's 32 keys
+  f16 v[TILE];           // V' rows
 };
 
 struct DqRegs {
-  bf16x8 kn[2], vn[2];
-  f16x8 kt[2];
+  f16x8 k[2], v[2];
 };
 
 __device__ __forceinline__ void dq_load(const AttnBwdArgs& a, int b, int g, int j0, int t,
                                         DqRegs& r) {
-  const Dims& dm = a.dm;
-  const int S = a.S;
-  const bf16* kb = reinterpret_cast<const bf16*>(a.k) + ((long)(b * dm.Hkv + g) * S) * D;
-  const bf16* vb = reinterpret_cast<const bf16*>(a.v) + ((long)(b * dm.Hkv + g) * S) * D;
-  const f16* ktb = reinterpret_cast<const f16*>(a.kT) + ((long)(b * dm.Hkv + g) * D) * a.s_pad;
-  // K and V rows through resources that end at row S - 1: rows past it read as
-  // zero without a branch, so the six loads of a thread issue back to back
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, S * D * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, S * D * 2, 0x00020000);
+  const long kvrow = (long)(b * a.dm.Hkv + g) * a.s_pad;
+  const __amdgpu_buffer_rsrc_t krs = rows16(a.k16, kvrow, a.s_pad);
+  const __amdgpu_buffer_rsrc_t vrs = rows16(a.v16, kvrow, a.s_pad);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int f = t + 256 * i;
     const int row = f >> 4, ch = (f & 15) * 8;
-    const int j = j0 + row;
-    r.kn[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, (j * D + ch) * 2, 0, 0));
-    r.vn[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, (j * D + ch) * 2, 0, 0));
-    const int c = f >> 2, col = (f & 3) * 8;
-    r.kt[i] = *reinterpret_cast<const f16x8*>(ktb + (long)c * a.s_pad + j0 + col);
+    r.k[i] = load16(krs, (j0 + row) * D + ch);
+    r.v[i] = load16(vrs, (j0 + row) * D + ch);
   }
 }
 
@@ -429,11 +463,9 @@ __device__ __forceinline__ void dq_store(DqStage& st, int t, const DqRegs& r) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int f = t + 256 * i;
-    const int row = f >> 4, ch = (f & 15) * 8;
-    *reinterpret_cast<bf16x8*>(st.kn + row * NLD + ch) = r.kn[i];
-    *reinterpret_cast<bf16x8*>(st.vn + row * NLD + ch) = r.vn[i];
-    const int c = f >> 2, col = (f & 3) * 8;
-    *reinterpret_cast<f16x8*>(st.kt + c * TLD + col) = r.kt[i];
+    const int row = f >> 4, ch = f & 15;
+    *reinterpret_cast<f16x8*>(st.k + tile_off(row, ch)) = r.k[i];
+    *reinterpret_cast<f16x8*>(st.v + tile_off(row, ch)) = r.v[i];
   }
 }
 
@@ -447,34 +479,28 @@ void bwd_dq_kernel(AttnBwdArgs a) {
   const int qb = nqb - 1 - (int)(blockIdx.x / per);          // heaviest blocks first
   const int h = (blockIdx.x % per) % dm.Hq, b = (blockIdx.x % per) / dm.Hq;
   const int g = h / dm.G;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int q0 = qb * 128;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + l32;
   const float c1 = kLog2e / sqrtf((float)D);
+  const long hrow = (long)(b * dm.Hq + h);
 
   // B operands for S^T = K Q^T and dP^T = V dO^T: lane (query l32, hi) holds
-  // channels 16 ks + 8 hi + 0..7 of its query's Q'' and dO rows.
-  bf16x8 qf[8], df[8];
+  // channels 16 ks + 8 hi + 0..7 of its query's Q'' and dO rows (fp16 copies).
+  f16x8 qf[8], df[8];
   {
-    const bf16* qbp = reinterpret_cast<const bf16*>(a.q) + ((long)(b * dm.Hq + h) * S) * D;
-    const bf16* dob = reinterpret_cast<const bf16*>(a.dO) + (long)b * S * dm.nq + h * D;
-    // rows past S read as zero through the resources' range check
-    const __amdgpu_buffer_rsrc_t qrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)qbp, 0, S * D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t drs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)dob, 0, ((S - 1) * dm.nq + D) * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t qrs = rows16(a.q16, hrow * a.s_pad, a.s_pad);
+    const __amdgpu_buffer_rsrc_t drs = rows16(a.do16, hrow * a.s_pad, a.s_pad);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                              qrs, (my_q * D + ks * 16 + hi * 8) * 2, 0, 0));
-      df[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                              drs, (my_q * dm.nq + ks * 16 + hi * 8) * 2, 0, 0));
+      qf[ks] = load16(qrs, my_q * D + ks * 16 + hi * 8);
+      df[ks] = load16(drs, my_q * D + ks * 16 + hi * 8);
     }
   }
-  const float lse2 = my_q < S ? a.lse[(long)(b * dm.Hq + h) * S + my_q] * kLog2e : INFINITY;
-  const float dsm = my_q < S ? a.Dsum[(long)(b * dm.Hq + h) * S + my_q] : 0.0f;
+  const float lse2 = my_q < S ? a.lse[hrow * S + my_q] * kLog2e : INFINITY;
+  const float dsm = my_q < S ? a.Dsum[hrow * S + my_q] : 0.0f;
   f32x16 dq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -483,7 +509,9 @@ void bwd_dq_kernel(AttnBwdArgs a) {
 
   const int q_last = min(S, q0 + 128) - 1;
   const int nsteps = q_last / TB + 1;
-  const int prow = perm_row(l32);
+  int ao[2], to[2];
+  a_offsets(perm_row(l32), hi, ao);
+  t_offsets(lane, to);
   DqRegs pre;
   dq_load(a, b, g, 0, t, pre);
   dq_store(stg[0], t, pre);
@@ -511,28 +539,28 @@ void bwd_dq_kernel(AttnBwdArgs a) {
       }
       // K and V fragments through a ring of 4: the reads run 4 k slices ahead
       // of the MFMAs instead of one read-wait-MFMA per slice
-      bf16x8 ka[4], va[4];
+      f16x8 ka[4], va[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        ka[ks] = *reinterpret_cast<const bf16x8*>(st.kn + prow * NLD + ks * 16 + hi * 8);
-        va[ks] = *reinterpret_cast<const bf16x8*>(st.vn + prow * NLD + ks * 16 + hi * 8);
+        ka[ks] = read_a(st.k, ao, ks);
+        va[ks] = read_a(st.v, ao, ks);
       }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 3], qf[ks], sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks & 3], df[ks], pacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks & 3], qf[ks], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[ks & 3], df[ks], pacc, 0, 0, 0);
         if (ks + 4 < 8) {
-          ka[ks & 3] = *reinterpret_cast<const bf16x8*>(st.kn + prow * NLD + (ks + 4) * 16 + hi * 8);
-          va[ks & 3] = *reinterpret_cast<const bf16x8*>(st.vn + prow * NLD + (ks + 4) * 16 + hi * 8);
+          ka[ks & 3] = read_a(st.k, ao, ks + 4);
+          va[ks & 3] = read_a(st.v, ao, ks + 4);
         }
       }
-      // K^T fragments of dQ += dS K, read before the softmax arithmetic covers them
+      // K^T fragments of dQ += dS K, read (transposed) before the softmax
+      // arithmetic covers them
       f16x8 kt[2][4];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          kt[ks][nb] = *reinterpret_cast<const f16x8*>(st.kt + (nb * 32 + l32) * TLD + ks * 16 + hi * 8);
+        for (int nb = 0; nb < 4; ++nb) kt[ks][nb] = read_t(st.k, to, ks, nb);
       // lane (query l32, hi): register r is key j0 + 16 (r / 8) + 8 hi + r % 8
       f16x8 sf[2];
 #pragma unroll
@@ -559,7 +587,7 @@ void bwd_dq_kernel(AttnBwdArgs a) {
 
   // D layout: lane holds channel nb*32 + l32, query rows 8 (r/4) + 4 hi + r%4
   const float inv = 1.0f / sqrtf((float)D);
-  float* dqb = a.dq + ((long)(b * dm.Hq + h) * S) * D;
+  float* dqb = a.dq + hrow * S * D;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -577,18 +605,18 @@ size_t attn_bwd_transpose_bytes(const Dims& dm, int B, int S) {
   if (!mfma_bwd(dm)) return 0;
   const size_t sp = (size_t)(S + 63) / 64 * 64;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return al((size_t)B * dm.nq * sp * 2) + al((size_t)B * dm.nk * sp * 2) +
-         al((size_t)B * dm.nq * sp * 2) + 2 * al((size_t)B * S * dm.nk * 4);
+  return 2 * al((size_t)B * dm.nq * sp * 2) + 2 * al((size_t)B * dm.nk * sp * 2) +
+         2 * al((size_t)B * S * dm.nk * 4);
 }
 
 hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) {
   const Dims& dm = a.dm;
-  if (!mfma_bwd(dm) || !a.qT || !a.kT || !a.dOT || a.s_pad < a.S || a.s_pad % 64 != 0)
+  if (!mfma_bwd(dm) || !a.q16 || !a.k16 || !a.v16 || !a.do16 || a.s_pad < a.S ||
+      a.s_pad % 64 != 0 || !a.dk2 || !a.dv2)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(a.s_pad / 64, dm.Hq + dm.Hkv, a.B), dim3(256), 0, s,
                      a);
-  if (!a.dk2 || !a.dv2) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(2 * ((a.S + 127) / 128), dm.Hkv, a.B), dim3(256), 0, s,
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(2 * ((a.S + 127) / 128), dm.Hkv, a.B), dim3(512), 0, s,
                      a);
   if (!a.sum_by_consumer) {
     const long n4 = (long)a.B * dm.Hkv * a.S * D / 4;

@@ -189,11 +189,12 @@ struct AttnBwdArgs {
   float* dq;         // dQ'' [B,Hq,S,d] fp32
   float* dk;         // dK'' [B,Hkv,S,d] fp32
   float* dv;         // dV'  [B,Hkv,S,d] fp32
-  // MFMA path workspace (bf16 storage, d = 128): fp16 transposed copies, rows
-  // padded to s_pad
-  void* qT;          // Q''^T [B,Hq,d,s_pad] fp16
-  void* kT;          // K''^T [B,Hkv,d,s_pad]
-  void* dOT;         // dO^T  [B,Hq,d,s_pad]
+  // MFMA path workspace (bf16 storage, d = 128): fp16 copies as head-major
+  // rows, s_pad rows per head (zero from row S)
+  void* q16;         // Q'' [B,Hq,s_pad,d] fp16
+  void* k16;         // K'' [B,Hkv,s_pad,d]
+  void* v16;         // V'  [B,Hkv,s_pad,d]
+  void* do16;        // dO  [B,Hq,s_pad,d]
   int s_pad;         // S rounded up to a multiple of 64
   // dK / dV of the second half of each key block's query range (fp32, same
   // layout as dk / dv), added into dk / dv before the kernels return, unless
@@ -206,7 +207,7 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 // True when launch_attn_bwd takes the MFMA kernels (bf16, d = 128), which
 // produce the dk2 / dv2 second-half partials.
 bool attn_bwd_mfma_supported(const Dims& dm);
-// Bytes of the MFMA attention backward's workspace: the transposed copies and
+// Bytes of the MFMA attention backward's workspace: the fp16 copies and
 // the second-half dK / dV partials (0 when the config takes the generic path).
 size_t attn_bwd_transpose_bytes(const Dims& dm, int B, int S);
 
