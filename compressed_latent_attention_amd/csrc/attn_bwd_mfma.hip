@@ -389,8 +389,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
       dkdv_store(sm.stg[0], tc, r0);
       load_next(r0);
       lds_barrier();
-      // iteration s: dV of step s - 1; stage step s + 1 and load step s + 3
+      // iteration s: stage step s + 1 and load step s + 3, then dV of step
+      // s - 1 (its MFMAs then run while the producer's softmax does)
       auto iter = [&](int s, DkdvRegs& rs) {
+        if (s + 1 < nsteps) {
+          dkdv_store(sm.stg[(s + 1) % 3], tc, rs);
+          load_next(rs);
+        }
         if (s >= 1) {
           const DkdvStage& sp = sm.stg[(s - 1) % 3];
           const f16* pr = sm.pbuf[(s - 1) & 1][pair] + lane * 8;
@@ -403,10 +408,6 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
             for (int nb = 0; nb < 4; ++nb)
               dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], read_t(sp.dO, to, ks, nb),
                                                               dv[nb], 0, 0, 0);
-        }
-        if (s + 1 < nsteps) {
-          dkdv_store(sm.stg[(s + 1) % 3], tc, rs);
-          load_next(rs);
         }
         lds_barrier();
       };
