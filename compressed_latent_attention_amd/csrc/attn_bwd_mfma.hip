@@ -19,10 +19,11 @@
 //           of the group's heads, otherwise half of each head's query range;
 //           query blocks run in descending order, so the work-groups of a head
 //           read the same tile at about the same time;
-//   dq    — work-group = 128 queries of one head, 4 waves of 32 queries; loops
-//           over the key blocks (32 keys) up to the diagonal:
-//             S^T = K Q^T, dP^T = V dO^T (B = the wave's Q / dO rows held in
-//             registers), dQ += dS K.
+//   dq    — work-group = 128 queries of one head, 8 waves, looping over the key
+//           blocks (32 keys) up to the diagonal.  Producers (waves 0-3, 32
+//           queries each, Q and dO rows in registers) compute S^T = K Q^T,
+//           dP^T = V dO^T and dS; consumers stage the K / V tiles and add
+//           dQ += dS K one step behind.
 // Every product is a v_mfma_f32_32x32x16_f16 with fp32 accumulation.  The fp16
 // copies hold the stored bf16 values exactly while they lie in fp16's normal
 // range (|x| in [2^-14, 65504]; smaller gradients would need a loss scale); P
@@ -470,9 +471,17 @@ __device__ __forceinline__ void dq_store(DqStage& st, int t, const DqRegs& r) {
   }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_kernel(AttnBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) DqStage stg[2];
+// Producer / consumer split as in dkdv: waves 0-3 (producers, 32 queries
+// each, Q and dO rows in registers) compute S^T, dP^T and dS and leave dS in
+// LDS; waves 4-7 (consumers, same queries) stage the K / V tiles and add
+// dQ += dS K one step behind, with K^T read transposed from that step's tile.
+struct DqSmem {
+  DqStage stg[3];
+  f16 sbuf[2][4][2 * 64 * 8];    // dS of a step per producer: [parity][producer][ks][lane][8]
+};
+
+__global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) DqSmem sm;
   const Dims& dm = a.dm;
   const int S = a.S;
   const int nqb = (S + 127) / 128;
@@ -480,122 +489,136 @@ void bwd_dq_kernel(AttnBwdArgs a) {
   const int qb = nqb - 1 - (int)(blockIdx.x / per);          // heaviest blocks first
   const int h = (blockIdx.x % per) % dm.Hq, b = (blockIdx.x % per) / dm.Hq;
   const int g = h / dm.G;
-  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int pair = wave & 3;
   const int l32 = lane & 31, hi = lane >> 5;
   const int q0 = qb * 128;
-  const int qw0 = q0 + wave * 32;
+  const int qw0 = q0 + pair * 32;
   const int my_q = qw0 + l32;
-  const float c1 = kLog2e / sqrtf((float)D);
   const long hrow = (long)(b * dm.Hq + h);
-
-  // B operands for S^T = K Q^T and dP^T = V dO^T: lane (query l32, hi) holds
-  // channels 16 ks + 8 hi + 0..7 of its query's Q'' and dO rows (fp16 copies).
-  f16x8 qf[8], df[8];
-  {
-    const __amdgpu_buffer_rsrc_t qrs = rows16(a.q16, hrow * a.s_pad, a.s_pad);
-    const __amdgpu_buffer_rsrc_t drs = rows16(a.do16, hrow * a.s_pad, a.s_pad);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      qf[ks] = load16(qrs, my_q * D + ks * 16 + hi * 8);
-      df[ks] = load16(drs, my_q * D + ks * 16 + hi * 8);
-    }
-  }
-  const float lse2 = my_q < S ? a.lse[hrow * S + my_q] * kLog2e : INFINITY;
-  const float dsm = my_q < S ? a.Dsum[hrow * S + my_q] : 0.0f;
-  f32x16 dq[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dq[i][r] = 0.0f;
-
   const int q_last = min(S, q0 + 128) - 1;
   const int nsteps = q_last / TB + 1;
-  int ao[2], to[2];
-  a_offsets(perm_row(l32), hi, ao);
-  t_offsets(lane, to);
-  DqRegs pre;
-  dq_load(a, b, g, 0, t, pre);
-  dq_store(stg[0], t, pre);
-  if (nsteps > 1) dq_load(a, b, g, TB, t, pre);
-  __syncthreads();
 
-  for (int s = 0; s < nsteps; ++s) {
-    const DqStage& st = stg[s & 1];
-    const int j0 = s * TB;
-    if (j0 <= qw0 + 31) {                    // else every key follows every query of the wave
-      f32x16 sacc, pacc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pacc[r] = 0.0f;
-      // S^T starts at -inf where the key follows the lane's query (only the
-      // steps whose keys reach past the wave's first query have any), so exp2
-      // gives P = 0 there without a per-element test.  Lane (query l32, hi):
-      // register r is key j0 + 16 (r / 8) + 8 hi + r % 8.
-      if (j0 + 31 > qw0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sacc[r] = j0 + 16 * (r >> 3) + 8 * hi + (r & 7) > my_q ? -INFINITY : 0.0f;
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
-      }
-      // K and V fragments through a ring of 4: the reads run 4 k slices ahead
-      // of the MFMAs instead of one read-wait-MFMA per slice
-      f16x8 ka[4], va[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        ka[ks] = read_a(st.k, ao, ks);
-        va[ks] = read_a(st.v, ao, ks);
-      }
+  if (wave < 4) {
+    // ---------------- producer: S^T, dP^T, dS
+    const float c1 = kLog2e / sqrtf((float)D);
+    // B operands for S^T = K Q^T and dP^T = V dO^T: lane (query l32, hi) holds
+    // channels 16 ks + 8 hi + 0..7 of its query's Q'' and dO rows (fp16 copies).
+    f16x8 qf[8], df[8];
+    {
+      const __amdgpu_buffer_rsrc_t qrs = rows16(a.q16, hrow * a.s_pad, a.s_pad);
+      const __amdgpu_buffer_rsrc_t drs = rows16(a.do16, hrow * a.s_pad, a.s_pad);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks & 3], qf[ks], sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[ks & 3], df[ks], pacc, 0, 0, 0);
-        if (ks + 4 < 8) {
-          ka[ks & 3] = read_a(st.k, ao, ks + 4);
-          va[ks & 3] = read_a(st.v, ao, ks + 4);
-        }
+        qf[ks] = load16(qrs, my_q * D + ks * 16 + hi * 8);
+        df[ks] = load16(drs, my_q * D + ks * 16 + hi * 8);
       }
-      // K^T fragments of dQ += dS K, read (transposed) before the softmax
-      // arithmetic covers them
-      f16x8 kt[2][4];
+    }
+    const float lse2 = my_q < S ? a.lse[hrow * S + my_q] * kLog2e : INFINITY;
+    const float dsm = my_q < S ? a.Dsum[hrow * S + my_q] : 0.0f;
+    int ao[2];
+    a_offsets(perm_row(l32), hi, ao);
+    lds_barrier();                                 // the consumers have staged step 0
+    for (int s = 0; s < nsteps; ++s) {
+      const DqStage& st = sm.stg[s % 3];
+      const int j0 = s * TB;
+      if (j0 <= qw0 + 31) {                  // else every key follows every query of the wave
+        f32x16 sacc, pacc;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+        for (int r = 0; r < 16; ++r) pacc[r] = 0.0f;
+        // S^T starts at -inf where the key follows the lane's query (only the
+        // steps whose keys reach past the wave's first query have any), so
+        // exp2 gives P = 0 there without a per-element test.  Lane (query l32,
+        // hi): register r is key j0 + 16 (r / 8) + 8 hi + r % 8.
+        if (j0 + 31 > qw0) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) kt[ks][nb] = read_t(st.k, to, ks, nb);
-      // lane (query l32, hi): register r is key j0 + 16 (r / 8) + 8 hi + r % 8
-      f16x8 sf[2];
+          for (int r = 0; r < 16; ++r)
+            sacc[r] = j0 + 16 * (r >> 3) + 8 * hi + (r & 7) > my_q ? -INFINITY : 0.0f;
+        } else {
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * half + e;
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c1, -lse2));
-          sf[half][e] = (f16)(p * (pacc[r] - dsm));
+          for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
         }
-      // dQ += dS K: A = dS (lane = query row), B = K^T columns
+        f16x8 ka[8], va[8];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 8; ++ks) {
+          ka[ks] = read_a(st.k, ao, ks);
+          va[ks] = read_a(st.v, ao, ks);
+        }
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sf[ks], kt[ks][nb], dq[nb], 0, 0, 0);
+        for (int ks = 0; ks < 8; ++ks) {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks], qf[ks], sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[ks], df[ks], pacc, 0, 0, 0);
+        }
+        f16x8 sf[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * half + e;
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c1, -lse2));
+            sf[half][e] = (f16)(p * (pacc[r] - dsm));
+          }
+        f16* sw = sm.sbuf[s & 1][pair] + lane * 8;
+        *reinterpret_cast<f16x8*>(sw) = sf[0];
+        *reinterpret_cast<f16x8*>(sw + 512) = sf[1];
+      }
+      lds_barrier();
     }
-    if (s + 1 < nsteps) {
-      dq_store(stg[(s + 1) & 1], t, pre);
-      if (s + 2 < nsteps) dq_load(a, b, g, (s + 2) * TB, t, pre);
+    lds_barrier();                                 // the consumers' last step
+  } else {
+    // ---------------- consumer: staging and dQ += dS K, one step behind
+    const int tc = t - 256;
+    f32x16 dq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[i][r] = 0.0f;
+    int to[2];
+    t_offsets(lane, to);
+    DqRegs r0, r1;                                 // step j is staged through r(j % 2)
+    dq_load(a, b, g, 0, tc, r0);
+    dq_load(a, b, g, min(1, nsteps - 1) * TB, tc, r1);
+    dq_store(sm.stg[0], tc, r0);
+    dq_load(a, b, g, min(2, nsteps - 1) * TB, tc, r0);
+    lds_barrier();
+    // iteration s: stage step s + 1 and load step s + 3, then dQ of step s - 1
+    auto iter = [&](int s, DqRegs& rs) {
+      if (s + 1 < nsteps) {
+        dq_store(sm.stg[(s + 1) % 3], tc, rs);
+        dq_load(a, b, g, min(s + 3, nsteps - 1) * TB, tc, rs);
+      }
+      if (s >= 1 && (s - 1) * TB <= qw0 + 31) {
+        const DqStage& sp = sm.stg[(s - 1) % 3];
+        const f16* sr = sm.sbuf[(s - 1) & 1][pair] + lane * 8;
+        f16x8 sa[2];
+        sa[0] = *reinterpret_cast<const f16x8*>(sr);
+        sa[1] = *reinterpret_cast<const f16x8*>(sr + 512);
+        // dQ += dS K: A = dS (lane = query row), B = K^T read transposed
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[ks], read_t(sp.k, to, ks, nb), dq[nb],
+                                                            0, 0, 0);
+      }
+      lds_barrier();
+    };
+    for (int s = 0; s <= nsteps; s += 2) {
+      iter(s, r1);                                 // stores step s + 1 (in r1), loads s + 3
+      if (s + 1 <= nsteps) iter(s + 1, r0);
     }
-    __syncthreads();
+    // D layout: lane holds channel nb*32 + l32, query rows 8 (r/4) + 4 hi + r%4
+    const float inv = 1.0f / sqrtf((float)D);
+    float* dqb = a.dq + hrow * S * D;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = qw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (q < S) dqb[(long)q * D + nb * 32 + l32] = dq[nb][r] * inv;
+      }
   }
-
-  // D layout: lane holds channel nb*32 + l32, query rows 8 (r/4) + 4 hi + r%4
-  const float inv = 1.0f / sqrtf((float)D);
-  float* dqb = a.dq + hrow * S * D;
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int q = qw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (q < S) dqb[(long)q * D + nb * 32 + l32] = dq[nb][r] * inv;
-    }
 }
 
 }  // namespace
@@ -624,7 +647,7 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(bwd_dkdv_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
                        a.dk, a.dk2, a.dv, a.dv2, n4);
   }
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3(((a.S + 127) / 128) * dm.Hq * a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(((a.S + 127) / 128) * dm.Hq * a.B), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
