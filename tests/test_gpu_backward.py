@@ -34,6 +34,14 @@ CASES = [
              kind="backward"),
     Workload("bf16_bwd_g8_flags", B=1, S=150, E=1024, C=1, Hq=8, Hkv=1, flags=1 | 4 | 8, sv=40,
              seed=70, kind="backward"),
+    # three query heads per KV head: the attention backward splits each head's
+    # query range between the two work-groups of a key block (odd group size)
+    # and a separate kernel adds the second partial; ragged S
+    Workload("bf16_bwd_g3", B=1, S=97, E=768, C=1, Hq=6, Hkv=2, seed=71, kind="backward"),
+    # two heads per KV head over a longer ragged sequence: the work-groups of a
+    # key block take one head each, query blocks in descending order
+    Workload("bf16_bwd_s1000", B=1, S=1000, E=512, C=1, Hq=4, Hkv=2, kq=3, kk=2, seed=72,
+             kind="backward"),
     # large enough that the weight gradients run split over K (16 partial sums)
     # on the 256 x 256 kernel, and the attention backward spans 16 key blocks
     Workload("bf16_bwd_splitk", B=1, S=2048, E=1024, C=2, Hq=4, Hkv=2, seed=67,
