@@ -551,6 +551,26 @@ cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, cons
       gout.a = at; gout.lda = Mp; gout.b_ptr[0] = bt; gout.ldb = Mp; gout.K = Mp;
       return launch_gemm(gout, GemmLayout::NT, true, true, s);
     };
+    // The same product straight from the token-major operands a_tok [M x Mo]
+    // and b_tok [M x No] (K-major tiles, no transposed copies), split over K
+    // into the fp32 partials; false (nothing launched) when the shape does
+    // not suit the 256 x 256 kernel.
+    auto weight_grad_tn = [&](int Mo, int No, const void* a_tok, long lda, const void* b_tok,
+                              long ldb, GemmArgs gout, hipError_t* e) -> bool {
+      GemmArgs gg = gemm_nt(Mo, No, Mp, a_tok, lda, b_tok, ldb, gpart, No);
+      gg.k_valid = (int)M;
+      const int tiles = ((Mo + 255) / 256) * ((No + 255) / 256);
+      int ks = 1;
+      while (ks < kMaxSplit && tiles * ks < 256 && (Mp / 64) % (2 * ks) == 0) ks *= 2;
+      if (ks < 2) return false;
+      gg.ksplit = ks;
+      gg.c_split_stride = (long)Mo * No;
+      if (!launch_gemm_nt_big(gg, true, s, e, GemmLayout::TN)) return false;
+      if (*e != hipSuccess) return true;
+      float* outs[3] = {(float*)gout.c_ptr[0], (float*)gout.c_ptr[1], (float*)gout.c_ptr[2]};
+      *e = launch_splitk_reduce(gpart, ks, Mo, No, outs, gout.c_start, gout.c_nseg, gout.ldc, s);
+      return true;
+    };
 
     // dO = dY W_o ; dW_o = dY^T O
     if (nt) {
@@ -561,10 +581,12 @@ cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, cons
         return launch_gemm(g1, GemmLayout::NT, true, false, s);
       }));
       CCA_TRY_HIP(timed(h, "bwd_proj_up_dw", s, [&] {
-        hipError_t e = launch_transpose_bf16(dy, dm.E, M, dm.E, Mp, tA, Mp, s);
+        GemmArgs gout = gemm_nt(dm.E, dm.nq, Mp, nullptr, 0, nullptr, 0, g->dw_o, dm.nq);
+        hipError_t e = hipSuccess;
+        if (weight_grad_tn(dm.E, dm.nq, dy, dm.E, o, dm.nq, gout, &e)) return e;
+        e = launch_transpose_bf16(dy, dm.E, M, dm.E, Mp, tA, Mp, s);
         if (e == hipSuccess) e = launch_transpose_bf16(o, dm.nq, M, dm.nq, Mp, tB, Mp, s);
         if (e != hipSuccess) return e;
-        GemmArgs gout = gemm_nt(dm.E, dm.nq, Mp, nullptr, 0, nullptr, 0, g->dw_o, dm.nq);
         return weight_grad(dm.E, dm.nq, tA, tB, gout);
       }));
     } else {
@@ -627,7 +649,9 @@ cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, cons
         return launch_gemm(g3, GemmLayout::NT, true, false, s);
       }));
       CCA_TRY_HIP(timed(h, "bwd_proj_down_dw", s, [&] {
-        hipError_t e = launch_transpose_bf16(dqkv, dm.nqkv, M, dm.nqkv, Mp, tB, Mp, s);
+        hipError_t e = hipSuccess;
+        if (weight_grad_tn(dm.nqkv, dm.E, dqkv, dm.nqkv, x, dm.E, g4, &e)) return e;
+        e = launch_transpose_bf16(dqkv, dm.nqkv, M, dm.nqkv, Mp, tB, Mp, s);
         if (e == hipSuccess) e = launch_transpose_bf16(x, dm.E, M, dm.E, Mp, tA, Mp, s);
         if (e != hipSuccess) return e;
         return weight_grad(dm.nqkv, dm.E, tB, tA, g4);

@@ -57,6 +57,9 @@ struct GemmArgs {
   // c_ptr[0] + z * c_split_stride (one segment); 0 or 1 = no split
   int ksplit;
   long c_split_stride;
+  // K-major operands (256 x 256 kernel, TN layout): rows of A and B at or past
+  // k_valid read as zero, so K may be rounded up; 0 = K
+  int k_valid;
 };
 
 enum class GemmLayout { NT, NN, TN };   // (a_kc, b_kc) = (1,1), (1,0), (0,0)
@@ -67,7 +70,8 @@ hipError_t launch_gemm(const GemmArgs& g, GemmLayout layout, bool in_bf16, bool 
 
 // The 256 x 256 bf16 NT kernel when the shape suits it (see gemm_nt_mfma.hip);
 // false and nothing launched otherwise.
-bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError_t* err);
+bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError_t* err,
+                        GemmLayout layout = GemmLayout::NT);
 // Split-K NT GEMM for few rows of A (the decode step): partial tiles in an fp32
 // buffer of gemm_skinny_part_floats() floats, then a fixed-order sum; false when
 // the shape does not suit it (nothing launched).

@@ -20,7 +20,12 @@
 // 16-byte chunks XOR-swizzled by row, so that the fragment reads are free of
 // bank conflicts.
 // Rows past M or past the end of B's segment read as zero (buffer range
-// check), so ragged M and N need no special path.  Tiles are numbered so that
+// check), so ragged M and N need no special path.
+// TN layout (C = A^T B with A [K, M] and B [K, N] both row-major, as the weight
+// gradients dY^T O and dQKV^T x over the tokens): the tiles are copied as 64
+// k-rows of 256 elements (512 B) and the MFMA fragments, 8 consecutive k per
+// lane, are read transposed with ds_read_b64_tr_b16; k-rows at or past k_valid
+// read as zero.  Tiles are numbered so that
 // the tiles of one XCD (work-groups are dealt to the 8 XCDs round-robin) are
 // consecutive and share rows of A in that XCD's L2.
 #include "cca_internal.h"
@@ -76,10 +81,59 @@ __device__ __forceinline__ void dma_part(char* dst, const bf16* base, long ld, i
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16, src, 0, 0, 0);
 }
 
+// K-major operand tile: k-rows k0 .. k0 + 63, columns r0 .. r0 + 255 of a
+// row-major [K, R] matrix (row stride ld), as 64 LDS rows of 512 B with chunk c
+// (columns 8 c .. 8 c + 7) of row k at chunk c ^ 4 (k & 3): the 4 k-rows of a
+// transposing read then fall on distinct banks.  Block i of this wave's share:
+// 1 KB = two k-rows; lane L lands at row 2 blk + L / 32, chunk position L % 32.
+// The resource ends at row k_valid - 1: later rows read as zero, and columns
+// past R (next row's data, or zero past the end) only reach C rows / columns
+// that are never stored.
+template <int CB>
+__device__ __forceinline__ void dma_part_t(char* dst, const bf16* mat, long ld, int r0,
+                                           int kvalid, int k0, int wave, int lane, int i) {
+  const long rem = (long)(kvalid - k0) * ld - r0;
+  const int nrec = rem > 0 ? (int)(rem * 2) : 0;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(mat + (long)k0 * ld + r0), 0, nrec, 0x00020000);
+  const int blk = wave * CB + i;
+  const int kr = 2 * blk + (lane >> 5), pos = lane & 31;
+  const int src = (kr * (int)ld + 8 * (pos ^ (4 * (kr & 3)))) * 2;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16, src, 0, 0, 0);
+}
+
+template <int CB>
+__device__ __forceinline__ void dma_tile_t(char* dst, const bf16* mat, long ld, int r0, int kvalid,
+                                           int k0, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < CB; ++i) dma_part_t<CB>(dst, mat, ld, r0, kvalid, k0, wave, lane, i);
+}
+
+// Byte offset (within a stage's K-major tile, before + 8192 ks) of the
+// transposing reads that give lane (column col0 + l32, hi) the k-rows
+// 16 ks + 8 hi + 0..7: lane c of each 16-lane group addresses k-row
+// 8 hi + (c >> 2) (+ 4 for the second read) and columns col0 + 16 g + 4 (c & 3).
+__device__ __forceinline__ int t_frag_off(int lane, int col0) {
+  const int c = lane & 15, g = (lane >> 4) & 1, hi = lane >> 5;
+  const int kr = 8 * hi + (c >> 2);
+  const int col = col0 + 16 * g + 4 * (c & 3);
+  return kr * 512 + (((col >> 3) ^ (4 * (kr & 3))) << 4) + (col & 7) * 2;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ bf16x8 t_frag(const char* p) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 2048));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // NW = 4: waves of 128 x 128 (256 accumulator registers), one per SIMD;
 // NW = 8: waves of 128 x 64, two per SIMD, so one wave's MFMAs cover the
 // other's copy issue, fragment waits and barrier.
-template <typename OutT, int NW>
+// KT: both operands K-major (TN layout).
+template <typename OutT, int NW, bool KT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   constexpr int WN = NW / 2;                 // waves along N
@@ -113,8 +167,16 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   const int brows = min(seg_end - n0, TN);
 
   const int nk = klen / TK;
-  dma_tile<CB>(lds, abase, g.lda, arows, g.K, kbeg, wave, lane);
-  dma_tile<CB>(lds + A_BYTES, bbase, g.ldb, brows, g.K, kbeg, wave, lane);
+  const int kvalid = g.k_valid > 0 ? g.k_valid : g.K;
+  const bf16* amat = reinterpret_cast<const bf16*>(g.a);
+  const bf16* bmat = reinterpret_cast<const bf16*>(g.b_ptr[0]);
+  if constexpr (KT) {
+    dma_tile_t<CB>(lds, amat, g.lda, m0, kvalid, kbeg, wave, lane);
+    dma_tile_t<CB>(lds + A_BYTES, bmat, g.ldb, n0, kvalid, kbeg, wave, lane);
+  } else {
+    dma_tile<CB>(lds, abase, g.lda, arows, g.K, kbeg, wave, lane);
+    dma_tile<CB>(lds + A_BYTES, bbase, g.ldb, brows, g.K, kbeg, wave, lane);
+  }
 
   f32x16 acc[4][NJ];
 #pragma unroll
@@ -127,12 +189,26 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   // fragment addresses within a stage: row (wm*128 + i*32 + l32) of A and
   // (wn*128 + j*32 + l32) of B, chunk 2 ks + hi; the swizzle term depends on
   // l32 only, so the i / j blocks are immediate offsets.
+  // K-major tiles: per block i / j instead (t_frag_off), ks as + 8192 ks.
   int aoff[4], boff[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    aoff[ks] = sw(wm * 128 + l32, 2 * ks + hi);
-    boff[ks] = A_BYTES + sw(wn * (NJ * 32) + l32, 2 * ks + hi);
+  for (int u = 0; u < 4; ++u) {
+    if constexpr (KT) {
+      aoff[u] = t_frag_off(lane, wm * 128 + u * 32);
+      boff[u] = A_BYTES + t_frag_off(lane, wn * (NJ * 32) + (u % NJ) * 32);
+    } else {
+      aoff[u] = sw(wm * 128 + l32, 2 * u + hi);
+      boff[u] = A_BYTES + sw(wn * (NJ * 32) + l32, 2 * u + hi);
+    }
   }
+  auto frag_a = [&](const char* st, int ks, int i) -> bf16x8 {
+    if constexpr (KT) return t_frag(st + aoff[i] + 8192 * ks);
+    else return *reinterpret_cast<const bf16x8*>(st + aoff[ks] + i * 32 * 128);
+  };
+  auto frag_b = [&](const char* st, int ks, int j) -> bf16x8 {
+    if constexpr (KT) return t_frag(st + boff[j] + 8192 * ks);
+    else return *reinterpret_cast<const bf16x8*>(st + boff[ks] + j * 32 * 128);
+  };
   wait_dma();
   __syncthreads();
 
@@ -145,19 +221,17 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     const int knx = kbeg + min(kt + 1, nk - 1) * TK;
     bf16x8 fa[2][4], fb[2][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(st + aoff[0] + i * 32 * 128);
+    for (int i = 0; i < 4; ++i) fa[0][i] = frag_a(st, 0, i);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) fb[0][j] = *reinterpret_cast<const bf16x8*>(st + boff[0] + j * 32 * 128);
+    for (int j = 0; j < NJ; ++j) fb[0][j] = frag_b(st, 0, j);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int cur = ks & 1;
       if (ks + 1 < 4) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fa[cur ^ 1][i] = *reinterpret_cast<const bf16x8*>(st + aoff[ks + 1] + i * 32 * 128);
+        for (int i = 0; i < 4; ++i) fa[cur ^ 1][i] = frag_a(st, ks + 1, i);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          fb[cur ^ 1][j] = *reinterpret_cast<const bf16x8*>(st + boff[ks + 1] + j * 32 * 128);
+        for (int j = 0; j < NJ; ++j) fb[cur ^ 1][j] = frag_b(st, ks + 1, j);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -172,8 +246,13 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
 #pragma unroll
           for (int u = 0; u < CB / 4; ++u) {
             const int blk = pt * (CB / 4) + u;   // A blocks 0 .. CB-1, then B
-            if (blk < CB) dma_part<CB>(nx, abase, g.lda, arows, g.K, knx, wave, lane, blk);
-            else dma_part<CB>(nx + A_BYTES, bbase, g.ldb, brows, g.K, knx, wave, lane, blk - CB);
+            if constexpr (KT) {
+              if (blk < CB) dma_part_t<CB>(nx, amat, g.lda, m0, kvalid, knx, wave, lane, blk);
+              else dma_part_t<CB>(nx + A_BYTES, bmat, g.ldb, n0, kvalid, knx, wave, lane, blk - CB);
+            } else {
+              if (blk < CB) dma_part<CB>(nx, abase, g.lda, arows, g.K, knx, wave, lane, blk);
+              else dma_part<CB>(nx + A_BYTES, bbase, g.ldb, brows, g.K, knx, wave, lane, blk - CB);
+            }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -211,9 +290,18 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
 // every B segment starting at a multiple of 256, one C segment, row strides
 // that keep 16-byte alignment, and enough tiles to fill the chip.  Returns false (nothing
 // launched) otherwise.
-bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError_t* err) {
+bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError_t* err,
+                        GemmLayout layout) {
   if (g.K % TK != 0 || g.K <= 0 || g.lda % 8 != 0 || g.ldb % 8 != 0 || g.c_nseg != 1)
     return false;
+  const bool kt = layout == GemmLayout::TN;
+  if (layout == GemmLayout::NN) return false;
+  if (kt) {
+    // fp32 output only (the weight gradients), one B segment, 32-bit offsets
+    const long kv = g.k_valid > 0 ? g.k_valid : g.K;
+    if (!out_f32 || g.b_nseg != 1 || kv * g.lda * 2 >= (1L << 31) || kv * g.ldb * 2 >= (1L << 31))
+      return false;
+  }
   if ((long)TM * g.ldc * 4 >= (1L << 31)) return false;
   for (int i = 1; i < g.b_nseg; ++i)
     if (g.b_start[i] % TN != 0) return false;
@@ -227,12 +315,15 @@ bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError
   // the second wave per SIMD hides stalls); fewer: 4 waves of 128 x 128, whose
   // larger wave tiles read less LDS per MFMA
   const bool w8 = (long)tiles_m * tiles_n * nsplit >= 512;
-  if (out_f32) {
-    if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
-    else hipLaunchKernelGGL((gemm_nt_256_kernel<float, 4>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
+  if (kt) {
+    if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, true>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+    else hipLaunchKernelGGL((gemm_nt_256_kernel<float, 4, true>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
+  } else if (out_f32) {
+    if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, false>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+    else hipLaunchKernelGGL((gemm_nt_256_kernel<float, 4, false>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
   } else {
-    if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 8>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
-    else hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 4>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
+    if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 8, false>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+    else hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 4, false>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
   }
   *err = hipGetLastError();
   return true;
