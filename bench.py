@@ -296,8 +296,10 @@ def bench_backward(args, torch, cca):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # ~0.1 s of prefill steps: fewer left the shader clock still ramping in the
+    # timed loop (0.475 vs 0.451 ms per step after 5 and after ~100 steps)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--rows", default="prefill,decode,backward",
                     help="comma list: prefill (headline, always run), decode, backward")
     ap.add_argument("--bwd-steps", type=int, default=3, help="timed backward steps")
