@@ -34,6 +34,9 @@ CASES = [
              kind="backward"),
     Workload("bf16_bwd_g8_flags", B=1, S=150, E=1024, C=1, Hq=8, Hkv=1, flags=1 | 4 | 8, sv=40,
              seed=70, kind="backward"),
+    # a single token: one step in each attention backward kernel, the weight
+    # gradients on the transposed-copy path
+    Workload("bf16_bwd_single", B=2, S=1, E=512, C=1, Hq=4, Hkv=2, seed=73, kind="backward"),
     # three query heads per KV head: the attention backward splits each head's
     # query range between the two work-groups of a key block (odd group size)
     # and a separate kernel adds the second partial; ragged S
@@ -56,10 +59,21 @@ def check_backward(w, inp):
     g = r["layer"].backward(r["w"], r["x"], dy, r["saved"])
     torch.cuda.synchronize()
     ref = O.backward(inp["x"], inp["dy"], params_of(inp), spec_of(w))
-    errs = {k: rel(host(g[k]), ref[k]) for k in ref}
+    # With one token every query sees only its own key: P = 1, O = V, dP = D,
+    # so dS and every gradient that flows through Q or K are exactly zero and
+    # the oracle's are rounding noise.  Those are checked against the scale of
+    # the gradients that do not vanish instead of relative to themselves.
+    vanish = {"dw_q", "dw_k", "dconv_q", "dconv_k"} if w.S == 1 else set()
+    errs = {k: rel(host(g[k]), ref[k]) for k in ref if k not in vanish}
     say(f"  rel errors {errs}")
     for k, e in errs.items():
         assert e <= TOL[w.dtype], (k, e)
+    if vanish:
+        scale = max(float(np.linalg.norm(ref[k])) for k in ("dw_v", "dw_o"))
+        small = {k: float(np.linalg.norm(host(g[k]).astype(np.float64))) / scale for k in vanish}
+        say(f"  vanishing gradients / scale {small}")
+        for k, e in small.items():
+            assert e <= 1e-4, (k, e)
     return g
 
 

@@ -159,3 +159,36 @@ def test_prefill_is_deterministic():
     vb = saved_views(b["layer"], b["saved"], w, w.B, w.S)
     for k in va:
         assert torch.equal(va[k], vb[k]), k
+
+
+def test_empty_batch_or_sequence_is_rejected():
+    """B = 0 or S = 0: prefill and backward return CCA_ERR_INVALID_ARG before
+    any launch and leave their outputs as they were."""
+    import ctypes
+
+    import compressed_latent_attention_amd as cca
+    w = Workload("bf16_empty", B=1, S=8, E=512, C=1, Hq=4, Hkv=2, seed=43)
+    r = run_prefill(w, make_inputs(w), with_saved=True)
+    lib, h = cca.load(), r["layer"].handle
+    wts = cca._weights(r["w"])
+    y = torch.full_like(r["y"], 7.0)
+    ws = r["layer"].workspace(cca.CCA_OP_PREFILL, 1, 8)
+    for B, S in ((0, 8), (1, 0)):
+        st = lib.cca_forward_prefill(h, ctypes.byref(wts), cca._ptr(r["x"]), B, S, cca._ptr(y),
+                                     None, None, None, None, cca._ptr(ws), None)
+        assert st == cca.CCA_ERR_INVALID_ARG, (B, S, st)
+    g = cca.cca_grads()
+    dx = torch.full_like(r["x"], 7.0)
+    g.dx = cca._ptr(dx)
+    grads = {n: torch.zeros(r["w"][n[1:]].shape, dtype=torch.float32, device="cuda")
+             for n in ("dw_q", "dw_k", "dw_v", "dw_o", "dconv_q", "dconv_k")}
+    for n, t in grads.items():
+        setattr(g, n, cca._ptr(t))
+    wsb = r["layer"].workspace(cca.CCA_OP_BACKWARD, 1, 8)
+    for B, S in ((0, 8), (1, 0)):
+        st = lib.cca_backward(h, ctypes.byref(wts), cca._ptr(r["x"]), cca._ptr(r["x"]),
+                              cca._ptr(r["saved"]), B, S, ctypes.byref(g), cca._ptr(wsb), None)
+        assert st == cca.CCA_ERR_INVALID_ARG, (B, S, st)
+    torch.cuda.synchronize()
+    assert bool((y == 7.0).all()) and bool((dx == 7.0).all())
+    assert all(int(torch.count_nonzero(t)) == 0 for t in grads.values())
