@@ -19,8 +19,8 @@
 //           of the group's heads, otherwise half of each head's query range;
 //           query blocks run in descending order, so the work-groups of a head
 //           read the same tile at about the same time;
-//   dq    — work-group = 128 queries of one head, 8 waves, looping over the key
-//           blocks (32 keys) up to the diagonal.  Producers (waves 0-3, 32
+//   dq    — work-group = 128 queries of one head, 8 waves, looping over the keys
+//           up to the diagonal, 64 per step (two 32-key blocks per barrier).  Producers (waves 0-3, 32
 //           queries each, Q and dO rows in registers) compute S^T = K Q^T,
 //           dP^T = V dO^T and dS; consumers stage the K / V tiles and add
 //           dQ += dS K one step behind.
@@ -437,13 +437,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_sum_kernel(float* dk, const floa
 }
 
 // ------------------------------------------------------------------ dq
+constexpr int DQ_KB = 2;         // 32-key blocks per dQ step
 struct DqStage {
-  f16 k[TILE];           // K'' rows of the step's 32 keys
-  f16 v[TILE];           // V' rows
+  f16 k[DQ_KB * TILE];   // K'' rows of the step's 64 keys
+  f16 v[DQ_KB * TILE];   // V' rows
 };
 
 struct DqRegs {
-  f16x8 k[2], v[2];
+  f16x8 k[2 * DQ_KB], v[2 * DQ_KB];
 };
 
 __device__ __forceinline__ void dq_load(const AttnBwdArgs& a, int b, int g, int j0, int t,
@@ -452,7 +453,7 @@ __device__ __forceinline__ void dq_load(const AttnBwdArgs& a, int b, int g, int 
   const __amdgpu_buffer_rsrc_t krs = rows16(a.k16, kvrow, a.s_pad);
   const __amdgpu_buffer_rsrc_t vrs = rows16(a.v16, kvrow, a.s_pad);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 2 * DQ_KB; ++i) {
     const int f = t + 256 * i;
     const int row = f >> 4, ch = (f & 15) * 8;
     r.k[i] = load16(krs, (j0 + row) * D + ch);
@@ -462,7 +463,7 @@ __device__ __forceinline__ void dq_load(const AttnBwdArgs& a, int b, int g, int 
 
 __device__ __forceinline__ void dq_store(DqStage& st, int t, const DqRegs& r) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 2 * DQ_KB; ++i) {
     const int f = t + 256 * i;
     const int row = f >> 4, ch = f & 15;
     *reinterpret_cast<f16x8*>(st.k + tile_off(row, ch)) = r.k[i];
@@ -476,7 +477,7 @@ __device__ __forceinline__ void dq_store(DqStage& st, int t, const DqRegs& r) {
 // dQ += dS K one step behind, with K^T read transposed from that step's tile.
 struct DqSmem {
   DqStage stg[3];
-  f16 sbuf[2][4][2 * 64 * 8];    // dS of a step per producer: [parity][producer][ks][lane][8]
+  f16 sbuf[2][4][DQ_KB][2 * 64 * 8];  // dS per producer: [parity][producer][key block][ks][lane][8]
 };
 
 __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
   const int my_q = qw0 + l32;
   const long hrow = (long)(b * dm.Hq + h);
   const int q_last = min(S, q0 + 128) - 1;
-  const int nsteps = q_last / TB + 1;
+  const int nsteps = q_last / (DQ_KB * TB) + 1;
 
   if (wave < 4) {
     // ---------------- producer: S^T, dP^T, dS
@@ -521,13 +522,17 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
     lds_barrier();                                 // the consumers have staged step 0
     for (int s = 0; s < nsteps; ++s) {
       const DqStage& st = sm.stg[s % 3];
-      const int j0 = s * TB;
+#pragma unroll
+      for (int kb = 0; kb < DQ_KB; ++kb) {
+      const int j0 = (s * DQ_KB + kb) * TB;
+      const f16* tk = st.k + kb * TILE;
+      const f16* tv = st.v + kb * TILE;
       if (j0 <= qw0 + 31) {                  // else every key follows every query of the wave
         f32x16 sacc, pacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) pacc[r] = 0.0f;
         // S^T starts at -inf where the key follows the lane's query (only the
-        // steps whose keys reach past the wave's first query have any), so
+        // blocks whose keys reach past the wave's first query have any), so
         // exp2 gives P = 0 there without a per-element test.  Lane (query l32,
         // hi): register r is key j0 + 16 (r / 8) + 8 hi + r % 8.
         if (j0 + 31 > qw0) {
@@ -541,8 +546,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
         f16x8 ka[8], va[8];
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          ka[ks] = read_a(st.k, ao, ks);
-          va[ks] = read_a(st.v, ao, ks);
+          ka[ks] = read_a(tk, ao, ks);
+          va[ks] = read_a(tv, ao, ks);
         }
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
@@ -558,9 +563,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
             const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c1, -lse2));
             sf[half][e] = (f16)(p * (pacc[r] - dsm));
           }
-        f16* sw = sm.sbuf[s & 1][pair] + lane * 8;
+        f16* sw = sm.sbuf[s & 1][pair][kb] + lane * 8;
         *reinterpret_cast<f16x8*>(sw) = sf[0];
         *reinterpret_cast<f16x8*>(sw + 512) = sf[1];
+      }
       }
       lds_barrier();
     }
@@ -575,31 +581,36 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
       for (int r = 0; r < 16; ++r) dq[i][r] = 0.0f;
     int to[2];
     t_offsets(lane, to);
+    constexpr int SB = DQ_KB * TB;                 // keys per step
     DqRegs r0, r1;                                 // step j is staged through r(j % 2)
     dq_load(a, b, g, 0, tc, r0);
-    dq_load(a, b, g, min(1, nsteps - 1) * TB, tc, r1);
+    dq_load(a, b, g, min(1, nsteps - 1) * SB, tc, r1);
     dq_store(sm.stg[0], tc, r0);
-    dq_load(a, b, g, min(2, nsteps - 1) * TB, tc, r0);
+    dq_load(a, b, g, min(2, nsteps - 1) * SB, tc, r0);
     lds_barrier();
     // iteration s: stage step s + 1 and load step s + 3, then dQ of step s - 1
     auto iter = [&](int s, DqRegs& rs) {
       if (s + 1 < nsteps) {
         dq_store(sm.stg[(s + 1) % 3], tc, rs);
-        dq_load(a, b, g, min(s + 3, nsteps - 1) * TB, tc, rs);
+        dq_load(a, b, g, min(s + 3, nsteps - 1) * SB, tc, rs);
       }
-      if (s >= 1 && (s - 1) * TB <= qw0 + 31) {
+      if (s >= 1) {
         const DqStage& sp = sm.stg[(s - 1) % 3];
-        const f16* sr = sm.sbuf[(s - 1) & 1][pair] + lane * 8;
-        f16x8 sa[2];
-        sa[0] = *reinterpret_cast<const f16x8*>(sr);
-        sa[1] = *reinterpret_cast<const f16x8*>(sr + 512);
-        // dQ += dS K: A = dS (lane = query row), B = K^T read transposed
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int kb = 0; kb < DQ_KB; ++kb) {
+          if (((s - 1) * DQ_KB + kb) * TB > qw0 + 31) break;
+          const f16* sr = sm.sbuf[(s - 1) & 1][pair][kb] + lane * 8;
+          f16x8 sa[2];
+          sa[0] = *reinterpret_cast<const f16x8*>(sr);
+          sa[1] = *reinterpret_cast<const f16x8*>(sr + 512);
+          // dQ += dS K: A = dS (lane = query row), B = K^T read transposed
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[ks], read_t(sp.k, to, ks, nb), dq[nb],
-                                                            0, 0, 0);
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+              dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                  sa[ks], read_t(sp.k + kb * TILE, to, ks, nb), dq[nb], 0, 0, 0);
+        }
       }
       lds_barrier();
     };
