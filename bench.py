@@ -191,6 +191,19 @@ def _time_loop(torch, fn, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
+def _time_warm(torch, fn, steps, warm_s=0.15):
+    """Mean seconds per call over `steps` calls after at least `warm_s` seconds
+    of untimed calls (sized from one probe call): the shader clock takes tens
+    of milliseconds of load to settle after the host-side set-up between
+    configurations."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-5)
+    return _time_loop(torch, fn, steps, max(steps, int(warm_s / one)))
+
+
 def bench_decode(args, torch, cca):
     """32-sequence CCGQA decode step over a 32768-token cache.  The cache, the
     state and x_new are drawn on the GPU from a seeded torch generator (N(0,1),
@@ -221,7 +234,7 @@ def bench_decode(args, torch, cca):
         cca.cca_decode_step(layer.handle, wts, xn, arr_pos, w.B, kc, vc, st, yn, ws, stream)
 
     steps = max(args.steps, 10)
-    sec = _time_loop(torch, step, steps, args.warmup)
+    sec = _time_warm(torch, step, steps)
     cca.cca_profile_enable(layer.handle, True)
     _time_loop(torch, step, 5, 0)
     prof = cca.cca_profile_read(layer.handle)
@@ -270,7 +283,7 @@ def bench_backward(args, torch, cca):
         cca.cca_backward(layer.handle, wts, x, dy, saved, w.B, w.S, grads, ws, stream)
 
     steps = max(1, args.bwd_steps)
-    sec = _time_loop(torch, step, steps, 1)
+    sec = _time_warm(torch, step, steps)
     cca.cca_profile_enable(layer.handle, True)
     _time_loop(torch, step, 1, 0)
     prof = cca.cca_profile_read(layer.handle)
@@ -293,6 +306,99 @@ def bench_backward(args, torch, cca):
     }
 
 
+def _gpu_layer(torch, cca, w, gen):
+    """A layer of workload w with weights drawn on the GPU (seeded N(0, 1)
+    scaled like the parity recipe; the timing does not depend on the values)."""
+    layer = cca.CCALayer(w.E, w.C, w.Hq, w.Hkv, w.capacity, w.kq, w.kk, w.s_v, w.flags,
+                         w.rope_base, w.dtype)
+    d, E = w.d, w.E
+    rnd = lambda shape, std: (torch.randn(shape, generator=gen, device="cuda") * std).to(
+        torch.bfloat16)
+    wts = {"w_q": rnd((w.Hq * d, E), E ** -0.5), "w_k": rnd((w.Hkv * d, E), E ** -0.5),
+           "w_v": rnd((w.Hkv * d, E), E ** -0.5), "w_o": rnd((E, w.Hq * d), E ** -0.5),
+           "conv_q": rnd((w.Hq, w.kq, d, d), (w.kq * d) ** -0.5),
+           "conv_k": rnd((w.Hkv, w.kk, d, d), (w.kk * d) ** -0.5)}
+    return layer, wts, rnd
+
+
+N1_SWEEP = (4096, 8192, 16384, 32768, 65536)
+
+
+
+
+
+def bench_n1(args, torch, cca):
+    """The same-GPU comparators: prefill of the CCGQA layer and of MHA and GQA
+    of the same hidden size through the same kernels (C = 1, 16 query heads of
+    128, a one-tap convolution, no QK-mean or value shift) over S = 4k .. 64k,
+    and the backward of all three at 16k.  MHA's layer time includes the mix
+    pass its one-tap convolution still runs; `mha_core_ms` sums only its
+    projections and attention (kernel events, a second loop)."""
+    from compressed_latent_attention_amd.synthetic import WORKLOADS
+    base = {n: WORKLOADS[k] for n, k in (("ccgqa", "ccgqa_prefill_16k"),
+                                         ("mha", "mha_prefill_16k"),
+                                         ("gqa", "gqa_prefill_16k"))}
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda")
+    sweep = []
+    for S in N1_SWEEP:
+        row = {"S": S}
+        for name, w0 in base.items():
+            w = w0.replace(S=S)
+            gen.manual_seed(w.seed)
+            layer, wts, rnd = _gpu_layer(torch, cca, w, gen)
+            x = rnd((1, S, w.E), 1.0)
+            y = torch.empty_like(x)
+            ws = layer.workspace(cca.CCA_OP_PREFILL, 1, S)
+
+            def step():
+                cca.cca_forward_prefill(layer.handle, wts, x, 1, S, y, None, None, None, None,
+                                        ws, stream)
+
+            steps = 20 if S <= 8192 else 5
+            row[name + "_ms"] = _time_warm(torch, step, steps) * 1e3
+            if name == "mha":
+                cca.cca_profile_enable(layer.handle, True)
+                _time_loop(torch, step, steps, 0)
+                prof = cca.cca_profile_read(layer.handle)
+                cca.cca_profile_enable(layer.handle, False)
+                row["mha_core_ms"] = sum(v[1] / max(v[0], 1) for k, v in prof.items()
+                                         if k in ("proj_down", "attn", "proj_up"))
+            layer.close()
+            del x, y, ws, wts
+        row["mha_over_ccgqa"] = row["mha_ms"] / row["ccgqa_ms"]
+        row["mha_core_over_ccgqa"] = row["mha_core_ms"] / row["ccgqa_ms"]
+        row["gqa_over_ccgqa"] = row["gqa_ms"] / row["ccgqa_ms"]
+        sweep.append(row)
+        torch.cuda.empty_cache()
+    bwd = {}
+    for name, w0 in base.items():
+        w = w0.replace(kind="backward")
+        gen.manual_seed(w.seed)
+        layer, wts, rnd = _gpu_layer(torch, cca, w, gen)
+        x, dy = rnd((1, w.S, w.E), 1.0), rnd((1, w.S, w.E), 1.0)
+        saved = torch.empty(layer.saved_bytes(1, w.S), dtype=torch.uint8, device="cuda")
+        layer.forward_prefill(wts, x, saved=saved)
+        grads = {"dx": torch.empty_like(x)}
+        for n in ("w_q", "w_k", "w_v", "w_o", "conv_q", "conv_k"):
+            grads["d" + n] = torch.empty(wts[n].shape, dtype=torch.float32, device="cuda")
+        ws = layer.workspace(cca.CCA_OP_BACKWARD, 1, w.S)
+
+        def bstep():
+            cca.cca_backward(layer.handle, wts, x, dy, saved, 1, w.S, grads, ws, stream)
+
+        bwd[name + "_ms"] = _time_warm(torch, bstep, max(1, args.bwd_steps)) * 1e3
+        layer.close()
+        del x, dy, saved, grads, ws, wts
+        torch.cuda.empty_cache()
+    bwd["mha_over_ccgqa"] = bwd["mha_ms"] / bwd["ccgqa_ms"]
+    bwd["gqa_over_ccgqa"] = bwd["gqa_ms"] / bwd["ccgqa_ms"]
+    return {"note": "same-GPU comparators through the same kernels: MHA = C 1, 16 heads of 128, "
+                    "one-tap convolution, RoPE, no QK-mean or value shift; GQA = the same with "
+                    "2 KV heads (the CCGQA layer's KV-cache size); E = 2048, B = 1, bf16",
+            "prefill": sweep, "backward_16k": bwd}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,7 +407,8 @@ def main():
     # timed loop (0.475 vs 0.451 ms per step after 5 and after ~100 steps)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--rows", default="prefill,decode,backward",
-                    help="comma list: prefill (headline, always run), decode, backward")
+                    help="comma list: prefill (headline, always run), decode, backward; n1 "
+                         "adds the MHA / GQA comparators over S = 4k .. 64k (not run by default)")
     ap.add_argument("--bwd-steps", type=int, default=3, help="timed backward steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -371,6 +478,8 @@ def main():
         out["decode"] = bench_decode(args, torch, cca)
     if "backward" in rows:
         out["backward"] = bench_backward(args, torch, cca)
+    if "n1" in rows:
+        out["n1"] = bench_n1(args, torch, cca)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = time_oracle_sample(w, inp)
     print(json.dumps(out), flush=True)

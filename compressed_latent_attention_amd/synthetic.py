@@ -69,7 +69,11 @@ class Workload:
 
 
 # The five workloads: tiny fp32 CCA, CCA prefill at 4k, CCGQA prefill at 16k,
-# CCGQA decode over a 32768-token cache, CCGQA backward at 16k.
+# CCGQA decode over a 32768-token cache, CCGQA backward at 16k; then the two
+# same-GPU comparators of the same hidden size run through the same kernels:
+# MHA (no compression, 16 heads of 128, one-tap convolution, no QK-mean, no
+# value shift, RoPE kept) and GQA (the same with 2 KV heads, the KV-cache
+# size of the CCGQA layer).
 WORKLOADS: Dict[str, Workload] = {
     "cca_tiny_f32": Workload("cca_tiny_f32", B=1, S=128, E=256, C=4, Hq=4, Hkv=4,
                              dtype="f32", seed=1),
@@ -81,6 +85,10 @@ WORKLOADS: Dict[str, Workload] = {
                                  Hkv=2, seed=4, kind="decode", max_seq_len=32832),
     "ccgqa_backward_16k": Workload("ccgqa_backward_16k", B=1, S=16384, E=2048, C=4, Hq=4,
                                    Hkv=2, seed=5, kind="backward"),
+    "mha_prefill_16k": Workload("mha_prefill_16k", B=1, S=16384, E=2048, C=1, Hq=16, Hkv=16,
+                                kq=1, kk=1, flags=4, seed=6),
+    "gqa_prefill_16k": Workload("gqa_prefill_16k", B=1, S=16384, E=2048, C=1, Hq=16, Hkv=2,
+                                kq=1, kk=1, flags=4, seed=7),
 }
 
 

@@ -45,6 +45,12 @@ CASES = [
     # key block take one head each, query blocks in descending order
     Workload("bf16_bwd_s1000", B=1, S=1000, E=512, C=1, Hq=4, Hkv=2, kq=3, kk=2, seed=72,
              kind="backward"),
+    # the MHA and GQA comparators of the 16k layer (C = 1, 16 heads of 128,
+    # one-tap convolution, RoPE only; GQA with 2 KV heads)
+    Workload("bf16_bwd_mha_c1", B=1, S=150, E=2048, C=1, Hq=16, Hkv=16, kq=1, kk=1, flags=4,
+             seed=74, kind="backward"),
+    Workload("bf16_bwd_gqa_c1", B=1, S=150, E=2048, C=1, Hq=16, Hkv=2, kq=1, kk=1, flags=4,
+             seed=75, kind="backward"),
     # large enough that the weight gradients run split over K (16 partial sums)
     # on the 256 x 256 kernel, and the attention backward spans 16 key blocks
     Workload("bf16_bwd_splitk", B=1, S=2048, E=1024, C=2, Hq=4, Hkv=2, seed=67,

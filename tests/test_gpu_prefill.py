@@ -72,6 +72,12 @@ SMALL_BF16 = [
     Workload("bf16_g4_k3", B=1, S=200, E=512, C=1, Hq=4, Hkv=1, kq=3, kk=2, seed=33),
     Workload("bf16_single_token", B=2, S=1, E=512, C=1, Hq=4, Hkv=2, seed=34),
     Workload("bf16_no_extras", B=1, S=130, E=512, C=1, Hq=4, Hkv=4, flags=0, seed=35),
+    # the same-GPU comparators of the 16k layer at small S: MHA (no compression,
+    # 16 heads of 128, one-tap convolution, RoPE only) and GQA (2 KV heads)
+    Workload("bf16_mha_c1", B=1, S=200, E=2048, C=1, Hq=16, Hkv=16, kq=1, kk=1, flags=4,
+             seed=36),
+    Workload("bf16_gqa_c1", B=1, S=200, E=2048, C=1, Hq=16, Hkv=2, kq=1, kk=1, flags=4,
+             seed=37),
     Workload("bf16_tiny_tail", B=1, S=65, E=512, C=2, Hq=2, Hkv=1, flags=1 | 4 | 8, sv=40,
              seed=36),
 ]
