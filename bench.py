@@ -204,13 +204,15 @@ def _time_warm(torch, fn, steps, warm_s=0.15):
     return _time_loop(torch, fn, steps, max(steps, int(warm_s / one)))
 
 
-def bench_decode(args, torch, cca):
+def bench_decode(args, torch, cca, hkv=None):
     """32-sequence CCGQA decode step over a 32768-token cache.  The cache, the
     state and x_new are drawn on the GPU from a seeded torch generator (N(0,1),
     the same law as the parity workload; the timing does not depend on the
     values), the weights from the seeded parity recipe."""
     from compressed_latent_attention_amd.synthetic import WORKLOADS, make_inputs
     w = WORKLOADS["ccgqa_decode_32k"]
+    if hkv is not None:
+        w = w.replace(Hkv=hkv)
     layer = cca.CCALayer(w.E, w.C, w.Hq, w.Hkv, w.capacity, w.kq, w.kk, w.s_v, w.flags,
                          w.rope_base, w.dtype)
     wi = make_inputs(w.replace(S=1, B=1))     # weights only (same draw order and seed)
@@ -337,7 +339,8 @@ def bench_n1(args, torch, cca):
     from compressed_latent_attention_amd.synthetic import WORKLOADS
     base = {n: WORKLOADS[k] for n, k in (("ccgqa", "ccgqa_prefill_16k"),
                                          ("mha", "mha_prefill_16k"),
-                                         ("gqa", "gqa_prefill_16k"))}
+                                         ("gqa", "gqa_prefill_16k"),
+                                         ("ccgqa16", "ccgqa16_prefill_16k"))}
     stream = torch.cuda.current_stream()
     gen = torch.Generator(device="cuda")
     sweep = []
@@ -369,6 +372,7 @@ def bench_n1(args, torch, cca):
         row["mha_over_ccgqa"] = row["mha_ms"] / row["ccgqa_ms"]
         row["mha_core_over_ccgqa"] = row["mha_core_ms"] / row["ccgqa_ms"]
         row["gqa_over_ccgqa"] = row["gqa_ms"] / row["ccgqa_ms"]
+        row["ccgqa16_over_ccgqa"] = row["ccgqa16_ms"] / row["ccgqa_ms"]
         sweep.append(row)
         torch.cuda.empty_cache()
     bwd = {}
@@ -393,10 +397,18 @@ def bench_n1(args, torch, cca):
         torch.cuda.empty_cache()
     bwd["mha_over_ccgqa"] = bwd["mha_ms"] / bwd["ccgqa_ms"]
     bwd["gqa_over_ccgqa"] = bwd["gqa_ms"] / bwd["ccgqa_ms"]
+    bwd["ccgqa16_over_ccgqa"] = bwd["ccgqa16_ms"] / bwd["ccgqa_ms"]
+    # decode over a 32k-token cache: one KV head halves the cache the step reads
+    d2 = bench_decode(args, torch, cca)
+    d1 = bench_decode(args, torch, cca, hkv=1)
+    dec = {"ccgqa_ms": d2["ms_per_step"], "ccgqa16_ms": d1["ms_per_step"],
+           "ccgqa16_over_ccgqa": d1["ms_per_step"] / d2["ms_per_step"],
+           "ccgqa16_frac_of_hbm_peak": d1["frac_of_hbm_peak"]}
     return {"note": "same-GPU comparators through the same kernels: MHA = C 1, 16 heads of 128, "
                     "one-tap convolution, RoPE, no QK-mean or value shift; GQA = the same with "
-                    "2 KV heads (the CCGQA layer's KV-cache size); E = 2048, B = 1, bf16",
-            "prefill": sweep, "backward_16k": bwd}
+                    "2 KV heads (the CCGQA layer's KV-cache size); ccgqa16 = the CCGQA layer "
+                    "with one KV head (16x); E = 2048, B = 1, bf16",
+            "prefill": sweep, "backward_16k": bwd, "decode_32k": dec}
 
 
 def main():

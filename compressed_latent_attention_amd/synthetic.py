@@ -73,7 +73,7 @@ class Workload:
 # same-GPU comparators of the same hidden size run through the same kernels:
 # MHA (no compression, 16 heads of 128, one-tap convolution, no QK-mean, no
 # value shift, RoPE kept) and GQA (the same with 2 KV heads, the KV-cache
-# size of the CCGQA layer).
+# size of the CCGQA layer); and the CCGQA layer with one KV head (16x).
 WORKLOADS: Dict[str, Workload] = {
     "cca_tiny_f32": Workload("cca_tiny_f32", B=1, S=128, E=256, C=4, Hq=4, Hkv=4,
                              dtype="f32", seed=1),
@@ -89,6 +89,9 @@ WORKLOADS: Dict[str, Workload] = {
                                 kq=1, kk=1, flags=4, seed=6),
     "gqa_prefill_16k": Workload("gqa_prefill_16k", B=1, S=16384, E=2048, C=1, Hq=16, Hkv=2,
                                 kq=1, kk=1, flags=4, seed=7),
+    # the 16x-compressed variant: one KV head (half the CCGQA layer's KV cache)
+    "ccgqa16_prefill_16k": Workload("ccgqa16_prefill_16k", B=1, S=16384, E=2048, C=4, Hq=4,
+                                    Hkv=1, seed=8),
 }
 
 

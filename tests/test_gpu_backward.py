@@ -51,6 +51,9 @@ CASES = [
              seed=74, kind="backward"),
     Workload("bf16_bwd_gqa_c1", B=1, S=150, E=2048, C=1, Hq=16, Hkv=2, kq=1, kk=1, flags=4,
              seed=75, kind="backward"),
+    # the 16x variant (one KV head) and d = 64 (the generic kernels)
+    Workload("bf16_bwd_ccgqa16", B=1, S=150, E=2048, C=4, Hq=4, Hkv=1, seed=76, kind="backward"),
+    Workload("bf16_bwd_d64", B=1, S=120, E=512, C=2, Hq=4, Hkv=2, seed=77, kind="backward"),
     # large enough that the weight gradients run split over K (16 partial sums)
     # on the 256 x 256 kernel, and the attention backward spans 16 key blocks
     Workload("bf16_bwd_splitk", B=1, S=2048, E=1024, C=2, Hq=4, Hkv=2, seed=67,

@@ -78,6 +78,9 @@ SMALL_BF16 = [
              seed=36),
     Workload("bf16_gqa_c1", B=1, S=200, E=2048, C=1, Hq=16, Hkv=2, kq=1, kk=1, flags=4,
              seed=37),
+    # the 16x variant (one KV head) and d = 64 (the generic kernels)
+    Workload("bf16_ccgqa16", B=1, S=200, E=2048, C=4, Hq=4, Hkv=1, seed=38),
+    Workload("bf16_d64", B=1, S=150, E=512, C=2, Hq=4, Hkv=2, seed=39),
     Workload("bf16_tiny_tail", B=1, S=65, E=512, C=2, Hq=2, Hkv=1, flags=1 | 4 | 8, sv=40,
              seed=36),
 ]
