@@ -611,10 +611,17 @@ cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, cons
       ab.do16 = (char*)ab.v16 + align256((size_t)B * dm.nk * sp * 2);
       ab.dk2 = (float*)((char*)ab.do16 + align256((size_t)B * dm.nq * sp * 2));
       ab.dv2 = (float*)((char*)ab.dk2 + align256((size_t)B * S * dm.nk * 4));
+      if (attn_bwd_mfma_supported(dm) && attn_bwd_parts(dm) == 4) {
+        ab.dk3 = (float*)((char*)ab.dv2 + align256((size_t)B * S * dm.nk * 4));
+        ab.dv3 = (float*)((char*)ab.dk3 + align256((size_t)B * S * dm.nk * 4));
+        ab.dk4 = (float*)((char*)ab.dv3 + align256((size_t)B * S * dm.nk * 4));
+        ab.dv4 = (float*)((char*)ab.dk4 + align256((size_t)B * S * dm.nk * 4));
+      }
     }
     // the mix backward's pointwise pass adds the second-half dK / dV partials
     // as it reads dK / dV, when it can (no separate sum launch)
-    const bool sum_in_mix = attn_bwd_mfma_supported(dm) && mix_bwd_adds_dkdv2(dm);
+    const bool sum_in_mix = attn_bwd_mfma_supported(dm) && mix_bwd_adds_dkdv2(dm) &&
+                            attn_bwd_parts(dm) == 2;
     ab.sum_by_consumer = sum_in_mix;
     CCA_TRY_HIP(timed(h, "bwd_attn", s, [&] { return launch_attn_bwd(ab, s); }));
 

@@ -15,8 +15,9 @@
 //           consumers (waves 4-7, wave w + 4 on the SIMD of wave w) stage the
 //           Q / dO tiles into LDS and add dV += P^T dO one step behind.  The two
 //           waves of a SIMD overlap one's softmax with the other's MFMAs.  Two
-//           work-groups per key block: with an even group size each takes half
-//           of the group's heads, otherwise half of each head's query range;
+//           or four work-groups per key block: each takes a half (a quarter,
+//           when the group size is a multiple of 4) of the group's heads, or
+//           with an odd group size half of each head's query range;
 //           query blocks run in descending order, so the work-groups of a head
 //           read the same tile at about the same time;
 //   dq    — work-group = 128 queries of one head, 8 waves, looping over the keys
@@ -240,8 +241,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
   __shared__ __attribute__((aligned(16))) DkdvSmem sm;
   const Dims& dm = a.dm;
   const int S = a.S, G = dm.G;
-  const int part = blockIdx.x & 1;
-  const int k0 = (blockIdx.x >> 1) * 128, g = blockIdx.y, b = blockIdx.z;
+  const int nparts = dm.G % 4 == 0 ? 4 : 2;          // work-groups per key block
+  const int part = blockIdx.x % nparts;
+  const int k0 = (int)(blockIdx.x / nparts) * 128, g = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int pair = wave & 3;
@@ -252,10 +254,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
   // Steps: (head, query block), head-major, query blocks in descending order.
   const int qb_last = (S + TB - 1) / TB - 1;
   const int nqb_all = qb_last + 1 - k0 / TB;
-  const bool split_heads = (G & 1) == 0;
+  const bool split_heads = G % nparts == 0;           // else two parts, odd G
   const int nfirst = (nqb_all + 1) / 2;
-  const int hbase = g * G + (split_heads ? part * (G / 2) : 0);
-  const int nh = split_heads ? G / 2 : G;
+  const int hbase = g * G + (split_heads ? part * (G / nparts) : 0);
+  const int nh = split_heads ? G / nparts : G;
   const int qtop = split_heads || part ? qb_last : k0 / TB + nfirst - 1;
   const int nqb = split_heads ? nqb_all : (part ? nqb_all - nfirst : nfirst);
   const int nsteps = nh * nqb;
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
       lds_barrier();                               // the consumers' last step
     }
     const float inv = 1.0f / sqrtf((float)D);
-    float* dkb = (part ? a.dk2 : a.dk) + kvrow * S * D;
+    float* dkb = (part == 0 ? a.dk : part == 1 ? a.dk2 : part == 2 ? a.dk3 : a.dk4) + kvrow * S * D;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
         if (s + 1 <= nsteps) iter(s + 1, r0);
       }
     }
-    float* dvb = (part ? a.dv2 : a.dv) + kvrow * S * D;
+    float* dvb = (part == 0 ? a.dv : part == 1 ? a.dv2 : part == 2 ? a.dv3 : a.dv4) + kvrow * S * D;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -427,13 +429,21 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
   }
 }
 
-// dk += dk2, dv += dv2: the two halves of every key block, in a fixed order.
-__global__ __launch_bounds__(256) void bwd_dkdv_sum_kernel(float* dk, const float* dk2, float* dv,
-                                                           const float* dv2, long n4) {
+// dk += dk2 (+ dk3 + dk4), dv likewise: the partials of every key block's
+// work-groups, in a fixed order.
+__global__ __launch_bounds__(256) void bwd_dkdv_sum_kernel(AttnBwdArgs a, long n4) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
-  reinterpret_cast<f32x4*>(dk)[i] += reinterpret_cast<const f32x4*>(dk2)[i];
-  reinterpret_cast<f32x4*>(dv)[i] += reinterpret_cast<const f32x4*>(dv2)[i];
+  f32x4 k = reinterpret_cast<const f32x4*>(a.dk)[i] + reinterpret_cast<const f32x4*>(a.dk2)[i];
+  f32x4 v = reinterpret_cast<const f32x4*>(a.dv)[i] + reinterpret_cast<const f32x4*>(a.dv2)[i];
+  if (a.dk3) {
+    k = k + reinterpret_cast<const f32x4*>(a.dk3)[i];
+    k = k + reinterpret_cast<const f32x4*>(a.dk4)[i];
+    v = v + reinterpret_cast<const f32x4*>(a.dv3)[i];
+    v = v + reinterpret_cast<const f32x4*>(a.dv4)[i];
+  }
+  reinterpret_cast<f32x4*>(a.dk)[i] = k;
+  reinterpret_cast<f32x4*>(a.dv)[i] = v;
 }
 
 // ------------------------------------------------------------------ dq
@@ -635,12 +645,14 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
 
 bool attn_bwd_mfma_supported(const Dims& dm) { return mfma_bwd(dm); }
 
+int attn_bwd_parts(const Dims& dm) { return dm.G % 4 == 0 ? 4 : 2; }
+
 size_t attn_bwd_transpose_bytes(const Dims& dm, int B, int S) {
   if (!mfma_bwd(dm)) return 0;
   const size_t sp = (size_t)(S + 63) / 64 * 64;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   return 2 * al((size_t)B * dm.nq * sp * 2) + 2 * al((size_t)B * dm.nk * sp * 2) +
-         2 * al((size_t)B * S * dm.nk * 4);
+         2 * (attn_bwd_parts(dm) - 1) * al((size_t)B * S * dm.nk * 4);
 }
 
 hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) {
@@ -648,14 +660,19 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) {
   if (!mfma_bwd(dm) || !a.q16 || !a.k16 || !a.v16 || !a.do16 || a.s_pad < a.S ||
       a.s_pad % 64 != 0 || !a.dk2 || !a.dv2)
     return hipErrorInvalidValue;
+  const int nparts = attn_bwd_parts(dm);
+  if (nparts == 4 && (!a.dk3 || !a.dv3 || !a.dk4 || !a.dv4 || a.sum_by_consumer))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(a.s_pad / 64, dm.Hq + dm.Hkv, a.B), dim3(256), 0, s,
                      a);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(2 * ((a.S + 127) / 128), dm.Hkv, a.B), dim3(512), 0, s,
-                     a);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(nparts * ((a.S + 127) / 128), dm.Hkv, a.B), dim3(512),
+                     0, s, a);
   if (!a.sum_by_consumer) {
+    AttnBwdArgs sa = a;
+    if (nparts == 2) sa.dk3 = sa.dv3 = sa.dk4 = sa.dv4 = nullptr;
     const long n4 = (long)a.B * dm.Hkv * a.S * D / 4;
     hipLaunchKernelGGL(bwd_dkdv_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
-                       a.dk, a.dk2, a.dv, a.dv2, n4);
+                       sa, n4);
   }
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(((a.S + 127) / 128) * dm.Hq * a.B), dim3(512), 0, s, a);
   return hipGetLastError();

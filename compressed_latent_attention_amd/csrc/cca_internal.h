@@ -200,17 +200,25 @@ struct AttnBwdArgs {
   void* v16;         // V'  [B,Hkv,s_pad,d]
   void* do16;        // dO  [B,Hq,s_pad,d]
   int s_pad;         // S rounded up to a multiple of 64
-  // dK / dV of the second half of each key block's query range (fp32, same
-  // layout as dk / dv), added into dk / dv before the kernels return, unless
-  // the consumer adds them as it reads dk / dv (sum_by_consumer)
+  // dK / dV partials of the other work-groups of each key block (fp32, same
+  // layout as dk / dv; dk3 .. dv4 only with four parts, see attn_bwd_parts),
+  // added into dk / dv before the kernels return, unless the consumer adds
+  // dk2 / dv2 as it reads dk / dv (sum_by_consumer, two parts only)
   float* dk2;
   float* dv2;
+  float* dk3;
+  float* dv3;
+  float* dk4;
+  float* dv4;
   bool sum_by_consumer;
 };
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 // True when launch_attn_bwd takes the MFMA kernels (bf16, d = 128), which
 // produce the dk2 / dv2 second-half partials.
 bool attn_bwd_mfma_supported(const Dims& dm);
+// Work-groups per key block of the MFMA dK / dV kernel: 4 when the group size
+// is a multiple of 4 (each takes a quarter of the group's heads), else 2.
+int attn_bwd_parts(const Dims& dm);
 // Bytes of the MFMA attention backward's workspace: the fp16 copies and
 // the second-half dK / dV partials (0 when the config takes the generic path).
 size_t attn_bwd_transpose_bytes(const Dims& dm, int B, int S);
