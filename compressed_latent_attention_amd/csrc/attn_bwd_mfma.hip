@@ -148,19 +148,31 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnBwdArgs a) {
   const long ld1 = is_q ? dm.nq : D;
   f16* dst0 = reinterpret_cast<f16*>(is_q ? a.q16 : a.k16) + hrow * sp * D;
   f16* dst1 = reinterpret_cast<f16*>(is_q ? a.do16 : a.v16) + hrow * sp * D;
-  // thread -> (row, 8 channels); rows past S are written as zero
-  for (int f = threadIdx.x; f < 64 * (D / 8); f += 256) {
-    const int r = f >> 4, c = (f & 15) * 8;
-    const int t = t0 + r;
-    bf16x8 v, w;
+  // thread -> (row, 8 channels), four rows apart; every load is issued before
+  // the first store (the copies may not alias the sources as far as the
+  // compiler knows, so a load-convert-store loop would run its four memory
+  // round trips one after another).  The resources end at row S - 1: rows past
+  // it read as zero, and are written as zero.
+  const __amdgpu_buffer_rsrc_t rs0 =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src0, 0, S * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs1 =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src1, 0, (int)(((long)(S - 1) * ld1 + D) * 2),
+                                        0x00020000);
+  bf16x8 v[4], w[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = w[e] = (bf16)0.0f;
-    if (t < S) {
-      v = *reinterpret_cast<const bf16x8*>(src0 + (long)t * D + c);
-      w = *reinterpret_cast<const bf16x8*>(src1 + (long)t * ld1 + c);
-    }
-    *reinterpret_cast<f16x8*>(dst0 + (long)t * D + c) = to_f16(v);
-    *reinterpret_cast<f16x8*>(dst1 + (long)t * D + c) = to_f16(w);
+  for (int i = 0; i < 4; ++i) {
+    const int f = threadIdx.x + 256 * i;
+    const int t = t0 + (f >> 4), c = (f & 15) * 8;
+    v[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs0, (t * D + c) * 2, 0, 0));
+    w[i] = __builtin_bit_cast(bf16x8,
+                              __builtin_amdgcn_raw_buffer_load_b128(rs1, (int)((t * ld1 + c) * 2), 0, 0));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int f = threadIdx.x + 256 * i;
+    const int t = t0 + (f >> 4), c = (f & 15) * 8;
+    *reinterpret_cast<f16x8*>(dst0 + (long)t * D + c) = to_f16(v[i]);
+    *reinterpret_cast<f16x8*>(dst1 + (long)t * D + c) = to_f16(w[i]);
   }
   // D_t = <dO_t, O_t> in fp32: each thread sums 32 channels of one token
   if (is_q) {
@@ -663,6 +675,8 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) {
   const int nparts = attn_bwd_parts(dm);
   if (nparts == 4 && (!a.dk3 || !a.dv3 || !a.dk4 || !a.dv4 || a.sum_by_consumer))
     return hipErrorInvalidValue;
+  // 32-bit byte offsets within one sequence's token-major dO rows
+  if ((long)a.S * dm.nq * 2 >= (1L << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(a.s_pad / 64, dm.Hq + dm.Hkv, a.B), dim3(256), 0, s,
                      a);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(nparts * ((a.S + 127) / 128), dm.Hkv, a.B), dim3(512),
