@@ -572,9 +572,11 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
     r = 16 * (pidx & 3) + (lane & 15);
     c4 = 4 * (4 * (pidx >> 2) + (lane >> 4));
   };
-  for (int c0 = tb0; c0 < tend; c0 += GT) {
-    // 64 tokens x 32 float4 per operand: 8 of each per thread, all in flight
-    f32x4 gv[8], xv[8];
+  // 64 tokens x 32 float4 per operand: 8 of each per thread, all in flight.
+  // The next chunk's loads go out once this chunk is staged, so they land
+  // while its MFMAs run.
+  f32x4 gv[8], xv[8];
+  auto load_chunk = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       int r, c4;
@@ -586,6 +588,9 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
       xv[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                             xrs, ((tok - j - xr0) * dm.nqkv + c4) * 4, 0, 0));
     }
+  };
+  load_chunk(tb0);
+  for (int c0 = tb0; c0 < tend; c0 += GT) {
     __syncthreads();                                     // the previous chunk's reads are done
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -603,6 +608,7 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
       }
     }
     __syncthreads();
+    if (c0 + GT < tend) load_chunk(c0 + GT);
 #pragma unroll
     for (int ks = 0; ks < GT / 16; ++ks) {
       bf16x8 ah[2], al[2], bh[2], bl[2];
@@ -644,8 +650,19 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_reduce(MixBwdArgs a, int nblk
   const long per_blk = nq + (long)dm.Hkv * dm.kk * dm.d * dm.d;
   const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= per_blk) return;
+  // 16 loads in flight per batch, added in block order (the same fixed order
+  // as one at a time)
+  constexpr int RB = 16;
   float s = 0.0f;
-  for (int i = 0; i < nblk; ++i) s += a.dconv_part[(long)i * per_blk + e];
+  int i = 0;
+  for (; i + RB <= nblk; i += RB) {
+    float v[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) v[u] = a.dconv_part[(long)(i + u) * per_blk + e];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) s += v[u];
+  }
+  for (; i < nblk; ++i) s += a.dconv_part[(long)i * per_blk + e];
   if (e < nq)
     a.dconv_q[e] = s;
   else
