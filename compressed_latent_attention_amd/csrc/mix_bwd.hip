@@ -572,11 +572,9 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
     r = 16 * (pidx & 3) + (lane & 15);
     c4 = 4 * (4 * (pidx >> 2) + (lane >> 4));
   };
-  // 64 tokens x 32 float4 per operand: 8 of each per thread, all in flight.
-  // The next chunk's loads go out once this chunk is staged, so they land
-  // while its MFMAs run.
-  f32x4 gv[8], xv[8];
-  auto load_chunk = [&](int c0) {
+  for (int c0 = tb0; c0 < tend; c0 += GT) {
+    // 64 tokens x 32 float4 per operand: 8 of each per thread, all in flight
+    f32x4 gv[8], xv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       int r, c4;
@@ -588,9 +586,6 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
       xv[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                             xrs, ((tok - j - xr0) * dm.nqkv + c4) * 4, 0, 0));
     }
-  };
-  load_chunk(tb0);
-  for (int c0 = tb0; c0 < tend; c0 += GT) {
     __syncthreads();                                     // the previous chunk's reads are done
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -608,7 +603,6 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
       }
     }
     __syncthreads();
-    if (c0 + GT < tend) load_chunk(c0 + GT);
 #pragma unroll
     for (int ks = 0; ks < GT / 16; ++ks) {
       bf16x8 ah[2], al[2], bh[2], bl[2];
