@@ -18,7 +18,7 @@
 namespace cca {
 namespace {
 
-constexpr int TB = 256;        // tokens per tap-gradient partial block
+constexpr int TB = 512;        // tokens per tap-gradient partial block
 
 template <typename T>
 __device__ __forceinline__ float ldf(const void* p, long i) {
