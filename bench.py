@@ -7,8 +7,8 @@ A step is one cca_forward_prefill: down-projection, mix, attention,
 up-projection.  Prints one JSON line (rank 0) with tokens/s over K timed steps,
 the roofline of the dominant kernel (attention) timed with HIP events on the
 launch stream over a second loop of K steps (the events add to the step time,
-so the first loop runs without them), and the float64 CPU oracle timed on a
-bounded sample of the same workload.
+so the first loop runs without them), and the float64 CPU oracle's forward over
+the same workload, timed once.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--rows prefill,decode,backward]
 """
@@ -67,12 +67,10 @@ def attention_traffic_bytes():
         return None
 
 
-def time_oracle_sample(w, inp, n_rows=256):
-    """The oracle's forward on the full sequence for every linear step, and
-    attention plus the output projection for n_rows query rows spread evenly
-    over the sequence; the full-workload time is extrapolated as
-    t_linear + t_rows * S / n_rows (attention cost per row grows linearly with
-    its position, so evenly spaced rows average it)."""
+def time_oracle_forward(w, inp):
+    """The float64 oracle's forward over the whole workload (every token, every
+    step: projections, convolution, QK-mean, shift, RoPE, attention, W_o),
+    timed once, wall clock, on the host cores numpy's BLAS uses."""
     from oracle import cca as O
     try:
         from threadpoolctl import threadpool_info
@@ -82,31 +80,14 @@ def time_oracle_sample(w, inp, n_rows=256):
     spec = O.Spec(E=w.E, C=w.C, Hq=w.Hq, Hkv=w.Hkv, kq=w.kq, kk=w.kk, rope_base=w.rope_base,
                   s_v=w.s_v)
     p = {k: inp[k] for k in ("w_q", "w_k", "w_v", "w_o", "conv_q", "conv_k")}
-    x = inp["x"][0].astype(np.float64)
-    S, G, d = w.S, w.G, w.d
     t0 = time.perf_counter()
-    q_lat = O.project(x, p["w_q"]).reshape(S, w.Hq, d)
-    k_lat = O.project(x, p["w_k"]).reshape(S, w.Hkv, d)
-    v_lat = O.project(x, p["w_v"]).reshape(S, w.Hkv, d)
-    q_c = O.conv_causal(q_lat, p["conv_q"])
-    k_c = O.conv_causal(k_lat, p["conv_k"])
-    q_m, k_m = O.qk_mean(q_lat, k_lat, q_c, k_c, G, True, True)
-    v_s = O.value_shift(v_lat, spec.mask())
-    pos = np.arange(S)
-    k_r = O.rope(k_m, pos, w.rope_base)
-    q_r = O.rope(q_m, pos, w.rope_base)
-    t_lin = time.perf_counter() - t0
-    rows = np.linspace(0, S - 1, n_rows).astype(np.int64)
-    t1 = time.perf_counter()
-    o, _ = O.attention(q_r[rows], k_r, v_s, G, q_pos=rows, block=16)
-    O.project(o.reshape(len(rows), -1), p["w_o"])
-    t_rows = time.perf_counter() - t1
-    est = t_lin + t_rows * S / n_rows
-    return {"value": S / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"float64 numpy oracle: every linear step over all {S} tokens "
-                       f"({t_lin:.1f} s) plus attention and W_o for {n_rows} evenly spaced "
-                       f"query rows ({t_rows:.1f} s), extrapolated to the full sequence "
-                       f"({est:.1f} s)")}
+    O.forward(inp["x"], p, spec)
+    sec = time.perf_counter() - t0
+    return {"value": w.B * w.S / sec, "unit": "tokens/s", "cores": int(threads),
+            "host_cpu_count": os.cpu_count(), "kind": "oracle",
+            "sample": (f"the whole workload, not a sample: float64 numpy oracle forward over "
+                       f"all {w.B * w.S} tokens in {sec:.1f} s, one run, BLAS threads "
+                       f"{threads} of {os.cpu_count()} host CPUs")}
 
 
 def bench_prefill(args, torch, cca, w, inp):
@@ -125,9 +106,18 @@ def bench_prefill(args, torch, cca, w, inp):
     def step():
         cca.cca_forward_prefill(layer.handle, wts, x, B, S, y, None, None, None, None, ws, stream)
 
+    # W warm-up steps, then more until at least args.warm_s seconds of steps
+    # have run: the shader clock takes ~0.1 s of load to settle
+    t0 = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    warm_steps = args.warmup
+    while time.perf_counter() - t0 < args.warm_s:
+        for _ in range(20):
+            step()
+        warm_steps += 20
+        torch.cuda.synchronize()
     # the step time: K steps with nothing recorded between the kernels
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -146,7 +136,7 @@ def bench_prefill(args, torch, cca, w, inp):
     elapsed_prof = time.perf_counter() - t0
     prof = cca.cca_profile_read(layer.handle)
     cca.cca_profile_enable(layer.handle, False)
-    return elapsed, elapsed_prof, prof, layer
+    return elapsed, elapsed_prof, prof, layer, warm_steps
 
 
 DECODE_BYTES_NOTE = ("K and V caches over positions 0..pos of every sequence + all weights "
@@ -418,6 +408,8 @@ def main():
     # ~0.1 s of prefill steps: fewer left the shader clock still ramping in the
     # timed loop (0.475 vs 0.451 ms per step after 5 and after ~100 steps)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warm-s", type=float, default=0.3,
+                    help="untimed prefill steps continue past --warmup until this many seconds")
     ap.add_argument("--rows", default="prefill,decode,backward",
                     help="comma list: prefill (headline, always run), decode, backward; n1 "
                          "adds the MHA / GQA comparators over S = 4k .. 64k (not run by default)")
@@ -447,7 +439,7 @@ def main():
 
     w = WORKLOADS["ccgqa_prefill_16k"]
     inp = make_inputs(w)
-    elapsed, elapsed_prof, prof, _ = bench_prefill(args, torch, cca, w, inp)
+    elapsed, elapsed_prof, prof, _, warm_steps = bench_prefill(args, torch, cca, w, inp)
     ms = elapsed * 1000.0 / args.steps
     tokens = w.B * w.S * args.steps
     fl = prefill_flops(w)
@@ -465,6 +457,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_note": f"{warm_steps} untimed steps ran before the timed ones: the {args.warmup} "
+                       f"asked for, then more until {args.warm_s} s of steps had run (the "
+                       f"shader clock settles after ~0.1 s of load)",
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -493,7 +488,7 @@ def main():
     if "n1" in rows:
         out["n1"] = bench_n1(args, torch, cca)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = time_oracle_sample(w, inp)
+        out["cpu_baseline"] = time_oracle_forward(w, inp)
     print(json.dumps(out), flush=True)
 
 

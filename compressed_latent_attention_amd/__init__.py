@@ -66,13 +66,16 @@ _SIGNATURES = {
     "cca_profile_enable": (c_int, [c_void_p, c_int]),
     "cca_profile_read": (c_int, [c_void_p, POINTER(cca_kernel_time), c_int]),
     "cca_status_string": (c_char_p, [c_int]),
+    "cca_source_hash": (c_char_p, []),
 }
 
 _lib = None
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Loads libcca.so (built by ``build.py``); raises if it is missing."""
+    """Loads libcca.so (built by ``build.py``); raises if it is missing or was
+    built from sources other than the ones beside it (its compiled-in source
+    hash differs from the hash of csrc/ and include/cca.h)."""
     global _lib
     if _lib is not None:
         return _lib
@@ -84,6 +87,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    from .build import source_hash
+    built, now = lib.cca_source_hash().decode(), source_hash()
+    if built != now:
+        raise ImportError(f"{path} is stale: built from sources with hash {built[:16]}, the "
+                          f"sources now hash to {now[:16]}; rebuild with "
+                          "`python -m compressed_latent_attention_amd.build`")
     _lib = lib
     return lib
 

@@ -3,10 +3,15 @@
 Every source under csrc/ is compiled with hipcc into an object file in
 ``_build/`` next to this file, then linked into ``libcca.so`` in the package
 directory.  Packed-fp32 instructions are disabled for all device code.
+
+The SHA-256 of the sources (csrc/ and include/cca.h) is compiled into the
+library (``cca_source_hash``); the binding refuses a library whose hash differs
+from the sources beside it, so a stale build fails loudly.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -30,11 +35,25 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-def _compile(src: str) -> str:
+def source_hash() -> str:
+    """SHA-256 over the names and bytes of every file the library is built
+    from: csrc/*.hip, *.cpp, *.h and include/cca.h."""
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp", ".h")))
+    h = hashlib.sha256()
+    for path in [os.path.join(CSRC, f) for f in files] + [os.path.join(ROOT, "include", "cca.h")]:
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
+def _compile(src: str, digest: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", src, "-o", obj]
+        cmd = [HIPCC] + FLAGS + [f'-DCCA_SOURCE_SHA256="{digest}"', "-x", "hip", "-c", src,
+                                 "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -44,8 +63,9 @@ def _compile(src: str) -> str:
 def build(jobs: int = 8, verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
+    digest = source_hash()
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda src: _compile(src, digest), srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -199,7 +199,13 @@ GemmArgs gemm_down(const Dims& dm, int M, const void* a, const cca_weights* w, v
 
 }  // namespace
 
+#ifndef CCA_SOURCE_SHA256
+#define CCA_SOURCE_SHA256 "unknown"
+#endif
+
 extern "C" {
+
+const char* cca_source_hash(void) { return CCA_SOURCE_SHA256; }
 
 const char* cca_status_string(cca_status s) {
   switch (s) {

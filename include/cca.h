@@ -201,6 +201,11 @@ int cca_profile_read(cca_handle* h, cca_kernel_time* out, int max);
 /* Static text for a status code. */
 const char* cca_status_string(cca_status s);
 
+/* Build identification: the hex SHA-256 of the sources this library was
+ * compiled from (static text; "unknown" when built without it).  The binding
+ * compares it with the sources beside the library and refuses a stale build. */
+const char* cca_source_hash(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,6 +40,18 @@ def rel(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
+def block_rel(a, b, axis: int, block: int = 128) -> float:
+    """The largest relative L2 error over blocks of `block` rows along `axis`
+    (the token axis), so that one wrong tile cannot hide in a whole-tensor
+    norm."""
+    a = np.moveaxis(np.asarray(a, np.float64), axis, 0)
+    b = np.moveaxis(np.asarray(b, np.float64), axis, 0)
+    worst = 0.0
+    for t0 in range(0, a.shape[0], block):
+        worst = max(worst, rel(a[t0:t0 + block], b[t0:t0 + block]))
+    return worst
+
+
 def spec_of(w: Workload) -> O.Spec:
     return O.Spec(E=w.E, C=w.C, Hq=w.Hq, Hkv=w.Hkv, kq=w.kq, kk=w.kk, rope_base=w.rope_base,
                   qk_pre=bool(w.flags & 1), qk_post=bool(w.flags & 2),

@@ -1,5 +1,8 @@
 """GPU parity of the backward pass against the float64 oracle: dx and every
-weight and tap gradient, element by element (relative L2 per tensor)."""
+weight and tap gradient, element by element (relative L2 per tensor; dx also
+per block of 128 tokens), up to the full 16k CCGQA backward the benchmark
+times, and with upstream gradients scaled down to the size a token-mean loss
+gives (2^-20, 2^-24)."""
 import numpy as np
 import pytest
 
@@ -12,7 +15,8 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
-from gpu_helpers import TOL, dev, host, params_of, rel, run_prefill, say, spec_of  # noqa: E402
+from gpu_helpers import (TOL, block_rel, dev, host, params_of, rel, run_prefill,  # noqa: E402
+                         say, spec_of)
 
 CASES = [
     Workload("f32_bwd_tiny", B=1, S=128, E=256, C=4, Hq=4, Hkv=4, dtype="f32", seed=61,
@@ -58,10 +62,15 @@ CASES = [
     # on the 256 x 256 kernel, and the attention backward spans 16 key blocks
     Workload("bf16_bwd_splitk", B=1, S=2048, E=1024, C=2, Hq=4, Hkv=2, seed=67,
              kind="backward"),
+    # two sequences of 4500 tokens: 18 blocks of tap-gradient partials (the
+    # batched reduce loop) with a ragged last block, split-K weight gradients
+    # over 9000 tokens
+    Workload("bf16_bwd_taps18", B=2, S=4500, E=512, C=1, Hq=4, Hkv=2, seed=78,
+             kind="backward"),
 ]
 
 
-def check_backward(w, inp):
+def check_backward(w, inp, block_check=True):
     say(f"[backward] {w}")
     r = run_prefill(w, inp, with_saved=True)
     dy = dev(inp["dy"], w)
@@ -73,10 +82,16 @@ def check_backward(w, inp):
     # the oracle's are rounding noise.  Those are checked against the scale of
     # the gradients that do not vanish instead of relative to themselves.
     vanish = {"dw_q", "dw_k", "dconv_q", "dconv_k"} if w.S == 1 else set()
-    errs = {k: rel(host(g[k]), ref[k]) for k in ref if k not in vanish}
+    got = {k: host(g[k]) for k in ref}
+    errs = {k: rel(got[k], ref[k]) for k in ref if k not in vanish}
     say(f"  rel errors {errs}")
     for k, e in errs.items():
         assert e <= TOL[w.dtype], (k, e)
+    assert all(np.all(np.isfinite(a)) for a in got.values())
+    if block_check:
+        e_blk = block_rel(got["dx"], ref["dx"], 1)
+        say(f"  dx worst 128-token block {e_blk:.2e}")
+        assert e_blk <= TOL[w.dtype], ("dx block", e_blk)
     if vanish:
         scale = max(float(np.linalg.norm(ref[k])) for k in ("dw_v", "dw_o"))
         small = {k: float(np.linalg.norm(host(g[k]).astype(np.float64))) / scale for k in vanish}
@@ -89,6 +104,35 @@ def check_backward(w, inp):
 @pytest.mark.parametrize("w", CASES, ids=[c.name for c in CASES])
 def test_backward(w):
     check_backward(w, make_inputs(w))
+
+
+def test_backward_ccgqa_16k_full():
+    """The full-size CCGQA backward (S = 16384, E = 2048) the benchmark times:
+    the eight-wave dx GEMM, split-K weight gradients over 16384 tokens and 32
+    blocks of tap-gradient partials, every gradient against the oracle."""
+    w = WORKLOADS["ccgqa_backward_16k"]
+    check_backward(w, make_inputs(w))
+
+
+@pytest.mark.parametrize("dy_log2", [-20, -24])
+def test_backward_small_upstream_gradient(dy_log2):
+    """dY scaled by 2^-20 and 2^-24, the size of the upstream gradient of a
+    loss averaged over many tokens.  Every gradient is linear in dY, so the
+    relative error bound is the same as at dY ~ N(0, 1)."""
+    w = Workload(f"bf16_bwd_dy_2^{dy_log2}", B=1, S=300, E=512, C=1, Hq=4, Hkv=2, seed=79,
+                 kind="backward")
+    inp = make_inputs(w)
+    inp["dy"] = inp["dy"] * np.float32(2.0 ** dy_log2)
+    check_backward(w, inp)
+
+
+def test_backward_small_input():
+    """x scaled by 2^-12 (Q'', K'' and V' of order 2^-12)."""
+    w = Workload("bf16_bwd_x_small", B=1, S=300, E=512, C=1, Hq=4, Hkv=2, seed=80,
+                 kind="backward")
+    inp = make_inputs(w)
+    inp["x"] = inp["x"] * np.float32(2.0 ** -12)
+    check_backward(w, inp)
 
 
 def test_backward_is_deterministic():

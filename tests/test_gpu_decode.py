@@ -105,6 +105,51 @@ def test_decode_ccgqa_32k_full_size():
     assert torch.equal(kc[:, :, :p], dev(inp["k_cache"][:, :, :p], w))
 
 
+def test_decode_ragged_positions_32k_cache():
+    """One batch whose sequences sit at different positions over a seeded
+    32768-token cache: a new sequence (pos 0), the first blocks' edges (1, 31,
+    32, 33), a mid-length one (1000) and the last slot of the capacity (32767).
+    Cache slots past each sequence's position hold random values, so a read past
+    a sequence's keys would change its output.  y, the written cache rows and
+    the advanced state against the oracle, and every other cache row untouched."""
+    positions = [0, 1, 31, 32, 33, 1000, 32767]
+    w = Workload("ccgqa_decode_ragged", B=len(positions), S=32767, E=2048, C=4, Hq=4, Hkv=2,
+                 seed=44, kind="decode", max_seq_len=32768)
+    say(f"[decode ragged] {w} positions {positions}")
+    inp = make_inputs(w)
+    pos = np.asarray(positions, np.int32)
+    layer = layer_of(w)
+    wts = dev_weights(inp, w)
+    kc = dev(inp["k_cache"], w)
+    vc = dev(inp["v_cache"], w)
+    kc0, vc0 = kc.clone(), vc.clone()
+    st = dev(inp["state"], w)
+    xn = dev(inp["x_new"], w)
+    y = layer.decode_step(wts, xn, positions, kc, vc, st)
+    torch.cuda.synchronize()
+    y_ref, kc_ref, vc_ref, st_ref = O.decode_step(inp["x_new"], params_of(inp), spec_of(w),
+                                                  inp["k_cache"], inp["v_cache"], inp["state"],
+                                                  pos)
+    bi = np.arange(w.B)
+    tbi, tpos = torch.as_tensor(bi, device="cuda"), torch.as_tensor(pos.astype(np.int64),
+                                                                     device="cuda")
+    errs = {"y": rel(host(y), y_ref),
+            "k": rel(host(kc[tbi, :, tpos]), kc_ref[bi, :, pos]),
+            "v": rel(host(vc[tbi, :, tpos]), vc_ref[bi, :, pos]),
+            "state": rel(host(st), st_ref)}
+    per_seq = [rel(host(y[b]), y_ref[b]) for b in range(w.B)]
+    say(f"  rel errors {errs}; y per sequence {['%.1e' % e for e in per_seq]}")
+    for k, e in errs.items():
+        assert e <= TOL["bf16"], (k, e)
+    for b, e in enumerate(per_seq):
+        assert e <= TOL["bf16"], (positions[b], e)
+    # every cache row other than (b, pos[b]) is untouched
+    for b, p in enumerate(positions):
+        for c, c0 in ((kc, kc0), (vc, vc0)):
+            assert torch.equal(c[b, :, :p], c0[b, :, :p]), (b, p)
+            assert torch.equal(c[b, :, p + 1:], c0[b, :, p + 1:]), (b, p)
+
+
 def test_decode_rejects_positions_beyond_capacity():
     import compressed_latent_attention_amd as cca
     w = Workload("bf16_cap", B=1, S=4, E=512, C=1, Hq=4, Hkv=2, seed=57, max_seq_len=8)
