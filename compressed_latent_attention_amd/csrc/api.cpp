@@ -115,7 +115,7 @@ DecodeLayout decode_layout(const Dims& dm, long B) {
 }
 
 struct BwdLayout {
-  size_t dO, Dsum, dq, dk, dv, dqkv, part, scratch, trans, tapT;
+  size_t dO, Dsum, dq, dk, dv, dqkv, part, scratch, trans, tapT, amax;
   size_t wT, tA, tB, gpart;   // bf16 backward GEMMs: transposed operands, split-K partials
   size_t total;
 };
@@ -139,6 +139,7 @@ BwdLayout bwd_layout(const Dims& dm, long B, long S) {
   L.scratch = o; o = align256(o + mix_bwd_scratch_floats(dm, (int)B, (int)S) * 4);
   L.trans = o;   o = align256(o + attn_bwd_transpose_bytes(dm, (int)B, (int)S));
   L.tapT = o;    o = align256(o + mix_bwd_tapT_bytes(dm));
+  L.amax = o;    o = align256(o + (kAmaxParts + 1) * 4);   // dO absmax partials, then 2^-e
   L.wT = L.tA = L.tB = L.gpart = o;
   if (bwd_gemm_nt(dm)) {
     const size_t Mp = (size_t)pad64(B * S);
@@ -606,6 +607,8 @@ cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, cons
     ab.dm = dm; ab.B = B; ab.S = S;
     ab.q = qr; ab.k = kr; ab.v = vs; ab.o32 = o32; ab.dO = dO; ab.lse = lse; ab.Dsum = Dsum;
     ab.dq = dq; ab.dk = dk; ab.dv = dv;
+    ab.amax_part = (float*)(wb + L.amax);
+    ab.dscale = ab.amax_part + kAmaxParts;
     {
       // fp16 copies for the MFMA path: Q'' | K'' | V' | dO, each 256-byte aligned
       const long sp = pad64(S);

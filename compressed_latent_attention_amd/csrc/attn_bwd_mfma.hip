@@ -26,9 +26,15 @@
 //           dP^T = V dO^T and dS; consumers stage the K / V tiles and add
 //           dQ += dS K one step behind.
 // Every product is a v_mfma_f32_32x32x16_f16 with fp32 accumulation.  The fp16
-// copies hold the stored bf16 values exactly while they lie in fp16's normal
-// range (|x| in [2^-14, 65504]; smaller gradients would need a loss scale); P
-// and dS are rounded to fp16 (11 significant bits).  dS = P (dP - D) has rows
+// copies of Q'', K'' and V' hold the stored bf16 values exactly while they lie
+// in fp16's normal range (|x| in [2^-14, 65504]; below it a value keeps an
+// absolute error under 2^-25).  dO is different: the upstream gradient of a
+// loss averaged over many tokens is tiny (2^-20 and less), so its copy is
+// taken as dO * 2^e with e chosen per call from max|dO| (an absmax pass before
+// prep) to put that maximum in [4, 8).  D, dP, dS, dV, dQ and dK are all
+// linear in dO and scale with it; the epilogues multiply by 2^-e.  Both
+// scalings are exact, and dS = P (dP - D) stays in fp16's range for value rows
+// of norm up to ~360.  P and dS are rounded to fp16 (11 significant bits).  dS = P (dP - D) has rows
 // that sum to zero, so dQ and dK cancel heavily; bf16 dS (8 bits) would cost
 // ~1% in them.  The transposed operands (Q^T and dO^T of dK and dV, K^T of dQ)
 // are read from the natural LDS tiles with ds_read_b64_tr_b16, so only natural
@@ -131,6 +137,34 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// ------------------------------------------------------------------ dO scale
+// max|dO| over the whole [B*S, nq] tensor, per work-group (grid-stride over
+// 16-byte chunks); prep combines the kAmaxParts partials.
+__global__ __launch_bounds__(256) void bwd_do_absmax_kernel(const bf16* dO, long n8,
+                                                            float* part) {
+  __shared__ float red[4];
+  float m = 0.0f;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
+    const bf16x8 v = reinterpret_cast<const bf16x8*>(dO)[i];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)v[e]));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// 2^e with e such that m * 2^e lies in [4, 8) (1 for m = 0), clamped so both
+// 2^e and 2^-e are normal fp32 numbers.
+__device__ __forceinline__ int do_scale_exp(float m) {
+  if (!(m > 0.0f)) return 0;
+  int k;
+  frexpf(m, &k);                       // m in [2^(k-1), 2^k)
+  return min(max(3 - k, -120), 120);
+}
+
 // ------------------------------------------------------------------ prep
 // 64 tokens of one head per work-group.  blockIdx.y: 0..Hq-1 -> Q'' and dO of
 // head y (and D); Hq.. -> K'' and V' of KV head y - Hq.
@@ -148,6 +182,21 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnBwdArgs a) {
   const long ld1 = is_q ? dm.nq : D;
   f16* dst0 = reinterpret_cast<f16*>(is_q ? a.q16 : a.k16) + hrow * sp * D;
   f16* dst1 = reinterpret_cast<f16*>(is_q ? a.do16 : a.v16) + hrow * sp * D;
+  // dO's scale 2^e from the absmax partials (every Q work-group reduces them
+  // alike; the first one publishes 2^-e for the dK / dV and dQ epilogues)
+  float dscale = 1.0f;
+  if (is_q) {
+    __shared__ float red[4];
+    float m = a.amax_part[threadIdx.x];            // kAmaxParts == blockDim.x
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int e = do_scale_exp(m);
+    dscale = ldexpf(1.0f, e);
+    if (blockIdx.x == 0 && y == 0 && b == 0 && threadIdx.x == 0) a.dscale[0] = ldexpf(1.0f, -e);
+  }
   // thread -> (row, 8 channels), four rows apart; every load is issued before
   // the first store (the copies may not alias the sources as far as the
   // compiler knows, so a load-convert-store loop would run its four memory
@@ -172,7 +221,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnBwdArgs a) {
     const int f = threadIdx.x + 256 * i;
     const int t = t0 + (f >> 4), c = (f & 15) * 8;
     *reinterpret_cast<f16x8*>(dst0 + (long)t * D + c) = to_f16(v[i]);
-    *reinterpret_cast<f16x8*>(dst1 + (long)t * D + c) = to_f16(w[i]);
+    f16x8 o;                               // V' as stored, or dO * 2^e
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (f16)((float)w[i][e] * dscale);
+    *reinterpret_cast<f16x8*>(dst1 + (long)t * D + c) = o;
   }
   // D_t = <dO_t, O_t> in fp32: each thread sums 32 channels of one token
   if (is_q) {
@@ -187,7 +239,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnBwdArgs a) {
     }
     sacc += __shfl_xor(sacc, 1);
     sacc += __shfl_xor(sacc, 2);
-    if (part == 0 && t < S) a.Dsum[hrow * S + t] = sacc;
+    if (part == 0 && t < S) a.Dsum[hrow * S + t] = sacc * dscale;
   }
 }
 
@@ -368,7 +420,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
       }
       lds_barrier();                               // the consumers' last step
     }
-    const float inv = 1.0f / sqrtf((float)D);
+    const float inv = a.dscale[0] / sqrtf((float)D);   // 2^-e exactly, then 1/sqrt(d)
     float* dkb = (part == 0 ? a.dk : part == 1 ? a.dk2 : part == 2 ? a.dk3 : a.dk4) + kvrow * S * D;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -431,12 +483,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
       }
     }
     float* dvb = (part == 0 ? a.dv : part == 1 ? a.dv2 : part == 2 ? a.dv3 : a.dv4) + kvrow * S * D;
+    const float unscale = a.dscale[0];               // 2^-e: exact
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (key < S) dvb[(long)key * D + nb * 32 + l32] = dv[nb][r];
+        if (key < S) dvb[(long)key * D + nb * 32 + l32] = dv[nb][r] * unscale;
       }
   }
 }
@@ -641,7 +694,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
       if (s + 1 <= nsteps) iter(s + 1, r0);
     }
     // D layout: lane holds channel nb*32 + l32, query rows 8 (r/4) + 4 hi + r%4
-    const float inv = 1.0f / sqrtf((float)D);
+    const float inv = a.dscale[0] / sqrtf((float)D);   // 2^-e exactly, then 1/sqrt(d)
     float* dqb = a.dq + hrow * S * D;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -677,6 +730,10 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   // 32-bit byte offsets within one sequence's token-major dO rows
   if ((long)a.S * dm.nq * 2 >= (1L << 31)) return hipErrorInvalidValue;
+  if (!a.amax_part || !a.dscale || dm.nq % 8 != 0) return hipErrorInvalidValue;
+  const long n8 = (long)a.B * a.S * dm.nq / 8;
+  hipLaunchKernelGGL(bwd_do_absmax_kernel, dim3(kAmaxParts), dim3(256), 0, s,
+                     reinterpret_cast<const bf16*>(a.dO), n8, a.amax_part);
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(a.s_pad / 64, dm.Hq + dm.Hkv, a.B), dim3(256), 0, s,
                      a);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(nparts * ((a.S + 127) / 128), dm.Hkv, a.B), dim3(512),

@@ -211,7 +211,16 @@ struct AttnBwdArgs {
   float* dk4;
   float* dv4;
   bool sum_by_consumer;
+  // MFMA path: dO enters its fp16 copy multiplied by 2^e, chosen from max|dO|
+  // so the copy and dS stay inside fp16's normal range whatever the size of the
+  // upstream gradient; every product is linear in dO, so the fp32 results are
+  // multiplied by 2^-e on the way out (both scalings exact).  amax_part holds
+  // the per-work-group maxima of an absmax pass (kAmaxParts floats); dscale[0]
+  // receives 2^-e.
+  float* amax_part;
+  float* dscale;
 };
+constexpr int kAmaxParts = 256;
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 // True when launch_attn_bwd takes the MFMA kernels (bf16, d = 128), which
 // produce the dk2 / dv2 second-half partials.

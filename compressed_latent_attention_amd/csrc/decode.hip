@@ -8,9 +8,9 @@
 // each cache byte is read once per step.  The 4 nsplit waves of one (b, g)
 // take its 32-key blocks round robin, so together they sweep its K and V as
 // one window; every wave keeps its own online softmax:
-//   1. S = Q K^T on MFMA: A = the G queries (rows, padded to 32 with zeros,
-//      scaled to log2 units), B = K^T straight from global memory (lane = key,
-//      16 bytes of its row per load).
+//   1. S = Q K^T on MFMA: A = the G queries as stored (rows, padded to 32
+//      with zeros), B = K^T straight from global memory (lane = key, 16 bytes
+//      of its row per load); the fp32 scores are then scaled to log2 units.
 //   2. Block max over the 32 keys by DPP and a swizzle, rescale of the running
 //      O and l, p = exp2(s - m) to a per-wave LDS row block.
 //   3. O += P V on the vector ALU: lane = 8 channels of one of 4 keys, so a
@@ -92,8 +92,10 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, nkeys * D * 2, 0x00020000);
 
   // S = Q K^T on MFMA.  A operand: lane (l32 = query row, hi) holds channels
-  // 16 ks + 8 hi + 0..7 of query g*G + l32 (zero rows past G), scaled to log2
-  // units; B operand: lane (l32 = key, hi) holds the same channels of its key.
+  // 16 ks + 8 hi + 0..7 of query g*G + l32 as stored (zero rows past G); B
+  // operand: lane (l32 = key, hi) holds the same channels of its key.  The
+  // fp32 scores are scaled to log2 units (log2(e) / sqrt(d)) before the
+  // softmax, so Q is not rounded a second time.
   // D[query][key]: lane holds key l32, query rows 4 hi + r in acc[r], r < 4.
   const float scale = 1.44269504088896340736f / sqrtf((float)D);
   bf16x8 qf[8];
@@ -101,12 +103,9 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
     const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + ((long)b * dm.Hq + g * G + l32) * D;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      bf16x8 v;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (bf16)0.0f;
-      if (l32 < G) v = *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + hi * 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)((float)v[e] * scale);
+      for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)0.0f;
+      if (l32 < G) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + hi * 8);
     }
   }
   // P V on the vector ALU: lane = (key slot L / 16, channels 8 (L % 16) .. + 7)
@@ -157,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
     float p[4], al[4];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      const float s = valid ? acc[r] : -INFINITY;
+      const float s = valid ? acc[r] * scale : -INFINITY;
       float mb = s;
       mb = half_max(mb);
       const float mn = fmaxf(m[r], mb);            // finite: key 32 blk is valid

@@ -114,6 +114,18 @@ def test_status_strings():
     assert lib.cca_status_string(99) == b"unknown status"
 
 
+def test_stale_library_is_refused(monkeypatch):
+    """load() compares the source hash compiled into the library with the
+    hash of the sources beside it and raises on a mismatch."""
+    import compressed_latent_attention_amd.build as build
+    lib = cca.load()
+    assert lib.cca_source_hash().decode() == build.source_hash()
+    monkeypatch.setattr(cca, "_lib", None)
+    monkeypatch.setattr(build, "source_hash", lambda: "0" * 64)
+    with pytest.raises(ImportError, match="stale"):
+        cca.load()
+
+
 def test_invalid_config_message():
     st, msg = cca.cca_validate_config(cfg(n_kv_heads=3))
     assert st == cca.CCA_ERR_INVALID_CONFIG and "n_kv_heads" in msg
