@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcca.so")
 
 CCA_OK, CCA_ERR_INVALID_CONFIG, CCA_ERR_INVALID_ARG, CCA_ERR_UNSUPPORTED = 0, 1, 2, 3
-CCA_ERR_CAPACITY, CCA_ERR_HIP, CCA_ERR_OOM = 4, 5, 6
+CCA_ERR_CAPACITY, CCA_ERR_HIP, CCA_ERR_OOM, CCA_ERR_SCRATCH = 4, 5, 6, 7
 CCA_F32, CCA_BF16 = 0, 1
 CCA_QKMEAN_PRE, CCA_QKMEAN_POST, CCA_ROPE, CCA_VSHIFT, CCA_DEFAULT_FLAGS = 1, 2, 4, 8, 15
 CCA_OP_PREFILL, CCA_OP_DECODE, CCA_OP_BACKWARD = 0, 1, 2
@@ -61,6 +61,9 @@ _SIGNATURES = {
     "cca_decode_step": (c_int, [c_void_p, POINTER(cca_weights), c_void_p, POINTER(c_int32),
                                 c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_void_p]),
+    "cca_decode_step_noalloc": (c_int, [c_void_p, POINTER(cca_weights), c_void_p,
+                                        POINTER(c_int32), c_int32, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_void_p]),
     "cca_backward": (c_int, [c_void_p, POINTER(cca_weights), c_void_p, c_void_p, c_void_p,
                              c_int32, c_int32, POINTER(cca_grads), c_void_p, c_void_p]),
     "cca_profile_enable": (c_int, [c_void_p, c_int]),
@@ -177,6 +180,15 @@ def cca_decode_step(h, w, x_new, pos, B, k_cache, v_cache, state, y_new, workspa
                                   _ptr(v_cache), _ptr(state), _ptr(y_new), _ptr(workspace),
                                   _stream(stream)),
            "cca_decode_step")
+
+
+def cca_decode_step_noalloc(h, w, x_new, pos, B, k_cache, v_cache, state, y_new,
+                            stream=None) -> None:
+    arr = (c_int32 * B)(*[int(p) for p in pos])
+    _check(load().cca_decode_step_noalloc(h, byref(_weights(w)), _ptr(x_new), arr, B,
+                                          _ptr(k_cache), _ptr(v_cache), _ptr(state),
+                                          _ptr(y_new), _stream(stream)),
+           "cca_decode_step_noalloc")
 
 
 def cca_backward(h, w, x, dy, saved, B, S, grads, workspace, stream=None) -> None:

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -28,12 +29,43 @@ struct cca_handle {
   Dims dm;
   float2* rope = nullptr;     // [max_seq_len][d/2] (cos, sin)
   int device = 0;
+  void* scratch = nullptr;    // this device's copy of `scratch` (below), or null
   bool profiling = false;
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> pool;
 };
 
+// Workspace of cca_decode_step_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host it names a stand-in, not device memory):
+// cca_create resolves each device's address once with hipGetSymbolAddress
+// and every use goes through that pointer.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];          // resolved address per device
+bool g_scratch_done[kMaxDevices];
+
+// The current device's scratch address (resolved on first use per device),
+// or null if the lookup failed.
+void* device_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_done[device]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      ptr = nullptr;
+    }
+    g_scratch_ptr[device] = ptr;
+    g_scratch_done[device] = true;
+  }
+  return g_scratch_ptr[device];
+}
 
 void put_msg(char* msg, size_t len, const char* fmt, ...) {
   if (!msg || len == 0) return;
@@ -153,10 +185,12 @@ BwdLayout bwd_layout(const Dims& dm, long B, long S) {
   return L;
 }
 
-// Runs one launch, bracketed by timing events when profiling is on.
+// Runs one launch, bracketed by timing events when profiling is on (never for
+// the allocation-free entry point, whose `h` is null here: event creation may
+// allocate).
 template <typename F>
 hipError_t timed(cca_handle* h, const char* name, hipStream_t s, F&& launch) {
-  if (!h->profiling) return launch();
+  if (!h || !h->profiling) return launch();
   ProfRec r{name, nullptr, nullptr};
   for (hipEvent_t* e : {&r.start, &r.stop}) {
     if (!h->pool.empty()) {
@@ -217,6 +251,7 @@ const char* cca_status_string(cca_status s) {
     case CCA_ERR_CAPACITY: return "position or length exceeds max_seq_len";
     case CCA_ERR_HIP: return "HIP runtime error";
     case CCA_ERR_OOM: return "out of device memory";
+    case CCA_ERR_SCRATCH: return "workspace needed exceeds the static scratch area";
   }
   return "unknown status";
 }
@@ -297,6 +332,7 @@ cca_status cca_create(const cca_config* cfg, cca_handle** out) {
   h->cfg = *cfg;
   h->dm = make_dims(*cfg);
   if (hipGetDevice(&h->device) != hipSuccess) { delete h; return CCA_ERR_HIP; }
+  h->scratch = device_scratch(h->device);
   // RoPE angles p * base^(-2i/d) in float64, stored as fp32 cos/sin pairs
   const int half = h->dm.d / 2;
   const size_t n = (size_t)cfg->max_seq_len * half;
@@ -425,9 +461,15 @@ cca_status cca_forward_prefill(cca_handle* h, const cca_weights* w, const void* 
   }
 }
 
-cca_status cca_decode_step(cca_handle* h, const cca_weights* w, const void* x_new,
-                           const int32_t* pos_host, int32_t B, void* k_cache, void* v_cache,
-                           void* state, void* y_new, void* workspace, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One decode step (both entry points).  th is the handle events are recorded
+// into, or null (no timing).
+cca_status decode_step(cca_handle* h, cca_handle* th, const cca_weights* w, const void* x_new,
+                       const int32_t* pos_host, int32_t B, void* k_cache, void* v_cache,
+                       void* state, void* y_new, void* workspace, void* stream) {
   try {
     if (!h || !w || !x_new || !pos_host || !k_cache || !v_cache || !state || !y_new || !workspace)
       return CCA_ERR_INVALID_ARG;
@@ -462,7 +504,7 @@ cca_status cca_decode_step(cca_handle* h, const cca_weights* w, const void* x_ne
     };
     // the fused mix sums the skinny GEMM's K-slice partials itself (no reduce launch)
     SkinnyPartials sp{qkv, 1, 0, dm.nqkv};
-    CCA_TRY_HIP(timed(h, "decode_proj_down", s, [&] {
+    CCA_TRY_HIP(timed(th, "decode_proj_down", s, [&] {
       hipError_t e = hipSuccess;
       if (mix_decode_fused_ok(dm) && launch_gemm_skinny(gd, true, gpart, s, &e, &sp)) return e;
       sp = SkinnyPartials{qkv, 1, 0, dm.nqkv};
@@ -475,7 +517,7 @@ cca_status cca_decode_step(cca_handle* h, const cca_weights* w, const void* x_ne
     md.conv_q = w->conv_q; md.conv_k = w->conv_k; md.rope = h->rope;
     md.state = state; md.k_cache = k_cache; md.v_cache = v_cache; md.q_out = qn;
     md.cv = (float*)(base + L.cv);
-    CCA_TRY_HIP(timed(h, "decode_mix", s, [&] { return launch_mix_decode(md, s); }));
+    CCA_TRY_HIP(timed(th, "decode_mix", s, [&] { return launch_mix_decode(md, s); }));
 
     AttnArgs aa{};
     aa.dm = dm; aa.B = B; aa.Sq = 1;
@@ -483,10 +525,10 @@ cca_status cca_decode_step(cca_handle* h, const cca_weights* w, const void* x_ne
     aa.kv_bs = (long)dm.Hkv * dm.max_seq_len * dm.d; aa.kv_hs = (long)dm.max_seq_len * dm.d;
     aa.o = on; aa.lse = nullptr; aa.decode = true; aa.pos = pos;
     aa.part = (float*)(base + L.part); aa.nsplit = decode_nsplit(dm, B);
-    CCA_TRY_HIP(timed(h, "decode_attn", s, [&] { return launch_attn_decode(aa, s); }));
+    CCA_TRY_HIP(timed(th, "decode_attn", s, [&] { return launch_attn_decode(aa, s); }));
 
     GemmArgs gu = gemm_nt(B, dm.E, dm.nq, on, dm.nq, w->w_o, dm.nq, y_new, dm.E);
-    CCA_TRY_HIP(timed(h, "decode_proj_up", s, [&] { return gemm_decode(gu, false); }));
+    CCA_TRY_HIP(timed(th, "decode_proj_up", s, [&] { return gemm_decode(gu, false); }));
     return CCA_OK;
   } catch (const std::bad_alloc&) {
     return CCA_ERR_OOM;
@@ -494,6 +536,32 @@ cca_status cca_decode_step(cca_handle* h, const cca_weights* w, const void* x_ne
     return CCA_ERR_HIP;
   }
 }
+
+}  // namespace
+
+extern "C" {
+
+cca_status cca_decode_step(cca_handle* h, const cca_weights* w, const void* x_new,
+                           const int32_t* pos_host, int32_t B, void* k_cache, void* v_cache,
+                           void* state, void* y_new, void* workspace, void* stream) {
+  return decode_step(h, h, w, x_new, pos_host, B, k_cache, v_cache, state, y_new, workspace,
+                     stream);
+}
+
+cca_status cca_decode_step_noalloc(cca_handle* h, const cca_weights* w, const void* x_new,
+                                   const int32_t* pos_host, int32_t B, void* k_cache,
+                                   void* v_cache, void* state, void* y_new, void* stream) {
+  if (!h) return CCA_ERR_INVALID_ARG;
+  if (B < 1) return CCA_ERR_INVALID_ARG;
+  if (B > kMaxDecodeBatch) return CCA_ERR_UNSUPPORTED;
+  if (decode_layout(h->dm, B).total > kScratchBytes) return CCA_ERR_SCRATCH;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return CCA_ERR_INVALID_ARG;
+  if (!h->scratch) return CCA_ERR_HIP;
+  return decode_step(h, nullptr, w, x_new, pos_host, B, k_cache, v_cache, state, y_new,
+                     h->scratch, stream);
+}
+
 
 cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, const void* dy,
                         const void* saved, int32_t B, int32_t S, const cca_grads* g,

@@ -55,7 +55,8 @@ typedef enum {
   CCA_ERR_UNSUPPORTED = 3,     /* valid config this build has no kernel for */
   CCA_ERR_CAPACITY = 4,        /* a position or length exceeds max_seq_len */
   CCA_ERR_HIP = 5,             /* HIP runtime error */
-  CCA_ERR_OOM = 6              /* cca_create could not allocate its table */
+  CCA_ERR_OOM = 6,             /* cca_create could not allocate its table */
+  CCA_ERR_SCRATCH = 7          /* the call needs more than the static scratch area */
 } cca_status;
 
 typedef enum { CCA_F32 = 0, CCA_BF16 = 1 } cca_dtype;   /* accumulation is fp32 */
@@ -174,6 +175,23 @@ cca_status cca_forward_prefill(cca_handle* h, const cca_weights* w, const void* 
 cca_status cca_decode_step(cca_handle* h, const cca_weights* w, const void* x_new,
                            const int32_t* pos_host, int32_t B, void* k_cache, void* v_cache,
                            void* state, void* y_new, void* workspace, void* stream);
+
+/* cca_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, outputs and errors as
+ * cca_decode_step; its workspace is a static device array of 16 MiB per GPU
+ * (allocated with the library's code object, held until the process ends),
+ * whose address cca_create resolves once per device.  The call allocates and
+ * frees nothing and records no timing events.  Returns CCA_ERR_SCRATCH when
+ * cca_workspace_bytes(h, CCA_OP_DECODE, B, 0) exceeds 16 MiB (the 32-sequence
+ * CCGQA step at E = 2048 needs ~1.5 MiB) and CCA_ERR_INVALID_ARG when the
+ * current device is not the handle's.  Every call on one GPU shares that
+ * GPU's array: calls that may overlap on one GPU (other streams, other
+ * threads, other handles) race and must be serialised by the caller.  The
+ * array keeps the last call's contents; no part of it needs to start at zero. */
+cca_status cca_decode_step_noalloc(cca_handle* h, const cca_weights* w, const void* x_new,
+                                   const int32_t* pos_host, int32_t B, void* k_cache,
+                                   void* v_cache, void* state, void* y_new, void* stream);
 
 /* Backward of cca_forward_prefill for L = <dy, y> (CCA-es §4, training
  * backward): x, dy [B, S, E] dt; saved: what the prefill of the same x wrote.

@@ -100,6 +100,8 @@ def test_null_arguments_are_rejected_before_any_gpu_call():
                                None) == cca.CCA_ERR_INVALID_ARG
     assert lib.cca_backward(None, None, None, None, None, 1, 1, None, None,
                             None) == cca.CCA_ERR_INVALID_ARG
+    assert lib.cca_decode_step_noalloc(None, None, None, None, 1, None, None, None, None,
+                                       None) == cca.CCA_ERR_INVALID_ARG
     assert lib.cca_workspace_bytes(None, 0, 1, 1) == 0
     assert lib.cca_saved_bytes(None, 1, 1) == 0
     assert lib.cca_state_bytes(None, 1) == 0
@@ -109,7 +111,7 @@ def test_null_arguments_are_rejected_before_any_gpu_call():
 
 def test_status_strings():
     lib = cca.load()
-    for s in range(7):
+    for s in range(8):
         assert lib.cca_status_string(s)
     assert lib.cca_status_string(99) == b"unknown status"
 
