@@ -139,6 +139,66 @@ def bench_prefill(args, torch, cca, w, inp):
     return elapsed, elapsed_prof, prof, layer, warm_steps
 
 
+def mix_bytes(w) -> dict:
+    """Algorithmic HBM bytes of the mix over one prefill: the bf16 latent
+    q~|k~|v~ read once, the conv taps, and Q'', K'', V' written once; plus the
+    fp32 cos/sin rows of the RoPE table this implementation reads (listed
+    apart)."""
+    d, nq, nk = w.d, w.Hq * w.d, w.Hkv * w.d
+    tokens = w.B * w.S
+    return {"latent_in": tokens * (nq + 2 * nk) * 2.0,
+            "taps": (w.Hq * w.kq + w.Hkv * w.kk) * d * d * 2.0,
+            "out": tokens * (nq + 2 * nk) * 2.0,
+            "rope_table": w.S * (d // 2) * 8.0}
+
+
+def bench_mix_cold(args, torch, cca, w, inp):
+    """The mix kernel of the 16k prefill timed alone with cold caches: before
+    each timed launch the library writes a 1 GiB buffer (evicting L2 and the
+    256 MB MALL), so its inputs come from HBM."""
+    dt = torch.bfloat16
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt)
+    layer = cca.CCALayer(w.E, w.C, w.Hq, w.Hkv, w.capacity, w.kq, w.kk, w.s_v, w.flags,
+                         w.rope_base, w.dtype)
+    wts = {k: dev(inp[k]) for k in ("w_q", "w_k", "w_v", "w_o", "conv_q", "conv_k")}
+    x = dev(inp["x"])
+    y = torch.empty_like(x)
+    ws = layer.workspace(cca.CCA_OP_PREFILL, w.B, w.S)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        cca.cca_forward_prefill(layer.handle, wts, x, w.B, w.S, y, None, None, None, None, ws,
+                                stream)
+
+    _time_warm(torch, step, 10)
+    cca.cca_profile_enable(layer.handle, True)
+    cca.cca_profile_flush(layer.handle, flush)
+    n = max(args.steps // 5, 5)
+    _time_loop(torch, step, n, 0)
+    prof = cca.cca_profile_read(layer.handle)
+    cca.cca_profile_flush(layer.handle, None)
+    cca.cca_profile_enable(layer.handle, False)
+    layer.close()
+    del flush
+    torch.cuda.empty_cache()
+    launches, total = prof["mix"]
+    ms = total / max(launches, 1)
+    by = mix_bytes(w)
+    alg = by["latent_in"] + by["taps"] + by["out"]
+    return {"workload": f"ccgqa_prefill_16k mix (conv, QK-mean, value shift, RoPE): S={w.S}, "
+                        f"Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}, bf16",
+            "avg_ms_cold": ms, "launches": launches,
+            "bytes_algorithmic": alg,
+            "bytes_note": "bf16 latent q~|k~|v~ read once + taps + Q'', K'', V' written once; "
+                          f"the fp32 RoPE table rows ({by['rope_table'] / 1e6:.1f} MB) not counted",
+            "GBps": alg / (ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "timing": "HIP events around each mix launch, a 1 GiB write before each (L2 and MALL "
+                      "evicted)",
+            "other_kernels_cold_ms": {k: v[1] / max(v[0], 1) for k, v in prof.items()}}
+
+
 DECODE_BYTES_NOTE = ("K and V caches over positions 0..pos of every sequence + all weights "
                      "+ x_new, y_new, the rolling state and the new cache rows")
 
@@ -410,9 +470,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--warm-s", type=float, default=0.3,
                     help="untimed prefill steps continue past --warmup until this many seconds")
-    ap.add_argument("--rows", default="prefill,decode,backward",
-                    help="comma list: prefill (headline, always run), decode, backward; n1 "
-                         "adds the MHA / GQA comparators over S = 4k .. 64k (not run by default)")
+    ap.add_argument("--rows", default="prefill,mix,decode,backward",
+                    help="comma list: prefill (headline, always run), mix (the mix kernel with "
+                         "cold caches), decode, backward; n1 adds the MHA / GQA comparators over "
+                         "S = 4k .. 64k (not run by default)")
     ap.add_argument("--bwd-steps", type=int, default=3, help="timed backward steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -481,6 +542,8 @@ def main():
         "ms_per_step_with_kernel_events": elapsed_prof * 1000.0 / args.steps,
     }
     rows = [r.strip() for r in args.rows.split(",") if r.strip()]
+    if "mix" in rows:
+        out["mix_cold"] = bench_mix_cold(args, torch, cca, w, inp)
     if "decode" in rows:
         out["decode"] = bench_decode(args, torch, cca)
     if "backward" in rows:

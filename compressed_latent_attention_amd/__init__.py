@@ -68,6 +68,7 @@ _SIGNATURES = {
                              c_int32, c_int32, POINTER(cca_grads), c_void_p, c_void_p]),
     "cca_profile_enable": (c_int, [c_void_p, c_int]),
     "cca_profile_read": (c_int, [c_void_p, POINTER(cca_kernel_time), c_int]),
+    "cca_profile_flush": (c_int, [c_void_p, c_void_p, c_size_t]),
     "cca_status_string": (c_char_p, [c_int]),
     "cca_source_hash": (c_char_p, []),
 }
@@ -202,6 +203,13 @@ def cca_backward(h, w, x, dy, saved, B, S, grads, workspace, stream=None) -> Non
 
 def cca_profile_enable(h, enable: bool) -> None:
     _check(load().cca_profile_enable(h, 1 if enable else 0), "cca_profile_enable")
+
+
+def cca_profile_flush(h, buf) -> None:
+    """Cold-cache timing: write over the torch uint8 tensor `buf` before every
+    timed launch (None turns it off)."""
+    _check(load().cca_profile_flush(h, _ptr(buf), 0 if buf is None else buf.numel()),
+           "cca_profile_flush")
 
 
 def cca_profile_read(h) -> Dict[str, tuple]:

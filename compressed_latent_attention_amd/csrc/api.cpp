@@ -31,6 +31,8 @@ struct cca_handle {
   int device = 0;
   void* scratch = nullptr;    // this device's copy of `scratch` (below), or null
   bool profiling = false;
+  void* flush_buf = nullptr;  // written before each timed launch when set
+  size_t flush_bytes = 0;
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> pool;
 };
@@ -199,6 +201,11 @@ hipError_t timed(cca_handle* h, const char* name, hipStream_t s, F&& launch) {
     } else if (hipEventCreate(e) != hipSuccess) {
       return hipErrorOutOfMemory;
     }
+  }
+  if (h->flush_buf) {
+    // evict the caches so the launch reads its inputs from HBM
+    const hipError_t e = launch_fill(h->flush_buf, h->flush_bytes, 0u, s);
+    if (e != hipSuccess) return e;
   }
   hipEventRecord(r.start, s);
   hipError_t err = launch();
@@ -419,7 +426,7 @@ cca_status cca_forward_prefill(cca_handle* h, const cca_weights* w, const void* 
     hipStream_t s = (hipStream_t)stream;
     SavedLayout L = saved_layout(dm, B, S);
     char* base = (char*)buf;
-    float* qkv = (float*)(base + L.off[0]);
+    void* qkv = base + L.off[0];
     void* qr = base + L.off[1];
     void* kr = base + L.off[2];
     void* vs = base + L.off[3];
@@ -431,17 +438,21 @@ cca_status cca_forward_prefill(cca_handle* h, const cca_weights* w, const void* 
     const int M = B * S;
 
     GemmArgs gd = gemm_down(dm, M, x, w, qkv);
-    CCA_TRY_HIP(timed(h, "proj_down", s, [&] { return launch_gemm(gd, GemmLayout::NT, dm.bf16, true, s); }));
+    // The latent q~|k~|v~ is fp32 when the call saves for the backward (whose
+    // dQ and dK amplify any rounding of it) or the storage is fp32; an
+    // inference prefill of bf16 storage keeps it in bf16 (half the bytes).
+    const bool lat_f32 = saved != nullptr || !dm.bf16;
+    CCA_TRY_HIP(timed(h, "proj_down", s, [&] { return launch_gemm(gd, GemmLayout::NT, dm.bf16, lat_f32, s); }));
 
     MixArgs ma{};
-    ma.dm = dm; ma.B = B; ma.S = S; ma.qkv = qkv;
+    ma.dm = dm; ma.B = B; ma.S = S; ma.qkv = qkv; ma.qkv_f32 = lat_f32;
     ma.conv_q = w->conv_q; ma.conv_k = w->conv_k; ma.rope = h->rope;
     ma.q_out = qr; ma.k_out = kr; ma.v_out = (saved || !mfma) ? vs : nullptr;
     ma.k_out2 = k_cache; ma.v_out2 = v_cache; ma.cap2 = dm.max_seq_len;
     ma.vt_out = vt; ma.s_pad = (int)pad64(S);
     CCA_TRY_HIP(timed(h, "mix", s, [&] { return launch_mix_fwd(ma, s); }));
     if (state)
-      CCA_TRY_HIP(timed(h, "write_state", s, [&] { return launch_write_state(dm, B, S, qkv, state, s); }));
+      CCA_TRY_HIP(timed(h, "write_state", s, [&] { return launch_write_state(dm, B, S, qkv, lat_f32, state, s); }));
 
     AttnArgs aa{};
     aa.dm = dm; aa.B = B; aa.Sq = S;
@@ -761,6 +772,14 @@ cca_status cca_profile_enable(cca_handle* h, int enable) {
   for (auto& r : h->recs) { h->pool.push_back(r.start); h->pool.push_back(r.stop); }
   h->recs.clear();
   h->profiling = enable != 0;
+  return CCA_OK;
+}
+
+cca_status cca_profile_flush(cca_handle* h, void* buf, size_t bytes) {
+  if (!h) return CCA_ERR_INVALID_ARG;
+  if (buf && (!aligned16(buf) || bytes % 16 != 0 || bytes == 0)) return CCA_ERR_INVALID_ARG;
+  h->flush_buf = buf;
+  h->flush_bytes = buf ? bytes : 0;
   return CCA_OK;
 }
 

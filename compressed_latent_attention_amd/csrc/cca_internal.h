@@ -97,14 +97,17 @@ hipError_t launch_splitk_reduce(const float* part, int ksplit, int M, int N, flo
 
 // ------------------------------------------------------------------ mix
 // Causal conv + QK-mean + value shift + RoPE over a prefill.
-//   qkv [B*S, nqkv] (q~ | k~ | v~); rope [max_seq_len, d/2] float2 (cos, sin).
+//   qkv [B*S, nqkv] (q~ | k~ | v~), fp32 when qkv_f32 else bf16 (bf16 storage
+//   only: the latent of an inference prefill; one that saves for the backward
+//   keeps fp32); rope [max_seq_len, d/2] float2 (cos, sin).
 //   Outputs (row stride in tokens given by *_ld, batch stride by *_bs elems):
 //   q_out [B, Hq, S, d]; k_out, v_out [B, Hkv, ld, d].  k2/v2 optional second
 //   destination (the cache) with its own row capacity.
 struct MixArgs {
   Dims dm;
   int B, S;
-  const float* qkv;
+  const void* qkv;
+  bool qkv_f32;
   const void* conv_q;
   const void* conv_k;
   const float2* rope;
@@ -123,8 +126,8 @@ hipError_t launch_mix_fwd(const MixArgs& a, hipStream_t s);
 bool prefill_uses_mfma(const Dims& dm);
 
 // Writes the rolling state after the last token of each sequence.
-hipError_t launch_write_state(const Dims& dm, int B, int S, const float* qkv, void* state,
-                              hipStream_t s);
+hipError_t launch_write_state(const Dims& dm, int B, int S, const void* qkv, bool qkv_f32,
+                              void* state, hipStream_t s);
 
 // Decode: one token per sequence; reads/updates state, writes the cache row
 // pos[b] and q_out [B, Hq, d].
@@ -258,5 +261,9 @@ size_t mix_bwd_tapT_bytes(const Dims& dm);
 bool mix_bwd_adds_dkdv2(const Dims& dm);
 size_t mix_bwd_part_floats(const Dims& dm, int B, int S);
 size_t mix_bwd_scratch_floats(const Dims& dm, int B, int S);
+
+// ------------------------------------------------------------------ utilities
+// Fills `bytes` (a multiple of 16, 16-byte aligned) at p with the 32-bit v.
+hipError_t launch_fill(void* p, size_t bytes, uint32_t v, hipStream_t s);
 
 }  // namespace cca

@@ -27,6 +27,10 @@ template <typename T>
 __device__ __forceinline__ void stf(void* p, long i, float v) {
   reinterpret_cast<T*>(p)[i] = (T)v;
 }
+// Element i of the latent: fp32, or bf16 (the inference latent).
+__device__ __forceinline__ float lat(const void* p, bool f32, long i) {
+  return f32 ? reinterpret_cast<const float*>(p)[i] : (float)reinterpret_cast<const bf16*>(p)[i];
+}
 
 constexpr int TT = 4;   // tokens per work-group in the generic prefill mix
 
@@ -72,7 +76,8 @@ __global__ __launch_bounds__(256) void mix_fwd_simple(MixArgs a) {
     const int r = i / (NH * d), hh = (i / d) % NH, c = i % d;
     const int t = t0 - (KM - 1) + r;
     const int col = hh < G ? (g * G + hh) * d : dm.nq + g * d;
-    u[i] = (t >= 0 && t < a.S) ? a.qkv[(long)(b * a.S + t) * dm.nqkv + col + c] : 0.0f;
+    u[i] = (t >= 0 && t < a.S) ? lat(a.qkv, a.qkv_f32, (long)(b * a.S + t) * dm.nqkv + col + c)
+                               : 0.0f;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < TT * NH * d; i += blockDim.x) {
@@ -114,17 +119,17 @@ __global__ __launch_bounds__(256) void mix_fwd_simple(MixArgs a) {
     const long vcol = dm.nq + dm.nk + g * d + c;
     float v;
     if (shifted)
-      v = t > 0 ? a.qkv[(long)(b * a.S + t - 1) * dm.nqkv + vcol] : 0.0f;
+      v = t > 0 ? lat(a.qkv, a.qkv_f32, (long)(b * a.S + t - 1) * dm.nqkv + vcol) : 0.0f;
     else
-      v = a.qkv[(long)(b * a.S + t) * dm.nqkv + vcol];
+      v = lat(a.qkv, a.qkv_f32, (long)(b * a.S + t) * dm.nqkv + vcol);
     stf<T>(a.v_out, ((long)(b * dm.Hkv + g) * a.S + t) * d + c, v);
     if (a.v_out2) stf<T>(a.v_out2, ((long)(b * dm.Hkv + g) * a.cap2 + t) * d + c, v);
   }
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void write_state_kernel(Dims dm, int S, const float* qkv,
-                                                          void* state) {
+__global__ __launch_bounds__(256) void write_state_kernel(Dims dm, int S, const void* qkv,
+                                                          bool qkv_f32, void* state) {
   const int b = blockIdx.x;
   const int nqpart = (dm.kq - 1) * dm.nq, nkpart = (dm.kk - 1) * dm.nk;
   for (int i = threadIdx.x; i < dm.state_w; i += blockDim.x) {
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(256) void write_state_kernel(Dims dm, int S, const 
       col = dm.nq + dm.nk + (i - nqpart - nkpart);
     }
     const int t = S - lag;
-    const float v = t >= 0 ? qkv[(long)(b * S + t) * dm.nqkv + col] : 0.0f;
+    const float v = t >= 0 ? lat(qkv, qkv_f32, (long)(b * S + t) * dm.nqkv + col) : 0.0f;
     stf<T>(state, (long)b * dm.state_w + i, v);
   }
 }
@@ -557,14 +562,16 @@ __global__ __launch_bounds__(1024) void mix_decode_fused_kernel(MixDecodeArgs a)
 
 }  // namespace
 
-hipError_t launch_mix_fwd_mfma(const MixArgs& a, hipStream_t s);   // mix_mfma.hip
+hipError_t launch_mix_fwd_mfma(const MixArgs& a, hipStream_t s);          // mix_mfma.hip
+hipError_t launch_mix_fwd_mfma_f32lat(const MixArgs& a, hipStream_t s);   // mix_mfma_f32lat.hip
 bool mix_fwd_mfma_supported(const Dims& dm);
 
 bool prefill_uses_mfma(const Dims& dm) { return dm.bf16 && mix_fwd_mfma_supported(dm); }
 
 hipError_t launch_mix_fwd(const MixArgs& a, hipStream_t s) {
   const Dims& dm = a.dm;
-  if (prefill_uses_mfma(dm)) return launch_mix_fwd_mfma(a, s);
+  if (prefill_uses_mfma(dm))
+    return a.qkv_f32 ? launch_mix_fwd_mfma_f32lat(a, s) : launch_mix_fwd_mfma(a, s);
   const int KM = max(dm.kq, dm.kk);
   const size_t lds = (size_t)((TT + KM - 1) + TT) * (dm.G + 1) * dm.d * sizeof(float);
   dim3 grid((a.S + TT - 1) / TT, dm.Hkv, a.B);
@@ -575,12 +582,14 @@ hipError_t launch_mix_fwd(const MixArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_write_state(const Dims& dm, int B, int S, const float* qkv, void* state,
-                              hipStream_t s) {
+hipError_t launch_write_state(const Dims& dm, int B, int S, const void* qkv, bool qkv_f32,
+                              void* state, hipStream_t s) {
   if (dm.bf16)
-    hipLaunchKernelGGL(write_state_kernel<bf16>, dim3(B), dim3(256), 0, s, dm, S, qkv, state);
+    hipLaunchKernelGGL(write_state_kernel<bf16>, dim3(B), dim3(256), 0, s, dm, S, qkv, qkv_f32,
+                       state);
   else
-    hipLaunchKernelGGL(write_state_kernel<float>, dim3(B), dim3(256), 0, s, dm, S, qkv, state);
+    hipLaunchKernelGGL(write_state_kernel<float>, dim3(B), dim3(256), 0, s, dm, S, qkv, qkv_f32,
+                       state);
   return hipGetLastError();
 }
 

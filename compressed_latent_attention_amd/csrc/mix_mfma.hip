@@ -3,30 +3,85 @@
 // (§2.B.3) and RoPE (§3 item 2) in one pass per (64 tokens, KV group).
 //
 // The convolution of one head is a GEMM: out[t, c] = sum_{j, c'} u[t - j, c'] *
-// A_j[c, c'] with M = tokens, N = channels, K = k * d.  The fp32 latent tile of
-// the head (64 tokens plus the k - 1 halo tokens before them) is read with
-// coalesced 16-byte loads and staged in LDS as two bf16 halves, hi = bf16(u)
-// and lo = bf16(u - hi), each converted once; operand A is read from both, so
-// the product keeps ~16 mantissa bits of q~ and k~ with fp32 accumulation
-// (hi + lo also stands in for u in QK-mean, and V' = bf16(v~) is hi itself);
-// operand B is the bf16 tap row A_j[c, 8 channels] read from L2.  With lane = output channel and registers = tokens,
-// everything QK-mean needs (the same token and channel of the group's query
-// heads and its K head) and both channels of a RoPE pair (c, c + d/2) sit in
-// one lane.
+// A_j[c, c'] with M = tokens, N = channels, K = k * d.  The bf16 latent tiles
+// the work-group needs (k~, v~ and up to two q~ heads, 64 tokens plus a 4-row
+// halo before them, enough for k <= 4 taps and the one-token value shift) are
+// read with 16-byte buffer loads, all issued in one round at the start, so a
+// work-group waits for memory once, and stored to LDS in rows padded to 272
+// bytes: the MFMA operand reads (32 consecutive token rows, one 16-byte chunk
+// each) are free of bank conflicts and an epilogue read is a base register
+// plus a constant offset.  Operand A is read from the tile, operand B is the
+// bf16 tap row A_j[c, 8 channels] read from L2.  With lane = output channel
+// and registers = tokens, everything QK-mean needs (the same token and channel
+// of the group's query heads and its K head) sits in one lane.
 //
-// Wave w of the 4: tokens t0 + 32*(w/2) .. +31, channel blocks {w%2, w%2 + 2}.
+// Wave w of the 4 owns a quarter of the output channels, all 64 tokens: MFMA
+// column n < 16 is channel 16 w + n and column n >= 16 its RoPE partner
+// 64 + 16 w + n - 16, so a rotation pair sits in lanes l and l ^ 16 (one lane
+// swap), every tap fragment feeds the MFMAs of both 32-token blocks, and the
+// four waves together read each tap row of the group once.
+// Work-groups are numbered so the KV groups of one token tile run on the same
+// XCD (ids 8 apart): the second reads the tile's RoPE rows from that XCD's L2.
 #include "cca_internal.h"
 
 namespace cca {
 namespace {
 
 constexpr int D = 128;
-constexpr int TW = 64;               // tokens per work-group
-constexpr int ULD = D + 8;           // LDS row stride (bf16): 272 B, conflict-free b128 reads
-constexpr int UROWS = TW + kMaxConv - 1;
-constexpr int UHALF = UROWS * ULD;   // lo rows follow the hi rows
+constexpr int TW = 64;                      // tokens per work-group
+constexpr int HALO = 4;                     // staged rows before the tile (>= kMaxConv - 1)
+constexpr int TROWS = TW + HALO;            // tile row i = token t0 - HALO + i
+constexpr int ROWB = 272;                   // LDS row stride in bytes (256 + 16)
+constexpr int TBYTES = TROWS * ROWB;
+constexpr int NQS = 2;                      // q~ tiles resident at once
+constexpr int XCDS = 8;
+constexpr int CHUNKS = TROWS * (D / 8);     // 16-byte chunks per tile
 
-typedef f32x16 Acc2[2];              // [channel block]
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float tile_val(const char* tile, int r, int ch) {
+  return (float)*reinterpret_cast<const bf16*>(tile + r * ROWB + ch * 2);
+}
+
+// The latent tiles of column blocks cols[0 .. n) (128 channels each), rows
+// t0 - HALO .. t0 + TW - 1, into LDS tiles dst[0 .. n): every load of the
+// work-group is issued before the first LDS store.  Each resource spans the
+// rows inside [0, S): rows before 0 (an offset that wraps) and past S read as
+// zero without a branch.
+template <int NMAX>
+__device__ __forceinline__ void load_tiles(char* const (&dst)[NMAX], const int (&cols)[NMAX],
+                                           int n, const bf16* qkv_b, int nqkv, int S, int t0) {
+  constexpr int PER = (CHUNKS + 255) / 256;  // chunks per thread per tile
+  const int r0 = max(t0 - HALO, 0), r1 = min(S, t0 + TW);
+  bf16x8 v[NMAX][PER];
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i) {
+    if (i >= n) break;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(qkv_b + (long)r0 * nqkv + cols[i]), 0,
+        r1 > r0 ? ((r1 - r0 - 1) * nqkv + D) * 2 : 0, 0x00020000);
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = min((int)threadIdx.x + 256 * p, CHUNKS - 1);
+      const int r = e >> 4, c = e & 15;
+      const int t = t0 - HALO + r;
+      v[i][p] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, ((t - r0) * nqkv + c * 8) * 2, 0, 0));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i) {
+    if (i >= n) break;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = (int)threadIdx.x + 256 * p;
+      if (e < CHUNKS)
+        *reinterpret_cast<bf16x8*>(dst[i] + (e >> 4) * ROWB + (e & 15) * 16) = v[i][p];
+    }
+  }
+}
+
+typedef f32x16 Acc2[2];                     // [channel block]
 
 __device__ __forceinline__ void zero(Acc2& a) {
 #pragma unroll
@@ -35,61 +90,43 @@ __device__ __forceinline__ void zero(Acc2& a) {
     for (int r = 0; r < 16; ++r) a[j][r] = 0.0f;
 }
 
-// Rows t0 - halo .. t0 + TW - 1 of latent column block `col` into LDS as hi
-// (u[0 .. UHALF)) and lo (u[UHALF ..)) bf16 halves (zero outside [0, S)).  LDS
-// row i holds token t0 - halo + i.  The loads go through a buffer resource over
-// the tile's rows inside [0, S) (a row before it wraps to a huge offset):
-// out-of-range rows read as zero without a branch, so each batch of four loads is in flight
-// together before its conversions and LDS stores.
-__device__ __forceinline__ void load_tile(bf16* u, const float* qkv_b, int nqkv, int col, int S,
-                                          int t0, int halo) {
-  const int n = (TW + halo) * (D / 4);
-  // resource over the tile's rows inside [0, S), based at its first one
-  const int r0 = max(t0 - halo, 0), r1 = min(S, t0 + TW);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(qkv_b + (long)r0 * nqkv + col), 0, r1 > r0 ? ((r1 - r0 - 1) * nqkv + D) * 4 : 0,
-      0x00020000);
-  constexpr int NB = 4;
-  for (int base = 0; base < n; base += NB * 256) {
-    f32x4 v[NB];
+// acc[mb] += conv of the head whose tile is at `tile` for token block mb (A
+// rows = tokens 32 mb + l32 at lag j, tile row 32 mb + l32 - j + HALO), B =
+// taps[j][ch][c_in] for this lane's output channel ch; the 8 B fragments of a
+// lag are loaded before its MFMAs and each serves both token blocks.
+__device__ __forceinline__ void conv_head(Acc2& acc, const char* tile, const bf16* taps, int k,
+                                          int ch, int lane) {
+  const int l32 = lane & 31, hi = lane >> 5;
+  for (int j = 0; j < k; ++j) {
+    const bf16* trow = taps + ((long)j * D + ch) * D + hi * 8;
+    bf16x8 bf[8];
 #pragma unroll
-    for (int r = 0; r < NB; ++r) {
-      const int e = min(base + r * 256 + (int)threadIdx.x, n - 1);
-      const int i = e / (D / 4), ch = (e % (D / 4)) * 4;
-      const int t = t0 - halo + i;
-      v[r] = __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((t - r0) * nqkv + ch) * 4, 0, 0));
-    }
+    for (int ks = 0; ks < 8; ++ks) bf[ks] = *reinterpret_cast<const bf16x8*>(trow + ks * 16);
 #pragma unroll
-    for (int r = 0; r < NB; ++r) {
-      const int e = base + r * 256 + (int)threadIdx.x;
-      if (e < n) {
-        const int i = e / (D / 4), ch = (e % (D / 4)) * 4;
-        bf16x4 h, l;
+    for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          h[q] = (bf16)v[r][q];
-          l[q] = (bf16)(v[r][q] - (float)h[q]);
-        }
-        *reinterpret_cast<bf16x4*>(u + i * ULD + ch) = h;
-        *reinterpret_cast<bf16x4*>(u + UHALF + i * ULD + ch) = l;
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = 32 * mb + l32 - j + HALO;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(tile + row * ROWB + (2 * ks + hi) * 16);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[ks], acc[mb], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);     // keep the A reads next to their MFMAs
     }
   }
 }
 
-// cos / sin of channel pair c_lo for the 16 token rows a lane's accumulator
-// registers hold (row r: first + 8 (r / 4) + r % 4, relative to the tile), all
-// 16 loads in flight together; (1, 0) without RoPE.  Rows past the sequence
-// (nrem = tokens of the tile inside it) read the last row: no branch, and
-// their results are never stored.
-__device__ __forceinline__ void load_rope(float2 (&cs)[16], const float2* rope_t0, int first,
-                                          int c_lo, int nrem) {
+// cos / sin of RoPE pair p for the 16 tokens of token block mb a lane's
+// accumulator registers hold (register r: token 32 mb + 8 (r / 4) + 4 hi +
+// r % 4 of the tile), all 16 loads in flight together; (1, 0) without RoPE.
+// Tokens past the sequence (nrem = tokens of the tile inside it) read the last
+// row: no branch, and their results are never stored.
+__device__ __forceinline__ void load_rope(float2 (&cs)[16], const float2* rope_t0, int mb, int hi,
+                                          int p, int nrem) {
   if (rope_t0) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int tr = min(first + 8 * (r >> 2) + (r & 3), nrem - 1);
-      cs[r] = rope_t0[tr * (D / 2) + c_lo];
+      const int tr = min(32 * mb + 8 * (r >> 2) + 4 * hi + (r & 3), nrem - 1);
+      cs[r] = rope_t0[tr * (D / 2) + p];
     }
   } else {
 #pragma unroll
@@ -97,173 +134,177 @@ __device__ __forceinline__ void load_rope(float2 (&cs)[16], const float2* rope_t
   }
 }
 
-// The pre-convolution value hi + lo of LDS row i, channel c.
-__device__ __forceinline__ float uval(const bf16* u, int i, int c) {
-  return (float)u[i * ULD + c] + (float)u[UHALF + i * ULD + c];
+// RoPE of one value given its partner (lane ^ 16): lo lanes hold channel p,
+// hi lanes channel p + 64.
+__device__ __forceinline__ float rotate(float x, float2 cs, bool lo_lane) {
+  const float xp = __shfl_xor(x, 16);
+  return lo_lane ? x * cs.x - xp * cs.y : x * cs.x + xp * cs.y;
 }
 
-// acc += conv of one head whose tile is in LDS (row of token t: t - t0 + halo).
-__device__ __forceinline__ void conv_head(Acc2& acc, const bf16* u, int halo, int tw0_rel,
-                                          const bf16* taps, int k, int cb0, int lane) {
-  const int l32 = lane & 31, hi = lane >> 5;
-  for (int j = 0; j < k; ++j) {
-    const bf16* urow = u + (tw0_rel + l32 - j + halo) * ULD + hi * 8;
-    const bf16* trow0 = taps + ((long)j * D + cb0 * 32 + l32) * D + hi * 8;
-    const bf16* trow1 = trow0 + 64 * D;
-#pragma unroll 4
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(urow + ks * 16);
-      const bf16x8 alo = *reinterpret_cast<const bf16x8*>(urow + UHALF + ks * 16);
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(trow0 + ks * 16);
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(trow1 + ks * 16);
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b0, acc[0], 0, 0, 0);
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b0, acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b1, acc[1], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b1, acc[1], 0, 0, 0);
-    }
-  }
-}
-
+// GC: the group size when known at compile time (1 or 2: every q~ tile stays
+// resident, so the K side's pre-convolution group mean is read back from LDS
+// instead of being summed in registers, and the head loop unrolls), 0 for any
+// other group size.
+template <int GC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void mix_fwd_mfma_kernel(MixArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 uk[2 * UHALF];   // k~ tile (hi, lo)
-  __shared__ __attribute__((aligned(16))) bf16 uq[2 * UHALF];   // current q~ tile, then v~
+void mix_fwd_mfma_kernel(MixArgs a, int ntiles8) {
+  constexpr bool QRES = GC > 0;
+  __shared__ __attribute__((aligned(1024))) char lds[(2 + NQS) * TBYTES];
+  char* tk = lds;                            // k~ tile
+  char* tv = lds + TBYTES;                   // v~ tile
+  char* tq = lds + 2 * TBYTES;               // q~ tiles, NQS slots
   const Dims& dm = a.dm;
-  const int G = dm.G, S = a.S;
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int t0 = blockIdx.x * TW;
+  const int G = GC > 0 ? GC : dm.G, S = a.S;
+  // (tile, KV group, sequence) from the work-group id: the Hkv groups of tiles
+  // 8 i .. 8 i + 7 take ids 8 Hkv i + 8 g + (tile % 8)
+  const int per_b = ntiles8 * dm.Hkv;
+  const int b = blockIdx.x / per_b, q = blockIdx.x % per_b;
+  const int g = (q % (XCDS * dm.Hkv)) / XCDS;
+  const int tile = (q / (XCDS * dm.Hkv)) * XCDS + q % XCDS;
+  const int t0 = tile * TW;
+  if (t0 >= S) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int tw0_rel = 32 * (wave >> 1);      // this wave's first token, relative to t0
-  const int cb0 = wave & 1;                  // channel blocks cb0 and cb0 + 2
-  const float* qkv_b = a.qkv + (long)b * S * dm.nqkv;
+  const bool lo_lane = l32 < 16;
+  const int pair = 16 * wave + (l32 & 15);   // RoPE pair of this lane's channel
+  const int ch = lo_lane ? pair : pair + 64; // this lane's output channel
+  const bf16* qkv_b = reinterpret_cast<const bf16*>(a.qkv) + (long)b * S * dm.nqkv;
   const float A = (dm.flags & kQkPre) ? 0.5f : 0.0f;
   const float Bc = (dm.flags & kQkPost) ? 0.5f : 0.0f;
   const bool rope = (dm.flags & kRope) != 0;
-  const int kcol = dm.nq + g * D;
-  const int hq = dm.kq - 1, hk = dm.kk - 1;  // halo rows of the q and k tiles
-  const int c_lo = cb0 * 32 + l32;           // < 64: RoPE pair (c_lo, c_lo + 64)
-  // register r holds token tw0_rel + 8*(r/4) + 4*hi + r%4 (relative to t0)
-  auto trel = [&](int r) { return tw0_rel + 8 * (r >> 2) + 4 * hi + (r & 3); };
+  // register r of token block mb holds token 32 mb + 8*(r/4) + 4*hi + r%4 (of the tile)
+  auto trel = [&](int mb, int r) { return 32 * mb + 8 * (r >> 2) + 4 * hi + (r & 3); };
 
+  // every tile the work-group needs, in one round
+  {
+    char* const dst[2 + NQS] = {tk, tv, tq, tq + TBYTES};
+    const int cols[2 + NQS] = {dm.nq + g * D, dm.nq + dm.nk + g * D, g * G * D, (g * G + 1) * D};
+    load_tiles(dst, cols, 2 + min(G, NQS), qkv_b, dm.nqkv, S, t0);
+  }
   const float2* rope_t0 = rope ? a.rope + (long)t0 * (D / 2) : nullptr;
-  load_tile(uk, qkv_b, dm.nqkv, kcol, S, t0, hk);
   __syncthreads();
+
   Acc2 kacc, qacc, mpost, mpre;
   zero(kacc);
-  conv_head(kacc, uk, hk, tw0_rel,
-            reinterpret_cast<const bf16*>(a.conv_k) + (long)g * dm.kk * D * D, dm.kk, cb0, lane);
+  conv_head(kacc, tk, reinterpret_cast<const bf16*>(a.conv_k) + (long)g * dm.kk * D * D, dm.kk,
+            ch, lane);
   zero(mpost);
-  zero(mpre);
+  if (!QRES) zero(mpre);
 
+#pragma unroll
   for (int i = 0; i < G; ++i) {
+    __builtin_amdgcn_sched_barrier(0);         // heads one after another (registers)
     const int h = g * G + i;
-    if (i > 0) __syncthreads();              // every wave is done with the previous q tile
-    load_tile(uq, qkv_b, dm.nqkv, h * D, S, t0, hq);
-    __syncthreads();
+    if (i > 0 && i % NQS == 0) {
+      // the next q~ tiles into the slots once every wave is done with them
+      __syncthreads();
+      char* const dst[NQS] = {tq, tq + TBYTES};
+      const int cols[NQS] = {h * D, (h + 1) * D};
+      load_tiles(dst, cols, min(NQS, G - i), qkv_b, dm.nqkv, S, t0);
+      __syncthreads();
+    }
+    const char* tqi = tq + (i % NQS) * TBYTES;
     zero(qacc);
-    conv_head(qacc, uq, hq, tw0_rel,
-              reinterpret_cast<const bf16*>(a.conv_q) + (long)h * dm.kq * D * D, dm.kq, cb0,
-              lane);
-    // tile bases plus 32-bit offsets (tokens relative to t0)
-    bf16* qo = reinterpret_cast<bf16*>(a.q_out) + ((long)(b * dm.Hq + h) * S + t0) * D;
-    float2 csr[16];
-    load_rope(csr, rope_t0, trel(0), c_lo, S - t0);
+    conv_head(qacc, tqi, reinterpret_cast<const bf16*>(a.conv_q) + (long)h * dm.kq * D * D,
+              dm.kq, ch, lane);
+    bf16* qo = reinterpret_cast<bf16*>(a.q_out) + ((long)(b * dm.Hq + h) * S + t0) * D + ch;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tr = trel(r);
-      const int t = t0 + tr;
-      float x[2];
+    for (int mb = 0; mb < 2; ++mb) {
+      __builtin_amdgcn_sched_barrier(0);       // one token block at a time (registers)
+      // the same rows for every head: an opaque copy of the base keeps the
+      // compiler from hoisting these loads out of the head loop (they would
+      // hold 64 registers through every convolution)
+      const float2* rp = rope_t0;
+      asm volatile("" : "+s"(rp));
+      float2 csr[16];
+      load_rope(csr, rp, mb, hi, pair, S - t0);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int c = c_lo + 64 * cb;
-        const float qh = qacc[cb][r], kh = kacc[cb][r];
-        const float qp = uval(uq, tr + hq, c);
-        const float kp = uval(uk, tr + hk, c);
-        mpost[cb][r] += qh;
-        mpre[cb][r] += qp;
-        x[cb] = qh + A * (qp + kp) + Bc * (qh + kh);
-      }
-      if (t < S) {
-        const float2 cs = csr[r];
-        qo[tr * D + c_lo] = (bf16)(x[0] * cs.x - x[1] * cs.y);
-        qo[tr * D + c_lo + 64] = (bf16)(x[1] * cs.x + x[0] * cs.y);
+      for (int r = 0; r < 16; ++r) {
+        const int tr = trel(mb, r);
+        const float qh = qacc[mb][r], kh = kacc[mb][r];
+        const float qp = tile_val(tqi, tr + HALO, ch);
+        const float kp = tile_val(tk, tr + HALO, ch);
+        mpost[mb][r] += qh;
+        if (!QRES) mpre[mb][r] += qp;
+        const float y = rotate(qh + A * (qp + kp) + Bc * (qh + kh), csr[r], lo_lane);
+        if (t0 + tr < S) qo[tr * D] = (bf16)y;
       }
     }
   }
 
   // k' = k^ + a/2 (mean_g q~ + k~) + b/2 (mean_g q^ + k^)
+  __builtin_amdgcn_sched_barrier(0);
   const float invG = 1.0f / (float)G;
-  bf16* ko = reinterpret_cast<bf16*>(a.k_out) + ((long)(b * dm.Hkv + g) * S + t0) * D;
-  bf16* ko2 = a.k_out2
-                  ? reinterpret_cast<bf16*>(a.k_out2) + ((long)(b * dm.Hkv + g) * a.cap2 + t0) * D
-                  : nullptr;
-  float2 csr[16];
-  load_rope(csr, rope_t0, trel(0), c_lo, S - t0);
+  bf16* ko = reinterpret_cast<bf16*>(a.k_out) + ((long)(b * dm.Hkv + g) * S + t0) * D + ch;
+  bf16* ko2 = a.k_out2 ? reinterpret_cast<bf16*>(a.k_out2) +
+                             ((long)(b * dm.Hkv + g) * a.cap2 + t0) * D + ch
+                       : nullptr;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int tr = trel(r);
-    const int t = t0 + tr;
-    float x[2];
+  for (int mb = 0; mb < 2; ++mb) {
+    __builtin_amdgcn_sched_barrier(0);
+    const float2* rp = rope_t0;
+    asm volatile("" : "+s"(rp));
+    float2 csr[16];
+    load_rope(csr, rp, mb, hi, pair, S - t0);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int c = c_lo + 64 * cb;
-      const float kh = kacc[cb][r];
-      const float kp = uval(uk, tr + hk, c);
-      x[cb] = kh + A * (mpre[cb][r] * invG + kp) + Bc * (mpost[cb][r] * invG + kh);
-    }
-    if (t < S) {
-      const float2 cs = csr[r];
-      const bf16 lo = (bf16)(x[0] * cs.x - x[1] * cs.y);
-      const bf16 hv = (bf16)(x[1] * cs.x + x[0] * cs.y);
-      ko[tr * D + c_lo] = lo;
-      ko[tr * D + c_lo + 64] = hv;
-      if (ko2) {
-        ko2[tr * D + c_lo] = lo;
-        ko2[tr * D + c_lo + 64] = hv;
+    for (int r = 0; r < 16; ++r) {
+      const int tr = trel(mb, r);
+      const float kh = kacc[mb][r];
+      const float kp = tile_val(tk, tr + HALO, ch);
+      float qpre = 0.0f;
+      if (QRES) {
+        for (int i = 0; i < G; ++i) qpre += tile_val(tq + i * TBYTES, tr + HALO, ch);
+      } else {
+        qpre = mpre[mb][r];
+      }
+      const float y = rotate(kh + A * (qpre * invG + kp) + Bc * (mpost[mb][r] * invG + kh),
+                             csr[r], lo_lane);
+      if (t0 + tr < S) {
+        ko[tr * D] = (bf16)y;
+        if (ko2) ko2[tr * D] = (bf16)y;
       }
     }
   }
 
-  // value shift: v~ rows t0 - 1 .. t0 + TW - 1 into LDS (reusing the q tile),
-  // then V' in the standard layout (when asked) and transposed, V'^T[c][t]
-  __syncthreads();
-  const int vcol = dm.nq + dm.nk + g * D;
-  load_tile(uq, qkv_b, dm.nqkv, vcol, S, t0, 1);
-  __syncthreads();
+  // value shift from the v~ tile: V'[t, c] = v~[t - 1, c] for the last s_v
+  // channels (tile row tr + HALO - 1; row HALO - 1 is token t0 - 1, zero
+  // before token 0), else v~[t, c]
   const int first_shift = (dm.flags & kVShift) ? D - dm.sv : D;
+  auto vrow = [&](int tr, int c) { return tr + HALO - (c >= first_shift ? 1 : 0); };
   bf16* vo = a.v_out ? reinterpret_cast<bf16*>(a.v_out) + ((long)(b * dm.Hkv + g) * S) * D
                      : nullptr;
   bf16* vo2 = a.v_out2 ? reinterpret_cast<bf16*>(a.v_out2) + ((long)(b * dm.Hkv + g) * a.cap2) * D
                        : nullptr;
   if (vo || vo2) {
-    for (int e = threadIdx.x; e < TW * D; e += 256) {
-      const int tr = e / D, c = e % D;
+    // thread = (token, 8 channels): 16-byte stores
+    for (int e = threadIdx.x; e < TW * (D / 8); e += 256) {
+      const int tr = e / (D / 8), c8 = (e % (D / 8)) * 8;
       const int t = t0 + tr;
       if (t >= S) break;
-      const bf16 v = uq[(tr + (c >= first_shift ? 0 : 1)) * ULD + c];   // hi = bf16(v~)
-      if (vo) vo[(long)t * D + c] = v;
-      if (vo2) vo2[(long)t * D + c] = v;
+      bf16x8 v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v[i] = *reinterpret_cast<const bf16*>(tv + vrow(tr, c8 + i) * ROWB + (c8 + i) * 2);
+      if (vo) *reinterpret_cast<bf16x8*>(vo + (long)t * D + c8) = v;
+      if (vo2) *reinterpret_cast<bf16x8*>(vo2 + (long)t * D + c8) = v;
     }
   }
   if (a.vt_out) {
     // V'^T feeds only the attention's P V product, which runs in fp16 so that P
     // keeps 11 significant bits.  It holds the stored bf16 V' values, converted
-    // exactly, so the forward's O and the backward (which reads the bf16 V')
-    // see the same V'.
+    // exactly (within fp16's range), so the forward's O and the backward (which
+    // reads the bf16 V') see the same V'.
     _Float16* vt = reinterpret_cast<_Float16*>(a.vt_out) + (long)(b * dm.Hkv + g) * D * a.s_pad;
-    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
     for (int e = threadIdx.x; e < D * (TW / 8); e += 256) {
       const int c = e % D, m = e / D;
       const int t = t0 + 8 * m;
       if (t >= a.s_pad) continue;
-      const int row_off = c >= first_shift ? 0 : 1;
       f16x8 pk;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         // tokens at or past S are zero: the padding of V'^T up to s_pad
-        const bf16 v = t + i < S ? uq[(8 * m + i + row_off) * ULD + c] : (bf16)0.0f;
-        pk[i] = (_Float16)(float)v;
+        const float v = t + i < S ? tile_val(tv, vrow(8 * m + i, c), c) : 0.0f;
+        pk[i] = (_Float16)v;
       }
       *reinterpret_cast<f16x8*>(vt + (long)c * a.s_pad + t) = pk;
     }
@@ -276,8 +317,17 @@ bool mix_fwd_mfma_supported(const Dims& dm) { return dm.bf16 && dm.d == D; }
 
 hipError_t launch_mix_fwd_mfma(const MixArgs& a, hipStream_t s) {
   if (a.vt_out && (a.s_pad % 64 != 0 || a.s_pad < a.S)) return hipErrorInvalidValue;
-  dim3 grid((a.S + TW - 1) / TW, a.dm.Hkv, a.B);
-  hipLaunchKernelGGL(mix_fwd_mfma_kernel, grid, dim3(256), 0, s, a);
+  // 32-bit byte offsets within one sequence's latent rows
+  if ((long)a.S * a.dm.nqkv * 2 >= (1L << 31)) return hipErrorInvalidValue;
+  const int ntiles = (a.S + TW - 1) / TW;
+  const int ntiles8 = (ntiles + XCDS - 1) / XCDS * XCDS;
+  const dim3 grid((unsigned)(ntiles8 * a.dm.Hkv * a.B));
+  if (a.dm.G == 1)
+    hipLaunchKernelGGL(mix_fwd_mfma_kernel<1>, grid, dim3(256), 0, s, a, ntiles8);
+  else if (a.dm.G == 2)
+    hipLaunchKernelGGL(mix_fwd_mfma_kernel<2>, grid, dim3(256), 0, s, a, ntiles8);
+  else
+    hipLaunchKernelGGL(mix_fwd_mfma_kernel<0>, grid, dim3(256), 0, s, a, ntiles8);
   return hipGetLastError();
 }
 

@@ -155,7 +155,12 @@ size_t cca_state_bytes(const cca_handle* h, int32_t B);
  *     rows 0..S-1 receive K'' and V' of every token (the compressed latent
  *     cache, CCA-es §2.C).
  *   state (nullable): [B, W] dt, receives the rolling decode state after token S-1.
- *   workspace: cca_workspace_bytes(h, CCA_OP_PREFILL, B, S) bytes.
+ *   workspace: cca_workspace_bytes(h, CCA_OP_PREFILL, B, S) bytes (used only
+ *     when saved is NULL; the saved buffer serves as the workspace otherwise).
+ * Precision: with bf16 storage, a prefill that saves for the backward keeps
+ * the latent q~|k~|v~ in fp32 (the softmax gradient amplifies its rounding
+ * into dQ and dK); without saved (inference) the latent is rounded to bf16.
+ * Both stay within the bf16 parity bound on y, the cache and the state.
  * Requires 1 <= S <= max_seq_len and B >= 1 (else CCA_ERR_CAPACITY /
  * CCA_ERR_INVALID_ARG). */
 cca_status cca_forward_prefill(cca_handle* h, const cca_weights* w, const void* x, int32_t B,
@@ -215,6 +220,13 @@ typedef struct {
 } cca_kernel_time;
 cca_status cca_profile_enable(cca_handle* h, int enable);
 int cca_profile_read(cca_handle* h, cca_kernel_time* out, int max);
+/* Cold-cache timing: while timing is enabled and buf is not NULL, every timed
+ * launch is preceded (outside its events) by a write of `bytes` over the
+ * caller's device buffer buf (16-byte aligned, bytes a multiple of 16), which
+ * evicts L2 and the 256 MB MALL when bytes exceeds them, so the launch reads
+ * its inputs from HBM.  buf = NULL turns it off.  The buffer's contents are
+ * overwritten. */
+cca_status cca_profile_flush(cca_handle* h, void* buf, size_t bytes);
 
 /* Static text for a status code. */
 const char* cca_status_string(cca_status s);

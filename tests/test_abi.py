@@ -106,6 +106,7 @@ def test_null_arguments_are_rejected_before_any_gpu_call():
     assert lib.cca_saved_bytes(None, 1, 1) == 0
     assert lib.cca_state_bytes(None, 1) == 0
     assert lib.cca_profile_read(None, None, 0) == -1
+    assert lib.cca_profile_flush(None, None, 0) == cca.CCA_ERR_INVALID_ARG
     lib.cca_destroy(None)
 
 

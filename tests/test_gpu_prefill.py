@@ -25,6 +25,10 @@ from gpu_helpers import (TOL, block_rel, host, params_of, rel, run_prefill,  # n
 
 
 def check_prefill(w: Workload, inp, stages=True):
+    """Two prefills of the same x: one that saves its stages for the backward
+    (fp32 latent) and an inference one that writes the cache and the state
+    instead (bf16 latent with bf16 storage); every observable of both against
+    the oracle."""
     say(f"[prefill] {w}")
     r = run_prefill(w, inp)
     spec = spec_of(w)
@@ -32,8 +36,18 @@ def check_prefill(w: Workload, inp, stages=True):
     tol = TOL[w.dtype]
     # (GPU result, oracle, token axis) per stage
     pairs = {"y": (host(r["y"]), y_ref, 1)}
+    ri = run_prefill(w, inp, with_saved=False, with_cache=True, layer=r["layer"])
+    B, S = w.B, w.S
+    pairs["inference y"] = (host(ri["y"]), y_ref, 1)
+    pairs["inference cache K''"] = (host(ri["k_cache"])[:, :, :S],
+                                    np.stack(sv["k_rope"]).transpose(0, 2, 1, 3), 2)
+    pairs["inference cache V'"] = (host(ri["v_cache"])[:, :, :S],
+                                   np.stack(sv["v_shift"]).transpose(0, 2, 1, 3), 2)
+    st_ref = np.stack(sv["state"])
+    errs_state = rel(host(ri["state"]), st_ref)
+    say(f"  inference state rel error {errs_state:.2e}")
+    assert errs_state <= tol
     if stages:
-        B, S = w.B, w.S
         v = saved_views(r["layer"], r["saved"], w, B, S)
         qkv_ref = np.concatenate([np.stack(sv["q_lat"]).reshape(B, S, -1),
                                   np.stack(sv["k_lat"]).reshape(B, S, -1),
