@@ -64,6 +64,11 @@ _SIGNATURES = {
     "cca_decode_step_noalloc": (c_int, [c_void_p, POINTER(cca_weights), c_void_p,
                                         POINTER(c_int32), c_int32, c_void_p, c_void_p, c_void_p,
                                         c_void_p, c_void_p]),
+    "cca_forward_prefill_varlen": (c_int, [c_void_p, POINTER(cca_weights), c_void_p,
+                                           POINTER(c_int32), POINTER(c_int32), c_int32, c_void_p,
+                                           c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "cca_varlen_workspace_bytes": (c_size_t, [c_void_p, POINTER(c_int32), POINTER(c_int32),
+                                              c_int32]),
     "cca_backward": (c_int, [c_void_p, POINTER(cca_weights), c_void_p, c_void_p, c_void_p,
                              c_int32, c_int32, POINTER(cca_grads), c_void_p, c_void_p]),
     "cca_profile_enable": (c_int, [c_void_p, c_int]),
@@ -192,6 +197,25 @@ def cca_decode_step_noalloc(h, w, x_new, pos, B, k_cache, v_cache, state, y_new,
            "cca_decode_step_noalloc")
 
 
+def _i32(vals):
+    return None if vals is None else (c_int32 * len(vals))(*[int(v) for v in vals])
+
+
+def cca_varlen_workspace_bytes(h, offsets, starts=None) -> int:
+    return load().cca_varlen_workspace_bytes(h, _i32(offsets), _i32(starts), len(offsets) - 1)
+
+
+def cca_forward_prefill_varlen(h, w, x, offsets, starts, y, k_cache, v_cache, state, workspace,
+                               stream=None) -> None:
+    """offsets: B + 1 token offsets into the packed rows of x and y; starts: B
+    cached-token counts or None (all 0)."""
+    _check(load().cca_forward_prefill_varlen(h, byref(_weights(w)), _ptr(x), _i32(offsets),
+                                             _i32(starts), len(offsets) - 1, _ptr(y),
+                                             _ptr(k_cache), _ptr(v_cache), _ptr(state),
+                                             _ptr(workspace), _stream(stream)),
+           "cca_forward_prefill_varlen")
+
+
 def cca_backward(h, w, x, dy, saved, B, S, grads, workspace, stream=None) -> None:
     g = cca_grads()
     for n in ("dx", "dw_q", "dw_k", "dw_v", "dw_o", "dconv_q", "dconv_k"):
@@ -290,6 +314,18 @@ class CCALayer:
         y = torch.empty_like(x_new)
         ws = self.workspace(CCA_OP_DECODE, B, 0, x_new.device)
         cca_decode_step(self.handle, w, x_new, pos, B, k_cache, v_cache, state, y, ws, stream)
+        return y
+
+    def forward_prefill_varlen(self, w, x, offsets, starts, k_cache, v_cache, state,
+                               stream=None):
+        """Chunked variable-length prefill of packed rows x [T, E]; returns y."""
+        import torch
+        y = torch.empty_like(x)
+        n = load().cca_varlen_workspace_bytes(self.handle, _i32(offsets), _i32(starts),
+                                              len(offsets) - 1)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+        cca_forward_prefill_varlen(self.handle, w, x, offsets, starts, y, k_cache, v_cache,
+                                   state, ws, stream)
         return y
 
     def backward(self, w, x, dy, saved, stream=None):

@@ -233,6 +233,47 @@ GemmArgs gemm_down(const Dims& dm, int M, const void* a, const cca_weights* w, v
   return g;
 }
 
+// Variable-length prefill: per-sequence maps for the mix (64-token tiles)
+// and the attention (128-query blocks), and the workspace regions.
+struct VarlenPlan {
+  VarlenMap mix, attn;
+  int T, s_pad;
+  size_t lat, q, vt, o, total;
+};
+
+cca_status varlen_plan(const cca_handle* h, const int32_t* off, const int32_t* start, int32_t B,
+                       VarlenPlan* P) {
+  if (!h || !off || B < 1) return CCA_ERR_INVALID_ARG;
+  if (B > kMaxVarlenBatch) return CCA_ERR_UNSUPPORTED;
+  if (off[0] != 0) return CCA_ERR_INVALID_ARG;
+  const Dims& dm = h->dm;
+  std::memset(P, 0, sizeof(*P));
+  P->mix.B = P->attn.B = B;
+  int lmax = 0;
+  for (int b = 0; b < B; ++b) {
+    const long n = (long)off[b + 1] - off[b];
+    const long st = start ? start[b] : 0;
+    if (n < 0 || st < 0) return CCA_ERR_INVALID_ARG;
+    if (st + n > dm.max_seq_len) return CCA_ERR_CAPACITY;
+    P->mix.tok[b] = P->attn.tok[b] = off[b];
+    P->mix.start[b] = P->attn.start[b] = (int32_t)st;
+    P->mix.blk[b + 1] = P->mix.blk[b] + (int32_t)((n + 63) / 64);
+    P->attn.blk[b + 1] = P->attn.blk[b] + (int32_t)((n + 127) / 128);
+    lmax = std::max(lmax, (int)(st + n));
+  }
+  P->mix.tok[B] = P->attn.tok[B] = off[B];
+  P->T = off[B];
+  P->s_pad = (int)pad64(lmax);
+  const size_t T = (size_t)P->T;
+  size_t o = 0;
+  P->lat = o; o = align256(o + T * dm.nqkv * 2);
+  P->q = o;   o = align256(o + T * dm.nq * 2);
+  P->vt = o;  o = align256(o + (size_t)B * dm.nk * P->s_pad * 2);
+  P->o = o;   o = align256(o + T * dm.nq * 2);
+  P->total = o;
+  return CCA_OK;
+}
+
 #define CCA_TRY_HIP(expr)                         \
   do {                                            \
     hipError_t e_ = (expr);                       \
@@ -573,6 +614,74 @@ cca_status cca_decode_step_noalloc(cca_handle* h, const cca_weights* w, const vo
                      h->scratch, stream);
 }
 
+
+size_t cca_varlen_workspace_bytes(const cca_handle* h, const int32_t* offsets_host,
+                                  const int32_t* start_host, int32_t B) {
+  VarlenPlan P;
+  if (varlen_plan(h, offsets_host, start_host, B, &P) != CCA_OK) return 0;
+  return P.total;
+}
+
+cca_status cca_forward_prefill_varlen(cca_handle* h, const cca_weights* w, const void* x,
+                                      const int32_t* offsets_host, const int32_t* start_host,
+                                      int32_t B, void* y, void* k_cache, void* v_cache,
+                                      void* state, void* workspace, void* stream) {
+  try {
+    if (!h || !w || !offsets_host) return CCA_ERR_INVALID_ARG;
+    VarlenPlan P;
+    const cca_status st = varlen_plan(h, offsets_host, start_host, B, &P);
+    if (st != CCA_OK) return st;
+    const Dims& dm = h->dm;
+    if (!prefill_uses_mfma(dm)) return CCA_ERR_UNSUPPORTED;
+    if (P.T == 0) return CCA_OK;
+    if (!x || !y || !k_cache || !v_cache || !state || !workspace) return CCA_ERR_INVALID_ARG;
+    if (!w->w_q || !w->w_k || !w->w_v || !w->w_o || !w->conv_q || !w->conv_k)
+      return CCA_ERR_INVALID_ARG;
+    for (const void* p : {x, (const void*)y, (const void*)k_cache, (const void*)v_cache,
+                          (const void*)state, (const void*)workspace, w->w_q, w->w_k, w->w_v,
+                          w->w_o, w->conv_q, w->conv_k})
+      if (!aligned16(p)) return CCA_ERR_INVALID_ARG;
+    if ((long)P.T * dm.nqkv * 2 >= (1L << 31)) return CCA_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)workspace;
+    void* lat = base + P.lat;
+    void* q = base + P.q;
+    void* vt = base + P.vt;
+    void* o = base + P.o;
+
+    GemmArgs gd = gemm_down(dm, P.T, x, w, lat);
+    CCA_TRY_HIP(timed(h, "varlen_proj_down", s, [&] { return launch_gemm(gd, GemmLayout::NT, true, false, s); }));
+
+    MixArgs ma{};
+    ma.dm = dm; ma.B = B; ma.S = P.T; ma.qkv = lat; ma.qkv_f32 = false;
+    ma.conv_q = w->conv_q; ma.conv_k = w->conv_k; ma.rope = h->rope;
+    ma.q_out = q; ma.k_out = nullptr; ma.v_out = nullptr;
+    ma.k_out2 = k_cache; ma.v_out2 = v_cache; ma.cap2 = dm.max_seq_len;
+    ma.vt_out = nullptr; ma.s_pad = 0; ma.state = state;
+    CCA_TRY_HIP(timed(h, "varlen_mix", s, [&] { return launch_mix_varlen_mfma(ma, P.mix, s); }));
+    // the mix has read the old state: advance it past each chunk
+    CCA_TRY_HIP(timed(h, "varlen_state", s, [&] { return launch_state_varlen(dm, P.mix, lat, state, s); }));
+    CCA_TRY_HIP(timed(h, "varlen_vt", s, [&] {
+      return launch_vt_varlen(dm, P.mix, v_cache, dm.max_seq_len, vt, P.s_pad, s);
+    }));
+
+    AttnArgs aa{};
+    aa.dm = dm; aa.B = B; aa.Sq = P.T;
+    aa.q = q; aa.k = k_cache; aa.v = v_cache;
+    aa.kv_bs = (long)dm.Hkv * dm.max_seq_len * dm.d; aa.kv_hs = (long)dm.max_seq_len * dm.d;
+    aa.vt = vt; aa.s_pad = P.s_pad;
+    aa.o = o; aa.o32 = nullptr; aa.lse = nullptr; aa.decode = false;
+    CCA_TRY_HIP(timed(h, "varlen_attn", s, [&] { return launch_attn_varlen_mfma(aa, P.attn, s); }));
+
+    GemmArgs gu = gemm_nt(P.T, dm.E, dm.nq, o, dm.nq, w->w_o, dm.nq, y, dm.E);
+    CCA_TRY_HIP(timed(h, "varlen_proj_up", s, [&] { return launch_gemm(gu, GemmLayout::NT, true, false, s); }));
+    return CCA_OK;
+  } catch (const std::bad_alloc&) {
+    return CCA_ERR_OOM;
+  } catch (...) {
+    return CCA_ERR_HIP;
+  }
+}
 
 cca_status cca_backward(cca_handle* h, const cca_weights* w, const void* x, const void* dy,
                         const void* saved, int32_t B, int32_t S, const cca_grads* g,

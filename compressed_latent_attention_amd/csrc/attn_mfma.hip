@@ -146,17 +146,52 @@ __device__ __forceinline__ void mfma_phase(bool pv, bool qk, f32x16 (&oacc)[4],
   }
 }
 
+// The work-group's query block.  Fixed length: B sequences of a.Sq tokens, Q
+// head-major per sequence, query t at position t.  Variable length (VARLEN):
+// sequence b has nq = tok[b + 1] - tok[b] queries at positions start[b] ..,
+// Q packed [Hq][T][d] over all T tokens, K and V'^T covering keys 0 ..
+// start[b] + nq - 1, O rows packed like the tokens.
+// (The body sits in the kernel template itself: moved into a device function
+// it compiles to a slower schedule of the same arithmetic.)
+struct NoMap {};
+template <bool VARLEN, typename Map>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_mfma_kernel(AttnArgs a) {
+void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * HALF_BYTES];
 
   const Dims& dm = a.dm;
-  const int S = a.Sq;
-  const int nqb = (S + BM - 1) / BM;
-  const int per_qb = dm.Hq * a.B;
-  const int qb = nqb - 1 - (int)(blockIdx.x / per_qb);      // heaviest blocks first
-  const int hb = blockIdx.x % per_qb;
-  const int h = hb % dm.Hq, b = hb / dm.Hq;
+  int b, h, qb, nq, pos0;
+  long qrow0, orow0;                         // Q row and O row of query 0 of the block's sequence
+  if constexpr (!VARLEN) {
+    nq = a.Sq;
+    pos0 = 0;
+    const int nqb = (nq + BM - 1) / BM;
+    const int per_qb = dm.Hq * a.B;
+    qb = nqb - 1 - (int)(blockIdx.x / per_qb);             // heaviest blocks first
+    const int hb = blockIdx.x % per_qb;
+    h = hb % dm.Hq;
+    b = hb / dm.Hq;
+    qrow0 = (long)(b * dm.Hq + h) * nq;
+    orow0 = (long)b * nq;
+  } else {
+    // blocks numbered (sequence, query block, head); the last ones (the
+    // longest key ranges of each sequence) start first
+    const int L = vm.blk[vm.B] * dm.Hq - 1 - (int)blockIdx.x;
+    const int blk = L / dm.Hq;
+    h = L % dm.Hq;
+    int lo = 0, hi2 = vm.B - 1;                             // last b with blk[b] <= blk
+    while (lo < hi2) {
+      const int mid = (lo + hi2 + 1) >> 1;
+      if (vm.blk[mid] <= blk) lo = mid; else hi2 = mid - 1;
+    }
+    b = lo;
+    qb = blk - vm.blk[b];
+    nq = vm.tok[b + 1] - vm.tok[b];
+    pos0 = vm.start[b];
+    qrow0 = (long)h * vm.tok[vm.B] + vm.tok[b];
+    orow0 = vm.tok[b];
+  }
+  const int nkeys = pos0 + nq;               // keys 0 .. nkeys - 1 exist
   const int g = h / dm.G;
 
   const int lane = threadIdx.x & 63;
@@ -179,18 +214,18 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
   auto kbuf = [&](int i) { return hbase + i * KT_BYTES; };
   auto vbuf = [&](int i) { return hbase + 2 * KT_BYTES + i * VT_BYTES; };
 
-  const bf16* qbase = reinterpret_cast<const bf16*>(a.q) + ((long)(b * dm.Hq + h) * S) * D;
+  const bf16* qbase = reinterpret_cast<const bf16*>(a.q) + qrow0 * D;
   const bf16* kbase = reinterpret_cast<const bf16*>(a.k) + (long)b * a.kv_bs + (long)g * a.kv_hs;
   const bf16* vtbase =
       reinterpret_cast<const bf16*>(a.vt) + (long)(b * dm.Hkv + g) * D * a.s_pad;
 
-  const int q_last = min(S, q0 + BM) - 1;
-  const int ntiles = q_last / BN + 1;
+  const int q_last = min(nq, q0 + BM) - 1;
+  const int ntiles = (pos0 + q_last) / BN + 1;
   const int niter = (ntiles + 1) / 2;              // tiles of half 0 (>= those of half 1)
   const int nj = (ntiles - half + 1) / 2;          // tiles of this half
   auto key_of = [&](int j) { return (2 * j + half) * BN; };
   // tiles this wave computes: those of its half up to its last row's diagonal
-  const int kt_max = min(ntiles - 1, (r0 + 31) / BN);
+  const int kt_max = min(ntiles - 1, (pos0 + r0 + 31) / BN);
   const int nvalid = kt_max >= half ? (kt_max - half) / 2 + 1 : 0;
   const float scale = 1.44269504088896340736f / sqrtf((float)D);
 
@@ -200,7 +235,7 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
   bf16x8 qf[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    if (my_q < S) {
+    if (my_q < nq) {
       qf[ks] = *reinterpret_cast<const bf16x8*>(qbase + (long)my_q * D + ks * 16 + hi * 8);
     } else {
 #pragma unroll
@@ -213,10 +248,10 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
   // never uses).
   {
     const int key = min(half, ntiles - 1) * BN;
-    dma_k(kbuf(0), kbase, key, S, wq, lane);
+    dma_k(kbuf(0), kbase, key, nkeys, wq, lane);
     dma_v(vbuf(0), vtbase, a.s_pad, key, wq, lane);
   }
-  if (nj > 1) dma_k(kbuf(1), kbase, key_of(1), S, wq, lane);
+  if (nj > 1) dma_k(kbuf(1), kbase, key_of(1), nkeys, wq, lane);
   wait_dma();
 
   f32x16 oacc[4];
@@ -247,17 +282,18 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
     __builtin_amdgcn_s_barrier();
 
     // ---- softmax phase V(j)
-    // Every lane of a wave that takes a tile sees its first key (key0 <= r0):
-    // tiles start at multiples of 64 and wave rows at multiples of 32.
+    // With positions aligned to the tiles (fixed length), every lane of a wave
+    // that takes a tile sees the tile's first key; with a position offset a
+    // lane may see none (its max is then -inf, see the offset rule below).
     if (j < nvalid) {
       const int key0 = key_of(j);
-      if (key0 + BN - 1 > r0) {              // diagonal tile: mask keys after the query
+      if (key0 + BN - 1 > pos0 + r0) {       // diagonal tile: mask keys after the query
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = key0 + kb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
-            if (key > my_q) sacc[kb][r] = -INFINITY;
+            if (key > pos0 + my_q) sacc[kb][r] = -INFINITY;
           }
       }
       float mt = fmaxf(sacc[0][0], sacc[1][0]);
@@ -266,12 +302,16 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
       mt = xhalf_max(mt);
-      // The first tile sets the offset to the row max; later tiles raise it
-      // only for rows that outgrew it by more than 2^8.  The branch is taken
-      // when any row of the wave needs it, but every other row shifts by an
-      // exact 0, so a row's arithmetic never depends on another row's scores
-      // (an earlier row stays bit-identical whatever later tokens hold).
-      const bool grow = j == 0 || mt > lazy_raw;
+      // The first tile with a visible key sets the offset to the row max
+      // (tile 0 at fixed length; with a position offset l_run is 0 until
+      // then, and at least 1 after: the max scores exp2(0)); later tiles
+      // raise it only for rows that outgrew it by more than 2^8.  The branch
+      // is taken when any row of the wave needs it, but every other row
+      // shifts by an exact 0, so a row's arithmetic never depends on another
+      // row's scores (an earlier row stays bit-identical whatever later
+      // tokens hold).
+      const bool first = VARLEN ? (l_run == 0.0f && mt != -INFINITY) : j == 0;
+      const bool grow = first || mt > lazy_raw;
       if (__any(grow)) {
         const float delta = grow ? mt : 0.0f;
         const float alpha = __builtin_amdgcn_exp2f(-delta * scale);
@@ -305,7 +345,7 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
     // j + 2 into the K buffer tile j used (both last read in M(j)).
     wait_dma();
     if (j + 1 < nj) dma_v(vbuf((j + 1) & 1), vtbase, a.s_pad, key_of(j + 1), wq, lane);
-    if (j + 2 < nj) dma_k(kbuf(j & 1), kbase, key_of(j + 2), S, wq, lane);
+    if (j + 2 < nj) dma_k(kbuf(j & 1), kbase, key_of(j + 2), nkeys, wq, lane);
     __builtin_amdgcn_s_barrier();
   }
   if (half == 0) __builtin_amdgcn_s_barrier();
@@ -342,10 +382,11 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: lane holds query my_q, channels 32*mb + 8*(r/4) + 4*hi + r%4
-  if (my_q < S) {
+  if (my_q < nq) {
     const float inv = 1.0f / l_run;
-    bf16* orow = reinterpret_cast<bf16*>(a.o) + ((long)(b * S + my_q) * dm.Hq + h) * D;
-    float* orow32 = a.o32 ? a.o32 + ((long)(b * S + my_q) * dm.Hq + h) * D : nullptr;
+    const long row = VARLEN ? orow0 + my_q : (long)(b * nq + my_q);
+    bf16* orow = reinterpret_cast<bf16*>(a.o) + (row * dm.Hq + h) * D;
+    float* orow32 = a.o32 ? a.o32 + (row * dm.Hq + h) * D : nullptr;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -363,7 +404,7 @@ void attn_fwd_mfma_kernel(AttnArgs a) {
       }
     // natural-log LSE of the scaled scores: (m log2(e)/sqrt(d) + log2 l) ln 2
     if (hi == 0 && a.lse)
-      a.lse[(long)(b * dm.Hq + h) * S + my_q] =
+      a.lse[qrow0 + my_q] =
           (m_use * scale + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f;
   }
 }
@@ -375,7 +416,21 @@ hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const int nqb = (a.Sq + BM - 1) / BM;
   dim3 grid(nqb * a.dm.Hq * a.B);
-  hipLaunchKernelGGL(attn_fwd_mfma_kernel, grid, dim3(512), 0, s, a);
+  hipLaunchKernelGGL((attn_fwd_mfma_kernel<false, NoMap>), grid, dim3(512), 0, s, a, NoMap{});
+  return hipGetLastError();
+}
+
+// Variable-length attention: a.q packed [Hq][T][d], a.k / a.v the caches (kv_bs,
+// kv_hs), a.vt the V'^T of every sequence [B][Hkv][d][s_pad], a.o packed
+// [T][Hq*d]; vm.blk counts 128-query blocks.  No lse / o32.
+hipError_t launch_attn_varlen_mfma(const AttnArgs& a, const VarlenMap& vm, hipStream_t s) {
+  if (a.dm.d != D || a.vt == nullptr || a.s_pad % BN != 0 || a.lse || a.o32 || vm.B < 1 ||
+      vm.B > kMaxVarlenBatch)
+    return hipErrorInvalidValue;
+  const long nblk = (long)vm.blk[vm.B] * a.dm.Hq;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_fwd_mfma_kernel<true, VarlenMap>), dim3((unsigned)nblk), dim3(512), 0, s,
+                     a, vm);
   return hipGetLastError();
 }
 

@@ -119,6 +119,7 @@ struct MixArgs {
   int cap2;                 // row capacity of k_out2 / v_out2
   void* vt_out;             // V' transposed [B, Hkv, d, s_pad] (MFMA path), nullable
   int s_pad;                // S rounded up to a multiple of 64; rows [S, s_pad) are zero
+  const void* state;        // variable-length chunks: rolling state [B, state_w] before them
 };
 hipError_t launch_mix_fwd(const MixArgs& a, hipStream_t s);
 // True when prefill uses the MFMA mix + attention pair, which exchange V' in
@@ -154,6 +155,31 @@ hipError_t launch_mix_decode(const MixDecodeArgs& a, hipStream_t s);
 bool mix_decode_fused_ok(const Dims& dm);
 size_t mix_decode_cv_floats(const Dims& dm, int B);
 
+// ------------------------------------------------------------------ variable length
+// Per-sequence layout of a chunked, variable-length batched prefill (host
+// arrays passed by value): sequence b owns packed token rows tok[b] ..
+// tok[b + 1] - 1, which sit at positions start[b] .. of its cache; blk[b] is
+// the prefix sum of its work blocks for the kernel the map is built for.
+constexpr int kMaxVarlenBatch = 128;
+struct VarlenMap {
+  int32_t tok[kMaxVarlenBatch + 1];
+  int32_t start[kMaxVarlenBatch];
+  int32_t blk[kMaxVarlenBatch + 1];
+  int32_t B;
+};
+
+// Chunked variable-length prefill (bf16, d = 128): the mix (vm.blk over
+// 64-token tiles; a.S = T packed tokens, Q'' to [Hq][T][d], K'' / V' to the
+// caches at their positions, history from a.state), the state advanced past
+// each chunk (from the bf16 latent), the fp16 V'^T of each sequence's cache
+// rows 0 .. start + n - 1 ([B][Hkv][d][s_pad], zero past them), and the
+// attention over them (vm.blk over 128-query blocks).
+hipError_t launch_mix_varlen_mfma(const MixArgs& a, const VarlenMap& vm, hipStream_t s);
+hipError_t launch_state_varlen(const Dims& dm, const VarlenMap& vm, const void* lat, void* state,
+                               hipStream_t s);
+hipError_t launch_vt_varlen(const Dims& dm, const VarlenMap& vm, const void* v_cache, int cap,
+                            void* vt, int s_pad, hipStream_t s);
+
 // ------------------------------------------------------------------ attention
 // Causal attention.  Query row t of sequence b sits at position
 // (decode ? pos[b] : t) and sees keys 0..position.
@@ -178,6 +204,7 @@ struct AttnArgs {
   int nsplit;
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_varlen_mfma(const AttnArgs& a, const VarlenMap& vm, hipStream_t s);
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);
 int decode_nsplit(const Dims& dm, int B);
 size_t decode_part_floats(const Dims& dm, int B);

@@ -141,34 +141,79 @@ __device__ __forceinline__ float rotate(float x, float2 cs, bool lo_lane) {
   return lo_lane ? x * cs.x - xp * cs.y : x * cs.x + xp * cs.y;
 }
 
+// Rows 0 .. HALO - 1 of a tile of the first 64 tokens of a chunk (tokens -4 ..
+// -1) from the rolling state: state + off holds lag 1 of this tile's 128
+// channels, lag l at + (l - 1) * lag_stride; lags past nlag are zero.
+__device__ __forceinline__ void fill_halo(char* tile, const bf16* st, int nlag, long lag_stride) {
+  for (int e = threadIdx.x; e < HALO * D; e += 256) {
+    const int r = e / D, c = e % D, lag = HALO - r;
+    const bf16 v = lag <= nlag ? st[(lag - 1) * lag_stride + c] : (bf16)0.0f;
+    *reinterpret_cast<bf16*>(tile + r * ROWB + c * 2) = v;
+  }
+}
+
 // GC: the group size when known at compile time (1 or 2: every q~ tile stays
 // resident, so the K side's pre-convolution group mean is read back from LDS
 // instead of being summed in registers, and the head loop unrolls), 0 for any
 // other group size.
-template <int GC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void mix_fwd_mfma_kernel(MixArgs a, int ntiles8) {
+// VARLEN: a chunk of a variable-length batch (vm, 64-token tiles in vm.blk):
+// sequence b's tokens are latent rows vm.tok[b] .., at positions vm.start[b]
+// ..; the conv and shift history before its first token comes from a.state;
+// Q'' goes to the packed [Hq][T][d] (T = a.S), K'' and V' to the caches at
+// their positions, and no V'^T is written.
+// A variable-length launch runs one work-group per CU (the full register
+// file: the per-sequence indexing does not fit the two-per-CU budget without
+// spills).  The body sits in the kernel template itself: moved into a device
+// function it compiles to a slower schedule of the same arithmetic.
+struct NoMap {};
+template <int GC, bool VARLEN, typename Map>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VARLEN ? 1 : 2,
+                                                                     VARLEN ? 1 : 2)))
+void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
   constexpr bool QRES = GC > 0;
   __shared__ __attribute__((aligned(1024))) char lds[(2 + NQS) * TBYTES];
   char* tk = lds;                            // k~ tile
   char* tv = lds + TBYTES;                   // v~ tile
   char* tq = lds + 2 * TBYTES;               // q~ tiles, NQS slots
   const Dims& dm = a.dm;
-  const int G = GC > 0 ? GC : dm.G, S = a.S;
+  const int G = GC > 0 ? GC : dm.G;
   // (tile, KV group, sequence) from the work-group id: the Hkv groups of tiles
   // 8 i .. 8 i + 7 take ids 8 Hkv i + 8 g + (tile % 8)
-  const int per_b = ntiles8 * dm.Hkv;
-  const int b = blockIdx.x / per_b, q = blockIdx.x % per_b;
+  const int q = blockIdx.x % (ntiles8 * dm.Hkv);
   const int g = (q % (XCDS * dm.Hkv)) / XCDS;
   const int tile = (q / (XCDS * dm.Hkv)) * XCDS + q % XCDS;
-  const int t0 = tile * TW;
+  int b, t0, S, pos0;
+  long lat0, q_row0, q_hstride;              // latent row of token 0; Q'' row of (head 0, token 0)
+  if constexpr (!VARLEN) {
+    b = blockIdx.x / (ntiles8 * dm.Hkv);
+    S = a.S;
+    t0 = tile * TW;
+    pos0 = 0;
+    lat0 = (long)b * S;
+    q_row0 = (long)b * dm.Hq * S;
+    q_hstride = S;
+  } else {
+    if (tile >= vm.blk[vm.B]) return;
+    int lo = 0, hi2 = vm.B - 1;             // last b with blk[b] <= tile
+    while (lo < hi2) {
+      const int mid = (lo + hi2 + 1) >> 1;
+      if (vm.blk[mid] <= tile) lo = mid; else hi2 = mid - 1;
+    }
+    b = lo;
+    S = vm.tok[b + 1] - vm.tok[b];
+    t0 = (tile - vm.blk[b]) * TW;
+    pos0 = vm.start[b];
+    lat0 = vm.tok[b];
+    q_row0 = vm.tok[b];
+    q_hstride = a.S;
+  }
   if (t0 >= S) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const bool lo_lane = l32 < 16;
   const int pair = 16 * wave + (l32 & 15);   // RoPE pair of this lane's channel
   const int ch = lo_lane ? pair : pair + 64; // this lane's output channel
-  const bf16* qkv_b = reinterpret_cast<const bf16*>(a.qkv) + (long)b * S * dm.nqkv;
+  const bf16* qkv_b = reinterpret_cast<const bf16*>(a.qkv) + lat0 * dm.nqkv;
   const float A = (dm.flags & kQkPre) ? 0.5f : 0.0f;
   const float Bc = (dm.flags & kQkPost) ? 0.5f : 0.0f;
   const bool rope = (dm.flags & kRope) != 0;
@@ -181,7 +226,17 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8) {
     const int cols[2 + NQS] = {dm.nq + g * D, dm.nq + dm.nk + g * D, g * G * D, (g * G + 1) * D};
     load_tiles(dst, cols, 2 + min(G, NQS), qkv_b, dm.nqkv, S, t0);
   }
-  const float2* rope_t0 = rope ? a.rope + (long)t0 * (D / 2) : nullptr;
+  // the state: [q~ lags 1..kq-1 | k~ lags 1..kk-1 | v~ lag 1], most recent first
+  const bf16* st = VARLEN ? reinterpret_cast<const bf16*>(a.state) + (long)b * dm.state_w : nullptr;
+  const long st_k = (long)(dm.kq - 1) * dm.nq, st_v = st_k + (long)(dm.kk - 1) * dm.nk;
+  if (VARLEN && t0 == 0) {
+    __syncthreads();                         // the zero halo rows are stored
+    fill_halo(tk, st + st_k + g * D, dm.kk - 1, dm.nk);
+    fill_halo(tv, st + st_v + g * D, 1, dm.nk);
+    for (int i = 0; i < min(G, NQS); ++i)
+      fill_halo(tq + i * TBYTES, st + (g * G + i) * D, dm.kq - 1, dm.nq);
+  }
+  const float2* rope_t0 = rope ? a.rope + (long)(pos0 + t0) * (D / 2) : nullptr;
   __syncthreads();
 
   Acc2 kacc, qacc, mpost, mpre;
@@ -201,13 +256,19 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8) {
       char* const dst[NQS] = {tq, tq + TBYTES};
       const int cols[NQS] = {h * D, (h + 1) * D};
       load_tiles(dst, cols, min(NQS, G - i), qkv_b, dm.nqkv, S, t0);
+      if (VARLEN && t0 == 0) {
+        __syncthreads();
+        for (int s2 = 0; s2 < NQS && i + s2 < G; ++s2)
+          fill_halo(tq + s2 * TBYTES, st + (h + s2) * D, dm.kq - 1, dm.nq);
+      }
       __syncthreads();
     }
     const char* tqi = tq + (i % NQS) * TBYTES;
     zero(qacc);
     conv_head(qacc, tqi, reinterpret_cast<const bf16*>(a.conv_q) + (long)h * dm.kq * D * D,
               dm.kq, ch, lane);
-    bf16* qo = reinterpret_cast<bf16*>(a.q_out) + ((long)(b * dm.Hq + h) * S + t0) * D + ch;
+    const long qrow = VARLEN ? q_row0 + h * q_hstride + t0 : (long)(b * dm.Hq + h) * S + t0;
+    bf16* qo = reinterpret_cast<bf16*>(a.q_out) + qrow * D + ch;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       __builtin_amdgcn_sched_barrier(0);       // one token block at a time (registers)
@@ -235,9 +296,10 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8) {
   // k' = k^ + a/2 (mean_g q~ + k~) + b/2 (mean_g q^ + k^)
   __builtin_amdgcn_sched_barrier(0);
   const float invG = 1.0f / (float)G;
-  bf16* ko = reinterpret_cast<bf16*>(a.k_out) + ((long)(b * dm.Hkv + g) * S + t0) * D + ch;
+  bf16* ko = VARLEN ? nullptr
+                    : reinterpret_cast<bf16*>(a.k_out) + ((long)(b * dm.Hkv + g) * S + t0) * D + ch;
   bf16* ko2 = a.k_out2 ? reinterpret_cast<bf16*>(a.k_out2) +
-                             ((long)(b * dm.Hkv + g) * a.cap2 + t0) * D + ch
+                             ((long)(b * dm.Hkv + g) * a.cap2 + pos0 + t0) * D + ch
                        : nullptr;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
@@ -260,7 +322,7 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8) {
       const float y = rotate(kh + A * (qpre * invG + kp) + Bc * (mpost[mb][r] * invG + kh),
                              csr[r], lo_lane);
       if (t0 + tr < S) {
-        ko[tr * D] = (bf16)y;
+        if (!VARLEN) ko[tr * D] = (bf16)y;
         if (ko2) ko2[tr * D] = (bf16)y;
       }
     }
@@ -273,7 +335,8 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8) {
   auto vrow = [&](int tr, int c) { return tr + HALO - (c >= first_shift ? 1 : 0); };
   bf16* vo = a.v_out ? reinterpret_cast<bf16*>(a.v_out) + ((long)(b * dm.Hkv + g) * S) * D
                      : nullptr;
-  bf16* vo2 = a.v_out2 ? reinterpret_cast<bf16*>(a.v_out2) + ((long)(b * dm.Hkv + g) * a.cap2) * D
+  bf16* vo2 = a.v_out2 ? reinterpret_cast<bf16*>(a.v_out2) +
+                             ((long)(b * dm.Hkv + g) * a.cap2 + pos0) * D
                        : nullptr;
   if (vo || vo2) {
     // thread = (token, 8 channels): 16-byte stores
@@ -289,7 +352,7 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8) {
       if (vo2) *reinterpret_cast<bf16x8*>(vo2 + (long)t * D + c8) = v;
     }
   }
-  if (a.vt_out) {
+  if (!VARLEN && a.vt_out) {
     // V'^T feeds only the attention's P V product, which runs in fp16 so that P
     // keeps 11 significant bits.  It holds the stored bf16 V' values, converted
     // exactly (within fp16's range), so the forward's O and the backward (which
@@ -315,6 +378,29 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8) {
 
 bool mix_fwd_mfma_supported(const Dims& dm) { return dm.bf16 && dm.d == D; }
 
+// Variable-length mix (see mix_body): a.S = T, the packed token count; vm.blk
+// counts 64-token tiles; a.state holds each sequence's history before its chunk.
+hipError_t launch_mix_varlen_mfma(const MixArgs& a, const VarlenMap& vm, hipStream_t s) {
+  if (!mix_fwd_mfma_supported(a.dm) || a.qkv_f32 || !a.state || !a.k_out2 || !a.v_out2 ||
+      a.k_out || a.v_out || vm.B < 1 || vm.B > kMaxVarlenBatch)
+    return hipErrorInvalidValue;
+  if ((long)a.S * a.dm.nqkv * 2 >= (1L << 31)) return hipErrorInvalidValue;
+  const int ntiles = vm.blk[vm.B];
+  if (ntiles == 0) return hipSuccess;
+  const int ntiles8 = (ntiles + XCDS - 1) / XCDS * XCDS;
+  const dim3 grid((unsigned)(ntiles8 * a.dm.Hkv));
+  if (a.dm.G == 1)
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<1, true, VarlenMap>), grid, dim3(256), 0, s, a,
+                       ntiles8, vm);
+  else if (a.dm.G == 2)
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<2, true, VarlenMap>), grid, dim3(256), 0, s, a,
+                       ntiles8, vm);
+  else
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<0, true, VarlenMap>), grid, dim3(256), 0, s, a,
+                       ntiles8, vm);
+  return hipGetLastError();
+}
+
 hipError_t launch_mix_fwd_mfma(const MixArgs& a, hipStream_t s) {
   if (a.vt_out && (a.s_pad % 64 != 0 || a.s_pad < a.S)) return hipErrorInvalidValue;
   // 32-bit byte offsets within one sequence's latent rows
@@ -323,11 +409,14 @@ hipError_t launch_mix_fwd_mfma(const MixArgs& a, hipStream_t s) {
   const int ntiles8 = (ntiles + XCDS - 1) / XCDS * XCDS;
   const dim3 grid((unsigned)(ntiles8 * a.dm.Hkv * a.B));
   if (a.dm.G == 1)
-    hipLaunchKernelGGL(mix_fwd_mfma_kernel<1>, grid, dim3(256), 0, s, a, ntiles8);
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<1, false, NoMap>), grid, dim3(256), 0, s, a, ntiles8,
+                       NoMap{});
   else if (a.dm.G == 2)
-    hipLaunchKernelGGL(mix_fwd_mfma_kernel<2>, grid, dim3(256), 0, s, a, ntiles8);
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<2, false, NoMap>), grid, dim3(256), 0, s, a, ntiles8,
+                       NoMap{});
   else
-    hipLaunchKernelGGL(mix_fwd_mfma_kernel<0>, grid, dim3(256), 0, s, a, ntiles8);
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<0, false, NoMap>), grid, dim3(256), 0, s, a, ntiles8,
+                       NoMap{});
   return hipGetLastError();
 }
 

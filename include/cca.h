@@ -198,6 +198,37 @@ cca_status cca_decode_step_noalloc(cca_handle* h, const cca_weights* w, const vo
                                    const int32_t* pos_host, int32_t B, void* k_cache,
                                    void* v_cache, void* state, void* y_new, void* stream);
 
+/* Chunked, variable-length batched prefill: the serving handoff that fills the
+ * compressed latent cache (CCA-es §2.C and §1 item 2; CCA-fr §4 "Décodage").
+ * Sequence b (b < B <= 128) contributes n_b = offsets_host[b + 1] -
+ * offsets_host[b] >= 0 new tokens, packed rows offsets_host[b] .. of x and y,
+ * at positions s_b .. s_b + n_b - 1 where s_b = start_host[b] (start_host
+ * NULL: all 0) is the number of tokens already in its cache.  The result is
+ * the same as n_b decode steps of sequence b: the convolution and value-shift
+ * history before its first new token comes from state, each new token
+ * attends over cache rows 0 .. its position, rows s_b .. s_b + n_b - 1 of
+ * k_cache and v_cache receive the new K'' and V', and state is advanced past
+ * the chunk.  For a new sequence pass s_b = 0 and a zeroed state row.
+ *   x, y [T, E] dt with T = offsets_host[B]; offsets_host: HOST array of B + 1
+ *     int32, offsets_host[0] = 0, nondecreasing; start_host: HOST array of B
+ *     int32 or NULL.
+ *   k_cache, v_cache [B, Hkv, max_seq_len, d] dt; state [B, W] dt (read and
+ *     advanced in place); workspace: cca_varlen_workspace_bytes(h, offsets_host,
+ *     start_host, B) bytes.
+ * bf16 storage with d = 128 only (else CCA_ERR_UNSUPPORTED).  Returns
+ * CCA_ERR_CAPACITY if some s_b + n_b > max_seq_len, CCA_ERR_INVALID_ARG for a
+ * negative length or start, CCA_ERR_UNSUPPORTED for B > 128; nothing is
+ * launched then.  T = 0 launches nothing.  Inference only (nothing is saved
+ * for a backward; the latent is rounded to bf16). */
+cca_status cca_forward_prefill_varlen(cca_handle* h, const cca_weights* w, const void* x,
+                                      const int32_t* offsets_host, const int32_t* start_host,
+                                      int32_t B, void* y, void* k_cache, void* v_cache,
+                                      void* state, void* workspace, void* stream);
+/* Workspace bytes of cca_forward_prefill_varlen for these host arrays; 0 on
+ * an invalid argument. */
+size_t cca_varlen_workspace_bytes(const cca_handle* h, const int32_t* offsets_host,
+                                  const int32_t* start_host, int32_t B);
+
 /* Backward of cca_forward_prefill for L = <dy, y> (CCA-es §4, training
  * backward): x, dy [B, S, E] dt; saved: what the prefill of the same x wrote.
  * Fills every pointer of g (all required).  Attention probabilities are

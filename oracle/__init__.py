@@ -26,9 +26,10 @@ on the readings listed in ``Spec``'s docstring: the pages print no numeric
 output of the layer, so no printed value pins the composition itself.
 """
 from .cca import (Spec, project, conv_causal, qk_mean, value_shift, rope_angles, rope,
-                  attention, forward, decode_step, backward, default_vmask,
+                  attention, forward, decode_step, prefill_chunks, backward, default_vmask,
                   attention_flops, kv_cache_values_per_token, param_count)
 
 __all__ = ["Spec", "project", "conv_causal", "qk_mean", "value_shift", "rope_angles",
-           "rope", "attention", "forward", "decode_step", "backward", "default_vmask",
+           "rope", "attention", "forward", "decode_step", "prefill_chunks", "backward",
+           "default_vmask",
            "attention_flops", "kv_cache_values_per_token", "param_count"]

@@ -369,6 +369,34 @@ def decode_step(x_new: np.ndarray, params: Dict[str, np.ndarray], spec: Spec,
     return y, kc, vc, st_out
 
 
+def prefill_chunks(x: np.ndarray, offsets, starts, params: Dict[str, np.ndarray], spec: Spec,
+                   k_cache: np.ndarray, v_cache: np.ndarray, state: np.ndarray):
+    """Chunked, variable-length batched prefill over the compressed latent
+    cache (CCA-es §1 item 2 and §2.C on the cache; CCA-fr §4 "Décodage").
+
+    Sequence b brings the packed rows offsets[b] .. offsets[b+1]-1 of x [T, E]
+    as new tokens at positions starts[b] ..; each is taken through
+    ``decode_step`` in order (a chunk is its tokens decoded one after another:
+    conv and shift history from the state, attention over the cache up to the
+    token's own row).  Returns y [T, E] and updated copies of (k_cache,
+    v_cache, state).
+    """
+    x = np.asarray(x, f64)
+    B = len(offsets) - 1
+    kc = np.array(k_cache, f64)
+    vc = np.array(v_cache, f64)
+    st = np.array(state, f64)
+    y = np.zeros((x.shape[0], x.shape[1]), f64)
+    for b in range(B):
+        p0 = 0 if starts is None else int(starts[b])
+        for i, row in enumerate(range(int(offsets[b]), int(offsets[b + 1]))):
+            yb, kcb, vcb, stb = decode_step(x[row][None], params, spec, kc[b:b + 1],
+                                            vc[b:b + 1], st[b:b + 1], np.array([p0 + i]))
+            y[row] = yb[0]
+            kc[b], vc[b], st[b] = kcb[0], vcb[0], stb[0]
+    return y, kc, vc, st
+
+
 # ---------------------------------------------------------------- backward
 
 def _attention_backward(q, k, v, o, lse, do, G, block=256):

@@ -293,6 +293,53 @@ def test_decode_first_token_from_zero_state_equals_prefill_of_one():
     assert rel(y, y_ref) < 1e-13
 
 
+# ------------------------------------------------------- chunked prefill
+
+def _fresh_caches(spec, B, cap):
+    W = (spec.kq - 1) * spec.Hq * spec.d + (spec.kk - 1) * spec.Hkv * spec.d + spec.Hkv * spec.d
+    return (np.zeros((B, spec.Hkv, cap, spec.d)), np.zeros((B, spec.Hkv, cap, spec.d)),
+            np.zeros((B, W)))
+
+
+def test_chunked_prefill_of_new_sequences_equals_prefill():
+    """Ragged new sequences (start 0, zero state) in one packed batch give each
+    sequence's prefill output, cache rows and final state."""
+    rng = np.random.default_rng(16)
+    spec = O.Spec(E=64, C=4, Hq=4, Hkv=2, kq=3, kk=2)
+    p = rand_params(spec, rng)
+    lens = [1, 6, 0, 4]
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    x = rng.standard_normal((offs[-1], 64))
+    kc, vc, st = _fresh_caches(spec, len(lens), 8)
+    y, kc2, vc2, st2 = O.prefill_chunks(x, offs, None, p, spec, kc, vc, st)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(kc2[b] == 0) and np.all(st2[b] == 0)
+            continue
+        yb, sv = O.forward(x[None, offs[b]:offs[b + 1]], p, spec, return_saved=True)
+        assert rel(y[offs[b]:offs[b + 1]], yb[0]) < 1e-12
+        assert rel(kc2[b, :, :n], np.transpose(sv["k_rope"][0], (1, 0, 2))) < 1e-12
+        assert rel(vc2[b, :, :n], np.transpose(sv["v_shift"][0], (1, 0, 2))) < 1e-12
+        assert rel(st2[b], sv["state"][0]) < 1e-14
+        assert np.all(kc2[b, :, n:] == 0)
+
+
+def test_chunked_prefill_is_independent_of_the_chunking():
+    """A sequence fed as one chunk of 7 tokens, or as chunks of 3 and 4 (the
+    second starting where the first left the cache and state), gives the same
+    outputs, cache and state."""
+    rng = np.random.default_rng(17)
+    spec = O.Spec(E=64, C=4, Hq=4, Hkv=1, kq=2, kk=3)
+    p = rand_params(spec, rng)
+    x = rng.standard_normal((7, 64))
+    kc, vc, st = _fresh_caches(spec, 1, 10)
+    y1, kc1, vc1, st1 = O.prefill_chunks(x, [0, 7], [0], p, spec, kc, vc, st)
+    ya, kca, vca, sta = O.prefill_chunks(x[:3], [0, 3], [0], p, spec, kc, vc, st)
+    yb, kcb, vcb, stb = O.prefill_chunks(x[3:], [0, 4], [3], p, spec, kca, vca, sta)
+    assert rel(np.concatenate([ya, yb]), y1) < 1e-13
+    assert rel(kcb, kc1) < 1e-13 and rel(vcb, vc1) < 1e-13 and rel(stb, st1) < 1e-13
+
+
 # ------------------------------------------------------- backward
 
 def _loss(x, dy, p, spec):
