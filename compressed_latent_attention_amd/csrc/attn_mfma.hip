@@ -47,51 +47,68 @@
 namespace cca {
 namespace {
 
-constexpr int D = 128;
 constexpr int BM = 128;        // query rows per work-group
 constexpr int BN = 64;         // keys per tile
-constexpr int KT_BYTES = BN * D * 2;      // K tile: 64 rows of 256 B
-constexpr int VT_BYTES = D * BN * 2;      // V^T tile: 128 rows of 128 B
-constexpr int HALF_BYTES = 2 * (KT_BYTES + VT_BYTES);   // one half's two K + V^T buffers
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr float kLazyLog2 = 8.0f;                        // rescale when the max grows by > 2^8
-constexpr int MERGE_STRIDE = 66;                         // floats per lane: 64 of O^T, m, l
+
+// Sizes that follow the head dimension D (128 or 64).
+template <int D>
+struct Geom {
+  static constexpr int NKS = D / 16;                     // 16-channel k-steps of S = K Q^T
+  static constexpr int NMB = D / 32;                     // 32-channel blocks of O^T
+  static constexpr int KT_BYTES = BN * D * 2;            // K tile: 64 rows of 2D bytes
+  static constexpr int VT_BYTES = D * BN * 2;            // V^T tile: D rows of 128 B
+  static constexpr int HALF_BYTES = 2 * (KT_BYTES + VT_BYTES);  // one half's two K + V^T buffers
+  static constexpr int MERGE_STRIDE = NMB * 16 + 2;      // floats per lane: O^T, m, l
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS byte offset of 16-byte chunk c of K-tile row r (16 chunks per row) and of
-// V^T-tile row r (8 chunks per row).  The XOR spreads the 16 rows a half-wave
-// reads in one ds_read_b128 over all 64 banks.
-__device__ __forceinline__ int k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+// LDS byte offset of 16-byte chunk c of K-tile row r (D / 8 chunks per row)
+// and of V^T-tile row r (8 chunks per row).  The XOR spreads the 16 rows a
+// half-wave reads in one ds_read_b128 over all 64 banks: with 256-byte rows
+// the 16 rows take distinct chunk positions; with 128-byte rows (two rows per
+// bank sweep) each parity class of 8 rows does.
 __device__ __forceinline__ int v_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+template <int D>
+__device__ __forceinline__ int k_off(int r, int c) {
+  if constexpr (D == 128) return r * 256 + ((c ^ (r & 15)) << 4);
+  else return v_off(r, c);
+}
 
 // K tile of keys key0 .. key0+63 into LDS at kt: each wave of the half (wq)
-// writes 4 KB as 4 buffer loads of 1 KB (64 lanes x 16 B), lane L landing at
-// row (4 (4 wq + i) + L / 16), chunk position L % 16, so it fetches the global
-// chunk that the swizzle puts there.  The resource ends at row nkeys - 1: rows
-// past the sequence read as zero.
+// writes a quarter of the tile as buffer loads of 1 KB (64 lanes x 16 B), lane
+// L of block blk landing at row (blk * 1024 / 2D + L / (D / 8)), chunk
+// position L % (D / 8), so it fetches the global chunk that the swizzle puts
+// there.  The resource ends at row nkeys - 1: rows past the sequence read as
+// zero.
+template <int D>
 __device__ __forceinline__ void dma_k(char* kt, const bf16* kb, int key0, int nkeys, int wq,
                                       int lane) {
+  constexpr int NB = Geom<D>::KT_BYTES / 4096, CPR = D / 8;   // blocks per wave, chunks per row
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(kb + (long)key0 * D), 0, max(nkeys - key0, 0) * D * 2, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = wq * 4 + i;                 // 1 KB block of the tile
-    const int r = blk * 4 + (lane >> 4), pos = lane & 15;
-    const int src = r * 256 + ((pos ^ (r & 15)) << 4);
+  for (int i = 0; i < NB; ++i) {
+    const int blk = wq * NB + i;                // 1 KB block of the tile
+    const int r = blk * (1024 / (2 * D)) + lane / CPR, pos = lane % CPR;
+    const int src = k_off<D>(r, pos);           // the swizzle is an involution per row
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kt + blk * 1024), 16, src, 0, 0, 0);
   }
 }
 
-// V^T tile (128 channel rows x keys key0 .. key0+63) into LDS at vt, the same
-// way: row (8 (4 wq + i) + L / 8), chunk position L % 8.
+// V^T tile (D channel rows x keys key0 .. key0+63) into LDS at vt, the same
+// way: row (8 blk + L / 8), chunk position L % 8.
+template <int D>
 __device__ __forceinline__ void dma_v(char* vt, const bf16* vtb, int s_pad, int key0, int wq,
                                       int lane) {
+  constexpr int NB = Geom<D>::VT_BYTES / 4096;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(vtb + key0), 0, (D - 1) * s_pad * 2 + BN * 2, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = wq * 4 + i;
+  for (int i = 0; i < NB; ++i) {
+    const int blk = wq * NB + i;
     const int r = blk * 8 + (lane >> 3), pos = lane & 7;
     const int src = r * s_pad * 2 + ((pos ^ ((r >> 1) & 7)) << 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(vt + blk * 1024), 16, src, 0, 0, 0);
@@ -118,16 +135,17 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // four accumulator chains), then S^T - m = K Q^T started from minit (= -m) for
 // the current tile (when qk, two chains).  krow: the K row this lane's
 // accumulator column block reads, l32 with bits 2 and 3 swapped.
-__device__ __forceinline__ void mfma_phase(bool pv, bool qk, f32x16 (&oacc)[4],
+template <int D>
+__device__ __forceinline__ void mfma_phase(bool pv, bool qk, f32x16 (&oacc)[Geom<D>::NMB],
                                            const f16x8 (&pf)[4], const char* vs_,
                                            f32x16 (&sacc)[2], const char* ks_,
-                                           const bf16x8 (&qf)[8], const f32x16& minit, int l32,
-                                           int krow, int hi) {
+                                           const bf16x8 (&qf)[Geom<D>::NKS], const f32x16& minit,
+                                           int l32, int krow, int hi) {
   if (pv) {
 #pragma unroll
     for (int pk = 0; pk < 4; ++pk)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < Geom<D>::NMB; ++mb) {
         const f16x8 vf =
             *reinterpret_cast<const f16x8*>(vs_ + v_off(mb * 32 + l32, 2 * pk + hi));
         oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[pk], oacc[mb], 0, 0, 0);
@@ -135,11 +153,11 @@ __device__ __forceinline__ void mfma_phase(bool pv, bool qk, f32x16 (&oacc)[4],
   }
   if (qk) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < Geom<D>::NKS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(ks_ + k_off(kb * 32 + krow, 2 * ks + hi));
+            *reinterpret_cast<const bf16x8*>(ks_ + k_off<D>(kb * 32 + krow, 2 * ks + hi));
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? minit : sacc[kb],
                                                            0, 0, 0);
       }
@@ -154,9 +172,12 @@ __device__ __forceinline__ void mfma_phase(bool pv, bool qk, f32x16 (&oacc)[4],
 // (The body sits in the kernel template itself: moved into a device function
 // it compiles to a slower schedule of the same arithmetic.)
 struct NoMap {};
-template <bool VARLEN, typename Map>
+template <int D, bool VARLEN, typename Map>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
+  using GM = Geom<D>;
+  constexpr int NKS = GM::NKS, NMB = GM::NMB, KT_BYTES = GM::KT_BYTES, VT_BYTES = GM::VT_BYTES;
+  constexpr int HALF_BYTES = GM::HALF_BYTES, MERGE_STRIDE = GM::MERGE_STRIDE;
   __shared__ __attribute__((aligned(1024))) char lds[2 * HALF_BYTES];
 
   const Dims& dm = a.dm;
@@ -232,9 +253,9 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
   // Q^T fragments first: the prologue's waits then cover them, so no later
   // wait stalls on them.
   // Lane holds query my_q, channels 16*ks + 8*hi + 0..7.
-  bf16x8 qf[8];
+  bf16x8 qf[NKS];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
+  for (int ks = 0; ks < NKS; ++ks) {
     if (my_q < nq) {
       qf[ks] = *reinterpret_cast<const bf16x8*>(qbase + (long)my_q * D + ks * 16 + hi * 8);
     } else {
@@ -248,15 +269,15 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
   // never uses).
   {
     const int key = min(half, ntiles - 1) * BN;
-    dma_k(kbuf(0), kbase, key, nkeys, wq, lane);
-    dma_v(vbuf(0), vtbase, a.s_pad, key, wq, lane);
+    dma_k<D>(kbuf(0), kbase, key, nkeys, wq, lane);
+    dma_v<D>(vbuf(0), vtbase, a.s_pad, key, wq, lane);
   }
-  if (nj > 1) dma_k(kbuf(1), kbase, key_of(1), nkeys, wq, lane);
+  if (nj > 1) dma_k<D>(kbuf(1), kbase, key_of(1), nkeys, wq, lane);
   wait_dma();
 
-  f32x16 oacc[4];
+  f32x16 oacc[NMB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NMB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
   float m_use = 0.0f, l_run = 0.0f;    // exponent offset (raw score units), row sum
@@ -277,7 +298,7 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
   if (half == 1) __builtin_amdgcn_s_barrier();
   for (int j = 0; j <= niter; ++j) {
     // ---- matrix phase M(j)
-    mfma_phase(j >= 1 && j - 1 < nvalid, j < nvalid, oacc, pf, vbuf((j - 1) & 1), sacc,
+    mfma_phase<D>(j >= 1 && j - 1 < nvalid, j < nvalid, oacc, pf, vbuf((j - 1) & 1), sacc,
                kbuf(j & 1), qf, minit, l32, krow, hi);
     __builtin_amdgcn_s_barrier();
 
@@ -318,7 +339,7 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
         m_use += delta;
         l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NMB; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
 #pragma unroll
@@ -344,8 +365,8 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
     // issue V of tile j + 1 into the V buffer tile j - 1 used and K of tile
     // j + 2 into the K buffer tile j used (both last read in M(j)).
     wait_dma();
-    if (j + 1 < nj) dma_v(vbuf((j + 1) & 1), vtbase, a.s_pad, key_of(j + 1), wq, lane);
-    if (j + 2 < nj) dma_k(kbuf(j & 1), kbase, key_of(j + 2), nkeys, wq, lane);
+    if (j + 1 < nj) dma_v<D>(vbuf((j + 1) & 1), vtbase, a.s_pad, key_of(j + 1), wq, lane);
+    if (j + 2 < nj) dma_k<D>(kbuf(j & 1), kbase, key_of(j + 2), nkeys, wq, lane);
     __builtin_amdgcn_s_barrier();
   }
   if (half == 0) __builtin_amdgcn_s_barrier();
@@ -359,24 +380,24 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
   wait_dma();
   if (half == 1) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mg[(mb * 16 + r) * 64] = oacc[mb][r];
-    mg[64 * 64] = m_use;
-    mg[65 * 64] = l_run;
+    mg[NMB * 16 * 64] = m_use;
+    mg[(NMB * 16 + 1) * 64] = l_run;
   }
   __syncthreads();
   if (half == 1) return;
   {
     // half 0 always took tile 0, so its offset is finite.
-    const float m_b = mg[64 * 64], l_b = mg[65 * 64];
+    const float m_b = mg[NMB * 16 * 64], l_b = mg[(NMB * 16 + 1) * 64];
     const float mn = fmaxf(m_use, m_b);
     const float wa = __builtin_amdgcn_exp2f((m_use - mn) * scale);
     const float wb = __builtin_amdgcn_exp2f((m_b - mn) * scale);
     l_run = l_run * wa + l_b * wb;
     m_use = mn;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[mb][r] = oacc[mb][r] * wa + mg[(mb * 16 + r) * 64] * wb;
   }
@@ -388,7 +409,7 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
     bf16* orow = reinterpret_cast<bf16*>(a.o) + (row * dm.Hq + h) * D;
     float* orow32 = a.o32 ? a.o32 + (row * dm.Hq + h) * D : nullptr;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = mb * 32 + 8 * j + 4 * hi;
@@ -412,11 +433,16 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
 }  // namespace
 
 hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s) {
-  if (a.dm.d != D || a.vt == nullptr || a.s_pad < a.Sq || a.s_pad % BN != 0)
+  if ((a.dm.d != 128 && a.dm.d != 64) || a.vt == nullptr || a.s_pad < a.Sq || a.s_pad % BN != 0)
     return hipErrorInvalidValue;
   const int nqb = (a.Sq + BM - 1) / BM;
   dim3 grid(nqb * a.dm.Hq * a.B);
-  hipLaunchKernelGGL((attn_fwd_mfma_kernel<false, NoMap>), grid, dim3(512), 0, s, a, NoMap{});
+  if (a.dm.d == 128)
+    hipLaunchKernelGGL((attn_fwd_mfma_kernel<128, false, NoMap>), grid, dim3(512), 0, s, a,
+                       NoMap{});
+  else
+    hipLaunchKernelGGL((attn_fwd_mfma_kernel<64, false, NoMap>), grid, dim3(512), 0, s, a,
+                       NoMap{});
   return hipGetLastError();
 }
 
@@ -424,12 +450,12 @@ hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s) {
 // kv_hs), a.vt the V'^T of every sequence [B][Hkv][d][s_pad], a.o packed
 // [T][Hq*d]; vm.blk counts 128-query blocks.  No lse / o32.
 hipError_t launch_attn_varlen_mfma(const AttnArgs& a, const VarlenMap& vm, hipStream_t s) {
-  if (a.dm.d != D || a.vt == nullptr || a.s_pad % BN != 0 || a.lse || a.o32 || vm.B < 1 ||
+  if (a.dm.d != 128 || a.vt == nullptr || a.s_pad % BN != 0 || a.lse || a.o32 || vm.B < 1 ||
       vm.B > kMaxVarlenBatch)
     return hipErrorInvalidValue;
   const long nblk = (long)vm.blk[vm.B] * a.dm.Hq;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_mfma_kernel<true, VarlenMap>), dim3((unsigned)nblk), dim3(512), 0, s,
+  hipLaunchKernelGGL((attn_fwd_mfma_kernel<128, true, VarlenMap>), dim3((unsigned)nblk), dim3(512), 0, s,
                      a, vm);
   return hipGetLastError();
 }

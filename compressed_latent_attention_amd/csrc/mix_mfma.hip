@@ -27,30 +27,44 @@
 namespace cca {
 namespace {
 
-constexpr int D = 128;
-constexpr int TW = 64;                      // tokens per work-group
 constexpr int HALO = 4;                     // staged rows before the tile (>= kMaxConv - 1)
-constexpr int TROWS = TW + HALO;            // tile row i = token t0 - HALO + i
-constexpr int ROWB = 272;                   // LDS row stride in bytes (256 + 16)
-constexpr int TBYTES = TROWS * ROWB;
 constexpr int NQS = 2;                      // q~ tiles resident at once
 constexpr int XCDS = 8;
-constexpr int CHUNKS = TROWS * (D / 8);     // 16-byte chunks per tile
+
+// Sizes that follow the head dimension D (128 or 64).  The 4 waves split the
+// D / 32 channel groups of 32 MFMA columns first, then the tokens: with
+// D = 64 two waves share each channel group and the tile is 128 tokens, so a
+// wave still holds two 32-token blocks.
+template <int D>
+struct MGeom {
+  static constexpr int NCW = D / 32;                 // channel groups (waves per token group)
+  static constexpr int NTG = 4 / NCW;                // token groups of 64
+  static constexpr int TW = 64 * NTG;                // tokens per work-group
+  static constexpr int TROWS = TW + HALO;            // tile row i = token t0 - HALO + i
+  static constexpr int ROWB = 2 * D + 16;            // LDS row stride in bytes (one chunk of pad)
+  static constexpr int TBYTES = TROWS * ROWB;
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int CHUNKS = TROWS * CPR;         // 16-byte chunks per tile
+  static constexpr int NKS = D / 16;                 // 16-channel k-steps of one tap
+};
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
+template <int D>
 __device__ __forceinline__ float tile_val(const char* tile, int r, int ch) {
-  return (float)*reinterpret_cast<const bf16*>(tile + r * ROWB + ch * 2);
+  return (float)*reinterpret_cast<const bf16*>(tile + r * MGeom<D>::ROWB + ch * 2);
 }
 
-// The latent tiles of column blocks cols[0 .. n) (128 channels each), rows
+// The latent tiles of column blocks cols[0 .. n) (D channels each), rows
 // t0 - HALO .. t0 + TW - 1, into LDS tiles dst[0 .. n): every load of the
 // work-group is issued before the first LDS store.  Each resource spans the
 // rows inside [0, S): rows before 0 (an offset that wraps) and past S read as
 // zero without a branch.
-template <int NMAX>
+template <int D, int NMAX>
 __device__ __forceinline__ void load_tiles(char* const (&dst)[NMAX], const int (&cols)[NMAX],
                                            int n, const bf16* qkv_b, int nqkv, int S, int t0) {
+  constexpr int TW = MGeom<D>::TW, CHUNKS = MGeom<D>::CHUNKS, CPR = MGeom<D>::CPR;
+  constexpr int ROWB = MGeom<D>::ROWB;
   constexpr int PER = (CHUNKS + 255) / 256;  // chunks per thread per tile
   const int r0 = max(t0 - HALO, 0), r1 = min(S, t0 + TW);
   bf16x8 v[NMAX][PER];
@@ -63,7 +77,7 @@ __device__ __forceinline__ void load_tiles(char* const (&dst)[NMAX], const int (
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int e = min((int)threadIdx.x + 256 * p, CHUNKS - 1);
-      const int r = e >> 4, c = e & 15;
+      const int r = e / CPR, c = e % CPR;
       const int t = t0 - HALO + r;
       v[i][p] = __builtin_bit_cast(
           bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, ((t - r0) * nqkv + c * 8) * 2, 0, 0));
@@ -76,7 +90,7 @@ __device__ __forceinline__ void load_tiles(char* const (&dst)[NMAX], const int (
     for (int p = 0; p < PER; ++p) {
       const int e = (int)threadIdx.x + 256 * p;
       if (e < CHUNKS)
-        *reinterpret_cast<bf16x8*>(dst[i] + (e >> 4) * ROWB + (e & 15) * 16) = v[i][p];
+        *reinterpret_cast<bf16x8*>(dst[i] + (e / CPR) * ROWB + (e % CPR) * 16) = v[i][p];
     }
   }
 }
@@ -90,23 +104,26 @@ __device__ __forceinline__ void zero(Acc2& a) {
     for (int r = 0; r < 16; ++r) a[j][r] = 0.0f;
 }
 
-// acc[mb] += conv of the head whose tile is at `tile` for token block mb (A
-// rows = tokens 32 mb + l32 at lag j, tile row 32 mb + l32 - j + HALO), B =
-// taps[j][ch][c_in] for this lane's output channel ch; the 8 B fragments of a
-// lag are loaded before its MFMAs and each serves both token blocks.
+// acc[mb] += conv of the head whose tile is at `tile` for the wave's token
+// block mb (A rows = tokens tb0 + 32 mb + l32 at lag j, tile row tb0 + 32 mb +
+// l32 - j + HALO), B = taps[j][ch][c_in] for this lane's output channel ch;
+// the D / 16 B fragments of a lag are loaded before its MFMAs and each serves
+// both token blocks.
+template <int D>
 __device__ __forceinline__ void conv_head(Acc2& acc, const char* tile, const bf16* taps, int k,
-                                          int ch, int lane) {
+                                          int ch, int lane, int tb0) {
+  constexpr int NKS = MGeom<D>::NKS, ROWB = MGeom<D>::ROWB;
   const int l32 = lane & 31, hi = lane >> 5;
   for (int j = 0; j < k; ++j) {
     const bf16* trow = taps + ((long)j * D + ch) * D + hi * 8;
-    bf16x8 bf[8];
+    bf16x8 bf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) bf[ks] = *reinterpret_cast<const bf16x8*>(trow + ks * 16);
+    for (int ks = 0; ks < NKS; ++ks) bf[ks] = *reinterpret_cast<const bf16x8*>(trow + ks * 16);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const int row = 32 * mb + l32 - j + HALO;
+        const int row = tb0 + 32 * mb + l32 - j + HALO;
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(tile + row * ROWB + (2 * ks + hi) * 16);
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[ks], acc[mb], 0, 0, 0);
       }
@@ -116,16 +133,17 @@ __device__ __forceinline__ void conv_head(Acc2& acc, const char* tile, const bf1
 }
 
 // cos / sin of RoPE pair p for the 16 tokens of token block mb a lane's
-// accumulator registers hold (register r: token 32 mb + 8 (r / 4) + 4 hi +
-// r % 4 of the tile), all 16 loads in flight together; (1, 0) without RoPE.
+// accumulator registers hold (register r: token tb0 + 32 mb + 8 (r / 4) + 4 hi
+// + r % 4 of the tile), all 16 loads in flight together; (1, 0) without RoPE.
 // Tokens past the sequence (nrem = tokens of the tile inside it) read the last
 // row: no branch, and their results are never stored.
-__device__ __forceinline__ void load_rope(float2 (&cs)[16], const float2* rope_t0, int mb, int hi,
-                                          int p, int nrem) {
+template <int D>
+__device__ __forceinline__ void load_rope(float2 (&cs)[16], const float2* rope_t0, int tb0, int mb,
+                                          int hi, int p, int nrem) {
   if (rope_t0) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int tr = min(32 * mb + 8 * (r >> 2) + 4 * hi + (r & 3), nrem - 1);
+      const int tr = min(tb0 + 32 * mb + 8 * (r >> 2) + 4 * hi + (r & 3), nrem - 1);
       cs[r] = rope_t0[tr * (D / 2) + p];
     }
   } else {
@@ -135,20 +153,21 @@ __device__ __forceinline__ void load_rope(float2 (&cs)[16], const float2* rope_t
 }
 
 // RoPE of one value given its partner (lane ^ 16): lo lanes hold channel p,
-// hi lanes channel p + 64.
+// hi lanes channel p + D / 2.
 __device__ __forceinline__ float rotate(float x, float2 cs, bool lo_lane) {
   const float xp = __shfl_xor(x, 16);
   return lo_lane ? x * cs.x - xp * cs.y : x * cs.x + xp * cs.y;
 }
 
-// Rows 0 .. HALO - 1 of a tile of the first 64 tokens of a chunk (tokens -4 ..
-// -1) from the rolling state: state + off holds lag 1 of this tile's 128
-// channels, lag l at + (l - 1) * lag_stride; lags past nlag are zero.
+// Rows 0 .. HALO - 1 of the first tile of a chunk (tokens -4 .. -1) from the
+// rolling state: st holds lag 1 of this tile's D channels, lag l at + (l - 1)
+// * lag_stride; lags past nlag are zero.
+template <int D>
 __device__ __forceinline__ void fill_halo(char* tile, const bf16* st, int nlag, long lag_stride) {
   for (int e = threadIdx.x; e < HALO * D; e += 256) {
     const int r = e / D, c = e % D, lag = HALO - r;
     const bf16 v = lag <= nlag ? st[(lag - 1) * lag_stride + c] : (bf16)0.0f;
-    *reinterpret_cast<bf16*>(tile + r * ROWB + c * 2) = v;
+    *reinterpret_cast<bf16*>(tile + r * MGeom<D>::ROWB + c * 2) = v;
   }
 }
 
@@ -156,7 +175,7 @@ __device__ __forceinline__ void fill_halo(char* tile, const bf16* st, int nlag, 
 // resident, so the K side's pre-convolution group mean is read back from LDS
 // instead of being summed in registers, and the head loop unrolls), 0 for any
 // other group size.
-// VARLEN: a chunk of a variable-length batch (vm, 64-token tiles in vm.blk):
+// VARLEN (D = 128): a chunk of a variable-length batch (vm, 64-token tiles in vm.blk):
 // sequence b's tokens are latent rows vm.tok[b] .., at positions vm.start[b]
 // ..; the conv and shift history before its first token comes from a.state;
 // Q'' goes to the packed [Hq][T][d] (T = a.S), K'' and V' to the caches at
@@ -166,10 +185,13 @@ __device__ __forceinline__ void fill_halo(char* tile, const bf16* st, int nlag, 
 // spills).  The body sits in the kernel template itself: moved into a device
 // function it compiles to a slower schedule of the same arithmetic.
 struct NoMap {};
-template <int GC, bool VARLEN, typename Map>
+template <int D, int GC, bool VARLEN, typename Map>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VARLEN ? 1 : 2,
                                                                      VARLEN ? 1 : 2)))
 void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
+  using MG = MGeom<D>;
+  constexpr int TW = MG::TW, TBYTES = MG::TBYTES, ROWB = MG::ROWB;
+  static_assert(!VARLEN || D == 128, "variable-length chunks use 64-token tiles");
   constexpr bool QRES = GC > 0;
   __shared__ __attribute__((aligned(1024))) char lds[(2 + NQS) * TBYTES];
   char* tk = lds;                            // k~ tile
@@ -211,38 +233,40 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const bool lo_lane = l32 < 16;
-  const int pair = 16 * wave + (l32 & 15);   // RoPE pair of this lane's channel
-  const int ch = lo_lane ? pair : pair + 64; // this lane's output channel
+  const int cw = MG::NTG == 1 ? wave : wave % MG::NCW;       // channel group of this wave
+  const int tb0 = MG::NTG == 1 ? 0 : 64 * (wave / MG::NCW);  // first tile token of its two blocks
+  const int pair = 16 * cw + (l32 & 15);     // RoPE pair of this lane's channel
+  const int ch = lo_lane ? pair : pair + D / 2;  // this lane's output channel
   const bf16* qkv_b = reinterpret_cast<const bf16*>(a.qkv) + lat0 * dm.nqkv;
   const float A = (dm.flags & kQkPre) ? 0.5f : 0.0f;
   const float Bc = (dm.flags & kQkPost) ? 0.5f : 0.0f;
   const bool rope = (dm.flags & kRope) != 0;
-  // register r of token block mb holds token 32 mb + 8*(r/4) + 4*hi + r%4 (of the tile)
-  auto trel = [&](int mb, int r) { return 32 * mb + 8 * (r >> 2) + 4 * hi + (r & 3); };
+  // register r of token block mb holds token tb0 + 32 mb + 8*(r/4) + 4*hi + r%4 (of the tile)
+  auto trel = [&](int mb, int r) { return tb0 + 32 * mb + 8 * (r >> 2) + 4 * hi + (r & 3); };
 
   // every tile the work-group needs, in one round
   {
     char* const dst[2 + NQS] = {tk, tv, tq, tq + TBYTES};
     const int cols[2 + NQS] = {dm.nq + g * D, dm.nq + dm.nk + g * D, g * G * D, (g * G + 1) * D};
-    load_tiles(dst, cols, 2 + min(G, NQS), qkv_b, dm.nqkv, S, t0);
+    load_tiles<D>(dst, cols, 2 + min(G, NQS), qkv_b, dm.nqkv, S, t0);
   }
   // the state: [q~ lags 1..kq-1 | k~ lags 1..kk-1 | v~ lag 1], most recent first
   const bf16* st = VARLEN ? reinterpret_cast<const bf16*>(a.state) + (long)b * dm.state_w : nullptr;
   const long st_k = (long)(dm.kq - 1) * dm.nq, st_v = st_k + (long)(dm.kk - 1) * dm.nk;
   if (VARLEN && t0 == 0) {
     __syncthreads();                         // the zero halo rows are stored
-    fill_halo(tk, st + st_k + g * D, dm.kk - 1, dm.nk);
-    fill_halo(tv, st + st_v + g * D, 1, dm.nk);
+    fill_halo<D>(tk, st + st_k + g * D, dm.kk - 1, dm.nk);
+    fill_halo<D>(tv, st + st_v + g * D, 1, dm.nk);
     for (int i = 0; i < min(G, NQS); ++i)
-      fill_halo(tq + i * TBYTES, st + (g * G + i) * D, dm.kq - 1, dm.nq);
+      fill_halo<D>(tq + i * TBYTES, st + (g * G + i) * D, dm.kq - 1, dm.nq);
   }
   const float2* rope_t0 = rope ? a.rope + (long)(pos0 + t0) * (D / 2) : nullptr;
   __syncthreads();
 
   Acc2 kacc, qacc, mpost, mpre;
   zero(kacc);
-  conv_head(kacc, tk, reinterpret_cast<const bf16*>(a.conv_k) + (long)g * dm.kk * D * D, dm.kk,
-            ch, lane);
+  conv_head<D>(kacc, tk, reinterpret_cast<const bf16*>(a.conv_k) + (long)g * dm.kk * D * D, dm.kk,
+               ch, lane, tb0);
   zero(mpost);
   if (!QRES) zero(mpre);
 
@@ -255,18 +279,18 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
       __syncthreads();
       char* const dst[NQS] = {tq, tq + TBYTES};
       const int cols[NQS] = {h * D, (h + 1) * D};
-      load_tiles(dst, cols, min(NQS, G - i), qkv_b, dm.nqkv, S, t0);
+      load_tiles<D>(dst, cols, min(NQS, G - i), qkv_b, dm.nqkv, S, t0);
       if (VARLEN && t0 == 0) {
         __syncthreads();
         for (int s2 = 0; s2 < NQS && i + s2 < G; ++s2)
-          fill_halo(tq + s2 * TBYTES, st + (h + s2) * D, dm.kq - 1, dm.nq);
+          fill_halo<D>(tq + s2 * TBYTES, st + (h + s2) * D, dm.kq - 1, dm.nq);
       }
       __syncthreads();
     }
     const char* tqi = tq + (i % NQS) * TBYTES;
     zero(qacc);
-    conv_head(qacc, tqi, reinterpret_cast<const bf16*>(a.conv_q) + (long)h * dm.kq * D * D,
-              dm.kq, ch, lane);
+    conv_head<D>(qacc, tqi, reinterpret_cast<const bf16*>(a.conv_q) + (long)h * dm.kq * D * D,
+                 dm.kq, ch, lane, tb0);
     const long qrow = VARLEN ? q_row0 + h * q_hstride + t0 : (long)(b * dm.Hq + h) * S + t0;
     bf16* qo = reinterpret_cast<bf16*>(a.q_out) + qrow * D + ch;
 #pragma unroll
@@ -278,13 +302,13 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
       const float2* rp = rope_t0;
       asm volatile("" : "+s"(rp));
       float2 csr[16];
-      load_rope(csr, rp, mb, hi, pair, S - t0);
+      load_rope<D>(csr, rp, tb0, mb, hi, pair, S - t0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tr = trel(mb, r);
         const float qh = qacc[mb][r], kh = kacc[mb][r];
-        const float qp = tile_val(tqi, tr + HALO, ch);
-        const float kp = tile_val(tk, tr + HALO, ch);
+        const float qp = tile_val<D>(tqi, tr + HALO, ch);
+        const float kp = tile_val<D>(tk, tr + HALO, ch);
         mpost[mb][r] += qh;
         if (!QRES) mpre[mb][r] += qp;
         const float y = rotate(qh + A * (qp + kp) + Bc * (qh + kh), csr[r], lo_lane);
@@ -307,15 +331,15 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
     const float2* rp = rope_t0;
     asm volatile("" : "+s"(rp));
     float2 csr[16];
-    load_rope(csr, rp, mb, hi, pair, S - t0);
+    load_rope<D>(csr, rp, tb0, mb, hi, pair, S - t0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tr = trel(mb, r);
       const float kh = kacc[mb][r];
-      const float kp = tile_val(tk, tr + HALO, ch);
+      const float kp = tile_val<D>(tk, tr + HALO, ch);
       float qpre = 0.0f;
       if (QRES) {
-        for (int i = 0; i < G; ++i) qpre += tile_val(tq + i * TBYTES, tr + HALO, ch);
+        for (int i = 0; i < G; ++i) qpre += tile_val<D>(tq + i * TBYTES, tr + HALO, ch);
       } else {
         qpre = mpre[mb][r];
       }
@@ -366,7 +390,7 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         // tokens at or past S are zero: the padding of V'^T up to s_pad
-        const float v = t + i < S ? tile_val(tv, vrow(8 * m + i, c), c) : 0.0f;
+        const float v = t + i < S ? tile_val<D>(tv, vrow(8 * m + i, c), c) : 0.0f;
         pk[i] = (_Float16)v;
       }
       *reinterpret_cast<f16x8*>(vt + (long)c * a.s_pad + t) = pk;
@@ -376,12 +400,12 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
 
 }  // namespace
 
-bool mix_fwd_mfma_supported(const Dims& dm) { return dm.bf16 && dm.d == D; }
+bool mix_fwd_mfma_supported(const Dims& dm) { return dm.bf16 && (dm.d == 128 || dm.d == 64); }
 
 // Variable-length mix (see mix_body): a.S = T, the packed token count; vm.blk
 // counts 64-token tiles; a.state holds each sequence's history before its chunk.
 hipError_t launch_mix_varlen_mfma(const MixArgs& a, const VarlenMap& vm, hipStream_t s) {
-  if (!mix_fwd_mfma_supported(a.dm) || a.qkv_f32 || !a.state || !a.k_out2 || !a.v_out2 ||
+  if (a.dm.d != 128 || !a.dm.bf16 || a.qkv_f32 || !a.state || !a.k_out2 || !a.v_out2 ||
       a.k_out || a.v_out || vm.B < 1 || vm.B > kMaxVarlenBatch)
     return hipErrorInvalidValue;
   if ((long)a.S * a.dm.nqkv * 2 >= (1L << 31)) return hipErrorInvalidValue;
@@ -390,14 +414,31 @@ hipError_t launch_mix_varlen_mfma(const MixArgs& a, const VarlenMap& vm, hipStre
   const int ntiles8 = (ntiles + XCDS - 1) / XCDS * XCDS;
   const dim3 grid((unsigned)(ntiles8 * a.dm.Hkv));
   if (a.dm.G == 1)
-    hipLaunchKernelGGL((mix_fwd_mfma_kernel<1, true, VarlenMap>), grid, dim3(256), 0, s, a,
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<128, 1, true, VarlenMap>), grid, dim3(256), 0, s, a,
                        ntiles8, vm);
   else if (a.dm.G == 2)
-    hipLaunchKernelGGL((mix_fwd_mfma_kernel<2, true, VarlenMap>), grid, dim3(256), 0, s, a,
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<128, 2, true, VarlenMap>), grid, dim3(256), 0, s, a,
                        ntiles8, vm);
   else
-    hipLaunchKernelGGL((mix_fwd_mfma_kernel<0, true, VarlenMap>), grid, dim3(256), 0, s, a,
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<128, 0, true, VarlenMap>), grid, dim3(256), 0, s, a,
                        ntiles8, vm);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mix_fwd_mfma_d(const MixArgs& a, hipStream_t s) {
+  const int ntiles = (a.S + MGeom<D>::TW - 1) / MGeom<D>::TW;
+  const int ntiles8 = (ntiles + XCDS - 1) / XCDS * XCDS;
+  const dim3 grid((unsigned)(ntiles8 * a.dm.Hkv * a.B));
+  if (a.dm.G == 1)
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<D, 1, false, NoMap>), grid, dim3(256), 0, s, a,
+                       ntiles8, NoMap{});
+  else if (a.dm.G == 2)
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<D, 2, false, NoMap>), grid, dim3(256), 0, s, a,
+                       ntiles8, NoMap{});
+  else
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<D, 0, false, NoMap>), grid, dim3(256), 0, s, a,
+                       ntiles8, NoMap{});
   return hipGetLastError();
 }
 
@@ -405,19 +446,9 @@ hipError_t launch_mix_fwd_mfma(const MixArgs& a, hipStream_t s) {
   if (a.vt_out && (a.s_pad % 64 != 0 || a.s_pad < a.S)) return hipErrorInvalidValue;
   // 32-bit byte offsets within one sequence's latent rows
   if ((long)a.S * a.dm.nqkv * 2 >= (1L << 31)) return hipErrorInvalidValue;
-  const int ntiles = (a.S + TW - 1) / TW;
-  const int ntiles8 = (ntiles + XCDS - 1) / XCDS * XCDS;
-  const dim3 grid((unsigned)(ntiles8 * a.dm.Hkv * a.B));
-  if (a.dm.G == 1)
-    hipLaunchKernelGGL((mix_fwd_mfma_kernel<1, false, NoMap>), grid, dim3(256), 0, s, a, ntiles8,
-                       NoMap{});
-  else if (a.dm.G == 2)
-    hipLaunchKernelGGL((mix_fwd_mfma_kernel<2, false, NoMap>), grid, dim3(256), 0, s, a, ntiles8,
-                       NoMap{});
-  else
-    hipLaunchKernelGGL((mix_fwd_mfma_kernel<0, false, NoMap>), grid, dim3(256), 0, s, a, ntiles8,
-                       NoMap{});
-  return hipGetLastError();
+  if (a.dm.d == 128) return launch_mix_fwd_mfma_d<128>(a, s);
+  if (a.dm.d == 64) return launch_mix_fwd_mfma_d<64>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace cca

@@ -1,7 +1,7 @@
-// cca_mix for bf16 storage with an fp32 latent, d = 128, on MFMA: the causal
+// cca_mix for bf16 storage with an fp32 latent, d = 128 or 64, on MFMA: the causal
 // grouped convolution of q~ and k~ (CCA-es §2.B.1 "Mezcla Convolucional"),
 // QK-mean (§2.B.2), value shift (§2.B.3) and RoPE (§3 item 2) in one pass per
-// (64 tokens, KV group).  This is the prefill that saves its stages for the
+// (64 tokens (128 for d = 64), KV group).  This is the prefill that saves its stages for the
 // backward: the latent stays fp32 (split into bf16 hi / lo halves for the
 // MFMAs) because the softmax gradient amplifies a rounding of q~ and k~ into
 // dQ and dK.  The bf16-latent pass for inference is in mix_mfma.hip.
@@ -18,17 +18,24 @@
 // heads and its K head) and both channels of a RoPE pair (c, c + d/2) sit in
 // one lane.
 //
-// Wave w of the 4: tokens t0 + 32*(w/2) .. +31, channel blocks {w%2, w%2 + 2}.
+// The d / 32 channel blocks of 32 pair up as (cb, cb + d / 64) (RoPE partners
+// d / 2 apart).  Wave w of the 4, with P = d / 64 pairs: tokens t0 + 32 (w / P)
+// .. + 31, channel blocks {w % P, w % P + P}; so a work-group covers 64 tokens
+// at d = 128 and 128 at d = 64.
 #include "cca_internal.h"
 
 namespace cca {
 namespace {
 
-constexpr int D = 128;
-constexpr int TW = 64;               // tokens per work-group
-constexpr int ULD = D + 8;           // LDS row stride (bf16): 272 B, conflict-free b128 reads
-constexpr int UROWS = TW + kMaxConv - 1;
-constexpr int UHALF = UROWS * ULD;   // lo rows follow the hi rows
+template <int D>
+struct FGeom {
+  static constexpr int P = D / 64;             // channel-block pairs (waves per token block)
+  static constexpr int TW = 32 * 4 / P;        // tokens per work-group
+  static constexpr int ULD = D + 8;            // LDS row stride (bf16): one 16-byte chunk of pad,
+                                               // conflict-free b128 reads
+  static constexpr int UROWS = TW + kMaxConv - 1;
+  static constexpr int UHALF = UROWS * ULD;    // lo rows follow the hi rows
+};
 
 typedef f32x16 Acc2[2];              // [channel block]
 
@@ -45,8 +52,10 @@ __device__ __forceinline__ void zero(Acc2& a) {
 // the tile's rows inside [0, S) (a row before it wraps to a huge offset):
 // out-of-range rows read as zero without a branch, so each batch of four loads is in flight
 // together before its conversions and LDS stores.
+template <int D>
 __device__ __forceinline__ void load_tile(bf16* u, const float* qkv_b, int nqkv, int col, int S,
                                           int t0, int halo) {
+  constexpr int TW = FGeom<D>::TW, ULD = FGeom<D>::ULD, UHALF = FGeom<D>::UHALF;
   const int n = (TW + halo) * (D / 4);
   // resource over the tile's rows inside [0, S), based at its first one
   const int r0 = max(t0 - halo, 0), r1 = min(S, t0 + TW);
@@ -87,6 +96,7 @@ __device__ __forceinline__ void load_tile(bf16* u, const float* qkv_b, int nqkv,
 // 16 loads in flight together; (1, 0) without RoPE.  Rows past the sequence
 // (nrem = tokens of the tile inside it) read the last row: no branch, and
 // their results are never stored.
+template <int D>
 __device__ __forceinline__ void load_rope(float2 (&cs)[16], const float2* rope_t0, int first,
                                           int c_lo, int nrem) {
   if (rope_t0) {
@@ -102,20 +112,24 @@ __device__ __forceinline__ void load_rope(float2 (&cs)[16], const float2* rope_t
 }
 
 // The pre-convolution value hi + lo of LDS row i, channel c.
+template <int D>
 __device__ __forceinline__ float uval(const bf16* u, int i, int c) {
+  constexpr int ULD = FGeom<D>::ULD, UHALF = FGeom<D>::UHALF;
   return (float)u[i * ULD + c] + (float)u[UHALF + i * ULD + c];
 }
 
 // acc += conv of one head whose tile is in LDS (row of token t: t - t0 + halo).
+template <int D>
 __device__ __forceinline__ void conv_head(Acc2& acc, const bf16* u, int halo, int tw0_rel,
                                           const bf16* taps, int k, int cb0, int lane) {
+  constexpr int ULD = FGeom<D>::ULD, UHALF = FGeom<D>::UHALF;
   const int l32 = lane & 31, hi = lane >> 5;
   for (int j = 0; j < k; ++j) {
     const bf16* urow = u + (tw0_rel + l32 - j + halo) * ULD + hi * 8;
     const bf16* trow0 = taps + ((long)j * D + cb0 * 32 + l32) * D + hi * 8;
-    const bf16* trow1 = trow0 + 64 * D;
+    const bf16* trow1 = trow0 + (D / 2) * D;
 #pragma unroll 4
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < D / 16; ++ks) {
       const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(urow + ks * 16);
       const bf16x8 alo = *reinterpret_cast<const bf16x8*>(urow + UHALF + ks * 16);
       const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(trow0 + ks * 16);
@@ -128,8 +142,11 @@ __device__ __forceinline__ void conv_head(Acc2& acc, const bf16* u, int halo, in
   }
 }
 
+template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mix_fwd_mfma_f32lat_kernel(MixArgs a) {
+  using FG = FGeom<D>;
+  constexpr int TW = FG::TW, ULD = FG::ULD, UHALF = FG::UHALF, P = FG::P;
   __shared__ __attribute__((aligned(16))) bf16 uk[2 * UHALF];   // k~ tile (hi, lo)
   __shared__ __attribute__((aligned(16))) bf16 uq[2 * UHALF];   // current q~ tile, then v~
   const Dims& dm = a.dm;
@@ -138,24 +155,24 @@ void mix_fwd_mfma_f32lat_kernel(MixArgs a) {
   const int t0 = blockIdx.x * TW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int tw0_rel = 32 * (wave >> 1);      // this wave's first token, relative to t0
-  const int cb0 = wave & 1;                  // channel blocks cb0 and cb0 + 2
+  const int tw0_rel = 32 * (wave / P);       // this wave's first token, relative to t0
+  const int cb0 = wave % P;                  // channel blocks cb0 and cb0 + P
   const float* qkv_b = reinterpret_cast<const float*>(a.qkv) + (long)b * S * dm.nqkv;
   const float A = (dm.flags & kQkPre) ? 0.5f : 0.0f;
   const float Bc = (dm.flags & kQkPost) ? 0.5f : 0.0f;
   const bool rope = (dm.flags & kRope) != 0;
   const int kcol = dm.nq + g * D;
   const int hq = dm.kq - 1, hk = dm.kk - 1;  // halo rows of the q and k tiles
-  const int c_lo = cb0 * 32 + l32;           // < 64: RoPE pair (c_lo, c_lo + 64)
+  const int c_lo = cb0 * 32 + l32;           // < D / 2: RoPE pair (c_lo, c_lo + D / 2)
   // register r holds token tw0_rel + 8*(r/4) + 4*hi + r%4 (relative to t0)
   auto trel = [&](int r) { return tw0_rel + 8 * (r >> 2) + 4 * hi + (r & 3); };
 
   const float2* rope_t0 = rope ? a.rope + (long)t0 * (D / 2) : nullptr;
-  load_tile(uk, qkv_b, dm.nqkv, kcol, S, t0, hk);
+  load_tile<D>(uk, qkv_b, dm.nqkv, kcol, S, t0, hk);
   __syncthreads();
   Acc2 kacc, qacc, mpost, mpre;
   zero(kacc);
-  conv_head(kacc, uk, hk, tw0_rel,
+  conv_head<D>(kacc, uk, hk, tw0_rel,
             reinterpret_cast<const bf16*>(a.conv_k) + (long)g * dm.kk * D * D, dm.kk, cb0, lane);
   zero(mpost);
   zero(mpre);
@@ -163,16 +180,16 @@ void mix_fwd_mfma_f32lat_kernel(MixArgs a) {
   for (int i = 0; i < G; ++i) {
     const int h = g * G + i;
     if (i > 0) __syncthreads();              // every wave is done with the previous q tile
-    load_tile(uq, qkv_b, dm.nqkv, h * D, S, t0, hq);
+    load_tile<D>(uq, qkv_b, dm.nqkv, h * D, S, t0, hq);
     __syncthreads();
     zero(qacc);
-    conv_head(qacc, uq, hq, tw0_rel,
+    conv_head<D>(qacc, uq, hq, tw0_rel,
               reinterpret_cast<const bf16*>(a.conv_q) + (long)h * dm.kq * D * D, dm.kq, cb0,
               lane);
     // tile bases plus 32-bit offsets (tokens relative to t0)
     bf16* qo = reinterpret_cast<bf16*>(a.q_out) + ((long)(b * dm.Hq + h) * S + t0) * D;
     float2 csr[16];
-    load_rope(csr, rope_t0, trel(0), c_lo, S - t0);
+    load_rope<D>(csr, rope_t0, trel(0), c_lo, S - t0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tr = trel(r);
@@ -180,10 +197,10 @@ void mix_fwd_mfma_f32lat_kernel(MixArgs a) {
       float x[2];
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const int c = c_lo + 64 * cb;
+        const int c = c_lo + (D / 2) * cb;
         const float qh = qacc[cb][r], kh = kacc[cb][r];
-        const float qp = uval(uq, tr + hq, c);
-        const float kp = uval(uk, tr + hk, c);
+        const float qp = uval<D>(uq, tr + hq, c);
+        const float kp = uval<D>(uk, tr + hk, c);
         mpost[cb][r] += qh;
         mpre[cb][r] += qp;
         x[cb] = qh + A * (qp + kp) + Bc * (qh + kh);
@@ -191,7 +208,7 @@ void mix_fwd_mfma_f32lat_kernel(MixArgs a) {
       if (t < S) {
         const float2 cs = csr[r];
         qo[tr * D + c_lo] = (bf16)(x[0] * cs.x - x[1] * cs.y);
-        qo[tr * D + c_lo + 64] = (bf16)(x[1] * cs.x + x[0] * cs.y);
+        qo[tr * D + c_lo + D / 2] = (bf16)(x[1] * cs.x + x[0] * cs.y);
       }
     }
   }
@@ -203,7 +220,7 @@ void mix_fwd_mfma_f32lat_kernel(MixArgs a) {
                   ? reinterpret_cast<bf16*>(a.k_out2) + ((long)(b * dm.Hkv + g) * a.cap2 + t0) * D
                   : nullptr;
   float2 csr[16];
-  load_rope(csr, rope_t0, trel(0), c_lo, S - t0);
+  load_rope<D>(csr, rope_t0, trel(0), c_lo, S - t0);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int tr = trel(r);
@@ -211,9 +228,9 @@ void mix_fwd_mfma_f32lat_kernel(MixArgs a) {
     float x[2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const int c = c_lo + 64 * cb;
+      const int c = c_lo + (D / 2) * cb;
       const float kh = kacc[cb][r];
-      const float kp = uval(uk, tr + hk, c);
+      const float kp = uval<D>(uk, tr + hk, c);
       x[cb] = kh + A * (mpre[cb][r] * invG + kp) + Bc * (mpost[cb][r] * invG + kh);
     }
     if (t < S) {
@@ -221,10 +238,10 @@ void mix_fwd_mfma_f32lat_kernel(MixArgs a) {
       const bf16 lo = (bf16)(x[0] * cs.x - x[1] * cs.y);
       const bf16 hv = (bf16)(x[1] * cs.x + x[0] * cs.y);
       ko[tr * D + c_lo] = lo;
-      ko[tr * D + c_lo + 64] = hv;
+      ko[tr * D + c_lo + D / 2] = hv;
       if (ko2) {
         ko2[tr * D + c_lo] = lo;
-        ko2[tr * D + c_lo + 64] = hv;
+        ko2[tr * D + c_lo + D / 2] = hv;
       }
     }
   }
@@ -233,7 +250,7 @@ void mix_fwd_mfma_f32lat_kernel(MixArgs a) {
   // then V' in the standard layout (when asked) and transposed, V'^T[c][t]
   __syncthreads();
   const int vcol = dm.nq + dm.nk + g * D;
-  load_tile(uq, qkv_b, dm.nqkv, vcol, S, t0, 1);
+  load_tile<D>(uq, qkv_b, dm.nqkv, vcol, S, t0, 1);
   __syncthreads();
   const int first_shift = (dm.flags & kVShift) ? D - dm.sv : D;
   bf16* vo = a.v_out ? reinterpret_cast<bf16*>(a.v_out) + ((long)(b * dm.Hkv + g) * S) * D
@@ -278,8 +295,15 @@ void mix_fwd_mfma_f32lat_kernel(MixArgs a) {
 
 hipError_t launch_mix_fwd_mfma_f32lat(const MixArgs& a, hipStream_t s) {
   if (a.vt_out && (a.s_pad % 64 != 0 || a.s_pad < a.S)) return hipErrorInvalidValue;
-  dim3 grid((a.S + TW - 1) / TW, a.dm.Hkv, a.B);
-  hipLaunchKernelGGL(mix_fwd_mfma_f32lat_kernel, grid, dim3(256), 0, s, a);
+  if (a.dm.d == 128) {
+    dim3 grid((a.S + FGeom<128>::TW - 1) / FGeom<128>::TW, a.dm.Hkv, a.B);
+    hipLaunchKernelGGL(mix_fwd_mfma_f32lat_kernel<128>, grid, dim3(256), 0, s, a);
+  } else if (a.dm.d == 64) {
+    dim3 grid((a.S + FGeom<64>::TW - 1) / FGeom<64>::TW, a.dm.Hkv, a.B);
+    hipLaunchKernelGGL(mix_fwd_mfma_f32lat_kernel<64>, grid, dim3(256), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

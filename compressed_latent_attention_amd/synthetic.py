@@ -92,6 +92,10 @@ WORKLOADS: Dict[str, Workload] = {
     # the 16x-compressed variant: one KV head (half the CCGQA layer's KV cache)
     "ccgqa16_prefill_16k": Workload("ccgqa16_prefill_16k", B=1, S=16384, E=2048, C=4, Hq=4,
                                     Hkv=1, seed=8),
+    # head dimension 64: the same latent (512 query, 256 KV channels) as 8 query
+    # heads and 4 KV heads of 64, so the same 8x smaller KV cache than MHA
+    "ccgqa_d64_prefill_16k": Workload("ccgqa_d64_prefill_16k", B=1, S=16384, E=2048, C=4, Hq=8,
+                                      Hkv=4, seed=9),
 }
 
 

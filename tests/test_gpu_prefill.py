@@ -101,9 +101,13 @@ SMALL_BF16 = [
              seed=36),
     Workload("bf16_gqa_c1", B=1, S=200, E=2048, C=1, Hq=16, Hkv=2, kq=1, kk=1, flags=4,
              seed=37),
-    # the 16x variant (one KV head) and d = 64 (the generic kernels)
+    # the 16x variant (one KV head) and d = 64: group sizes 2, 1 and 4, three
+    # taps, the flag subsets, several 128-token tiles with ragged tails
     Workload("bf16_ccgqa16", B=1, S=200, E=2048, C=4, Hq=4, Hkv=1, seed=38),
     Workload("bf16_d64", B=1, S=150, E=512, C=2, Hq=4, Hkv=2, seed=39),
+    Workload("bf16_d64_g1_b2", B=2, S=333, E=512, C=2, Hq=4, Hkv=4, seed=45),
+    Workload("bf16_d64_g4_k3", B=1, S=260, E=1024, C=2, Hq=8, Hkv=2, kq=3, kk=2, seed=46),
+    Workload("bf16_d64_flags", B=1, S=129, E=512, C=2, Hq=4, Hkv=2, flags=2 | 8, sv=17, seed=47),
     Workload("bf16_tiny_tail", B=1, S=65, E=512, C=2, Hq=2, Hkv=1, flags=1 | 4 | 8, sv=40,
              seed=36),
 ]
@@ -124,6 +128,13 @@ def test_prefill_ccgqa_16k_full():
     configuration the benchmark times: y and every saved stage against the
     oracle's forward, whole-tensor and per 128-token block."""
     w = WORKLOADS["ccgqa_prefill_16k"]
+    check_prefill(w, make_inputs(w))
+
+
+def test_prefill_ccgqa_d64_16k_full():
+    """The d = 64 CCGQA layer at full size (S = 16384, E = 2048, 8 query heads
+    and 4 KV heads of 64): y and every saved stage against the oracle."""
+    w = WORKLOADS["ccgqa_d64_prefill_16k"]
     check_prefill(w, make_inputs(w))
 
 
