@@ -254,13 +254,13 @@ def _time_warm(torch, fn, steps, warm_s=0.15):
     return _time_loop(torch, fn, steps, max(steps, int(warm_s / one)))
 
 
-def bench_decode(args, torch, cca, hkv=None):
+def bench_decode(args, torch, cca, hkv=None, w=None):
     """32-sequence CCGQA decode step over a 32768-token cache.  The cache, the
     state and x_new are drawn on the GPU from a seeded torch generator (N(0,1),
     the same law as the parity workload; the timing does not depend on the
     values), the weights from the seeded parity recipe."""
     from compressed_latent_attention_amd.synthetic import WORKLOADS, make_inputs
-    w = WORKLOADS["ccgqa_decode_32k"]
+    w = w or WORKLOADS["ccgqa_decode_32k"]
     if hkv is not None:
         w = w.replace(Hkv=hkv)
     layer = cca.CCALayer(w.E, w.C, w.Hq, w.Hkv, w.capacity, w.kq, w.kk, w.s_v, w.flags,
@@ -297,7 +297,7 @@ def bench_decode(args, torch, cca, hkv=None):
     cache_bytes = 2.0 * w.B * w.Hkv * (w.S + 1) * w.d * 2
     layer.close()
     return {
-        "workload": f"ccgqa_decode_32k: B={w.B}, cache {w.S} tokens, E={w.E}, Hq={w.Hq}, "
+        "workload": f"{w.name}: B={w.B}, cache {w.S} tokens, E={w.E}, Hq={w.Hq}, "
                     f"Hkv={w.Hkv}, d={w.d}, bf16",
         "tokens_per_s": w.B / sec,
         "ms_per_step": sec * 1e3,
@@ -312,10 +312,10 @@ def bench_decode(args, torch, cca, hkv=None):
     }
 
 
-def bench_backward(args, torch, cca):
+def bench_backward(args, torch, cca, w=None):
     """CCGQA backward at S=16384 from a saved prefill of the same seeded x."""
     from compressed_latent_attention_amd.synthetic import WORKLOADS, make_inputs
-    w = WORKLOADS["ccgqa_backward_16k"]
+    w = w or WORKLOADS["ccgqa_backward_16k"]
     inp = make_inputs(w)
     layer = cca.CCALayer(w.E, w.C, w.Hq, w.Hkv, w.capacity, w.kq, w.kk, w.s_v, w.flags,
                          w.rope_base, w.dtype)
@@ -345,7 +345,7 @@ def bench_backward(args, torch, cca):
     kernels = {k: {"avg_ms": v[1] / max(v[0], 1), "launches": v[0]} for k, v in prof.items()}
     layer.close()
     return {
-        "workload": f"ccgqa_backward_16k: B={w.B}, S={w.S}, E={w.E}, Hq={w.Hq}, Hkv={w.Hkv}, "
+        "workload": f"{w.name}: B={w.B}, S={w.S}, E={w.E}, Hq={w.Hq}, Hkv={w.Hkv}, "
                     f"d={w.d}, bf16 storage, fp32 accumulation",
         "tokens_per_s": w.B * w.S / sec,
         "ms_per_step": sec * 1e3,
@@ -356,6 +356,38 @@ def bench_backward(args, torch, cca):
         "frac_of_bf16_peak": total / sec / 1e12 / PEAK_BF16_TFLOPS,
         "kernels": kernels,
     }
+
+
+def bench_d64(args, torch, cca):
+    """The CCGQA layer with head dimension 64 (8 query and 4 KV heads of 64:
+    the same latent widths and KV-cache size as the d = 128 layer): the 16k
+    prefill with its kernel times and the attention's MFMA fraction, the
+    decode step over a 32k cache and the 16k backward."""
+    from compressed_latent_attention_amd.synthetic import WORKLOADS, make_inputs
+    w = WORKLOADS["ccgqa_d64_prefill_16k"]
+    inp = make_inputs(w)
+    a2 = argparse.Namespace(**vars(args))
+    a2.steps = 20
+    elapsed, _, prof, layer, _ = bench_prefill(a2, torch, cca, w, inp)
+    layer.close()
+    ms = elapsed * 1e3 / a2.steps
+    fl = prefill_flops(w)
+    kernels = {k: {"avg_ms": v[1] / max(v[0], 1), "launches": v[0],
+                   "tflops": (fl[k] / (v[1] / max(v[0], 1) * 1e-3) / 1e12) if k in fl else None}
+               for k, v in prof.items()}
+    attn = kernels.get("attn", {})
+    pre = {"workload": f"{w.name}: B={w.B}, S={w.S}, E={w.E}, C={w.C}, Hq={w.Hq}, Hkv={w.Hkv}, "
+                       f"d={w.d}, bf16",
+           "tokens_per_s": w.B * w.S / elapsed * a2.steps, "ms_per_step": ms,
+           "layer_frac_of_bf16_peak": sum(fl.values()) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "attn_frac_of_bf16_peak": (attn.get("tflops") or float("nan")) / PEAK_BF16_TFLOPS,
+           "kernels": kernels}
+    dec = bench_decode(args, torch, cca,
+                       w=WORKLOADS["ccgqa_decode_32k"].replace(name="ccgqa_d64_decode_32k", Hq=8,
+                                                               Hkv=4))
+    bwd = bench_backward(args, torch, cca,
+                         w=w.replace(name="ccgqa_d64_backward_16k", kind="backward"))
+    return {"prefill": pre, "decode": dec, "backward": bwd}
 
 
 def _gpu_layer(torch, cca, w, gen):
@@ -470,9 +502,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--warm-s", type=float, default=0.3,
                     help="untimed prefill steps continue past --warmup until this many seconds")
-    ap.add_argument("--rows", default="prefill,mix,decode,backward",
+    ap.add_argument("--rows", default="prefill,mix,decode,backward,d64",
                     help="comma list: prefill (headline, always run), mix (the mix kernel with "
-                         "cold caches), decode, backward; n1 adds the MHA / GQA comparators over "
+                         "cold caches), decode, backward, d64 (the head-dimension-64 layer: "
+                         "prefill, decode, backward); n1 adds the MHA / GQA comparators over "
                          "S = 4k .. 64k (not run by default)")
     ap.add_argument("--bwd-steps", type=int, default=3, help="timed backward steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -548,6 +581,8 @@ def main():
         out["decode"] = bench_decode(args, torch, cca)
     if "backward" in rows:
         out["backward"] = bench_backward(args, torch, cca)
+    if "d64" in rows:
+        out["d64"] = bench_d64(args, torch, cca)
     if "n1" in rows:
         out["n1"] = bench_n1(args, torch, cca)
     if not args.no_cpu_baseline:

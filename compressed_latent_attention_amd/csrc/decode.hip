@@ -13,13 +13,14 @@
 //      of its row per load); the fp32 scores are then scaled to log2 units.
 //   2. Block max over the 32 keys by DPP and a swizzle, rescale of the running
 //      O and l, p = exp2(s - m) to a per-wave LDS row block.
-//   3. O += P V on the vector ALU: lane = 8 channels of one of 4 keys, so a
-//      wave load covers four 256-byte V rows.
+//   3. O += P V on the vector ALU: lane = 8 channels of one of 64 / (d / 8)
+//      keys, so a wave load covers 1 KB of whole V rows (4 rows at d = 128,
+//      8 at d = 64).
 // The next block's K and V rows are requested while the current one is
 // computed.  The four waves of a work-group merge in LDS into one partial
 // (O, m, l); a second kernel merges the partials of each (sequence, query
 // head) and writes O in bf16.
-// bf16 storage, d = 128; fp32 accumulation and softmax.
+// bf16 storage, d = 128 or 64; fp32 accumulation and softmax.
 #include "cca_internal.h"
 
 #include <algorithm>
@@ -27,14 +28,16 @@
 namespace cca {
 namespace {
 
-constexpr int D = 128;
 constexpr int NW = 4;            // waves per work-group
 constexpr int TARGET_WGS = 256;  // work-groups per launch: two per CU, all resident at once
-constexpr int PSTRIDE = D + 2;   // floats per partial: O[0..D), m, l
 
 constexpr int MAX_SPLIT = 1024;  // work-groups per (sequence, KV head) the merge kernel holds
 
-bool fast_decode(const Dims& dm) { return dm.bf16 && dm.d == D && dm.G <= kMaxGroup; }
+bool fast_decode(const Dims& dm) {
+  return dm.bf16 && (dm.d == 128 || dm.d == 64) && dm.G <= kMaxGroup;
+}
+// floats per partial: O[0..d), m, l
+int pstride(const Dims& dm) { return dm.d + 2; }
 
 // Max over each 32-lane half of the wave: DPP within rows of 16 lanes (swap
 // neighbours, pairs, mirror in 8, mirror in 16), then a swizzle that exchanges
@@ -63,8 +66,13 @@ __device__ __forceinline__ float half_max(float v) {
 // block n + 1 are already requested (a ring of 8 + 8 fragment registers, each
 // slot refilled as soon as it has been read).  The four waves are merged in
 // LDS at the end.
-template <int GQ>
+template <int D, int GQ>
 __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
+  constexpr int PSTRIDE = D + 2;
+  constexpr int NKS = D / 16;                        // 16-channel k-steps of S = Q K^T
+  constexpr int CPL = D / 8;                         // lanes per V row in P V
+  constexpr int SLOTS = 64 / CPL;                    // V rows per wave load
+  constexpr int NV = 32 / SLOTS;                     // V loads per 32-key block
   constexpr int PW = 8;                              // p row per key: queries 0..7
   constexpr int NR = GQ < 4 ? GQ : 4;                // score rows per lane half that matter
   __shared__ __attribute__((aligned(16))) float pbuf[NW][32 * PW];   // p of the current block
@@ -98,27 +106,27 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
   // softmax, so Q is not rounded a second time.
   // D[query][key]: lane holds key l32, query rows 4 hi + r in acc[r], r < 4.
   const float scale = 1.44269504088896340736f / sqrtf((float)D);
-  bf16x8 qf[8];
+  bf16x8 qf[NKS];
   {
     const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + ((long)b * dm.Hq + g * G + l32) * D;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)0.0f;
       if (l32 < G) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + hi * 8);
     }
   }
-  // P V on the vector ALU: lane = (key slot L / 16, channels 8 (L % 16) .. + 7)
-  // takes keys slot + 4 i (i < 8) of a block, so one wave load covers four
-  // whole 256-byte V rows.
-  const int slot = lane >> 4, cc = (lane & 15) * 8;
+  // P V on the vector ALU: lane = (key slot L / CPL, channels 8 (L % CPL) ..
+  // + 7) takes keys slot + SLOTS i (i < NV) of a block, so one wave load
+  // covers SLOTS whole V rows.
+  const int slot = lane / CPL, cc = (lane % CPL) * 8;
   auto kload = [&](int blk, int ks) {
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                           krs, ((blk * 32 + l32) * D + ks * 16 + hi * 8) * 2, 0, 0));
   };
   auto vload = [&](int blk, int i) {
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                          vrs, ((blk * 32 + slot + 4 * i) * D + cc) * 2, 0, 0));
+                                          vrs, ((blk * 32 + slot + SLOTS * i) * D + cc) * 2, 0, 0));
   };
 
   float m[NR], lsum[NR];                 // running max and this lane's share of the sum
@@ -133,12 +141,12 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[q][e] = 0.0f;
 
-  bf16x8 kr[8], vr[8];
+  bf16x8 kr[NKS], vr[NV];
   int blk = first;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) kr[j] = kload(blk, j);
+  for (int j = 0; j < NKS; ++j) kr[j] = kload(blk, j);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) vr[j] = vload(blk, j);
+  for (int j = 0; j < NV; ++j) vr[j] = vload(blk, j);
   float* pw = pbuf[wave];
   for (int it = 0; it < nit; ++it) {
     const int nxt = blk + stride;
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kr[ks], acc, 0, 0, 0);
       kr[ks] = kload(nxt, ks);
     }
@@ -179,15 +187,15 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[q][e] *= aq;
     }
-    // the p rows of this lane's 8 keys, read together (one wait)
-    f32x4 pa[8], pb[8];
+    // the p rows of this lane's NV keys, read together (one wait)
+    f32x4 pa[NV], pb[NV];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pa[i] = *reinterpret_cast<const f32x4*>(&pw[(slot + 4 * i) * PW]);
-      if (GQ > 4) pb[i] = *reinterpret_cast<const f32x4*>(&pw[(slot + 4 * i) * PW + 4]);
+    for (int i = 0; i < NV; ++i) {
+      pa[i] = *reinterpret_cast<const f32x4*>(&pw[(slot + SLOTS * i) * PW]);
+      if (GQ > 4) pb[i] = *reinterpret_cast<const f32x4*>(&pw[(slot + SLOTS * i) * PW + 4]);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NV; ++i) {
       // the slot is refilled only once its rows are converted, so the new
       // load lands in the same registers (no copy that would wait for it)
       float vf[8];
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
     }
     blk = nxt;
   }
-  // this wave's l (over the 32 lanes of each half) and O (over the 4 key slots)
+  // this wave's l (over the 32 lanes of each half) and O (over the key slots)
 #pragma unroll
   for (int r = 0; r < NR; ++r)
 #pragma unroll
@@ -212,10 +220,9 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
 #pragma unroll
   for (int q = 0; q < GQ; ++q)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[q][e] += __shfl_xor(o[q][e], 16);
-      o[q][e] += __shfl_xor(o[q][e], 32);
-    }
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int off = CPL; off < 64; off <<= 1) o[q][e] += __shfl_xor(o[q][e], off);
   if (slot == 0)
 #pragma unroll
     for (int q = 0; q < GQ; ++q)
@@ -261,7 +268,9 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
 // and weights in parallel (one thread per partial, through LDS), then one
 // thread per channel sums its weighted partial O over them.  Partial 0 always
 // holds key 0, so the merged max is finite and the weight sum is >= 1.
+template <int D>
 __global__ __launch_bounds__(D) void attn_decode_merge_kernel(AttnArgs a) {
+  constexpr int PSTRIDE = D + 2;
   __shared__ float wgt[MAX_SPLIT];
   __shared__ float red[D / 64][2];
   const Dims& dm = a.dm;
@@ -311,23 +320,33 @@ int decode_nsplit(const Dims& dm, int B) {
 }
 
 size_t decode_part_floats(const Dims& dm, int B) {
-  return fast_decode(dm) ? (size_t)B * dm.Hq * decode_nsplit(dm, B) * PSTRIDE : 0;
+  return fast_decode(dm) ? (size_t)B * dm.Hq * decode_nsplit(dm, B) * pstride(dm) : 0;
 }
+
+namespace {
+template <int D>
+void launch_decode_d(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(a.nsplit, a.dm.Hkv, a.B);
+  if (a.dm.G <= 1)
+    hipLaunchKernelGGL((attn_decode_split_kernel<D, 1>), grid, dim3(256), 0, s, a);
+  else if (a.dm.G <= 2)
+    hipLaunchKernelGGL((attn_decode_split_kernel<D, 2>), grid, dim3(256), 0, s, a);
+  else if (a.dm.G <= 4)
+    hipLaunchKernelGGL((attn_decode_split_kernel<D, 4>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_decode_split_kernel<D, 8>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(a.dm.Hq, a.B), dim3(D), 0, s, a);
+}
+}  // namespace
 
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s) {
   if (!fast_decode(a.dm)) return launch_attn_fwd(a, s);
   if (a.part == nullptr || a.nsplit != decode_nsplit(a.dm, a.B) || a.nsplit > MAX_SPLIT)
     return hipErrorInvalidValue;
-  const dim3 grid(a.nsplit, a.dm.Hkv, a.B);
-  if (a.dm.G <= 1)
-    hipLaunchKernelGGL(attn_decode_split_kernel<1>, grid, dim3(256), 0, s, a);
-  else if (a.dm.G <= 2)
-    hipLaunchKernelGGL(attn_decode_split_kernel<2>, grid, dim3(256), 0, s, a);
-  else if (a.dm.G <= 4)
-    hipLaunchKernelGGL(attn_decode_split_kernel<4>, grid, dim3(256), 0, s, a);
+  if (a.dm.d == 128)
+    launch_decode_d<128>(a, s);
   else
-    hipLaunchKernelGGL(attn_decode_split_kernel<8>, grid, dim3(256), 0, s, a);
-  hipLaunchKernelGGL(attn_decode_merge_kernel, dim3(a.dm.Hq, a.B), dim3(D), 0, s, a);
+    launch_decode_d<64>(a, s);
   return hipGetLastError();
 }
 

@@ -375,6 +375,13 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
+// The same over rows of 8 lanes (neighbours, pairs, mirror within 8).
+__device__ __forceinline__ float row8_sum(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141>(v);   // row_half_mirror
+  return v;
+}
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_mov<0xB1>(v);    // quad_perm [1, 0, 3, 2]
   v += dpp_mov<0x4E>(v);    // quad_perm [2, 3, 0, 1]
@@ -383,7 +390,7 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-// Decode-step mix in one kernel (bf16 storage, d = 128, at most 4 taps):
+// Decode-step mix in one kernel (bf16 storage, d = 128 or 64, at most 4 taps):
 // one work-group of 1024 threads per (KV group g, sequence b) does what the
 // two kernels above do for that group, with the token's latents summed from
 // the projection's K-slice partials as they are read.  The step is a chain of
@@ -392,20 +399,23 @@ __device__ __forceinline__ float row16_sum(float v) {
 // of position p, and the tap rows of each wave's first 12 convolution groups.
 //   1. lag 0 of the G query heads, the key head and the new v (sums of the
 //      partials), the lags >= 1 and the previous v to LDS;
-//   2. convolution: a group = 4 consecutive output channels of one (head, tap)
-//      pair, whose tap rows are 1 KB contiguous: one 16-byte load per lane
-//      (lane = row slot L / 16, input channels 8 (L % 16) .. + 7), partial dot
-//      products with the lag-j latent from LDS, summed over the 16 lanes of a
-//      row by DPP;
+//   2. convolution: a group = the 1024 / 2d consecutive output channels of
+//      one (head, tap) pair whose tap rows make 1 KB: one 16-byte load per
+//      lane (lane = row slot L / (d / 8), input channels 8 (L % (d / 8)) ..
+//      + 7), partial dot products with the lag-j latent from LDS, summed over
+//      the d / 8 lanes of a row by DPP;
 //   3. the taps' terms summed per (head, channel), then QK-mean, RoPE, value
 //      shift, the q / cache stores and the advanced state as above.
 // The group's state is read in 1. and written in 3. by this work-group only.
-constexpr int FD = 128;                 // head dim of the fused path
 constexpr int FKMAX = 4;                // taps per convolution at most
 constexpr int FNH = kMaxGroup + 1;      // heads of a KV group: G query heads + 1 key head
 constexpr int FZ = 8;                   // K-slice partials read in the first round
 
+template <int FD>
 __global__ __launch_bounds__(1024) void mix_decode_fused_kernel(MixDecodeArgs a) {
+  constexpr int LPR = FD / 8;             // lanes per tap row
+  constexpr int GCH = 64 / LPR;           // output channels (tap rows) per group
+  constexpr int GPP = FD / GCH;           // groups per (head, tap) pair
   __shared__ __attribute__((aligned(16))) float u[FKMAX][FNH][FD];     // pre-conv latents by lag
   __shared__ __attribute__((aligned(16))) float cvp[FKMAX][FNH][FD];   // convolution terms by tap
   __shared__ __attribute__((aligned(16))) float cv[FNH][FD];           // convolution outputs
@@ -418,12 +428,12 @@ __global__ __launch_bounds__(1024) void mix_decode_fused_kernel(MixDecodeArgs a)
   // the wave index in a scalar register: group indices, (head, tap) pairs and
   // the choice of tap tensor are then uniform, with no per-lane pointer select
   const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int slot = lane >> 4, ci = (lane & 15) * 8;
+  const int slot = lane / LPR, ci = (lane % LPR) * 8;
   const long srow = (long)b * dm.state_w;
   const int nqpart = (kq - 1) * dm.nq, nkpart = (kk - 1) * dm.nk;
   const bf16* st = reinterpret_cast<const bf16*>(a.state);
   const int half = FD / 2;
-  const int nr = G * kq + kk, ngroups = nr * (FD / 4);
+  const int nr = G * kq + kk, ngroups = nr * GPP;
   // integer division by run-time values expands to long scalar sequences that
   // every wave would issue; the divisors here are small: k <= 4 as
   // r * ceil(65536 / k) >> 16 (exact for r < 4096), NH <= 9 through a float
@@ -444,7 +454,7 @@ __global__ __launch_bounds__(1024) void mix_decode_fused_kernel(MixDecodeArgs a)
   const long dqk = reinterpret_cast<const char*>(a.conv_k) - tq;
   const int GK = G * kq;
   auto tap_load = [&](int q) {                      // this lane's 16 bytes of group q
-    const int r = q >> 5, c = (q & 31) * 4 + slot;  // FD / 4 = 32 groups per pair
+    const int r = q / GPP, c = (q % GPP) * GCH + slot;
     const long mat = r < GK ? (long)g * GK + r : (long)g * kk + (r - GK);
     const char* row = tq + (r < GK ? 0 : dqk) + ((mat * FD + c) * FD + ci) * 2;
     return *reinterpret_cast<const bf16x8*>(row);
@@ -505,7 +515,7 @@ __global__ __launch_bounds__(1024) void mix_decode_fused_kernel(MixDecodeArgs a)
       const int q = q0 + 16 * i;
       if (q >= ngroups) break;                         // uniform over the wave
       int hh, j;
-      pair_of(q / (FD / 4), hh, j);
+      pair_of(q / GPP, hh, j);
       const f32x4 x0 = *reinterpret_cast<const f32x4*>(&u[j][hh][ci]);
       const f32x4 x1 = *reinterpret_cast<const f32x4*>(&u[j][hh][ci + 4]);
       float sum = 0.0f;
@@ -514,8 +524,8 @@ __global__ __launch_bounds__(1024) void mix_decode_fused_kernel(MixDecodeArgs a)
         sum = fmaf((float)w[i][e], x0[e], sum);
         sum = fmaf((float)w[i][4 + e], x1[e], sum);
       }
-      // every lane of the row holds the sum: all 16 store it (same address, same value)
-      cvp[j][hh][(q % (FD / 4)) * 4 + slot] = row16_sum(sum);
+      // every lane of the row holds the sum: all of them store it (same address, same value)
+      cvp[j][hh][(q % GPP) * GCH + slot] = LPR == 16 ? row16_sum(sum) : row8_sum(sum);
     }
   }
   __syncthreads();
@@ -596,15 +606,18 @@ hipError_t launch_write_state(const Dims& dm, int B, int S, const void* qkv, boo
 size_t mix_decode_cv_floats(const Dims& dm, int B) { return (size_t)B * (dm.Hq + dm.Hkv) * dm.d; }
 
 bool mix_decode_fused_ok(const Dims& dm) {
-  return dm.bf16 && dm.d == FD && dm.G <= kMaxGroup && dm.kq >= 1 && dm.kq <= FKMAX &&
-         dm.kk >= 1 && dm.kk <= FKMAX;
+  return dm.bf16 && (dm.d == 128 || dm.d == 64) && dm.G <= kMaxGroup && dm.kq >= 1 &&
+         dm.kq <= FKMAX && dm.kk >= 1 && dm.kk <= FKMAX;
 }
 
 hipError_t launch_mix_decode(const MixDecodeArgs& a, hipStream_t s) {
   const Dims& dm = a.dm;
   if (a.qkv_ks < 1 || a.qkv_ld < dm.nqkv) return hipErrorInvalidValue;
   if (mix_decode_fused_ok(dm)) {
-    hipLaunchKernelGGL(mix_decode_fused_kernel, dim3(dm.Hkv, a.B), dim3(1024), 0, s, a);
+    if (dm.d == 128)
+      hipLaunchKernelGGL(mix_decode_fused_kernel<128>, dim3(dm.Hkv, a.B), dim3(1024), 0, s, a);
+    else
+      hipLaunchKernelGGL(mix_decode_fused_kernel<64>, dim3(dm.Hkv, a.B), dim3(1024), 0, s, a);
     return hipGetLastError();
   }
   if (a.cv == nullptr || a.qkv_ks != 1 || a.qkv_ld != dm.nqkv) return hipErrorInvalidValue;

@@ -34,6 +34,10 @@ CASES = [
     # one sequence over a longer cache: several work-groups per head, waves
     # with no block, a partly valid last block
     Workload("bf16_decode_long", B=1, S=1000, E=512, C=1, Hq=4, Hkv=2, seed=59),
+    # head dimension 64: group sizes 2, 1 and 4, three taps, a longer cache
+    Workload("bf16_decode_d64", B=3, S=150, E=512, C=2, Hq=4, Hkv=2, seed=60),
+    Workload("bf16_decode_d64_mha", B=2, S=90, E=256, C=1, Hq=4, Hkv=4, seed=61),
+    Workload("bf16_decode_d64_g4_k3", B=2, S=700, E=1024, C=2, Hq=8, Hkv=2, kq=3, kk=2, seed=62),
 ]
 
 
@@ -105,16 +109,18 @@ def test_decode_ccgqa_32k_full_size():
     assert torch.equal(kc[:, :, :p], dev(inp["k_cache"][:, :, :p], w))
 
 
-def test_decode_ragged_positions_32k_cache():
+@pytest.mark.parametrize("heads", [(4, 2), (8, 4)], ids=["d128", "d64"])
+def test_decode_ragged_positions_32k_cache(heads):
     """One batch whose sequences sit at different positions over a seeded
     32768-token cache: a new sequence (pos 0), the first blocks' edges (1, 31,
     32, 33), a mid-length one (1000) and the last slot of the capacity (32767).
     Cache slots past each sequence's position hold random values, so a read past
     a sequence's keys would change its output.  y, the written cache rows and
-    the advanced state against the oracle, and every other cache row untouched."""
+    the advanced state against the oracle, and every other cache row untouched.
+    Heads of 128 (4 query, 2 KV) and of 64 (8 query, 4 KV)."""
     positions = [0, 1, 31, 32, 33, 1000, 32767]
-    w = Workload("ccgqa_decode_ragged", B=len(positions), S=32767, E=2048, C=4, Hq=4, Hkv=2,
-                 seed=44, kind="decode", max_seq_len=32768)
+    w = Workload("ccgqa_decode_ragged", B=len(positions), S=32767, E=2048, C=4, Hq=heads[0],
+                 Hkv=heads[1], seed=44, kind="decode", max_seq_len=32768)
     say(f"[decode ragged] {w} positions {positions}")
     inp = make_inputs(w)
     pos = np.asarray(positions, np.int32)
