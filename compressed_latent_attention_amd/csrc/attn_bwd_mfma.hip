@@ -1,4 +1,4 @@
-// cca_bwd, attention part, bf16 with d = 128 (CCA-es §4, training backward;
+// cca_bwd, attention part, bf16 with d = 128 or 64 (CCA-es §4, training backward;
 // CCA-fr §4 "Rétropropagation"): gradients of causal softmax attention on the
 // latent heads, recompute-style (P is never stored):
 //   P = exp(Q K^T / sqrt(d) - lse),  D_t = <dO_t, O_t>,
@@ -47,10 +47,9 @@
 namespace cca {
 namespace {
 
-constexpr int D = 128;
 constexpr int TB = 32;          // tokens per step
 constexpr int TROW = 160;       // LDS tile row stride, fp16 elements (320 B = 20 chunks of 16 B)
-constexpr int TILE = TB * TROW; // one tile: 32 token rows of 128 channels
+constexpr int TILE = TB * TROW; // one tile: 32 token rows of up to 128 channels
 constexpr float kLog2e = 1.44269504088896340736f;
 
 typedef _Float16 f16;
@@ -58,7 +57,14 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-bool mfma_bwd(const Dims& dm) { return dm.bf16 && dm.d == D; }
+bool mfma_bwd(const Dims& dm) { return dm.bf16 && (dm.d == 128 || dm.d == 64); }
+
+// Counts that follow the head dimension D: 16-channel k-steps, 32-channel
+// output blocks, 16-byte chunks per row.
+template <int D>
+struct BG {
+  static constexpr int NKS = D / 16, NMB = D / 32, CPR = D / 8;
+};
 
 __device__ __forceinline__ int perm_row(int i) {   // swap bits 2 and 3
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
@@ -72,7 +78,8 @@ __device__ __forceinline__ f16x8 to_f16(const bf16x8& v) {
 }
 
 // ------------------------------------------------------------------ LDS tiles
-// A tile holds 32 token rows of 128 fp16 channels; chunk ch (channels 8 ch ..
+// A tile holds 32 token rows of D fp16 channels (the row stride is the same
+// for D = 64, which uses the first 8 chunks); chunk ch (channels 8 ch ..
 // 8 ch + 7) of row r sits at chunk ch ^ ((r >> 2) & 3) of a 20-chunk row.  The
 // row stride (4 chunks past a multiple of 16) spreads the 4 rows of a
 // transposing read over the 64 banks and the XOR spreads the 16 rows of an
@@ -119,6 +126,7 @@ __device__ __forceinline__ f16x8 read_a(const f16* tile, const int (&ao)[2], int
   return *reinterpret_cast<const f16x8*>(tile + ao[ks & 1] + 32 * (ks >> 1));
 }
 
+template <int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows16(const void* base, long row0, int nrows) {
   return __builtin_amdgcn_make_buffer_rsrc(
       (void*)(reinterpret_cast<const f16*>(base) + row0 * D), 0, nrows * D * 2, 0x00020000);
@@ -168,7 +176,9 @@ __device__ __forceinline__ int do_scale_exp(float m) {
 // ------------------------------------------------------------------ prep
 // 64 tokens of one head per work-group.  blockIdx.y: 0..Hq-1 -> Q'' and dO of
 // head y (and D); Hq.. -> K'' and V' of KV head y - Hq.
+template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnBwdArgs a) {
+  constexpr int CPR = BG<D>::CPR, NI = 64 * CPR / 256;   // 16-byte chunks per thread and array
   const Dims& dm = a.dm;
   const int S = a.S, sp = a.s_pad;
   const int t0 = blockIdx.x * 64, y = blockIdx.y, b = blockIdx.z;
@@ -207,35 +217,35 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnBwdArgs a) {
   const __amdgpu_buffer_rsrc_t rs1 =
       __builtin_amdgcn_make_buffer_rsrc((void*)src1, 0, (int)(((long)(S - 1) * ld1 + D) * 2),
                                         0x00020000);
-  bf16x8 v[4], w[4];
+  bf16x8 v[NI], w[NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int f = threadIdx.x + 256 * i;
-    const int t = t0 + (f >> 4), c = (f & 15) * 8;
+    const int t = t0 + f / CPR, c = (f % CPR) * 8;
     v[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs0, (t * D + c) * 2, 0, 0));
     w[i] = __builtin_bit_cast(bf16x8,
                               __builtin_amdgcn_raw_buffer_load_b128(rs1, (int)((t * ld1 + c) * 2), 0, 0));
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int f = threadIdx.x + 256 * i;
-    const int t = t0 + (f >> 4), c = (f & 15) * 8;
+    const int t = t0 + f / CPR, c = (f % CPR) * 8;
     *reinterpret_cast<f16x8*>(dst0 + (long)t * D + c) = to_f16(v[i]);
     f16x8 o;                               // V' as stored, or dO * 2^e
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (f16)((float)w[i][e] * dscale);
     *reinterpret_cast<f16x8*>(dst1 + (long)t * D + c) = o;
   }
-  // D_t = <dO_t, O_t> in fp32: each thread sums 32 channels of one token
+  // D_t = <dO_t, O_t> in fp32: each thread sums D / 4 channels of one token
   if (is_q) {
     const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
     const int t = t0 + r;
     float sacc = 0.0f;
     if (t < S) {
-      const float* orow = a.o32 + ((long)(b * S + t) * dm.Hq + h) * D + part * 32;
-      const bf16* drow = src1 + (long)t * dm.nq + part * 32;
+      const float* orow = a.o32 + ((long)(b * S + t) * dm.Hq + h) * D + part * (D / 4);
+      const bf16* drow = src1 + (long)t * dm.nq + part * (D / 4);
 #pragma unroll 8
-      for (int c = 0; c < 32; ++c) sacc = fmaf((float)drow[c], orow[c], sacc);
+      for (int c = 0; c < D / 4; ++c) sacc = fmaf((float)drow[c], orow[c], sacc);
     }
     sacc += __shfl_xor(sacc, 1);
     sacc += __shfl_xor(sacc, 2);
@@ -256,25 +266,29 @@ struct DkdvSmem {
   f16 pbuf[2][4][2 * 64 * 8];    // P of a step per producer: [parity][producer][ks][lane][8]
 };
 
+template <int D>
 struct DkdvRegs {
-  f16x8 q[2], dO[2];
+  static constexpr int NL = TB * BG<D>::CPR / 256;   // 16-byte chunks per thread and tile
+  f16x8 q[NL], dO[NL];
   float lse, dsum, pad;
 };
 
 // Registers of one step (thread tc of the 256 consumers): rows of the fp16
 // copies (in range up to s_pad, so no test), lse / D of the step's queries
 // through resources that end at row S - 1 (past it: lse +inf, so P = 0).
+template <int D>
 __device__ __forceinline__ void dkdv_load(const AttnBwdArgs& a, int b, int h, int q0, int tc,
-                                          DkdvRegs& r) {
+                                          DkdvRegs<D>& r) {
+  constexpr int CPR = BG<D>::CPR;
   const Dims& dm = a.dm;
   const int S = a.S;
   const long hrow = (long)(b * dm.Hq + h);
-  const __amdgpu_buffer_rsrc_t qrs = rows16(a.q16, hrow * a.s_pad, a.s_pad);
-  const __amdgpu_buffer_rsrc_t drs = rows16(a.do16, hrow * a.s_pad, a.s_pad);
+  const __amdgpu_buffer_rsrc_t qrs = rows16<D>(a.q16, hrow * a.s_pad, a.s_pad);
+  const __amdgpu_buffer_rsrc_t drs = rows16<D>(a.do16, hrow * a.s_pad, a.s_pad);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < DkdvRegs<D>::NL; ++i) {
     const int f = tc + 256 * i;
-    const int row = f >> 4, ch = (f & 15) * 8;
+    const int row = f / CPR, ch = (f % CPR) * 8;
     r.q[i] = load16(qrs, (q0 + row) * D + ch);
     r.dO[i] = load16(drs, (q0 + row) * D + ch);
   }
@@ -288,11 +302,12 @@ __device__ __forceinline__ void dkdv_load(const AttnBwdArgs& a, int b, int h, in
   r.pad = q < S ? 0.0f : INFINITY;
 }
 
-__device__ __forceinline__ void dkdv_store(DkdvStage& st, int tc, const DkdvRegs& r) {
+template <int D>
+__device__ __forceinline__ void dkdv_store(DkdvStage& st, int tc, const DkdvRegs<D>& r) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < DkdvRegs<D>::NL; ++i) {
     const int f = tc + 256 * i;
-    const int row = f >> 4, ch = f & 15;
+    const int row = f / BG<D>::CPR, ch = f % BG<D>::CPR;
     *reinterpret_cast<f16x8*>(st.q + tile_off(row, ch)) = r.q[i];
     *reinterpret_cast<f16x8*>(st.dO + tile_off(row, ch)) = r.dO[i];
   }
@@ -301,7 +316,9 @@ __device__ __forceinline__ void dkdv_store(DkdvStage& st, int tc, const DkdvRegs
   st.dsum[tc & (TB - 1)] = r.dsum;
 }
 
+template <int D>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
+  constexpr int NKS = BG<D>::NKS, NMB = BG<D>::NMB;
   __shared__ __attribute__((aligned(16))) DkdvSmem sm;
   const Dims& dm = a.dm;
   const int S = a.S, G = dm.G;
@@ -336,19 +353,19 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
     // B operands for S = Q K^T and dP = dO V^T: lane (key l32, hi) holds
     // channels 16 ks + 8 hi + 0..7 of its key's K'' and V' rows (fp16 copies;
     // rows past s_pad read as zero).
-    f16x8 kf[8], vf[8];
+    f16x8 kf[NKS], vf[NKS];
     {
-      const __amdgpu_buffer_rsrc_t krs = rows16(a.k16, kvrow * a.s_pad, a.s_pad);
-      const __amdgpu_buffer_rsrc_t vrs = rows16(a.v16, kvrow * a.s_pad, a.s_pad);
+      const __amdgpu_buffer_rsrc_t krs = rows16<D>(a.k16, kvrow * a.s_pad, a.s_pad);
+      const __amdgpu_buffer_rsrc_t vrs = rows16<D>(a.v16, kvrow * a.s_pad, a.s_pad);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+      for (int ks = 0; ks < NKS; ++ks) {
         kf[ks] = load16(krs, my_key * D + ks * 16 + hi * 8);
         vf[ks] = load16(vrs, my_key * D + ks * 16 + hi * 8);
       }
     }
-    f32x16 dk[4];
+    f32x16 dk[NMB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NMB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) dk[i][r] = 0.0f;
     if (nsteps > 0) {
@@ -360,9 +377,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
         const DkdvStage& st = sm.stg[s % 3];
         const int q0 = (qtop - cur_qi) * TB;
         cur_qi = cur_qi + 1 == nqb ? 0 : cur_qi + 1;
-        f16x8 qa[8], da[8];
+        f16x8 qa[NKS], da[NKS];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
           qa[ks] = read_a(st.q, ao, ks);
           da[ks] = read_a(st.dO, ao, ks);
         }
@@ -382,7 +399,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) pacc[r] = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[ks], kf[ks], sacc, 0, 0, 0);
           pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[ks], vf[ks], pacc, 0, 0, 0);
         }
@@ -408,12 +425,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
         f16* pw = sm.pbuf[s & 1][pair] + lane * 8;
         *reinterpret_cast<f16x8*>(pw) = pf[0];
         *reinterpret_cast<f16x8*>(pw + 512) = pf[1];
-        // dK += dS^T Q: 4 channel blocks x 2 steps of 16 queries, Q^T read
-        // transposed from the Q tile
+        // dK += dS^T Q: D / 32 channel blocks x 2 steps of 16 queries, Q^T
+        // read transposed from the Q tile
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
+          for (int nb = 0; nb < NMB; ++nb)
             dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sf[ks], read_t(st.q, to, ks, nb), dk[nb],
                                                             0, 0, 0);
         lds_barrier();
@@ -423,7 +440,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
     const float inv = a.dscale[0] / sqrtf((float)D);   // 2^-e exactly, then 1/sqrt(d)
     float* dkb = (part == 0 ? a.dk : part == 1 ? a.dk2 : part == 2 ? a.dk3 : a.dk4) + kvrow * S * D;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NMB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -432,16 +449,16 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
   } else {
     // ---------------- consumer: staging and dV += P^T dO, one step behind
     const int tc = t - 256;
-    f32x16 dv[4];
+    f32x16 dv[NMB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NMB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) dv[i][r] = 0.0f;
     if (nsteps > 0) {
       // steps are loaded in order; the loaded step stops at the last one, so
       // loads past the end repeat it into registers nobody stores
       int ld_s = 0, ld_h = 0, ld_qi = 0;
-      auto load_next = [&](DkdvRegs& r) {
+      auto load_next = [&](DkdvRegs<D>& r) {
         dkdv_load(a, b, hbase + ld_h, (qtop - ld_qi) * TB, tc, r);
         const bool more = ld_s < nsteps - 1;
         const bool wrap = more && ld_qi + 1 == nqb;
@@ -449,7 +466,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
         ld_qi = wrap ? 0 : ld_qi + (more ? 1 : 0);
         ld_h += wrap ? 1 : 0;
       };
-      DkdvRegs r0, r1;                             // step j is staged through r(j % 2)
+      DkdvRegs<D> r0, r1;                          // step j is staged through r(j % 2)
       load_next(r0);
       load_next(r1);
       dkdv_store(sm.stg[0], tc, r0);
@@ -457,7 +474,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
       lds_barrier();
       // iteration s: stage step s + 1 and load step s + 3, then dV of step
       // s - 1 (its MFMAs then run while the producer's softmax does)
-      auto iter = [&](int s, DkdvRegs& rs) {
+      auto iter = [&](int s, DkdvRegs<D>& rs) {
         if (s + 1 < nsteps) {
           dkdv_store(sm.stg[(s + 1) % 3], tc, rs);
           load_next(rs);
@@ -471,7 +488,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+            for (int nb = 0; nb < NMB; ++nb)
               dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], read_t(sp.dO, to, ks, nb),
                                                               dv[nb], 0, 0, 0);
         }
@@ -485,7 +502,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnBwdArgs a) {
     float* dvb = (part == 0 ? a.dv : part == 1 ? a.dv2 : part == 2 ? a.dv3 : a.dv4) + kvrow * S * D;
     const float unscale = a.dscale[0];               // 2^-e: exact
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NMB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -518,29 +535,34 @@ struct DqStage {
   f16 v[DQ_KB * TILE];   // V' rows
 };
 
+template <int D>
 struct DqRegs {
-  f16x8 k[2 * DQ_KB], v[2 * DQ_KB];
+  static constexpr int NL = DQ_KB * TB * BG<D>::CPR / 256;   // 16-byte chunks per thread and array
+  f16x8 k[NL], v[NL];
 };
 
+template <int D>
 __device__ __forceinline__ void dq_load(const AttnBwdArgs& a, int b, int g, int j0, int t,
-                                        DqRegs& r) {
+                                        DqRegs<D>& r) {
+  constexpr int CPR = BG<D>::CPR;
   const long kvrow = (long)(b * a.dm.Hkv + g) * a.s_pad;
-  const __amdgpu_buffer_rsrc_t krs = rows16(a.k16, kvrow, a.s_pad);
-  const __amdgpu_buffer_rsrc_t vrs = rows16(a.v16, kvrow, a.s_pad);
+  const __amdgpu_buffer_rsrc_t krs = rows16<D>(a.k16, kvrow, a.s_pad);
+  const __amdgpu_buffer_rsrc_t vrs = rows16<D>(a.v16, kvrow, a.s_pad);
 #pragma unroll
-  for (int i = 0; i < 2 * DQ_KB; ++i) {
+  for (int i = 0; i < DqRegs<D>::NL; ++i) {
     const int f = t + 256 * i;
-    const int row = f >> 4, ch = (f & 15) * 8;
+    const int row = f / CPR, ch = (f % CPR) * 8;
     r.k[i] = load16(krs, (j0 + row) * D + ch);
     r.v[i] = load16(vrs, (j0 + row) * D + ch);
   }
 }
 
-__device__ __forceinline__ void dq_store(DqStage& st, int t, const DqRegs& r) {
+template <int D>
+__device__ __forceinline__ void dq_store(DqStage& st, int t, const DqRegs<D>& r) {
 #pragma unroll
-  for (int i = 0; i < 2 * DQ_KB; ++i) {
+  for (int i = 0; i < DqRegs<D>::NL; ++i) {
     const int f = t + 256 * i;
-    const int row = f >> 4, ch = f & 15;
+    const int row = f / BG<D>::CPR, ch = f % BG<D>::CPR;
     *reinterpret_cast<f16x8*>(st.k + tile_off(row, ch)) = r.k[i];
     *reinterpret_cast<f16x8*>(st.v + tile_off(row, ch)) = r.v[i];
   }
@@ -555,7 +577,9 @@ struct DqSmem {
   f16 sbuf[2][4][DQ_KB][2 * 64 * 8];  // dS per producer: [parity][producer][key block][ks][lane][8]
 };
 
+template <int D>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
+  constexpr int NKS = BG<D>::NKS, NMB = BG<D>::NMB;
   __shared__ __attribute__((aligned(16))) DqSmem sm;
   const Dims& dm = a.dm;
   const int S = a.S;
@@ -580,12 +604,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
     const float c1 = kLog2e / sqrtf((float)D);
     // B operands for S^T = K Q^T and dP^T = V dO^T: lane (query l32, hi) holds
     // channels 16 ks + 8 hi + 0..7 of its query's Q'' and dO rows (fp16 copies).
-    f16x8 qf[8], df[8];
+    f16x8 qf[NKS], df[NKS];
     {
-      const __amdgpu_buffer_rsrc_t qrs = rows16(a.q16, hrow * a.s_pad, a.s_pad);
-      const __amdgpu_buffer_rsrc_t drs = rows16(a.do16, hrow * a.s_pad, a.s_pad);
+      const __amdgpu_buffer_rsrc_t qrs = rows16<D>(a.q16, hrow * a.s_pad, a.s_pad);
+      const __amdgpu_buffer_rsrc_t drs = rows16<D>(a.do16, hrow * a.s_pad, a.s_pad);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+      for (int ks = 0; ks < NKS; ++ks) {
         qf[ks] = load16(qrs, my_q * D + ks * 16 + hi * 8);
         df[ks] = load16(drs, my_q * D + ks * 16 + hi * 8);
       }
@@ -618,14 +642,14 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
         }
-        f16x8 ka[8], va[8];
+        f16x8 ka[NKS], va[NKS];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
           ka[ks] = read_a(tk, ao, ks);
           va[ks] = read_a(tv, ao, ks);
         }
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks], qf[ks], sacc, 0, 0, 0);
           pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[ks], df[ks], pacc, 0, 0, 0);
         }
@@ -649,22 +673,22 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
   } else {
     // ---------------- consumer: staging and dQ += dS K, one step behind
     const int tc = t - 256;
-    f32x16 dq[4];
+    f32x16 dq[NMB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NMB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) dq[i][r] = 0.0f;
     int to[2];
     t_offsets(lane, to);
     constexpr int SB = DQ_KB * TB;                 // keys per step
-    DqRegs r0, r1;                                 // step j is staged through r(j % 2)
+    DqRegs<D> r0, r1;                              // step j is staged through r(j % 2)
     dq_load(a, b, g, 0, tc, r0);
     dq_load(a, b, g, min(1, nsteps - 1) * SB, tc, r1);
     dq_store(sm.stg[0], tc, r0);
     dq_load(a, b, g, min(2, nsteps - 1) * SB, tc, r0);
     lds_barrier();
     // iteration s: stage step s + 1 and load step s + 3, then dQ of step s - 1
-    auto iter = [&](int s, DqRegs& rs) {
+    auto iter = [&](int s, DqRegs<D>& rs) {
       if (s + 1 < nsteps) {
         dq_store(sm.stg[(s + 1) % 3], tc, rs);
         dq_load(a, b, g, min(s + 3, nsteps - 1) * SB, tc, rs);
@@ -682,7 +706,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+            for (int nb = 0; nb < NMB; ++nb)
               dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                   sa[ks], read_t(sp.k + kb * TILE, to, ks, nb), dq[nb], 0, 0, 0);
         }
@@ -697,7 +721,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(AttnBwdArgs a) {
     const float inv = a.dscale[0] / sqrtf((float)D);   // 2^-e exactly, then 1/sqrt(d)
     float* dqb = a.dq + hrow * S * D;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NMB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int q = qw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -734,18 +758,27 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) {
   const long n8 = (long)a.B * a.S * dm.nq / 8;
   hipLaunchKernelGGL(bwd_do_absmax_kernel, dim3(kAmaxParts), dim3(256), 0, s,
                      reinterpret_cast<const bf16*>(a.dO), n8, a.amax_part);
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3(a.s_pad / 64, dm.Hq + dm.Hkv, a.B), dim3(256), 0, s,
-                     a);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(nparts * ((a.S + 127) / 128), dm.Hkv, a.B), dim3(512),
-                     0, s, a);
+  const dim3 gprep(a.s_pad / 64, dm.Hq + dm.Hkv, a.B);
+  const dim3 gdkdv(nparts * ((a.S + 127) / 128), dm.Hkv, a.B);
+  if (dm.d == 128) {
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, gprep, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, gdkdv, dim3(512), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, gprep, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, gdkdv, dim3(512), 0, s, a);
+  }
   if (!a.sum_by_consumer) {
     AttnBwdArgs sa = a;
     if (nparts == 2) sa.dk3 = sa.dv3 = sa.dk4 = sa.dv4 = nullptr;
-    const long n4 = (long)a.B * dm.Hkv * a.S * D / 4;
+    const long n4 = (long)a.B * dm.Hkv * a.S * dm.d / 4;
     hipLaunchKernelGGL(bwd_dkdv_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
                        sa, n4);
   }
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3(((a.S + 127) / 128) * dm.Hq * a.B), dim3(512), 0, s, a);
+  const dim3 gdq(((a.S + 127) / 128) * dm.Hq * a.B);
+  if (dm.d == 128)
+    hipLaunchKernelGGL(bwd_dq_kernel<128>, gdq, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(bwd_dq_kernel<64>, gdq, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -55,9 +55,16 @@ CASES = [
              seed=74, kind="backward"),
     Workload("bf16_bwd_gqa_c1", B=1, S=150, E=2048, C=1, Hq=16, Hkv=2, kq=1, kk=1, flags=4,
              seed=75, kind="backward"),
-    # the 16x variant (one KV head) and d = 64 (the generic kernels)
+    # the 16x variant (one KV head) and d = 64: group sizes 2, 1 (two
+    # sequences) and 4 (four parts per key block), three taps, the flag
+    # subsets, several key blocks with ragged tails
     Workload("bf16_bwd_ccgqa16", B=1, S=150, E=2048, C=4, Hq=4, Hkv=1, seed=76, kind="backward"),
     Workload("bf16_bwd_d64", B=1, S=120, E=512, C=2, Hq=4, Hkv=2, seed=77, kind="backward"),
+    Workload("bf16_bwd_d64_g1_b2", B=2, S=200, E=512, C=2, Hq=4, Hkv=4, seed=81, kind="backward"),
+    Workload("bf16_bwd_d64_g4_k3", B=1, S=300, E=1024, C=2, Hq=8, Hkv=2, kq=3, kk=2, seed=82,
+             kind="backward"),
+    Workload("bf16_bwd_d64_flags", B=1, S=129, E=512, C=2, Hq=4, Hkv=2, flags=1 | 4 | 8, sv=20,
+             seed=83, kind="backward"),
     # large enough that the weight gradients run split over K (16 partial sums)
     # on the 256 x 256 kernel, and the attention backward spans 16 key blocks
     Workload("bf16_bwd_splitk", B=1, S=2048, E=1024, C=2, Hq=4, Hkv=2, seed=67,
@@ -111,6 +118,13 @@ def test_backward_ccgqa_16k_full():
     the eight-wave dx GEMM, split-K weight gradients over 16384 tokens and 32
     blocks of tap-gradient partials, every gradient against the oracle."""
     w = WORKLOADS["ccgqa_backward_16k"]
+    check_backward(w, make_inputs(w))
+
+
+def test_backward_ccgqa_d64_16k_full():
+    """The d = 64 CCGQA layer's backward at full size (S = 16384, E = 2048, 8
+    query and 4 KV heads of 64), every gradient against the oracle."""
+    w = WORKLOADS["ccgqa_d64_prefill_16k"].replace(name="ccgqa_d64_backward_16k", kind="backward")
     check_backward(w, make_inputs(w))
 
 
