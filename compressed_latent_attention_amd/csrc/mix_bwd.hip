@@ -281,23 +281,26 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_128(MixBwdArgs a) {
   }
 }
 
-// ---- d = 128, group size G = 1, 2, 4 or 8 (compile-time, so the group's rows
-// stay in named registers): the pointwise adjoints with 16 tokens per
-// work-group.  Thread =
-// (token t0 + tid / 16, channels 4 (tid % 16) .. + 3 of the low half and their
-// RoPE partners + 64 in the high half) for every head of the KV group, so the
-// inverse rotation, the QK-mean adjoint (which mixes the group's heads at one
-// channel) and the value-shift adjoint stay in registers, with 16-byte loads
-// and stores.
-constexpr int PT = 16;                       // tokens per work-group
+// ---- d = 128 or 64, group size G = 1, 2, 4 or 8 (compile-time, so the
+// group's rows stay in named registers): the pointwise adjoints with 256 / (d
+// / 8) tokens per work-group.  Thread = (token t0 + tid / (d / 8), channels 4
+// (tid % (d / 8)) .. + 3 of the low half and their RoPE partners + d / 2 in
+// the high half) for every head of the KV group, so the inverse rotation, the
+// QK-mean adjoint (which mixes the group's heads at one channel) and the
+// value-shift adjoint stay in registers, with 16-byte loads and stores.
+template <int TD>
+struct PW {
+  static constexpr int TPT = TD / 8;         // threads per token
+  static constexpr int PT = 256 / TPT;       // tokens per work-group
+};
 
-template <typename T, int G>
-__global__ __launch_bounds__(256) void mix_bwd_pointwise_128(MixBwdArgs a) {
+template <typename T, int G, int TD>
+__global__ __launch_bounds__(256) void mix_bwd_pointwise_group(MixBwdArgs a) {
   const Dims& dm = a.dm;
   const int S = a.S;
-  constexpr int H = TD / 2;
+  constexpr int H = TD / 2, TPT = PW<TD>::TPT;
   const int g = blockIdx.y, b = blockIdx.z;
-  const int t = blockIdx.x * PT + threadIdx.x / 16, cq = (threadIdx.x % 16) * 4;
+  const int t = blockIdx.x * PW<TD>::PT + threadIdx.x / TPT, cq = (threadIdx.x % TPT) * 4;
   if (t >= S) return;
   // every read first (the group's rows, both dV' rows, then the RoPE pairs),
   // so they are in flight together
@@ -381,12 +384,13 @@ __global__ __launch_bounds__(256) void mix_bwd_pointwise_128(MixBwdArgs a) {
   }
 }
 
-// ---- bf16 storage, d = 128: the convolution adjoint on MFMA.
+// ---- bf16 storage, d = 128 or 64: the convolution adjoint on MFMA.
 // The adjoint contracts the taps over their first index (dq~[c'] = sum_c
 // A_j[c][c'] dq^[c]), and an MFMA operand lane holds 8 consecutive elements of
 // the contracted index, so the tap matrices are transposed once per call:
 // tapT[m][c'][c] = A_m[c][c'], m running over (head, tap) pairs as the taps are
 // stored (query heads, then key heads).
+template <int TD>
 __global__ __launch_bounds__(256) void mix_bwd_tap_transpose(MixBwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 tile[TD][TD + 8];
   const Dims& dm = a.dm;
@@ -413,12 +417,20 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_transpose(MixBwdArgs a) {
 // them, zero past S) is staged in LDS once as two bf16 halves, hi = bf16(g) and
 // lo = bf16(g - hi), and operand A is read from both (~16 mantissa bits of dq^,
 // fp32 accumulation); operand B is a row of tapT (exact bf16 taps) from L2.
-// Wave w: tokens 32 (w / 2) .. + 31, output channel blocks 2 (w % 2), + 1.
-constexpr int CT = 64;                       // tokens per work-group
-constexpr int GLD = TD + 8;                  // LDS row stride (bf16): conflict-free 16-byte reads
-constexpr int GPLANE = (CT + kMaxConv - 1) * GLD;
+// With P = d / 64 pairs of 32-channel output blocks, wave w takes tokens 32 (w
+// / P) .. + 31 and output channel blocks 2 (w % P), + 1: a work-group covers
+// 64 tokens at d = 128, 128 at d = 64.
+template <int TD>
+struct CG {
+  static constexpr int P = TD / 64;
+  static constexpr int CT = 32 * 4 / P;              // tokens per work-group
+  static constexpr int GLD = TD + 8;                 // LDS row stride (bf16): conflict-free reads
+  static constexpr int GPLANE = (CT + kMaxConv - 1) * GLD;
+};
 
+template <int TD>
 __global__ __launch_bounds__(256) void mix_bwd_conv_input_mfma(MixBwdArgs a) {
+  constexpr int CT = CG<TD>::CT, GLD = CG<TD>::GLD, GPLANE = CG<TD>::GPLANE, P = CG<TD>::P;
   __shared__ __attribute__((aligned(16))) bf16 gs[2 * GPLANE];
   const Dims& dm = a.dm;
   const int S = a.S;
@@ -439,7 +451,7 @@ __global__ __launch_bounds__(256) void mix_bwd_conv_input_mfma(MixBwdArgs a) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(srow0 + (long)t0 * W + col), 0, r1 > t0 ? ((r1 - t0 - 1) * W + TD) * 4 : 0, 0x00020000);
   const int n = nrow * (TD / 4);
-  constexpr int CNB = 9;                       // 9 x 256 >= 67 rows x 32 float4: one round
+  constexpr int CNB = 9;                       // 9 x 256 >= (CT + 3) rows x TD / 4 float4: one round
   for (int base = 0; base < n; base += CNB * 256) {
     f32x4 v[CNB];
 #pragma unroll
@@ -467,7 +479,7 @@ __global__ __launch_bounds__(256) void mix_bwd_conv_input_mfma(MixBwdArgs a) {
   __syncthreads();
 
   const int lane = t & 63, wave = t >> 6, l32 = lane & 31, hi = lane >> 5;
-  const int tw = 32 * (wave >> 1), nb0 = 2 * (wave & 1);
+  const int tw = 32 * (wave / P), nb0 = 2 * (wave % P);
   f32x16 acc[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -490,7 +502,7 @@ __global__ __launch_bounds__(256) void mix_bwd_conv_input_mfma(MixBwdArgs a) {
     const bf16* b0p = reinterpret_cast<const bf16*>(a.tapT) + ((long)(m0 + j) * TD + nb0 * 32 + l32) * TD + hi * 8;
     const bf16* b1p = b0p + 32 * TD;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < TD / 16; ++ks) {
       const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(arow + ks * 16);
       const bf16x8 alo = *reinterpret_cast<const bf16x8*>(arow + GPLANE + ks * 16);
       const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(b0p + ks * 16);
@@ -520,12 +532,16 @@ __global__ __launch_bounds__(256) void mix_bwd_conv_input_mfma(MixBwdArgs a) {
 // tokens per lane, so chunks of 64 tokens of dq^ and of q~ (shifted by j) are
 // staged transposed, [channel][token], as bf16 hi / lo halves; each product
 // takes hi*hi + hi*lo + lo*hi (~16 mantissa bits, fp32 accumulation).
-// Wave w: c blocks 2 (w / 2), + 1 and c' blocks 2 (w % 2), + 1 of 32.
+// With NI = d / 64 blocks of 32 per wave and dimension, wave w takes c blocks
+// NI (w / 2) .. + NI - 1 and c' blocks NI (w % 2) .. + NI - 1.
 constexpr int GT = 64;                       // tokens per LDS chunk
 constexpr int TLDT = GT + 8;                 // transposed row stride (bf16)
-constexpr int TPLANE = TD * TLDT;
 
+template <int TD>
 __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
+  constexpr int TPLANE = TD * TLDT;
+  constexpr int NI = TD / 64;                          // 32-blocks per wave in c and in c'
+  constexpr int NLD = TD / 16;                         // staging loads per thread and operand
   __shared__ __attribute__((aligned(16))) bf16 gT[2 * TPLANE];   // dq^ [c][t], hi then lo
   __shared__ __attribute__((aligned(16))) bf16 xT[2 * TPLANE];   // q~[t - j] [c'][t], hi then lo
   const Dims& dm = a.dm;
@@ -543,7 +559,7 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
   const long off = isq ? (long)h * dm.kq * TD * TD
                        : (long)dm.Hq * dm.kq * TD * TD + (long)h * dm.kk * TD * TD;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, hi = lane >> 5;
-  const int mb0 = 2 * (wave >> 1), nb0 = 2 * (wave & 1);
+  const int mb0 = NI * (wave >> 1), nb0 = NI * (wave & 1);
   const int tend = min(S, tb0 + TB);
   // resources over the rows this block reads: dq^ rows [tb0, tend), q~ rows
   // [max(tb0 - j, 0), tend - j); rows outside read as zero without a branch
@@ -555,28 +571,28 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)xbase, 0, xr1 > xr0 ? ((xr1 - xr0 - 1) * dm.nqkv + TD) * 4 : 0, 0x00020000);
 
-  f32x16 acc[2][2];
+  f32x16 acc[NI][NI];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < NI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  // Staging map: load p = 8 wave + i covers tokens 16 (p % 4) + L % 16 and
+  // Staging map: load p = NLD wave + i covers tokens 16 (p % 4) + L % 16 and
   // float4 groups 4 (p / 4) + L / 16, so one wave's transposed 2-byte stores of
   // a channel row go to 16 consecutive tokens (bank-conflict free) while each
   // load reads 64 contiguous bytes of 16 rows.
   auto stage_rc = [&](int i, int& r, int& c4) {
-    const int pidx = 8 * wave + i;
+    const int pidx = NLD * wave + i;
     r = 16 * (pidx & 3) + (lane & 15);
     c4 = 4 * (4 * (pidx >> 2) + (lane >> 4));
   };
   for (int c0 = tb0; c0 < tend; c0 += GT) {
-    // 64 tokens x 32 float4 per operand: 8 of each per thread, all in flight
-    f32x4 gv[8], xv[8];
+    // 64 tokens x TD / 4 float4 per operand: NLD of each per thread, all in flight
+    f32x4 gv[NLD], xv[NLD];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NLD; ++i) {
       int r, c4;
       stage_rc(i, r, c4);
       const int tok = c0 + r;
@@ -588,7 +604,7 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
     }
     __syncthreads();                                     // the previous chunk's reads are done
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NLD; ++i) {
       int r, c4;
       stage_rc(i, r, c4);
       const bool live = c0 + r < tend;                   // tokens past the block: zero
@@ -605,9 +621,9 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < GT / 16; ++ks) {
-      bf16x8 ah[2], al[2], bh[2], bl[2];
+      bf16x8 ah[NI], al[NI], bh[NI], bl[NI];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < NI; ++i) {
         const int ar = ((mb0 + i) * 32 + l32) * TLDT + ks * 16 + hi * 8;
         const int br = ((nb0 + i) * 32 + l32) * TLDT + ks * 16 + hi * 8;
         ah[i] = *reinterpret_cast<const bf16x8*>(gT + ar);
@@ -616,9 +632,9 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
         bl[i] = *reinterpret_cast<const bf16x8*>(xT + TPLANE + br);
       }
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < NI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
+        for (int ni = 0; ni < NI; ++ni) {
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mi], bh[ni], acc[mi][ni], 0, 0, 0);
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mi], bl[ni], acc[mi][ni], 0, 0, 0);
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mi], bh[ni], acc[mi][ni], 0, 0, 0);
@@ -628,9 +644,9 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
   // D: lane holds column c' = nb 32 + l32, register r row c = mb 32 + 8 (r / 4) + 4 hi + r % 4
   float* out = a.dconv_part + blk * per_blk + off + (long)j * TD * TD;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < NI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int c = (mb0 + mi) * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -672,26 +688,34 @@ size_t mix_bwd_part_floats(const Dims& dm, int B, int S) {
   return (size_t)tap_blocks(B, S) * per_blk;
 }
 
-// The d = 128 pointwise kernel for the group sizes it is instantiated for;
-// false (nothing launched) for others.
-template <typename T>
-bool launch_pointwise_128(const MixBwdArgs& a, hipStream_t s) {
-  const dim3 grid((a.S + PT - 1) / PT, a.dm.Hkv, a.B);
+// The register-blocked pointwise kernel (d = 128 or 64) for the group sizes
+// it is instantiated for; false (nothing launched) for others.
+template <typename T, int D>
+bool launch_pointwise_d(const MixBwdArgs& a, hipStream_t s) {
+  const dim3 grid((a.S + PW<D>::PT - 1) / PW<D>::PT, a.dm.Hkv, a.B);
   switch (a.dm.G) {
-    case 1: hipLaunchKernelGGL((mix_bwd_pointwise_128<T, 1>), grid, dim3(256), 0, s, a); return true;
-    case 2: hipLaunchKernelGGL((mix_bwd_pointwise_128<T, 2>), grid, dim3(256), 0, s, a); return true;
-    case 4: hipLaunchKernelGGL((mix_bwd_pointwise_128<T, 4>), grid, dim3(256), 0, s, a); return true;
-    case 8: hipLaunchKernelGGL((mix_bwd_pointwise_128<T, 8>), grid, dim3(256), 0, s, a); return true;
+    case 1: hipLaunchKernelGGL((mix_bwd_pointwise_group<T, 1, D>), grid, dim3(256), 0, s, a); return true;
+    case 2: hipLaunchKernelGGL((mix_bwd_pointwise_group<T, 2, D>), grid, dim3(256), 0, s, a); return true;
+    case 4: hipLaunchKernelGGL((mix_bwd_pointwise_group<T, 4, D>), grid, dim3(256), 0, s, a); return true;
+    case 8: hipLaunchKernelGGL((mix_bwd_pointwise_group<T, 8, D>), grid, dim3(256), 0, s, a); return true;
     default: return false;
   }
 }
+template <typename T>
+bool launch_pointwise_group(const MixBwdArgs& a, hipStream_t s) {
+  if (a.dm.d == 128) return launch_pointwise_d<T, 128>(a, s);
+  if (a.dm.d == 64) return launch_pointwise_d<T, 64>(a, s);
+  return false;
+}
+
+bool mfma_d(const Dims& dm) { return dm.d == 128 || dm.d == 64; }
 
 bool mix_bwd_adds_dkdv2(const Dims& dm) {
-  return dm.d == TD && (dm.G == 1 || dm.G == 2 || dm.G == 4 || dm.G == 8);
+  return mfma_d(dm) && (dm.G == 1 || dm.G == 2 || dm.G == 4 || dm.G == 8);
 }
 
 size_t mix_bwd_tapT_bytes(const Dims& dm) {
-  return dm.bf16 && dm.d == TD ? (size_t)(dm.Hq * dm.kq + dm.Hkv * dm.kk) * TD * TD * 2 : 0;
+  return dm.bf16 && mfma_d(dm) ? (size_t)(dm.Hq * dm.kq + dm.Hkv * dm.kk) * dm.d * dm.d * 2 : 0;
 }
 
 size_t mix_bwd_scratch_floats(const Dims& dm, int B, int S) {
@@ -704,19 +728,28 @@ hipError_t launch_mix_bwd(const MixBwdArgs& a, hipStream_t s) {
   const long per_blk = (long)dm.Hq * dm.kq * dm.d * dm.d + (long)dm.Hkv * dm.kk * dm.d * dm.d;
   const int kmax = std::max(dm.kq, dm.kk);
   if ((a.dk2 || a.dv2) && !mix_bwd_adds_dkdv2(dm)) return hipErrorInvalidValue;
-  if (dm.d == TD) {
-    const dim3 gin((a.S + 63) / 64, dm.Hq + dm.Hkv, a.B), gtap(nblk, dm.Hq + dm.Hkv, kmax);
-    if (dm.bf16) {
-      if (a.tapT == nullptr) return hipErrorInvalidValue;
-      hipLaunchKernelGGL(mix_bwd_tap_transpose, dim3(dm.Hq * dm.kq + dm.Hkv * dm.kk), dim3(256), 0,
-                         s, a);
-      if (!launch_pointwise_128<bf16>(a, s))
-        hipLaunchKernelGGL(mix_bwd_pointwise<bf16>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
-      hipLaunchKernelGGL(mix_bwd_conv_input_mfma, dim3((a.S + CT - 1) / CT, dm.Hq + dm.Hkv, a.B),
+  if (dm.bf16 && mfma_d(dm)) {
+    if (a.tapT == nullptr) return hipErrorInvalidValue;
+    const dim3 gtap(nblk, dm.Hq + dm.Hkv, kmax), gtr(dm.Hq * dm.kq + dm.Hkv * dm.kk);
+    if (!launch_pointwise_group<bf16>(a, s))
+      hipLaunchKernelGGL(mix_bwd_pointwise<bf16>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
+    if (dm.d == 128) {
+      hipLaunchKernelGGL(mix_bwd_tap_transpose<128>, gtr, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(mix_bwd_conv_input_mfma<128>,
+                         dim3((a.S + CG<128>::CT - 1) / CG<128>::CT, dm.Hq + dm.Hkv, a.B),
                          dim3(256), 0, s, a);
-      hipLaunchKernelGGL(mix_bwd_tap_partial_mfma, gtap, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(mix_bwd_tap_partial_mfma<128>, gtap, dim3(256), 0, s, a);
     } else {
-      if (!launch_pointwise_128<float>(a, s))
+      hipLaunchKernelGGL(mix_bwd_tap_transpose<64>, gtr, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(mix_bwd_conv_input_mfma<64>,
+                         dim3((a.S + CG<64>::CT - 1) / CG<64>::CT, dm.Hq + dm.Hkv, a.B),
+                         dim3(256), 0, s, a);
+      hipLaunchKernelGGL(mix_bwd_tap_partial_mfma<64>, gtap, dim3(256), 0, s, a);
+    }
+  } else if (dm.d == TD) {
+    const dim3 gin((a.S + 63) / 64, dm.Hq + dm.Hkv, a.B), gtap(nblk, dm.Hq + dm.Hkv, kmax);
+    {
+      if (!launch_pointwise_group<float>(a, s))
         hipLaunchKernelGGL(mix_bwd_pointwise<float>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
       hipLaunchKernelGGL(mix_bwd_conv_input_128<float>, gin, dim3(256), 0, s, a);
       hipLaunchKernelGGL(mix_bwd_tap_partial_128<float>, gtap, dim3(256), 0, s, a);
