@@ -90,12 +90,13 @@ def time_oracle_forward(w, inp):
                        f"{threads} of {os.cpu_count()} host CPUs")}
 
 
-def bench_prefill(args, torch, cca, w, inp):
-    from compressed_latent_attention_amd.synthetic import WORKLOADS  # noqa: F401
+def bench_prefill(args, torch, cca, w, inp, fused=False):
     dt = torch.bfloat16
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt)
     layer = cca.CCALayer(w.E, w.C, w.Hq, w.Hkv, w.capacity, w.kq, w.kk, w.s_v, w.flags,
                          w.rope_base, w.dtype)
+    if fused:
+        layer.set_prefill_fusion(True)
     wts = {k: dev(inp[k]) for k in ("w_q", "w_k", "w_v", "w_o", "conv_q", "conv_k")}
     x = dev(inp["x"])
     B, S = w.B, w.S
@@ -358,6 +359,29 @@ def bench_backward(args, torch, cca, w=None):
     }
 
 
+def bench_fused(args, torch, cca, w, inp):
+    """The 16k prefill with the query side of the mix fused into the attention
+    (cca_set_prefill_fusion) against the separate passes, alternately on the
+    same layer, same warm-up: step times and kernel times of both."""
+    out = {"note": "fused: the attention forms Q'' from the bf16 latent and the mix writes no Q''; "
+                   "separate: the default path (the headline row)"}
+    a2 = argparse.Namespace(**vars(args))
+    a2.steps = 30
+    res = {}
+    for rep_i in range(2):
+        for mode in ("separate", "fused"):
+            elapsed, _, prof, layer, _ = bench_prefill(a2, torch, cca, w, inp,
+                                                       fused=(mode == "fused"))
+            layer.close()
+            ms = elapsed * 1e3 / a2.steps
+            kern = {k: round(v[1] / max(v[0], 1) * 1e3, 2) for k, v in prof.items()}
+            if mode not in res or ms < res[mode]["ms_per_step"]:
+                res[mode] = {"ms_per_step": ms, "kernels_us": kern}
+    out.update(res)
+    out["fused_over_separate"] = res["fused"]["ms_per_step"] / res["separate"]["ms_per_step"]
+    return out
+
+
 def bench_d64(args, torch, cca):
     """The CCGQA layer with head dimension 64 (8 query and 4 KV heads of 64:
     the same latent widths and KV-cache size as the d = 128 layer): the 16k
@@ -502,11 +526,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--warm-s", type=float, default=0.3,
                     help="untimed prefill steps continue past --warmup until this many seconds")
-    ap.add_argument("--rows", default="prefill,mix,decode,backward,d64",
+    ap.add_argument("--rows", default="prefill,mix,fused,decode,backward,d64",
                     help="comma list: prefill (headline, always run), mix (the mix kernel with "
-                         "cold caches), decode, backward, d64 (the head-dimension-64 layer: "
-                         "prefill, decode, backward); n1 adds the MHA / GQA comparators over "
-                         "S = 4k .. 64k (not run by default)")
+                         "cold caches), fused (the prefill with the query side of the mix in "
+                         "the attention, against the separate passes), decode, backward, d64 "
+                         "(the head-dimension-64 layer: prefill, decode, backward); n1 adds the "
+                         "MHA / GQA comparators over S = 4k .. 64k (not run by default)")
     ap.add_argument("--bwd-steps", type=int, default=3, help="timed backward steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -577,6 +602,8 @@ def main():
     rows = [r.strip() for r in args.rows.split(",") if r.strip()]
     if "mix" in rows:
         out["mix_cold"] = bench_mix_cold(args, torch, cca, w, inp)
+    if "fused" in rows:
+        out["fused_q"] = bench_fused(args, torch, cca, w, inp)
     if "decode" in rows:
         out["decode"] = bench_decode(args, torch, cca)
     if "backward" in rows:

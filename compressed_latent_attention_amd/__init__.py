@@ -74,6 +74,7 @@ _SIGNATURES = {
     "cca_profile_enable": (c_int, [c_void_p, c_int]),
     "cca_profile_read": (c_int, [c_void_p, POINTER(cca_kernel_time), c_int]),
     "cca_profile_flush": (c_int, [c_void_p, c_void_p, c_size_t]),
+    "cca_set_prefill_fusion": (c_int, [c_void_p, c_int32]),
     "cca_status_string": (c_char_p, [c_int]),
     "cca_source_hash": (c_char_p, []),
 }
@@ -236,6 +237,11 @@ def cca_profile_flush(h, buf) -> None:
            "cca_profile_flush")
 
 
+def cca_set_prefill_fusion(h, on: bool) -> None:
+    """Inference prefill with the query side of the mix inside the attention."""
+    _check(load().cca_set_prefill_fusion(h, 1 if on else 0), "cca_set_prefill_fusion")
+
+
 def cca_profile_read(h) -> Dict[str, tuple]:
     lib = load()
     n = lib.cca_profile_read(h, None, 0)
@@ -285,6 +291,9 @@ class CCALayer:
             buf = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
             self._ws[key] = buf
         return buf
+
+    def set_prefill_fusion(self, on: bool) -> None:
+        cca_set_prefill_fusion(self.handle, on)
 
     def saved_bytes(self, B, S) -> int:
         return load().cca_saved_bytes(self.handle, B, S)

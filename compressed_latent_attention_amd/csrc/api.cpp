@@ -31,6 +31,7 @@ struct cca_handle {
   int device = 0;
   void* scratch = nullptr;    // this device's copy of `scratch` (below), or null
   bool profiling = false;
+  bool fuse_q = false;        // cca_set_prefill_fusion
   void* flush_buf = nullptr;  // written before each timed launch when set
   size_t flush_bytes = 0;
   std::vector<ProfRec> recs;
@@ -485,10 +486,12 @@ cca_status cca_forward_prefill(cca_handle* h, const cca_weights* w, const void* 
     const bool lat_f32 = saved != nullptr || !dm.bf16;
     CCA_TRY_HIP(timed(h, "proj_down", s, [&] { return launch_gemm(gd, GemmLayout::NT, dm.bf16, lat_f32, s); }));
 
+    // fused Q: the attention forms Q'' from the bf16 latent (inference, d = 128)
+    const bool fuse_q = h->fuse_q && !saved && mfma && dm.bf16 && dm.d == 128 && !lat_f32;
     MixArgs ma{};
     ma.dm = dm; ma.B = B; ma.S = S; ma.qkv = qkv; ma.qkv_f32 = lat_f32;
     ma.conv_q = w->conv_q; ma.conv_k = w->conv_k; ma.rope = h->rope;
-    ma.q_out = qr; ma.k_out = kr; ma.v_out = (saved || !mfma) ? vs : nullptr;
+    ma.q_out = fuse_q ? nullptr : qr; ma.k_out = kr; ma.v_out = (saved || !mfma) ? vs : nullptr;
     ma.k_out2 = k_cache; ma.v_out2 = v_cache; ma.cap2 = dm.max_seq_len;
     ma.vt_out = vt; ma.s_pad = (int)pad64(S);
     CCA_TRY_HIP(timed(h, "mix", s, [&] { return launch_mix_fwd(ma, s); }));
@@ -501,6 +504,9 @@ cca_status cca_forward_prefill(cca_handle* h, const cca_weights* w, const void* 
     aa.kv_bs = (long)dm.Hkv * S * dm.d; aa.kv_hs = (long)S * dm.d;
     aa.vt = vt; aa.s_pad = (int)pad64(S);
     aa.o = o; aa.o32 = o32; aa.lse = lse; aa.decode = false;
+    if (fuse_q) {
+      aa.qlat = qkv; aa.conv_q = w->conv_q; aa.conv_k = w->conv_k; aa.rope = h->rope;
+    }
     CCA_TRY_HIP(timed(h, "attn", s, [&] { return launch_attn_fwd(aa, s); }));
 
     GemmArgs gu = gemm_nt(M, dm.E, dm.nq, o, dm.nq, w->w_o, dm.nq, y, dm.E);
@@ -881,6 +887,12 @@ cca_status cca_profile_enable(cca_handle* h, int enable) {
   for (auto& r : h->recs) { h->pool.push_back(r.start); h->pool.push_back(r.stop); }
   h->recs.clear();
   h->profiling = enable != 0;
+  return CCA_OK;
+}
+
+cca_status cca_set_prefill_fusion(cca_handle* h, int32_t on) {
+  if (!h) return CCA_ERR_INVALID_ARG;
+  h->fuse_q = on != 0;
   return CCA_OK;
 }
 

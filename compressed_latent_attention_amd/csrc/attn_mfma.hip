@@ -164,6 +164,131 @@ __device__ __forceinline__ void mfma_phase(bool pv, bool qk, f32x16 (&oacc)[Geom
   }
 }
 
+// ------------------------------------------------------------------ fused Q
+// The mix's query side inside the attention (the convolution fused with the
+// attention, as CCA-es §3 item 4 and CCA-fr §3 describe the authors' kernel):
+// the work-group forms Q'' of its 128 queries itself from the bf16 latent,
+// Q'' = RoPE(q^ + a/2 (q~ + k~) + b/2 (q^ + k^)) with q^, k^ the causal
+// grouped convolutions of its head's q~ and its KV head's k~ (CCA-es §2.B.1,
+// §2.B.2), in the arithmetic and order of the mix kernel.  LDS (before the
+// K / V tiles use it): the q~ and k~ tiles (the 128 rows plus 4 halo rows,
+// 272-byte rows) and the Q'' tile.
+constexpr int FQ_HALO = 4;
+constexpr int FQ_ROWB = 272;
+constexpr int FQ_TROWS = BM + FQ_HALO;
+constexpr int FQ_TBYTES = FQ_TROWS * FQ_ROWB;
+constexpr int FQ_QOFF = 2 * FQ_TBYTES;                     // Q'' tile: 128 rows of FQ_ROWB
+
+__device__ __forceinline__ float fq_val(const char* tile, int r, int ch) {
+  return (float)*reinterpret_cast<const bf16*>(tile + r * FQ_ROWB + ch * 2);
+}
+
+// Q'' rows q0 .. q0 + 127 of head h (KV head g, sequence b of S tokens) into
+// the LDS tile at lds + FQ_QOFF (rows past S hold values never read).
+__device__ __forceinline__ void fused_q_tile(const AttnArgs& a, char* lds, int b, int h, int g,
+                                             int q0, int S) {
+  constexpr int D = 128, CPR = D / 8, CH = FQ_TROWS * CPR;   // 16-byte chunks per tile
+  constexpr int PER = (CH + 511) / 512;
+  const Dims& dm = a.dm;
+  const bf16* lat = reinterpret_cast<const bf16*>(a.qlat) + (long)b * S * dm.nqkv;
+  char* tq = lds;
+  char* tk = lds + FQ_TBYTES;
+  char* qo = lds + FQ_QOFF;
+  // wave w: MFMA column set w % 4 (column n < 16 is channel 16 (w % 4) + n,
+  // n >= 16 its RoPE partner + 64) for tokens 64 (w / 4) .. + 63 (two blocks
+  // of 32), so each tap fragment serves two MFMAs and a work-group reads each
+  // tap row twice
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const bool lo_lane = l32 < 16;
+  const int tb = 64 * (wave >> 2);
+  const int pair = 16 * (wave & 3) + (l32 & 15);
+  const int ch = lo_lane ? pair : pair + 64;
+  const bf16* tq_taps = reinterpret_cast<const bf16*>(a.conv_q) + (long)h * dm.kq * D * D;
+  const bf16* tk_taps = reinterpret_cast<const bf16*>(a.conv_k) + (long)g * dm.kk * D * D;
+  // the B fragments of one lag (8 k-steps), all in flight together
+  bf16x8 bf[8];
+  auto load_taps = [&](const bf16* taps, int j) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      bf[ks] = *reinterpret_cast<const bf16x8*>(taps + ((long)j * D + ch) * D + hi * 8 + ks * 16);
+  };
+  // both tiles and the first lag's taps in one round; rows outside [0, S) read
+  // as zero (resource bounds)
+  {
+    const int r0 = max(q0 - FQ_HALO, 0), r1 = min(S, q0 + BM);
+    bf16x8 v[2][PER];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int col = i == 0 ? h * D : dm.nq + g * D;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(lat + (long)r0 * dm.nqkv + col), 0,
+          r1 > r0 ? ((r1 - r0 - 1) * dm.nqkv + D) * 2 : 0, 0x00020000);
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int e = min((int)threadIdx.x + 512 * p, CH - 1);
+        const int t = q0 - FQ_HALO + e / CPR;
+        v[i][p] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rs, ((t - r0) * dm.nqkv + (e % CPR) * 8) * 2, 0, 0));
+      }
+    }
+    load_taps(tq_taps, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int e = (int)threadIdx.x + 512 * p;
+        if (e < CH)
+          *reinterpret_cast<bf16x8*>((i ? tk : tq) + (e / CPR) * FQ_ROWB + (e % CPR) * 16) = v[i][p];
+      }
+  }
+  __syncthreads();
+  f32x16 qacc[2], kacc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) qacc[i][r] = kacc[i][r] = 0.0f;
+  // lag j of one head's convolution with the taps in bf (loaded beforehand);
+  // acc[mb] holds token block mb of the wave
+  auto conv_lag = [&](f32x16 (&acc)[2], const char* tile, int j) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(
+            tile + (tb + 32 * mb + l32 - j + FQ_HALO) * FQ_ROWB + hi * 16 + ks * 32);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[ks], acc[mb], 0, 0, 0);
+      }
+  };
+  for (int j = 0; j < dm.kq; ++j) {
+    if (j > 0) load_taps(tq_taps, j);
+    conv_lag(qacc, tq, j);
+  }
+  for (int j = 0; j < dm.kk; ++j) {
+    load_taps(tk_taps, j);
+    conv_lag(kacc, tk, j);
+  }
+  const float A = (dm.flags & kQkPre) ? 0.5f : 0.0f;
+  const float Bc = (dm.flags & kQkPost) ? 0.5f : 0.0f;
+  const bool rope = (dm.flags & kRope) != 0;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tr = tb + 32 * mb + 8 * (r >> 2) + 4 * hi + (r & 3);
+      const float qh = qacc[mb][r], kh = kacc[mb][r];
+      const float qp = fq_val(tq, tr + FQ_HALO, ch);
+      const float kp = fq_val(tk, tr + FQ_HALO, ch);
+      const float x = qh + A * (qp + kp) + Bc * (qh + kh);
+      const float2 cs = rope ? a.rope[(long)min(q0 + tr, S - 1) * (D / 2) + pair]
+                             : make_float2(1.f, 0.f);
+      const float xp = __shfl_xor(x, 16);
+      const float y = lo_lane ? x * cs.x - xp * cs.y : x * cs.x + xp * cs.y;
+      *reinterpret_cast<bf16*>(qo + tr * FQ_ROWB + ch * 2) = (bf16)y;
+    }
+  __syncthreads();
+}
+
 // The work-group's query block.  Fixed length: B sequences of a.Sq tokens, Q
 // head-major per sequence, query t at position t.  Variable length (VARLEN):
 // sequence b has nq = tok[b + 1] - tok[b] queries at positions start[b] ..,
@@ -171,10 +296,12 @@ __device__ __forceinline__ void mfma_phase(bool pv, bool qk, f32x16 (&oacc)[Geom
 // start[b] + nq - 1, O rows packed like the tokens.
 // (The body sits in the kernel template itself: moved into a device function
 // it compiles to a slower schedule of the same arithmetic.)
+// FQ: Q'' formed in the kernel from the latent (fixed length, D = 128).
 struct NoMap {};
-template <int D, bool VARLEN, typename Map>
+template <int D, bool VARLEN, bool FQ, typename Map>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
+  static_assert(!FQ || (D == 128 && !VARLEN), "fused Q: fixed length, d = 128");
   using GM = Geom<D>;
   constexpr int NKS = GM::NKS, NMB = GM::NMB, KT_BYTES = GM::KT_BYTES, VT_BYTES = GM::VT_BYTES;
   constexpr int HALF_BYTES = GM::HALF_BYTES, MERGE_STRIDE = GM::MERGE_STRIDE;
@@ -254,13 +381,28 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
   // wait stalls on them.
   // Lane holds query my_q, channels 16*ks + 8*hi + 0..7.
   bf16x8 qf[NKS];
+  if constexpr (FQ) {
+    fused_q_tile(a, lds, b, h, g, q0, nq);
+    const char* qrow = lds + FQ_QOFF + (wq * 32 + l32) * FQ_ROWB + hi * 16;
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    if (my_q < nq) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(qbase + (long)my_q * D + ks * 16 + hi * 8);
-    } else {
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (my_q < nq) {
+        qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)0.0f;
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)0.0f;
+      }
+    }
+    __syncthreads();                         // every wave has its Q before the tiles land
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (my_q < nq) {
+        qf[ks] = *reinterpret_cast<const bf16x8*>(qbase + (long)my_q * D + ks * 16 + hi * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)0.0f;
+      }
     }
   }
 
@@ -437,12 +579,19 @@ hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const int nqb = (a.Sq + BM - 1) / BM;
   dim3 grid(nqb * a.dm.Hq * a.B);
-  if (a.dm.d == 128)
-    hipLaunchKernelGGL((attn_fwd_mfma_kernel<128, false, NoMap>), grid, dim3(512), 0, s, a,
+  if (a.qlat) {
+    if (a.dm.d != 128 || !a.dm.bf16 || !a.conv_q || !a.conv_k || !a.rope || a.dm.kq > FQ_HALO + 1 ||
+        a.dm.kk > FQ_HALO + 1 || (long)a.Sq * a.dm.nqkv * 2 >= (1L << 31))
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_fwd_mfma_kernel<128, false, true, NoMap>), grid, dim3(512), 0, s, a,
                        NoMap{});
-  else
-    hipLaunchKernelGGL((attn_fwd_mfma_kernel<64, false, NoMap>), grid, dim3(512), 0, s, a,
+  } else if (a.dm.d == 128) {
+    hipLaunchKernelGGL((attn_fwd_mfma_kernel<128, false, false, NoMap>), grid, dim3(512), 0, s, a,
                        NoMap{});
+  } else {
+    hipLaunchKernelGGL((attn_fwd_mfma_kernel<64, false, false, NoMap>), grid, dim3(512), 0, s, a,
+                       NoMap{});
+  }
   return hipGetLastError();
 }
 
@@ -455,7 +604,7 @@ hipError_t launch_attn_varlen_mfma(const AttnArgs& a, const VarlenMap& vm, hipSt
     return hipErrorInvalidValue;
   const long nblk = (long)vm.blk[vm.B] * a.dm.Hq;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_mfma_kernel<128, true, VarlenMap>), dim3((unsigned)nblk), dim3(512), 0, s,
+  hipLaunchKernelGGL((attn_fwd_mfma_kernel<128, true, false, VarlenMap>), dim3((unsigned)nblk), dim3(512), 0, s,
                      a, vm);
   return hipGetLastError();
 }

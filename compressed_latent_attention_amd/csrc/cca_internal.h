@@ -202,6 +202,13 @@ struct AttnArgs {
   // split-key partials for decode (fp32 workspace), see launch_attn_decode
   float* part;
   int nsplit;
+  // fused-Q prefill (inference, bf16, d = 128): when qlat is set the attention
+  // forms Q'' itself from the bf16 latent [B*S, nqkv] (q~ of its head, k~ of
+  // its KV head), the taps and the RoPE table, and a.q is not read
+  const void* qlat;
+  const void* conv_q;
+  const void* conv_k;
+  const float2* rope;
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_varlen_mfma(const AttnArgs& a, const VarlenMap& vm, hipStream_t s);

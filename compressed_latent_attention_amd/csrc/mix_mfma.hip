@@ -184,8 +184,10 @@ __device__ __forceinline__ void fill_halo(char* tile, const bf16* st, int nlag, 
 // file: the per-sequence indexing does not fit the two-per-CU budget without
 // spills).  The body sits in the kernel template itself: moved into a device
 // function it compiles to a slower schedule of the same arithmetic.
+// NOQ: the attention forms Q'' itself (fused Q): the query heads are still
+// convolved for the key side's group means, but no Q'' is written.
 struct NoMap {};
-template <int D, int GC, bool VARLEN, typename Map>
+template <int D, int GC, bool VARLEN, bool NOQ, typename Map>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VARLEN ? 1 : 2,
                                                                      VARLEN ? 1 : 2)))
 void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
@@ -291,6 +293,16 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
     zero(qacc);
     conv_head<D>(qacc, tqi, reinterpret_cast<const bf16*>(a.conv_q) + (long)h * dm.kq * D * D,
                  dm.kq, ch, lane, tb0);
+    if constexpr (NOQ) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          mpost[mb][r] += qacc[mb][r];
+          if (!QRES) mpre[mb][r] += tile_val<D>(tqi, trel(mb, r) + HALO, ch);
+        }
+      continue;
+    }
     const long qrow = VARLEN ? q_row0 + h * q_hstride + t0 : (long)(b * dm.Hq + h) * S + t0;
     bf16* qo = reinterpret_cast<bf16*>(a.q_out) + qrow * D + ch;
 #pragma unroll
@@ -414,30 +426,30 @@ hipError_t launch_mix_varlen_mfma(const MixArgs& a, const VarlenMap& vm, hipStre
   const int ntiles8 = (ntiles + XCDS - 1) / XCDS * XCDS;
   const dim3 grid((unsigned)(ntiles8 * a.dm.Hkv));
   if (a.dm.G == 1)
-    hipLaunchKernelGGL((mix_fwd_mfma_kernel<128, 1, true, VarlenMap>), grid, dim3(256), 0, s, a,
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<128, 1, true, false, VarlenMap>), grid, dim3(256), 0, s, a,
                        ntiles8, vm);
   else if (a.dm.G == 2)
-    hipLaunchKernelGGL((mix_fwd_mfma_kernel<128, 2, true, VarlenMap>), grid, dim3(256), 0, s, a,
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<128, 2, true, false, VarlenMap>), grid, dim3(256), 0, s, a,
                        ntiles8, vm);
   else
-    hipLaunchKernelGGL((mix_fwd_mfma_kernel<128, 0, true, VarlenMap>), grid, dim3(256), 0, s, a,
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<128, 0, true, false, VarlenMap>), grid, dim3(256), 0, s, a,
                        ntiles8, vm);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool NOQ>
 hipError_t launch_mix_fwd_mfma_d(const MixArgs& a, hipStream_t s) {
   const int ntiles = (a.S + MGeom<D>::TW - 1) / MGeom<D>::TW;
   const int ntiles8 = (ntiles + XCDS - 1) / XCDS * XCDS;
   const dim3 grid((unsigned)(ntiles8 * a.dm.Hkv * a.B));
   if (a.dm.G == 1)
-    hipLaunchKernelGGL((mix_fwd_mfma_kernel<D, 1, false, NoMap>), grid, dim3(256), 0, s, a,
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<D, 1, false, NOQ, NoMap>), grid, dim3(256), 0, s, a,
                        ntiles8, NoMap{});
   else if (a.dm.G == 2)
-    hipLaunchKernelGGL((mix_fwd_mfma_kernel<D, 2, false, NoMap>), grid, dim3(256), 0, s, a,
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<D, 2, false, NOQ, NoMap>), grid, dim3(256), 0, s, a,
                        ntiles8, NoMap{});
   else
-    hipLaunchKernelGGL((mix_fwd_mfma_kernel<D, 0, false, NoMap>), grid, dim3(256), 0, s, a,
+    hipLaunchKernelGGL((mix_fwd_mfma_kernel<D, 0, false, NOQ, NoMap>), grid, dim3(256), 0, s, a,
                        ntiles8, NoMap{});
   return hipGetLastError();
 }
@@ -446,8 +458,10 @@ hipError_t launch_mix_fwd_mfma(const MixArgs& a, hipStream_t s) {
   if (a.vt_out && (a.s_pad % 64 != 0 || a.s_pad < a.S)) return hipErrorInvalidValue;
   // 32-bit byte offsets within one sequence's latent rows
   if ((long)a.S * a.dm.nqkv * 2 >= (1L << 31)) return hipErrorInvalidValue;
-  if (a.dm.d == 128) return launch_mix_fwd_mfma_d<128>(a, s);
-  if (a.dm.d == 64) return launch_mix_fwd_mfma_d<64>(a, s);
+  // no Q'' output: the fused-Q prefill (d = 128), whose attention forms Q''
+  if (!a.q_out) return a.dm.d == 128 ? launch_mix_fwd_mfma_d<128, true>(a, s) : hipErrorInvalidValue;
+  if (a.dm.d == 128) return launch_mix_fwd_mfma_d<128, false>(a, s);
+  if (a.dm.d == 64) return launch_mix_fwd_mfma_d<64, false>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -259,6 +259,17 @@ int cca_profile_read(cca_handle* h, cca_kernel_time* out, int max);
  * overwritten. */
 cca_status cca_profile_flush(cca_handle* h, void* buf, size_t bytes);
 
+/* Prefill variant with the query side of the mix fused into the attention
+ * (CCA-es §3 item 4, "Implementación Eficiente", and CCA-fr §3 "Implémentation
+ * Efficace": the authors' kernel fuses the convolutions with the attention).
+ * When on, an inference prefill (saved == NULL) of bf16 storage with d = 128
+ * has its attention form Q'' from the latent itself: the mix then writes only
+ * K'', V' and the cache, and Q'' never reaches HBM.  Results equal the
+ * separate passes up to the rounding of Q'' to bf16.  Other calls ignore the
+ * switch.  Off by default; on = 0 turns it off.  CCA_ERR_INVALID_ARG for a
+ * NULL handle. */
+cca_status cca_set_prefill_fusion(cca_handle* h, int32_t on);
+
 /* Static text for a status code. */
 const char* cca_status_string(cca_status s);
 
