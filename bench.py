@@ -382,6 +382,76 @@ def bench_fused(args, torch, cca, w, inp):
     return out
 
 
+def varlen_layout(total=16384, nseq=16, cap=32768, seed=11):
+    """A serving-like chunked prefill batch: nseq chunks of ragged lengths
+    (uniform in [total / (2 nseq), 3 total / (2 nseq)], scaled to sum to
+    total) continuing sequences at ragged cached lengths (uniform below
+    cap - chunk)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = rng.uniform(0.5, 1.5, nseq)
+    lens = np.floor(lens / lens.sum() * total).astype(np.int64)
+    lens[-1] += total - lens.sum()
+    starts = np.array([int(rng.integers(0, cap - n + 1)) for n in lens], dtype=np.int64)
+    offsets = np.concatenate([[0], np.cumsum(lens)])
+    return offsets, starts
+
+
+def bench_varlen(args, torch, cca):
+    """Chunked variable-length prefill of the CCGQA layer (16 chunks, 16384 new
+    tokens in all, over caches of up to 32768 tokens): tokens/s and the
+    attention kernel's MFMA fraction (algorithmic FLOPs: every new query
+    against its cached and earlier new keys)."""
+    from compressed_latent_attention_amd.synthetic import WORKLOADS, make_inputs
+    w = WORKLOADS["ccgqa_prefill_16k"]
+    cap = 32768
+    offsets, starts = varlen_layout(cap=cap)
+    T = int(offsets[-1])
+    wi = make_inputs(w.replace(S=1, B=1))
+    dt = torch.bfloat16
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt)
+    wts = {k: dev(wi[k]) for k in ("w_q", "w_k", "w_v", "w_o", "conv_q", "conv_k")}
+    layer = cca.CCALayer(w.E, w.C, w.Hq, w.Hkv, cap, w.kq, w.kk, w.s_v, w.flags, w.rope_base,
+                         w.dtype)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    B = len(starts)
+    shape = (B, w.Hkv, cap, w.d)
+    kc = torch.randn(shape, generator=gen, device="cuda").to(dt)
+    vc = torch.randn(shape, generator=gen, device="cuda").to(dt)
+    st = torch.randn((B, layer.state_width()), generator=gen, device="cuda").to(dt)
+    x = torch.randn((T, w.E), generator=gen, device="cuda").to(dt)
+    y = torch.empty_like(x)
+    n = cca.cca_varlen_workspace_bytes(layer.handle, offsets.tolist(), starts.tolist())
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    offs, sts = offsets.tolist(), starts.tolist()
+
+    def step():
+        # the caches and states advance every call; the positions stay the
+        # same, so every call does the same work
+        cca.cca_forward_prefill_varlen(layer.handle, wts, x, offs, sts, y, kc, vc, st, ws, stream)
+
+    sec = _time_warm(torch, step, 20)
+    cca.cca_profile_enable(layer.handle, True)
+    _time_loop(torch, step, 10, 0)
+    prof = cca.cca_profile_read(layer.handle)
+    cca.cca_profile_enable(layer.handle, False)
+    layer.close()
+    lens = np.diff(offsets)
+    pairs = float(sum(int(n) * int(s) + int(n) * (int(n) + 1) // 2 for n, s in zip(lens, starts)))
+    attn_fl = 4.0 * w.Hq * w.d * pairs
+    kernels = {k: {"avg_ms": v[1] / max(v[0], 1), "launches": v[0]} for k, v in prof.items()}
+    attn_ms = kernels.get("varlen_attn", {}).get("avg_ms", float("nan"))
+    return {"workload": f"ccgqa chunked prefill: {B} chunks, {T} new tokens (lengths "
+                        f"{int(lens.min())}..{int(lens.max())}) at cached lengths "
+                        f"{int(starts.min())}..{int(starts.max())}, capacity {cap}, E={w.E}, "
+                        f"Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}, bf16",
+            "tokens_per_s": T / sec, "ms_per_call": sec * 1e3,
+            "attn_flops": attn_fl, "attn_tflops": attn_fl / (attn_ms * 1e-3) / 1e12,
+            "attn_frac_of_bf16_peak": attn_fl / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "kernels": kernels}
+
+
 def bench_d64(args, torch, cca):
     """The CCGQA layer with head dimension 64 (8 query and 4 KV heads of 64:
     the same latent widths and KV-cache size as the d = 128 layer): the 16k
@@ -526,10 +596,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--warm-s", type=float, default=0.3,
                     help="untimed prefill steps continue past --warmup until this many seconds")
-    ap.add_argument("--rows", default="prefill,mix,fused,decode,backward,d64",
+    ap.add_argument("--rows", default="prefill,mix,fused,varlen,decode,backward,d64",
                     help="comma list: prefill (headline, always run), mix (the mix kernel with "
                          "cold caches), fused (the prefill with the query side of the mix in "
-                         "the attention, against the separate passes), decode, backward, d64 "
+                         "the attention, against the separate passes), varlen (the chunked "
+                         "variable-length prefill), decode, backward, d64 "
                          "(the head-dimension-64 layer: prefill, decode, backward); n1 adds the "
                          "MHA / GQA comparators over S = 4k .. 64k (not run by default)")
     ap.add_argument("--bwd-steps", type=int, default=3, help="timed backward steps")
@@ -604,6 +675,8 @@ def main():
         out["mix_cold"] = bench_mix_cold(args, torch, cca, w, inp)
     if "fused" in rows:
         out["fused_q"] = bench_fused(args, torch, cca, w, inp)
+    if "varlen" in rows:
+        out["varlen"] = bench_varlen(args, torch, cca)
     if "decode" in rows:
         out["decode"] = bench_decode(args, torch, cca)
     if "backward" in rows:
