@@ -81,6 +81,29 @@ __device__ __forceinline__ void dma_part(char* dst, const bf16* base, long ld, i
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16, src, 0, 0, 0);
 }
 
+// Block i of this wave's share of a B tile whose 256 rows may cross segments
+// of B (the concatenated q / k / v weights when a segment does not start at a
+// multiple of 256): each 1 KB block (8 rows) resolves its own segment, so a
+// segment start must be a multiple of 8.  Rows past the end of B read as zero.
+template <int CB>
+__device__ __forceinline__ void dma_part_seg(char* dst, const GemmArgs& g, int n0, int k0,
+                                             int wave, int lane, int i) {
+  const int blk = wave * CB + i;
+  const int row0 = n0 + blk * 8;
+  int s = 0;
+  if (g.b_nseg > 1 && row0 >= g.b_start[1]) s = 1;
+  if (g.b_nseg > 2 && row0 >= g.b_start[2]) s = 2;
+  const int seg_end = s + 1 < g.b_nseg ? g.b_start[s + 1] : g.N;
+  const int rows = min(seg_end - row0, 8);
+  const bf16* base = reinterpret_cast<const bf16*>(g.b_ptr[s]) + (long)(row0 - g.b_start[s]) * g.ldb;
+  const int nrec = rows > 0 ? ((rows - 1) * (int)g.ldb + g.K - k0) * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(base + k0), 0, nrec, 0x00020000);
+  const int r = blk * 8 + (lane >> 3), pos = lane & 7;
+  const int src = (lane >> 3) * (int)g.ldb * 2 + ((pos ^ ((r >> 1) & 7)) << 4);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16, src, 0, 0, 0);
+}
+
 // K-major operand tile: k-rows k0 .. k0 + 63, columns r0 .. r0 + 255 of a
 // row-major [K, R] matrix (row stride ld), as 64 LDS rows of 512 B with chunk c
 // (columns 8 c .. 8 c + 7) of row k at chunk c ^ 4 (k & 3): the 4 k-rows of a
@@ -132,8 +155,9 @@ __device__ __forceinline__ bf16x8 t_frag(const char* p) {
 // NW = 4: waves of 128 x 128 (256 accumulator registers), one per SIMD;
 // NW = 8: waves of 128 x 64, two per SIMD, so one wave's MFMAs cover the
 // other's copy issue, fragment waits and barrier.
-// KT: both operands K-major (TN layout).
-template <typename OutT, int NW, bool KT>
+// KT: both operands K-major (TN layout).  SB: B tiles may cross segments of
+// B (dma_part_seg).
+template <typename OutT, int NW, bool KT, bool SB = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   constexpr int WN = NW / 2;                 // waves along N
@@ -175,7 +199,12 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     dma_tile_t<CB>(lds + A_BYTES, bmat, g.ldb, n0, kvalid, kbeg, wave, lane);
   } else {
     dma_tile<CB>(lds, abase, g.lda, arows, g.K, kbeg, wave, lane);
-    dma_tile<CB>(lds + A_BYTES, bbase, g.ldb, brows, g.K, kbeg, wave, lane);
+    if constexpr (SB) {
+#pragma unroll
+      for (int i = 0; i < CB; ++i) dma_part_seg<CB>(lds + A_BYTES, g, n0, kbeg, wave, lane, i);
+    } else {
+      dma_tile<CB>(lds + A_BYTES, bbase, g.ldb, brows, g.K, kbeg, wave, lane);
+    }
   }
 
   f32x16 acc[4][NJ];
@@ -251,6 +280,7 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
               else dma_part_t<CB>(nx + A_BYTES, bmat, g.ldb, n0, kvalid, knx, wave, lane, blk - CB);
             } else {
               if (blk < CB) dma_part<CB>(nx, abase, g.lda, arows, g.K, knx, wave, lane, blk);
+              else if constexpr (SB) dma_part_seg<CB>(nx + A_BYTES, g, n0, knx, wave, lane, blk - CB);
               else dma_part<CB>(nx + A_BYTES, bbase, g.ldb, brows, g.K, knx, wave, lane, blk - CB);
             }
           }
@@ -303,8 +333,13 @@ bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError
       return false;
   }
   if ((long)TM * g.ldc * 4 >= (1L << 31)) return false;
-  for (int i = 1; i < g.b_nseg; ++i)
-    if (g.b_start[i] % TN != 0) return false;
+  // B segments starting inside a tile: per-block segment lookup (NT only)
+  bool sb = false;
+  for (int i = 1; i < g.b_nseg; ++i) {
+    if (g.b_start[i] % 8 != 0) return false;
+    if (g.b_start[i] % TN != 0) sb = true;
+  }
+  if (sb && (kt || (long)8 * g.ldb * 2 >= (1L << 31))) return false;
   if ((long)TM * g.lda * 2 >= (1L << 31) || (long)TN * g.ldb * 2 >= (1L << 31)) return false;
   const int tiles_m = (g.M + TM - 1) / TM, tiles_n = (g.N + TN - 1) / TN;
   const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
@@ -318,6 +353,14 @@ bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError
   if (kt) {
     if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, true>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
     else hipLaunchKernelGGL((gemm_nt_256_kernel<float, 4, true>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
+  } else if (sb) {
+    if (out_f32) {
+      if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, false, true>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+      else hipLaunchKernelGGL((gemm_nt_256_kernel<float, 4, false, true>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
+    } else {
+      if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 8, false, true>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+      else hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 4, false, true>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
+    }
   } else if (out_f32) {
     if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, false>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
     else hipLaunchKernelGGL((gemm_nt_256_kernel<float, 4, false>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);

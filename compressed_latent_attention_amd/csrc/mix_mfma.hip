@@ -180,16 +180,19 @@ __device__ __forceinline__ void fill_halo(char* tile, const bf16* st, int nlag, 
 // ..; the conv and shift history before its first token comes from a.state;
 // Q'' goes to the packed [Hq][T][d] (T = a.S), K'' and V' to the caches at
 // their positions, and no V'^T is written.
-// A variable-length launch runs one work-group per CU (the full register
-// file: the per-sequence indexing does not fit the two-per-CU budget without
-// spills).  The body sits in the kernel template itself: moved into a device
-// function it compiles to a slower schedule of the same arithmetic.
+// A variable-length launch, and the general group size (GC = 0: the group
+// loop is not unrolled and the pre-convolution group mean stays in
+// registers), run one work-group per CU with the full register file: at two
+// per CU they spill (the general instance 112 registers, its 16x-layer mix
+// 70 us against 46 us at one per CU).  The body sits in the kernel template
+// itself: moved into a device function it compiles to a slower schedule of
+// the same arithmetic.
 // NOQ: the attention forms Q'' itself (fused Q): the query heads are still
 // convolved for the key side's group means, but no Q'' is written.
 struct NoMap {};
 template <int D, int GC, bool VARLEN, bool NOQ, typename Map>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VARLEN ? 1 : 2,
-                                                                     VARLEN ? 1 : 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VARLEN || GC == 0 ? 1 : 2,
+                                                                     VARLEN || GC == 0 ? 1 : 2)))
 void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
   using MG = MGeom<D>;
   constexpr int TW = MG::TW, TBYTES = MG::TBYTES, ROWB = MG::ROWB;
