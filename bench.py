@@ -204,15 +204,15 @@ DECODE_BYTES_NOTE = ("K and V caches over positions 0..pos of every sequence + a
                      "+ x_new, y_new, the rolling state and the new cache rows")
 
 
-def decode_bytes(w) -> float:
+def decode_bytes(w, positions=None) -> float:
     """Algorithmic HBM bytes of one decode step: the cache rows attention reads
     (positions 0..pos, K and V), every weight once, and the per-token
     activations (x_new, y_new, the state read and written, the cache rows
     written)."""
     es = 2
     d, nq, nk = w.d, w.Hq * w.d, w.Hkv * w.d
-    keys = w.S + 1
-    cache = 2.0 * w.B * w.Hkv * keys * d * es
+    keys = w.B * (w.S + 1) if positions is None else sum(int(p) + 1 for p in positions)
+    cache = 2.0 * w.Hkv * keys * d * es
     weights = (w.E * (nq + 2 * nk) + w.E * nq + (w.Hq * w.kq + w.Hkv * w.kk) * d * d) * es
     state_w = (w.kq - 1) * nq + (w.kk - 1) * nk + nk
     acts = w.B * (2 * w.E + 2 * state_w + 2 * nk) * es
@@ -255,7 +255,18 @@ def _time_warm(torch, fn, steps, warm_s=0.15):
     return _time_loop(torch, fn, steps, max(steps, int(warm_s / one)))
 
 
-def bench_decode(args, torch, cca, hkv=None, w=None):
+def ragged_positions(B=32, cap=32768, seed=13):
+    """A ragged decode batch: a quarter of the sequences long (16k..32k cached
+    tokens), the rest short (512..4096), seeded."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n_long = B // 4
+    pos = [int(rng.integers(16384, cap)) for _ in range(n_long)]
+    pos += [int(rng.integers(512, 4097)) for _ in range(B - n_long)]
+    rng.shuffle(pos)
+    return pos
+
+
+def bench_decode(args, torch, cca, hkv=None, w=None, positions=None):
     """32-sequence CCGQA decode step over a 32768-token cache.  The cache, the
     state and x_new are drawn on the GPU from a seeded torch generator (N(0,1),
     the same law as the parity workload; the timing does not depend on the
@@ -277,7 +288,7 @@ def bench_decode(args, torch, cca, hkv=None, w=None):
     vc = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(dt)
     st = torch.randn((w.B, layer.state_width()), generator=gen, device="cuda").to(dt)
     xn = torch.randn((w.B, w.E), generator=gen, device="cuda").to(dt)
-    pos = [w.S] * w.B
+    pos = [w.S] * w.B if positions is None else list(positions)
     ws = layer.workspace(cca.CCA_OP_DECODE, w.B, 0)
     yn = torch.empty_like(xn)
     stream = torch.cuda.current_stream()
@@ -292,13 +303,15 @@ def bench_decode(args, torch, cca, hkv=None, w=None):
     _time_loop(torch, step, 5, 0)
     prof = cca.cca_profile_read(layer.handle)
     cca.cca_profile_enable(layer.handle, False)
-    byts = decode_bytes(w)
+    byts = decode_bytes(w, positions)
     kernels = {k: {"avg_ms": v[1] / max(v[0], 1), "launches": v[0]} for k, v in prof.items()}
     attn_ms = kernels.get("decode_attn", {}).get("avg_ms", float("nan"))
-    cache_bytes = 2.0 * w.B * w.Hkv * (w.S + 1) * w.d * 2
+    cache_bytes = 2.0 * w.Hkv * sum(p + 1 for p in pos) * w.d * 2
     layer.close()
+    cached = (f"cache {w.S} tokens" if positions is None else
+              f"ragged caches of {min(pos)}..{max(pos)} tokens ({sum(pos)} in all)")
     return {
-        "workload": f"{w.name}: B={w.B}, cache {w.S} tokens, E={w.E}, Hq={w.Hq}, "
+        "workload": f"{w.name}: B={w.B}, {cached}, E={w.E}, Hq={w.Hq}, "
                     f"Hkv={w.Hkv}, d={w.d}, bf16",
         "tokens_per_s": w.B / sec,
         "ms_per_step": sec * 1e3,
@@ -679,6 +692,7 @@ def main():
         out["varlen"] = bench_varlen(args, torch, cca)
     if "decode" in rows:
         out["decode"] = bench_decode(args, torch, cca)
+        out["decode_ragged"] = bench_decode(args, torch, cca, positions=ragged_positions())
     if "backward" in rows:
         out["backward"] = bench_backward(args, torch, cca)
     if "d64" in rows:

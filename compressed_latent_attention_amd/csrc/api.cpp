@@ -582,7 +582,7 @@ cca_status decode_step(cca_handle* h, cca_handle* th, const cca_weights* w, cons
     aa.q = qn; aa.k = k_cache; aa.v = v_cache;
     aa.kv_bs = (long)dm.Hkv * dm.max_seq_len * dm.d; aa.kv_hs = (long)dm.max_seq_len * dm.d;
     aa.o = on; aa.lse = nullptr; aa.decode = true; aa.pos = pos;
-    aa.part = (float*)(base + L.part); aa.nsplit = decode_nsplit(dm, B);
+    aa.part = (float*)(base + L.part); aa.nsplit = decode_splits(dm, B, aa.pos);
     CCA_TRY_HIP(timed(th, "decode_attn", s, [&] { return launch_attn_decode(aa, s); }));
 
     GemmArgs gu = gemm_nt(B, dm.E, dm.nq, on, dm.nq, w->w_o, dm.nq, y_new, dm.E);

@@ -30,6 +30,9 @@ struct Dims {
 
 struct DecodePos {
   int32_t p[kMaxDecodeBatch];
+  // split-key decode: sequence b's work-groups per KV head are off[b] ..
+  // off[b + 1] - 1 of the flattened grid (sized per sequence from its length)
+  int32_t off[kMaxDecodeBatch + 1];
 };
 
 // ------------------------------------------------------------------ GEMM
@@ -213,7 +216,9 @@ struct AttnArgs {
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_varlen_mfma(const AttnArgs& a, const VarlenMap& vm, hipStream_t s);
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);
-int decode_nsplit(const Dims& dm, int B);
+// Split-key work-groups per KV head for each sequence (into pos.off, from
+// pos.p); returns their total.  The fast path only.
+int decode_splits(const Dims& dm, int B, DecodePos& pos);
 size_t decode_part_floats(const Dims& dm, int B);
 
 // ------------------------------------------------------------------ backward

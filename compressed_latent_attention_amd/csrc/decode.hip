@@ -3,9 +3,10 @@
 // decoding; CCA-fr §4 "Décodage").  The step streams the K and V caches once,
 // so it is bound by HBM bandwidth.
 //
-// Split over keys (flash-decoding): about 256 work-groups in all, nsplit per
-// (KV head g, sequence b), each serving all G query heads that read head g, so
-// each cache byte is read once per step.  The 4 nsplit waves of one (b, g)
+// Split over keys (flash-decoding): about 256 work-groups in all, nsplit_b per
+// (KV head g, sequence b) in proportion to the sequence's length (a ragged
+// batch spreads its long caches over the chip), each serving all G query
+// heads that read head g, so each cache byte is read once per step.  The 4 nsplit waves of one (b, g)
 // take its 32-key blocks round robin, so together they sweep its K and V as
 // one window; every wave keeps its own online softmax:
 //   1. S = Q K^T on MFMA: A = the G queries as stored (rows, padded to 32
@@ -58,8 +59,10 @@ __device__ __forceinline__ float half_max(float v) {
 // GQ: the group size rounded up to a power of two (the kernel is instantiated
 // for 1, 2, 4, 8), so P V keeps only that many accumulator rows in registers.
 //
-// Work-group (split, KV head g, sequence b); its wave w takes the 32-key
-// blocks (i nsplit + split) NW + w, i = 0, 1, ..., so the nsplit NW waves of
+// Work-group (flattened split index over the sequences, KV head g): sequence
+// b owns indices pos.off[b] .. pos.off[b + 1] - 1 (nsplit of them); its wave w
+// takes the 32-key blocks (i nsplit + split) NW + w, i = 0, 1, ..., so the
+// nsplit NW waves of
 // one (sequence, head) read consecutive 8 KB blocks and sweep its K and V as
 // one wide window.  Each wave runs its own online softmax over its blocks with
 // no barrier: while block n is scored and accumulated, the K and V rows of
@@ -81,8 +84,18 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
 
   const Dims& dm = a.dm;
   const int G = dm.G;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int nsplit = gridDim.x;
+  const int g = blockIdx.y;
+  int b = 0;
+  {
+    int lo = 0, hi2 = a.B - 1;                        // last b with off[b] <= blockIdx.x
+    while (lo < hi2) {
+      const int mid = (lo + hi2 + 1) >> 1;
+      if (a.pos.off[mid] <= (int)blockIdx.x) lo = mid; else hi2 = mid - 1;
+    }
+    b = lo;
+  }
+  const int off_b = a.pos.off[b];
+  const int split = (int)blockIdx.x - off_b, nsplit = a.pos.off[b + 1] - off_b;
   const int nkeys = a.pos.p[b] + 1;
   const int nblk = (nkeys + 31) / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -237,8 +250,8 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
       }
   __syncthreads();
   // merge the four waves (a wave with no block has m = -inf, l = 0, O = 0)
-  // partial of (b, query head g*G + q, split): part[((b*Hq + g*G + q)*nsplit + split)*PSTRIDE]
-  float* part = a.part + ((long)(b * dm.Hq + g * G) * nsplit + split) * PSTRIDE;
+  // partial of (b, query head h, split): part[(off_b Hq + h nsplit + split) PSTRIDE]
+  float* part = a.part + ((long)off_b * dm.Hq + (long)g * G * nsplit + split) * PSTRIDE;
   for (int e = threadIdx.x; e < G * D; e += 256) {
     const int q = e / D, c = e % D;
     float mx = -INFINITY;
@@ -275,9 +288,9 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(AttnArgs a) {
   __shared__ float red[D / 64][2];
   const Dims& dm = a.dm;
   const int h = blockIdx.x, b = blockIdx.y;
-  const int nsplit = a.nsplit;
+  const int off_b = a.pos.off[b], nsplit = a.pos.off[b + 1] - off_b;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const float* part = a.part + (long)(b * dm.Hq + h) * nsplit * PSTRIDE;
+  const float* part = a.part + ((long)off_b * dm.Hq + (long)h * nsplit) * PSTRIDE;
   float m = -INFINITY;
   for (int c = t; c < nsplit; c += D) m = fmaxf(m, part[(long)c * PSTRIDE + D]);
 #pragma unroll
@@ -310,23 +323,35 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(AttnArgs a) {
 
 }  // namespace
 
-// Work-groups per (sequence, KV head): about TARGET_WGS in all, at most one
-// wave per 32-key block of the cache.
-int decode_nsplit(const Dims& dm, int B) {
-  if (!fast_decode(dm)) return 1;
-  const int nblk = (dm.max_seq_len + 31) / 32;
-  const int ns = TARGET_WGS / std::max(1, B * dm.Hkv);
-  return std::max(1, std::min({ns, nblk / NW, MAX_SPLIT}));
+// Work-groups per (sequence, KV head): about TARGET_WGS in all, shared in
+// proportion to the sequences' 32-key block counts, at least one, at most one
+// wave per block and MAX_SPLIT.  Equal lengths give every sequence
+// TARGET_WGS / (B Hkv).
+int decode_splits(const Dims& dm, int B, DecodePos& pos) {
+  long total_blk = 0;
+  for (int b = 0; b < B; ++b) total_blk += (pos.p[b] + 1 + 31) / 32;
+  pos.off[0] = 0;
+  for (int b = 0; b < B; ++b) {
+    const long nb = (pos.p[b] + 1 + 31) / 32;
+    const long share = (long)(TARGET_WGS / dm.Hkv) * nb / std::max(1L, total_blk);
+    const int ns = (int)std::max(1L, std::min({share, nb / NW, (long)MAX_SPLIT}));
+    pos.off[b + 1] = pos.off[b] + ns;
+  }
+  return pos.off[B];
 }
 
+// Partials: at most TARGET_WGS / Hkv + B split work-groups per KV head (the
+// shares sum to at most the first term, the one-per-sequence floor adds B).
 size_t decode_part_floats(const Dims& dm, int B) {
-  return fast_decode(dm) ? (size_t)B * dm.Hq * decode_nsplit(dm, B) * pstride(dm) : 0;
+  return fast_decode(dm)
+             ? (size_t)(TARGET_WGS / dm.Hkv + B) * dm.Hq * pstride(dm)
+             : 0;
 }
 
 namespace {
 template <int D>
 void launch_decode_d(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.nsplit, a.dm.Hkv, a.B);
+  const dim3 grid(a.nsplit, a.dm.Hkv);
   if (a.dm.G <= 1)
     hipLaunchKernelGGL((attn_decode_split_kernel<D, 1>), grid, dim3(256), 0, s, a);
   else if (a.dm.G <= 2)
@@ -341,7 +366,9 @@ void launch_decode_d(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s) {
   if (!fast_decode(a.dm)) return launch_attn_fwd(a, s);
-  if (a.part == nullptr || a.nsplit != decode_nsplit(a.dm, a.B) || a.nsplit > MAX_SPLIT)
+  // a.nsplit: the flattened split count, pos.off[B]
+  if (a.part == nullptr || a.nsplit < a.B || a.nsplit != a.pos.off[a.B] ||
+      a.nsplit > TARGET_WGS / a.dm.Hkv + a.B)
     return hipErrorInvalidValue;
   if (a.dm.d == 128)
     launch_decode_d<128>(a, s);
