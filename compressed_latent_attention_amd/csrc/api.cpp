@@ -638,7 +638,8 @@ cca_status cca_forward_prefill_varlen(cca_handle* h, const cca_weights* w, const
     const cca_status st = varlen_plan(h, offsets_host, start_host, B, &P);
     if (st != CCA_OK) return st;
     const Dims& dm = h->dm;
-    if (!prefill_uses_mfma(dm)) return CCA_ERR_UNSUPPORTED;
+    // the variable-length kernels are built for bf16 with d = 128
+    if (!prefill_uses_mfma(dm) || dm.d != 128) return CCA_ERR_UNSUPPORTED;
     if (P.T == 0) return CCA_OK;
     if (!x || !y || !k_cache || !v_cache || !state || !workspace) return CCA_ERR_INVALID_ARG;
     if (!w->w_q || !w->w_k || !w->w_v || !w->w_o || !w->conv_q || !w->conv_k)

@@ -145,3 +145,15 @@ def test_varlen_rejects_bad_layouts():
     torch.cuda.synchronize()
     assert int(torch.count_nonzero(kc)) == 0 and int(torch.count_nonzero(st)) == 0
     layer.close()
+    # head dimension 64: not built for chunks, refused before any launch
+    w64 = Workload("varlen_d64", B=1, S=1, E=512, C=2, Hq=4, Hkv=2, seed=0)
+    l64 = layer_of(w64, max_seq_len=64)
+    inp64 = make_inputs(Workload("wts64", B=1, S=1, E=512, C=2, Hq=4, Hkv=2, seed=3))
+    x64 = torch.zeros((10, 512), dtype=torch.bfloat16, device="cuda")
+    kc64 = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16, device="cuda")
+    st64 = torch.zeros((1, l64.state_width()), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(cca.CCAError) as ei:
+        l64.forward_prefill_varlen(dev_weights(inp64, w64), x64, [0, 10], [0], kc64,
+                                   torch.zeros_like(kc64), st64)
+    assert ei.value.status == cca.CCA_ERR_UNSUPPORTED
+    l64.close()
