@@ -395,26 +395,12 @@ def bench_fused(args, torch, cca, w, inp):
     return out
 
 
-def varlen_layout(total=16384, nseq=16, cap=32768, seed=11):
-    """A serving-like chunked prefill batch: nseq chunks of ragged lengths
-    (uniform in [total / (2 nseq), 3 total / (2 nseq)], scaled to sum to
-    total) continuing sequences at ragged cached lengths (uniform below
-    cap - chunk)."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    lens = rng.uniform(0.5, 1.5, nseq)
-    lens = np.floor(lens / lens.sum() * total).astype(np.int64)
-    lens[-1] += total - lens.sum()
-    starts = np.array([int(rng.integers(0, cap - n + 1)) for n in lens], dtype=np.int64)
-    offsets = np.concatenate([[0], np.cumsum(lens)])
-    return offsets, starts
-
-
 def bench_varlen(args, torch, cca):
     """Chunked variable-length prefill of the CCGQA layer (16 chunks, 16384 new
     tokens in all, over caches of up to 32768 tokens): tokens/s and the
     attention kernel's MFMA fraction (algorithmic FLOPs: every new query
     against its cached and earlier new keys)."""
-    from compressed_latent_attention_amd.synthetic import WORKLOADS, make_inputs
+    from compressed_latent_attention_amd.synthetic import WORKLOADS, make_inputs, varlen_layout
     w = WORKLOADS["ccgqa_prefill_16k"]
     cap = 32768
     offsets, starts = varlen_layout(cap=cap)

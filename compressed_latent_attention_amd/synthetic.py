@@ -167,6 +167,20 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray
     return out
 
 
+def varlen_layout(total: int = 16384, nseq: int = 16, cap: int = 32768, seed: int = 11):
+    """A serving-like chunked prefill batch: nseq chunks of ragged lengths
+    (uniform in [total / (2 nseq), 3 total / (2 nseq)], scaled to sum to
+    total) continuing sequences at ragged cached lengths (uniform below
+    cap - chunk).  Returns (offsets [nseq + 1], starts [nseq]) as int64."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = rng.uniform(0.5, 1.5, nseq)
+    lens = np.floor(lens / lens.sum() * total).astype(np.int64)
+    lens[-1] += total - lens.sum()
+    starts = np.array([int(rng.integers(0, cap - n + 1)) for n in lens], dtype=np.int64)
+    offsets = np.concatenate([[0], np.cumsum(lens)])
+    return offsets, starts
+
+
 def state_width(w: Workload) -> int:
     """Elements of rolling decode state per sequence: [q lags 1..kq-1 |
     k lags 1..kk-1 | v at lag 1], most recent lag first."""

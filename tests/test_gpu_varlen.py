@@ -13,7 +13,7 @@ cache rows outside the chunks must be untouched.
 import numpy as np
 import pytest
 
-from compressed_latent_attention_amd.synthetic import Workload, make_inputs
+from compressed_latent_attention_amd.synthetic import WORKLOADS, Workload, make_inputs, varlen_layout
 from oracle import cca as O
 
 pytestmark = pytest.mark.gpu
@@ -118,6 +118,45 @@ def test_varlen_one_chunk_equals_two():
     say(f"[varlen] one chunk vs two: y {e:.2e}")
     assert e <= TOL["bf16"]
     assert rel(host(kc2), host(kc)) <= TOL["bf16"] and rel(host(st2), host(st)) <= TOL["bf16"]
+    layer.close()
+
+
+def test_varlen_bench_layout_sampled():
+    """The benchmark's launch configuration: 16 chunks (583..1598 tokens,
+    16384 in all) continuing sequences at cached lengths 4298..30930 over
+    32768-token caches, all in one call.  The oracle decodes the first 128
+    tokens of two of the chunks one by one (a chunk's first tokens depend on
+    nothing after them); their y rows and cache rows are compared."""
+    w = WORKLOADS["ccgqa_prefill_16k"]
+    cap = 32768
+    offsets, starts = varlen_layout(cap=cap)
+    B, T = len(starts), int(offsets[-1])
+    say(f"[varlen] bench layout: {B} chunks, {T} tokens, cap {cap}")
+    x = make_inputs(Workload("varlen_bench_x", B=1, S=T, E=w.E, C=w.C, Hq=w.Hq, Hkv=w.Hkv,
+                             seed=21))["x"][0]
+    pin = make_inputs(w.replace(name="varlen_bench_cache", B=B, S=cap, kind="decode",
+                                max_seq_len=cap, seed=23))
+    layer = layer_of(w, max_seq_len=cap)
+    kc, vc, st = dev(pin["k_cache"], w), dev(pin["v_cache"], w), dev(pin["state"], w)
+    y = layer.forward_prefill_varlen(dev_weights(pin, w), dev(x, w), offsets.tolist(),
+                                     starts.tolist(), kc, vc, st)
+    torch.cuda.synchronize()
+    yh = host(y)
+    m = 128
+    for b in (10, 3):
+        s0, r0 = int(starts[b]), int(offsets[b])
+        rows = slice(0, s0 + m)
+        y_ref, kc_ref, vc_ref, _ = O.prefill_chunks(
+            x[r0:r0 + m], np.array([0, m]), np.array([s0]), params_of(pin), spec_of(w),
+            pin["k_cache"][b:b + 1, :, rows], pin["v_cache"][b:b + 1, :, rows],
+            pin["state"][b:b + 1])
+        errs = {"y": rel(yh[r0:r0 + m], y_ref),
+                "k": rel(host(kc[b, :, s0:s0 + m]), kc_ref[0, :, s0:s0 + m]),
+                "v": rel(host(vc[b, :, s0:s0 + m]), vc_ref[0, :, s0:s0 + m])}
+        say(f"  sequence {b} (start {s0}): rel errors {errs}")
+        for k, e in errs.items():
+            assert e <= TOL["bf16"], (b, k, e)
+    assert np.all(np.isfinite(yh))
     layer.close()
 
 
