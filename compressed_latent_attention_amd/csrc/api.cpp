@@ -236,6 +236,9 @@ GemmArgs gemm_down(const Dims& dm, int M, const void* a, const cca_weights* w, v
 
 // Variable-length prefill: per-sequence maps for the mix (64-token tiles)
 // and the attention (128-query blocks), and the workspace regions.
+// the variable-length attention kernel takes both by value (4 KB of kernel arguments at most)
+static_assert(sizeof(AttnArgs) + sizeof(VarlenMap) <= 4096, "kernel arguments exceed 4 KB");
+
 struct VarlenPlan {
   VarlenMap mix, attn;
   int T, s_pad;

@@ -595,8 +595,6 @@ hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-static_assert(sizeof(AttnArgs) + sizeof(VarlenMap) <= 4096, "kernel arguments exceed 4 KB");
-
 // Variable-length attention: a.q packed [Hq][T][d], a.k / a.v the caches (kv_bs,
 // kv_hs), a.vt the V'^T of every sequence [B][Hkv][d][s_pad], a.o packed
 // [T][Hq*d]; vm.blk counts 128-query blocks.  No lse / o32.
