@@ -236,20 +236,33 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnBwdArgs a) {
     for (int e = 0; e < 8; ++e) o[e] = (f16)((float)w[i][e] * dscale);
     *reinterpret_cast<f16x8*>(dst1 + (long)t * D + c) = o;
   }
-  // D_t = <dO_t, O_t> in fp32: each thread sums D / 4 channels of one token
+  // D_t = <dO_t, O_t> in fp32 from the dO chunks above and the same chunks of
+  // O (fp32, rows past S read as zero): each thread's 8 channels, then a sum
+  // over the CPR consecutive lanes that hold one token
   if (is_q) {
-    const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
-    const int t = t0 + r;
-    float sacc = 0.0f;
-    if (t < S) {
-      const float* orow = a.o32 + ((long)(b * S + t) * dm.Hq + h) * D + part * (D / 4);
-      const bf16* drow = src1 + (long)t * dm.nq + part * (D / 4);
-#pragma unroll 8
-      for (int c = 0; c < D / 4; ++c) sacc = fmaf((float)drow[c], orow[c], sacc);
+    const long orow0 = ((long)b * S * dm.Hq + h) * D;
+    const int ldo = dm.Hq * D;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.o32 + orow0), 0, ((S - 1) * ldo + D) * 4, 0x00020000);
+    f32x4 ov[NI][2];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int f = threadIdx.x + 256 * i;
+      const int t = t0 + f / CPR, c = (f % CPR) * 8;
+      ov[i][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, (t * ldo + c) * 4, 0, 0));
+      ov[i][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, (t * ldo + c + 4) * 4, 0, 0));
     }
-    sacc += __shfl_xor(sacc, 1);
-    sacc += __shfl_xor(sacc, 2);
-    if (part == 0 && t < S) a.Dsum[hrow * S + t] = sacc * dscale;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int f = threadIdx.x + 256 * i;
+      const int t = t0 + f / CPR;
+      float sacc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sacc = fmaf((float)w[i][e], ov[i][e >> 2][e & 3], sacc);
+#pragma unroll
+      for (int off = 1; off < CPR; off <<= 1) sacc += __shfl_xor(sacc, off);
+      if (f % CPR == 0 && t < S) a.Dsum[hrow * S + t] = sacc * dscale;
+    }
   }
 }
 
@@ -752,8 +765,8 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) {
   const int nparts = attn_bwd_parts(dm);
   if (nparts == 4 && (!a.dk3 || !a.dv3 || !a.dk4 || !a.dv4 || a.sum_by_consumer))
     return hipErrorInvalidValue;
-  // 32-bit byte offsets within one sequence's token-major dO rows
-  if ((long)a.S * dm.nq * 2 >= (1L << 31)) return hipErrorInvalidValue;
+  // 32-bit byte offsets within one sequence's token-major dO (bf16) and O (fp32) rows
+  if ((long)a.S * dm.nq * 4 >= (1L << 31)) return hipErrorInvalidValue;
   if (!a.amax_part || !a.dscale || dm.nq % 8 != 0) return hipErrorInvalidValue;
   const long n8 = (long)a.B * a.S * dm.nq / 8;
   hipLaunchKernelGGL(bwd_do_absmax_kernel, dim3(kAmaxParts), dim3(256), 0, s,

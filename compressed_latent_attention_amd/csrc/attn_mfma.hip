@@ -152,15 +152,29 @@ __device__ __forceinline__ void mfma_phase(bool pv, bool qk, f32x16 (&oacc)[Geom
       }
   }
   if (qk) {
+    // K fragment i: k-step i / 2, key block i % 2.  The reads run four
+    // fragments ahead of the MFMAs (the scheduler alone keeps two in flight,
+    // and an MFMA then waits out most of an LDS round trip).
+    constexpr int NQ = 2 * Geom<D>::NKS, AHEAD = 4;
+    bf16x8 kf[NQ];
 #pragma unroll
-    for (int ks = 0; ks < Geom<D>::NKS; ++ks)
+    for (int i = 0; i < NQ; ++i)
+      kf[i] = *reinterpret_cast<const bf16x8*>(ks_ + k_off<D>((i & 1) * 32 + krow,
+                                                              2 * (i >> 1) + hi));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(ks_ + k_off<D>(kb * 32 + krow, 2 * ks + hi));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? minit : sacc[kb],
-                                                           0, 0, 0);
-      }
+    for (int i = 0; i < NQ; ++i)
+      sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1],
+                                                            i < 2 ? minit : sacc[i & 1], 0, 0, 0);
+    // order: AHEAD LDS reads, then (MFMA, LDS read) pairs, then the last MFMAs
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NQ - AHEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
 }
 

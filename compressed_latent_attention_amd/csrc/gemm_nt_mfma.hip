@@ -8,7 +8,8 @@
 // SIMD (each wave holds 16 accumulator blocks of v_mfma_f32_32x32x16_bf16, 256
 // registers, and issues 16 MFMAs per 16-wide k step), or eight waves of
 // 128 x 64, two per SIMD, when the grid holds two or more work-groups per CU;
-// operand fragments are double-buffered.  Tiles of A and B move from global memory to LDS
+// when 256-row tiles would leave CUs idle (and nothing splits K), 128 x 256
+// tiles of four waves of 64 x 128.  Operand fragments are double-buffered.  Tiles of A and B move from global memory to LDS
 // with buffer loads that write LDS directly (16 bytes per lane), two stages
 // deep; the next stage's 1 KB copies (16 per wave with four waves, 8 with
 // eight) are issued after every four MFMAs over the first half of the k step
@@ -34,9 +35,7 @@ namespace cca {
 namespace {
 
 constexpr int TM = 256, TN = 256, TK = 64;
-constexpr int A_BYTES = TM * TK * 2;
 constexpr int B_BYTES = TN * TK * 2;
-constexpr int STAGE = A_BYTES + B_BYTES;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -156,24 +155,42 @@ __device__ __forceinline__ bf16x8 t_frag(const char* p) {
 // NW = 8: waves of 128 x 64, two per SIMD, so one wave's MFMAs cover the
 // other's copy issue, fragment waits and barrier.
 // KT: both operands K-major (TN layout).  SB: B tiles may cross segments of
-// B (dma_part_seg).
-template <typename OutT, int NW, bool KT, bool SB = false>
+// B (dma_part_seg).  TMT: tile rows, 256 or (NT only) 128, which doubles the
+// tiles of a grid that would leave CUs idle (waves of 64 x 128 with NW = 4).
+template <typename OutT, int NW, bool KT, bool SB = false, int TMT = TM>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  static_assert(TMT == TM || (TMT == 128 && !KT), "128-row tiles: NT layout only");
   constexpr int WN = NW / 2;                 // waves along N
   constexpr int NJ = TN / WN / 32;           // 32-column blocks per wave: 4 or 2
-  constexpr int CB = 32 / NW;                // 1 KB copy blocks per wave per operand tile
-  // split-K: this work-group sums k in [kbeg, kbeg + klen)
+  constexpr int MI = TMT / 64;               // 32-row blocks per wave: 4 or 2
+  constexpr int CB = 32 / NW;                // 1 KB copy blocks per wave per B tile
+  constexpr int CBA = TMT / 8 / NW;          // and per A tile
+  constexpr int ABYTES = TMT * TK * 2, STG = ABYTES + B_BYTES;
   const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
-  const int klen = g.K / nsplit, kbeg = blockIdx.y * klen;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STG];
 
-  // tile of this work-group: XCD x (= blockIdx % 8) takes a consecutive run
+  // tile (and K range) of this work-group: XCD x (= dispatch index % 8) takes
+  // a consecutive run of tiles; with split K, a consecutive run of
+  // (K range, tile) pairs, K range outermost, so the work-groups of one XCD
+  // read the same k-rows of A and B at about the same time and each XCD's L2
+  // fetches its K range once rather than every tile's rows over all of K
   const int nt = tiles_m * tiles_n;
-  const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
-  const int t = xcd * (nt >> 3) + min(xcd, nt & 7) + loc;
+  int t, split = 0;
+  if (nsplit > 1) {
+    const int W = nt * nsplit, lin = blockIdx.x + gridDim.x * blockIdx.y;
+    const int xcd = lin & 7, loc = lin >> 3;
+    const int q = xcd * (W >> 3) + min(xcd, W & 7) + loc;
+    split = q / nt;
+    t = q - split * nt;
+  } else {
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    t = xcd * (nt >> 3) + min(xcd, nt & 7) + loc;
+  }
+  // split K: this work-group sums k in [kbeg, kbeg + klen)
+  const int klen = g.K / nsplit, kbeg = split * klen;
   const int tm = t / tiles_n, tn = t % tiles_n;
-  const int m0 = tm * TM, n0 = tn * TN;
+  const int m0 = tm * TMT, n0 = tn * TN;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -182,7 +199,7 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
 
   // A rows m0 .., B rows n0 .. (inside one segment of B, checked by the host)
   const bf16* abase = reinterpret_cast<const bf16*>(g.a) + (long)m0 * g.lda;
-  const int arows = min(g.M - m0, TM);
+  const int arows = min(g.M - m0, TMT);
   int s = 0;
   if (g.b_nseg > 1 && n0 >= g.b_start[1]) s = 1;
   if (g.b_nseg > 2 && n0 >= g.b_start[2]) s = 2;
@@ -196,20 +213,20 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   const bf16* bmat = reinterpret_cast<const bf16*>(g.b_ptr[0]);
   if constexpr (KT) {
     dma_tile_t<CB>(lds, amat, g.lda, m0, kvalid, kbeg, wave, lane);
-    dma_tile_t<CB>(lds + A_BYTES, bmat, g.ldb, n0, kvalid, kbeg, wave, lane);
+    dma_tile_t<CB>(lds + ABYTES, bmat, g.ldb, n0, kvalid, kbeg, wave, lane);
   } else {
-    dma_tile<CB>(lds, abase, g.lda, arows, g.K, kbeg, wave, lane);
+    dma_tile<CBA>(lds, abase, g.lda, arows, g.K, kbeg, wave, lane);
     if constexpr (SB) {
 #pragma unroll
-      for (int i = 0; i < CB; ++i) dma_part_seg<CB>(lds + A_BYTES, g, n0, kbeg, wave, lane, i);
+      for (int i = 0; i < CB; ++i) dma_part_seg<CB>(lds + ABYTES, g, n0, kbeg, wave, lane, i);
     } else {
-      dma_tile<CB>(lds + A_BYTES, bbase, g.ldb, brows, g.K, kbeg, wave, lane);
+      dma_tile<CB>(lds + ABYTES, bbase, g.ldb, brows, g.K, kbeg, wave, lane);
     }
   }
 
-  f32x16 acc[4][NJ];
+  f32x16 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -224,10 +241,10 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   for (int u = 0; u < 4; ++u) {
     if constexpr (KT) {
       aoff[u] = t_frag_off(lane, wm * 128 + u * 32);
-      boff[u] = A_BYTES + t_frag_off(lane, wn * (NJ * 32) + (u % NJ) * 32);
+      boff[u] = ABYTES + t_frag_off(lane, wn * (NJ * 32) + (u % NJ) * 32);
     } else {
-      aoff[u] = sw(wm * 128 + l32, 2 * u + hi);
-      boff[u] = A_BYTES + sw(wn * (NJ * 32) + l32, 2 * u + hi);
+      aoff[u] = sw(wm * (TMT / 2) + l32, 2 * u + hi);
+      boff[u] = ABYTES + sw(wn * (NJ * 32) + l32, 2 * u + hi);
     }
   }
   auto frag_a = [&](const char* st, int ks, int i) -> bf16x8 {
@@ -242,15 +259,15 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   __syncthreads();
 
   for (int kt = 0; kt < nk; ++kt) {
-    const char* st = lds + (kt & 1) * STAGE;
+    const char* st = lds + (kt & 1) * STG;
     // next stage's copy, one 1 KB block after every four MFMAs (the last step
     // copies its own k range again into the idle stage, so the loop body has
     // no branch)
-    char* nx = lds + ((kt + 1) & 1) * STAGE;
+    char* nx = lds + ((kt + 1) & 1) * STG;
     const int knx = kbeg + min(kt + 1, nk - 1) * TK;
-    bf16x8 fa[2][4], fb[2][NJ];
+    bf16x8 fa[2][MI], fb[2][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = frag_a(st, 0, i);
+    for (int i = 0; i < MI; ++i) fa[0][i] = frag_a(st, 0, i);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) fb[0][j] = frag_b(st, 0, j);
 #pragma unroll
@@ -258,30 +275,34 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
       const int cur = ks & 1;
       if (ks + 1 < 4) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[cur ^ 1][i] = frag_a(st, ks + 1, i);
+        for (int i = 0; i < MI; ++i) fa[cur ^ 1][i] = frag_a(st, ks + 1, i);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) fb[cur ^ 1][j] = frag_b(st, ks + 1, j);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j],
                                                               0, 0, 0);
-        // issue points 0..15; the 2 CB copies go out over the first 8 (CB / 4 each)
-        const int pt = ks * 4 + i;
+        // issue points 0 .. 4 MI - 1; the CBA + CB copies go out over the
+        // first half, PER at each
+        constexpr int HALF = 2 * MI, PER = (CBA + CB + HALF - 1) / HALF;
+        const int pt = ks * MI + i;
         __builtin_amdgcn_sched_barrier(0);
-        if (pt < 8) {
+        if (pt < HALF) {
 #pragma unroll
-          for (int u = 0; u < CB / 4; ++u) {
-            const int blk = pt * (CB / 4) + u;   // A blocks 0 .. CB-1, then B
+          for (int u = 0; u < PER; ++u) {
+            const int blk = pt * PER + u;        // A blocks 0 .. CBA-1, then B
             if constexpr (KT) {
-              if (blk < CB) dma_part_t<CB>(nx, amat, g.lda, m0, kvalid, knx, wave, lane, blk);
-              else dma_part_t<CB>(nx + A_BYTES, bmat, g.ldb, n0, kvalid, knx, wave, lane, blk - CB);
+              if (blk < CBA) dma_part_t<CB>(nx, amat, g.lda, m0, kvalid, knx, wave, lane, blk);
+              else dma_part_t<CB>(nx + ABYTES, bmat, g.ldb, n0, kvalid, knx, wave, lane, blk - CBA);
             } else {
-              if (blk < CB) dma_part<CB>(nx, abase, g.lda, arows, g.K, knx, wave, lane, blk);
-              else if constexpr (SB) dma_part_seg<CB>(nx + A_BYTES, g, n0, knx, wave, lane, blk - CB);
-              else dma_part<CB>(nx + A_BYTES, bbase, g.ldb, brows, g.K, knx, wave, lane, blk - CB);
+              if (blk < CBA) dma_part<CBA>(nx, abase, g.lda, arows, g.K, knx, wave, lane, blk);
+              else if (blk < CBA + CB) {
+                if constexpr (SB) dma_part_seg<CB>(nx + ABYTES, g, n0, knx, wave, lane, blk - CBA);
+                else dma_part<CB>(nx + ABYTES, bbase, g.ldb, brows, g.K, knx, wave, lane, blk - CBA);
+              }
             }
           }
         }
@@ -296,17 +317,17 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   // One C segment (checked by the host): a uniform tile base plus 32-bit lane
   // offsets.
   char* cbase = reinterpret_cast<char*>(g.c_ptr[0]) +
-                ((long)blockIdx.y * g.c_split_stride + (long)m0 * g.ldc + n0) * sizeof(OutT);
+                ((long)split * g.c_split_stride + (long)m0 * g.ldc + n0) * sizeof(OutT);
   const int ldc = (int)g.ldc;
   const int mrem = g.M - m0, nrem = g.N - n0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int nl = wn * (NJ * 32) + j * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int ml = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const int ml = wm * (TMT / 2) + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
         if (ml < mrem && nl < nrem)
           store_out(reinterpret_cast<OutT*>(cbase + (ml * ldc + nl) * (int)sizeof(OutT)),
                     acc[i][j][r]);
@@ -345,6 +366,20 @@ bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError
   const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
   if (nsplit > 1 && (!out_f32 || (g.K / nsplit) % TK != 0 || g.K % nsplit != 0)) return false;
   if ((long)tiles_m * tiles_n * nsplit < 64) return false;
+  // fewer 256-row tiles than CUs (a narrow output such as the backward's
+  // dY W_o with N = 512): 128-row tiles, twice as many work-groups
+  if (!kt && !sb && nsplit == 1 && tiles_m * tiles_n < 256) {
+    const int tm128 = (g.M + 127) / 128;
+    dim3 grid128(tm128 * tiles_n);
+    if (out_f32)
+      hipLaunchKernelGGL((gemm_nt_256_kernel<float, 4, false, false, 128>), grid128, dim3(256), 0, s,
+                         g, tm128, tiles_n);
+    else
+      hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 4, false, false, 128>), grid128, dim3(256), 0, s,
+                         g, tm128, tiles_n);
+    *err = hipGetLastError();
+    return true;
+  }
   dim3 grid(tiles_m * tiles_n, nsplit);
   // two or more work-groups per CU: 8 waves (they run one after another, and
   // the second wave per SIMD hides stalls); fewer: 4 waves of 128 x 128, whose
