@@ -268,6 +268,67 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
   const float2* rope_t0 = rope ? a.rope + (long)(pos0 + t0) * (D / 2) : nullptr;
   __syncthreads();
 
+  // value shift from the v~ tile: V'[t, c] = v~[t - 1, c] for the last s_v
+  // channels (tile row tr + HALO - 1; row HALO - 1 is token t0 - 1, zero
+  // before token 0), else v~[t, c]
+  const int first_shift = (dm.flags & kVShift) ? D - dm.sv : D;
+  auto vrow = [&](int tr, int c) { return tr + HALO - (c >= first_shift ? 1 : 0); };
+  bf16* vo = a.v_out ? reinterpret_cast<bf16*>(a.v_out) + ((long)(b * dm.Hkv + g) * S) * D
+                     : nullptr;
+  bf16* vo2 = a.v_out2 ? reinterpret_cast<bf16*>(a.v_out2) +
+                             ((long)(b * dm.Hkv + g) * a.cap2 + pos0) * D
+                       : nullptr;
+  if (vo || vo2) {
+    // thread = (token, 8 channels): 16-byte stores
+    for (int e = threadIdx.x; e < TW * (D / 8); e += 256) {
+      const int tr = e / (D / 8), c8 = (e % (D / 8)) * 8;
+      const int t = t0 + tr;
+      if (t >= S) break;
+      bf16x8 v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v[i] = *reinterpret_cast<const bf16*>(tv + vrow(tr, c8 + i) * ROWB + (c8 + i) * 2);
+      if (vo) *reinterpret_cast<bf16x8*>(vo + (long)t * D + c8) = v;
+      if (vo2) *reinterpret_cast<bf16x8*>(vo2 + (long)t * D + c8) = v;
+    }
+  }
+  if (!VARLEN && a.vt_out) {
+    // V'^T feeds only the attention's P V product, which runs in fp16 so that P
+    // keeps 11 significant bits.  It holds the stored bf16 V' values, converted
+    // exactly (within fp16's range), so the forward's O and the backward (which
+    // reads the bf16 V') see the same V'.
+    _Float16* vt = reinterpret_cast<_Float16*>(a.vt_out) + (long)(b * dm.Hkv + g) * D * a.s_pad;
+    for (int e = threadIdx.x; e < D * (TW / 8); e += 256) {
+      const int m = e % (TW / 8), c = e / (TW / 8);   // 8-token groups of a channel row together
+      const int t = t0 + 8 * m;
+      if (t >= a.s_pad) continue;
+      f16x8 pk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // tokens at or past S are zero: the padding of V'^T up to s_pad
+        const float v = t + i < S ? tile_val<D>(tv, vrow(8 * m + i, c), c) : 0.0f;
+        pk[i] = (_Float16)v;
+      }
+      *reinterpret_cast<f16x8*>(vt + (long)c * a.s_pad + t) = pk;
+    }
+  }
+  // every read of the v~ tile is done: it now stages each output tile (Q'' of
+  // a head, then K''), so that the global stores are whole 16-byte row pieces
+  __syncthreads();
+  char* const so = tv;
+  // the staged tile's rows inside the sequence to global rows dst + tr * D
+  auto flush = [&](bf16* dst, bf16* dst2) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < TW * (D / 8); e += 256) {
+      const int tr = e / (D / 8), c8 = (e % (D / 8)) * 8;
+      if (t0 + tr >= S) break;
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(so + tr * ROWB + c8 * 2);
+      if (dst) *reinterpret_cast<bf16x8*>(dst + (long)tr * D + c8) = v;
+      if (dst2) *reinterpret_cast<bf16x8*>(dst2 + (long)tr * D + c8) = v;
+    }
+    __syncthreads();
+  };
+
   Acc2 kacc, qacc, mpost, mpre;
   zero(kacc);
   conv_head<D>(kacc, tk, reinterpret_cast<const bf16*>(a.conv_k) + (long)g * dm.kk * D * D, dm.kk,
@@ -307,7 +368,6 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
       continue;
     }
     const long qrow = VARLEN ? q_row0 + h * q_hstride + t0 : (long)(b * dm.Hq + h) * S + t0;
-    bf16* qo = reinterpret_cast<bf16*>(a.q_out) + qrow * D + ch;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       __builtin_amdgcn_sched_barrier(0);       // one token block at a time (registers)
@@ -327,18 +387,19 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
         mpost[mb][r] += qh;
         if (!QRES) mpre[mb][r] += qp;
         const float y = rotate(qh + A * (qp + kp) + Bc * (qh + kh), csr[r], lo_lane);
-        if (t0 + tr < S) qo[tr * D] = (bf16)y;
+        *reinterpret_cast<bf16*>(so + tr * ROWB + ch * 2) = (bf16)y;
       }
     }
+    flush(reinterpret_cast<bf16*>(a.q_out) + qrow * D, nullptr);
   }
 
   // k' = k^ + a/2 (mean_g q~ + k~) + b/2 (mean_g q^ + k^)
   __builtin_amdgcn_sched_barrier(0);
   const float invG = 1.0f / (float)G;
   bf16* ko = VARLEN ? nullptr
-                    : reinterpret_cast<bf16*>(a.k_out) + ((long)(b * dm.Hkv + g) * S + t0) * D + ch;
+                    : reinterpret_cast<bf16*>(a.k_out) + ((long)(b * dm.Hkv + g) * S + t0) * D;
   bf16* ko2 = a.k_out2 ? reinterpret_cast<bf16*>(a.k_out2) +
-                             ((long)(b * dm.Hkv + g) * a.cap2 + pos0 + t0) * D + ch
+                             ((long)(b * dm.Hkv + g) * a.cap2 + pos0 + t0) * D
                        : nullptr;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
@@ -360,57 +421,11 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
       }
       const float y = rotate(kh + A * (qpre * invG + kp) + Bc * (mpost[mb][r] * invG + kh),
                              csr[r], lo_lane);
-      if (t0 + tr < S) {
-        if (!VARLEN) ko[tr * D] = (bf16)y;
-        if (ko2) ko2[tr * D] = (bf16)y;
-      }
+      *reinterpret_cast<bf16*>(so + tr * ROWB + ch * 2) = (bf16)y;
     }
   }
+  flush(ko, ko2);
 
-  // value shift from the v~ tile: V'[t, c] = v~[t - 1, c] for the last s_v
-  // channels (tile row tr + HALO - 1; row HALO - 1 is token t0 - 1, zero
-  // before token 0), else v~[t, c]
-  const int first_shift = (dm.flags & kVShift) ? D - dm.sv : D;
-  auto vrow = [&](int tr, int c) { return tr + HALO - (c >= first_shift ? 1 : 0); };
-  bf16* vo = a.v_out ? reinterpret_cast<bf16*>(a.v_out) + ((long)(b * dm.Hkv + g) * S) * D
-                     : nullptr;
-  bf16* vo2 = a.v_out2 ? reinterpret_cast<bf16*>(a.v_out2) +
-                             ((long)(b * dm.Hkv + g) * a.cap2 + pos0) * D
-                       : nullptr;
-  if (vo || vo2) {
-    // thread = (token, 8 channels): 16-byte stores
-    for (int e = threadIdx.x; e < TW * (D / 8); e += 256) {
-      const int tr = e / (D / 8), c8 = (e % (D / 8)) * 8;
-      const int t = t0 + tr;
-      if (t >= S) break;
-      bf16x8 v;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        v[i] = *reinterpret_cast<const bf16*>(tv + vrow(tr, c8 + i) * ROWB + (c8 + i) * 2);
-      if (vo) *reinterpret_cast<bf16x8*>(vo + (long)t * D + c8) = v;
-      if (vo2) *reinterpret_cast<bf16x8*>(vo2 + (long)t * D + c8) = v;
-    }
-  }
-  if (!VARLEN && a.vt_out) {
-    // V'^T feeds only the attention's P V product, which runs in fp16 so that P
-    // keeps 11 significant bits.  It holds the stored bf16 V' values, converted
-    // exactly (within fp16's range), so the forward's O and the backward (which
-    // reads the bf16 V') see the same V'.
-    _Float16* vt = reinterpret_cast<_Float16*>(a.vt_out) + (long)(b * dm.Hkv + g) * D * a.s_pad;
-    for (int e = threadIdx.x; e < D * (TW / 8); e += 256) {
-      const int c = e % D, m = e / D;
-      const int t = t0 + 8 * m;
-      if (t >= a.s_pad) continue;
-      f16x8 pk;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // tokens at or past S are zero: the padding of V'^T up to s_pad
-        const float v = t + i < S ? tile_val<D>(tv, vrow(8 * m + i, c), c) : 0.0f;
-        pk[i] = (_Float16)v;
-      }
-      *reinterpret_cast<f16x8*>(vt + (long)c * a.s_pad + t) = pk;
-    }
-  }
 }
 
 }  // namespace
