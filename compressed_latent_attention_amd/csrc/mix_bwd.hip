@@ -501,16 +501,23 @@ __global__ __launch_bounds__(256) void mix_bwd_conv_input_mfma(MixBwdArgs a) {
     const bf16* arow = gs + (tw + l32 + j) * GLD + hi * 8;
     const bf16* b0p = reinterpret_cast<const bf16*>(a.tapT) + ((long)(m0 + j) * TD + nb0 * 32 + l32) * TD + hi * 8;
     const bf16* b1p = b0p + 32 * TD;
+    // the lag's tap fragments (from L2) all requested before its MFMAs, so the
+    // wave waits for L2 once per lag rather than once per k-step
+    bf16x8 b0[TD / 16], b1[TD / 16];
+#pragma unroll
+    for (int ks = 0; ks < TD / 16; ++ks) {
+      b0[ks] = *reinterpret_cast<const bf16x8*>(b0p + ks * 16);
+      b1[ks] = *reinterpret_cast<const bf16x8*>(b1p + ks * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < TD / 16; ++ks) {
       const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(arow + ks * 16);
       const bf16x8 alo = *reinterpret_cast<const bf16x8*>(arow + GPLANE + ks * 16);
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(b0p + ks * 16);
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(b1p + ks * 16);
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b0, acc[0], 0, 0, 0);
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b0, acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b1, acc[1], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b1, acc[1], 0, 0, 0);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b0[ks], acc[0], 0, 0, 0);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b0[ks], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b1[ks], acc[1], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b1[ks], acc[1], 0, 0, 0);
     }
   }
   // D: lane holds column c' = nb 32 + l32, register r token tw + 8 (r / 4) + 4 hi + r % 4
