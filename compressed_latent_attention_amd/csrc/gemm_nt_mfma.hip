@@ -7,9 +7,10 @@
 // Work-group tile 256 x 256 x 64, either four waves of 128 x 128, one wave per
 // SIMD (each wave holds 16 accumulator blocks of v_mfma_f32_32x32x16_bf16, 256
 // registers, and issues 16 MFMAs per 16-wide k step), or eight waves of
-// 128 x 64, two per SIMD, when the grid holds two or more work-groups per CU;
+// 128 x 64, two per SIMD, when the grid holds two or more work-groups per CU
+// and always in the TN layout below;
 // when 256-row tiles would leave CUs idle (and nothing splits K), 128 x 256
-// tiles of four waves of 64 x 128.  Operand fragments are double-buffered.  Tiles of A and B move from global memory to LDS
+// tiles of eight waves of 64 x 64.  Operand fragments are double-buffered.  Tiles of A and B move from global memory to LDS
 // with buffer loads that write LDS directly (16 bytes per lane), two stages
 // deep; the next stage's 1 KB copies (16 per wave with four waves, 8 with
 // eight) are issued after every four MFMAs over the first half of the k step
@@ -156,7 +157,7 @@ __device__ __forceinline__ bf16x8 t_frag(const char* p) {
 // other's copy issue, fragment waits and barrier.
 // KT: both operands K-major (TN layout).  SB: B tiles may cross segments of
 // B (dma_part_seg).  TMT: tile rows, 256 or (NT only) 128, which doubles the
-// tiles of a grid that would leave CUs idle (waves of 64 x 128 with NW = 4).
+// tiles of a grid that would leave CUs idle (waves of 64 x 64 with NW = 8).
 template <typename OutT, int NW, bool KT, bool SB = false, int TMT = TM>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
@@ -372,10 +373,10 @@ bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError
     const int tm128 = (g.M + 127) / 128;
     dim3 grid128(tm128 * tiles_n);
     if (out_f32)
-      hipLaunchKernelGGL((gemm_nt_256_kernel<float, 4, false, false, 128>), grid128, dim3(256), 0, s,
+      hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, false, false, 128>), grid128, dim3(512), 0, s,
                          g, tm128, tiles_n);
     else
-      hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 4, false, false, 128>), grid128, dim3(256), 0, s,
+      hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 8, false, false, 128>), grid128, dim3(512), 0, s,
                          g, tm128, tiles_n);
     *err = hipGetLastError();
     return true;
@@ -386,8 +387,9 @@ bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError
   // larger wave tiles read less LDS per MFMA
   const bool w8 = (long)tiles_m * tiles_n * nsplit >= 512;
   if (kt) {
-    if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, true>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
-    else hipLaunchKernelGGL((gemm_nt_256_kernel<float, 4, true>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
+    // eight waves even in one round: the transposing fragment reads (two per
+    // fragment) leave a lone wave per SIMD waiting on LDS
+    hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, true>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
   } else if (sb) {
     if (out_f32) {
       if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, false, true>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
