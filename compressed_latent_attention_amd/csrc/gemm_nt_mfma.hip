@@ -4,21 +4,19 @@
 // q~ | k~ | v~ (CCA-es §2.A "Principio Fundamental"; CCA-fr §2 "Projection
 // vers l'Espace Latent") and the output projection O W_o^T.
 //
-// Work-group tile 256 x 256 x 64, either four waves of 128 x 128, one wave per
-// SIMD (each wave holds 16 accumulator blocks of v_mfma_f32_32x32x16_bf16, 256
-// registers, and issues 16 MFMAs per 16-wide k step), or eight waves of
-// 128 x 64, two per SIMD, when the grid holds two or more work-groups per CU
-// and always in the TN layout below;
-// when 256-row tiles would leave CUs idle (and nothing splits K), 128 x 256
-// tiles of eight waves of 64 x 64.  Operand fragments are double-buffered.  Tiles of A and B move from global memory to LDS
-// with buffer loads that write LDS directly (16 bytes per lane), two stages
-// deep; the next stage's 1 KB copies (16 per wave with four waves, 8 with
-// eight) are issued after every four MFMAs over the first half of the k step
-// rather than in a burst:
-// a copy's issue waits until the address unit takes it, and with one wave per
-// SIMD a burst would leave the MFMA unit idle for that long, while copies
-// spread over the whole step leave the last ones' memory latency exposed at
-// the end-of-step wait.  LDS rows (64 k = 128 B) are unpadded with their
+// Work-group tile 256 x 256 x 64 as eight waves of 128 x 64, two per SIMD
+// (each wave holds 8 accumulator blocks of v_mfma_f32_32x32x16_bf16 and issues
+// 8 MFMAs per 16-wide k step; the template also has a four-wave form of
+// 128 x 128, one wave per SIMD, which measured slower); when 256-row tiles
+// would leave CUs idle (and nothing splits K), 128 x 256 tiles of eight waves
+// of 64 x 64.  Operand fragments are double-buffered.  Tiles of A and B move
+// from global memory to LDS with buffer loads that write LDS directly (16
+// bytes per lane), two stages deep; the next stage's 1 KB copies (8 per wave)
+// are issued at MFMA issue points over the first half of the k step rather
+// than in a burst: a copy's issue waits until the address unit takes it, and a
+// burst would leave the MFMA unit idle for that long, while copies spread over
+// the whole step leave the last ones' memory latency exposed at the
+// end-of-step wait.  LDS rows (64 k = 128 B) are unpadded with their
 // 16-byte chunks XOR-swizzled by row, so that the fragment reads are free of
 // bank conflicts.
 // Rows past M or past the end of B's segment read as zero (buffer range
@@ -382,29 +380,20 @@ bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError
     return true;
   }
   dim3 grid(tiles_m * tiles_n, nsplit);
-  // two or more work-groups per CU: 8 waves (they run one after another, and
-  // the second wave per SIMD hides stalls); fewer: 4 waves of 128 x 128, whose
-  // larger wave tiles read less LDS per MFMA
-  const bool w8 = (long)tiles_m * tiles_n * nsplit >= 512;
-  if (kt) {
-    // eight waves even in one round: the transposing fragment reads (two per
-    // fragment) leave a lone wave per SIMD waiting on LDS
+  // eight waves of 128 x 64, two per SIMD, also when the grid is one round:
+  // the second wave of a SIMD covers the other's fragment waits, copy issue
+  // and barrier (measured faster than four waves of 128 x 128 on every layout
+  // here, although those read less LDS per MFMA)
+  if (kt)
     hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, true>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
-  } else if (sb) {
-    if (out_f32) {
-      if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, false, true>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
-      else hipLaunchKernelGGL((gemm_nt_256_kernel<float, 4, false, true>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
-    } else {
-      if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 8, false, true>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
-      else hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 4, false, true>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
-    }
-  } else if (out_f32) {
-    if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, false>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
-    else hipLaunchKernelGGL((gemm_nt_256_kernel<float, 4, false>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
-  } else {
-    if (w8) hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 8, false>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
-    else hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 4, false>), grid, dim3(256), 0, s, g, tiles_m, tiles_n);
-  }
+  else if (sb && out_f32)
+    hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, false, true>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+  else if (sb)
+    hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 8, false, true>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+  else if (out_f32)
+    hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, false>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 8, false>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
   *err = hipGetLastError();
   return true;
 }
