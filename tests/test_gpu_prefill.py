@@ -181,10 +181,20 @@ def check_sampled_rows(w: Workload, n_random=43):
 
 
 def test_prefill_ragged_large_sampled_rows():
-    """S = 5000 at E = 2048: the 256 x 256 projection GEMMs with a ragged last
-    row tile (5000 = 19 * 256 + 136) and the attention's ragged last block."""
+    """S = 5000 at E = 2048: the projection GEMMs on 128-row tiles (80 and 160
+    tiles of 256 rows would leave CUs idle) with a ragged last row tile
+    (5000 = 39 * 128 + 8) and the attention's ragged last block."""
     check_sampled_rows(Workload("ccgqa_ragged_5000", B=1, S=5000, E=2048, C=4, Hq=4, Hkv=2,
                                 seed=43), n_random=60)
+
+
+def test_prefill_ccgqa16_large_sampled_rows():
+    """The 16x variant (one KV head) at S = 6000, E = 2048: the concatenated
+    q | k | v weights of the down-projection have a segment start (column 640)
+    inside a 256-column tile, so the 256 x 256 GEMM (24 x 3 tiles) resolves the
+    segment per 8-row block; ragged last row tile and query block."""
+    check_sampled_rows(Workload("ccgqa16_ragged_6000", B=1, S=6000, E=2048, C=4, Hq=4, Hkv=1,
+                                seed=48), n_random=40)
 
 
 def test_causality_bit_identical_on_gpu():
