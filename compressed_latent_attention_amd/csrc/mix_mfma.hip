@@ -2,23 +2,24 @@
 // k~ (CCA-es §2.B.1 "Mezcla Convolucional"), QK-mean (§2.B.2), value shift
 // (§2.B.3) and RoPE (§3 item 2) in one pass per (64 tokens, KV group).
 //
-// The convolution of one head is a GEMM: out[t, c] = sum_{j, c'} u[t - j, c'] *
-// A_j[c, c'] with M = tokens, N = channels, K = k * d.  The bf16 latent tiles
-// the work-group needs (k~, v~ and up to two q~ heads, 64 tokens plus a 4-row
-// halo before them, enough for k <= 4 taps and the one-token value shift) are
-// read with 16-byte buffer loads, all issued in one round at the start, so a
-// work-group waits for memory once, and stored to LDS in rows padded to 272
-// bytes: the MFMA operand reads (32 consecutive token rows, one 16-byte chunk
-// each) are free of bank conflicts and an epilogue read is a base register
-// plus a constant offset.  Operand A is read from the tile, operand B is the
-// bf16 tap row A_j[c, 8 channels] read from L2.  With lane = output channel
-// and registers = tokens, everything QK-mean needs (the same token and channel
-// of the group's query heads and its K head) sits in one lane.
+// The convolution of one head is a GEMM, taken transposed: out[c, t] =
+// sum_{j, c'} A_j[c, c'] u[t - j, c'] with M = channels, N = tokens, K = k * d.
+// The bf16 latent tiles the work-group needs (k~, v~ and up to two q~ heads, 64
+// tokens plus a 4-row halo before them, enough for k <= 4 taps and the
+// one-token value shift) are read with 16-byte buffer loads, all issued in one
+// round at the start, so a work-group waits for memory once, and stored to LDS
+// in rows padded to 272 bytes: the MFMA operand reads (32 consecutive token
+// rows, one 16-byte chunk each) are free of bank conflicts.  Operand A is the
+// bf16 tap row A_j[c, 8 channels] read from L2, operand B the tile.  With lane
+// = token and each 4 registers = 4 consecutive channels, everything QK-mean
+// needs (the same token and channels of the group's query heads and its K head)
+// sits in one lane, the epilogue reads the pre-convolution values and the RoPE
+// cos / sin of 4 channels at once, and writes 4 outputs at once.
 //
 // Wave w of the 4 owns a quarter of the output channels, all 64 tokens: MFMA
-// column n < 16 is channel 16 w + n and column n >= 16 its RoPE partner
-// 64 + 16 w + n - 16, so a rotation pair sits in lanes l and l ^ 16 (one lane
-// swap), every tap fragment feeds the MFMAs of both 32-token blocks, and the
+// row m < 16 is channel 16 w + m and row m >= 16 its RoPE partner
+// 64 + 16 w + m - 16, so a rotation pair sits in registers r and r + 8 of one
+// lane; every tap fragment feeds the MFMAs of both 32-token blocks, and the
 // four waves together read each tap row of the group once.
 // Work-groups are numbered so the KV groups of one token tile run on the same
 // XCD (ids 8 apart): the second reads the tile's RoPE rows from that XCD's L2.
@@ -105,8 +106,9 @@ __device__ __forceinline__ void zero(Acc2& a) {
 }
 
 // acc[mb] += conv of the head whose tile is at `tile` for the wave's token
-// block mb (A rows = tokens tb0 + 32 mb + l32 at lag j, tile row tb0 + 32 mb +
-// l32 - j + HALO), B = taps[j][ch][c_in] for this lane's output channel ch;
+// block mb, transposed (rows = output channels, columns = tokens): A =
+// taps[j][ch][c_in] for output channel ch of MFMA row l32, B = the tile rows of
+// tokens tb0 + 32 mb + l32 at lag j (tile row tb0 + 32 mb + l32 - j + HALO);
 // the D / 16 B fragments of a lag are loaded before its MFMAs and each serves
 // both token blocks.
 template <int D>
@@ -124,39 +126,44 @@ __device__ __forceinline__ void conv_head(Acc2& acc, const char* tile, const bf1
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int row = tb0 + 32 * mb + l32 - j + HALO;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(tile + row * ROWB + (2 * ks + hi) * 16);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[ks], acc[mb], 0, 0, 0);
+        const bf16x8 u = *reinterpret_cast<const bf16x8*>(tile + row * ROWB + (2 * ks + hi) * 16);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[ks], u, acc[mb], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);     // keep the A reads next to their MFMAs
     }
   }
 }
 
-// cos / sin of RoPE pair p for the 16 tokens of token block mb a lane's
-// accumulator registers hold (register r: token tb0 + 32 mb + 8 (r / 4) + 4 hi
-// + r % 4 of the tile), all 16 loads in flight together; (1, 0) without RoPE.
-// Tokens past the sequence (nrem = tokens of the tile inside it) read the last
-// row: no branch, and their results are never stored.
+// Channels c0 .. c0 + 3 of tile row r as floats (one 8-byte LDS read).
 template <int D>
-__device__ __forceinline__ void load_rope(float2 (&cs)[16], const float2* rope_t0, int tb0, int mb,
-                                          int hi, int p, int nrem) {
+__device__ __forceinline__ f32x4 tile_vec4(const char* tile, int r, int c0) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(tile + r * MGeom<D>::ROWB + c0 * 2);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+// cos / sin of RoPE pairs p0 .. p0 + 3 of tile token tr (the last token inside
+// the sequence past its end, whose results are never stored): two 16-byte
+// loads; (1, 0) without RoPE.
+template <int D>
+__device__ __forceinline__ void load_rope4(f32x4& cs, f32x4& sn, const float2* rope_t0, int tr,
+                                           int p0, int nrem) {
   if (rope_t0) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tr = min(tb0 + 32 * mb + 8 * (r >> 2) + 4 * hi + (r & 3), nrem - 1);
-      cs[r] = rope_t0[tr * (D / 2) + p];
-    }
+    const float* rp = reinterpret_cast<const float*>(rope_t0 + min(tr, nrem - 1) * (D / 2) + p0);
+    const f32x4 r0 = *reinterpret_cast<const f32x4*>(rp);
+    const f32x4 r1 = *reinterpret_cast<const f32x4*>(rp + 4);
+    cs = f32x4{r0[0], r0[2], r1[0], r1[2]};
+    sn = f32x4{r0[1], r0[3], r1[1], r1[3]};
   } else {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) cs[r] = make_float2(1.f, 0.f);
+    cs = f32x4{1.f, 1.f, 1.f, 1.f};
+    sn = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
-// RoPE of one value given its partner (lane ^ 16): lo lanes hold channel p,
-// hi lanes channel p + D / 2.
-__device__ __forceinline__ float rotate(float x, float2 cs, bool lo_lane) {
-  const float xp = __shfl_xor(x, 16);
-  return lo_lane ? x * cs.x - xp * cs.y : x * cs.x + xp * cs.y;
+// 4 values to channels c0 .. c0 + 3 of staging row r (one 8-byte LDS write).
+template <int D>
+__device__ __forceinline__ void stage4(char* so, int r, int c0, const f32x4& v) {
+  const bf16x4 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  *reinterpret_cast<bf16x4*>(so + r * MGeom<D>::ROWB + c0 * 2) = b;
 }
 
 // Rows 0 .. HALO - 1 of the first tile of a chunk (tokens -4 .. -1) from the
@@ -194,6 +201,9 @@ template <int D, int GC, bool VARLEN, bool NOQ, typename Map>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VARLEN || GC == 0 ? 1 : 2,
                                                                      VARLEN || GC == 0 ? 1 : 2)))
 void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
+  // every product rounded on its own (no contraction into FMAs): the
+  // instances with and without Q'' then compute K'' bit for bit alike
+#pragma clang fp contract(off)
   using MG = MGeom<D>;
   constexpr int TW = MG::TW, TBYTES = MG::TBYTES, ROWB = MG::ROWB;
   static_assert(!VARLEN || D == 128, "variable-length chunks use 64-token tiles");
@@ -237,17 +247,19 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
   if (t0 >= S) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const bool lo_lane = l32 < 16;
   const int cw = MG::NTG == 1 ? wave : wave % MG::NCW;       // channel group of this wave
   const int tb0 = MG::NTG == 1 ? 0 : 64 * (wave / MG::NCW);  // first tile token of its two blocks
-  const int pair = 16 * cw + (l32 & 15);     // RoPE pair of this lane's channel
-  const int ch = lo_lane ? pair : pair + D / 2;  // this lane's output channel
+  // output channel of MFMA row l32 (the tap row this lane loads): rows 0..15
+  // are channels 16 cw + 0..15, rows 16..31 their RoPE partners D / 2 further
+  const int ch = l32 < 16 ? 16 * cw + l32 : D / 2 + 16 * cw + l32 - 16;
   const bf16* qkv_b = reinterpret_cast<const bf16*>(a.qkv) + lat0 * dm.nqkv;
   const float A = (dm.flags & kQkPre) ? 0.5f : 0.0f;
   const float Bc = (dm.flags & kQkPost) ? 0.5f : 0.0f;
   const bool rope = (dm.flags & kRope) != 0;
-  // register r of token block mb holds token tb0 + 32 mb + 8*(r/4) + 4*hi + r%4 (of the tile)
-  auto trel = [&](int mb, int r) { return tb0 + 32 * mb + 8 * (r >> 2) + 4 * hi + (r & 3); };
+  // accumulator of token block mb: the lane holds tile token tb0 + 32 mb + l32;
+  // registers 4 g .. 4 g + 3 (g = 0, 1) channels 16 cw + 8 g + 4 hi + 0..3 and
+  // registers 8 + 4 g .. their RoPE partners D / 2 further (MFMA row 8 (r / 4) +
+  // 4 hi + r % 4 is channel ch of lane row l32 = that row)
 
   // every tile the work-group needs, in one round
   {
@@ -359,35 +371,67 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
                  dm.kq, ch, lane, tb0);
     if constexpr (NOQ) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb) {
+        const int tr = tb0 + 32 * mb + l32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          mpost[mb][r] += qacc[mb][r];
-          if (!QRES) mpre[mb][r] += tile_val<D>(tqi, trel(mb, r) + HALO, ch);
+        for (int g4 = 0; g4 < 2; ++g4) {
+          const int c0 = 16 * cw + 8 * g4 + 4 * hi;
+          f32x4 qpl = {0.f, 0.f, 0.f, 0.f}, qph = {0.f, 0.f, 0.f, 0.f};
+          if (!QRES) {
+            qpl = tile_vec4<D>(tqi, tr + HALO, c0);
+            qph = tile_vec4<D>(tqi, tr + HALO, c0 + D / 2);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int rl = 4 * g4 + e, rh = rl + 8;
+            mpost[mb][rl] += qacc[mb][rl];
+            mpost[mb][rh] += qacc[mb][rh];
+            if (!QRES) {
+              mpre[mb][rl] += qpl[e];
+              mpre[mb][rh] += qph[e];
+            }
+          }
         }
+      }
       continue;
     }
     const long qrow = VARLEN ? q_row0 + h * q_hstride + t0 : (long)(b * dm.Hq + h) * S + t0;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       __builtin_amdgcn_sched_barrier(0);       // one token block at a time (registers)
+      const int tr = tb0 + 32 * mb + l32;
       // the same rows for every head: an opaque copy of the base keeps the
       // compiler from hoisting these loads out of the head loop (they would
-      // hold 64 registers through every convolution)
+      // hold their registers through every convolution)
       const float2* rp = rope_t0;
       asm volatile("" : "+s"(rp));
-      float2 csr[16];
-      load_rope<D>(csr, rp, tb0, mb, hi, pair, S - t0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tr = trel(mb, r);
-        const float qh = qacc[mb][r], kh = kacc[mb][r];
-        const float qp = tile_val<D>(tqi, tr + HALO, ch);
-        const float kp = tile_val<D>(tk, tr + HALO, ch);
-        mpost[mb][r] += qh;
-        if (!QRES) mpre[mb][r] += qp;
-        const float y = rotate(qh + A * (qp + kp) + Bc * (qh + kh), csr[r], lo_lane);
-        *reinterpret_cast<bf16*>(so + tr * ROWB + ch * 2) = (bf16)y;
+      for (int g4 = 0; g4 < 2; ++g4) {
+        const int c0 = 16 * cw + 8 * g4 + 4 * hi;   // this group's pairs; partners c0 + D / 2
+        f32x4 cs, sn;
+        load_rope4<D>(cs, sn, rp, tr, c0, S - t0);
+        const f32x4 qpl = tile_vec4<D>(tqi, tr + HALO, c0), qph = tile_vec4<D>(tqi, tr + HALO, c0 + D / 2);
+        const f32x4 kpl = tile_vec4<D>(tk, tr + HALO, c0), kph = tile_vec4<D>(tk, tr + HALO, c0 + D / 2);
+        f32x4 ylo, yhi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rl = 4 * g4 + e, rh = rl + 8;
+          const float qhl = qacc[mb][rl], qhh = qacc[mb][rh];
+          const float khl = kacc[mb][rl], khh = kacc[mb][rh];
+          mpost[mb][rl] += qhl;
+          mpost[mb][rh] += qhh;
+          if (!QRES) {
+            mpre[mb][rl] += qpl[e];
+            mpre[mb][rh] += qph[e];
+          }
+          const float xl = qhl + A * (qpl[e] + kpl[e]) + Bc * (qhl + khl);
+          const float xh = qhh + A * (qph[e] + kph[e]) + Bc * (qhh + khh);
+          // RoPE of the pair (low channel, partner)
+          ylo[e] = xl * cs[e] - xh * sn[e];
+          yhi[e] = xh * cs[e] + xl * sn[e];
+        }
+        stage4<D>(so, tr, c0, ylo);
+        stage4<D>(so, tr, c0 + D / 2, yhi);
       }
     }
     flush(reinterpret_cast<bf16*>(a.q_out) + qrow * D, nullptr);
@@ -404,24 +448,40 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     __builtin_amdgcn_sched_barrier(0);
+    const int tr = tb0 + 32 * mb + l32;
     const float2* rp = rope_t0;
     asm volatile("" : "+s"(rp));
-    float2 csr[16];
-    load_rope<D>(csr, rp, tb0, mb, hi, pair, S - t0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tr = trel(mb, r);
-      const float kh = kacc[mb][r];
-      const float kp = tile_val<D>(tk, tr + HALO, ch);
-      float qpre = 0.0f;
+    for (int g4 = 0; g4 < 2; ++g4) {
+      const int c0 = 16 * cw + 8 * g4 + 4 * hi;
+      f32x4 cs, sn;
+      load_rope4<D>(cs, sn, rp, tr, c0, S - t0);
+      const f32x4 kpl = tile_vec4<D>(tk, tr + HALO, c0), kph = tile_vec4<D>(tk, tr + HALO, c0 + D / 2);
+      f32x4 qsl = {0.f, 0.f, 0.f, 0.f}, qsh = {0.f, 0.f, 0.f, 0.f};
       if (QRES) {
-        for (int i = 0; i < G; ++i) qpre += tile_val<D>(tq + i * TBYTES, tr + HALO, ch);
+        for (int i = 0; i < G; ++i) {
+          qsl += tile_vec4<D>(tq + i * TBYTES, tr + HALO, c0);
+          qsh += tile_vec4<D>(tq + i * TBYTES, tr + HALO, c0 + D / 2);
+        }
       } else {
-        qpre = mpre[mb][r];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qsl[e] = mpre[mb][4 * g4 + e];
+          qsh[e] = mpre[mb][8 + 4 * g4 + e];
+        }
       }
-      const float y = rotate(kh + A * (qpre * invG + kp) + Bc * (mpost[mb][r] * invG + kh),
-                             csr[r], lo_lane);
-      *reinterpret_cast<bf16*>(so + tr * ROWB + ch * 2) = (bf16)y;
+      f32x4 ylo, yhi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rl = 4 * g4 + e, rh = rl + 8;
+        const float khl = kacc[mb][rl], khh = kacc[mb][rh];
+        const float xl = khl + A * (qsl[e] * invG + kpl[e]) + Bc * (mpost[mb][rl] * invG + khl);
+        const float xh = khh + A * (qsh[e] * invG + kph[e]) + Bc * (mpost[mb][rh] * invG + khh);
+        ylo[e] = xl * cs[e] - xh * sn[e];
+        yhi[e] = xh * cs[e] + xl * sn[e];
+      }
+      stage4<D>(so, tr, c0, ylo);
+      stage4<D>(so, tr, c0 + D / 2, yhi);
     }
   }
   flush(ko, ko2);
