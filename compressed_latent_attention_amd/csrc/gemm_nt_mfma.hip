@@ -45,6 +45,17 @@ __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70);
 
 __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(bf16* p, float v) { *p = (bf16)v; }
+// 16 bytes of OutT elements
+template <typename T> struct OutVT;
+template <> struct OutVT<float> { typedef f32x4 type; };
+template <> struct OutVT<bf16> { typedef bf16x8 type; };
+template <typename T> using OutV = typename OutVT<T>::type;
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+}
 
 // One 256-row x 64-k operand tile into LDS: rows row0 .. of a K-contiguous
 // matrix at base (row stride ld elements), `rows` of them valid; k from k0.
@@ -282,7 +293,7 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j],
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j],
                                                               0, 0, 0);
         // issue points 0 .. 4 MI - 1; the CBA + CB copies go out over the
         // first half, PER at each
@@ -312,26 +323,55 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     __syncthreads();
   }
 
-  // D layout of 32x32 MFMA: lane holds column l32, rows 8*(r/4) + 4*hi + r%4.
-  // One C segment (checked by the host): a uniform tile base plus 32-bit lane
-  // offsets.
+  // The MFMAs take B's fragment as their first operand, so each accumulator
+  // block is C^T: lane = output row l32 of the block, registers 4 q .. 4 q + 3
+  // = the 4 consecutive output columns 8 q + 4 hi + 0..3.  The tile leaves
+  // through LDS (free after the loop's last barrier) in MI passes of 64 rows
+  // (block i of every wave): 8- or 16-byte LDS writes, then whole-row 16-byte
+  // global stores.  Staging rows carry 8 elements of padding, so the 32 rows
+  // one write instruction touches fall on distinct banks.  One C segment
+  // (checked by the host, with 16-byte aligned rows): a uniform tile base plus
+  // 32-bit offsets.
   char* cbase = reinterpret_cast<char*>(g.c_ptr[0]) +
                 ((long)split * g.c_split_stride + (long)m0 * g.ldc + n0) * sizeof(OutT);
   const int ldc = (int)g.ldc;
   const int mrem = g.M - m0, nrem = g.N - n0;
+  constexpr int ES = sizeof(OutT), SROWB = (TN + 8) * ES, CPRO = TN * ES / 16, EPC = 16 / ES;
+  static_assert(64 * SROWB <= 2 * STG, "staging fits the operand buffers");
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < MI; ++i) {
+    char* srow = lds + (wm * 32 + l32) * SROWB;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int nl = wn * (NJ * 32) + j * 32 + l32;
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ml = wm * (TMT / 2) + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (ml < mrem && nl < nrem)
-          store_out(reinterpret_cast<OutT*>(cbase + (ml * ldc + nl) * (int)sizeof(OutT)),
-                    acc[i][j][r]);
+      for (int q = 0; q < 4; ++q) {
+        const int nl = wn * (NJ * 32) + j * 32 + 8 * q + 4 * hi;
+        store4(reinterpret_cast<OutT*>(srow + nl * ES), acc[i][j][4 * q], acc[i][j][4 * q + 1],
+               acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 64 * CPRO / (64 * NW); ++u) {
+      const int e = (int)threadIdx.x + 64 * NW * u;
+      const int r = e / CPRO, c = e % CPRO;
+      const int ml = (r >> 5) * (TMT / 2) + i * 32 + (r & 31), nl = c * EPC;
+      if (ml < mrem && nl < nrem) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(lds + r * SROWB + c * 16);
+        char* dst = cbase + (ml * ldc + nl) * ES;
+        if (nl + EPC <= nrem) {
+          *reinterpret_cast<f32x4*>(dst) = v;
+        } else {
+          // the row's last columns, one element at a time (constant indices
+          // keep v in registers)
+          const auto ve = __builtin_bit_cast(OutV<OutT>, v);
+#pragma unroll
+          for (int x = 0; x < EPC; ++x)
+            if (nl + x < nrem) reinterpret_cast<OutT*>(dst)[x] = ve[x];
+        }
       }
     }
+    __syncthreads();
+  }
 }
 
 }  // namespace
@@ -343,6 +383,10 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
 bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError_t* err,
                         GemmLayout layout) {
   if (g.K % TK != 0 || g.K <= 0 || g.lda % 8 != 0 || g.ldb % 8 != 0 || g.c_nseg != 1)
+    return false;
+  // C rows (and split-K slices) 16-byte aligned for the 4-column stores
+  if (g.ldc % 4 != 0 || reinterpret_cast<uintptr_t>(g.c_ptr[0]) % 16 != 0 ||
+      (g.ksplit > 1 && g.c_split_stride % 4 != 0))
     return false;
   const bool kt = layout == GemmLayout::TN;
   if (layout == GemmLayout::NN) return false;
