@@ -49,12 +49,7 @@ struct MGeom {
   static constexpr int NKS = D / 16;                 // 16-channel k-steps of one tap
 };
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-template <int D>
-__device__ __forceinline__ float tile_val(const char* tile, int r, int ch) {
-  return (float)*reinterpret_cast<const bf16*>(tile + r * MGeom<D>::ROWB + ch * 2);
-}
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // The latent tiles of column blocks cols[0 .. n) (D channels each), rows
 // t0 - HALO .. t0 + TW - 1, into LDS tiles dst[0 .. n): every load of the
@@ -284,22 +279,31 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
   // channels (tile row tr + HALO - 1; row HALO - 1 is token t0 - 1, zero
   // before token 0), else v~[t, c]
   const int first_shift = (dm.flags & kVShift) ? D - dm.sv : D;
-  auto vrow = [&](int tr, int c) { return tr + HALO - (c >= first_shift ? 1 : 0); };
   bf16* vo = a.v_out ? reinterpret_cast<bf16*>(a.v_out) + ((long)(b * dm.Hkv + g) * S) * D
                      : nullptr;
   bf16* vo2 = a.v_out2 ? reinterpret_cast<bf16*>(a.v_out2) +
                              ((long)(b * dm.Hkv + g) * a.cap2 + pos0) * D
                        : nullptr;
+  // the 8 channels c8 .. c8 + 7 of V' at tile token tr: one 16-byte read of
+  // the token's row, and of the row before when the chunk reaches the shifted
+  // channels
+  auto vchunk = [&](int tr, int c8) {
+    bf16x8 v = *reinterpret_cast<const bf16x8*>(tv + (tr + HALO) * ROWB + c8 * 2);
+    if (c8 + 8 > first_shift) {
+      const bf16x8 p = *reinterpret_cast<const bf16x8*>(tv + (tr + HALO - 1) * ROWB + c8 * 2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (c8 + i >= first_shift) v[i] = p[i];
+    }
+    return v;
+  };
   if (vo || vo2) {
     // thread = (token, 8 channels): 16-byte stores
     for (int e = threadIdx.x; e < TW * (D / 8); e += 256) {
       const int tr = e / (D / 8), c8 = (e % (D / 8)) * 8;
       const int t = t0 + tr;
       if (t >= S) break;
-      bf16x8 v;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        v[i] = *reinterpret_cast<const bf16*>(tv + vrow(tr, c8 + i) * ROWB + (c8 + i) * 2);
+      const bf16x8 v = vchunk(tr, c8);
       if (vo) *reinterpret_cast<bf16x8*>(vo + (long)t * D + c8) = v;
       if (vo2) *reinterpret_cast<bf16x8*>(vo2 + (long)t * D + c8) = v;
     }
@@ -309,19 +313,25 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
     // keeps 11 significant bits.  It holds the stored bf16 V' values, converted
     // exactly (within fp16's range), so the forward's O and the backward (which
     // reads the bf16 V') see the same V'.
+    // Thread = (4 tokens, 8 channels): four 16-byte row reads, eight 8-byte
+    // stores, one per channel row; the 4-token groups of a channel chunk sit
+    // in consecutive lanes, so a store instruction writes whole 128-byte runs.
     _Float16* vt = reinterpret_cast<_Float16*>(a.vt_out) + (long)(b * dm.Hkv + g) * D * a.s_pad;
-    for (int e = threadIdx.x; e < D * (TW / 8); e += 256) {
-      const int m = e % (TW / 8), c = e / (TW / 8);   // 8-token groups of a channel row together
-      const int t = t0 + 8 * m;
-      if (t >= a.s_pad) continue;
-      f16x8 pk;
+    static_assert((TW / 4) * (D / 8) == 256, "one (4 tokens, 8 channels) item per thread");
+    const int m4 = threadIdx.x % (TW / 4), c8 = (threadIdx.x / (TW / 4)) * 8;
+    const int t = t0 + 4 * m4;
+    if (t < a.s_pad) {
+      f16x4 pk[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // tokens at or past S are zero: the padding of V'^T up to s_pad
-        const float v = t + i < S ? tile_val<D>(tv, vrow(8 * m + i, c), c) : 0.0f;
-        pk[i] = (_Float16)v;
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 v = vchunk(4 * m4 + i, c8);
+#pragma unroll
+        for (int x = 0; x < 8; ++x)   // tokens at or past S: the zero padding up to s_pad
+          pk[x][i] = t + i < S ? (_Float16)(float)v[x] : (_Float16)0.0f;
       }
-      *reinterpret_cast<f16x8*>(vt + (long)c * a.s_pad + t) = pk;
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+        *reinterpret_cast<f16x4*>(vt + (long)(c8 + x) * a.s_pad + t) = pk[x];
     }
   }
   // every read of the v~ tile is done: it now stages each output tile (Q'' of
