@@ -293,11 +293,11 @@ __device__ __forceinline__ void fused_q_tile(const AttnArgs& a, char* lds, int b
       const float qh = qacc[mb][r], kh = kacc[mb][r];
       const float qp = fq_val(tq, tr + FQ_HALO, ch);
       const float kp = fq_val(tk, tr + FQ_HALO, ch);
-      const float x = qh + A * (qp + kp) + Bc * (qh + kh);
+      const float x = __builtin_fmaf(Bc, qh + kh, __builtin_fmaf(A, qp + kp, qh));
       const float2 cs = rope ? a.rope[(long)min(q0 + tr, S - 1) * (D / 2) + pair]
                              : make_float2(1.f, 0.f);
       const float xp = __shfl_xor(x, 16);
-      const float y = lo_lane ? x * cs.x - xp * cs.y : x * cs.x + xp * cs.y;
+      const float y = __builtin_fmaf(x, cs.x, lo_lane ? -(xp * cs.y) : xp * cs.y);
       *reinterpret_cast<bf16*>(qo + tr * FQ_ROWB + ch * 2) = (bf16)y;
     }
   __syncthreads();

@@ -25,6 +25,8 @@
 // XCD (ids 8 apart): the second reads the tile's RoPE rows from that XCD's L2.
 #include "cca_internal.h"
 
+#include <type_traits>
+
 namespace cca {
 namespace {
 
@@ -100,33 +102,58 @@ __device__ __forceinline__ void zero(Acc2& a) {
     for (int r = 0; r < 16; ++r) a[j][r] = 0.0f;
 }
 
-// acc[mb] += conv of the head whose tile is at `tile` for the wave's token
+// The tap fragments of lag j this lane feeds to its MFMAs: output channel ch
+// (its MFMA row), input channels 16 ks + 8 hi .. + 7 for ks = 0 .. D / 16 - 1.
+template <int D>
+__device__ __forceinline__ void load_taps(bf16x8 (&bf)[MGeom<D>::NKS], const bf16* taps, int j,
+                                          int ch, int hi) {
+  const bf16* trow = taps + ((long)j * D + ch) * D + hi * 8;
+#pragma unroll
+  for (int ks = 0; ks < MGeom<D>::NKS; ++ks)
+    bf[ks] = *reinterpret_cast<const bf16x8*>(trow + ks * 16);
+}
+
+// acc[mb] = conv of the head whose tile is at `tile` for the wave's token
 // block mb, transposed (rows = output channels, columns = tokens): A =
 // taps[j][ch][c_in] for output channel ch of MFMA row l32, B = the tile rows of
-// tokens tb0 + 32 mb + l32 at lag j (tile row tb0 + 32 mb + l32 - j + HALO);
-// the D / 16 B fragments of a lag are loaded before its MFMAs and each serves
-// both token blocks.
+// tokens tb0 + 32 mb + l32 at lag j (tile row tb0 + 32 mb + l32 - j + HALO).
+// cur holds lag 0's tap fragments on entry (requested earlier); each lag's
+// MFMAs run while the next lag's fragments are in flight, and after the last
+// lag those of the next head's lag 0 (next_taps; none when null), which cur
+// holds on return.  Each fragment serves both token blocks.
 template <int D>
 __device__ __forceinline__ void conv_head(Acc2& acc, const char* tile, const bf16* taps, int k,
-                                          int ch, int lane, int tb0) {
+                                          int ch, int lane, int tb0,
+                                          bf16x8 (&cur)[MGeom<D>::NKS], const bf16* next_taps) {
   constexpr int NKS = MGeom<D>::NKS, ROWB = MGeom<D>::ROWB;
   const int l32 = lane & 31, hi = lane >> 5;
-  for (int j = 0; j < k; ++j) {
-    const bf16* trow = taps + ((long)j * D + ch) * D + hi * 8;
-    bf16x8 bf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) bf[ks] = *reinterpret_cast<const bf16x8*>(trow + ks * 16);
+  // lag j; the first one starts both chains from zero
+  auto lag = [&](int j, auto first) {
+    bf16x8 nxt[NKS];
+    const bool more = j + 1 < k;
+    if (more) load_taps<D>(nxt, taps, j + 1, ch, hi);
+    else if (next_taps) load_taps<D>(nxt, next_taps, 0, ch, hi);
+    __builtin_amdgcn_sched_barrier(0);       // the requests go out before the MFMAs
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int row = tb0 + 32 * mb + l32 - j + HALO;
         const bf16x8 u = *reinterpret_cast<const bf16x8*>(tile + row * ROWB + (2 * ks + hi) * 16);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[ks], u, acc[mb], 0, 0, 0);
+        if (decltype(first)::value && ks == 0)
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[ks], u, f32x16{}, 0, 0, 0);
+        else
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[ks], u, acc[mb], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);     // keep the A reads next to their MFMAs
+      __builtin_amdgcn_sched_barrier(0);     // keep the B reads next to their MFMAs
     }
-  }
+    if (more || next_taps) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) cur[ks] = nxt[ks];
+    }
+  };
+  lag(0, std::true_type{});
+  for (int j = 1; j < k; ++j) lag(j, std::false_type{});
 }
 
 // Channels c0 .. c0 + 3 of tile row r as floats (one 8-byte LDS read).
@@ -196,8 +223,9 @@ template <int D, int GC, bool VARLEN, bool NOQ, typename Map>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VARLEN || GC == 0 ? 1 : 2,
                                                                      VARLEN || GC == 0 ? 1 : 2)))
 void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
-  // every product rounded on its own (no contraction into FMAs): the
-  // instances with and without Q'' then compute K'' bit for bit alike
+  // no implicit contraction: every fused multiply-add is written out, so the
+  // instances with and without Q'' (and the attention's fused-Q prologue)
+  // compute K'' and Q'' bit for bit alike
 #pragma clang fp contract(off)
   using MG = MGeom<D>;
   constexpr int TW = MG::TW, TBYTES = MG::TBYTES, ROWB = MG::ROWB;
@@ -256,7 +284,12 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
   // registers 8 + 4 g .. their RoPE partners D / 2 further (MFMA row 8 (r / 4) +
   // 4 hi + r % 4 is channel ch of lane row l32 = that row)
 
-  // every tile the work-group needs, in one round
+  const bf16* const taps_q = reinterpret_cast<const bf16*>(a.conv_q);
+  const bf16* const taps_k = reinterpret_cast<const bf16*>(a.conv_k) + (long)g * dm.kk * D * D;
+  auto qtaps = [&](int h) { return taps_q + (long)h * dm.kq * D * D; };
+  // the K head's lag-0 taps, then every tile the work-group needs, in one round
+  bf16x8 tf[MG::NKS];
+  load_taps<D>(tf, taps_k, 0, ch, hi);
   {
     char* const dst[2 + NQS] = {tk, tv, tq, tq + TBYTES};
     const int cols[2 + NQS] = {dm.nq + g * D, dm.nq + dm.nk + g * D, g * G * D, (g * G + 1) * D};
@@ -352,9 +385,7 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
   };
 
   Acc2 kacc, qacc, mpost, mpre;
-  zero(kacc);
-  conv_head<D>(kacc, tk, reinterpret_cast<const bf16*>(a.conv_k) + (long)g * dm.kk * D * D, dm.kk,
-               ch, lane, tb0);
+  conv_head<D>(kacc, tk, taps_k, dm.kk, ch, lane, tb0, tf, qtaps(g * G));
   zero(mpost);
   if (!QRES) zero(mpre);
 
@@ -376,9 +407,7 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
       __syncthreads();
     }
     const char* tqi = tq + (i % NQS) * TBYTES;
-    zero(qacc);
-    conv_head<D>(qacc, tqi, reinterpret_cast<const bf16*>(a.conv_q) + (long)h * dm.kq * D * D,
-                 dm.kq, ch, lane, tb0);
+    conv_head<D>(qacc, tqi, qtaps(h), dm.kq, ch, lane, tb0, tf, i + 1 < G ? qtaps(h + 1) : nullptr);
     if constexpr (NOQ) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
@@ -434,11 +463,11 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
             mpre[mb][rl] += qpl[e];
             mpre[mb][rh] += qph[e];
           }
-          const float xl = qhl + A * (qpl[e] + kpl[e]) + Bc * (qhl + khl);
-          const float xh = qhh + A * (qph[e] + kph[e]) + Bc * (qhh + khh);
+          const float xl = __builtin_fmaf(Bc, qhl + khl, __builtin_fmaf(A, qpl[e] + kpl[e], qhl));
+          const float xh = __builtin_fmaf(Bc, qhh + khh, __builtin_fmaf(A, qph[e] + kph[e], qhh));
           // RoPE of the pair (low channel, partner)
-          ylo[e] = xl * cs[e] - xh * sn[e];
-          yhi[e] = xh * cs[e] + xl * sn[e];
+          ylo[e] = __builtin_fmaf(xl, cs[e], -(xh * sn[e]));
+          yhi[e] = __builtin_fmaf(xh, cs[e], xl * sn[e]);
         }
         stage4<D>(so, tr, c0, ylo);
         stage4<D>(so, tr, c0 + D / 2, yhi);
@@ -485,10 +514,12 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
       for (int e = 0; e < 4; ++e) {
         const int rl = 4 * g4 + e, rh = rl + 8;
         const float khl = kacc[mb][rl], khh = kacc[mb][rh];
-        const float xl = khl + A * (qsl[e] * invG + kpl[e]) + Bc * (mpost[mb][rl] * invG + khl);
-        const float xh = khh + A * (qsh[e] * invG + kph[e]) + Bc * (mpost[mb][rh] * invG + khh);
-        ylo[e] = xl * cs[e] - xh * sn[e];
-        yhi[e] = xh * cs[e] + xl * sn[e];
+        const float xl = __builtin_fmaf(Bc, __builtin_fmaf(mpost[mb][rl], invG, khl),
+                                        __builtin_fmaf(A, __builtin_fmaf(qsl[e], invG, kpl[e]), khl));
+        const float xh = __builtin_fmaf(Bc, __builtin_fmaf(mpost[mb][rh], invG, khh),
+                                        __builtin_fmaf(A, __builtin_fmaf(qsh[e], invG, kph[e]), khh));
+        ylo[e] = __builtin_fmaf(xl, cs[e], -(xh * sn[e]));
+        yhi[e] = __builtin_fmaf(xh, cs[e], xl * sn[e]);
       }
       stage4<D>(so, tr, c0, ylo);
       stage4<D>(so, tr, c0 + D / 2, yhi);

@@ -38,7 +38,8 @@ def check_fused(w: Workload):
     errs = {k: rel(a, b) for k, (a, b, _) in pairs.items()}
     blk = {k: block_rel(a, b, ax) for k, (a, b, ax) in pairs.items() if k != "state"}
     vs_plain = rel(host(fused["y"]), host(plain["y"]))
-    say(f"  rel errors {errs}; worst block {blk}; fused vs separate y {vs_plain:.2e}")
+    say(f"  rel errors {errs}; worst block {blk}; fused vs separate y {vs_plain:.2e} "
+        f"(identical: {torch.equal(fused['y'], plain['y'])})")
     for k, e in list(errs.items()) + list(blk.items()):
         assert e <= TOL[w.dtype], (k, e)
     # K'', V' and the state come from the same mix arithmetic: identical
