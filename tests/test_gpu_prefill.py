@@ -197,6 +197,16 @@ def test_prefill_ccgqa16_large_sampled_rows():
                                 seed=48), n_random=40)
 
 
+def test_prefill_narrow_ragged_columns_sampled_rows():
+    """E = 576 with three query heads of 64 on one KV head (C = 3): proj_down
+    (N = 320, q | k | v segments starting inside a tile: 256-row tiles) and
+    proj_up (N = 576: 128-row tiles) each end in a column tile with 64 of its
+    256 columns inside C; the general-group mix, the d = 64 attention and a
+    ragged last row tile."""
+    check_sampled_rows(Workload("e576_g3_ragged_8200", B=1, S=8200, E=576, C=3, Hq=3, Hkv=1,
+                                seed=49), n_random=40)
+
+
 def test_causality_bit_identical_on_gpu():
     """Perturbing tokens t >= t0 leaves y[:t0] bitwise unchanged."""
     w = Workload("bf16_causal", B=1, S=700, E=512, C=1, Hq=4, Hkv=2, seed=41)
