@@ -293,7 +293,8 @@ __device__ __forceinline__ void fused_q_tile(const AttnArgs& a, char* lds, int b
       const float qh = qacc[mb][r], kh = kacc[mb][r];
       const float qp = fq_val(tq, tr + FQ_HALO, ch);
       const float kp = fq_val(tk, tr + FQ_HALO, ch);
-      const float x = __builtin_fmaf(Bc, qh + kh, __builtin_fmaf(A, qp + kp, qh));
+      // (1 + b/2) q^ + a/2 q~ + (a/2 k~ + b/2 k^)
+      const float x = __builtin_fmaf(1.0f + Bc, qh, __builtin_fmaf(A, qp, __builtin_fmaf(A, kp, Bc * kh)));
       const float2 cs = rope ? a.rope[(long)min(q0 + tr, S - 1) * (D / 2) + pair]
                              : make_float2(1.f, 0.f);
       const float xp = __shfl_xor(x, 16);

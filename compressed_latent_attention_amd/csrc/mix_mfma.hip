@@ -388,6 +388,28 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
   conv_head<D>(kacc, tk, taps_k, dm.kk, ch, lane, tb0, tf, qtaps(g * G));
   zero(mpost);
   if (!QRES) zero(mpre);
+  // The query side's key terms, the same for every head of the group:
+  // q' = (1 + b/2) q^ + a/2 q~ + kq with kq = a/2 k~ + b/2 k^ (per token and
+  // channel, in the accumulator layout)
+  Acc2 kq;
+  if constexpr (!NOQ) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int tr = tb0 + 32 * mb + l32;
+#pragma unroll
+      for (int g4 = 0; g4 < 2; ++g4) {
+        const int c0 = 16 * cw + 8 * g4 + 4 * hi;
+        const f32x4 kpl = tile_vec4<D>(tk, tr + HALO, c0), kph = tile_vec4<D>(tk, tr + HALO, c0 + D / 2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rl = 4 * g4 + e, rh = rl + 8;
+          kq[mb][rl] = __builtin_fmaf(A, kpl[e], Bc * kacc[mb][rl]);
+          kq[mb][rh] = __builtin_fmaf(A, kph[e], Bc * kacc[mb][rh]);
+        }
+      }
+    }
+  }
+  const float Bp1 = 1.0f + Bc;
 
 #pragma unroll
   for (int i = 0; i < G; ++i) {
@@ -450,21 +472,19 @@ void mix_fwd_mfma_kernel(MixArgs a, int ntiles8, Map vm) {
         f32x4 cs, sn;
         load_rope4<D>(cs, sn, rp, tr, c0, S - t0);
         const f32x4 qpl = tile_vec4<D>(tqi, tr + HALO, c0), qph = tile_vec4<D>(tqi, tr + HALO, c0 + D / 2);
-        const f32x4 kpl = tile_vec4<D>(tk, tr + HALO, c0), kph = tile_vec4<D>(tk, tr + HALO, c0 + D / 2);
         f32x4 ylo, yhi;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int rl = 4 * g4 + e, rh = rl + 8;
           const float qhl = qacc[mb][rl], qhh = qacc[mb][rh];
-          const float khl = kacc[mb][rl], khh = kacc[mb][rh];
           mpost[mb][rl] += qhl;
           mpost[mb][rh] += qhh;
           if (!QRES) {
             mpre[mb][rl] += qpl[e];
             mpre[mb][rh] += qph[e];
           }
-          const float xl = __builtin_fmaf(Bc, qhl + khl, __builtin_fmaf(A, qpl[e] + kpl[e], qhl));
-          const float xh = __builtin_fmaf(Bc, qhh + khh, __builtin_fmaf(A, qph[e] + kph[e], qhh));
+          const float xl = __builtin_fmaf(Bp1, qhl, __builtin_fmaf(A, qpl[e], kq[mb][rl]));
+          const float xh = __builtin_fmaf(Bp1, qhh, __builtin_fmaf(A, qph[e], kq[mb][rh]));
           // RoPE of the pair (low channel, partner)
           ylo[e] = __builtin_fmaf(xl, cs[e], -(xh * sn[e]));
           yhi[e] = __builtin_fmaf(xh, cs[e], xl * sn[e]);
