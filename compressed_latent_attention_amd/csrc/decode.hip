@@ -32,7 +32,7 @@ namespace {
 constexpr int NW = 4;            // waves per work-group
 constexpr int TARGET_WGS = 256;  // work-groups per launch: two per CU, all resident at once
 
-constexpr int MAX_SPLIT = 1024;  // work-groups per (sequence, KV head) the merge kernel holds
+constexpr int MAX_SPLIT = 1024;  // work-groups per (sequence, KV head) at most
 
 bool fast_decode(const Dims& dm) {
   return dm.bf16 && (dm.d == 128 || dm.d == 64) && dm.G <= kMaxGroup;
@@ -277,47 +277,51 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(AttnArgs a) {
   }
 }
 
-// Merge of the nsplit partials of (sequence b, query head h): their maxima
-// and weights in parallel (one thread per partial, through LDS), then one
-// thread per channel sums its weighted partial O over them.  Partial 0 always
-// holds key 0, so the merged max is finite and the weight sum is >= 1.
+// Merge of the nsplit partials of (sequence b, query head h), one thread per
+// channel.  Every thread reads the partials' (max, weight) pairs itself
+// (broadcast loads) along with its channel of their O, eight partials per
+// round, so a sequence with at most eight partials costs one memory round and
+// no barrier; further rounds rescale the running sums to the new maximum.
+// Partial 0 always holds key 0, so the maximum is finite after the first round
+// and the weight sum is >= 1.
 template <int D>
 __global__ __launch_bounds__(D) void attn_decode_merge_kernel(AttnArgs a) {
-  constexpr int PSTRIDE = D + 2;
-  __shared__ float wgt[MAX_SPLIT];
-  __shared__ float red[D / 64][2];
+  constexpr int PSTRIDE = D + 2, CH = 8;
   const Dims& dm = a.dm;
   const int h = blockIdx.x, b = blockIdx.y;
   const int off_b = a.pos.off[b], nsplit = a.pos.off[b + 1] - off_b;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x;
   const float* part = a.part + ((long)off_b * dm.Hq + (long)h * nsplit) * PSTRIDE;
-  float m = -INFINITY;
-  for (int c = t; c < nsplit; c += D) m = fmaxf(m, part[(long)c * PSTRIDE + D]);
+  float m = -INFINITY, l = 0.0f, o = 0.0f;
+  for (int c0 = 0; c0 < nsplit; c0 += CH) {
+    float mc[CH], lc[CH], oc[CH];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (lane == 0) red[wave][0] = m;
-  __syncthreads();
-  m = red[0][0];
+    for (int i = 0; i < CH; ++i) {
+      const float* p = part + (long)min(c0 + i, nsplit - 1) * PSTRIDE;
+      mc[i] = p[D];
+      lc[i] = p[D + 1];
+      oc[i] = p[t];
+    }
+    float mn = m;
 #pragma unroll
-  for (int w = 1; w < D / 64; ++w) m = fmaxf(m, red[w][0]);
-  float l = 0.0f;
-  for (int c = t; c < nsplit; c += D) {
-    const float mc = part[(long)c * PSTRIDE + D];
-    const float wc = mc == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mc - m);
-    wgt[c] = wc;
-    l = fmaf(part[(long)c * PSTRIDE + D + 1], wc, l);
+    for (int i = 0; i < CH; ++i)
+      if (c0 + i < nsplit) mn = fmaxf(mn, mc[i]);
+    if (c0 > 0) {
+      const float sc = __builtin_amdgcn_exp2f(m - mn);
+      l *= sc;
+      o *= sc;
+    }
+    // weight 0 for the clamped repeats past nsplit (finite partials), so every
+    // load is used unconditionally and all of them go out together
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const float wc = c0 + i >= nsplit || mc[i] == -INFINITY ? 0.0f
+                                                              : __builtin_amdgcn_exp2f(mc[i] - mn);
+      l = fmaf(lc[i], wc, l);
+      o = fmaf(oc[i], wc, o);
+    }
+    m = mn;
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-  __syncthreads();
-  if (lane == 0) red[wave][1] = l;
-  __syncthreads();
-  l = red[0][1];
-#pragma unroll
-  for (int w = 1; w < D / 64; ++w) l += red[w][1];
-  float o = 0.0f;
-#pragma unroll 8
-  for (int c = 0; c < nsplit; ++c) o = fmaf(part[(long)c * PSTRIDE + t], wgt[c], o);
   reinterpret_cast<bf16*>(a.o)[((long)b * dm.Hq + h) * D + t] = (bf16)(o / l);
 }
 
