@@ -485,16 +485,18 @@ __global__ __launch_bounds__(256) void mix_bwd_conv_input_mfma(MixBwdArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
-  // the epilogue's direct terms, loaded now so their latency overlaps the MFMAs
-  const float* dir = srow0 + (long)t0 * W + dcol;
-  float dv[2][16];
+  // The MFMAs take the tap fragment as their first operand, so each
+  // accumulator is transposed: lane = token tw + l32, registers 4 q .. 4 q + 3
+  // = the 4 consecutive channels (nb0 + nbi) 32 + 8 q + 4 hi + 0..3.
+  // The epilogue's direct terms, loaded now (16 bytes per 4 channels) so their
+  // latency overlaps the MFMAs.
+  const float* dir = srow0 + (long)t0 * W + dcol + (long)min(tw + l32, S - 1 - t0) * W;
+  f32x4 dv[2][4];
 #pragma unroll
   for (int nbi = 0; nbi < 2; ++nbi)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tr = min(tw + 8 * (r >> 2) + 4 * hi + (r & 3), S - 1 - t0);
-      dv[nbi][r] = dir[(long)tr * W + (nb0 + nbi) * 32 + l32];
-    }
+    for (int q = 0; q < 4; ++q)
+      dv[nbi][q] = *reinterpret_cast<const f32x4*>(dir + (nb0 + nbi) * 32 + 8 * q + 4 * hi);
   for (int j = 0; j < k; ++j) {
     // A: lane (token tw + l32, hi) holds channels 16 ks + 8 hi .. of dq^[t + j];
     // B: lane (c' = nb 32 + l32, hi) holds the same channels of tapT row c'
@@ -514,22 +516,34 @@ __global__ __launch_bounds__(256) void mix_bwd_conv_input_mfma(MixBwdArgs a) {
     for (int ks = 0; ks < TD / 16; ++ks) {
       const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(arow + ks * 16);
       const bf16x8 alo = *reinterpret_cast<const bf16x8*>(arow + GPLANE + ks * 16);
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b0[ks], acc[0], 0, 0, 0);
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b0[ks], acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b1[ks], acc[1], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b1[ks], acc[1], 0, 0, 0);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0[ks], ahi, acc[0], 0, 0, 0);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0[ks], alo, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1[ks], ahi, acc[1], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1[ks], alo, acc[1], 0, 0, 0);
     }
   }
-  // D: lane holds column c' = nb 32 + l32, register r token tw + 8 (r / 4) + 4 hi + r % 4
-  bf16* out = reinterpret_cast<bf16*>(a.dqkv) + ((long)b * S + t0) * dm.nqkv + col;
+  // The CT x TD output tile leaves through LDS (the staged dq^ is no longer
+  // read): 8-byte writes of 4 channels into rows of GLD elements, then
+  // 16-byte stores of whole rows.
+  __syncthreads();
+  bf16* const so = gs;
 #pragma unroll
-  for (int nbi = 0; nbi < 2; ++nbi) {
-    const int c = (nb0 + nbi) * 32 + l32;
+  for (int nbi = 0; nbi < 2; ++nbi)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tr = tw + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (t0 + tr < S) out[(long)tr * dm.nqkv + c] = (bf16)(acc[nbi][r] + dv[nbi][r]);
+    for (int q = 0; q < 4; ++q) {
+      const bf16x4 v = {(bf16)(acc[nbi][4 * q] + dv[nbi][q][0]), (bf16)(acc[nbi][4 * q + 1] + dv[nbi][q][1]),
+                        (bf16)(acc[nbi][4 * q + 2] + dv[nbi][q][2]), (bf16)(acc[nbi][4 * q + 3] + dv[nbi][q][3])};
+      *reinterpret_cast<bf16x4*>(so + (tw + l32) * GLD + (nb0 + nbi) * 32 + 8 * q + 4 * hi) = v;
     }
+  __syncthreads();
+  bf16* out = reinterpret_cast<bf16*>(a.dqkv) + ((long)b * S + t0) * dm.nqkv + col;
+  static_assert(CT * TD / 8 % 256 == 0, "whole rows per pass");
+#pragma unroll
+  for (int u = 0; u < CT * TD / 8 / 256; ++u) {
+    const int e = t + 256 * u, tr = e / (TD / 8), c8 = (e % (TD / 8)) * 8;
+    if (t0 + tr < S)
+      *reinterpret_cast<bf16x8*>(out + (long)tr * dm.nqkv + c8) =
+          *reinterpret_cast<const bf16x8*>(so + tr * GLD + c8);
   }
 }
 
