@@ -600,43 +600,51 @@ __global__ __launch_bounds__(256) void mix_bwd_tap_partial_mfma(MixBwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  // Staging map: load p = NLD wave + i covers tokens 16 (p % 4) + L % 16 and
-  // float4 groups 4 (p / 4) + L / 16, so one wave's transposed 2-byte stores of
-  // a channel row go to 16 consecutive tokens (bank-conflict free) while each
-  // load reads 64 contiguous bytes of 16 rows.
-  auto stage_rc = [&](int i, int& r, int& c4) {
-    const int pidx = NLD * wave + i;
-    r = 16 * (pidx & 3) + (lane & 15);
-    c4 = 4 * (4 * (pidx >> 2) + (lane >> 4));
-  };
+  // Staging map: item e = t + 256 i (i < NIT) covers tokens 4 (e % 16) .. + 3
+  // and channels 4 (e / 16) .. + 3 of the chunk, one float4 load per token;
+  // its 4 tokens of each channel go to the transposed tiles as one 8-byte
+  // store per plane.  The 16 lanes of a channel group write one 128-byte run
+  // of a channel row, and each load instruction reads 64 contiguous bytes of
+  // 16 rows.
+  constexpr int NIT = GT * TD / 16 / 256;              // items per thread and operand
+  static_assert(NIT * 4 == NLD, "one float4 per token of an item");
   for (int c0 = tb0; c0 < tend; c0 += GT) {
-    // 64 tokens x TD / 4 float4 per operand: NLD of each per thread, all in flight
-    f32x4 gv[NLD], xv[NLD];
+    // GT tokens x TD / 4 float4 per operand: NLD of each per thread, all in flight
+    f32x4 gv[NIT][4], xv[NIT][4];
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      int r, c4;
-      stage_rc(i, r, c4);
-      const int tok = c0 + r;
-      gv[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            grs, ((tok - tb0) * W + c4) * 4, 0, 0));
-      // q~ row tok - j; before row 0 the offset wraps past the range (zero)
-      xv[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            xrs, ((tok - j - xr0) * dm.nqkv + c4) * 4, 0, 0));
+    for (int i = 0; i < NIT; ++i) {
+      const int e = t + 256 * i, r0 = 4 * (e % 16), c4 = 4 * (e / 16);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int tok = c0 + r0 + u;
+        gv[i][u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 grs, ((tok - tb0) * W + c4) * 4, 0, 0));
+        // q~ row tok - j; before row 0 the offset wraps past the range (zero)
+        xv[i][u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 xrs, ((tok - j - xr0) * dm.nqkv + c4) * 4, 0, 0));
+      }
     }
     __syncthreads();                                     // the previous chunk's reads are done
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      int r, c4;
-      stage_rc(i, r, c4);
-      const bool live = c0 + r < tend;                   // tokens past the block: zero
+    for (int i = 0; i < NIT; ++i) {
+      const int e = t + 256 * i, r0 = 4 * (e % 16), c4 = 4 * (e / 16);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float g = live ? gv[i][q] : 0.0f, x = live ? xv[i][q] : 0.0f;
-        const bf16 gh = (bf16)g, xh = (bf16)x;
-        gT[(c4 + q) * TLDT + r] = gh;
-        gT[TPLANE + (c4 + q) * TLDT + r] = (bf16)(g - (float)gh);
-        xT[(c4 + q) * TLDT + r] = xh;
-        xT[TPLANE + (c4 + q) * TLDT + r] = (bf16)(x - (float)xh);
+        bf16x4 gh, gl, xh, xl;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool live = c0 + r0 + u < tend;          // tokens past the block: zero
+          const float g = live ? gv[i][u][q] : 0.0f, x = live ? xv[i][u][q] : 0.0f;
+          gh[u] = (bf16)g;
+          gl[u] = (bf16)(g - (float)gh[u]);
+          xh[u] = (bf16)x;
+          xl[u] = (bf16)(x - (float)xh[u]);
+        }
+        const int o = (c4 + q) * TLDT + r0;
+        *reinterpret_cast<bf16x4*>(gT + o) = gh;
+        *reinterpret_cast<bf16x4*>(gT + TPLANE + o) = gl;
+        *reinterpret_cast<bf16x4*>(xT + o) = xh;
+        *reinterpret_cast<bf16x4*>(xT + TPLANE + o) = xl;
       }
     }
     __syncthreads();
