@@ -390,25 +390,33 @@ __global__ __launch_bounds__(256) void mix_bwd_pointwise_group(MixBwdArgs a) {
 // the contracted index, so the tap matrices are transposed once per call:
 // tapT[m][c'][c] = A_m[c][c'], m running over (head, tap) pairs as the taps are
 // stored (query heads, then key heads).
+// Work-group (m, quarter): source rows quarter * TD / 4 .. + TD / 4 - 1 of
+// tap matrix m, i.e. that column strip of every tapT row.  The strip is staged
+// in LDS with 16-byte row copies; a thread then gathers 8 consecutive source
+// rows of one column (consecutive lanes take consecutive columns, so every
+// 2-byte LDS read of a wave hits distinct banks) and stores them as one
+// 16-byte piece of a tapT row.
 template <int TD>
 __global__ __launch_bounds__(256) void mix_bwd_tap_transpose(MixBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 tile[TD][TD + 8];
+  constexpr int QR = TD / 4;                           // source rows per work-group
+  __shared__ __attribute__((aligned(16))) bf16 tile[QR][TD + 8];
   const Dims& dm = a.dm;
-  const int m = blockIdx.x, nqm = dm.Hq * dm.kq;
+  const int m = blockIdx.x, r0 = blockIdx.y * QR, nqm = dm.Hq * dm.kq;
   const bf16* src = m < nqm ? reinterpret_cast<const bf16*>(a.conv_q) + (long)m * TD * TD
                             : reinterpret_cast<const bf16*>(a.conv_k) + (long)(m - nqm) * TD * TD;
   bf16* dst = reinterpret_cast<bf16*>(a.tapT) + (long)m * TD * TD;
-  for (int e = threadIdx.x; e < TD * TD / 8; e += 256) {
+  for (int e = threadIdx.x; e < QR * TD / 8; e += 256) {
     const int r = e / (TD / 8), c8 = (e % (TD / 8)) * 8;
-    *reinterpret_cast<bf16x8*>(&tile[r][c8]) = *reinterpret_cast<const bf16x8*>(src + r * TD + c8);
+    *reinterpret_cast<bf16x8*>(&tile[r][c8]) =
+        *reinterpret_cast<const bf16x8*>(src + (long)(r0 + r) * TD + c8);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < TD * TD / 8; e += 256) {
-    const int r = e / (TD / 8), c8 = (e % (TD / 8)) * 8;
+  for (int e = threadIdx.x; e < TD * QR / 8; e += 256) {
+    const int c = e % TD, r8 = (e / TD) * 8;           // tapT row c, strip columns r8 .. + 7
     bf16x8 v;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = tile[c8 + i][r];
-    *reinterpret_cast<bf16x8*>(dst + r * TD + c8) = v;
+    for (int i = 0; i < 8; ++i) v[i] = tile[r8 + i][c];
+    *reinterpret_cast<bf16x8*>(dst + (long)c * TD + r0 + r8) = v;
   }
 }
 
@@ -759,7 +767,7 @@ hipError_t launch_mix_bwd(const MixBwdArgs& a, hipStream_t s) {
   if ((a.dk2 || a.dv2) && !mix_bwd_adds_dkdv2(dm)) return hipErrorInvalidValue;
   if (dm.bf16 && mfma_d(dm)) {
     if (a.tapT == nullptr) return hipErrorInvalidValue;
-    const dim3 gtap(nblk, dm.Hq + dm.Hkv, kmax), gtr(dm.Hq * dm.kq + dm.Hkv * dm.kk);
+    const dim3 gtap(nblk, dm.Hq + dm.Hkv, kmax), gtr(dm.Hq * dm.kq + dm.Hkv * dm.kk, 4);
     if (!launch_pointwise_group<bf16>(a, s))
       hipLaunchKernelGGL(mix_bwd_pointwise<bf16>, dim3(a.S, dm.Hkv, a.B), dim3(256), 0, s, a);
     if (dm.d == 128) {
