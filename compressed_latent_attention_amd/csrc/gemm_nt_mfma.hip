@@ -19,6 +19,10 @@
 // end-of-step wait.  LDS rows (64 k = 128 B) are unpadded with their
 // 16-byte chunks XOR-swizzled by row, so that the fragment reads are free of
 // bank conflicts.
+// Grids of 512 or more bf16 tiles run two tiles per work-group: the second
+// tile's first stage is copied during the first tile's last k step, and the
+// first tile leaves through the other stage, so its stores drain while the
+// second tile computes.
 // Rows past M or past the end of B's segment read as zero (buffer range
 // check), so ragged M and N need no special path.
 // TN layout (C = A^T B with A [K, M] and B [K, N] both row-major, as the weight
@@ -167,10 +171,11 @@ __device__ __forceinline__ bf16x8 t_frag(const char* p) {
 // KT: both operands K-major (TN layout).  SB: B tiles may cross segments of
 // B (dma_part_seg).  TMT: tile rows, 256 or (NT only) 128, which doubles the
 // tiles of a grid that would leave CUs idle (waves of 64 x 64 with NW = 8).
-template <typename OutT, int NW, bool KT, bool SB = false, int TMT = TM>
+template <typename OutT, int NW, bool KT, bool SB = false, int TMT = TM, int TPW = 1>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   static_assert(TMT == TM || (TMT == 128 && !KT), "128-row tiles: NT layout only");
+  static_assert(TPW == 1 || (!KT && !SB && TMT == TM), "several tiles per work-group: NT, one B segment");
   constexpr int WN = NW / 2;                 // waves along N
   constexpr int NJ = TN / WN / 32;           // 32-column blocks per wave: 4 or 2
   constexpr int MI = TMT / 64;               // 32-row blocks per wave: 4 or 2
@@ -186,8 +191,21 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   // read the same k-rows of A and B at about the same time and each XCD's L2
   // fetches its K range once rather than every tile's rows over all of K
   const int nt = tiles_m * tiles_n;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31, hi = lane >> 5;
+  // With TPW tiles per work-group (one K range), XCD x takes its nt / 8 tiles
+  // as TPW passes of its work-groups; the last k step of a tile copies the
+  // next tile's first k range, and the tile leaves through the other stage,
+  // so its stores drain while the next tile's MFMAs run.
+#pragma unroll 1
+  for (int it = 0; it < TPW; ++it) {
   int t, split = 0;
-  if (nsplit > 1) {
+  if constexpr (TPW > 1) {
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, P = nt >> 3;
+    t = xcd * P + loc + it * (P / TPW);
+  } else if (nsplit > 1) {
     const int W = nt * nsplit, lin = blockIdx.x + gridDim.x * blockIdx.y;
     const int xcd = lin & 7, loc = lin >> 3;
     const int q = xcd * (W >> 3) + min(xcd, W & 7) + loc;
@@ -201,11 +219,6 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   const int klen = g.K / nsplit, kbeg = split * klen;
   const int tm = t / tiles_n, tn = t % tiles_n;
   const int m0 = tm * TMT, n0 = tn * TN;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-  const int l32 = lane & 31, hi = lane >> 5;
 
   // A rows m0 .., B rows n0 .. (inside one segment of B, checked by the host)
   const bf16* abase = reinterpret_cast<const bf16*>(g.a) + (long)m0 * g.lda;
@@ -221,6 +234,21 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   const int kvalid = g.k_valid > 0 ? g.k_valid : g.K;
   const bf16* amat = reinterpret_cast<const bf16*>(g.a);
   const bf16* bmat = reinterpret_cast<const bf16*>(g.b_ptr[0]);
+  // the next tile's operand bases (TPW > 1: K range 0, one B segment)
+  const bf16* nabase = abase;
+  const bf16* nbbase = bbase;
+  int narows = arows, nbrows = brows;
+  if constexpr (TPW > 1) {
+    if (it + 1 < TPW) {
+      const int P = nt >> 3;
+      const int t2 = t + P / TPW, tm2 = t2 / tiles_n, tn2 = t2 % tiles_n;
+      nabase = reinterpret_cast<const bf16*>(g.a) + (long)(tm2 * TMT) * g.lda;
+      narows = min(g.M - tm2 * TMT, TMT);
+      nbbase = reinterpret_cast<const bf16*>(g.b_ptr[0]) + (long)(tn2 * TN) * g.ldb;
+      nbrows = min(g.N - tn2 * TN, TN);
+    }
+  }
+  if (TPW == 1 || it == 0) {
   if constexpr (KT) {
     dma_tile_t<CB>(lds, amat, g.lda, m0, kvalid, kbeg, wave, lane);
     dma_tile_t<CB>(lds + ABYTES, bmat, g.ldb, n0, kvalid, kbeg, wave, lane);
@@ -232,6 +260,7 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     } else {
       dma_tile<CB>(lds + ABYTES, bbase, g.ldb, brows, g.K, kbeg, wave, lane);
     }
+  }
   }
 
   f32x16 acc[MI][NJ];
@@ -265,8 +294,10 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     if constexpr (KT) return t_frag(st + boff[j] + 8192 * ks);
     else return *reinterpret_cast<const bf16x8*>(st + boff[ks] + j * 32 * 128);
   };
-  wait_dma();
-  __syncthreads();
+  if (TPW == 1 || it == 0) {
+    wait_dma();
+    __syncthreads();
+  }
 
   for (int kt = 0; kt < nk; ++kt) {
     const char* st = lds + (kt & 1) * STG;
@@ -274,7 +305,11 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
     // copies its own k range again into the idle stage, so the loop body has
     // no branch)
     char* nx = lds + ((kt + 1) & 1) * STG;
-    const int knx = kbeg + min(kt + 1, nk - 1) * TK;
+    const bool ntile = TPW > 1 && it + 1 < TPW && kt == nk - 1;
+    const int knx = ntile ? 0 : kbeg + min(kt + 1, nk - 1) * TK;
+    const bf16* cabase = ntile ? nabase : abase;
+    const bf16* cbbase = ntile ? nbbase : bbase;
+    const int carows = ntile ? narows : arows, cbrows = ntile ? nbrows : brows;
     bf16x8 fa[2][MI], fb[2][NJ];
 #pragma unroll
     for (int i = 0; i < MI; ++i) fa[0][i] = frag_a(st, 0, i);
@@ -308,10 +343,10 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
               if (blk < CBA) dma_part_t<CB>(nx, amat, g.lda, m0, kvalid, knx, wave, lane, blk);
               else dma_part_t<CB>(nx + ABYTES, bmat, g.ldb, n0, kvalid, knx, wave, lane, blk - CBA);
             } else {
-              if (blk < CBA) dma_part<CBA>(nx, abase, g.lda, arows, g.K, knx, wave, lane, blk);
+              if (blk < CBA) dma_part<CBA>(nx, cabase, g.lda, carows, g.K, knx, wave, lane, blk);
               else if (blk < CBA + CB) {
                 if constexpr (SB) dma_part_seg<CB>(nx + ABYTES, g, n0, knx, wave, lane, blk - CBA);
-                else dma_part<CB>(nx + ABYTES, bbase, g.ldb, brows, g.K, knx, wave, lane, blk - CBA);
+                else dma_part<CB>(nx + ABYTES, cbbase, g.ldb, cbrows, g.K, knx, wave, lane, blk - CBA);
               }
             }
           }
@@ -338,9 +373,11 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   const int mrem = g.M - m0, nrem = g.N - n0;
   constexpr int ES = sizeof(OutT), SROWB = (TN + 8) * ES, CPRO = TN * ES / 16, EPC = 16 / ES;
   static_assert(64 * SROWB <= 2 * STG, "staging fits the operand buffers");
+  static_assert(TPW == 1 || 64 * SROWB <= STG, "staging fits one stage");
+  char* const ebuf = lds + (TPW > 1 ? STG : 0);
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
-    char* srow = lds + (wm * 32 + l32) * SROWB;
+    char* srow = ebuf + (wm * 32 + l32) * SROWB;
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -356,7 +393,7 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
       const int r = e / CPRO, c = e % CPRO;
       const int ml = (r >> 5) * (TMT / 2) + i * 32 + (r & 31), nl = c * EPC;
       if (ml < mrem && nl < nrem) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(lds + r * SROWB + c * 16);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ebuf + r * SROWB + c * 16);
         char* dst = cbase + (ml * ldc + nl) * ES;
         if (nl + EPC <= nrem) {
           *reinterpret_cast<f32x4*>(dst) = v;
@@ -371,6 +408,7 @@ void gemm_nt_256_kernel(GemmArgs g, int tiles_m, int tiles_n) {
       }
     }
     __syncthreads();
+  }
   }
 }
 
@@ -436,6 +474,14 @@ bool launch_gemm_nt_big(const GemmArgs& g, bool out_f32, hipStream_t s, hipError
     hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 8, false, true>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
   else if (out_f32)
     hipLaunchKernelGGL((gemm_nt_256_kernel<float, 8, false>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+  // bf16 output over two or more rounds of tiles (the up-projection, the
+  // backward's dx): each work-group takes two tiles, the first tile's stores
+  // drain during the second tile's MFMAs and the second tile's first stage
+  // loads during the first tile's last k step (proj_up 45.0 -> 43.6 us)
+  else if (nsplit == 1 && g.b_nseg == 1 && (g.K / TK) % 2 == 0 && tiles_m * tiles_n >= 512 &&
+           (tiles_m * tiles_n) % 16 == 0)
+    hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 8, false, false, TM, 2>),
+                       dim3(tiles_m * tiles_n / 2), dim3(512), 0, s, g, tiles_m, tiles_n);
   else
     hipLaunchKernelGGL((gemm_nt_256_kernel<bf16, 8, false>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
   *err = hipGetLastError();
