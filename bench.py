@@ -483,6 +483,34 @@ def bench_d64(args, torch, cca):
     return {"prefill": pre, "decode": dec, "backward": bwd}
 
 
+def bench_cca4k(args, torch, cca):
+    """The CCA prefill at S = 4096 (B = 1, E = 2048, C = 4, 4 query and 4 KV
+    heads of 128, no head sharing): tokens/s, the layer's and the attention's
+    fraction of the dense bf16 peak and the kernel times.  A shorter sequence
+    puts more of the layer in the projections (attention is ~32% of its FLOPs)."""
+    from compressed_latent_attention_amd.synthetic import WORKLOADS, make_inputs
+    w = WORKLOADS["cca_prefill_4k"]
+    inp = make_inputs(w)
+    a2 = argparse.Namespace(**vars(args))
+    a2.steps = max(args.steps, 50)
+    elapsed, _, prof, layer, warm = bench_prefill(a2, torch, cca, w, inp)
+    layer.close()
+    ms = elapsed * 1e3 / a2.steps
+    fl = prefill_flops(w)
+    kernels = {k: {"avg_ms": v[1] / max(v[0], 1), "launches": v[0],
+                   "tflops": (fl[k] / (v[1] / max(v[0], 1) * 1e-3) / 1e12) if k in fl else None}
+               for k, v in prof.items()}
+    attn = kernels.get("attn", {})
+    return {"workload": f"{w.name}: B={w.B}, S={w.S}, E={w.E}, C={w.C}, Hq={w.Hq}, Hkv={w.Hkv}, "
+                        f"d={w.d}, bf16",
+            "tokens_per_s": w.B * w.S / elapsed * a2.steps, "ms_per_step": ms,
+            "warmup_steps": warm,
+            "layer_tflops": sum(fl.values()) / (ms * 1e-3) / 1e12,
+            "layer_frac_of_bf16_peak": sum(fl.values()) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "attn_frac_of_bf16_peak": (attn.get("tflops") or float("nan")) / PEAK_BF16_TFLOPS,
+            "kernels": kernels}
+
+
 def _gpu_layer(torch, cca, w, gen):
     """A layer of workload w with weights drawn on the GPU (seeded N(0, 1)
     scaled like the parity recipe; the timing does not depend on the values)."""
@@ -595,8 +623,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--warm-s", type=float, default=0.3,
                     help="untimed prefill steps continue past --warmup until this many seconds")
-    ap.add_argument("--rows", default="prefill,mix,fused,varlen,decode,backward,d64",
-                    help="comma list: prefill (headline, always run), mix (the mix kernel with "
+    ap.add_argument("--rows", default="prefill,cca4k,mix,fused,varlen,decode,backward,d64",
+                    help="comma list: prefill (headline, always run), cca4k (the CCA prefill at "
+                         "S = 4096, four query and four KV heads), mix (the mix kernel with "
                          "cold caches), fused (the prefill with the query side of the mix in "
                          "the attention, against the separate passes), varlen (the chunked "
                          "variable-length prefill), decode, backward, d64 "
@@ -670,6 +699,8 @@ def main():
         "ms_per_step_with_kernel_events": elapsed_prof * 1000.0 / args.steps,
     }
     rows = [r.strip() for r in args.rows.split(",") if r.strip()]
+    if "cca4k" in rows:
+        out["cca_prefill_4k"] = bench_cca4k(args, torch, cca)
     if "mix" in rows:
         out["mix_cold"] = bench_mix_cold(args, torch, cca, w, inp)
     if "fused" in rows:

@@ -131,6 +131,20 @@ SavedLayout saved_layout(const Dims& dm, long B, long S) {
   return L;
 }
 
+// Key-split parts per query block of an inference prefill's attention: with
+// fewer than two work-groups per CU (512 on the 256-CU MI355X, one 8-wave
+// work-group per CU at a time) the grid would leave CUs idle and the longest
+// query block alone would set the kernel's length; splitting each block's key
+// tiles over P work-groups (merged by a second kernel) fills the chip.
+constexpr int kAttnTargetWGs = 512;
+int prefill_ksplit(const Dims& dm, long B, long S) {
+  if (!prefill_uses_mfma(dm)) return 1;
+  const long grid = (S + 127) / 128 * dm.Hq * B;
+  if (grid >= kAttnTargetWGs) return 1;
+  const long P = (kAttnTargetWGs + grid - 1) / grid;
+  return (int)std::min<long>(P, 4);
+}
+
 struct DecodeLayout {
   size_t qkv, q, o, part, cv, gpart, total;
 };
@@ -444,7 +458,11 @@ size_t cca_state_bytes(const cca_handle* h, int32_t B) {
 size_t cca_workspace_bytes(const cca_handle* h, int op, int32_t B, int32_t S) {
   if (!h || B <= 0) return 0;
   switch (op) {
-    case CCA_OP_PREFILL: return S > 0 ? saved_layout(h->dm, B, S).total : 0;
+    case CCA_OP_PREFILL:
+      // the saved-tensor regions, then the key-split attention partials (inference)
+      return S > 0 ? saved_layout(h->dm, B, S).total +
+                         attn_split_part_bytes(h->dm, B, S, prefill_ksplit(h->dm, B, S))
+                   : 0;
     case CCA_OP_DECODE: return decode_layout(h->dm, B).total;
     case CCA_OP_BACKWARD: return S > 0 ? bwd_layout(h->dm, B, S).total : 0;
   }
@@ -509,6 +527,14 @@ cca_status cca_forward_prefill(cca_handle* h, const cca_weights* w, const void* 
     aa.o = o; aa.o32 = o32; aa.lse = lse; aa.decode = false;
     if (fuse_q) {
       aa.qlat = qkv; aa.conv_q = w->conv_q; aa.conv_k = w->conv_k; aa.rope = h->rope;
+    } else if (!saved && mfma) {
+      // an inference prefill's workspace holds the key-split partials after
+      // the saved-tensor regions (cca_workspace_bytes)
+      const int P = prefill_ksplit(dm, B, S);
+      if (P > 1) {
+        aa.ksplit = P;
+        aa.part = (float*)(base + L.total);
+      }
     }
     CCA_TRY_HIP(timed(h, "attn", s, [&] { return launch_attn_fwd(aa, s); }));
 

@@ -312,11 +312,18 @@ __device__ __forceinline__ void fused_q_tile(const AttnArgs& a, char* lds, int b
 // (The body sits in the kernel template itself: moved into a device function
 // it compiles to a slower schedule of the same arithmetic.)
 // FQ: Q'' formed in the kernel from the latent (fixed length, D = 128).
+// SPL: key-split (fixed length): a.ksplit = P work-groups per query block,
+// part p taking the block's key tiles t = p, p + P, p + 2P, ... (half 0 the
+// even ones of that list, half 1 the odd ones); each writes its unnormalised
+// (O, m, l) to a.part and attn_split_merge_kernel forms O and the LSE.  For
+// grids that would leave CUs idle (short sequences): P times the work-groups,
+// and the longest block no longer sets the kernel's length.
 struct NoMap {};
-template <int D, bool VARLEN, bool FQ, typename Map>
+template <int D, bool VARLEN, bool FQ, typename Map, bool SPL = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
   static_assert(!FQ || (D == 128 && !VARLEN), "fused Q: fixed length, d = 128");
+  static_assert(!SPL || (!VARLEN && !FQ), "key split: fixed length, Q'' as stored");
   using GM = Geom<D>;
   constexpr int NKS = GM::NKS, NMB = GM::NMB, KT_BYTES = GM::KT_BYTES, VT_BYTES = GM::VT_BYTES;
   constexpr int HALF_BYTES = GM::HALF_BYTES, MERGE_STRIDE = GM::MERGE_STRIDE;
@@ -324,8 +331,22 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
 
   const Dims& dm = a.dm;
   int b, h, qb, nq, pos0;
+  int part = 0;                              // SPL: this work-group's share of the key tiles
   long qrow0, orow0;                         // Q row and O row of query 0 of the block's sequence
-  if constexpr (!VARLEN) {
+  if constexpr (SPL) {
+    nq = a.Sq;
+    pos0 = 0;
+    const int nqb = (nq + BM - 1) / BM;
+    const int per_qb = dm.Hq * a.B * a.ksplit;
+    qb = nqb - 1 - (int)(blockIdx.x / per_qb);             // heaviest blocks first
+    const int rem = blockIdx.x % per_qb;
+    const int hb = rem / a.ksplit;
+    part = rem % a.ksplit;
+    h = hb % dm.Hq;
+    b = hb / dm.Hq;
+    qrow0 = (long)(b * dm.Hq + h) * nq;
+    orow0 = (long)b * nq;
+  } else if constexpr (!VARLEN) {
     nq = a.Sq;
     pos0 = 0;
     const int nqb = (nq + BM - 1) / BM;
@@ -383,13 +404,26 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
       reinterpret_cast<const bf16*>(a.vt) + (long)(b * dm.Hkv + g) * D * a.s_pad;
 
   const int q_last = min(nq, q0 + BM) - 1;
-  const int ntiles = (pos0 + q_last) / BN + 1;
+  // SPL: the part's tiles are the block's tiles part, part + P, ...; ntiles
+  // counts them, and tile j of a half is the part's tile 2 j + half
+  const int ntl = (pos0 + q_last) / BN + 1;        // key tiles of the block
+  const int ntiles = SPL ? (part < ntl ? (ntl - part + a.ksplit - 1) / a.ksplit : 0) : ntl;
+  if (SPL && ntiles == 0) return;                  // a part with no tile: the merge skips it
   const int niter = (ntiles + 1) / 2;              // tiles of half 0 (>= those of half 1)
   const int nj = (ntiles - half + 1) / 2;          // tiles of this half
-  auto key_of = [&](int j) { return (2 * j + half) * BN; };
+  auto key_of = [&](int j) {
+    if constexpr (SPL) return ((2 * j + half) * a.ksplit + part) * BN;
+    else return (2 * j + half) * BN;
+  };
   // tiles this wave computes: those of its half up to its last row's diagonal
-  const int kt_max = min(ntiles - 1, (pos0 + r0 + 31) / BN);
-  const int nvalid = kt_max >= half ? (kt_max - half) / 2 + 1 : 0;
+  const int kt_max = min(ntl - 1, (pos0 + r0 + 31) / BN);
+  int nvalid;
+  if constexpr (SPL) {
+    const int t0 = part + a.ksplit * half;           // the half's first tile
+    nvalid = kt_max >= t0 ? (kt_max - t0) / (2 * a.ksplit) + 1 : 0;
+  } else {
+    nvalid = kt_max >= half ? (kt_max - half) / 2 + 1 : 0;
+  }
   const float scale = 1.44269504088896340736f / sqrtf((float)D);
 
   // Q^T fragments first: the prologue's waits then cover them, so no later
@@ -425,9 +459,10 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
   // unconditionally (a one-tile block has half 1 load key tile 0, which it
   // never uses).
   {
-    const int key = min(half, ntiles - 1) * BN;
+    const int key = SPL ? key_of(0) : min(half, ntiles - 1) * BN;   // SPL: past the keys reads zero
     dma_k<D>(kbuf(0), kbase, key, nkeys, wq, lane);
-    dma_v<D>(vbuf(0), vtbase, a.s_pad, key, wq, lane);
+    // (SPL: an empty half's first tile may lie past s_pad; any in-range tile serves)
+    dma_v<D>(vbuf(0), vtbase, a.s_pad, SPL ? min(key, a.s_pad - BN) : key, wq, lane);
   }
   if (nj > 1) dma_k<D>(kbuf(1), kbase, key_of(1), nkeys, wq, lane);
   wait_dma();
@@ -488,11 +523,14 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
       // shifts by an exact 0, so a row's arithmetic never depends on another
       // row's scores (an earlier row stays bit-identical whatever later
       // tokens hold).
-      const bool first = VARLEN ? (l_run == 0.0f && mt != -INFINITY) : j == 0;
+      const bool first = (VARLEN || SPL) ? (l_run == 0.0f && mt != -INFINITY) : j == 0;
       const bool grow = first || mt > lazy_raw;
       if (__any(grow)) {
         const float delta = grow ? mt : 0.0f;
-        const float alpha = __builtin_amdgcn_exp2f(-delta * scale);
+        float alpha = __builtin_amdgcn_exp2f(-delta * scale);
+        // SPL: a row's first visible tile may lie far below the offset; O and
+        // l are still 0 then, so the rescale is skipped (no 0 * inf)
+        if constexpr (SPL) alpha = first ? 1.0f : alpha;
         m_use += delta;
         l_run *= alpha;
 #pragma unroll
@@ -533,6 +571,9 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
   // barrier has retired every read of the tile buffers.  A wave that took no
   // tile hands over m = -inf (weight 0).
   if (nvalid == 0) m_use = -INFINITY;
+  if constexpr (SPL) {
+    if (l_run == 0.0f) m_use = -INFINITY;    // a row that saw no key of its part's tiles
+  }
   float* mg = reinterpret_cast<float*>(lds) + wq * MERGE_STRIDE * 64 + lane;
   wait_dma();
   if (half == 1) {
@@ -546,11 +587,16 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
   __syncthreads();
   if (half == 1) return;
   {
-    // half 0 always took tile 0, so its offset is finite.
+    // half 0 always took tile 0, so its offset is finite (not with SPL: an
+    // empty half has m = -inf and weight 0)
     const float m_b = mg[NMB * 16 * 64], l_b = mg[(NMB * 16 + 1) * 64];
     const float mn = fmaxf(m_use, m_b);
-    const float wa = __builtin_amdgcn_exp2f((m_use - mn) * scale);
-    const float wb = __builtin_amdgcn_exp2f((m_b - mn) * scale);
+    float wa = __builtin_amdgcn_exp2f((m_use - mn) * scale);
+    float wb = __builtin_amdgcn_exp2f((m_b - mn) * scale);
+    if constexpr (SPL) {
+      wa = m_use == -INFINITY ? 0.0f : wa;
+      wb = m_b == -INFINITY ? 0.0f : wb;
+    }
     l_run = l_run * wa + l_b * wb;
     m_use = mn;
 #pragma unroll
@@ -560,6 +606,25 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
   }
 
   // ---- epilogue: lane holds query my_q, channels 32*mb + 8*(r/4) + 4*hi + r%4
+  if constexpr (SPL) {
+    // the part's unnormalised O and its (m, l): partial ((b Hq + h) P + part) S + my_q
+    if (my_q < nq) {
+      const long pi = ((long)(b * dm.Hq + h) * a.ksplit + part) * nq + my_q;
+      float* po = a.part + pi * D;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f32x4*>(po + mb * 32 + 8 * j + 4 * hi) =
+              f32x4{oacc[mb][4 * j], oacc[mb][4 * j + 1], oacc[mb][4 * j + 2], oacc[mb][4 * j + 3]};
+      if (hi == 0) {
+        float* pml = a.part + (long)a.B * dm.Hq * a.ksplit * nq * D + pi * 2;
+        pml[0] = m_use;
+        pml[1] = l_run;
+      }
+    }
+    return;
+  }
   if (my_q < nq) {
     const float inv = 1.0f / l_run;
     const long row = VARLEN ? orow0 + my_q : (long)(b * nq + my_q);
@@ -587,13 +652,86 @@ void attn_fwd_mfma_kernel(AttnArgs a, Map vm) {
   }
 }
 
+// The key-split partials of each query combined in a fixed order (parts 0 ..
+// P - 1; a part with no tile of the query's block, or whose rows saw no key,
+// has weight 0): O = sum_p w_p O_p / sum_p w_p l_p with w_p = 2^((m_p - m) s),
+// m the largest m_p; the LSE as in the unsplit kernel.  Thread = 4 channels of
+// one query of one head.
+template <int D>
+__global__ __launch_bounds__(256) void attn_split_merge_kernel(AttnArgs a) {
+  const Dims& dm = a.dm;
+  const int S = a.Sq, P = a.ksplit;
+  const long t = (long)blockIdx.x * 256 + threadIdx.x;
+  const long nqh = (long)a.B * dm.Hq * S;
+  if (t >= nqh * (D / 4)) return;
+  const long qi = t / (D / 4);                 // ((b Hq + h) S + q)
+  const int c = (int)(t % (D / 4)) * 4;
+  const int q = (int)(qi % S);
+  const long bh = qi / S;
+  const int h = (int)(bh % dm.Hq), b = (int)(bh / dm.Hq);
+  const int qb = q / BM;
+  const int ntl = (min(S, qb * BM + BM) - 1) / BN + 1;
+  const int np = min(P, ntl);
+  const float scale = 1.44269504088896340736f / sqrtf((float)D);
+  const float* pml = a.part + nqh * P * D;
+  float mn = -INFINITY;
+  for (int p = 0; p < np; ++p) {
+    const long pi = (bh * P + p) * S + q;
+    if (pml[pi * 2 + 1] > 0.0f) mn = fmaxf(mn, pml[pi * 2]);
+  }
+  float L = 0.0f;
+  f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int p = 0; p < np; ++p) {
+    const long pi = (bh * P + p) * S + q;
+    const float lp = pml[pi * 2 + 1];
+    const float w = lp > 0.0f ? __builtin_amdgcn_exp2f((pml[pi * 2] - mn) * scale) : 0.0f;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(a.part + pi * D + c);
+    L = __builtin_fmaf(w, lp, L);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(w, v[e], o[e]);
+  }
+  const float inv = 1.0f / L;
+  const long row = (long)b * S + q;
+  bf16x4 v4;
+  f32x4 f4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f4[e] = o[e] * inv;
+    v4[e] = (bf16)f4[e];
+  }
+  *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.o) + (row * dm.Hq + h) * D + c) = v4;
+  if (a.o32) *reinterpret_cast<f32x4*>(a.o32 + (row * dm.Hq + h) * D + c) = f4;
+  if (c == 0 && a.lse)
+    a.lse[bh * S + q] = (mn * scale + __builtin_amdgcn_logf(L)) * 0.69314718055994530942f;
+}
+
 }  // namespace
+
+size_t attn_split_part_bytes(const Dims& dm, int B, int S, int P) {
+  return P > 1 ? (size_t)B * dm.Hq * P * S * (dm.d + 2) * 4 : 0;
+}
 
 hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s) {
   if ((a.dm.d != 128 && a.dm.d != 64) || a.vt == nullptr || a.s_pad < a.Sq || a.s_pad % BN != 0)
     return hipErrorInvalidValue;
   const int nqb = (a.Sq + BM - 1) / BM;
   dim3 grid(nqb * a.dm.Hq * a.B);
+  if (a.ksplit > 1) {
+    if (a.qlat || a.part == nullptr || a.ksplit > kMaxAttnSplit) return hipErrorInvalidValue;
+    dim3 gsplit(nqb * a.dm.Hq * a.B * a.ksplit);
+    const long nt = (long)a.B * a.dm.Hq * a.Sq * (a.dm.d / 4);
+    const dim3 gm((unsigned)((nt + 255) / 256));
+    if (a.dm.d == 128) {
+      hipLaunchKernelGGL((attn_fwd_mfma_kernel<128, false, false, NoMap, true>), gsplit, dim3(512),
+                         0, s, a, NoMap{});
+      hipLaunchKernelGGL(attn_split_merge_kernel<128>, gm, dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((attn_fwd_mfma_kernel<64, false, false, NoMap, true>), gsplit, dim3(512),
+                         0, s, a, NoMap{});
+      hipLaunchKernelGGL(attn_split_merge_kernel<64>, gm, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+  }
   if (a.qlat) {
     if (a.dm.d != 128 || !a.dm.bf16 || !a.conv_q || !a.conv_k || !a.rope || a.dm.kq > FQ_HALO + 1 ||
         a.dm.kk > FQ_HALO + 1 || (long)a.Sq * a.dm.nqkv * 2 >= (1L << 31))

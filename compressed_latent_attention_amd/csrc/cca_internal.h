@@ -212,7 +212,14 @@ struct AttnArgs {
   const void* conv_q;
   const void* conv_k;
   const float2* rope;
+  // key-split prefill (fixed length, Q'' as stored): ksplit > 1 work-groups per
+  // query block, their partials in `part` (attn_split_part_bytes), merged by a
+  // second kernel; 0 or 1: one work-group per query block
+  int ksplit;
 };
+constexpr int kMaxAttnSplit = 8;
+// fp32 bytes of the key-split partials: (O, m, l) per query, head and part
+size_t attn_split_part_bytes(const Dims& dm, int B, int S, int P);
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_varlen_mfma(const AttnArgs& a, const VarlenMap& vm, hipStream_t s);
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);

@@ -2,8 +2,11 @@
 forms Q'' from the latent itself and the mix writes only K'', V' and the
 cache.  y, the cache and the state against the oracle (relative L2 <= 1e-2,
 whole and per 128-token block), and against the separate passes of the same
-library (identical: the attention forms Q'' with the mix's operations); a prefill that saves for
-the backward ignores the switch (bit-identical)."""
+library: identical where the separate attention runs one work-group per query
+block (the attention forms Q'' with the mix's operations), within 2e-3 where it
+splits each block's keys over several work-groups (short sequences: fewer than
+512 work-groups), which changes only the order of the softmax sums.  A prefill
+that saves for the backward ignores the switch (bit-identical)."""
 import numpy as np
 import pytest
 
@@ -18,6 +21,12 @@ if not torch.cuda.is_available():
 
 from gpu_helpers import (TOL, block_rel, host, layer_of, params_of, rel, run_prefill,  # noqa: E402
                          saved_views, say, spec_of)
+
+
+def separate_attention_splits(w: Workload) -> bool:
+    """Whether the separate inference prefill splits its attention's keys
+    (fewer than 512 work-groups of 128 queries)."""
+    return (w.S + 127) // 128 * w.Hq * w.B < 512
 
 
 def check_fused(w: Workload):
@@ -46,7 +55,11 @@ def check_fused(w: Workload):
     for k in ("k_cache", "v_cache", "state"):
         assert torch.equal(fused[k], plain[k]), k
     # the prologue forms Q'' with the mix's operations, so y is identical too
-    assert torch.equal(fused["y"], plain["y"]), vs_plain
+    # (up to the order of the softmax sums where the separate attention splits)
+    if separate_attention_splits(w):
+        assert vs_plain <= 2e-3, vs_plain
+    else:
+        assert torch.equal(fused["y"], plain["y"]), vs_plain
     # a saving prefill is unaffected by the switch
     s_on = run_prefill(w, inp, with_saved=True, layer=layer)
     layer.set_prefill_fusion(False)
