@@ -134,15 +134,16 @@ SavedLayout saved_layout(const Dims& dm, long B, long S) {
 // Key-split parts per query block of an inference prefill's attention: with
 // fewer than two work-groups per CU (512 on the 256-CU MI355X, one 8-wave
 // work-group per CU at a time) the grid would leave CUs idle and the longest
-// query block alone would set the kernel's length; splitting each block's key
-// tiles over P work-groups (merged by a second kernel) fills the chip.
+// query block alone would set the kernel's length; its key tiles are then
+// split over two work-groups (merged by a second kernel).  More parts measured
+// slower (CCA prefill at S = 4096, 128 blocks: attention 55.6 us unsplit,
+// 43.3 us with 2 parts, 44.6 / 56.4 / 67.1 us with 4 / 6 / 8): each part pays
+// its own Q load, pipeline fill and fp32 partials.
 constexpr int kAttnTargetWGs = 512;
 int prefill_ksplit(const Dims& dm, long B, long S) {
   if (!prefill_uses_mfma(dm)) return 1;
   const long grid = (S + 127) / 128 * dm.Hq * B;
-  if (grid >= kAttnTargetWGs) return 1;
-  const long P = (kAttnTargetWGs + grid - 1) / grid;
-  return (int)std::min<long>(P, 4);
+  return grid < kAttnTargetWGs ? 2 : 1;
 }
 
 struct DecodeLayout {

@@ -226,7 +226,7 @@ def test_causality_bit_identical_on_gpu():
 
 def test_prefill_is_deterministic():
     """Saving and inference prefills repeat bit for bit (the inference one at
-    this length splits its attention's keys over four work-groups per query
+    this length splits its attention's keys over two work-groups per query
     block, merged in a fixed order)."""
     w = Workload("bf16_det", B=1, S=513, E=512, C=1, Hq=4, Hkv=2, seed=42)
     inp = make_inputs(w)
