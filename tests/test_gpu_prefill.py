@@ -242,6 +242,22 @@ def test_prefill_is_deterministic():
         assert torch.equal(va[k], vb[k]), k
 
 
+def test_prefill_workspace_holds_key_split_partials():
+    """cca_workspace_bytes(PREFILL) is the saved-buffer size plus, when the
+    attention grid holds fewer than 512 work-groups of 128 queries, the fp32
+    partials of its two-way key split: (d + 2) floats per query, head and part."""
+    import compressed_latent_attention_amd as cca
+    for w, split in ((WORKLOADS["cca_prefill_4k"], True),
+                     (WORKLOADS["ccgqa_prefill_16k"], False),
+                     (Workload("ws_b3", B=3, S=1000, E=512, C=2, Hq=4, Hkv=2, seed=1), True)):
+        layer = cca.CCALayer(w.E, w.C, w.Hq, w.Hkv, w.capacity, w.kq, w.kk, w.s_v, w.flags,
+                             w.rope_base, w.dtype)
+        n = cca.load().cca_workspace_bytes(layer.handle, cca.CCA_OP_PREFILL, w.B, w.S)
+        extra = w.B * w.Hq * 2 * w.S * (w.d + 2) * 4 if split else 0
+        assert n == layer.saved_bytes(w.B, w.S) + extra, (w.name, n)
+        layer.close()
+
+
 def test_empty_batch_or_sequence_is_rejected():
     """B = 0 or S = 0: prefill and backward return CCA_ERR_INVALID_ARG before
     any launch and leave their outputs as they were."""
