@@ -139,11 +139,16 @@ SavedLayout saved_layout(const Dims& dm, long B, long S) {
 // slower (CCA prefill at S = 4096, 128 blocks: attention 55.6 us unsplit,
 // 43.3 us with 2 parts, 44.6 / 56.4 / 67.1 us with 4 / 6 / 8): each part pays
 // its own Q load, pipeline fill and fp32 partials.
+// Sequences of at most 8 blocks (16 key tiles or fewer per block) stay
+// unsplit: their chains are short and the partials and merge would cost more.
+// Splitting in proportion to the block's length (ceil((qb + 1) / c) parts)
+// measured slower still: 54.5 us with c = 8, 61.9 with c = 4.
 constexpr int kAttnTargetWGs = 512;
+constexpr int kAttnMinSplitBlocks = 9;
 int prefill_ksplit(const Dims& dm, long B, long S) {
   if (!prefill_uses_mfma(dm)) return 1;
-  const long grid = (S + 127) / 128 * dm.Hq * B;
-  return grid < kAttnTargetWGs ? 2 : 1;
+  const long nqb = (S + 127) / 128;
+  return nqb * dm.Hq * B < kAttnTargetWGs && nqb >= kAttnMinSplitBlocks ? 2 : 1;
 }
 
 struct DecodeLayout {

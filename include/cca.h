@@ -121,8 +121,9 @@ void cca_destroy(cca_handle* h);
 /* Bytes of scratch the caller passes as `workspace` to the named operation
  * (CCA_OP_*) with batch B and length S (S is ignored for decode).  0 on a bad
  * argument.  For CCA_OP_PREFILL it is the saved-buffer size plus, when the
- * prefill's attention grid would hold fewer than 512 work-groups (short
- * sequences, bf16 with d = 128 or 64), the fp32 partials of its key split. */
+ * prefill's attention grid would hold fewer than 512 work-groups of 128
+ * queries over more than 8 query blocks (short sequences, bf16 with d = 128
+ * or 64), the fp32 partials of its two-way key split. */
 size_t cca_workspace_bytes(const cca_handle* h, int op, int32_t B, int32_t S);
 
 /* Bytes of the `saved` buffer a prefill fills for cca_backward.  Its layout,

@@ -4,8 +4,8 @@ cache.  y, the cache and the state against the oracle (relative L2 <= 1e-2,
 whole and per 128-token block), and against the separate passes of the same
 library: identical where the separate attention runs one work-group per query
 block (the attention forms Q'' with the mix's operations), within 2e-3 where it
-splits each block's keys over several work-groups (short sequences: fewer than
-512 work-groups), which changes only the order of the softmax sums.  A prefill
+splits each block's keys over two work-groups (fewer than 512 work-groups and
+more than 8 blocks), which changes only the order of the softmax sums.  A prefill
 that saves for the backward ignores the switch (bit-identical)."""
 import numpy as np
 import pytest
@@ -25,8 +25,9 @@ from gpu_helpers import (TOL, block_rel, host, layer_of, params_of, rel, run_pre
 
 def separate_attention_splits(w: Workload) -> bool:
     """Whether the separate inference prefill splits its attention's keys
-    (fewer than 512 work-groups of 128 queries)."""
-    return (w.S + 127) // 128 * w.Hq * w.B < 512
+    (fewer than 512 work-groups of 128 queries, and more than 8 blocks)."""
+    nqb = (w.S + 127) // 128
+    return nqb * w.Hq * w.B < 512 and nqb > 8
 
 
 def check_fused(w: Workload):

@@ -118,6 +118,40 @@ def test_prefill_bf16(w):
     check_prefill(w, make_inputs(w))
 
 
+# short sequences whose attention splits each query block's keys over two
+# work-groups (fewer than 512 work-groups of 128 queries, more than 8 blocks):
+# two sequences with a ragged last block, d = 64, one KV head with three taps
+SPLIT_BF16 = [
+    Workload("split_gqa_ragged_b2", B=2, S=1500, E=512, C=1, Hq=4, Hkv=2, seed=101),
+    Workload("split_d64", B=1, S=2300, E=512, C=2, Hq=4, Hkv=2, seed=102),
+    Workload("split_g4_k3", B=1, S=1200, E=512, C=1, Hq=4, Hkv=1, kq=3, kk=2, seed=103),
+]
+
+
+@pytest.mark.parametrize("w", SPLIT_BF16, ids=[w.name for w in SPLIT_BF16])
+def test_prefill_key_split_bf16(w):
+    check_prefill(w, make_inputs(w))
+
+
+def test_causality_bit_identical_key_split():
+    """The key-split attention keeps causality bit-exact: perturbing tokens
+    t >= t0 leaves y[:t0] unchanged (parts whose tiles a row cannot see merge
+    with weight 0)."""
+    w = Workload("bf16_causal_split", B=1, S=1500, E=512, C=1, Hq=4, Hkv=2, seed=104)
+    inp = make_inputs(w)
+    y0 = run_prefill(w, inp, with_saved=False)["y"].clone()
+    inp2 = dict(inp)
+    x2 = inp["x"].copy()
+    t0 = 1100
+    x2[:, t0:] = np.asarray(np.random.default_rng(2).standard_normal(x2[:, t0:].shape),
+                            np.float32)
+    from compressed_latent_attention_amd.synthetic import round_bf16
+    inp2["x"] = round_bf16(x2)
+    y1 = run_prefill(w, inp2, with_saved=False)["y"]
+    assert torch.equal(y0[:, :t0], y1[:, :t0])
+    assert not torch.equal(y0[:, t0], y1[:, t0])
+
+
 def test_prefill_cca_4k_bf16():
     w = WORKLOADS["cca_prefill_4k"]
     check_prefill(w, make_inputs(w))
@@ -226,9 +260,9 @@ def test_causality_bit_identical_on_gpu():
 
 def test_prefill_is_deterministic():
     """Saving and inference prefills repeat bit for bit (the inference one at
-    this length splits its attention's keys over two work-groups per query
-    block, merged in a fixed order)."""
-    w = Workload("bf16_det", B=1, S=513, E=512, C=1, Hq=4, Hkv=2, seed=42)
+    this length splits each query block's keys over two work-groups, merged in
+    a fixed order)."""
+    w = Workload("bf16_det", B=1, S=1300, E=512, C=1, Hq=4, Hkv=2, seed=42)
     inp = make_inputs(w)
     a = run_prefill(w, inp)
     b = run_prefill(w, inp)
@@ -244,16 +278,18 @@ def test_prefill_is_deterministic():
 
 def test_prefill_workspace_holds_key_split_partials():
     """cca_workspace_bytes(PREFILL) is the saved-buffer size plus, when the
-    attention grid holds fewer than 512 work-groups of 128 queries, the fp32
-    partials of its two-way key split: (d + 2) floats per query, head and part."""
+    attention grid holds fewer than 512 work-groups of 128 queries and more
+    than 8 query blocks, the fp32 partials of its two-way key split: (d + 2)
+    floats per query, head and part."""
     import compressed_latent_attention_amd as cca
-    for w, split in ((WORKLOADS["cca_prefill_4k"], True),
-                     (WORKLOADS["ccgqa_prefill_16k"], False),
-                     (Workload("ws_b3", B=3, S=1000, E=512, C=2, Hq=4, Hkv=2, seed=1), True)):
+    for w, parts in ((WORKLOADS["cca_prefill_4k"], 2),
+                     (WORKLOADS["ccgqa_prefill_16k"], 0),
+                     (Workload("ws_b3", B=3, S=1000, E=512, C=2, Hq=4, Hkv=2, seed=1), 0),
+                     (Workload("ws_b2", B=2, S=2100, E=512, C=2, Hq=4, Hkv=2, seed=1), 2)):
         layer = cca.CCALayer(w.E, w.C, w.Hq, w.Hkv, w.capacity, w.kq, w.kk, w.s_v, w.flags,
                              w.rope_base, w.dtype)
         n = cca.load().cca_workspace_bytes(layer.handle, cca.CCA_OP_PREFILL, w.B, w.S)
-        extra = w.B * w.Hq * 2 * w.S * (w.d + 2) * 4 if split else 0
+        extra = w.B * w.Hq * parts * w.S * (w.d + 2) * 4
         assert n == layer.saved_bytes(w.B, w.S) + extra, (w.name, n)
         layer.close()
 
